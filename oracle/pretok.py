@@ -1,0 +1,117 @@
+"""Oracle pre-tokenizer: sequential regex split (the G stage of F = E* o G).
+
+TokTier summary page, §3.2 and Appendix A.1: GPT-style tokenization first cuts
+the text into pre-tokens with an ordered regex (leftmost alternative that
+matches wins, greedy quantifiers with backtracking), then encodes each piece on
+its own.  The pages name the rule families but never print the patterns, so
+the two rule sets below are this project's renderings of the feature lists it
+was given:
+
+  pattern 0, GPT-2-style: contractions (lower case), letters, digits,
+  punctuation, whitespace with the "not followed by a non-space" lookahead.
+
+  pattern 1, cl100k-style: contractions with ASCII-only case folding, letters
+  with one optional leading non-letter/non-digit/non-newline char, digit groups
+  of one to three, punctuation that swallows the CR/LF chars after it,
+  whitespace up to the last CR/LF, then the lookahead rule.
+
+Character sets (pinned by tests against the ``regex`` module's own classes):
+  L  = \\p{L}    N = \\p{N}    (Unicode tables of the ``regex`` module)
+  W  = the 25 code points with the Unicode White_Space property.  U+001C..U+001F
+       are *not* whitespace here (``str.isspace`` disagrees; we do not use it).
+  O  = everything else.
+
+Invalid UTF-8 is an error (raised by the strict decoder), never replaced.
+"""
+import regex
+
+# The Unicode White_Space property, spelled out (25 code points).
+WHITESPACE_CPS = (
+    [0x09, 0x0A, 0x0B, 0x0C, 0x0D, 0x20, 0x85, 0xA0, 0x1680]
+    + list(range(0x2000, 0x200B))
+    + [0x2028, 0x2029, 0x202F, 0x205F, 0x3000]
+)
+_W = "\\t\\n\\x0b\\x0c\\r \\x85\\xa0\\u1680\\u2000-\\u200a\\u2028\\u2029\\u202f\\u205f\\u3000"
+W_CLASS = "[" + _W + "]"          # one whitespace char
+NOT_W_CLASS = "[^" + _W + "]"     # one non-whitespace char
+O_CLASS = "[^" + _W + "\\p{L}\\p{N}]"  # neither whitespace, letter nor digit
+
+GPT2 = 0
+CL100K = 1
+
+# GPT-2-style, alternatives in priority order:
+#   G1 apostrophe contraction (lower case only)
+#   G2 optional space + letters      G3 optional space + digits
+#   G4 optional space + "other" run
+#   G5 whitespace not followed by a non-whitespace char   G6 whitespace
+_GPT2_RULES = [
+    "'(?:s|t|re|ve|m|ll|d)",
+    " ?\\p{L}+",
+    " ?\\p{N}+",
+    " ?" + O_CLASS + "+",
+    W_CLASS + "+(?!" + NOT_W_CLASS + ")",
+    W_CLASS + "+",
+]
+
+# cl100k-style, alternatives in priority order:
+#   C1 contraction, ASCII case-insensitive (explicit [sS] etc, no Unicode folding)
+#   C2 one optional char that is not CR/LF/letter/digit, then letters
+#   C3 one to three digits
+#   C4 optional space, "other" run, then any CR/LF chars
+#   C5 whitespace up to and including the last CR/LF of the whitespace run
+#   C6 whitespace not followed by a non-whitespace char   C7 whitespace
+_CL100K_RULES = [
+    "'(?:[sS]|[tT]|[rR][eE]|[vV][eE]|[mM]|[lL][lL]|[dD])",
+    "[^\\r\\n\\p{L}\\p{N}]?\\p{L}+",
+    "\\p{N}{1,3}",
+    " ?" + O_CLASS + "+[\\r\\n]*",
+    W_CLASS + "*[\\r\\n]+",
+    W_CLASS + "+(?!" + NOT_W_CLASS + ")",
+    W_CLASS + "+",
+]
+
+RULES = {GPT2: _GPT2_RULES, CL100K: _CL100K_RULES}
+PATTERNS = {k: "|".join(v) for k, v in RULES.items()}
+_COMPILED = {k: regex.compile(v, regex.VERSION0) for k, v in PATTERNS.items()}
+
+
+def split(text, pattern_id):
+    """Split a str into pre-tokens with the ordered rule set ``pattern_id``.
+
+    Plain left-to-right ``finditer``: each match starts where the previous one
+    ended.  The rule sets match every char, so the pieces tile the text.
+    """
+    pieces = [m.group() for m in _COMPILED[pattern_id].finditer(text)]
+    if "".join(pieces) != text or any(p == "" for p in pieces):
+        raise AssertionError("rule set did not tile the text")
+    return pieces
+
+
+def split_bytes(data, pattern_id):
+    """Split UTF-8 bytes; returns (pieces as bytes, byte offset of each piece).
+
+    Raises UnicodeDecodeError on invalid UTF-8 (strict decoding).
+    """
+    text = bytes(data).decode("utf-8", errors="strict")
+    pieces = split(text, pattern_id)
+    out, starts, pos = [], [], 0
+    for p in pieces:
+        b = p.encode("utf-8")
+        out.append(b)
+        starts.append(pos)
+        pos += len(b)
+    return out, starts
+
+
+def piece_starts_batch(data, offsets, pattern_id):
+    """Byte offsets (into the concatenation) of every piece of every sequence.
+
+    Each sequence ``data[offsets[s]:offsets[s+1]]`` is an independent text: its
+    end is end-of-text for the lookahead rules and no piece crosses it.
+    """
+    starts = []
+    for s in range(len(offsets) - 1):
+        a, b = offsets[s], offsets[s + 1]
+        _, st = split_bytes(data[a:b], pattern_id)
+        starts.extend(a + x for x in st)
+    return starts

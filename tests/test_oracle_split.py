@@ -1,0 +1,143 @@
+"""Pins for the oracle pre-tokenizer (oracle.pretok).
+
+What pins it, besides itself:
+  * worked examples derived by hand from the two rule tables;
+  * a second formulation (tests/runsplit.py: the run-decomposition predicate of
+    TokTier summary page §4.1, evaluated without any regex engine) that must
+    agree on every string of length <= 5 over a class-covering alphabet and on
+    random longer strings;
+  * a third-party implementation: HF ``tokenizers``' built-in GPT-2 ByteLevel
+    pre-tokenizer (its own copy of the GPT-2 pattern, run by Oniguruma), and the
+    cl100k-style pattern string run by Oniguruma instead of ``regex``;
+  * the whitespace set equals the ``regex`` module's \\s (Unicode White_Space).
+"""
+import itertools
+import random
+import re
+
+import pytest
+import regex
+
+from oracle.pretok import CL100K, GPT2, PATTERNS, WHITESPACE_CPS, split, split_bytes
+from runsplit import piece_starts
+
+EXAMPLES = [
+    # (text, GPT-2-style pieces, cl100k-style pieces)
+    ("don't", ["don", "'t"], ["don", "'t"]),
+    ("DON'T", ["DON", "'", "T"], ["DON", "'T"]),
+    ("a  b", ["a", " ", " b"], ["a", " ", " b"]),
+    ("12345", ["12345"], ["123", "45"]),
+    (" 123", [" 123"], [" ", "123"]),
+    ("x'ya", ["x", "'", "ya"], ["x", "'ya"]),
+    ("\n\nfoo", ["\n", "\n", "foo"], ["\n\n", "foo"]),
+    (";\n\n  foo", [";", "\n\n ", " foo"], [";\n\n", " ", " foo"]),
+    (".\tfoo", [".", "\t", "foo"], [".", "\tfoo"]),
+    (" .foo", [" .", "foo"], [" .", "foo"]),
+    ("x.'s", ["x", ".'", "s"], ["x", ".'", "s"]),
+    ("it's", ["it", "'s"], ["it", "'s"]),
+    ("'stop", ["'s", "top"], ["'s", "top"]),
+    ("we'll go", ["we", "'ll", " go"], ["we", "'ll", " go"]),
+    ("x 's", ["x", " '", "s"], ["x", " '", "s"]),
+    ("a   ", ["a", "   "], ["a", "   "]),
+    ("a \n b", ["a", " \n", " b"], ["a", " \n", " b"]),
+    ("a\n \n  b", ["a", "\n \n ", " b"], ["a", "\n \n", " ", " b"]),
+    ("1234567", ["1234567"], ["123", "456", "7"]),
+    ("x+=1", ["x", "+=", "1"], ["x", "+=", "1"]),
+    ("foo_bar", ["foo", "_", "bar"], ["foo", "_bar"]),
+    ("中文 é", ["中文", " é"], ["中文", " é"]),
+    ("a\r\nb", ["a", "\r", "\n", "b"], ["a", "\r\n", "b"]),
+]
+
+
+@pytest.mark.parametrize("text,gpt2,cl100k", EXAMPLES)
+def test_worked_examples(text, gpt2, cl100k):
+    assert split(text, GPT2) == gpt2
+    assert split(text, CL100K) == cl100k
+
+
+def _starts(pieces):
+    out, pos = [], 0
+    for p in pieces:
+        out.append(pos)
+        pos += len(p)
+    return out
+
+
+ALPHA = ["a", "s", "r", "e", "S", "1", ".", "'", " ", "\n", "\t", "\r"]
+
+
+@pytest.mark.parametrize("pattern_id", [GPT2, CL100K])
+def test_exhaustive_short_strings_against_run_decomposition(pattern_id):
+    bad = []
+    for length in range(6):
+        for tup in itertools.product(ALPHA, repeat=length):
+            s = "".join(tup)
+            if _starts(split(s, pattern_id)) != piece_starts(s, pattern_id):
+                bad.append(s)
+    assert bad == []
+
+
+ALPHA2 = ALPHA + list("lLvVmdDtTEé中😀") + ["　", "\xa0", "2", "²", "_", "(", "\x0b", "٣"]
+
+
+@pytest.mark.parametrize("pattern_id", [GPT2, CL100K])
+def test_random_strings_against_run_decomposition(pattern_id):
+    rng = random.Random(11 + pattern_id)
+    for _ in range(30_000):
+        s = "".join(rng.choice(ALPHA2) for _ in range(rng.randint(6, 30)))
+        assert _starts(split(s, pattern_id)) == piece_starts(s, pattern_id), repr(s)
+
+
+def test_long_runs_against_run_decomposition():
+    texts = ["a" + "1" * 1000 + "x", ".\n" * 3 + "\n" * 500 + " " * 700 + "z", " " * 999 + "7",
+             "\t" * 5 + "\n" + " " * 400, "x" + "٣" * 11 + "2" * 7]
+    for t in texts:
+        for pat in (GPT2, CL100K):
+            assert _starts(split(t, pat)) == piece_starts(t, pat)
+
+
+# Characters both engines classify identically (no U+001C..001F, no recent code points).
+HF_ALPHA = ALPHA + list("lLvVmdDtTEé中xyz09_(){};:,") + ["\xa0", "　", "é"]
+
+
+def test_gpt2_split_matches_hf_bytelevel():
+    pre = pytest.importorskip("tokenizers.pre_tokenizers")
+    bl = pre.ByteLevel(add_prefix_space=False, use_regex=True)
+    rng = random.Random(5)
+    for _ in range(5000):
+        s = "".join(rng.choice(HF_ALPHA) for _ in range(rng.randint(1, 40)))
+        hf = [a for _, (a, _) in bl.pre_tokenize_str(s)]
+        assert _starts(split(s, GPT2)) == hf, repr(s)
+
+
+def test_cl100k_pattern_under_oniguruma_matches_regex_module():
+    tk = pytest.importorskip("tokenizers")
+    # Oniguruma reads a two-digit hex escape as a raw byte; spell code points as x{...}.
+    pat = re.sub(r"\\(?:x([0-9a-f]{2})|u([0-9a-f]{4}))", lambda m: "\\x{%s}" % (m.group(1) or m.group(2)),
+                 PATTERNS[CL100K])
+    sp = tk.pre_tokenizers.Split(tk.Regex(pat), behavior="isolated")
+    rng = random.Random(6)
+    for _ in range(5000):
+        s = "".join(rng.choice(HF_ALPHA) for _ in range(rng.randint(1, 40)))
+        hf = [a for _, (a, _) in sp.pre_tokenize_str(s)]
+        assert _starts(split(s, CL100K)) == hf, repr(s)
+
+
+def test_whitespace_set_is_unicode_white_space():
+    s = regex.compile(r"\s")
+    got = [cp for cp in range(0x110000) if not 0xD800 <= cp <= 0xDFFF and s.match(chr(cp))]
+    assert got == sorted(WHITESPACE_CPS)
+    assert len(WHITESPACE_CPS) == 25
+    # str.isspace disagrees on the four information separators; we follow \s.
+    assert all(chr(c).isspace() for c in range(0x1C, 0x20))
+    assert not any(c in WHITESPACE_CPS for c in range(0x1C, 0x20))
+
+
+def test_split_bytes_offsets_and_invalid_utf8():
+    data = "x é中 12".encode()
+    pieces, starts = split_bytes(data, CL100K)
+    assert b"".join(pieces) == data
+    assert starts == [0, 1, 7, 8]
+    for bad in (b"\xff", b"a\x80", b"\xc3", b"\xed\xa0\x80", b"\xc0\xaf", b"\xf4\x90\x80\x80"):
+        with pytest.raises(UnicodeDecodeError):
+            split_bytes(bad, GPT2)
