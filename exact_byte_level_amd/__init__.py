@@ -1,0 +1,161 @@
+"""exact_byte_level_amd -- exact byte-level BPE tokenization on one MI355X.
+
+Thin ctypes binding over libtt.so (C ABI in include/tt.h).  Every step of the
+tokenization runs in the library's HIP kernels; this module only marshals
+arguments: PyTorch provides device memory (``data_ptr()``) and the current HIP
+stream.  If libtt.so is missing the binding raises; there is no CPU fallback.
+
+    import exact_byte_level_amd as tt
+    tt.load(merges, pattern_id=tt.PATTERN_CL100K)   # merges: int32 [M, 2], rank order
+    ids = tt.encode(torch.frombuffer(text, dtype=torch.uint8).cuda())
+"""
+import ctypes
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libtt.so")
+
+PATTERN_GPT2 = 0
+PATTERN_CL100K = 1
+
+TT_OK = 0
+TT_EINVAL = -1
+TT_ETABLE = -2
+TT_ENOMEM = -3
+TT_EHIP = -4
+TT_EUTF8 = -5
+TT_ENOTLOADED = -6
+TT_EOFFSETS = -7
+TT_ETOOBIG = -8
+
+_lib = None
+
+
+class TTError(RuntimeError):
+    def __init__(self, code, where):
+        self.code = code
+        super().__init__("%s: %s (%d)" % (where, strerror(code) if _lib else "error", code))
+
+
+def lib():
+    """The loaded libtt.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError("libtt.so not built (%s); run exact_byte_level_amd.build.build()" % LIB_PATH)
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32
+        L.tt_load_bpe.argtypes = [vp, vp, i64, i32]
+        L.tt_reserve.argtypes = [i64, i32]
+        L.tt_encode.argtypes = [vp, i64, vp, vp, vp]
+        L.tt_encode_batch.argtypes = [vp, i64, vp, i32, vp, vp, vp]
+        L.tt_pretokenize.argtypes = [vp, i64, vp, i32, vp, vp, vp]
+        L.tt_char_class.argtypes = [ctypes.c_uint32]
+        L.tt_free.argtypes = []
+        L.tt_free.restype = None
+        L.tt_strerror.argtypes = [ctypes.c_int]
+        L.tt_strerror.restype = ctypes.c_char_p
+        for f in ("tt_load_bpe", "tt_reserve", "tt_encode", "tt_encode_batch", "tt_pretokenize", "tt_char_class"):
+            getattr(L, f).restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def strerror(code):
+    return lib().tt_strerror(int(code)).decode()
+
+
+def _check(rc, where):
+    if rc != TT_OK:
+        raise TTError(rc, where)
+
+
+def _stream(stream):
+    import torch
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def load(merges, ranks=None, pattern_id=PATTERN_GPT2):
+    """Load a merge table: merges int32 [M, 2]; merge k makes id 256 + ranks[k]
+    (ranks defaults to 0..M-1, i.e. rows in rank order)."""
+    m = np.ascontiguousarray(np.asarray(merges, dtype=np.int32).reshape(-1, 2))
+    r = None if ranks is None else np.ascontiguousarray(np.asarray(ranks, dtype=np.int32).reshape(-1))
+    if r is not None and len(r) != len(m):
+        raise ValueError("ranks must have one entry per merge")
+    rc = lib().tt_load_bpe(m.ctypes.data if len(m) else None, None if r is None else r.ctypes.data,
+                           len(m), int(pattern_id))
+    _check(rc, "tt_load_bpe")
+
+
+def reserve(max_bytes, max_seqs=1):
+    _check(lib().tt_reserve(int(max_bytes), int(max_seqs)), "tt_reserve")
+
+
+def encode_into(data, out_ids, out_n, stream=None):
+    """Enqueue an encode of a uint8 CUDA tensor into caller buffers (no sync)."""
+    n = data.numel()
+    rc = lib().tt_encode(data.data_ptr() if n else None, n, out_ids.data_ptr(), out_n.data_ptr(), _stream(stream))
+    _check(rc, "tt_encode")
+
+
+def encode(data, stream=None):
+    """Token ids (int32 CUDA tensor) of one UTF-8 text held in a uint8 CUDA tensor."""
+    import torch
+    assert data.dtype == torch.uint8 and data.is_cuda and data.is_contiguous()
+    out = torch.empty(max(data.numel(), 1), dtype=torch.int32, device=data.device)
+    out_n = torch.empty(1, dtype=torch.int64, device=data.device)
+    encode_into(data, out, out_n, stream)
+    t = int(out_n.item())
+    if t < 0:
+        raise TTError(t, "tt_encode")
+    return out[:t]
+
+
+def encode_batch_into(data, offsets, out_ids, out_offsets, stream=None):
+    n = data.numel()
+    rc = lib().tt_encode_batch(data.data_ptr() if n else None, n, offsets.data_ptr(), offsets.numel() - 1,
+                               out_ids.data_ptr(), out_offsets.data_ptr(), _stream(stream))
+    _check(rc, "tt_encode_batch")
+
+
+def encode_batch(data, offsets, stream=None):
+    """(ids, out_offsets) for concatenated texts with int64 CUDA offsets [B+1]."""
+    import torch
+    assert offsets.dtype == torch.int64 and offsets.is_cuda
+    out = torch.empty(max(data.numel(), 1), dtype=torch.int32, device=data.device)
+    out_off = torch.empty(offsets.numel(), dtype=torch.int64, device=data.device)
+    encode_batch_into(data, offsets, out, out_off, stream)
+    off = out_off.cpu()
+    t = int(off[-1])
+    if t < 0:
+        raise TTError(t, "tt_encode_batch")
+    return out[:t], off
+
+
+def pretokenize(data, offsets=None, stream=None):
+    """Byte offsets (int32 CUDA tensor) of every pre-token start (no sentinel)."""
+    import torch
+    n = data.numel()
+    starts = torch.empty(n + 1, dtype=torch.int32, device=data.device)
+    out_np = torch.empty(1, dtype=torch.int64, device=data.device)
+    rc = lib().tt_pretokenize(data.data_ptr() if n else None, n,
+                              None if offsets is None else offsets.data_ptr(),
+                              1 if offsets is None else offsets.numel() - 1,
+                              starts.data_ptr(), out_np.data_ptr(), _stream(stream))
+    _check(rc, "tt_pretokenize")
+    p = int(out_np.item())
+    if p < 0:
+        raise TTError(p, "tt_pretokenize")
+    return starts[:p]
+
+
+def char_class(cp):
+    """Class of a code point in the compiled table: 0 other, 1 L, 2 N, 3 White_Space."""
+    return lib().tt_char_class(int(cp))
+
+
+def free():
+    lib().tt_free()

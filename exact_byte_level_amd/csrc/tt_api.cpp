@@ -1,0 +1,385 @@
+// tt_api.cpp -- C ABI of libtt: tokenizer loading, device tables, workspace,
+// and the enqueue-only encode entry points declared in include/tt.h.
+#include <algorithm>
+#include <cstring>
+#include <mutex>
+#include <unordered_map>
+#include <unordered_set>
+#include <vector>
+
+#include "tt.h"
+#include "tt_kernels.h"
+#include "unicode_table.inc"
+
+namespace {
+
+using namespace tt;
+
+const uint8_t h_uni_l1[TT_UNI_L1_SIZE] = {TT_UNI_L1_DATA};
+const uint8_t h_uni_l2[TT_UNI_NBLOCKS * 64] = {TT_UNI_L2_DATA};
+
+struct State {
+  bool loaded = false;
+  int pattern = 0;
+  int64_t n_merges = 0;
+  int device = -1;
+  uint32_t* d_byte_pair = nullptr;
+  uint64_t* d_pair = nullptr;
+  CacheEntry* d_cache = nullptr;
+  Tables tb{};
+  void* d_ws = nullptr;
+  int64_t ws_n = 0;     // bytes of input the workspace is sized for
+  Work w{};
+};
+
+State g;
+std::mutex g_mu;
+
+template <class T>
+void free_dev(T*& p) {
+  if (p) (void)hipFree((void*)p);
+  p = nullptr;
+}
+
+uint64_t next_pow2(uint64_t v) {
+  uint64_t p = 1;
+  while (p < v) p <<= 1;
+  return p;
+}
+
+int log2_u64(uint64_t p) {
+  int k = 0;
+  while ((1ull << k) < p) ++k;
+  return k;
+}
+
+// Classic lowest-rank-first BPE on the host, used once per token when the
+// whole-piece table is built (which token byte strings encode to themselves).
+std::vector<uint32_t> host_bpe(const std::vector<uint32_t>& in,
+                               const std::unordered_map<uint64_t, uint32_t>& rank) {
+  std::vector<uint32_t> ids = in;
+  for (;;) {
+    uint32_t best = RANK_NONE;
+    size_t bi = 0;
+    for (size_t i = 0; i + 1 < ids.size(); ++i) {
+      auto it = rank.find(pair_key(ids[i], ids[i + 1]));
+      if (it != rank.end() && it->second < best) {
+        best = it->second;
+        bi = i;
+      }
+    }
+    if (best == RANK_NONE) return ids;
+    ids[bi] = 256u + best;
+    ids.erase(ids.begin() + (ptrdiff_t)bi + 1);
+  }
+}
+
+void release_tables() {
+  free_dev(g.d_byte_pair);
+  free_dev(g.d_pair);
+  free_dev(g.d_cache);
+  g.loaded = false;
+}
+
+void release_workspace() {
+  if (g.d_ws) (void)hipFree(g.d_ws);
+  g.d_ws = nullptr;
+  g.ws_n = 0;
+  g.w = Work{};
+}
+
+size_t align_up(size_t v) { return (v + 255) & ~(size_t)255; }
+
+// Carve the workspace for inputs of up to n bytes.
+size_t layout(int64_t n, char* base, Work* w) {
+  const size_t ntiles = (size_t)((n + TILE - 1) / TILE) + 1;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    char* p = base ? base + off : nullptr;
+    off += align_up(bytes);
+    return p;
+  };
+  const size_t nn = (size_t)n + 1;
+  Work t{};
+  t.tile_fwd = (uint32_t*)take(ntiles * 4);
+  t.tile_bwd = (uint32_t*)take(ntiles * 4);
+  t.tile_cnt = (uint32_t*)take(ntiles * 4);
+  t.flags = (uint16_t*)take(ntiles * PT_THREADS * 2);
+  t.piece_start = (int32_t*)take((nn + 1) * 4);
+  t.piece_cnt = (int32_t*)take(nn * 4);
+  t.tmp_ids = (int32_t*)take(nn * 4);
+  t.tmp_rank = (uint32_t*)take(nn * 4);
+  t.tok_off = (int32_t*)take((nn + 1) * 4);
+  t.blk_sum = (uint32_t*)take((nn / EMIT_PER_BLOCK + 2) * 4);
+  t.long_list = (int32_t*)take((nn / (LANE_CAP + 1) + 2) * 4);
+  t.huge_list = (int32_t*)take((nn / HUGE_TOKENS + 2) * 4);
+  t.ctr = (uint32_t*)take(CTR_COUNT * 4);
+  if (w) *w = t;
+  return off;
+}
+
+// Make the workspace large enough for n input bytes (synchronises if it grows).
+int ensure_workspace(int64_t n) {
+  if (n <= g.ws_n && g.d_ws) return TT_OK;
+  int64_t want = std::max<int64_t>(n, (int64_t)1 << 16);
+  want = (want + TILE - 1) / TILE * TILE;
+  if (hipDeviceSynchronize() != hipSuccess) return TT_EHIP;
+  release_workspace();
+  size_t bytes = layout(want, nullptr, nullptr);
+  void* p = nullptr;
+  if (hipMalloc(&p, bytes) != hipSuccess) {
+    (void)hipGetLastError();
+    return TT_ENOMEM;
+  }
+  g.d_ws = p;
+  g.ws_n = want;
+  layout(want, (char*)p, &g.w);
+  return TT_OK;
+}
+
+template <class T>
+int upload(T** dst, const std::vector<T>& src) {
+  void* p = nullptr;
+  if (hipMalloc(&p, src.size() * sizeof(T)) != hipSuccess) {
+    (void)hipGetLastError();
+    return TT_ENOMEM;
+  }
+  if (hipMemcpy(p, src.data(), src.size() * sizeof(T), hipMemcpyHostToDevice) != hipSuccess) {
+    (void)hipFree(p);
+    return TT_EHIP;
+  }
+  *dst = (T*)p;
+  return TT_OK;
+}
+
+int check_stream_state() {
+  if (!g.loaded) return TT_ENOTLOADED;
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev != g.device) return TT_EINVAL;
+  return TT_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int tt_load_bpe(const int32_t* merges, const int32_t* ranks, int64_t n_merges, int32_t pattern_id) {
+  std::lock_guard<std::mutex> lock(g_mu);
+  if (pattern_id != TT_PATTERN_GPT2 && pattern_id != TT_PATTERN_CL100K) return TT_EINVAL;
+  if (n_merges < 0 || n_merges > TT_MAX_MERGES) return TT_EINVAL;
+  if (n_merges > 0 && !merges) return TT_EINVAL;
+  const size_t M = (size_t)n_merges;
+
+  // merge of rank r: (x, y) -> 256 + r
+  std::vector<uint32_t> mx(M), my(M);
+  std::vector<char> seen(M, 0);
+  for (size_t k = 0; k < M; ++k) {
+    int64_t r = ranks ? ranks[k] : (int64_t)k;
+    if (r < 0 || r >= n_merges || seen[r]) return TT_ETABLE;
+    seen[r] = 1;
+    mx[r] = (uint32_t)merges[2 * k];
+    my[r] = (uint32_t)merges[2 * k + 1];
+  }
+  std::unordered_map<uint64_t, uint32_t> rank;
+  rank.reserve(M * 2 + 1);
+  for (size_t r = 0; r < M; ++r) {
+    if ((int64_t)(int32_t)mx[r] < 0 || (int64_t)(int32_t)my[r] < 0 || mx[r] >= 256 + r || my[r] >= 256 + r)
+      return TT_ETABLE;
+    if (!rank.emplace(pair_key(mx[r], my[r]), (uint32_t)r).second) return TT_ETABLE;
+  }
+
+  // byte-pair table
+  std::vector<uint32_t> byte_pair(65536, RANK_NONE);
+  for (size_t r = 0; r < M; ++r)
+    if (mx[r] < 256 && my[r] < 256) byte_pair[(mx[r] << 8) | my[r]] = (uint32_t)r;
+
+  // pair-rank hash: buckets of PAIR_SLOTS entries, load factor <= 1/2
+  const uint64_t pair_nb = std::max<uint64_t>(next_pow2((M + 1) / 2), 1024);
+  const int pair_shift = 64 - log2_u64(pair_nb);
+  std::vector<uint64_t> pair_tab(pair_nb * PAIR_SLOTS, PAIR_EMPTY);
+  int pair_probe = 1;
+  for (size_t r = 0; r < M; ++r) {
+    uint64_t key = pair_key(mx[r], my[r]);
+    uint32_t b = pair_bucket(key, pair_shift);
+    for (int visited = 1;; ++visited, b = (uint32_t)((b + 1) & (pair_nb - 1))) {
+      uint64_t* bucket = &pair_tab[(size_t)b * PAIR_SLOTS];
+      int slot = -1;
+      for (int s = 0; s < PAIR_SLOTS; ++s)
+        if (bucket[s] == PAIR_EMPTY) { slot = s; break; }
+      if (slot >= 0) {
+        bucket[slot] = (key << ID_BITS) | r;
+        pair_probe = std::max(pair_probe, visited);
+        break;
+      }
+    }
+  }
+
+  // whole-pre-token table: token t of 2..16 bytes whose own BPE is [t]
+  std::vector<std::vector<uint8_t>> tok(256 + M);
+  for (int b = 0; b < 256; ++b) tok[b] = {(uint8_t)b};
+  for (size_t r = 0; r < M; ++r) {
+    tok[256 + r] = tok[mx[r]];
+    tok[256 + r].insert(tok[256 + r].end(), tok[my[r]].begin(), tok[my[r]].end());
+  }
+  std::vector<uint32_t> single;
+  for (size_t r = 0; r < M; ++r) {
+    const auto& bs = tok[256 + r];
+    if (bs.size() < 2 || bs.size() > (size_t)CACHE_MAXLEN) continue;
+    std::vector<uint32_t> ids(bs.begin(), bs.end());
+    std::vector<uint32_t> out = host_bpe(ids, rank);
+    if (out.size() == 1 && out[0] == 256u + r) single.push_back((uint32_t)(256 + r));
+  }
+  const uint64_t cache_n = std::max<uint64_t>(next_pow2(single.size() * 2 + 1), 1024);
+  const int cache_shift = 64 - log2_u64(cache_n);
+  std::vector<CacheEntry> cache(cache_n);
+  std::memset(cache.data(), 0, cache.size() * sizeof(CacheEntry));
+  int cache_probe = 1;
+  for (uint32_t t : single) {
+    const auto& bs = tok[t];
+    uint64_t w0 = 0, w1 = 0;
+    for (size_t k = 0; k < bs.size(); ++k) {
+      if (k < 8) w0 |= (uint64_t)bs[k] << (8 * k);
+      else w1 |= (uint64_t)bs[k] << (8 * (k - 8));
+    }
+    uint32_t h = cache_hash(w0, w1, (uint32_t)bs.size(), cache_shift);
+    for (int visited = 1;; ++visited, h = (uint32_t)((h + 1) & (cache_n - 1))) {
+      if (cache[h].meta == 0) {
+        cache[h].w0 = w0;
+        cache[h].w1 = w1;
+        cache[h].meta = (t << 5) | (uint32_t)bs.size();
+        cache_probe = std::max(cache_probe, visited);
+        break;
+      }
+    }
+  }
+
+  if (hipDeviceSynchronize() != hipSuccess) return TT_EHIP;
+  release_tables();
+  int rc;
+  if ((rc = upload(&g.d_byte_pair, byte_pair)) != TT_OK || (rc = upload(&g.d_pair, pair_tab)) != TT_OK ||
+      (rc = upload(&g.d_cache, cache)) != TT_OK) {
+    release_tables();
+    return rc;
+  }
+  if (hipGetDevice(&g.device) != hipSuccess) {
+    release_tables();
+    return TT_EHIP;
+  }
+  g.pattern = pattern_id;
+  g.n_merges = n_merges;
+  g.tb.byte_pair = g.d_byte_pair;
+  g.tb.pair_tab = g.d_pair;
+  g.tb.cache = g.d_cache;
+  g.tb.pair_mask = (uint32_t)(pair_nb - 1);
+  g.tb.pair_shift = pair_shift;
+  g.tb.pair_probe = pair_probe;
+  g.tb.cache_mask = (uint32_t)(cache_n - 1);
+  g.tb.cache_shift = cache_shift;
+  g.tb.cache_probe = cache_probe;
+  g.tb.pattern = pattern_id;
+  g.loaded = true;
+  return TT_OK;
+}
+
+int tt_reserve(int64_t max_bytes, int32_t max_seqs) {
+  std::lock_guard<std::mutex> lock(g_mu);
+  if (max_bytes < 0 || max_seqs < 0) return TT_EINVAL;
+  if (max_bytes >= TT_MAX_BYTES) return TT_ETOOBIG;
+  int rc = check_stream_state();
+  if (rc != TT_OK) return rc;
+  return ensure_workspace(max_bytes);
+}
+
+int tt_encode(const uint8_t* dev_bytes, int64_t n, int32_t* out_ids, int64_t* out_n, hipStream_t stream) {
+  std::lock_guard<std::mutex> lock(g_mu);
+  if (n < 0 || !out_n || (n > 0 && (!dev_bytes || !out_ids))) return TT_EINVAL;
+  if (n >= TT_MAX_BYTES) return TT_ETOOBIG;
+  int rc = check_stream_state();
+  if (rc != TT_OK) return rc;
+  if (n == 0) return launch_write_zeros(out_n, 1, stream) == hipSuccess ? TT_OK : TT_EHIP;
+  if ((rc = ensure_workspace(n)) != TT_OK) return rc;
+  if (launch_pretokenize(dev_bytes, n, nullptr, 1, g.pattern, g.w, g.w.piece_start, stream) != hipSuccess ||
+      launch_bpe_emit(dev_bytes, n, g.tb, g.w, out_ids, stream) != hipSuccess ||
+      launch_finish_count(g.w, CTR_T, out_n, stream) != hipSuccess)
+    return TT_EHIP;
+  return TT_OK;
+}
+
+int tt_encode_batch(const uint8_t* dev_bytes, int64_t n, const int64_t* dev_offsets, int32_t n_seqs,
+                    int32_t* out_ids, int64_t* out_offsets, hipStream_t stream) {
+  std::lock_guard<std::mutex> lock(g_mu);
+  if (n < 0 || n_seqs < 1 || !dev_offsets || !out_offsets || (n > 0 && (!dev_bytes || !out_ids)))
+    return TT_EINVAL;
+  if (n >= TT_MAX_BYTES || n_seqs >= (int64_t)1 << 30) return TT_ETOOBIG;
+  int rc = check_stream_state();
+  if (rc != TT_OK) return rc;
+  if ((rc = ensure_workspace(n)) != TT_OK) return rc;
+  if (n == 0) {
+    if (launch_zero_counters(g.w, stream) != hipSuccess ||
+        launch_check_offsets(dev_offsets, n_seqs, n, g.w, stream) != hipSuccess ||
+        launch_write_zeros(out_offsets, n_seqs, stream) != hipSuccess ||
+        launch_finish_count(g.w, CTR_T, out_offsets + n_seqs, stream) != hipSuccess)
+      return TT_EHIP;
+    return TT_OK;
+  }
+  if (launch_pretokenize(dev_bytes, n, dev_offsets, n_seqs, g.pattern, g.w, g.w.piece_start, stream) != hipSuccess ||
+      launch_bpe_emit(dev_bytes, n, g.tb, g.w, out_ids, stream) != hipSuccess ||
+      launch_batch_offsets(dev_offsets, n_seqs, n, g.w, out_offsets, stream) != hipSuccess)
+    return TT_EHIP;
+  return TT_OK;
+}
+
+int tt_pretokenize(const uint8_t* dev_bytes, int64_t n, const int64_t* dev_offsets, int32_t n_seqs,
+                   int32_t* out_starts, int64_t* out_np, hipStream_t stream) {
+  std::lock_guard<std::mutex> lock(g_mu);
+  if (n < 0 || !out_starts || !out_np || (n > 0 && !dev_bytes) || (dev_offsets && n_seqs < 1)) return TT_EINVAL;
+  if (n >= TT_MAX_BYTES || n_seqs >= (int64_t)1 << 30) return TT_ETOOBIG;
+  int rc = check_stream_state();
+  if (rc != TT_OK) return rc;
+  if ((rc = ensure_workspace(n)) != TT_OK) return rc;
+  const int nseq = dev_offsets ? n_seqs : 1;
+  if (n == 0) {
+    if (launch_zero_counters(g.w, stream) != hipSuccess ||
+        (dev_offsets && launch_check_offsets(dev_offsets, nseq, n, g.w, stream) != hipSuccess) ||
+        launch_write_zero_i32(out_starts, stream) != hipSuccess ||
+        launch_finish_count(g.w, CTR_P, out_np, stream) != hipSuccess)
+      return TT_EHIP;
+    return TT_OK;
+  }
+  if (launch_pretokenize(dev_bytes, n, dev_offsets, nseq, g.pattern, g.w, out_starts, stream) != hipSuccess ||
+      launch_finish_count(g.w, CTR_P, out_np, stream) != hipSuccess)
+    return TT_EHIP;
+  return TT_OK;
+}
+
+int tt_char_class(uint32_t cp) {
+  if (cp > 0x10FFFF || (cp >= 0xD800 && cp <= 0xDFFF)) return -1;
+  uint32_t hi = cp >> 8;
+  if (hi >= (uint32_t)TT_UNI_L1_SIZE) return 0;
+  uint32_t byte = h_uni_l2[h_uni_l1[hi] * 64u + ((cp & 255u) >> 2)];
+  return (int)((byte >> ((cp & 3u) * 2u)) & 3u);
+}
+
+void tt_free(void) {
+  std::lock_guard<std::mutex> lock(g_mu);
+  (void)hipDeviceSynchronize();
+  release_workspace();
+  release_tables();
+}
+
+const char* tt_strerror(int code) {
+  switch (code) {
+    case TT_OK: return "ok";
+    case TT_EINVAL: return "invalid argument";
+    case TT_ETABLE: return "invalid merge table";
+    case TT_ENOMEM: return "out of memory";
+    case TT_EHIP: return "HIP runtime error";
+    case TT_EUTF8: return "input is not valid UTF-8";
+    case TT_ENOTLOADED: return "no tokenizer loaded";
+    case TT_EOFFSETS: return "invalid batch offsets";
+    case TT_ETOOBIG: return "size beyond library limits";
+    default: return "unknown error";
+  }
+}
+
+}  // extern "C"

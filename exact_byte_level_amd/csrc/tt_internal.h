@@ -1,0 +1,109 @@
+// tt_internal.h -- layouts shared by the host table builder and the kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace tt {
+
+// ---------------------------------------------------------------- pre-tokenizer
+constexpr int TILE = 4096;              // bytes per pre-tokenizer workgroup
+constexpr int PT_THREADS = 256;         // threads per pre-tokenizer workgroup
+constexpr int PT_CHUNK = TILE / PT_THREADS;  // 16 contiguous bytes per thread
+constexpr int HALO = 16;                // context bytes kept on each side of a tile
+constexpr int SPAN = TILE + 2 * HALO;   // decoded positions per tile
+constexpr int BMAP_WORDS = (SPAN + 8 + 31) / 32;  // sequence-boundary bitmap
+
+// Char classes of the run decomposition.  WS = whitespace other than CR/LF,
+// WN = CR or LF.  CONT marks a UTF-8 continuation byte, OUT a position
+// outside the text.  NONE stands for "no char" (text or sequence edge).
+enum : uint32_t { C_NONE = 0, C_L = 1, C_N = 2, C_O = 3, C_WS = 4, C_WN = 5, C_CONT = 6, C_OUT = 7 };
+
+// Per-position code (uint16 in LDS):
+//   bits 0-2 class, bit 3 first char of its sequence, bit 4 last char of its
+//   sequence, bits 5-8 contraction letter (1..8 = s t r e v m l d, case
+//   folded), bit 9 ASCII upper case, bit 10 U+0020, bit 11 apostrophe,
+//   bit 12 invalid UTF-8 here, bits 13-14 byte length - 1.
+constexpr uint32_t K_SEQ_START = 1u << 3;
+constexpr uint32_t K_SEQ_LAST = 1u << 4;
+constexpr int K_LETTER_SHIFT = 5;
+constexpr uint32_t K_UPPER = 1u << 9;
+constexpr uint32_t K_SP = 1u << 10;
+constexpr uint32_t K_AP = 1u << 11;
+constexpr uint32_t K_BAD = 1u << 12;
+constexpr int K_LEN_SHIFT = 13;
+enum : uint32_t { LT_S = 1, LT_T = 2, LT_R = 3, LT_E = 4, LT_V = 5, LT_M = 6, LT_L = 7, LT_D = 8 };
+
+// ------------------------------------------------------------------------- BPE
+constexpr uint32_t RANK_NONE = 0xFFFFFFFFu;
+constexpr uint64_t PAIR_EMPTY = ~0ull;
+constexpr int ID_BITS = 20;             // token ids < 2^20
+constexpr uint32_t ID_MASK = (1u << ID_BITS) - 1;
+constexpr int PAIR_SLOTS = 4;           // 32-byte buckets of four 8-byte entries
+
+// Pair-rank hash entry: (left << 40) | (right << 20) | rank.
+__host__ __device__ inline uint64_t pair_key(uint32_t x, uint32_t y) {
+  return ((uint64_t)x << ID_BITS) | (uint64_t)y;
+}
+__host__ __device__ inline uint32_t pair_bucket(uint64_t key, int shift) {
+  return (uint32_t)((key * 0x9E3779B97F4A7C15ull) >> shift);
+}
+
+// Whole-pre-token cache entry (32 bytes): the piece bytes zero-padded into
+// w0/w1 (little endian), meta = (id << 5) | len, len in 2..16; meta 0 = empty.
+constexpr int CACHE_MAXLEN = 16;
+struct alignas(32) CacheEntry {
+  uint64_t w0, w1;
+  uint32_t meta, pad0;
+  uint64_t pad1;
+};
+__host__ __device__ inline uint32_t cache_hash(uint64_t w0, uint64_t w1, uint32_t len, int shift) {
+  uint64_t h = (w0 ^ (uint64_t)len * 0xD6E8FEB86659FD93ull) * 0x9E3779B97F4A7C15ull;
+  h ^= h >> 29;
+  h = (h ^ w1) * 0xBF58476D1CE4E5B9ull;
+  h ^= h >> 31;
+  return (uint32_t)((h * 0x94D049BB133111EBull) >> shift);
+}
+
+// Device-resident tables of the loaded tokenizer (passed by value).
+struct Tables {
+  const uint32_t* byte_pair;    // [65536] rank of (x, y), x, y < 256, or RANK_NONE
+  const uint64_t* pair_tab;     // [pair_nb * PAIR_SLOTS]
+  const CacheEntry* cache;      // [cache_n]
+  uint32_t pair_mask;           // pair_nb - 1
+  int pair_shift;               // 64 - log2(pair_nb)
+  int pair_probe;               // max buckets visited by any key
+  uint32_t cache_mask;          // cache_n - 1
+  int cache_shift;              // 64 - log2(cache_n)
+  int cache_probe;              // max slots visited by any key
+  int pattern;
+};
+
+// Device workspace of one encode.
+enum : int { CTR_P = 0, CTR_NLONG = 1, CTR_ERR = 2, CTR_LONG_TICKET = 3, CTR_T = 4, CTR_NHUGE = 5, CTR_COUNT = 8 };
+enum : uint32_t { ERR_UTF8 = 1u, ERR_OFFSETS = 2u };
+
+struct Work {
+  uint32_t* tile_fwd;    // [ntiles] forward run summary of each tile
+  uint32_t* tile_bwd;    // [ntiles] backward run summary
+  uint32_t* tile_cnt;    // [ntiles] pre-token starts in each tile
+  uint16_t* flags;       // [ntiles * PT_THREADS] start bits of 16 bytes each
+  int32_t* piece_start;  // [n + 1]
+  int32_t* piece_cnt;    // [n] tokens of each piece
+  int32_t* tmp_ids;      // [n] tokens of the piece starting at byte s live at [s, s + cnt)
+  uint32_t* tmp_rank;    // [n] pair ranks for the cooperative merge loop
+  int32_t* tok_off;      // [n + 1] exclusive prefix of piece_cnt
+  uint32_t* blk_sum;     // [n / EMIT_PER_BLOCK + 1]
+  int32_t* long_list;    // [n / (LANE_CAP + 1) + 1] pieces longer than LANE_CAP bytes
+  int32_t* huge_list;    // [n / HUGE_TOKENS + 1] pieces with more than HUGE_TOKENS tokens
+  uint32_t* ctr;         // [CTR_COUNT]
+};
+
+// ------------------------------------------------------------- BPE tiers
+constexpr int LANE_CAP = 32;            // pieces up to this many bytes: one lane each
+constexpr int BPE_THREADS = 128;
+constexpr int EMIT_THREADS = 256;
+constexpr int EMIT_PER_THREAD = 16;
+constexpr int EMIT_PER_BLOCK = EMIT_THREADS * EMIT_PER_THREAD;
+constexpr int HUGE_TOKENS = 4096;       // pieces with more tokens are copied grid-wide
+
+}  // namespace tt

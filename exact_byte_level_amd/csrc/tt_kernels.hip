@@ -1,0 +1,976 @@
+// tt_kernels.hip -- HIP kernels (gfx950, wave64) of exact byte-level BPE tokenization.
+//
+// Method: TokTier (arXiv:2607.29678v1), summary page.
+//   §4.1  run decomposition: the ordered-rule regex split is reproduced in
+//         parallel from char classes, maximal same-class runs, the offset in a
+//         run, a few chars of context and run-level facts (k_tile_summary,
+//         k_pretok, k_compact);
+//   §4.2  BPE per piece, pieces independent, tiered by length: one lane per
+//         short piece (k_bpe_short), a cooperative exact merge loop for long
+//         ones (k_bpe_long); the whole-piece lookup of single-token pieces is
+//         the exact form of the vocabulary short-circuit the page mentions;
+//   §4.3  no host synchronisation between kernels: every size a kernel needs
+//         after the first is read on the device (grids are sized for the
+//         worst case and exit early), so the chain is graph-capturable.
+//
+// Hot-path data (all integer; no floating point, no MFMA):
+//   bytes   uint8[n]         caller's UTF-8 text
+//   flags   uint16 per 16 B  pre-token start bits
+//   starts  int32[P + 1]     piece byte offsets + sentinel n
+//   tmp_ids int32[n]         tokens of the piece starting at byte s at [s, s+cnt)
+//   out_ids int32[T]         caller's output
+#include "tt_kernels.h"
+#include "unicode_table.inc"
+
+namespace tt {
+
+// ------------------------------------------------------------ Unicode classes
+
+__device__ const uint8_t g_uni_l1[TT_UNI_L1_SIZE] = {TT_UNI_L1_DATA};
+__device__ const uint8_t g_uni_l2[TT_UNI_NBLOCKS * 64] = {TT_UNI_L2_DATA};
+
+struct AsciiTab {
+  uint16_t v[128];
+};
+
+constexpr uint16_t ascii_code(int c) {
+  uint16_t code = C_O;
+  bool upper = c >= 'A' && c <= 'Z';
+  bool lower = c >= 'a' && c <= 'z';
+  if (upper || lower) {
+    int lc = c | 0x20;
+    uint16_t lt = lc == 's' ? LT_S : lc == 't' ? LT_T : lc == 'r' ? LT_R : lc == 'e' ? LT_E
+                : lc == 'v' ? LT_V : lc == 'm' ? LT_M : lc == 'l' ? LT_L : lc == 'd' ? LT_D : 0;
+    code = (uint16_t)(C_L | (lt << K_LETTER_SHIFT) | (upper ? K_UPPER : 0));
+  } else if (c >= '0' && c <= '9') {
+    code = C_N;
+  } else if (c == '\n' || c == '\r') {
+    code = C_WN;
+  } else if (c == '\t' || c == 0x0b || c == 0x0c || c == ' ') {
+    code = (uint16_t)(C_WS | (c == ' ' ? K_SP : 0));
+  } else if (c == '\'') {
+    code = (uint16_t)(C_O | K_AP);
+  }
+  return code;
+}
+
+constexpr AsciiTab make_ascii() {
+  AsciiTab t{};
+  for (int c = 0; c < 128; ++c) t.v[c] = ascii_code(c);
+  return t;
+}
+
+__device__ const AsciiTab g_ascii = make_ascii();
+
+// Wave-uniform copy of a value every lane already agrees on.  Loops that
+// contain wave collectives (shuffles, ballots) take their exit condition from
+// such a value, so the compiler keeps the loop uniform and never splits lanes
+// of one wavefront onto different paths around a collective.
+__device__ __forceinline__ uint32_t uniform(uint32_t x) { return __builtin_amdgcn_readfirstlane(x); }
+
+__device__ __forceinline__ uint32_t cls_of(uint32_t code) { return code & 7u; }
+__device__ __forceinline__ bool is_w(uint32_t k) { return k == C_WS || k == C_WN; }
+__device__ __forceinline__ bool is_char(uint32_t code) { return cls_of(code) - 1u < 5u; }
+__device__ __forceinline__ int clen(uint32_t code) { return (int)((code >> K_LEN_SHIFT) & 3u) + 1; }
+
+// Shared-memory state of one pre-tokenizer tile.
+struct TileSmem {
+  uint16_t code[SPAN];
+  uint32_t bmap[BMAP_WORDS];
+  uint8_t l1[TT_UNI_L1_SIZE];
+  uint8_t l2[TT_UNI_NBLOCKS * 64];
+  uint32_t red[8];
+  int64_t seq_lo, seq_hi;
+  uint32_t carry_fwd, carry_bwd;
+  int flag;
+};
+
+__device__ __forceinline__ bool bmap_bit(const uint32_t* bm, int j) {
+  return (bm[j >> 5] >> (j & 31)) & 1u;
+}
+
+// First index s in [0, cnt) with a[s] >= v (cnt if none).
+__device__ __forceinline__ int64_t lower_bound_i64(const int64_t* a, int64_t cnt, int64_t v) {
+  int64_t lo = 0, hi = cnt;
+  while (lo < hi) {
+    int64_t mid = (lo + hi) >> 1;
+    if (a[mid] < v) lo = mid + 1; else hi = mid;
+  }
+  return lo;
+}
+
+// Decode the char starting at tile position j (global position base + j).
+// Validates UTF-8 as strict decoding does: no overlong forms, no surrogates,
+// nothing above U+10FFFF, no truncated or stray continuation bytes, and no
+// char crossing a sequence boundary.
+__device__ __forceinline__ uint16_t decode_at(const uint8_t* __restrict__ bytes, int64_t n, int64_t base,
+                                              int j, const TileSmem& sm, bool table_in_lds) {
+  int64_t p = base + j;
+  if (p < 0 || p >= n) return (uint16_t)C_OUT;
+  uint32_t b0 = bytes[p];
+  bool start = bmap_bit(sm.bmap, j);
+  if ((b0 & 0xC0u) == 0x80u) return (uint16_t)(C_CONT | (start ? K_BAD : 0u));
+  uint32_t code;
+  int len = 1;
+  bool bad = false;
+  if (b0 < 0x80u) {
+    code = g_ascii.v[b0];
+  } else {
+    uint32_t cp = 0;
+    if (b0 >= 0xC2u && b0 <= 0xDFu) { len = 2; cp = b0 & 0x1Fu; }
+    else if (b0 >= 0xE0u && b0 <= 0xEFu) { len = 3; cp = b0 & 0x0Fu; }
+    else if (b0 >= 0xF0u && b0 <= 0xF4u) { len = 4; cp = b0 & 0x07u; }
+    else { bad = true; }
+    for (int k = 1; k < len && !bad; ++k) {
+      int64_t q = p + k;
+      if (q >= n || bmap_bit(sm.bmap, j + k)) { bad = true; break; }
+      uint32_t bk = bytes[q];
+      if ((bk & 0xC0u) != 0x80u) { bad = true; break; }
+      if (k == 1) {
+        if ((b0 == 0xE0u && bk < 0xA0u) || (b0 == 0xEDu && bk > 0x9Fu) ||
+            (b0 == 0xF0u && bk < 0x90u) || (b0 == 0xF4u && bk > 0x8Fu)) { bad = true; break; }
+      }
+      cp = (cp << 6) | (bk & 0x3Fu);
+    }
+    if (bad) {
+      len = 1;
+      code = C_O | K_BAD;
+    } else {
+      uint32_t hi = cp >> 8, u = 0;
+      if (hi < (uint32_t)TT_UNI_L1_SIZE) {
+        uint32_t blk = table_in_lds ? sm.l1[hi] : g_uni_l1[hi];
+        uint32_t idx = blk * 64u + ((cp & 255u) >> 2);
+        uint32_t byte = table_in_lds ? sm.l2[idx] : g_uni_l2[idx];
+        u = (byte >> ((cp & 3u) * 2u)) & 3u;
+      }
+      code = u == 1u ? C_L : u == 2u ? C_N : u == 3u ? C_WS : C_O;
+    }
+  }
+  // a continuation byte right after a complete char is stray
+  int64_t e = p + len;
+  bool last = e >= n || bmap_bit(sm.bmap, j + len);
+  if (!last && !bad && (bytes[e] & 0xC0u) == 0x80u) code |= K_BAD;
+  code |= (uint32_t)(len - 1) << K_LEN_SHIFT;
+  if (start) code |= K_SEQ_START;
+  if (last) code |= K_SEQ_LAST;
+  return (uint16_t)code;
+}
+
+// Stage the codes of positions [t0 - HALO, t0 + TILE + HALO) in LDS.
+// Returns true if some char starting inside the tile is invalid UTF-8.
+__device__ bool load_tile(const uint8_t* __restrict__ bytes, int64_t n, const int64_t* __restrict__ offs,
+                          int nseq, int64_t t0, TileSmem& sm) {
+  const int tid = threadIdx.x;
+  const int64_t base = t0 - HALO;
+  for (int i = tid; i < BMAP_WORDS; i += PT_THREADS) sm.bmap[i] = 0;
+  bool na = false;
+  for (int j = tid; j < SPAN; j += PT_THREADS) {
+    int64_t p = base + j;
+    if (p >= 0 && p < n && bytes[p] >= 0x80u) na = true;
+  }
+  if (tid == 0) {
+    if (offs) {
+      sm.seq_lo = lower_bound_i64(offs, (int64_t)nseq + 1, base);
+      sm.seq_hi = lower_bound_i64(offs, (int64_t)nseq + 1, base + SPAN + 8);
+    } else {
+      sm.seq_lo = 0;
+      sm.seq_hi = 0;
+    }
+  }
+  na = __syncthreads_or(na);
+  if (offs) {
+    for (int64_t s = sm.seq_lo + tid; s < sm.seq_hi; s += PT_THREADS) {
+      int64_t j = offs[s] - base;
+      if (j >= 0 && j < (int64_t)BMAP_WORDS * 32) atomicOr(&sm.bmap[j >> 5], 1u << (j & 31));
+    }
+  } else if (tid == 0 && base <= 0) {
+    int64_t j = -base;
+    if (j < (int64_t)BMAP_WORDS * 32) sm.bmap[j >> 5] |= 1u << (j & 31);
+  }
+  if (na) {
+    for (int i = tid; i < TT_UNI_L1_SIZE; i += PT_THREADS) sm.l1[i] = g_uni_l1[i];
+    for (int i = tid; i < TT_UNI_NBLOCKS * 64; i += PT_THREADS) sm.l2[i] = g_uni_l2[i];
+  }
+  __syncthreads();
+  bool bad = false;
+  for (int j = tid; j < SPAN; j += PT_THREADS) {
+    uint16_t c = decode_at(bytes, n, base, j, sm, na);
+    sm.code[j] = c;
+    if ((c & K_BAD) && j >= HALO && j < HALO + TILE) bad = true;
+  }
+  __syncthreads();
+  return bad;
+}
+
+// ---------------------------------------------------- run-state scan operators
+// Forward state of a range of chars, for the trailing run:
+//   bit 0 has chars, bit 1 open (the run reaches the range start and no
+//   sequence starts there), bits 2-4 class, bits 5-7 class of the char before
+//   the run (C_NONE at a sequence start), bits 8-9 run length mod 3.
+struct FwdOp {
+  static constexpr uint32_t IDENT = 0;
+  __device__ static __forceinline__ uint32_t elem(uint32_t code) {
+    uint32_t open = (code & K_SEQ_START) ? 0u : 2u;
+    return 1u | open | (cls_of(code) << 2) | (1u << 8);
+  }
+  __device__ static __forceinline__ uint32_t combine(uint32_t a, uint32_t b) {
+    if (!(b & 1u)) return a;
+    if (!(a & 1u)) return b;
+    if (b & 2u) {
+      uint32_t ca = (a >> 2) & 7u, cb = (b >> 2) & 7u;
+      if (ca == cb) {
+        uint32_t len = (((a >> 8) & 3u) + ((b >> 8) & 3u)) % 3u;
+        return (a & 0xFFu) | (len << 8);
+      }
+      return 1u | (cb << 2) | (ca << 5) | (b & 0x300u);
+    }
+    return b;
+  }
+};
+
+// Backward state, for the leading run: bit 0 has chars, bit 1 open (the run
+// reaches the range end and the last char does not end its sequence),
+// bits 2-4 class, bits 5-7 class of the char after the run (C_NONE at an end).
+struct BwdOp {
+  static constexpr uint32_t IDENT = 0;
+  __device__ static __forceinline__ uint32_t elem(uint32_t code) {
+    uint32_t open = (code & K_SEQ_LAST) ? 0u : 2u;
+    return 1u | open | (cls_of(code) << 2);
+  }
+  __device__ static __forceinline__ uint32_t combine(uint32_t a, uint32_t b) {
+    if (!(a & 1u)) return b;
+    if (!(b & 1u)) return a;
+    if (a & 2u) {
+      uint32_t ca = (a >> 2) & 7u, cb = (b >> 2) & 7u;
+      if (ca == cb) return 1u | (b & 2u) | (ca << 2) | (b & 0xE0u);
+      return 1u | (ca << 2) | (cb << 5);
+    }
+    return a;
+  }
+};
+
+template <class Op>
+__device__ __forceinline__ uint32_t wave_incl_fwd(uint32_t x, int lane) {
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    uint32_t o = __shfl_up(x, d);
+    if (lane >= d) x = Op::combine(o, x);
+  }
+  return x;
+}
+
+template <class Op>
+__device__ __forceinline__ uint32_t wave_incl_bwd(uint32_t x, int lane) {
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    uint32_t o = __shfl_down(x, d);
+    if (lane + d < 64) x = Op::combine(x, o);
+  }
+  return x;
+}
+
+// Exclusive ordered scan over the PT_THREADS threads of a block (left to
+// right).  *total receives the whole block's combination.
+template <class Op>
+__device__ uint32_t block_excl_fwd(uint32_t x, uint32_t* red, uint32_t* total) {
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  uint32_t inc = wave_incl_fwd<Op>(x, lane);
+  uint32_t exc = __shfl_up(inc, 1);
+  if (lane == 0) exc = Op::IDENT;
+  if (lane == 63) red[wid] = inc;
+  __syncthreads();
+  uint32_t pre = Op::IDENT, tot = Op::IDENT;
+  for (int w = 0; w < PT_THREADS / 64; ++w) {
+    if (w < wid) pre = Op::combine(pre, red[w]);
+    tot = Op::combine(tot, red[w]);
+  }
+  *total = tot;
+  __syncthreads();
+  return Op::combine(pre, exc);
+}
+
+// Exclusive ordered scan right to left.
+template <class Op>
+__device__ uint32_t block_excl_bwd(uint32_t x, uint32_t* red, uint32_t* total) {
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  uint32_t inc = wave_incl_bwd<Op>(x, lane);
+  uint32_t exc = __shfl_down(inc, 1);
+  if (lane == 63) exc = Op::IDENT;
+  if (lane == 0) red[wid] = inc;
+  __syncthreads();
+  uint32_t post = Op::IDENT, tot = Op::IDENT;
+  for (int w = PT_THREADS / 64 - 1; w >= 0; --w) {
+    if (w > wid) post = Op::combine(red[w], post);
+    tot = Op::combine(red[w], tot);
+  }
+  *total = tot;
+  __syncthreads();
+  return Op::combine(exc, post);
+}
+
+__device__ __forceinline__ uint32_t block_sum(uint32_t x, uint32_t* red) {
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) x += __shfl_xor(x, d);
+  if (lane == 0) red[wid] = x;
+  __syncthreads();
+  uint32_t t = 0;
+  for (int w = 0; w < (int)(blockDim.x >> 6); ++w) t += red[w];
+  __syncthreads();
+  return t;
+}
+
+// Exclusive prefix sum over the block; *total receives the block sum.
+__device__ __forceinline__ uint32_t block_excl_sum(uint32_t x, uint32_t* red, uint32_t* total) {
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  uint32_t inc = x;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    uint32_t o = __shfl_up(inc, d);
+    if (lane >= d) inc += o;
+  }
+  if (lane == 63) red[wid] = inc;
+  __syncthreads();
+  uint32_t pre = 0, tot = 0;
+  for (int w = 0; w < (int)(blockDim.x >> 6); ++w) {
+    if (w < wid) pre += red[w];
+    tot += red[w];
+  }
+  *total = tot;
+  __syncthreads();
+  return pre + inc - x;
+}
+
+// ---------------------------------------------------------- chunk summaries
+
+// Thread-chunk positions: tile indices [HALO + PT_CHUNK * tid, + PT_CHUNK).
+__device__ __forceinline__ uint32_t chunk_fwd(const TileSmem& sm) {
+  uint32_t s = FwdOp::IDENT;
+  const int j0 = HALO + PT_CHUNK * threadIdx.x;
+#pragma unroll
+  for (int k = 0; k < PT_CHUNK; ++k) {
+    uint32_t c = sm.code[j0 + k];
+    if (is_char(c)) s = FwdOp::combine(s, FwdOp::elem(c));
+  }
+  return s;
+}
+
+__device__ __forceinline__ uint32_t chunk_bwd(const TileSmem& sm) {
+  uint32_t s = BwdOp::IDENT;
+  const int j0 = HALO + PT_CHUNK * threadIdx.x;
+#pragma unroll
+  for (int k = PT_CHUNK - 1; k >= 0; --k) {
+    uint32_t c = sm.code[j0 + k];
+    if (is_char(c)) s = BwdOp::combine(BwdOp::elem(c), s);
+  }
+  return s;
+}
+
+// Pass 1 (cl100k-style rules only): forward and backward run summaries of
+// every tile, so that pass 2 can resolve runs that cross tiles (digit-group
+// phase, the last newline of a whitespace run, newlines absorbed after
+// punctuation) without a second look at distant bytes.
+__global__ __launch_bounds__(PT_THREADS) void k_tile_summary(const uint8_t* __restrict__ bytes, int64_t n,
+                                                             const int64_t* __restrict__ offs, int nseq,
+                                                             Work w) {
+  __shared__ TileSmem sm;
+  const int64_t t0 = (int64_t)blockIdx.x * TILE;
+  load_tile(bytes, n, offs, nseq, t0, sm);
+  uint32_t tf, tb;
+  block_excl_fwd<FwdOp>(chunk_fwd(sm), sm.red, &tf);
+  block_excl_bwd<BwdOp>(chunk_bwd(sm), sm.red, &tb);
+  if (threadIdx.x == 0) {
+    w.tile_fwd[blockIdx.x] = tf;
+    w.tile_bwd[blockIdx.x] = tb;
+  }
+}
+
+// Combine the summaries of all tiles left of `t` (wave 0) / right of `t`
+// (wave 1), 64 tiles per step, stopping once the run is closed.
+__device__ void tile_carries(const Work& w, int t, int ntiles, TileSmem& sm) {
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  if (wid == 0) {
+    uint32_t acc = FwdOp::IDENT;
+    for (int b = t - 1; b >= 0; b -= 64) {
+      int j = b - lane;
+      uint32_t v = j >= 0 ? w.tile_fwd[j] : FwdOp::IDENT;
+#pragma unroll
+      for (int d = 1; d < 64; d <<= 1) {
+        uint32_t o = __shfl_down(v, d);
+        if (lane + d < 64) v = FwdOp::combine(o, v);
+      }
+      v = __shfl(v, 0);
+      acc = uniform(FwdOp::combine(v, acc));
+      if ((acc & 1u) && !(acc & 2u)) break;
+    }
+    if (lane == 0) sm.carry_fwd = acc;
+  } else if (wid == 1) {
+    uint32_t acc = BwdOp::IDENT;
+    for (int b = t + 1; b < ntiles; b += 64) {
+      int j = b + lane;
+      uint32_t v = j < ntiles ? w.tile_bwd[j] : BwdOp::IDENT;
+#pragma unroll
+      for (int d = 1; d < 64; d <<= 1) {
+        uint32_t o = __shfl_down(v, d);
+        if (lane + d < 64) v = BwdOp::combine(v, o);
+      }
+      v = __shfl(v, 0);
+      acc = uniform(BwdOp::combine(acc, v));
+      if ((acc & 1u) && !(acc & 2u)) break;
+    }
+    if (lane == 0) sm.carry_bwd = acc;
+  }
+  __syncthreads();
+}
+
+// --------------------------------------------------------- boundary predicate
+
+// Previous char start before tile position j, or -1 at a sequence start.
+__device__ __forceinline__ int prev_char(const uint16_t* c, int j) {
+  if (c[j] & K_SEQ_START) return -1;
+  int k = j - 1;
+  while (k > 0 && cls_of(c[k]) == C_CONT && k > j - 4) --k;
+  return k;
+}
+
+// The apostrophe at q starts a piece: it is a one-char "other" run that no
+// space in front of it absorbs.
+__device__ __forceinline__ bool ap_starts_piece(const uint16_t* c, int q) {
+  uint32_t cq = c[q];
+  if (!(cq & K_AP)) return false;
+  if (cq & K_SEQ_START) return true;
+  uint32_t cr = c[prev_char(c, q)];
+  return cls_of(cr) != C_O && !(cr & K_SP);
+}
+
+// Length (1 or 2) of a contraction suffix whose first letter is at a, or 0.
+template <int PAT>
+__device__ __forceinline__ int contraction_len(const uint16_t* c, int a) {
+  uint32_t ca = c[a];
+  if (ca & K_SEQ_START) return 0;
+  if (!ap_starts_piece(c, prev_char(c, a))) return 0;
+  if (PAT == 0 && (ca & K_UPPER)) return 0;
+  uint32_t lt = (ca >> K_LETTER_SHIFT) & 15u;
+  if (lt == LT_S || lt == LT_T || lt == LT_M || lt == LT_D) return 1;
+  if ((lt == LT_R || lt == LT_V || lt == LT_L) && !(ca & K_SEQ_LAST)) {
+    uint32_t c2 = c[a + 1];
+    if (PAT == 0 && (c2 & K_UPPER)) return 0;
+    uint32_t l2 = (c2 >> K_LETTER_SHIFT) & 15u;
+    if ((lt == LT_R && l2 == LT_E) || (lt == LT_V && l2 == LT_E) || (lt == LT_L && l2 == LT_L)) return 2;
+  }
+  return 0;
+}
+
+// Letter at j is the first letter after a contraction suffix.
+template <int PAT>
+__device__ __forceinline__ bool after_contraction(const uint16_t* c, int j) {
+  int a = prev_char(c, j);
+  if (a < 0) return false;
+  if (contraction_len<PAT>(c, a) == 1) return true;
+  int a2 = prev_char(c, a);
+  return a2 >= 0 && contraction_len<PAT>(c, a2) == 2;
+}
+
+__device__ __forceinline__ bool pred_gpt2(const uint16_t* c, int j) {
+  uint32_t c0 = c[j];
+  if (c0 & K_SEQ_START) return true;
+  uint32_t k0 = cls_of(c0);
+  int p1 = prev_char(c, j);
+  uint32_t c1 = c[p1], k1 = cls_of(c1);
+  if (is_w(k0)) {
+    if (!is_w(k1)) return true;
+    if (c0 & K_SEQ_LAST) return false;
+    return !is_w(cls_of(c[j + clen(c0)]));
+  }
+  if (k1 == k0) return k0 == C_L && after_contraction<0>(c, j);
+  if (c1 & K_SP) return false;
+  if (k0 == C_L && contraction_len<0>(c, j) > 0) return false;
+  return true;
+}
+
+// fwd_prev: forward run state at the previous char; fwd_here: at this char;
+// ends_run: the whitespace run through this char is followed by no CR/LF.
+__device__ __forceinline__ bool pred_cl100k(const uint16_t* c, int j, uint32_t fwd_prev, uint32_t fwd_here,
+                                            bool ends_run) {
+  uint32_t c0 = c[j];
+  if (c0 & K_SEQ_START) return true;
+  uint32_t k0 = cls_of(c0);
+  int p1 = prev_char(c, j);
+  uint32_t c1 = c[p1], k1 = cls_of(c1);
+  switch (k0) {
+    case C_N:
+      return k1 != C_N || ((fwd_here >> 8) & 3u) == 1u;
+    case C_L:
+      if (k1 == C_L) return after_contraction<1>(c, j);
+      if (k1 == C_WS) return false;
+      if (k1 == C_O) {
+        if (c1 & K_SEQ_START) return false;
+        uint32_t c2 = c[prev_char(c, p1)];
+        return !(cls_of(c2) != C_O && !(c2 & K_SP));
+      }
+      return true;
+    case C_O:
+      if (k1 == C_O) return false;
+      return !(c1 & K_SP);
+    case C_WN:
+      if (is_w(k1)) return false;
+      return k1 != C_O;
+    case C_WS:
+      if (!is_w(k1)) return true;
+      if (k1 == C_WN) return ends_run || ((fwd_prev >> 5) & 7u) == C_O;
+      if (c0 & K_SEQ_LAST) return false;
+      return !is_w(cls_of(c[j + clen(c0)]));
+  }
+  return false;
+}
+
+// Pass 2: pre-token start bits of every byte of a tile, and the tile count.
+template <int PAT>
+__global__ __launch_bounds__(PT_THREADS) void k_pretok(const uint8_t* __restrict__ bytes, int64_t n,
+                                                       const int64_t* __restrict__ offs, int nseq, int ntiles,
+                                                       Work w) {
+  __shared__ TileSmem sm;
+  const int t = blockIdx.x;
+  const int64_t t0 = (int64_t)t * TILE;
+  bool bad = load_tile(bytes, n, offs, nseq, t0, sm);
+  if (bad) atomicOr(&w.ctr[CTR_ERR], ERR_UTF8);
+  const int j0 = HALO + PT_CHUNK * threadIdx.x;
+  uint32_t bits = 0;
+  if (PAT == 0) {
+#pragma unroll
+    for (int k = 0; k < PT_CHUNK; ++k) {
+      uint32_t c = sm.code[j0 + k];
+      if (is_char(c) && pred_gpt2(sm.code, j0 + k)) bits |= 1u << k;
+    }
+  } else {
+    tile_carries(w, t, ntiles, sm);
+    uint32_t tot;
+    uint32_t sb = BwdOp::combine(block_excl_bwd<BwdOp>(chunk_bwd(sm), sm.red, &tot), sm.carry_bwd);
+    uint32_t ends = 0;
+#pragma unroll
+    for (int k = PT_CHUNK - 1; k >= 0; --k) {
+      uint32_t c = sm.code[j0 + k];
+      if (is_char(c)) {
+        sb = BwdOp::combine(BwdOp::elem(c), sb);
+        if (((sb >> 5) & 7u) != C_WN) ends |= 1u << k;
+      }
+    }
+    uint32_t sf = FwdOp::combine(sm.carry_fwd, block_excl_fwd<FwdOp>(chunk_fwd(sm), sm.red, &tot));
+#pragma unroll
+    for (int k = 0; k < PT_CHUNK; ++k) {
+      uint32_t c = sm.code[j0 + k];
+      if (is_char(c)) {
+        uint32_t before = sf;
+        sf = FwdOp::combine(sf, FwdOp::elem(c));
+        if (pred_cl100k(sm.code, j0 + k, before, sf, (ends >> k) & 1u)) bits |= 1u << k;
+      }
+    }
+  }
+  w.flags[(int64_t)t * PT_THREADS + threadIdx.x] = (uint16_t)bits;
+  uint32_t cnt = block_sum(__popc(bits), sm.red);
+  if (threadIdx.x == 0) w.tile_cnt[t] = cnt;
+}
+
+// Pass 3: piece starts in order, by prefix sums of the start bits.
+__global__ __launch_bounds__(PT_THREADS) void k_compact(Work w, int ntiles, int64_t n, int32_t* __restrict__ starts) {
+  __shared__ uint32_t red[8];
+  const int t = blockIdx.x;
+  uint32_t s = 0;
+  for (int i = threadIdx.x; i < t; i += PT_THREADS) s += w.tile_cnt[i];
+  uint32_t base = block_sum(s, red);
+  uint32_t bits = w.flags[(int64_t)t * PT_THREADS + threadIdx.x];
+  uint32_t tot;
+  uint32_t pos = base + block_excl_sum(__popc(bits), red, &tot);
+  const int64_t p0 = (int64_t)t * TILE + (int64_t)PT_CHUNK * threadIdx.x;
+  while (bits) {
+    int k = __ffs(bits) - 1;
+    bits &= bits - 1;
+    starts[pos++] = (int32_t)(p0 + k);
+  }
+  if (t == ntiles - 1 && threadIdx.x == 0) {
+    starts[base + tot] = (int32_t)n;
+    w.ctr[CTR_P] = base + tot;
+  }
+}
+
+// ----------------------------------------------------------------------- BPE
+
+// Rank of merging the adjacent pair (x, y), or RANK_NONE.
+__device__ __forceinline__ uint32_t pair_rank(const Tables& tb, uint32_t x, uint32_t y) {
+  if ((x | y) < 256u) return tb.byte_pair[(x << 8) | y];
+  const uint64_t key = pair_key(x, y);
+  uint32_t b = pair_bucket(key, tb.pair_shift);
+  for (int i = 0; i < tb.pair_probe; ++i) {
+    const ulonglong2* bp = reinterpret_cast<const ulonglong2*>(tb.pair_tab + (size_t)b * PAIR_SLOTS);
+    ulonglong2 e0 = bp[0], e1 = bp[1];
+    if ((e0.x >> ID_BITS) == key) return (uint32_t)(e0.x & ID_MASK);
+    if ((e0.y >> ID_BITS) == key) return (uint32_t)(e0.y & ID_MASK);
+    if ((e1.x >> ID_BITS) == key) return (uint32_t)(e1.x & ID_MASK);
+    if ((e1.y >> ID_BITS) == key) return (uint32_t)(e1.y & ID_MASK);
+    if (e1.y == PAIR_EMPTY) return RANK_NONE;
+    b = (b + 1) & tb.pair_mask;
+  }
+  return RANK_NONE;
+}
+
+// Id of the single-token piece with these bytes (len 2..16), or RANK_NONE.
+__device__ __forceinline__ uint32_t cache_lookup(const Tables& tb, uint64_t w0, uint64_t w1, uint32_t len) {
+  uint32_t h = cache_hash(w0, w1, len, tb.cache_shift);
+  for (int i = 0; i < tb.cache_probe; ++i) {
+    const CacheEntry* e = tb.cache + h;
+    ulonglong2 a = *reinterpret_cast<const ulonglong2*>(e);
+    uint32_t meta = e->meta;
+    if (meta == 0) return RANK_NONE;
+    if ((meta & 31u) == len && a.x == w0 && a.y == w1) return meta >> 5;
+    h = (h + 1) & tb.cache_mask;
+  }
+  return RANK_NONE;
+}
+
+// Classic lowest-rank-first loop on one lane's piece held in LDS (element k
+// at I[k * BPE_THREADS]).  Returns the token count; tokens in I[0..count).
+__device__ int lane_bpe(uint32_t* I, uint32_t* R, int m, const Tables& tb) {
+  constexpr int S = BPE_THREADS;
+  for (int k = 0; k + 1 < m; ++k) R[k * S] = tb.byte_pair[(I[k * S] << 8) | I[(k + 1) * S]];
+  while (m > 1) {
+    uint32_t best = RANK_NONE;
+    int bk = -1;
+    for (int k = 0; k + 1 < m; ++k) {
+      uint32_t r = R[k * S];
+      if (r < best) { best = r; bk = k; }
+    }
+    if (bk < 0) break;
+    const uint32_t nid = 256u + best;
+    I[bk * S] = nid;
+    for (int k = bk + 1; k + 1 < m; ++k) I[k * S] = I[(k + 1) * S];
+    for (int k = bk + 1; k + 2 < m; ++k) R[k * S] = R[(k + 1) * S];
+    --m;
+    uint32_t rl = RANK_NONE, rr = RANK_NONE;
+    if (bk > 0) rl = pair_rank(tb, I[(bk - 1) * S], nid);
+    if (bk + 1 < m) rr = pair_rank(tb, nid, I[(bk + 1) * S]);
+    if (bk > 0) R[(bk - 1) * S] = rl;
+    if (bk + 1 < m) R[bk * S] = rr;
+  }
+  return m;
+}
+
+// Short pieces (<= LANE_CAP bytes): one lane each; whole-piece lookup first.
+// Longer pieces are queued for k_bpe_long.
+__global__ __launch_bounds__(BPE_THREADS) void k_bpe_short(const uint8_t* __restrict__ bytes, Work w,
+                                                           Tables tb) {
+  __shared__ uint32_t s_ids[LANE_CAP * BPE_THREADS];
+  __shared__ uint32_t s_rk[LANE_CAP * BPE_THREADS];
+  uint32_t* I = s_ids + threadIdx.x;
+  uint32_t* R = s_rk + threadIdx.x;
+  const uint32_t P = w.ctr[CTR_P];
+  for (uint32_t p = blockIdx.x * BPE_THREADS + threadIdx.x; p < P; p += gridDim.x * BPE_THREADS) {
+    const int32_t s = w.piece_start[p];
+    const int32_t len = w.piece_start[p + 1] - s;
+    if (len > LANE_CAP) {
+      uint32_t idx = atomicAdd(&w.ctr[CTR_NLONG], 1u);
+      w.long_list[idx] = (int32_t)p;
+      continue;
+    }
+    int cnt = 1;
+    if (len == 1) {
+      w.tmp_ids[s] = bytes[s];
+    } else {
+      uint64_t w0 = 0, w1 = 0;
+#pragma unroll
+      for (int k = 0; k < LANE_CAP; ++k) {
+        if (k < len) {
+          uint32_t b = bytes[s + k];
+          I[k * BPE_THREADS] = b;
+          if (k < 8) w0 |= (uint64_t)b << (8 * k);
+          else if (k < 16) w1 |= (uint64_t)b << (8 * (k - 8));
+        }
+      }
+      uint32_t hit = len <= CACHE_MAXLEN ? cache_lookup(tb, w0, w1, (uint32_t)len) : RANK_NONE;
+      if (hit != RANK_NONE) {
+        w.tmp_ids[s] = (int32_t)hit;
+      } else {
+        cnt = lane_bpe(I, R, len, tb);
+        for (int k = 0; k < cnt; ++k) w.tmp_ids[s + k] = (int32_t)I[k * BPE_THREADS];
+      }
+    }
+    w.piece_cnt[p] = cnt;
+  }
+}
+
+__device__ __forceinline__ uint32_t wave_min(uint32_t x) {
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) x = min(x, (uint32_t)__shfl_xor(x, d));
+  return x;
+}
+
+// Merge starts of one 64-position chunk: ms[k] = eq[k] && !ms[k-1], ms[-1] =
+// cin.  Inside a run of equal pairs this keeps every other position, which is
+// what leftmost-first merging does (x x x x -> xx xx).  Runs of ones are
+// filled from their start with a carry trick and masked by start parity.
+__device__ __forceinline__ uint64_t alt_mask(uint64_t eq, uint64_t cin) {
+  const uint64_t E = 0x5555555555555555ull;
+  uint64_t starts = eq & ~(eq << 1);
+  uint64_t se = starts & E, so = starts & ~E;
+  if (cin && (eq & 1ull)) { se &= ~1ull; so |= 1ull; }
+  uint64_t fe = eq & ~(eq + se);
+  uint64_t fo = eq & ~(eq + so);
+  return (fe & E) | (fo & ~E);
+}
+
+// Long pieces: one wavefront per piece, exact global-minimum rounds.  Each
+// round finds the lowest rank present, merges every occurrence of that pair
+// (alternating inside runs of equal pairs), compacts in place and recomputes
+// the pair ranks.  In a consistent table a merge only creates pairs of higher
+// rank, so this equals the classic loop.  Ids and ranks live in the piece's
+// own slice of tmp_ids / tmp_rank.
+__global__ __launch_bounds__(64) void k_bpe_long(const uint8_t* __restrict__ bytes, Work w, Tables tb) {
+  const int lane = threadIdx.x;
+  const uint64_t lt_mask = (1ull << lane) - 1ull;
+  const uint32_t nlong = w.ctr[CTR_NLONG];
+  // static assignment: wavefront b takes long pieces b, b + grid, ... (the
+  // index, the piece and its length are wave-uniform)
+  for (uint32_t i = blockIdx.x; i < nlong; i += gridDim.x) {
+    const uint32_t p = uniform((uint32_t)w.long_list[i]);
+    const int32_t s = (int32_t)uniform((uint32_t)w.piece_start[p]);
+    int m = (int)uniform((uint32_t)(w.piece_start[p + 1] - s));
+    uint32_t* I = reinterpret_cast<uint32_t*>(w.tmp_ids) + s;
+    uint32_t* R = w.tmp_rank + s;
+    uint32_t rmin = RANK_NONE;
+    for (int k = lane; k < m; k += 64) {
+      uint32_t b = bytes[s + k];
+      I[k] = b;
+      if (k + 1 < m) {
+        uint32_t r = tb.byte_pair[(b << 8) | bytes[s + k + 1]];
+        R[k] = r;
+        rmin = min(rmin, r);
+      }
+    }
+    rmin = uniform(wave_min(rmin));
+    __syncthreads();
+    while (rmin != RANK_NONE) {
+      uint64_t cin = 0;
+      int out = 0;
+      for (int base = 0; base < m; base += 64) {
+        const int k = base + lane;
+        const uint32_t id = k < m ? I[k] : 0u;
+        const uint32_t r = k + 1 < m ? R[k] : RANK_NONE;
+        const uint64_t eq = __ballot(r == rmin);
+        const uint64_t ms = alt_mask(eq, cin);
+        const uint64_t valid = (m - base >= 64) ? ~0ull : ((1ull << (m - base)) - 1ull);
+        const uint64_t keep = valid & ~((ms << 1) | cin);
+        if ((keep >> lane) & 1ull) I[out + __popcll(keep & lt_mask)] = ((ms >> lane) & 1ull) ? 256u + rmin : id;
+        out += __popcll(keep);
+        cin = ms >> 63;
+      }
+      m = (int)uniform((uint32_t)out);
+      __syncthreads();
+      rmin = RANK_NONE;
+      for (int k = lane; k + 1 < m; k += 64) {
+        uint32_t r = pair_rank(tb, I[k], I[k + 1]);
+        R[k] = r;
+        rmin = min(rmin, r);
+      }
+      rmin = uniform(wave_min(rmin));
+      __syncthreads();
+    }
+    if (lane == 0) {
+      w.piece_cnt[p] = m;
+      if (m > HUGE_TOKENS) w.huge_list[atomicAdd(&w.ctr[CTR_NHUGE], 1u)] = (int32_t)p;
+    }
+  }
+}
+
+// ------------------------------------------------------------------ emission
+
+__global__ __launch_bounds__(EMIT_THREADS) void k_emit_sums(Work w) {
+  __shared__ uint32_t red[8];
+  const uint32_t P = w.ctr[CTR_P];
+  const uint32_t p0 = blockIdx.x * EMIT_PER_BLOCK;
+  if (p0 >= P) return;
+  uint32_t s = 0;
+  for (uint32_t p = p0 + threadIdx.x; p < min(P, p0 + EMIT_PER_BLOCK); p += EMIT_THREADS) s += w.piece_cnt[p];
+  s = block_sum(s, red);
+  if (threadIdx.x == 0) w.blk_sum[blockIdx.x] = s;
+}
+
+// Token offsets of every piece and the copy of each piece's tokens into the
+// output.  Pieces with more than HUGE_TOKENS tokens are copied by k_copy_huge.
+__global__ __launch_bounds__(EMIT_THREADS) void k_emit(Work w, int32_t* __restrict__ out_ids) {
+  __shared__ uint32_t red[8];
+  const uint32_t P = w.ctr[CTR_P];
+  const uint32_t p0 = blockIdx.x * EMIT_PER_BLOCK;
+  if (p0 >= P) return;
+  uint32_t s = 0;
+  for (uint32_t b = threadIdx.x; b < blockIdx.x; b += EMIT_THREADS) s += w.blk_sum[b];
+  const uint32_t base = block_sum(s, red);
+  const uint32_t q0 = p0 + threadIdx.x * EMIT_PER_THREAD;
+  uint32_t c[EMIT_PER_THREAD];
+  uint32_t mine = 0;
+#pragma unroll
+  for (int j = 0; j < EMIT_PER_THREAD; ++j) {
+    c[j] = (q0 + j < P) ? (uint32_t)w.piece_cnt[q0 + j] : 0u;
+    mine += c[j];
+  }
+  uint32_t tot;
+  uint32_t off = base + block_excl_sum(mine, red, &tot);
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int j = 0; j < EMIT_PER_THREAD; ++j) {
+    const uint32_t p = q0 + j;
+    uint32_t src = 0;
+    if (p < P) {
+      w.tok_off[p] = (int32_t)off;
+      src = (uint32_t)w.piece_start[p];
+      if (c[j] <= 16) {
+        for (uint32_t k = 0; k < c[j]; ++k) out_ids[off + k] = w.tmp_ids[src + k];
+      }
+    }
+    // medium pieces: the whole wavefront copies one piece at a time
+    uint64_t big = __ballot(p < P && c[j] > 16 && c[j] <= HUGE_TOKENS);
+    while (big) {
+      int l = __ffsll((unsigned long long)big) - 1;
+      big &= big - 1;
+      uint32_t cs = __shfl(src, l), co = __shfl(off, l), cc = __shfl(c[j], l);
+      for (uint32_t k = lane; k < cc; k += 64) out_ids[co + k] = w.tmp_ids[cs + k];
+    }
+    off += c[j];
+  }
+  if (p0 + EMIT_PER_BLOCK >= P && threadIdx.x == 0) {
+    w.tok_off[P] = (int32_t)(base + tot);
+    w.ctr[CTR_T] = base + tot;
+  }
+}
+
+// Copy of pieces with more than HUGE_TOKENS tokens (only long pieces can have
+// them); every block takes a strided share of each such piece.
+__global__ __launch_bounds__(256) void k_copy_huge(Work w, int32_t* __restrict__ out_ids) {
+  const uint32_t nhuge = w.ctr[CTR_NHUGE];
+  for (uint32_t i = 0; i < nhuge; ++i) {
+    const uint32_t p = (uint32_t)w.huge_list[i];
+    const uint32_t cc = (uint32_t)w.piece_cnt[p];
+    const uint32_t src = (uint32_t)w.piece_start[p], dst = (uint32_t)w.tok_off[p];
+    for (uint32_t k = blockIdx.x * 256 + threadIdx.x; k < cc; k += gridDim.x * 256) out_ids[dst + k] = w.tmp_ids[src + k];
+  }
+}
+
+// ------------------------------------------------------------- small kernels
+
+__global__ void k_zero(uint32_t* ctr, int cnt) {
+  if ((int)threadIdx.x < cnt) ctr[threadIdx.x] = 0;
+}
+
+__global__ void k_check_offsets(const int64_t* __restrict__ offs, int nseq, int64_t n, uint32_t* ctr) {
+  int s = blockIdx.x * blockDim.x + threadIdx.x;
+  if (s > nseq) return;
+  int64_t o = offs[s];
+  bool bad = (s == 0 && o != 0) || (s == nseq && o != n) || o < 0 || o > n || (s < nseq && offs[s + 1] < o);
+  if (bad) atomicOr(&ctr[CTR_ERR], ERR_OFFSETS);
+}
+
+__device__ __forceinline__ int64_t err_code(uint32_t e) {
+  return (e & ERR_OFFSETS) ? -7 : (e & ERR_UTF8) ? -5 : 0;
+}
+
+__global__ void k_finish_count(const uint32_t* ctr, int which, int64_t* out) {
+  uint32_t e = ctr[CTR_ERR];
+  *out = e ? err_code(e) : (int64_t)ctr[which];
+}
+
+__global__ void k_batch_offsets(const int64_t* __restrict__ offs, int nseq, int64_t n, Work w,
+                                int64_t* __restrict__ out_off) {
+  int s = blockIdx.x * blockDim.x + threadIdx.x;
+  if (s > nseq) return;
+  const uint32_t e = w.ctr[CTR_ERR];
+  const uint32_t P = w.ctr[CTR_P];
+  if (s == nseq) {
+    out_off[s] = e ? err_code(e) : (int64_t)w.ctr[CTR_T];
+    return;
+  }
+  int64_t o = offs[s];
+  o = o < 0 ? 0 : (o > n ? n : o);
+  // first piece starting at or after o
+  uint32_t lo = 0, hi = P;
+  while (lo < hi) {
+    uint32_t mid = (lo + hi) >> 1;
+    if ((int64_t)w.piece_start[mid] < o) lo = mid + 1; else hi = mid;
+  }
+  out_off[s] = (int64_t)w.tok_off[lo];
+}
+
+__global__ void k_write_zero_i64(int64_t* out, int cnt) {
+  int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < cnt) out[i] = 0;
+}
+
+__global__ void k_write_zero_i32(int32_t* out) { *out = 0; }
+
+// ---------------------------------------------------------------- launchers
+
+static inline int ceil_div(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
+
+hipError_t launch_pretokenize(const uint8_t* bytes, int64_t n, const int64_t* offs, int nseq, int pattern,
+                              const Work& w, int32_t* starts, hipStream_t st) {
+  const int ntiles = ceil_div(n, TILE);
+  hipLaunchKernelGGL(k_zero, dim3(1), dim3(64), 0, st, w.ctr, (int)CTR_COUNT);
+  if (offs) hipLaunchKernelGGL(k_check_offsets, dim3(ceil_div((int64_t)nseq + 1, 256)), dim3(256), 0, st, offs, nseq, n, w.ctr);
+  if (pattern == 1) {
+    hipLaunchKernelGGL(k_tile_summary, dim3(ntiles), dim3(PT_THREADS), 0, st, bytes, n, offs, nseq, w);
+    hipLaunchKernelGGL(k_pretok<1>, dim3(ntiles), dim3(PT_THREADS), 0, st, bytes, n, offs, nseq, ntiles, w);
+  } else {
+    hipLaunchKernelGGL(k_pretok<0>, dim3(ntiles), dim3(PT_THREADS), 0, st, bytes, n, offs, nseq, ntiles, w);
+  }
+  hipLaunchKernelGGL(k_compact, dim3(ntiles), dim3(PT_THREADS), 0, st, w, ntiles, n, starts);
+  return hipGetLastError();
+}
+
+hipError_t launch_bpe_emit(const uint8_t* bytes, int64_t n, const Tables& tb, const Work& w, int32_t* out_ids,
+                           hipStream_t st) {
+  const int max_pieces = (int)n;
+  int g_short = ceil_div(max_pieces, BPE_THREADS);
+  if (g_short > 4096) g_short = 4096;
+  hipLaunchKernelGGL(k_bpe_short, dim3(g_short), dim3(BPE_THREADS), 0, st, bytes, w, tb);
+  int g_long = ceil_div(n, LANE_CAP + 1);
+  if (g_long > 2048) g_long = 2048;
+  hipLaunchKernelGGL(k_bpe_long, dim3(g_long), dim3(64), 0, st, bytes, w, tb);
+  const int g_emit = ceil_div(max_pieces, EMIT_PER_BLOCK);
+  hipLaunchKernelGGL(k_emit_sums, dim3(g_emit), dim3(EMIT_THREADS), 0, st, w);
+  hipLaunchKernelGGL(k_emit, dim3(g_emit), dim3(EMIT_THREADS), 0, st, w, out_ids);
+  int g_huge = ceil_div(n, 256 * 8);
+  if (g_huge > 1024) g_huge = 1024;
+  hipLaunchKernelGGL(k_copy_huge, dim3(g_huge), dim3(256), 0, st, w, out_ids);
+  return hipGetLastError();
+}
+
+hipError_t launch_finish_count(const Work& w, int which, int64_t* out, hipStream_t st) {
+  hipLaunchKernelGGL(k_finish_count, dim3(1), dim3(1), 0, st, w.ctr, which, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_batch_offsets(const int64_t* offs, int nseq, int64_t n, const Work& w, int64_t* out_off,
+                                hipStream_t st) {
+  hipLaunchKernelGGL(k_batch_offsets, dim3(ceil_div((int64_t)nseq + 1, 256)), dim3(256), 0, st, offs, nseq, n, w,
+                     out_off);
+  return hipGetLastError();
+}
+
+hipError_t launch_write_zeros(int64_t* out, int cnt, hipStream_t st) {
+  if (cnt > 0) hipLaunchKernelGGL(k_write_zero_i64, dim3(ceil_div(cnt, 256)), dim3(256), 0, st, out, cnt);
+  return hipGetLastError();
+}
+
+hipError_t launch_write_zero_i32(int32_t* out, hipStream_t st) {
+  hipLaunchKernelGGL(k_write_zero_i32, dim3(1), dim3(1), 0, st, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_zero_counters(const Work& w, hipStream_t st) {
+  hipLaunchKernelGGL(k_zero, dim3(1), dim3(64), 0, st, w.ctr, (int)CTR_COUNT);
+  return hipGetLastError();
+}
+
+hipError_t launch_check_offsets(const int64_t* offs, int nseq, int64_t n, const Work& w, hipStream_t st) {
+  hipLaunchKernelGGL(k_check_offsets, dim3(ceil_div((int64_t)nseq + 1, 256)), dim3(256), 0, st, offs, nseq, n, w.ctr);
+  return hipGetLastError();
+}
+
+}  // namespace tt

@@ -1,0 +1,145 @@
+/* tt.h -- exact fresh-session byte-level BPE tokenization on one gfx950 GPU.
+ *
+ * C ABI of libtt.so.  The library reproduces, bit for bit, a sequential
+ * ordered-rule regex pre-tokenizer followed by classic byte-level BPE on every
+ * pre-token (TokTier, arXiv:2607.29678v1, summary page: the factorisation
+ * F = E* o G of Appendix A.1; the run-decomposition pre-tokenizer of §4.1; the
+ * per-piece GPU BPE of §4.2; the CPU-sync-free, graph-capturable single
+ * request path of §4.3; IDs only, raw array output, §4.3 / §4.4).
+ *
+ * Conventions
+ *  - One tokenizer is loaded per process.  All calls are serialised by the
+ *    caller: the device workspace is shared, so two encodes that overlap in
+ *    time (on any streams) race.
+ *  - Token ids: 0..255 are raw byte values; the merge of rank r makes id
+ *    256 + r.  Ids are int32.
+ *  - Text is UTF-8 with no BOM handling (U+FEFF is an ordinary char).  A
+ *    "char" is a Unicode code point.
+ *  - Return values: 0 on success or a negative TT_E* code.  Codes returned
+ *    by tt_encode / tt_encode_batch / tt_pretokenize cover only synchronous
+ *    argument, state and launch errors; data errors (invalid UTF-8, bad batch
+ *    offsets) are written on the device into the count the caller reads.
+ */
+#ifndef TT_H
+#define TT_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define TT_OK          0
+#define TT_EINVAL     -1  /* bad argument (null pointer, negative size, bad pattern id) */
+#define TT_ETABLE     -2  /* merge table invalid (see tt_load_bpe) */
+#define TT_ENOMEM     -3  /* host or device allocation failed */
+#define TT_EHIP       -4  /* a HIP runtime call or kernel launch failed */
+#define TT_EUTF8      -5  /* input is not valid UTF-8 (device-side data error) */
+#define TT_ENOTLOADED -6  /* no tokenizer loaded */
+#define TT_EOFFSETS   -7  /* batch offsets not monotone / not ending at n (device-side) */
+#define TT_ETOOBIG    -8  /* size beyond the library's limits */
+
+#define TT_PATTERN_GPT2   0  /* GPT-2-style rules: lower-case contractions, ' ?letters', ' ?digits',
+                                ' ?other', whitespace with the not-followed-by-non-space rule */
+#define TT_PATTERN_CL100K 1  /* cl100k-style rules: ASCII case-insensitive contractions, letters
+                                with one optional non-letter/digit/newline prefix, 1-3 digit
+                                groups, punctuation absorbing following CR/LF, whitespace up to
+                                the last CR/LF, then the lookahead rule */
+
+/* Maximum merges: ids must fit in 20 bits. */
+#define TT_MAX_MERGES (1048576 - 256)
+/* Maximum bytes of one encode call (offsets are int32 inside the library). */
+#define TT_MAX_BYTES  ((int64_t)1 << 30)
+
+/* tt_load_bpe -- load a byte-level BPE merge table and a rule set.
+ *
+ * merges     host int32[n_merges][2]: (left id, right id) of merge k.
+ * ranks      host int32[n_merges]: rank of merge k, a permutation of
+ *            0..n_merges-1; merge k makes token id 256 + ranks[k].  May be
+ *            NULL, meaning ranks[k] = k.
+ * n_merges   0 .. TT_MAX_MERGES.  0 means ids are the UTF-8 bytes.
+ * pattern_id TT_PATTERN_GPT2 or TT_PATTERN_CL100K.
+ *
+ * The table must be consistent: both operands of the merge of rank r are ids
+ * below 256 + r (every table learned by BPE training is), and no pair may
+ * appear twice.  Otherwise TT_ETABLE and nothing changes.  The arrays are
+ * copied; the caller may free them on return.  Builds the device pair-rank
+ * tables and the whole-pre-token cache (each token whose own BPE is itself),
+ * synchronises the device, and replaces any previously loaded tokenizer.
+ * Returns TT_OK, TT_EINVAL, TT_ETABLE, TT_ENOMEM or TT_EHIP.
+ */
+int tt_load_bpe(const int32_t* merges, const int32_t* ranks, int64_t n_merges, int32_t pattern_id);
+
+/* tt_reserve -- size the device workspace for inputs of up to max_bytes
+ * bytes and up to max_seqs batch sequences, so that later encodes do no
+ * allocation (required before capturing an encode into a HIP graph).
+ * Without it, an encode that needs more workspace grows it, which
+ * synchronises the device.  Returns TT_OK, TT_EINVAL, TT_ETOOBIG, TT_ENOMEM,
+ * TT_EHIP or TT_ENOTLOADED. */
+int tt_reserve(int64_t max_bytes, int32_t max_seqs);
+
+/* tt_encode -- token ids of one text.
+ *
+ * dev_bytes  device uint8[n]: the UTF-8 text (caller-owned).
+ * n          0 .. TT_MAX_BYTES-1.
+ * out_ids    device int32[>= n] (caller-owned).  T <= n always holds, so a
+ *            capacity of n never overflows; this is not checked.
+ * out_n      device int64[1] (caller-owned): receives T >= 0, or TT_EUTF8
+ *            if the text is not valid UTF-8 (out_ids is then unspecified).
+ * stream     HIP stream the work is enqueued on (0 = null stream).
+ *
+ * Enqueues only: no host synchronisation, no allocation once the workspace is
+ * large enough (see tt_reserve), graph-capturable.  n == 0 gives *out_n = 0.
+ * Returns TT_OK, TT_EINVAL, TT_ETOOBIG, TT_ENOMEM, TT_EHIP or TT_ENOTLOADED.
+ */
+int tt_encode(const uint8_t* dev_bytes, int64_t n, int32_t* out_ids, int64_t* out_n,
+              hipStream_t stream);
+
+/* tt_encode_batch -- token ids of n_seqs independent texts in one call.
+ *
+ * dev_bytes    device uint8[n]: the texts, concatenated.
+ * n            total bytes; must equal dev_offsets[n_seqs].
+ * dev_offsets  device int64[n_seqs + 1]: text s is bytes
+ *              [dev_offsets[s], dev_offsets[s+1]); dev_offsets[0] == 0,
+ *              non-decreasing (empty texts are allowed).  Each text is a
+ *              separate fresh session: its end is end-of-text for the
+ *              lookahead rules and no pre-token crosses it.
+ * n_seqs       >= 1.
+ * out_ids      device int32[>= n].
+ * out_offsets  device int64[n_seqs + 1]: ids of text s are
+ *              out_ids[out_offsets[s] .. out_offsets[s+1]).  On a data error
+ *              out_offsets[n_seqs] receives TT_EUTF8 or TT_EOFFSETS.
+ * stream       HIP stream.
+ * Same enqueue-only contract as tt_encode.
+ */
+int tt_encode_batch(const uint8_t* dev_bytes, int64_t n, const int64_t* dev_offsets, int32_t n_seqs,
+                    int32_t* out_ids, int64_t* out_offsets, hipStream_t stream);
+
+/* tt_pretokenize -- the pre-tokenizer alone (run decomposition, §4.1):
+ * byte offsets of every pre-token start.
+ *
+ * dev_offsets may be NULL (one text of n bytes) or as in tt_encode_batch.
+ * out_starts   device int32[>= n + 1]: piece starts in increasing order,
+ *              followed by the sentinel n.
+ * out_np       device int64[1]: number of pieces P, or TT_EUTF8 / TT_EOFFSETS.
+ * Same enqueue-only contract as tt_encode.
+ */
+int tt_pretokenize(const uint8_t* dev_bytes, int64_t n, const int64_t* dev_offsets, int32_t n_seqs,
+                   int32_t* out_starts, int64_t* out_np, hipStream_t stream);
+
+/* tt_char_class -- host query of the compiled Unicode class table:
+ * 0 other, 1 letter (\p{L}), 2 number (\p{N}), 3 White_Space; -1 if cp is
+ * not a Unicode scalar value.  No device work. */
+int tt_char_class(uint32_t cp);
+
+/* tt_free -- release the tokenizer tables and the workspace (synchronises). */
+void tt_free(void);
+
+/* tt_strerror -- static description of a TT_* code. */
+const char* tt_strerror(int code);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* TT_H */

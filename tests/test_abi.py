@@ -1,0 +1,80 @@
+"""Host-side checks of libtt (no GPU needed).
+
+  * the library loads and exports every function include/tt.h declares;
+  * the compiled Unicode class table equals the regex module's classes on all
+    1,114,112 code points (the one pinned Unicode version; TokTier summary page
+    §5.2 reports a Unicode-version mismatch that mis-split 9,700 code points);
+  * tt_load_bpe rejects bad arguments and inconsistent tables before touching
+    the device; encode entry points reject bad arguments.
+"""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+import regex
+
+import exact_byte_level_amd as tt
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    with open(os.path.join(ROOT, "include", "tt.h")) as f:
+        src = f.read()
+    return sorted(set(re.findall(r"^(?:int|void|const char\*)\s+(tt_\w+)\(", src, re.M)))
+
+
+def test_exports_every_declared_symbol():
+    names = _declared()
+    assert names == sorted(["tt_load_bpe", "tt_reserve", "tt_encode", "tt_encode_batch", "tt_pretokenize",
+                            "tt_char_class", "tt_free", "tt_strerror"])
+    lib = ctypes.CDLL(tt.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_unicode_table_matches_regex_all_code_points():
+    is_l, is_n, is_w = regex.compile(r"\p{L}"), regex.compile(r"\p{N}"), regex.compile(r"\s")
+    cls = tt.char_class
+    diffs = []
+    for cp in range(0x110000):
+        if 0xD800 <= cp <= 0xDFFF:
+            assert cls(cp) == -1
+            continue
+        c = chr(cp)
+        want = 1 if is_l.match(c) else 2 if is_n.match(c) else 3 if is_w.match(c) else 0
+        if cls(cp) != want:
+            diffs.append(cp)
+    assert diffs == []
+    assert cls(0x110000) == -1
+    # code points added in Unicode 14-17 are letters in the pinned tables
+    for cp in (0x9FFD, 0x31350, 0x2EBF0, 0x1E5D0, 0x323B0, 0x16EA0):
+        assert cls(cp) == 1
+
+
+def test_load_rejects_bad_tables_without_device():
+    lib = tt.lib()
+
+    def load(merges, ranks=None, pattern=0):
+        m = np.ascontiguousarray(np.asarray(merges, dtype=np.int32).reshape(-1, 2))
+        r = None if ranks is None else np.ascontiguousarray(np.asarray(ranks, dtype=np.int32))
+        return lib.tt_load_bpe(m.ctypes.data, None if r is None else r.ctypes.data, len(m), pattern)
+
+    assert load([(97, 98)], pattern=2) == tt.TT_EINVAL
+    assert load([(97, 256)]) == tt.TT_ETABLE              # operand made later
+    assert load([(97, 98), (97, 98)]) == tt.TT_ETABLE     # duplicate pair
+    assert load([(97, 98), (98, 99)], ranks=[0, 0]) == tt.TT_ETABLE  # ranks not a permutation
+    assert load([(97, 98), (98, 99)], ranks=[0, 2]) == tt.TT_ETABLE
+    assert load([(97, 257), (98, 99)], ranks=[1, 0]) == tt.TT_ETABLE  # 257 = rank 1 itself
+    assert lib.tt_load_bpe(None, None, -1, 0) == tt.TT_EINVAL
+
+
+def test_encode_rejects_bad_arguments():
+    lib = tt.lib()
+    stream = ctypes.c_void_p(0)
+    assert lib.tt_encode(None, -1, None, None, stream) == tt.TT_EINVAL
+    assert lib.tt_encode_batch(None, 0, None, 1, None, None, stream) == tt.TT_EINVAL
+    assert lib.tt_pretokenize(None, 5, None, 1, None, None, stream) == tt.TT_EINVAL
+    assert tt.strerror(tt.TT_EUTF8) == "input is not valid UTF-8"
