@@ -1,0 +1,329 @@
+"""Benchmark: exact BPE encode throughput on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c2] [--all]
+
+One step = one full encode (pre-tokenization, BPE of every pre-token, token-id
+emission) of the workload's text, which is already resident in HBM.  Prints
+one JSON line: chars/s (value), ms per step and per 1M chars, the roofline of
+the dominant kernel (per-kernel HIP events recorded on the launch stream), and
+the CPU oracle timed on a bounded sample on this host as a reported baseline.
+
+Workloads (seeded, synthetic; the default is the 1,000,000-char single text
+the headline metric is quoted on):
+  c1  64 KiB ASCII code-like text, GPT-2-style rules, 4,096 merges
+  c2  1,000,000-char code/log mix, GPT-2-style rules, 50,000 merges
+  c3  1,000,000-char mix with 5 % multibyte chars, cl100k-style, 100,000 merges
+  c4  64 log-normal fresh texts (~8M chars) in one batch call
+  c5a..c5d adversarial 1,000,000-char texts (one giant piece, 100K-digit runs,
+      50K-space runs, alternating letter/punctuation)
+"""
+import argparse
+import hashlib
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "exact BPE encode throughput: chars/s and ms per 1M chars; % of HBM peak"
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
+
+
+def _sha(a):
+    import numpy as np
+    return hashlib.sha256(np.ascontiguousarray(a, dtype="<i4").tobytes()).hexdigest()
+
+
+def alg_bytes(kernel, n, P, T):
+    """Bytes a kernel must move at least once (inputs read + outputs written)."""
+    if kernel.startswith("k_pretok"):
+        return n + n / 8            # text in, one start bit per byte out
+    if kernel == "k_tile_summary":
+        return n
+    if kernel == "k_compact":
+        return n / 8 + 4 * (P + 1)  # start bits in, piece offsets out
+    if kernel in ("k_bpe_short", "k_bpe_long"):
+        return 4 * (P + 1) + n + 4 * T + 4 * P  # offsets + piece bytes in, tokens + counts out
+    if kernel == "k_emit":
+        return 12 * P + 8 * T       # counts, starts, tokens in; offsets, ids out
+    if kernel == "k_emit_sums":
+        return 4 * P
+    return 0
+
+
+def run_workload(name, steps, warmup, graph=True, cpu=True, traffic=None):
+    import numpy as np
+    import torch
+
+    import exact_byte_level_amd as tt
+    from synth.text import WORKLOADS, workload
+
+    data, offs, pat, voc = workload(name)
+    n = len(data)
+    chars = len(data.decode("utf-8"))
+    merges = np.load(os.path.join(ROOT, "data", "vocab_%s.npy" % voc))
+    tt.load(merges, pattern_id=pat)
+    nseq = 1 if offs is None else len(offs) - 1
+    tt.reserve(n, nseq)
+    dev = torch.device("cuda", 0)
+    x = torch.frombuffer(bytearray(data), dtype=torch.uint8).to(dev)
+    out = torch.empty(n, dtype=torch.int32, device=dev)
+    cnt = torch.empty(nseq + 1 if offs is not None else 1, dtype=torch.int64, device=dev)
+    off = None if offs is None else torch.tensor(offs, dtype=torch.int64, device=dev)
+
+    def step():
+        if off is None:
+            tt.encode_into(x, out, cnt)
+        else:
+            tt.encode_batch_into(x, off, out, cnt)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    T = int(cnt[-1].item())
+    if T < 0:
+        raise RuntimeError("encode reported error %d" % T)
+    ids = out[:T].cpu().numpy()
+    gold_path = os.path.join(ROOT, "tests", "golden", "expected.json")
+    verified = None
+    if os.path.exists(gold_path):
+        with open(gold_path) as f:
+            exp = json.load(f).get(name)
+        if exp:
+            verified = exp["tokens"] == T and exp["ids_sha256"] == _sha(ids)
+            if not verified:
+                raise RuntimeError("GPU ids differ from the oracle digest for %s" % name)
+
+    # timed region: exactly `steps` encodes, events on the launch stream
+    stream = torch.cuda.current_stream()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms_per_step = e0.elapsed_time(e1) / steps
+
+    # latency distribution: one event pair per encode
+    lat = []
+    for _ in range(steps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        step()
+        b.record(stream)
+        b.synchronize()
+        lat.append(a.elapsed_time(b))
+    lat.sort()
+    p50 = statistics.median(lat)
+    p99 = lat[min(len(lat) - 1, int(round(0.99 * (len(lat) - 1))))]
+
+    # host-inclusive latency: encode plus the D2H read of the count
+    t_host = []
+    for _ in range(min(steps, 50)):
+        t0 = time.perf_counter()
+        step()
+        int(cnt[-1].item())
+        t_host.append((time.perf_counter() - t0) * 1e3)
+    host_p50 = statistics.median(t_host)
+
+    # HIP graph replay of one captured encode
+    graph_p50 = None
+    if graph:
+        try:
+            g = torch.cuda.CUDAGraph()
+            side = torch.cuda.Stream()
+            side.wait_stream(stream)
+            with torch.cuda.stream(side):
+                step()
+            stream.wait_stream(side)
+            torch.cuda.synchronize()
+            with torch.cuda.graph(g):
+                step()
+            torch.cuda.synchronize()
+            glat = []
+            for _ in range(steps):
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record(stream)
+                g.replay()
+                b.record(stream)
+                b.synchronize()
+                glat.append(a.elapsed_time(b))
+            gT = int(cnt[-1].item())
+            if gT != T or _sha(out[:T].cpu().numpy()) != _sha(ids):
+                raise RuntimeError("graph replay result differs")
+            graph_p50 = statistics.median(glat)
+        except Exception as ex:  # graph capture is optional context
+            print("graph mode skipped: %r" % (ex,), file=sys.stderr)
+
+    # per-kernel durations from events recorded after each launch
+    tt.profile(True)
+    acc = {}
+    nprof = max(10, min(steps, 50))
+    for _ in range(nprof):
+        step()
+        for k, ms in tt.profile_read():
+            acc.setdefault(k, []).append(ms)
+    tt.profile(False)
+    kern = {k: statistics.mean(v) for k, v in acc.items()}
+    start_np = tt.pretokenize(x, off)
+    P = int(start_np.numel())
+    dom = max(kern, key=kern.get)
+    dom_ms = kern[dom]
+    a_bytes = alg_bytes(dom, n, P, T)
+    achieved = a_bytes / (dom_ms * 1e-3) / 1e9
+    roof = {
+        "bound": "hbm",
+        "kernel": dom,
+        "achieved": round(achieved, 3),
+        "peak": HBM_PEAK_GBS,
+        "unit": "GB/s",
+        "frac": achieved / HBM_PEAK_GBS,
+        "traffic": None,
+        "kernel_ms": round(dom_ms, 5),
+        "alg_bytes": int(a_bytes),
+    }
+    if traffic and traffic.get("workload") == name and traffic.get("kernel") == dom:
+        roof["traffic"] = traffic.get("bytes")
+
+    res = {
+        "name": name,
+        "desc": WORKLOADS[name][2],
+        "bytes": n,
+        "chars": chars,
+        "pieces": P,
+        "tokens": T,
+        "seqs": nseq,
+        "ms_per_step": ms_per_step,
+        "p50_ms": p50,
+        "p99_ms": p99,
+        "host_incl_p50_ms": host_p50,
+        "graph_p50_ms": graph_p50,
+        "kernels_ms": {k: round(v, 5) for k, v in sorted(kern.items(), key=lambda kv: -kv[1])},
+        "roofline": roof,
+        "verified": verified,
+    }
+
+    if cpu:
+        from oracle.bpe import Vocab, encode as oracle_encode
+        v = Vocab(merges)
+        # bounded sample (a few seconds of CPU work): the whole text, or the
+        # first texts of the batch up to ~4 MB
+        if offs is None:
+            parts, desc = [data], "the whole text"
+        else:
+            parts, tot = [], 0
+            for s in range(nseq):
+                seg = data[offs[s]:offs[s + 1]]
+                if tot + len(seg) > 4_000_000 and parts:
+                    break
+                parts.append(seg)
+                tot += len(seg)
+            desc = "first %d of %d texts (%d bytes)" % (len(parts), nseq, sum(len(p) for p in parts))
+        c_chars = sum(len(p.decode("utf-8")) for p in parts)
+        t0 = time.perf_counter()
+        for p in parts:
+            oracle_encode(p, v, pat)
+        dt = time.perf_counter() - t0
+        res["cpu_baseline"] = {
+            "value": c_chars / dt,
+            "unit": "chars/s",
+            "cores": 1,
+            "kind": "oracle",
+            "sample": "%s, %d chars, %.1f s (plain Python oracle, no piece memo)" % (desc, c_chars, dt),
+        }
+    return res
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="c2")
+    ap.add_argument("--all", action="store_true", help="also bench every workload (lines on stderr)")
+    ap.add_argument("--no-graph", action="store_true")
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "traffic.json"),
+                    help="measured HBM traffic of the dominant kernel (rocprofv3 PMC), if present")
+    ap.add_argument("--copy-probe", type=int, default=0,
+                    help="also run a plain device copy of this many MiB (counter calibration)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py: this path runs on one GPU only (no sharding or collectives are built); "
+              "run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU", file=sys.stderr)
+        sys.exit(2)
+    torch.cuda.set_device(0)
+
+    traffic = None
+    if os.path.exists(args.traffic):
+        with open(args.traffic) as f:
+            traffic = json.load(f)
+
+    if args.copy_probe:
+        src = torch.empty(args.copy_probe << 20, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+
+    res = run_workload(args.workload, args.steps, args.warmup, graph=not args.no_graph,
+                       cpu=not args.no_cpu, traffic=traffic)
+    chars_per_s = res["chars"] / (res["ms_per_step"] * 1e-3)
+    line = {
+        "metric": METRIC,
+        "value": chars_per_s,
+        "unit": "chars/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": res["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int32",
+        "data": "synthetic",
+        "config": {
+            "workload": "%s: %s" % (res["name"], res["desc"]),
+            "chars": res["chars"],
+            "bytes": res["bytes"],
+            "pieces": res["pieces"],
+            "tokens": res["tokens"],
+            "ms_per_1M_chars": res["ms_per_step"] * 1e6 / res["chars"],
+            "p50_ms": res["p50_ms"],
+            "p99_ms": res["p99_ms"],
+            "graph_p50_ms": res["graph_p50_ms"],
+            "host_incl_p50_ms": res["host_incl_p50_ms"],
+            "end_to_end_alg_GBps": (res["bytes"] + 4 * res["tokens"]) / (res["ms_per_step"] * 1e-3) / 1e9,
+            "kernels_ms": res["kernels_ms"],
+            "verified_against_oracle": res["verified"],
+            "parallelism": "single GPU",
+        },
+        "roofline": res["roofline"],
+    }
+    if "cpu_baseline" in res:
+        line["cpu_baseline"] = res["cpu_baseline"]
+    print(json.dumps(line), flush=True)
+
+    if args.all:
+        from synth.text import WORKLOADS
+        for name in WORKLOADS:
+            if name == args.workload:
+                continue
+            r = run_workload(name, args.steps, args.warmup, graph=not args.no_graph, cpu=False, traffic=traffic)
+            r["chars_per_s"] = r["chars"] / (r["ms_per_step"] * 1e-3)
+            r["ms_per_1M_chars"] = r["ms_per_step"] * 1e6 / r["chars"]
+            print(json.dumps(r), file=sys.stderr, flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -53,11 +53,14 @@ def lib():
         L.tt_encode_batch.argtypes = [vp, i64, vp, i32, vp, vp, vp]
         L.tt_pretokenize.argtypes = [vp, i64, vp, i32, vp, vp, vp]
         L.tt_char_class.argtypes = [ctypes.c_uint32]
+        L.tt_profile.argtypes = [ctypes.c_int]
+        L.tt_profile_read.argtypes = [ctypes.POINTER(ctypes.c_char_p), ctypes.POINTER(ctypes.c_float), ctypes.c_int]
         L.tt_free.argtypes = []
         L.tt_free.restype = None
         L.tt_strerror.argtypes = [ctypes.c_int]
         L.tt_strerror.restype = ctypes.c_char_p
-        for f in ("tt_load_bpe", "tt_reserve", "tt_encode", "tt_encode_batch", "tt_pretokenize", "tt_char_class"):
+        for f in ("tt_load_bpe", "tt_reserve", "tt_encode", "tt_encode_batch", "tt_pretokenize", "tt_char_class",
+                  "tt_profile", "tt_profile_read"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -155,6 +158,21 @@ def pretokenize(data, offsets=None, stream=None):
 def char_class(cp):
     """Class of a code point in the compiled table: 0 other, 1 L, 2 N, 3 White_Space."""
     return lib().tt_char_class(int(cp))
+
+
+def profile(enable):
+    """Switch per-kernel event timing of later calls on or off."""
+    _check(lib().tt_profile(1 if enable else 0), "tt_profile")
+
+
+def profile_read(cap=64):
+    """[(kernel name, ms)] of the last call (waits for it)."""
+    names = (ctypes.c_char_p * cap)()
+    ms = (ctypes.c_float * cap)()
+    k = lib().tt_profile_read(names, ms, cap)
+    if k < 0:
+        raise TTError(k, "tt_profile_read")
+    return [(names[i].decode(), float(ms[i])) for i in range(k)]
 
 
 def free():

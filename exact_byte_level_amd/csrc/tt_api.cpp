@@ -35,6 +35,22 @@ struct State {
 State g;
 std::mutex g_mu;
 
+// Per-kernel timing (measurement aid): events recorded after each launch.
+constexpr int PROF_CAP = 64;
+struct Prof {
+  bool on = false;
+  hipEvent_t start = nullptr;
+  hipEvent_t ev[PROF_CAP] = {};
+  const char* name[PROF_CAP] = {};
+  int n = 0;
+} g_prof;
+
+void prof_begin(hipStream_t st) {
+  if (!g_prof.on) return;
+  g_prof.n = 0;
+  (void)hipEventRecord(g_prof.start, st);
+}
+
 template <class T>
 void free_dev(T*& p) {
   if (p) (void)hipFree((void*)p);
@@ -160,6 +176,12 @@ int check_stream_state() {
 }
 
 }  // namespace
+
+void tt::prof_mark(const char* name, hipStream_t st) {
+  if (!g_prof.on || g_prof.n >= PROF_CAP) return;
+  (void)hipEventRecord(g_prof.ev[g_prof.n], st);
+  g_prof.name[g_prof.n++] = name;
+}
 
 extern "C" {
 
@@ -298,6 +320,7 @@ int tt_encode(const uint8_t* dev_bytes, int64_t n, int32_t* out_ids, int64_t* ou
   if (rc != TT_OK) return rc;
   if (n == 0) return launch_write_zeros(out_n, 1, stream) == hipSuccess ? TT_OK : TT_EHIP;
   if ((rc = ensure_workspace(n)) != TT_OK) return rc;
+  prof_begin(stream);
   if (launch_pretokenize(dev_bytes, n, nullptr, 1, g.pattern, g.w, g.w.piece_start, stream) != hipSuccess ||
       launch_bpe_emit(dev_bytes, n, g.tb, g.w, out_ids, stream) != hipSuccess ||
       launch_finish_count(g.w, CTR_T, out_n, stream) != hipSuccess)
@@ -322,6 +345,7 @@ int tt_encode_batch(const uint8_t* dev_bytes, int64_t n, const int64_t* dev_offs
       return TT_EHIP;
     return TT_OK;
   }
+  prof_begin(stream);
   if (launch_pretokenize(dev_bytes, n, dev_offsets, n_seqs, g.pattern, g.w, g.w.piece_start, stream) != hipSuccess ||
       launch_bpe_emit(dev_bytes, n, g.tb, g.w, out_ids, stream) != hipSuccess ||
       launch_batch_offsets(dev_offsets, n_seqs, n, g.w, out_offsets, stream) != hipSuccess)
@@ -346,6 +370,7 @@ int tt_pretokenize(const uint8_t* dev_bytes, int64_t n, const int64_t* dev_offse
       return TT_EHIP;
     return TT_OK;
   }
+  prof_begin(stream);
   if (launch_pretokenize(dev_bytes, n, dev_offsets, nseq, g.pattern, g.w, out_starts, stream) != hipSuccess ||
       launch_finish_count(g.w, CTR_P, out_np, stream) != hipSuccess)
     return TT_EHIP;
@@ -358,6 +383,36 @@ int tt_char_class(uint32_t cp) {
   if (hi >= (uint32_t)TT_UNI_L1_SIZE) return 0;
   uint32_t byte = h_uni_l2[h_uni_l1[hi] * 64u + ((cp & 255u) >> 2)];
   return (int)((byte >> ((cp & 3u) * 2u)) & 3u);
+}
+
+int tt_profile(int enable) {
+  std::lock_guard<std::mutex> lock(g_mu);
+  if (enable && !g_prof.on) {
+    if (hipEventCreate(&g_prof.start) != hipSuccess) return TT_EHIP;
+    for (int i = 0; i < PROF_CAP; ++i)
+      if (hipEventCreate(&g_prof.ev[i]) != hipSuccess) return TT_EHIP;
+    g_prof.on = true;
+    g_prof.n = 0;
+  } else if (!enable && g_prof.on) {
+    (void)hipDeviceSynchronize();
+    (void)hipEventDestroy(g_prof.start);
+    for (int i = 0; i < PROF_CAP; ++i) (void)hipEventDestroy(g_prof.ev[i]);
+    g_prof = Prof{};
+  }
+  return TT_OK;
+}
+
+int tt_profile_read(const char** names, float* ms, int cap) {
+  std::lock_guard<std::mutex> lock(g_mu);
+  if (!g_prof.on || (cap > 0 && (!names || !ms))) return TT_EINVAL;
+  if (g_prof.n == 0) return 0;
+  if (hipEventSynchronize(g_prof.ev[g_prof.n - 1]) != hipSuccess) return TT_EHIP;
+  int k = std::min(cap, g_prof.n);
+  for (int i = 0; i < k; ++i) {
+    names[i] = g_prof.name[i];
+    if (hipEventElapsedTime(&ms[i], i ? g_prof.ev[i - 1] : g_prof.start, g_prof.ev[i]) != hipSuccess) return TT_EHIP;
+  }
+  return k;
 }
 
 void tt_free(void) {

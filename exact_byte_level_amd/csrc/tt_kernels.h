@@ -4,6 +4,10 @@
 
 namespace tt {
 
+// Measurement hook, implemented by the host library: when per-kernel timing
+// is on, records a HIP event on `st` after the named kernel's launch.
+void prof_mark(const char* name, hipStream_t st);
+
 // Zero the counters, validate batch offsets (if any), and write the piece
 // starts (+ sentinel n) to `starts` and P to w.ctr[CTR_P].  n >= 1.
 hipError_t launch_pretokenize(const uint8_t* bytes, int64_t n, const int64_t* offs, int nseq, int pattern,

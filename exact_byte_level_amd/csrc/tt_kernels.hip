@@ -911,15 +911,18 @@ static inline int ceil_div(int64_t a, int64_t b) { return (int)((a + b - 1) / b)
 hipError_t launch_pretokenize(const uint8_t* bytes, int64_t n, const int64_t* offs, int nseq, int pattern,
                               const Work& w, int32_t* starts, hipStream_t st) {
   const int ntiles = ceil_div(n, TILE);
-  hipLaunchKernelGGL(k_zero, dim3(1), dim3(64), 0, st, w.ctr, (int)CTR_COUNT);
-  if (offs) hipLaunchKernelGGL(k_check_offsets, dim3(ceil_div((int64_t)nseq + 1, 256)), dim3(256), 0, st, offs, nseq, n, w.ctr);
-  if (pattern == 1) {
-    hipLaunchKernelGGL(k_tile_summary, dim3(ntiles), dim3(PT_THREADS), 0, st, bytes, n, offs, nseq, w);
-    hipLaunchKernelGGL(k_pretok<1>, dim3(ntiles), dim3(PT_THREADS), 0, st, bytes, n, offs, nseq, ntiles, w);
-  } else {
-    hipLaunchKernelGGL(k_pretok<0>, dim3(ntiles), dim3(PT_THREADS), 0, st, bytes, n, offs, nseq, ntiles, w);
+  hipLaunchKernelGGL(k_zero, dim3(1), dim3(64), 0, st, w.ctr, (int)CTR_COUNT); prof_mark("k_zero", st);
+  if (offs) {
+    hipLaunchKernelGGL(k_check_offsets, dim3(ceil_div((int64_t)nseq + 1, 256)), dim3(256), 0, st, offs, nseq, n, w.ctr);
+    prof_mark("k_check_offsets", st);
   }
-  hipLaunchKernelGGL(k_compact, dim3(ntiles), dim3(PT_THREADS), 0, st, w, ntiles, n, starts);
+  if (pattern == 1) {
+    hipLaunchKernelGGL(k_tile_summary, dim3(ntiles), dim3(PT_THREADS), 0, st, bytes, n, offs, nseq, w); prof_mark("k_tile_summary", st);
+    hipLaunchKernelGGL(k_pretok<1>, dim3(ntiles), dim3(PT_THREADS), 0, st, bytes, n, offs, nseq, ntiles, w); prof_mark("k_pretok<1>", st);
+  } else {
+    hipLaunchKernelGGL(k_pretok<0>, dim3(ntiles), dim3(PT_THREADS), 0, st, bytes, n, offs, nseq, ntiles, w); prof_mark("k_pretok<0>", st);
+  }
+  hipLaunchKernelGGL(k_compact, dim3(ntiles), dim3(PT_THREADS), 0, st, w, ntiles, n, starts); prof_mark("k_compact", st);
   return hipGetLastError();
 }
 
@@ -928,48 +931,51 @@ hipError_t launch_bpe_emit(const uint8_t* bytes, int64_t n, const Tables& tb, co
   const int max_pieces = (int)n;
   int g_short = ceil_div(max_pieces, BPE_THREADS);
   if (g_short > 4096) g_short = 4096;
-  hipLaunchKernelGGL(k_bpe_short, dim3(g_short), dim3(BPE_THREADS), 0, st, bytes, w, tb);
+  hipLaunchKernelGGL(k_bpe_short, dim3(g_short), dim3(BPE_THREADS), 0, st, bytes, w, tb); prof_mark("k_bpe_short", st);
   int g_long = ceil_div(n, LANE_CAP + 1);
   if (g_long > 2048) g_long = 2048;
-  hipLaunchKernelGGL(k_bpe_long, dim3(g_long), dim3(64), 0, st, bytes, w, tb);
+  hipLaunchKernelGGL(k_bpe_long, dim3(g_long), dim3(64), 0, st, bytes, w, tb); prof_mark("k_bpe_long", st);
   const int g_emit = ceil_div(max_pieces, EMIT_PER_BLOCK);
-  hipLaunchKernelGGL(k_emit_sums, dim3(g_emit), dim3(EMIT_THREADS), 0, st, w);
-  hipLaunchKernelGGL(k_emit, dim3(g_emit), dim3(EMIT_THREADS), 0, st, w, out_ids);
+  hipLaunchKernelGGL(k_emit_sums, dim3(g_emit), dim3(EMIT_THREADS), 0, st, w); prof_mark("k_emit_sums", st);
+  hipLaunchKernelGGL(k_emit, dim3(g_emit), dim3(EMIT_THREADS), 0, st, w, out_ids); prof_mark("k_emit", st);
   int g_huge = ceil_div(n, 256 * 8);
   if (g_huge > 1024) g_huge = 1024;
-  hipLaunchKernelGGL(k_copy_huge, dim3(g_huge), dim3(256), 0, st, w, out_ids);
+  hipLaunchKernelGGL(k_copy_huge, dim3(g_huge), dim3(256), 0, st, w, out_ids); prof_mark("k_copy_huge", st);
   return hipGetLastError();
 }
 
 hipError_t launch_finish_count(const Work& w, int which, int64_t* out, hipStream_t st) {
-  hipLaunchKernelGGL(k_finish_count, dim3(1), dim3(1), 0, st, w.ctr, which, out);
+  hipLaunchKernelGGL(k_finish_count, dim3(1), dim3(1), 0, st, w.ctr, which, out); prof_mark("k_finish_count", st);
   return hipGetLastError();
 }
 
 hipError_t launch_batch_offsets(const int64_t* offs, int nseq, int64_t n, const Work& w, int64_t* out_off,
                                 hipStream_t st) {
   hipLaunchKernelGGL(k_batch_offsets, dim3(ceil_div((int64_t)nseq + 1, 256)), dim3(256), 0, st, offs, nseq, n, w,
-                     out_off);
+                     out_off); prof_mark("k_batch_offsets", st);
   return hipGetLastError();
 }
 
 hipError_t launch_write_zeros(int64_t* out, int cnt, hipStream_t st) {
-  if (cnt > 0) hipLaunchKernelGGL(k_write_zero_i64, dim3(ceil_div(cnt, 256)), dim3(256), 0, st, out, cnt);
+  if (cnt > 0) {
+    hipLaunchKernelGGL(k_write_zero_i64, dim3(ceil_div(cnt, 256)), dim3(256), 0, st, out, cnt);
+    prof_mark("k_write_zero_i64", st);
+  }
   return hipGetLastError();
 }
 
 hipError_t launch_write_zero_i32(int32_t* out, hipStream_t st) {
-  hipLaunchKernelGGL(k_write_zero_i32, dim3(1), dim3(1), 0, st, out);
+  hipLaunchKernelGGL(k_write_zero_i32, dim3(1), dim3(1), 0, st, out); prof_mark("k_write_zero_i32", st);
   return hipGetLastError();
 }
 
 hipError_t launch_zero_counters(const Work& w, hipStream_t st) {
-  hipLaunchKernelGGL(k_zero, dim3(1), dim3(64), 0, st, w.ctr, (int)CTR_COUNT);
+  hipLaunchKernelGGL(k_zero, dim3(1), dim3(64), 0, st, w.ctr, (int)CTR_COUNT); prof_mark("k_zero", st);
   return hipGetLastError();
 }
 
 hipError_t launch_check_offsets(const int64_t* offs, int nseq, int64_t n, const Work& w, hipStream_t st) {
-  hipLaunchKernelGGL(k_check_offsets, dim3(ceil_div((int64_t)nseq + 1, 256)), dim3(256), 0, st, offs, nseq, n, w.ctr);
+  hipLaunchKernelGGL(k_check_offsets, dim3(ceil_div((int64_t)nseq + 1, 256)), dim3(256), 0, st, offs, nseq, n, w.ctr); prof_mark("k_check_offsets", st);
   return hipGetLastError();
 }
 

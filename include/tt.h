@@ -133,6 +133,20 @@ int tt_pretokenize(const uint8_t* dev_bytes, int64_t n, const int64_t* dev_offse
  * not a Unicode scalar value.  No device work. */
 int tt_char_class(uint32_t cp);
 
+/* tt_profile -- per-kernel timing of later calls (a measurement aid).
+ * enable != 0 creates a small pool of HIP events (this allocates: switch it
+ * on outside any graph capture); from then on every encode records an event
+ * on its stream after each kernel launch.  enable == 0 synchronises and
+ * destroys them.  Returns TT_OK or TT_EHIP. */
+int tt_profile(int enable);
+
+/* tt_profile_read -- kernel names and durations (ms, time from the previous
+ * event to the event after this kernel) of the last encode / pretokenize
+ * call.  Waits for that call to finish.  names[i] are static strings.
+ * Returns the number of entries written (<= cap), or TT_EINVAL if profiling
+ * is off, or TT_EHIP. */
+int tt_profile_read(const char** names, float* ms, int cap);
+
 /* tt_free -- release the tokenizer tables and the workspace (synchronises). */
 void tt_free(void);
 
