@@ -6,12 +6,13 @@
 namespace tt {
 
 // ---------------------------------------------------------------- pre-tokenizer
-constexpr int TILE = 4096;              // bytes per pre-tokenizer workgroup
+constexpr int TILE = 1024;              // bytes per pre-tokenizer workgroup
 constexpr int PT_THREADS = 256;         // threads per pre-tokenizer workgroup
-constexpr int PT_CHUNK = TILE / PT_THREADS;  // 16 contiguous bytes per thread
+constexpr int PT_CHUNK = TILE / PT_THREADS;  // 4 contiguous bytes per thread
 constexpr int HALO = 16;                // context bytes kept on each side of a tile
 constexpr int SPAN = TILE + 2 * HALO;   // decoded positions per tile
 constexpr int BMAP_WORDS = (SPAN + 8 + 31) / 32;  // sequence-boundary bitmap
+constexpr int RAW_WORDS = (SPAN + 16) / 16;       // raw tile bytes staged in LDS, 16 B words
 
 // Char classes of the run decomposition.  WS = whitespace other than CR/LF,
 // WN = CR or LF.  CONT marks a UTF-8 continuation byte, OUT a position
@@ -86,7 +87,7 @@ struct Work {
   uint32_t* tile_fwd;    // [ntiles] forward run summary of each tile
   uint32_t* tile_bwd;    // [ntiles] backward run summary
   uint32_t* tile_cnt;    // [ntiles] pre-token starts in each tile
-  uint16_t* flags;       // [ntiles * PT_THREADS] start bits of 16 bytes each
+  uint16_t* flags;       // [ntiles * PT_THREADS] start bits of each thread's PT_CHUNK bytes
   int32_t* piece_start;  // [n + 1]
   int32_t* piece_cnt;    // [n] tokens of each piece
   int32_t* tmp_ids;      // [n] tokens of the piece starting at byte s live at [s, s + cnt)
@@ -99,10 +100,9 @@ struct Work {
 };
 
 // ------------------------------------------------------------- BPE tiers
-constexpr int LANE_CAP = 32;            // pieces up to this many bytes: one lane each
-constexpr int BPE_THREADS = 128;
+constexpr int LANE_CAP = 64;            // pieces up to this many bytes: group BPE in one wavefront
 constexpr int EMIT_THREADS = 256;
-constexpr int EMIT_PER_THREAD = 16;
+constexpr int EMIT_PER_THREAD = 1;
 constexpr int EMIT_PER_BLOCK = EMIT_THREADS * EMIT_PER_THREAD;
 constexpr int HUGE_TOKENS = 4096;       // pieces with more tokens are copied grid-wide
 

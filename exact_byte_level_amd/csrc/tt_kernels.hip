@@ -15,7 +15,7 @@
 //
 // Hot-path data (all integer; no floating point, no MFMA):
 //   bytes   uint8[n]         caller's UTF-8 text
-//   flags   uint16 per 16 B  pre-token start bits
+//   flags   uint16 per 4 B   pre-token start bits
 //   starts  int32[P + 1]     piece byte offsets + sentinel n
 //   tmp_ids int32[n]         tokens of the piece starting at byte s at [s, s+cnt)
 //   out_ids int32[T]         caller's output
@@ -74,8 +74,15 @@ __device__ __forceinline__ bool is_char(uint32_t code) { return cls_of(code) - 1
 __device__ __forceinline__ int clen(uint32_t code) { return (int)((code >> K_LEN_SHIFT) & 3u) + 1; }
 
 // Shared-memory state of one pre-tokenizer tile.
+// Codes live in LDS at a padded index (one spare dword per 16 positions), so
+// threads that each walk their own run of 16 positions hit distinct banks.
+constexpr int CODE_SLOTS = SPAN + 2 * (SPAN / 16) + 4;
+__device__ __forceinline__ int cix(int j) { return j + 2 * (j >> 4); }
+
 struct TileSmem {
-  uint16_t code[SPAN];
+  uint4 raw[RAW_WORDS];   // bytes of positions [t0 - HALO, t0 - HALO + 16 * RAW_WORDS); 0 outside the text
+  uint16_t code[CODE_SLOTS];
+  uint16_t ascii[128];
   uint32_t bmap[BMAP_WORDS];
   uint8_t l1[TT_UNI_L1_SIZE];
   uint8_t l2[TT_UNI_NBLOCKS * 64];
@@ -99,22 +106,23 @@ __device__ __forceinline__ int64_t lower_bound_i64(const int64_t* a, int64_t cnt
   return lo;
 }
 
-// Decode the char starting at tile position j (global position base + j).
-// Validates UTF-8 as strict decoding does: no overlong forms, no surrogates,
-// nothing above U+10FFFF, no truncated or stray continuation bytes, and no
-// char crossing a sequence boundary.
-__device__ __forceinline__ uint16_t decode_at(const uint8_t* __restrict__ bytes, int64_t n, int64_t base,
-                                              int j, const TileSmem& sm, bool table_in_lds) {
+// Decode the char starting at tile position j (global position base + j) from
+// the raw bytes staged in LDS.  Validates UTF-8 as strict decoding does: no
+// overlong forms, no surrogates, nothing above U+10FFFF, no truncated or stray
+// continuation bytes, and no char crossing a sequence boundary.
+__device__ __forceinline__ uint16_t decode_at(int64_t n, int64_t base, int j, const TileSmem& sm,
+                                              bool table_in_lds) {
+  const uint8_t* raw = reinterpret_cast<const uint8_t*>(sm.raw);
   int64_t p = base + j;
   if (p < 0 || p >= n) return (uint16_t)C_OUT;
-  uint32_t b0 = bytes[p];
+  uint32_t b0 = raw[j];
   bool start = bmap_bit(sm.bmap, j);
   if ((b0 & 0xC0u) == 0x80u) return (uint16_t)(C_CONT | (start ? K_BAD : 0u));
   uint32_t code;
   int len = 1;
   bool bad = false;
   if (b0 < 0x80u) {
-    code = g_ascii.v[b0];
+    code = sm.ascii[b0];
   } else {
     uint32_t cp = 0;
     if (b0 >= 0xC2u && b0 <= 0xDFu) { len = 2; cp = b0 & 0x1Fu; }
@@ -122,9 +130,8 @@ __device__ __forceinline__ uint16_t decode_at(const uint8_t* __restrict__ bytes,
     else if (b0 >= 0xF0u && b0 <= 0xF4u) { len = 4; cp = b0 & 0x07u; }
     else { bad = true; }
     for (int k = 1; k < len && !bad; ++k) {
-      int64_t q = p + k;
-      if (q >= n || bmap_bit(sm.bmap, j + k)) { bad = true; break; }
-      uint32_t bk = bytes[q];
+      if (p + k >= n || bmap_bit(sm.bmap, j + k)) { bad = true; break; }
+      uint32_t bk = raw[j + k];
       if ((bk & 0xC0u) != 0x80u) { bad = true; break; }
       if (k == 1) {
         if ((b0 == 0xE0u && bk < 0xA0u) || (b0 == 0xEDu && bk > 0x9Fu) ||
@@ -149,24 +156,41 @@ __device__ __forceinline__ uint16_t decode_at(const uint8_t* __restrict__ bytes,
   // a continuation byte right after a complete char is stray
   int64_t e = p + len;
   bool last = e >= n || bmap_bit(sm.bmap, j + len);
-  if (!last && !bad && (bytes[e] & 0xC0u) == 0x80u) code |= K_BAD;
+  if (!last && !bad && (raw[j + len] & 0xC0u) == 0x80u) code |= K_BAD;
   code |= (uint32_t)(len - 1) << K_LEN_SHIFT;
   if (start) code |= K_SEQ_START;
   if (last) code |= K_SEQ_LAST;
   return (uint16_t)code;
 }
 
-// Stage the codes of positions [t0 - HALO, t0 + TILE + HALO) in LDS.
+// Stage the tile in LDS: raw bytes of [t0 - HALO, t0 + TILE + HALO + 16) with
+// one 16-byte load per thread (byte loads only at the text edges or for an
+// unaligned text), the sequence-boundary bitmap, the Unicode table if some byte
+// is non-ASCII, then the codes of positions [t0 - HALO, t0 + TILE + HALO).
 // Returns true if some char starting inside the tile is invalid UTF-8.
 __device__ bool load_tile(const uint8_t* __restrict__ bytes, int64_t n, const int64_t* __restrict__ offs,
                           int nseq, int64_t t0, TileSmem& sm) {
   const int tid = threadIdx.x;
   const int64_t base = t0 - HALO;
+  const bool aligned = (reinterpret_cast<uintptr_t>(bytes) & 15u) == 0;
   for (int i = tid; i < BMAP_WORDS; i += PT_THREADS) sm.bmap[i] = 0;
-  bool na = false;
-  for (int j = tid; j < SPAN; j += PT_THREADS) {
-    int64_t p = base + j;
-    if (p >= 0 && p < n && bytes[p] >= 0x80u) na = true;
+  for (int i = tid; i < 128; i += PT_THREADS) sm.ascii[i] = g_ascii.v[i];
+  uint32_t hi_bits = 0;
+  for (int i = tid; i < RAW_WORDS; i += PT_THREADS) {
+    const int64_t g = base + 16 * (int64_t)i;
+    uint4 v;
+    if (aligned && g >= 0 && g + 16 <= n) {
+      v = *reinterpret_cast<const uint4*>(bytes + g);
+    } else {
+      uint32_t wv[4] = {0u, 0u, 0u, 0u};
+      for (int k = 0; k < 16; ++k) {
+        const int64_t q = g + k;
+        if (q >= 0 && q < n) wv[k >> 2] |= (uint32_t)bytes[q] << (8 * (k & 3));
+      }
+      v = make_uint4(wv[0], wv[1], wv[2], wv[3]);
+    }
+    sm.raw[i] = v;
+    hi_bits |= v.x | v.y | v.z | v.w;
   }
   if (tid == 0) {
     if (offs) {
@@ -177,7 +201,7 @@ __device__ bool load_tile(const uint8_t* __restrict__ bytes, int64_t n, const in
       sm.seq_hi = 0;
     }
   }
-  na = __syncthreads_or(na);
+  const bool na = __syncthreads_or((hi_bits & 0x80808080u) != 0u);
   if (offs) {
     for (int64_t s = sm.seq_lo + tid; s < sm.seq_hi; s += PT_THREADS) {
       int64_t j = offs[s] - base;
@@ -194,8 +218,8 @@ __device__ bool load_tile(const uint8_t* __restrict__ bytes, int64_t n, const in
   __syncthreads();
   bool bad = false;
   for (int j = tid; j < SPAN; j += PT_THREADS) {
-    uint16_t c = decode_at(bytes, n, base, j, sm, na);
-    sm.code[j] = c;
+    uint16_t c = decode_at(n, base, j, sm, na);
+    sm.code[cix(j)] = c;
     if ((c & K_BAD) && j >= HALO && j < HALO + TILE) bad = true;
   }
   __syncthreads();
@@ -349,7 +373,7 @@ __device__ __forceinline__ uint32_t chunk_fwd(const TileSmem& sm) {
   const int j0 = HALO + PT_CHUNK * threadIdx.x;
 #pragma unroll
   for (int k = 0; k < PT_CHUNK; ++k) {
-    uint32_t c = sm.code[j0 + k];
+    uint32_t c = sm.code[cix(j0 + k)];
     if (is_char(c)) s = FwdOp::combine(s, FwdOp::elem(c));
   }
   return s;
@@ -360,7 +384,7 @@ __device__ __forceinline__ uint32_t chunk_bwd(const TileSmem& sm) {
   const int j0 = HALO + PT_CHUNK * threadIdx.x;
 #pragma unroll
   for (int k = PT_CHUNK - 1; k >= 0; --k) {
-    uint32_t c = sm.code[j0 + k];
+    uint32_t c = sm.code[cix(j0 + k)];
     if (is_char(c)) s = BwdOp::combine(BwdOp::elem(c), s);
   }
   return s;
@@ -425,35 +449,38 @@ __device__ void tile_carries(const Work& w, int t, int ntiles, TileSmem& sm) {
 
 // --------------------------------------------------------- boundary predicate
 
+// Code at tile position j of the padded LDS array.
+__device__ __forceinline__ uint32_t cat(const uint16_t* c, int j) { return c[cix(j)]; }
+
 // Previous char start before tile position j, or -1 at a sequence start.
 __device__ __forceinline__ int prev_char(const uint16_t* c, int j) {
-  if (c[j] & K_SEQ_START) return -1;
+  if (cat(c, j) & K_SEQ_START) return -1;
   int k = j - 1;
-  while (k > 0 && cls_of(c[k]) == C_CONT && k > j - 4) --k;
+  while (k > 0 && cls_of(cat(c, k)) == C_CONT && k > j - 4) --k;
   return k;
 }
 
 // The apostrophe at q starts a piece: it is a one-char "other" run that no
 // space in front of it absorbs.
 __device__ __forceinline__ bool ap_starts_piece(const uint16_t* c, int q) {
-  uint32_t cq = c[q];
+  uint32_t cq = cat(c, q);
   if (!(cq & K_AP)) return false;
   if (cq & K_SEQ_START) return true;
-  uint32_t cr = c[prev_char(c, q)];
+  uint32_t cr = cat(c, prev_char(c, q));
   return cls_of(cr) != C_O && !(cr & K_SP);
 }
 
 // Length (1 or 2) of a contraction suffix whose first letter is at a, or 0.
 template <int PAT>
 __device__ __forceinline__ int contraction_len(const uint16_t* c, int a) {
-  uint32_t ca = c[a];
+  uint32_t ca = cat(c, a);
   if (ca & K_SEQ_START) return 0;
   if (!ap_starts_piece(c, prev_char(c, a))) return 0;
   if (PAT == 0 && (ca & K_UPPER)) return 0;
   uint32_t lt = (ca >> K_LETTER_SHIFT) & 15u;
   if (lt == LT_S || lt == LT_T || lt == LT_M || lt == LT_D) return 1;
   if ((lt == LT_R || lt == LT_V || lt == LT_L) && !(ca & K_SEQ_LAST)) {
-    uint32_t c2 = c[a + 1];
+    uint32_t c2 = cat(c, a + 1);
     if (PAT == 0 && (c2 & K_UPPER)) return 0;
     uint32_t l2 = (c2 >> K_LETTER_SHIFT) & 15u;
     if ((lt == LT_R && l2 == LT_E) || (lt == LT_V && l2 == LT_E) || (lt == LT_L && l2 == LT_L)) return 2;
@@ -472,15 +499,15 @@ __device__ __forceinline__ bool after_contraction(const uint16_t* c, int j) {
 }
 
 __device__ __forceinline__ bool pred_gpt2(const uint16_t* c, int j) {
-  uint32_t c0 = c[j];
+  uint32_t c0 = cat(c, j);
   if (c0 & K_SEQ_START) return true;
   uint32_t k0 = cls_of(c0);
   int p1 = prev_char(c, j);
-  uint32_t c1 = c[p1], k1 = cls_of(c1);
+  uint32_t c1 = cat(c, p1), k1 = cls_of(c1);
   if (is_w(k0)) {
     if (!is_w(k1)) return true;
     if (c0 & K_SEQ_LAST) return false;
-    return !is_w(cls_of(c[j + clen(c0)]));
+    return !is_w(cls_of(cat(c, j + clen(c0))));
   }
   if (k1 == k0) return k0 == C_L && after_contraction<0>(c, j);
   if (c1 & K_SP) return false;
@@ -492,11 +519,11 @@ __device__ __forceinline__ bool pred_gpt2(const uint16_t* c, int j) {
 // ends_run: the whitespace run through this char is followed by no CR/LF.
 __device__ __forceinline__ bool pred_cl100k(const uint16_t* c, int j, uint32_t fwd_prev, uint32_t fwd_here,
                                             bool ends_run) {
-  uint32_t c0 = c[j];
+  uint32_t c0 = cat(c, j);
   if (c0 & K_SEQ_START) return true;
   uint32_t k0 = cls_of(c0);
   int p1 = prev_char(c, j);
-  uint32_t c1 = c[p1], k1 = cls_of(c1);
+  uint32_t c1 = cat(c, p1), k1 = cls_of(c1);
   switch (k0) {
     case C_N:
       return k1 != C_N || ((fwd_here >> 8) & 3u) == 1u;
@@ -505,7 +532,7 @@ __device__ __forceinline__ bool pred_cl100k(const uint16_t* c, int j, uint32_t f
       if (k1 == C_WS) return false;
       if (k1 == C_O) {
         if (c1 & K_SEQ_START) return false;
-        uint32_t c2 = c[prev_char(c, p1)];
+        uint32_t c2 = cat(c, prev_char(c, p1));
         return !(cls_of(c2) != C_O && !(c2 & K_SP));
       }
       return true;
@@ -519,7 +546,7 @@ __device__ __forceinline__ bool pred_cl100k(const uint16_t* c, int j, uint32_t f
       if (!is_w(k1)) return true;
       if (k1 == C_WN) return ends_run || ((fwd_prev >> 5) & 7u) == C_O;
       if (c0 & K_SEQ_LAST) return false;
-      return !is_w(cls_of(c[j + clen(c0)]));
+      return !is_w(cls_of(cat(c, j + clen(c0))));
   }
   return false;
 }
@@ -539,7 +566,7 @@ __global__ __launch_bounds__(PT_THREADS) void k_pretok(const uint8_t* __restrict
   if (PAT == 0) {
 #pragma unroll
     for (int k = 0; k < PT_CHUNK; ++k) {
-      uint32_t c = sm.code[j0 + k];
+      uint32_t c = sm.code[cix(j0 + k)];
       if (is_char(c) && pred_gpt2(sm.code, j0 + k)) bits |= 1u << k;
     }
   } else {
@@ -549,7 +576,7 @@ __global__ __launch_bounds__(PT_THREADS) void k_pretok(const uint8_t* __restrict
     uint32_t ends = 0;
 #pragma unroll
     for (int k = PT_CHUNK - 1; k >= 0; --k) {
-      uint32_t c = sm.code[j0 + k];
+      uint32_t c = sm.code[cix(j0 + k)];
       if (is_char(c)) {
         sb = BwdOp::combine(BwdOp::elem(c), sb);
         if (((sb >> 5) & 7u) != C_WN) ends |= 1u << k;
@@ -558,7 +585,7 @@ __global__ __launch_bounds__(PT_THREADS) void k_pretok(const uint8_t* __restrict
     uint32_t sf = FwdOp::combine(sm.carry_fwd, block_excl_fwd<FwdOp>(chunk_fwd(sm), sm.red, &tot));
 #pragma unroll
     for (int k = 0; k < PT_CHUNK; ++k) {
-      uint32_t c = sm.code[j0 + k];
+      uint32_t c = sm.code[cix(j0 + k)];
       if (is_char(c)) {
         uint32_t before = sf;
         sf = FwdOp::combine(sf, FwdOp::elem(c));
@@ -627,74 +654,174 @@ __device__ __forceinline__ uint32_t cache_lookup(const Tables& tb, uint64_t w0, 
   return RANK_NONE;
 }
 
-// Classic lowest-rank-first loop on one lane's piece held in LDS (element k
-// at I[k * BPE_THREADS]).  Returns the token count; tokens in I[0..count).
-__device__ int lane_bpe(uint32_t* I, uint32_t* R, int m, const Tables& tb) {
-  constexpr int S = BPE_THREADS;
-  for (int k = 0; k + 1 < m; ++k) R[k * S] = tb.byte_pair[(I[k * S] << 8) | I[(k + 1) * S]];
-  while (m > 1) {
-    uint32_t best = RANK_NONE;
-    int bk = -1;
-    for (int k = 0; k + 1 < m; ++k) {
-      uint32_t r = R[k * S];
-      if (r < best) { best = r; bk = k; }
-    }
-    if (bk < 0) break;
-    const uint32_t nid = 256u + best;
-    I[bk * S] = nid;
-    for (int k = bk + 1; k + 1 < m; ++k) I[k * S] = I[(k + 1) * S];
-    for (int k = bk + 1; k + 2 < m; ++k) R[k * S] = R[(k + 1) * S];
-    --m;
-    uint32_t rl = RANK_NONE, rr = RANK_NONE;
-    if (bk > 0) rl = pair_rank(tb, I[(bk - 1) * S], nid);
-    if (bk + 1 < m) rr = pair_rank(tb, nid, I[(bk + 1) * S]);
-    if (bk > 0) R[(bk - 1) * S] = rl;
-    if (bk + 1 < m) R[bk * S] = rr;
-  }
-  return m;
+// DPP move: each lane reads another lane's x (dpp_ctrl CTRL); lanes without a
+// source keep their own x.  Controls used: 0xB1 / 0x4E quad permutes (lane xor
+// 1 / xor 2), 0x141 half-row mirror, 0x140 row mirror, 0x130 wave shift (lane
+// i reads lane i + 1).
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_update_dpp((int)x, (int)x, CTRL, 0xF, 0xF, false);
 }
 
-// Short pieces (<= LANE_CAP bytes): one lane each; whole-piece lookup first.
-// Longer pieces are queued for k_bpe_long.
-__global__ __launch_bounds__(BPE_THREADS) void k_bpe_short(const uint8_t* __restrict__ bytes, Work w,
-                                                           Tables tb) {
-  __shared__ uint32_t s_ids[LANE_CAP * BPE_THREADS];
-  __shared__ uint32_t s_rk[LANE_CAP * BPE_THREADS];
-  uint32_t* I = s_ids + threadIdx.x;
-  uint32_t* R = s_rk + threadIdx.x;
+__device__ __forceinline__ uint32_t lane_up1(uint32_t x) { return dpp<0x130>(x); }
+
+// Minimum over each aligned group of G lanes (G = 8, 16, 32, 64): butterflies
+// inside a 16-lane row by DPP, then across rows by reading the row results.
+template <int G>
+__device__ __forceinline__ uint32_t group_min(uint32_t x) {
+  x = min(x, dpp<0xB1>(x));
+  x = min(x, dpp<0x4E>(x));
+  x = min(x, dpp<0x141>(x));
+  if (G >= 16) x = min(x, dpp<0x140>(x));
+  if (G == 32) {
+    const uint32_t r0 = (uint32_t)__builtin_amdgcn_readlane((int)x, 15), r1 = (uint32_t)__builtin_amdgcn_readlane((int)x, 31);
+    const uint32_t r2 = (uint32_t)__builtin_amdgcn_readlane((int)x, 47), r3 = (uint32_t)__builtin_amdgcn_readlane((int)x, 63);
+    x = ((threadIdx.x & 63u) < 32u) ? min(r0, r1) : min(r2, r3);
+  } else if (G == 64) {
+    const uint32_t r0 = (uint32_t)__builtin_amdgcn_readlane((int)x, 15), r1 = (uint32_t)__builtin_amdgcn_readlane((int)x, 31);
+    const uint32_t r2 = (uint32_t)__builtin_amdgcn_readlane((int)x, 47), r3 = (uint32_t)__builtin_amdgcn_readlane((int)x, 63);
+    x = min(min(r0, r1), min(r2, r3));
+  }
+  return x;
+}
+
+// Classic BPE of 64 / G pieces at once, one piece per aligned group of G
+// lanes and one byte position per lane (piece length <= G).  Each step takes
+// the group minimum of (rank << 6 | position) -- the lowest rank, leftmost
+// among equal pairs, exactly the classic choice -- merges that pair, shifts
+// the positions right of it one lane left, and the two lanes next to the new
+// token probe the pair-rank table (both probes in flight together).  The loop
+// runs while any group of the wavefront still has a merge (ballot: a
+// wave-uniform exit around the shuffles).  Tokens go to tmp_ids[s, s + cnt).
+template <int G>
+__device__ void group_bpe(const uint8_t* __restrict__ bytes, const Work& w, const Tables& tb,
+                          const uint32_t* queue, int qn, int chunk) {
+  const int lane = (int)(threadIdx.x & 63u);
+  const int g = lane & (G - 1);
+  const int qi = chunk * (64 / G) + lane / G;
+  const bool valid = qi < qn;
+  uint32_t p = 0;
+  int32_t s = 0;
+  int m = 0;
+  if (valid) {
+    p = queue[qi];
+    s = w.piece_start[p];
+    m = w.piece_start[p + 1] - s;
+  }
+  uint32_t id = (g < m) ? (uint32_t)bytes[s + g] : 0u;
+  const uint32_t nx = lane_up1(id);
+  uint32_t rk = (g + 1 < m) ? tb.byte_pair[(id << 8) | (nx & 255u)] : RANK_NONE;
+  for (;;) {
+    const uint32_t key = (g + 1 < m && rk != RANK_NONE) ? ((rk << 6) | (uint32_t)g) : 0xFFFFFFFFu;
+    const uint32_t kmin = group_min<G>(key);
+    const bool act = kmin != 0xFFFFFFFFu;
+    if (__ballot(act) == 0ull) break;
+    const int bk = (int)(kmin & 63u);
+    const uint32_t nid = 256u + (kmin >> 6);
+    const uint32_t id1 = lane_up1(id), id2 = lane_up1(id1), rk1 = lane_up1(rk);
+    const bool do_l = act && g == bk - 1;
+    const bool do_r = act && g == bk && bk + 2 < m;
+    uint32_t r = RANK_NONE;
+    if (do_l || do_r) r = pair_rank(tb, do_l ? id : nid, do_l ? nid : id2);
+    if (act) {
+      const uint32_t nid_here = (g < bk) ? id : ((g == bk) ? nid : id1);
+      rk = (g < bk - 1) ? rk : ((g == bk - 1 || g == bk) ? r : rk1);
+      id = nid_here;
+      --m;
+    }
+  }
+  if (valid) {
+    if (g < m) w.tmp_ids[s + g] = (int32_t)id;
+    if (g == 0) w.piece_cnt[p] = m;
+  }
+}
+
+constexpr int SHORT_THREADS = 256;
+constexpr int SHORT_WAVES = SHORT_THREADS / 64;
+constexpr int STAGE_BYTES = 8192;  // text bytes of a block's pieces staged in LDS
+
+// Pieces of up to LANE_CAP bytes, one per thread.  Single bytes and pieces
+// found in the single-token table finish at once; the rest are queued in LDS
+// by length class (<= 8, 16, 32, 64 bytes) and merged by group_bpe, each
+// wavefront of the block taking every fourth wave-load of each class.  Longer
+// pieces are queued for k_bpe_long.
+__global__ __launch_bounds__(SHORT_THREADS) void k_bpe_short(const uint8_t* __restrict__ bytes, int64_t n,
+                                                             Work w, Tables tb) {
+  __shared__ uint32_t q[4][SHORT_THREADS];
+  __shared__ int qn[4];
+  __shared__ uint4 stage[STAGE_BYTES / 16];
+  __shared__ int32_t st_lo, st_n;
   const uint32_t P = w.ctr[CTR_P];
-  for (uint32_t p = blockIdx.x * BPE_THREADS + threadIdx.x; p < P; p += gridDim.x * BPE_THREADS) {
+  const uint32_t p0 = blockIdx.x * SHORT_THREADS;
+  if (p0 >= P) return;
+  if (threadIdx.x < 4) qn[threadIdx.x] = 0;
+  if (threadIdx.x == 0) {
+    // the block's pieces cover one contiguous byte range; stage (a prefix of) it
+    const int32_t a = w.piece_start[p0];
+    const int32_t b = w.piece_start[min(P, p0 + SHORT_THREADS)];
+    const int32_t lo = a & ~15;
+    st_lo = lo;
+    st_n = min(b - lo, STAGE_BYTES);
+  }
+  __syncthreads();
+  const int32_t lo = st_lo, nst = st_n;
+  const bool aligned = (reinterpret_cast<uintptr_t>(bytes) & 15u) == 0;
+  for (int i = threadIdx.x; i * 16 < nst; i += SHORT_THREADS) {
+    const int64_t g = (int64_t)lo + 16 * i;
+    uint4 v;
+    if (aligned && g + 16 <= n) {
+      v = *reinterpret_cast<const uint4*>(bytes + g);
+    } else {
+      uint32_t wv[4] = {0u, 0u, 0u, 0u};
+      for (int k = 0; k < 16; ++k)
+        if (g + k < n) wv[k >> 2] |= (uint32_t)bytes[g + k] << (8 * (k & 3));
+      v = make_uint4(wv[0], wv[1], wv[2], wv[3]);
+    }
+    stage[i] = v;
+  }
+  __syncthreads();
+  const uint8_t* sb = reinterpret_cast<const uint8_t*>(stage);
+  const uint32_t p = p0 + threadIdx.x;
+  if (p < P) {
     const int32_t s = w.piece_start[p];
     const int32_t len = w.piece_start[p + 1] - s;
+    const bool in_stage = s - lo + len <= nst;
     if (len > LANE_CAP) {
-      uint32_t idx = atomicAdd(&w.ctr[CTR_NLONG], 1u);
-      w.long_list[idx] = (int32_t)p;
-      continue;
-    }
-    int cnt = 1;
-    if (len == 1) {
-      w.tmp_ids[s] = bytes[s];
+      w.long_list[atomicAdd(&w.ctr[CTR_NLONG], 1u)] = (int32_t)p;
+    } else if (len == 1) {
+      w.tmp_ids[s] = in_stage ? sb[s - lo] : bytes[s];
+      w.piece_cnt[p] = 1;
     } else {
-      uint64_t w0 = 0, w1 = 0;
+      uint32_t hit = RANK_NONE;
+      if (len <= CACHE_MAXLEN) {
+        uint64_t w0 = 0, w1 = 0;
 #pragma unroll
-      for (int k = 0; k < LANE_CAP; ++k) {
-        if (k < len) {
-          uint32_t b = bytes[s + k];
-          I[k * BPE_THREADS] = b;
-          if (k < 8) w0 |= (uint64_t)b << (8 * k);
-          else if (k < 16) w1 |= (uint64_t)b << (8 * (k - 8));
+        for (int k = 0; k < CACHE_MAXLEN; ++k) {
+          if (k < len) {
+            const uint64_t b = in_stage ? sb[s - lo + k] : bytes[s + k];
+            if (k < 8) w0 |= b << (8 * k);
+            else w1 |= b << (8 * (k - 8));
+          }
         }
+        hit = cache_lookup(tb, w0, w1, (uint32_t)len);
       }
-      uint32_t hit = len <= CACHE_MAXLEN ? cache_lookup(tb, w0, w1, (uint32_t)len) : RANK_NONE;
       if (hit != RANK_NONE) {
         w.tmp_ids[s] = (int32_t)hit;
+        w.piece_cnt[p] = 1;
       } else {
-        cnt = lane_bpe(I, R, len, tb);
-        for (int k = 0; k < cnt; ++k) w.tmp_ids[s + k] = (int32_t)I[k * BPE_THREADS];
+        const int cls = len <= 8 ? 0 : len <= 16 ? 1 : len <= 32 ? 2 : 3;
+        q[cls][atomicAdd(&qn[cls], 1)] = p;
       }
     }
-    w.piece_cnt[p] = cnt;
   }
+  __syncthreads();
+  const int wv = (int)uniform(threadIdx.x >> 6);
+  const int n8 = (int)uniform((uint32_t)qn[0]), n16 = (int)uniform((uint32_t)qn[1]);
+  const int n32 = (int)uniform((uint32_t)qn[2]), n64 = (int)uniform((uint32_t)qn[3]);
+  for (int c = wv; c * 8 < n8; c += SHORT_WAVES) group_bpe<8>(bytes, w, tb, q[0], n8, c);
+  for (int c = wv; c * 4 < n16; c += SHORT_WAVES) group_bpe<16>(bytes, w, tb, q[1], n16, c);
+  for (int c = wv; c * 2 < n32; c += SHORT_WAVES) group_bpe<32>(bytes, w, tb, q[2], n32, c);
+  for (int c = wv; c < n64; c += SHORT_WAVES) group_bpe<64>(bytes, w, tb, q[3], n64, c);
 }
 
 __device__ __forceinline__ uint32_t wave_min(uint32_t x) {
@@ -793,7 +920,8 @@ __global__ __launch_bounds__(EMIT_THREADS) void k_emit_sums(Work w) {
   if (threadIdx.x == 0) w.blk_sum[blockIdx.x] = s;
 }
 
-// Token offsets of every piece and the copy of each piece's tokens into the
+// Token offsets of every piece (one piece per thread: prefix of the earlier
+// blocks' sums plus a block scan) and the copy of each piece's tokens into the
 // output.  Pieces with more than HUGE_TOKENS tokens are copied by k_copy_huge.
 __global__ __launch_bounds__(EMIT_THREADS) void k_emit(Work w, int32_t* __restrict__ out_ids) {
   __shared__ uint32_t red[8];
@@ -803,37 +931,28 @@ __global__ __launch_bounds__(EMIT_THREADS) void k_emit(Work w, int32_t* __restri
   uint32_t s = 0;
   for (uint32_t b = threadIdx.x; b < blockIdx.x; b += EMIT_THREADS) s += w.blk_sum[b];
   const uint32_t base = block_sum(s, red);
-  const uint32_t q0 = p0 + threadIdx.x * EMIT_PER_THREAD;
-  uint32_t c[EMIT_PER_THREAD];
-  uint32_t mine = 0;
-#pragma unroll
-  for (int j = 0; j < EMIT_PER_THREAD; ++j) {
-    c[j] = (q0 + j < P) ? (uint32_t)w.piece_cnt[q0 + j] : 0u;
-    mine += c[j];
-  }
+  const uint32_t p = p0 + threadIdx.x;
+  const bool live = p < P;
+  const uint32_t c = live ? (uint32_t)w.piece_cnt[p] : 0u;
+  const uint32_t src = live ? (uint32_t)w.piece_start[p] : 0u;
   uint32_t tot;
-  uint32_t off = base + block_excl_sum(mine, red, &tot);
-  const int lane = threadIdx.x & 63;
+  const uint32_t off = base + block_excl_sum(c, red, &tot);
+  if (live) {
+    w.tok_off[p] = (int32_t)off;
+    if (c <= 8) {
 #pragma unroll
-  for (int j = 0; j < EMIT_PER_THREAD; ++j) {
-    const uint32_t p = q0 + j;
-    uint32_t src = 0;
-    if (p < P) {
-      w.tok_off[p] = (int32_t)off;
-      src = (uint32_t)w.piece_start[p];
-      if (c[j] <= 16) {
-        for (uint32_t k = 0; k < c[j]; ++k) out_ids[off + k] = w.tmp_ids[src + k];
-      }
+      for (uint32_t k = 0; k < 8; ++k)
+        if (k < c) out_ids[off + k] = w.tmp_ids[src + k];
     }
-    // medium pieces: the whole wavefront copies one piece at a time
-    uint64_t big = __ballot(p < P && c[j] > 16 && c[j] <= HUGE_TOKENS);
-    while (big) {
-      int l = __ffsll((unsigned long long)big) - 1;
-      big &= big - 1;
-      uint32_t cs = __shfl(src, l), co = __shfl(off, l), cc = __shfl(c[j], l);
-      for (uint32_t k = lane; k < cc; k += 64) out_ids[co + k] = w.tmp_ids[cs + k];
-    }
-    off += c[j];
+  }
+  // longer pieces: the whole wavefront copies one piece at a time
+  const int lane = (int)(threadIdx.x & 63u);
+  uint64_t big = __ballot(live && c > 8 && c <= (uint32_t)HUGE_TOKENS);
+  while (big) {
+    const int l = __ffsll((unsigned long long)big) - 1;
+    big &= big - 1;
+    const uint32_t cs = __shfl(src, l), co = __shfl(off, l), cc = __shfl(c, l);
+    for (uint32_t k = lane; k < cc; k += 64) out_ids[co + k] = w.tmp_ids[cs + k];
   }
   if (p0 + EMIT_PER_BLOCK >= P && threadIdx.x == 0) {
     w.tok_off[P] = (int32_t)(base + tot);
@@ -929,9 +1048,8 @@ hipError_t launch_pretokenize(const uint8_t* bytes, int64_t n, const int64_t* of
 hipError_t launch_bpe_emit(const uint8_t* bytes, int64_t n, const Tables& tb, const Work& w, int32_t* out_ids,
                            hipStream_t st) {
   const int max_pieces = (int)n;
-  int g_short = ceil_div(max_pieces, BPE_THREADS);
-  if (g_short > 4096) g_short = 4096;
-  hipLaunchKernelGGL(k_bpe_short, dim3(g_short), dim3(BPE_THREADS), 0, st, bytes, w, tb); prof_mark("k_bpe_short", st);
+  const int g_short = ceil_div(max_pieces, SHORT_THREADS);
+  hipLaunchKernelGGL(k_bpe_short, dim3(g_short), dim3(SHORT_THREADS), 0, st, bytes, n, w, tb); prof_mark("k_bpe_short", st);
   int g_long = ceil_div(n, LANE_CAP + 1);
   if (g_long > 2048) g_long = 2048;
   hipLaunchKernelGGL(k_bpe_long, dim3(g_long), dim3(64), 0, st, bytes, w, tb); prof_mark("k_bpe_long", st);

@@ -262,6 +262,18 @@ def test_bad_offsets_report_error():
         assert e.value.code == tt.TT_EOFFSETS
 
 
+def test_unaligned_input_pointer():
+    # the tile loader takes 16-byte loads only from a 16-byte aligned text
+    v = load("c2", GPT2)
+    data = mix_text(100_000, 78)
+    buf = dev(b"#" * 7 + data)
+    x = buf[7:]  # data_ptr is 7 bytes past an aligned allocation
+    assert x.data_ptr() % 16 != 0
+    assert np.array_equal(tt.encode(x).cpu().numpy(), np.asarray(oracle_encode(data, v, GPT2, {}), dtype=np.int32))
+    _, want = split_bytes(data, GPT2)
+    assert tt.pretokenize(x).cpu().numpy().tolist() == want
+
+
 def test_repeat_runs_are_identical():
     load("c2", GPT2)
     data = dev(mix_text(500_000, 77))
