@@ -129,6 +129,9 @@ size_t layout(int64_t n, char* base, Work* w) {
   t.blk_sum = (uint32_t*)take((nn / EMIT_PER_BLOCK + 2) * 4);
   t.long_list = (int32_t*)take((nn / (LANE_CAP + 1) + 2) * 4);
   t.huge_list = (int32_t*)take((nn / HUGE_TOKENS + 2) * 4);
+  // a class-c queue holds pieces of at least 2, 9, 17, 33 bytes
+  const size_t qmin[4] = {2, 9, 17, 33};
+  for (int c = 0; c < 4; ++c) t.queue[c] = (uint32_t*)take((nn / qmin[c] + 2) * 4);
   t.ctr = (uint32_t*)take(CTR_COUNT * 4);
   if (w) *w = t;
   return off;

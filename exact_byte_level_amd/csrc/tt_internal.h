@@ -80,7 +80,12 @@ struct Tables {
 };
 
 // Device workspace of one encode.
-enum : int { CTR_P = 0, CTR_NLONG = 1, CTR_ERR = 2, CTR_LONG_TICKET = 3, CTR_T = 4, CTR_NHUGE = 5, CTR_COUNT = 8 };
+enum : int {
+  CTR_P = 0, CTR_NLONG = 1, CTR_ERR = 2, CTR_LONG_TICKET = 3, CTR_T = 4, CTR_NHUGE = 5,
+  CTR_Q = 6,             // CTR_Q + c: pieces queued in class c (<= 8, 16, 32, 64 bytes)
+  CTR_TICKET = 10,       // next merge work item
+  CTR_COUNT = 16
+};
 enum : uint32_t { ERR_UTF8 = 1u, ERR_OFFSETS = 2u };
 
 struct Work {
@@ -96,6 +101,7 @@ struct Work {
   uint32_t* blk_sum;     // [n / EMIT_PER_BLOCK + 1]
   int32_t* long_list;    // [n / (LANE_CAP + 1) + 1] pieces longer than LANE_CAP bytes
   int32_t* huge_list;    // [n / HUGE_TOKENS + 1] pieces with more than HUGE_TOKENS tokens
+  uint32_t* queue[4];    // pieces for group BPE by class: <= 8 bytes [n/2], <= 16 [n/9], <= 32 [n/17], <= 64 [n/33]
   uint32_t* ctr;         // [CTR_COUNT]
 };
 

@@ -737,24 +737,21 @@ __device__ void group_bpe(const uint8_t* __restrict__ bytes, const Work& w, cons
 }
 
 constexpr int SHORT_THREADS = 256;
-constexpr int SHORT_WAVES = SHORT_THREADS / 64;
 constexpr int STAGE_BYTES = 8192;  // text bytes of a block's pieces staged in LDS
 
-// Pieces of up to LANE_CAP bytes, one per thread.  Single bytes and pieces
-// found in the single-token table finish at once; the rest are queued in LDS
-// by length class (<= 8, 16, 32, 64 bytes) and merged by group_bpe, each
-// wavefront of the block taking every fourth wave-load of each class.  Longer
-// pieces are queued for k_bpe_long.
-__global__ __launch_bounds__(SHORT_THREADS) void k_bpe_short(const uint8_t* __restrict__ bytes, int64_t n,
-                                                             Work w, Tables tb) {
-  __shared__ uint32_t q[4][SHORT_THREADS];
-  __shared__ int qn[4];
+// One thread per piece.  Single bytes and pieces found in the single-token
+// table finish here; pieces of up to LANE_CAP bytes go to the global queue of
+// their length class (<= 8, 16, 32, 64 bytes) for k_bpe_merge, longer ones to
+// the long list.  Queue slots are reserved with one atomic per class and block.
+__global__ __launch_bounds__(SHORT_THREADS) void k_bpe_classify(const uint8_t* __restrict__ bytes, int64_t n,
+                                                                Work w, Tables tb) {
   __shared__ uint4 stage[STAGE_BYTES / 16];
+  __shared__ uint32_t qn[5], qbase[5];
   __shared__ int32_t st_lo, st_n;
   const uint32_t P = w.ctr[CTR_P];
   const uint32_t p0 = blockIdx.x * SHORT_THREADS;
   if (p0 >= P) return;
-  if (threadIdx.x < 4) qn[threadIdx.x] = 0;
+  if (threadIdx.x < 5) qn[threadIdx.x] = 0;
   if (threadIdx.x == 0) {
     // the block's pieces cover one contiguous byte range; stage (a prefix of) it
     const int32_t a = w.piece_start[p0];
@@ -782,12 +779,14 @@ __global__ __launch_bounds__(SHORT_THREADS) void k_bpe_short(const uint8_t* __re
   __syncthreads();
   const uint8_t* sb = reinterpret_cast<const uint8_t*>(stage);
   const uint32_t p = p0 + threadIdx.x;
+  int cls = -1;
+  uint32_t slot = 0;
   if (p < P) {
     const int32_t s = w.piece_start[p];
     const int32_t len = w.piece_start[p + 1] - s;
     const bool in_stage = s - lo + len <= nst;
     if (len > LANE_CAP) {
-      w.long_list[atomicAdd(&w.ctr[CTR_NLONG], 1u)] = (int32_t)p;
+      cls = 4;
     } else if (len == 1) {
       w.tmp_ids[s] = in_stage ? sb[s - lo] : bytes[s];
       w.piece_cnt[p] = 1;
@@ -809,19 +808,47 @@ __global__ __launch_bounds__(SHORT_THREADS) void k_bpe_short(const uint8_t* __re
         w.tmp_ids[s] = (int32_t)hit;
         w.piece_cnt[p] = 1;
       } else {
-        const int cls = len <= 8 ? 0 : len <= 16 ? 1 : len <= 32 ? 2 : 3;
-        q[cls][atomicAdd(&qn[cls], 1)] = p;
+        cls = len <= 8 ? 0 : len <= 16 ? 1 : len <= 32 ? 2 : 3;
       }
     }
+    if (cls >= 0) slot = atomicAdd(&qn[cls], 1u);
   }
   __syncthreads();
-  const int wv = (int)uniform(threadIdx.x >> 6);
-  const int n8 = (int)uniform((uint32_t)qn[0]), n16 = (int)uniform((uint32_t)qn[1]);
-  const int n32 = (int)uniform((uint32_t)qn[2]), n64 = (int)uniform((uint32_t)qn[3]);
-  for (int c = wv; c * 8 < n8; c += SHORT_WAVES) group_bpe<8>(bytes, w, tb, q[0], n8, c);
-  for (int c = wv; c * 4 < n16; c += SHORT_WAVES) group_bpe<16>(bytes, w, tb, q[1], n16, c);
-  for (int c = wv; c * 2 < n32; c += SHORT_WAVES) group_bpe<32>(bytes, w, tb, q[2], n32, c);
-  for (int c = wv; c < n64; c += SHORT_WAVES) group_bpe<64>(bytes, w, tb, q[3], n64, c);
+  if (threadIdx.x < 5) {
+    const uint32_t c = qn[threadIdx.x];
+    qbase[threadIdx.x] = c ? atomicAdd(&w.ctr[threadIdx.x < 4 ? CTR_Q + threadIdx.x : CTR_NLONG], c) : 0u;
+  }
+  __syncthreads();
+  if (cls >= 0) {
+    uint32_t* q = cls < 4 ? w.queue[cls] : reinterpret_cast<uint32_t*>(w.long_list);
+    q[qbase[cls] + slot] = p;
+  }
+}
+
+// Group BPE of the queued pieces.  Work items are wavefront loads: one piece
+// of <= 64 bytes, two of <= 32, four of <= 16 or eight of <= 8, numbered
+// longest class first and dealt round-robin to the wavefronts of the grid, so
+// the longest merge chains start first and spread over the whole chip.  The
+// item index is the same in every lane, so the loop and the class branches
+// are scalar.
+constexpr int MERGE_THREADS = 256;
+__global__ __launch_bounds__(MERGE_THREADS) void k_bpe_merge(const uint8_t* __restrict__ bytes, Work w, Tables tb) {
+  const uint32_t n8 = w.ctr[CTR_Q + 0], n16 = w.ctr[CTR_Q + 1], n32 = w.ctr[CTR_Q + 2], n64 = w.ctr[CTR_Q + 3];
+  const uint32_t c64 = n64, c32 = (n32 + 1) / 2, c16 = (n16 + 3) / 4, c8 = (n8 + 7) / 8;
+  const uint32_t total = c64 + c32 + c16 + c8;
+  const uint32_t nwaves = gridDim.x * (MERGE_THREADS / 64);
+  for (uint32_t t = uniform(blockIdx.x * (MERGE_THREADS / 64) + (threadIdx.x >> 6)); t < total; t += nwaves) {
+    uint32_t u = t;
+    if (u < c64) {
+      group_bpe<64>(bytes, w, tb, w.queue[3], (int)n64, (int)u);
+    } else if ((u -= c64) < c32) {
+      group_bpe<32>(bytes, w, tb, w.queue[2], (int)n32, (int)u);
+    } else if ((u -= c32) < c16) {
+      group_bpe<16>(bytes, w, tb, w.queue[1], (int)n16, (int)u);
+    } else {
+      group_bpe<8>(bytes, w, tb, w.queue[0], (int)n8, (int)(u - c16));
+    }
+  }
 }
 
 __device__ __forceinline__ uint32_t wave_min(uint32_t x) {
@@ -1049,7 +1076,12 @@ hipError_t launch_bpe_emit(const uint8_t* bytes, int64_t n, const Tables& tb, co
                            hipStream_t st) {
   const int max_pieces = (int)n;
   const int g_short = ceil_div(max_pieces, SHORT_THREADS);
-  hipLaunchKernelGGL(k_bpe_short, dim3(g_short), dim3(SHORT_THREADS), 0, st, bytes, n, w, tb); prof_mark("k_bpe_short", st);
+  hipLaunchKernelGGL(k_bpe_classify, dim3(g_short), dim3(SHORT_THREADS), 0, st, bytes, n, w, tb);
+  prof_mark("k_bpe_classify", st);
+  // enough wavefronts to fill the chip; each one loops over work items
+  int g_merge = ceil_div(n, 256);
+  if (g_merge > 2048) g_merge = 2048;
+  hipLaunchKernelGGL(k_bpe_merge, dim3(g_merge), dim3(MERGE_THREADS), 0, st, bytes, w, tb); prof_mark("k_bpe_merge", st);
   int g_long = ceil_div(n, LANE_CAP + 1);
   if (g_long > 2048) g_long = 2048;
   hipLaunchKernelGGL(k_bpe_long, dim3(g_long), dim3(64), 0, st, bytes, w, tb); prof_mark("k_bpe_long", st);
