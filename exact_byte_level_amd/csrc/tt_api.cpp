@@ -126,9 +126,9 @@ size_t layout(int64_t n, char* base, Work* w) {
   t.tmp_ids = (int32_t*)take(nn * 4);
   t.tmp_rank = (uint32_t*)take(nn * 4);
   t.tok_off = (int32_t*)take((nn + 1) * 4);
-  t.blk_sum = (uint32_t*)take((nn / EMIT_PER_BLOCK + 2) * 4);
+  t.blk_sum = (uint32_t*)take((nn / EMIT_UNIT + 2) * 4);
   t.long_list = (int32_t*)take((nn / (LANE_CAP + 1) + 2) * 4);
-  t.huge_list = (int32_t*)take((nn / HUGE_TOKENS + 2) * 4);
+  t.huge_list = (int32_t*)take((nn / (HUGE_TOKENS + 1) + 2) * 4);
   // a class-c queue holds pieces of at least 2, 9, 17, 33 bytes
   const size_t qmin[4] = {2, 9, 17, 33};
   for (int c = 0; c < 4; ++c) t.queue[c] = (uint32_t*)take((nn / qmin[c] + 2) * 4);
@@ -324,9 +324,8 @@ int tt_encode(const uint8_t* dev_bytes, int64_t n, int32_t* out_ids, int64_t* ou
   if (n == 0) return launch_write_zeros(out_n, 1, stream) == hipSuccess ? TT_OK : TT_EHIP;
   if ((rc = ensure_workspace(n)) != TT_OK) return rc;
   prof_begin(stream);
-  if (launch_pretokenize(dev_bytes, n, nullptr, 1, g.pattern, g.w, g.w.piece_start, stream) != hipSuccess ||
-      launch_bpe_emit(dev_bytes, n, g.tb, g.w, out_ids, stream) != hipSuccess ||
-      launch_finish_count(g.w, CTR_T, out_n, stream) != hipSuccess)
+  if (launch_pretokenize(dev_bytes, n, nullptr, 1, g.pattern, g.w, g.w.piece_start, nullptr, stream) != hipSuccess ||
+      launch_bpe_emit(dev_bytes, n, g.tb, g.w, out_ids, out_n, stream) != hipSuccess)
     return TT_EHIP;
   return TT_OK;
 }
@@ -349,8 +348,9 @@ int tt_encode_batch(const uint8_t* dev_bytes, int64_t n, const int64_t* dev_offs
     return TT_OK;
   }
   prof_begin(stream);
-  if (launch_pretokenize(dev_bytes, n, dev_offsets, n_seqs, g.pattern, g.w, g.w.piece_start, stream) != hipSuccess ||
-      launch_bpe_emit(dev_bytes, n, g.tb, g.w, out_ids, stream) != hipSuccess ||
+  if (launch_pretokenize(dev_bytes, n, dev_offsets, n_seqs, g.pattern, g.w, g.w.piece_start, nullptr, stream) !=
+          hipSuccess ||
+      launch_bpe_emit(dev_bytes, n, g.tb, g.w, out_ids, nullptr, stream) != hipSuccess ||
       launch_batch_offsets(dev_offsets, n_seqs, n, g.w, out_offsets, stream) != hipSuccess)
     return TT_EHIP;
   return TT_OK;
@@ -374,8 +374,7 @@ int tt_pretokenize(const uint8_t* dev_bytes, int64_t n, const int64_t* dev_offse
     return TT_OK;
   }
   prof_begin(stream);
-  if (launch_pretokenize(dev_bytes, n, dev_offsets, nseq, g.pattern, g.w, out_starts, stream) != hipSuccess ||
-      launch_finish_count(g.w, CTR_P, out_np, stream) != hipSuccess)
+  if (launch_pretokenize(dev_bytes, n, dev_offsets, nseq, g.pattern, g.w, out_starts, out_np, stream) != hipSuccess)
     return TT_EHIP;
   return TT_OK;
 }

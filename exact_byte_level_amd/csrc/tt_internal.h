@@ -80,36 +80,43 @@ struct Tables {
 };
 
 // Device workspace of one encode.
+//
+// Counters: the last tile of the compaction pass writes P and the error bits
+// and zeroes the other per-call counters.
 enum : int {
-  CTR_P = 0, CTR_NLONG = 1, CTR_ERR = 2, CTR_LONG_TICKET = 3, CTR_T = 4, CTR_NHUGE = 5,
+  CTR_P = 0,             // pieces
+  CTR_NLONG = 1,         // pieces longer than LANE_CAP bytes (long_list)
+  CTR_ERR = 2,           // ERR_* bits
+  CTR_T = 4,             // tokens
+  CTR_NHUGE = 5,         // pieces with more than HUGE_TOKENS tokens (huge_list)
   CTR_Q = 6,             // CTR_Q + c: pieces queued in class c (<= 8, 16, 32, 64 bytes)
-  CTR_TICKET = 10,       // next merge work item
+  CTR_RESET_END = 12,    // counters [0, CTR_RESET_END) are per call
   CTR_COUNT = 16
 };
 enum : uint32_t { ERR_UTF8 = 1u, ERR_OFFSETS = 2u };
+constexpr int TILE_ERR_SHIFT = 30;     // tile_cnt[t] bits 30-31: ERR_* bits of tile t
 
 struct Work {
   uint32_t* tile_fwd;    // [ntiles] forward run summary of each tile
   uint32_t* tile_bwd;    // [ntiles] backward run summary
-  uint32_t* tile_cnt;    // [ntiles] pre-token starts in each tile
+  uint32_t* tile_cnt;    // [ntiles] pre-token starts of each tile | error bits << TILE_ERR_SHIFT
   uint16_t* flags;       // [ntiles * PT_THREADS] start bits of each thread's PT_CHUNK bytes
   int32_t* piece_start;  // [n + 1]
   int32_t* piece_cnt;    // [n] tokens of each piece
   int32_t* tmp_ids;      // [n] tokens of the piece starting at byte s live at [s, s + cnt)
-  uint32_t* tmp_rank;    // [n] pair ranks for the cooperative merge loop
-  int32_t* tok_off;      // [n + 1] exclusive prefix of piece_cnt
-  uint32_t* blk_sum;     // [n / EMIT_PER_BLOCK + 1]
+  uint32_t* tmp_rank;    // [n] pair ranks for the long-piece merge loop
+  int32_t* tok_off;      // [n + 1] token offset of each piece (first its offset inside its emission unit)
+  uint32_t* blk_sum;     // [n / EMIT_UNIT + 1] tokens of each emission unit
   int32_t* long_list;    // [n / (LANE_CAP + 1) + 1] pieces longer than LANE_CAP bytes
-  int32_t* huge_list;    // [n / HUGE_TOKENS + 1] pieces with more than HUGE_TOKENS tokens
+  int32_t* huge_list;    // [n / (HUGE_TOKENS + 1) + 1] pieces with more than HUGE_TOKENS tokens
   uint32_t* queue[4];    // pieces for group BPE by class: <= 8 bytes [n/2], <= 16 [n/9], <= 32 [n/17], <= 64 [n/33]
   uint32_t* ctr;         // [CTR_COUNT]
 };
 
 // ------------------------------------------------------------- BPE tiers
 constexpr int LANE_CAP = 64;            // pieces up to this many bytes: group BPE in one wavefront
-constexpr int EMIT_THREADS = 256;
-constexpr int EMIT_PER_THREAD = 1;
-constexpr int EMIT_PER_BLOCK = EMIT_THREADS * EMIT_PER_THREAD;
-constexpr int HUGE_TOKENS = 4096;       // pieces with more tokens are copied grid-wide
+constexpr int EMIT_UNIT = 256;          // pieces per emission unit (one workgroup pass)
+constexpr int HUGE_TOKENS = 64;         // pieces with more tokens are copied by the whole grid
+constexpr int GRID_CAP = 1024;          // workgroups of the grid-stride passes
 
 }  // namespace tt

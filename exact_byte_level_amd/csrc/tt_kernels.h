@@ -8,15 +8,17 @@ namespace tt {
 // is on, records a HIP event on `st` after the named kernel's launch.
 void prof_mark(const char* name, hipStream_t st);
 
-// Zero the counters, validate batch offsets (if any), and write the piece
-// starts (+ sentinel n) to `starts` and P to w.ctr[CTR_P].  n >= 1.
+// Pre-tokenize (validating the batch offsets, if any): piece starts (+
+// sentinel n) to `starts`, P and the error bits to w.ctr, the per-call
+// counters zeroed; *out_np = P or the error code if out_np is given.  n >= 1.
 hipError_t launch_pretokenize(const uint8_t* bytes, int64_t n, const int64_t* offs, int nseq, int pattern,
-                              const Work& w, int32_t* starts, hipStream_t st);
+                              const Work& w, int32_t* starts, int64_t* out_np, hipStream_t st);
 
 // BPE of every piece in w.piece_start, then token offsets and ids into out_ids;
-// the total goes to w.ctr[CTR_T].
+// the total goes to w.ctr[CTR_T] and, if out_n is given, T or the error code
+// to *out_n.
 hipError_t launch_bpe_emit(const uint8_t* bytes, int64_t n, const Tables& tb, const Work& w, int32_t* out_ids,
-                           hipStream_t st);
+                           int64_t* out_n, hipStream_t st);
 
 // *out = error code if any data error was flagged, else w.ctr[which].
 hipError_t launch_finish_count(const Work& w, int which, int64_t* out, hipStream_t st);

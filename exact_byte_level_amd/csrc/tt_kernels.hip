@@ -551,7 +551,36 @@ __device__ __forceinline__ bool pred_cl100k(const uint16_t* c, int j, uint32_t f
   return false;
 }
 
-// Pass 2: pre-token start bits of every byte of a tile, and the tile count.
+__device__ __forceinline__ int64_t err_code(uint32_t e) {
+  return (e & ERR_OFFSETS) ? -7 : (e & ERR_UTF8) ? -5 : 0;
+}
+
+// Sum over i < cnt of (a[i] & mask) by the whole workgroup of 256 threads:
+// coalesced, eight loads in flight per thread.  *hi gets the OR of this
+// thread's (a[i] & ~mask).
+__device__ uint32_t block_reduce(const uint32_t* __restrict__ a, int cnt, uint32_t mask, uint32_t* red,
+                                 uint32_t* hi) {
+  uint32_t sum = 0, orv = 0;
+  for (int c0 = 0; c0 < cnt; c0 += 256 * 8) {
+    uint32_t v[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int i = c0 + 256 * k + (int)threadIdx.x;
+      v[k] = i < cnt ? a[i] : 0u;
+    }
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      sum += v[k] & mask;
+      orv |= v[k] & ~mask;
+    }
+  }
+  *hi = orv;
+  return block_sum(sum, red);
+}
+
+// Pass 2: pre-token start bits of every byte of a tile and the tile count,
+// with the tile's error bits (invalid UTF-8; for a batch, the validity of a
+// share of the offsets) above TILE_ERR_SHIFT.
 template <int PAT>
 __global__ __launch_bounds__(PT_THREADS) void k_pretok(const uint8_t* __restrict__ bytes, int64_t n,
                                                        const int64_t* __restrict__ offs, int nseq, int ntiles,
@@ -559,8 +588,14 @@ __global__ __launch_bounds__(PT_THREADS) void k_pretok(const uint8_t* __restrict
   __shared__ TileSmem sm;
   const int t = blockIdx.x;
   const int64_t t0 = (int64_t)t * TILE;
-  bool bad = load_tile(bytes, n, offs, nseq, t0, sm);
-  if (bad) atomicOr(&w.ctr[CTR_ERR], ERR_UTF8);
+  const bool bad = load_tile(bytes, n, offs, nseq, t0, sm);
+  bool bad_off = false;
+  if (offs) {
+    for (int64_t q = (int64_t)t * PT_THREADS + threadIdx.x; q <= nseq; q += (int64_t)ntiles * PT_THREADS) {
+      const int64_t o = offs[q];
+      bad_off |= (q == 0 && o != 0) || (q == nseq && o != n) || o < 0 || o > n || (q < nseq && offs[q + 1] < o);
+    }
+  }
   const int j0 = HALO + PT_CHUNK * threadIdx.x;
   uint32_t bits = 0;
   if (PAT == 0) {
@@ -594,17 +629,25 @@ __global__ __launch_bounds__(PT_THREADS) void k_pretok(const uint8_t* __restrict
     }
   }
   w.flags[(int64_t)t * PT_THREADS + threadIdx.x] = (uint16_t)bits;
-  uint32_t cnt = block_sum(__popc(bits), sm.red);
-  if (threadIdx.x == 0) w.tile_cnt[t] = cnt;
+  const uint32_t cnt = block_sum(__popc(bits), sm.red);
+  const uint32_t err = (__syncthreads_or(bad) ? ERR_UTF8 : 0u) | (__syncthreads_or(bad_off) ? ERR_OFFSETS : 0u);
+  if (threadIdx.x == 0) w.tile_cnt[t] = cnt | (err << TILE_ERR_SHIFT);
 }
 
-// Pass 3: piece starts in order, by prefix sums of the start bits.
-__global__ __launch_bounds__(PT_THREADS) void k_compact(Work w, int ntiles, int64_t n, int32_t* __restrict__ starts) {
+// Pass 3: piece starts in order, from the counts of the tiles before and a
+// block scan of the start bits.  The last tile adds the sentinel n, sets P
+// and the error bits, zeroes the other per-call counters and, for a bare
+// pre-tokenization, writes P (or the error code) to *out_np.
+__global__ __launch_bounds__(PT_THREADS) void k_compact(Work w, int ntiles, int64_t n, int32_t* __restrict__ starts,
+                                                        int64_t* __restrict__ out_np) {
   __shared__ uint32_t red[8];
   const int t = blockIdx.x;
-  uint32_t s = 0;
-  for (int i = threadIdx.x; i < t; i += PT_THREADS) s += w.tile_cnt[i];
-  uint32_t base = block_sum(s, red);
+  const uint32_t cmask = (1u << TILE_ERR_SHIFT) - 1u;
+  const bool last = t == ntiles - 1;
+  uint32_t hi;
+  // the last tile also folds its own count and error bits into the totals
+  const uint32_t base = block_reduce(w.tile_cnt, last ? t + 1 : t, cmask, red, &hi) -
+                        (last ? (w.tile_cnt[t] & cmask) : 0u);
   uint32_t bits = w.flags[(int64_t)t * PT_THREADS + threadIdx.x];
   uint32_t tot;
   uint32_t pos = base + block_excl_sum(__popc(bits), red, &tot);
@@ -614,9 +657,15 @@ __global__ __launch_bounds__(PT_THREADS) void k_compact(Work w, int ntiles, int6
     bits &= bits - 1;
     starts[pos++] = (int32_t)(p0 + k);
   }
-  if (t == ntiles - 1 && threadIdx.x == 0) {
-    starts[base + tot] = (int32_t)n;
-    w.ctr[CTR_P] = base + tot;
+  if (last) {
+    const uint32_t e = (__syncthreads_or(hi & (ERR_UTF8 << TILE_ERR_SHIFT)) ? ERR_UTF8 : 0u) |
+                       (__syncthreads_or(hi & (ERR_OFFSETS << TILE_ERR_SHIFT)) ? ERR_OFFSETS : 0u);
+    const uint32_t P = base + tot;
+    if (threadIdx.x < CTR_RESET_END) w.ctr[threadIdx.x] = threadIdx.x == CTR_P ? P : threadIdx.x == CTR_ERR ? e : 0u;
+    if (threadIdx.x == 0) {
+      starts[P] = (int32_t)n;
+      if (out_np) *out_np = e ? err_code(e) : (int64_t)P;
+    }
   }
 }
 
@@ -737,117 +786,93 @@ __device__ void group_bpe(const uint8_t* __restrict__ bytes, const Work& w, cons
 }
 
 constexpr int SHORT_THREADS = 256;
-constexpr int STAGE_BYTES = 8192;  // text bytes of a block's pieces staged in LDS
+constexpr int STAGE_BYTES = 8192;  // text bytes of a unit's pieces staged in LDS
 
-// One thread per piece.  Single bytes and pieces found in the single-token
-// table finish here; pieces of up to LANE_CAP bytes go to the global queue of
-// their length class (<= 8, 16, 32, 64 bytes) for k_bpe_merge, longer ones to
-// the long list.  Queue slots are reserved with one atomic per class and block.
+// Pass 4: one thread per piece, 256 pieces per workgroup pass.  Single bytes
+// and pieces found in the single-token table finish here; pieces of up to
+// LANE_CAP bytes go to the global queue of their length class (<= 8, 16, 32,
+// 64 bytes) for k_bpe_merge, longer ones to the long list.  Queue slots are
+// reserved with one atomic per class and pass.
 __global__ __launch_bounds__(SHORT_THREADS) void k_bpe_classify(const uint8_t* __restrict__ bytes, int64_t n,
                                                                 Work w, Tables tb) {
   __shared__ uint4 stage[STAGE_BYTES / 16];
   __shared__ uint32_t qn[5], qbase[5];
   __shared__ int32_t st_lo, st_n;
   const uint32_t P = w.ctr[CTR_P];
-  const uint32_t p0 = blockIdx.x * SHORT_THREADS;
-  if (p0 >= P) return;
-  if (threadIdx.x < 5) qn[threadIdx.x] = 0;
-  if (threadIdx.x == 0) {
-    // the block's pieces cover one contiguous byte range; stage (a prefix of) it
-    const int32_t a = w.piece_start[p0];
-    const int32_t b = w.piece_start[min(P, p0 + SHORT_THREADS)];
-    const int32_t lo = a & ~15;
-    st_lo = lo;
-    st_n = min(b - lo, STAGE_BYTES);
-  }
-  __syncthreads();
-  const int32_t lo = st_lo, nst = st_n;
   const bool aligned = (reinterpret_cast<uintptr_t>(bytes) & 15u) == 0;
-  for (int i = threadIdx.x; i * 16 < nst; i += SHORT_THREADS) {
-    const int64_t g = (int64_t)lo + 16 * i;
-    uint4 v;
-    if (aligned && g + 16 <= n) {
-      v = *reinterpret_cast<const uint4*>(bytes + g);
-    } else {
-      uint32_t wv[4] = {0u, 0u, 0u, 0u};
-      for (int k = 0; k < 16; ++k)
-        if (g + k < n) wv[k >> 2] |= (uint32_t)bytes[g + k] << (8 * (k & 3));
-      v = make_uint4(wv[0], wv[1], wv[2], wv[3]);
-    }
-    stage[i] = v;
-  }
-  __syncthreads();
   const uint8_t* sb = reinterpret_cast<const uint8_t*>(stage);
-  const uint32_t p = p0 + threadIdx.x;
-  int cls = -1;
-  uint32_t slot = 0;
-  if (p < P) {
-    const int32_t s = w.piece_start[p];
-    const int32_t len = w.piece_start[p + 1] - s;
-    const bool in_stage = s - lo + len <= nst;
-    if (len > LANE_CAP) {
-      cls = 4;
-    } else if (len == 1) {
-      w.tmp_ids[s] = in_stage ? sb[s - lo] : bytes[s];
-      w.piece_cnt[p] = 1;
-    } else {
-      uint32_t hit = RANK_NONE;
-      if (len <= CACHE_MAXLEN) {
-        uint64_t w0 = 0, w1 = 0;
-#pragma unroll
-        for (int k = 0; k < CACHE_MAXLEN; ++k) {
-          if (k < len) {
-            const uint64_t b = in_stage ? sb[s - lo + k] : bytes[s + k];
-            if (k < 8) w0 |= b << (8 * k);
-            else w1 |= b << (8 * (k - 8));
-          }
-        }
-        hit = cache_lookup(tb, w0, w1, (uint32_t)len);
+  for (uint32_t p0 = blockIdx.x * SHORT_THREADS; p0 < P; p0 += gridDim.x * SHORT_THREADS) {
+    if (threadIdx.x < 5) qn[threadIdx.x] = 0;
+    if (threadIdx.x == 0) {
+      // the pass's pieces cover one contiguous byte range; stage (a prefix of) it
+      const int32_t a = w.piece_start[p0];
+      const int32_t b = w.piece_start[min(P, p0 + SHORT_THREADS)];
+      const int32_t lo = a & ~15;
+      st_lo = lo;
+      st_n = min(b - lo, STAGE_BYTES);
+    }
+    __syncthreads();
+    const int32_t lo = st_lo, nst = st_n;
+    for (int i = threadIdx.x; i * 16 < nst; i += SHORT_THREADS) {
+      const int64_t g = (int64_t)lo + 16 * i;
+      uint4 v;
+      if (aligned && g + 16 <= n) {
+        v = *reinterpret_cast<const uint4*>(bytes + g);
+      } else {
+        uint32_t wv[4] = {0u, 0u, 0u, 0u};
+        for (int k = 0; k < 16; ++k)
+          if (g + k < n) wv[k >> 2] |= (uint32_t)bytes[g + k] << (8 * (k & 3));
+        v = make_uint4(wv[0], wv[1], wv[2], wv[3]);
       }
-      if (hit != RANK_NONE) {
-        w.tmp_ids[s] = (int32_t)hit;
+      stage[i] = v;
+    }
+    __syncthreads();
+    const uint32_t p = p0 + threadIdx.x;
+    int cls = -1;
+    uint32_t slot = 0;
+    if (p < P) {
+      const int32_t s = w.piece_start[p];
+      const int32_t len = w.piece_start[p + 1] - s;
+      const bool in_stage = s - lo + len <= nst;
+      if (len > LANE_CAP) {
+        cls = 4;
+      } else if (len == 1) {
+        w.tmp_ids[s] = in_stage ? sb[s - lo] : bytes[s];
         w.piece_cnt[p] = 1;
       } else {
-        cls = len <= 8 ? 0 : len <= 16 ? 1 : len <= 32 ? 2 : 3;
+        uint32_t hit = RANK_NONE;
+        if (len <= CACHE_MAXLEN) {
+          uint64_t w0 = 0, w1 = 0;
+#pragma unroll
+          for (int k = 0; k < CACHE_MAXLEN; ++k) {
+            if (k < len) {
+              const uint64_t b = in_stage ? sb[s - lo + k] : bytes[s + k];
+              if (k < 8) w0 |= b << (8 * k);
+              else w1 |= b << (8 * (k - 8));
+            }
+          }
+          hit = cache_lookup(tb, w0, w1, (uint32_t)len);
+        }
+        if (hit != RANK_NONE) {
+          w.tmp_ids[s] = (int32_t)hit;
+          w.piece_cnt[p] = 1;
+        } else {
+          cls = len <= 8 ? 0 : len <= 16 ? 1 : len <= 32 ? 2 : 3;
+        }
       }
+      if (cls >= 0) slot = atomicAdd(&qn[cls], 1u);
     }
-    if (cls >= 0) slot = atomicAdd(&qn[cls], 1u);
-  }
-  __syncthreads();
-  if (threadIdx.x < 5) {
-    const uint32_t c = qn[threadIdx.x];
-    qbase[threadIdx.x] = c ? atomicAdd(&w.ctr[threadIdx.x < 4 ? CTR_Q + threadIdx.x : CTR_NLONG], c) : 0u;
-  }
-  __syncthreads();
-  if (cls >= 0) {
-    uint32_t* q = cls < 4 ? w.queue[cls] : reinterpret_cast<uint32_t*>(w.long_list);
-    q[qbase[cls] + slot] = p;
-  }
-}
-
-// Group BPE of the queued pieces.  Work items are wavefront loads: one piece
-// of <= 64 bytes, two of <= 32, four of <= 16 or eight of <= 8, numbered
-// longest class first and dealt round-robin to the wavefronts of the grid, so
-// the longest merge chains start first and spread over the whole chip.  The
-// item index is the same in every lane, so the loop and the class branches
-// are scalar.
-constexpr int MERGE_THREADS = 256;
-__global__ __launch_bounds__(MERGE_THREADS) void k_bpe_merge(const uint8_t* __restrict__ bytes, Work w, Tables tb) {
-  const uint32_t n8 = w.ctr[CTR_Q + 0], n16 = w.ctr[CTR_Q + 1], n32 = w.ctr[CTR_Q + 2], n64 = w.ctr[CTR_Q + 3];
-  const uint32_t c64 = n64, c32 = (n32 + 1) / 2, c16 = (n16 + 3) / 4, c8 = (n8 + 7) / 8;
-  const uint32_t total = c64 + c32 + c16 + c8;
-  const uint32_t nwaves = gridDim.x * (MERGE_THREADS / 64);
-  for (uint32_t t = uniform(blockIdx.x * (MERGE_THREADS / 64) + (threadIdx.x >> 6)); t < total; t += nwaves) {
-    uint32_t u = t;
-    if (u < c64) {
-      group_bpe<64>(bytes, w, tb, w.queue[3], (int)n64, (int)u);
-    } else if ((u -= c64) < c32) {
-      group_bpe<32>(bytes, w, tb, w.queue[2], (int)n32, (int)u);
-    } else if ((u -= c32) < c16) {
-      group_bpe<16>(bytes, w, tb, w.queue[1], (int)n16, (int)u);
-    } else {
-      group_bpe<8>(bytes, w, tb, w.queue[0], (int)n8, (int)(u - c16));
+    __syncthreads();
+    if (threadIdx.x < 5) {
+      const uint32_t c = qn[threadIdx.x];
+      qbase[threadIdx.x] = c ? atomicAdd(&w.ctr[threadIdx.x < 4 ? CTR_Q + threadIdx.x : CTR_NLONG], c) : 0u;
     }
+    __syncthreads();
+    if (cls >= 0) {
+      uint32_t* q = cls < 4 ? w.queue[cls] : reinterpret_cast<uint32_t*>(w.long_list);
+      q[qbase[cls] + slot] = p;
+    }
+    __syncthreads();
   }
 }
 
@@ -871,131 +896,186 @@ __device__ __forceinline__ uint64_t alt_mask(uint64_t eq, uint64_t cin) {
   return (fe & E) | (fo & ~E);
 }
 
-// Long pieces: one wavefront per piece, exact global-minimum rounds.  Each
-// round finds the lowest rank present, merges every occurrence of that pair
-// (alternating inside runs of equal pairs), compacts in place and recomputes
-// the pair ranks.  In a consistent table a merge only creates pairs of higher
-// rank, so this equals the classic loop.  Ids and ranks live in the piece's
-// own slice of tmp_ids / tmp_rank.
-__global__ __launch_bounds__(64) void k_bpe_long(const uint8_t* __restrict__ bytes, Work w, Tables tb) {
-  const int lane = threadIdx.x;
+// A piece longer than LANE_CAP bytes, by one wavefront: exact global-minimum
+// rounds.  Each round takes the lowest rank r present, merges every
+// occurrence of that pair (alternating inside runs of equal pairs), compacts
+// the ids in place and, in the same sweep, carries the rank of every pair that
+// did not change and looks up the ranks of the pairs next to a new token.  In
+// a consistent table a pair that contains the new token 256 + r ranks above
+// r, so this equals the classic loop.  Ids and ranks live in the piece's own
+// slice of tmp_ids / tmp_rank.
+__device__ void long_bpe(const uint8_t* __restrict__ bytes, const Work& w, const Tables& tb, uint32_t p) {
+  const int lane = (int)(threadIdx.x & 63u);
   const uint64_t lt_mask = (1ull << lane) - 1ull;
-  const uint32_t nlong = w.ctr[CTR_NLONG];
-  // static assignment: wavefront b takes long pieces b, b + grid, ... (the
-  // index, the piece and its length are wave-uniform)
-  for (uint32_t i = blockIdx.x; i < nlong; i += gridDim.x) {
-    const uint32_t p = uniform((uint32_t)w.long_list[i]);
-    const int32_t s = (int32_t)uniform((uint32_t)w.piece_start[p]);
-    int m = (int)uniform((uint32_t)(w.piece_start[p + 1] - s));
-    uint32_t* I = reinterpret_cast<uint32_t*>(w.tmp_ids) + s;
-    uint32_t* R = w.tmp_rank + s;
-    uint32_t rmin = RANK_NONE;
-    for (int k = lane; k < m; k += 64) {
-      uint32_t b = bytes[s + k];
+  const int32_t s = (int32_t)uniform((uint32_t)w.piece_start[p]);
+  int m = (int)uniform((uint32_t)(w.piece_start[p + 1] - s));
+  uint32_t* I = reinterpret_cast<uint32_t*>(w.tmp_ids) + s;
+  uint32_t* R = w.tmp_rank + s;
+  uint32_t rmin = RANK_NONE;
+  for (int base = 0; base < m; base += 64) {
+    const int k = base + lane;
+    if (k < m) {
+      const uint32_t b = bytes[s + k];
       I[k] = b;
-      if (k + 1 < m) {
-        uint32_t r = tb.byte_pair[(b << 8) | bytes[s + k + 1]];
-        R[k] = r;
-        rmin = min(rmin, r);
-      }
+      const uint32_t r = k + 1 < m ? tb.byte_pair[(b << 8) | bytes[s + k + 1]] : RANK_NONE;
+      R[k] = r;
+      rmin = min(rmin, r);
     }
-    rmin = uniform(wave_min(rmin));
-    __syncthreads();
-    while (rmin != RANK_NONE) {
-      uint64_t cin = 0;
-      int out = 0;
-      for (int base = 0; base < m; base += 64) {
-        const int k = base + lane;
-        const uint32_t id = k < m ? I[k] : 0u;
-        const uint32_t r = k + 1 < m ? R[k] : RANK_NONE;
-        const uint64_t eq = __ballot(r == rmin);
-        const uint64_t ms = alt_mask(eq, cin);
-        const uint64_t valid = (m - base >= 64) ? ~0ull : ((1ull << (m - base)) - 1ull);
-        const uint64_t keep = valid & ~((ms << 1) | cin);
-        if ((keep >> lane) & 1ull) I[out + __popcll(keep & lt_mask)] = ((ms >> lane) & 1ull) ? 256u + rmin : id;
-        out += __popcll(keep);
-        cin = ms >> 63;
+  }
+  rmin = uniform(wave_min(rmin));
+  __threadfence_block();
+  while (rmin != RANK_NONE) {
+    const uint32_t T = 256u + rmin;
+    uint64_t cin = 0;
+    uint32_t nmin = RANK_NONE;
+    int out = 0;
+    for (int base = 0; base < m; base += 64) {
+      const int k = base + lane;
+      const uint32_t id0 = k < m ? I[k] : 0u, id1 = k + 1 < m ? I[k + 1] : 0u, id2 = k + 2 < m ? I[k + 2] : 0u;
+      const uint32_t r0 = k + 1 < m ? R[k] : RANK_NONE;
+      const uint32_t r1 = k + 2 < m ? R[k + 1] : RANK_NONE;
+      const uint32_t r2 = k + 3 < m ? R[k + 2] : RANK_NONE;
+      const uint64_t ms = alt_mask(__ballot(r0 == rmin), cin);
+      const bool m0 = (ms >> lane) & 1ull;
+      const bool prev = lane ? ((ms >> (lane - 1)) & 1ull) : (cin != 0);
+      const bool m1 = r1 == rmin && !m0;   // merge starts at k + 1
+      const bool m2 = r2 == rmin && !m1;   // merge starts at k + 2
+      const bool keep = k < m && !prev;    // the right half of a merge drops out
+      const uint32_t nid = m0 ? T : id0;
+      // the next surviving token: k + 2 after a merge at k, else k + 1
+      const bool has_next = m0 ? (k + 2 < m) : (k + 1 < m);
+      const uint32_t nxt = m0 ? (m2 ? T : id2) : (m1 ? T : id1);
+      uint32_t nr = RANK_NONE;
+      if (keep && has_next) nr = (m0 || m1) ? pair_rank(tb, nid, nxt) : r0;
+      const uint64_t km = __ballot(keep);
+      if (keep) {
+        const int o = out + __popcll(km & lt_mask);
+        I[o] = nid;
+        R[o] = nr;
       }
-      m = (int)uniform((uint32_t)out);
-      __syncthreads();
-      rmin = RANK_NONE;
-      for (int k = lane; k + 1 < m; k += 64) {
-        uint32_t r = pair_rank(tb, I[k], I[k + 1]);
-        R[k] = r;
-        rmin = min(rmin, r);
-      }
-      rmin = uniform(wave_min(rmin));
-      __syncthreads();
+      nmin = min(nmin, nr);
+      out += __popcll(km);
+      cin = ms >> 63;
     }
-    if (lane == 0) {
-      w.piece_cnt[p] = m;
-      if (m > HUGE_TOKENS) w.huge_list[atomicAdd(&w.ctr[CTR_NHUGE], 1u)] = (int32_t)p;
+    m = (int)uniform((uint32_t)out);
+    rmin = uniform(wave_min(nmin));
+    __threadfence_block();
+  }
+  if (lane == 0) {
+    w.piece_cnt[p] = m;
+    if (m > HUGE_TOKENS) w.huge_list[atomicAdd(&w.ctr[CTR_NHUGE], 1u)] = (int32_t)p;
+  }
+}
+
+// Pass 5: BPE of the queued pieces.  Work items are wavefront loads: one long
+// piece, one piece of <= 64 bytes, two of <= 32, four of <= 16 or eight of
+// <= 8, numbered longest class first and dealt round-robin to the wavefronts
+// of the grid, so the longest merge chains start first and spread over the
+// whole chip.  The item index is the same in every lane, so the loop and the
+// class branches are scalar.
+constexpr int MERGE_THREADS = 256;
+__global__ __launch_bounds__(MERGE_THREADS) void k_bpe_merge(const uint8_t* __restrict__ bytes, Work w, Tables tb) {
+  const uint32_t nl = w.ctr[CTR_NLONG];
+  const uint32_t n8 = w.ctr[CTR_Q + 0], n16 = w.ctr[CTR_Q + 1], n32 = w.ctr[CTR_Q + 2], n64 = w.ctr[CTR_Q + 3];
+  const uint32_t c64 = n64, c32 = (n32 + 1) / 2, c16 = (n16 + 3) / 4, c8 = (n8 + 7) / 8;
+  const uint32_t total = nl + c64 + c32 + c16 + c8;
+  const uint32_t nwaves = gridDim.x * (MERGE_THREADS / 64);
+  for (uint32_t t = uniform(blockIdx.x * (MERGE_THREADS / 64) + (threadIdx.x >> 6)); t < total; t += nwaves) {
+    uint32_t u = t;
+    if (u < nl) {
+      long_bpe(bytes, w, tb, uniform((uint32_t)w.long_list[u]));
+    } else if ((u -= nl) < c64) {
+      group_bpe<64>(bytes, w, tb, w.queue[3], (int)n64, (int)u);
+    } else if ((u -= c64) < c32) {
+      group_bpe<32>(bytes, w, tb, w.queue[2], (int)n32, (int)u);
+    } else if ((u -= c32) < c16) {
+      group_bpe<16>(bytes, w, tb, w.queue[1], (int)n16, (int)u);
+    } else {
+      group_bpe<8>(bytes, w, tb, w.queue[0], (int)n8, (int)(u - c16));
     }
   }
 }
 
 // ------------------------------------------------------------------ emission
 
-__global__ __launch_bounds__(EMIT_THREADS) void k_emit_sums(Work w) {
+// Pass 6: token count of each emission unit of 256 pieces, and each piece's
+// token offset inside its unit (in tok_off).
+__global__ __launch_bounds__(EMIT_UNIT) void k_emit_sums(Work w) {
   __shared__ uint32_t red[8];
   const uint32_t P = w.ctr[CTR_P];
-  const uint32_t p0 = blockIdx.x * EMIT_PER_BLOCK;
-  if (p0 >= P) return;
-  uint32_t s = 0;
-  for (uint32_t p = p0 + threadIdx.x; p < min(P, p0 + EMIT_PER_BLOCK); p += EMIT_THREADS) s += w.piece_cnt[p];
-  s = block_sum(s, red);
-  if (threadIdx.x == 0) w.blk_sum[blockIdx.x] = s;
+  for (uint32_t u = blockIdx.x; u * EMIT_UNIT < P; u += gridDim.x) {
+    const uint32_t p = u * EMIT_UNIT + threadIdx.x;
+    const uint32_t c = p < P ? (uint32_t)w.piece_cnt[p] : 0u;
+    uint32_t tot;
+    const uint32_t e = block_excl_sum(c, red, &tot);
+    if (p < P) w.tok_off[p] = (int32_t)e;
+    if (threadIdx.x == 0) w.blk_sum[u] = tot;
+  }
 }
 
-// Token offsets of every piece (one piece per thread: prefix of the earlier
-// blocks' sums plus a block scan) and the copy of each piece's tokens into the
-// output.  Pieces with more than HUGE_TOKENS tokens are copied by k_copy_huge.
-__global__ __launch_bounds__(EMIT_THREADS) void k_emit(Work w, int32_t* __restrict__ out_ids) {
+constexpr uint32_t HUGE_CHUNK = 16384;  // tokens per grid work item of a huge piece
+
+// Pass 7: final token offsets (the counts of the earlier units plus the
+// offset inside the unit) and the copy of each piece's tokens into the
+// output: up to 8 tokens by the piece's own thread, up to HUGE_TOKENS by a
+// wavefront.  Pieces with more tokens are cut into HUGE_CHUNK-token items
+// dealt round-robin to the workgroups.  The workgroup with the last unit
+// writes T (and tok_off[P]); *out_n, if given, gets T or the error code.
+__global__ __launch_bounds__(EMIT_UNIT) void k_emit(Work w, int32_t* __restrict__ out_ids, int64_t* __restrict__ out_n) {
   __shared__ uint32_t red[8];
   const uint32_t P = w.ctr[CTR_P];
-  const uint32_t p0 = blockIdx.x * EMIT_PER_BLOCK;
-  if (p0 >= P) return;
-  uint32_t s = 0;
-  for (uint32_t b = threadIdx.x; b < blockIdx.x; b += EMIT_THREADS) s += w.blk_sum[b];
-  const uint32_t base = block_sum(s, red);
-  const uint32_t p = p0 + threadIdx.x;
-  const bool live = p < P;
-  const uint32_t c = live ? (uint32_t)w.piece_cnt[p] : 0u;
-  const uint32_t src = live ? (uint32_t)w.piece_start[p] : 0u;
-  uint32_t tot;
-  const uint32_t off = base + block_excl_sum(c, red, &tot);
-  if (live) {
-    w.tok_off[p] = (int32_t)off;
-    if (c <= 8) {
+  const uint32_t nunits = (P + EMIT_UNIT - 1) / EMIT_UNIT;
+  const int lane = (int)(threadIdx.x & 63u);
+  uint32_t hi;
+  for (uint32_t u = blockIdx.x; u < nunits; u += gridDim.x) {
+    const uint32_t base = block_reduce(w.blk_sum, (int)u, ~0u, red, &hi);
+    const uint32_t p = u * EMIT_UNIT + threadIdx.x;
+    const bool live = p < P;
+    const uint32_t c = live ? (uint32_t)w.piece_cnt[p] : 0u;
+    const uint32_t src = live ? (uint32_t)w.piece_start[p] : 0u;
+    const uint32_t off = live ? base + (uint32_t)w.tok_off[p] : 0u;
+    if (live) {
+      w.tok_off[p] = (int32_t)off;
+      if (c <= 8) {
 #pragma unroll
-      for (uint32_t k = 0; k < 8; ++k)
-        if (k < c) out_ids[off + k] = w.tmp_ids[src + k];
+        for (uint32_t k = 0; k < 8; ++k)
+          if (k < c) out_ids[off + k] = w.tmp_ids[src + k];
+      }
+    }
+    uint64_t big = __ballot(live && c > 8 && c <= (uint32_t)HUGE_TOKENS);
+    while (big) {
+      const int l = __ffsll((unsigned long long)big) - 1;
+      big &= big - 1;
+      const uint32_t cs = __shfl(src, l), co = __shfl(off, l), cc = __shfl(c, l);
+      if ((uint32_t)lane < cc) out_ids[co + lane] = w.tmp_ids[cs + lane];
+    }
+    if (u == nunits - 1 && threadIdx.x == 0) {
+      const uint32_t T = base + w.blk_sum[u];
+      w.ctr[CTR_T] = T;
+      w.tok_off[P] = (int32_t)T;
+      if (out_n) {
+        const uint32_t e = w.ctr[CTR_ERR];
+        *out_n = e ? err_code(e) : (int64_t)T;
+      }
     }
   }
-  // longer pieces: the whole wavefront copies one piece at a time
-  const int lane = (int)(threadIdx.x & 63u);
-  uint64_t big = __ballot(live && c > 8 && c <= (uint32_t)HUGE_TOKENS);
-  while (big) {
-    const int l = __ffsll((unsigned long long)big) - 1;
-    big &= big - 1;
-    const uint32_t cs = __shfl(src, l), co = __shfl(off, l), cc = __shfl(c, l);
-    for (uint32_t k = lane; k < cc; k += 64) out_ids[co + k] = w.tmp_ids[cs + k];
-  }
-  if (p0 + EMIT_PER_BLOCK >= P && threadIdx.x == 0) {
-    w.tok_off[P] = (int32_t)(base + tot);
-    w.ctr[CTR_T] = base + tot;
-  }
-}
-
-// Copy of pieces with more than HUGE_TOKENS tokens (only long pieces can have
-// them); every block takes a strided share of each such piece.
-__global__ __launch_bounds__(256) void k_copy_huge(Work w, int32_t* __restrict__ out_ids) {
+  // huge pieces: work item i = (piece, chunk) goes to workgroup i mod grid
   const uint32_t nhuge = w.ctr[CTR_NHUGE];
-  for (uint32_t i = 0; i < nhuge; ++i) {
-    const uint32_t p = (uint32_t)w.huge_list[i];
+  uint32_t item = 0;
+  for (uint32_t h = 0; h < nhuge; ++h) {
+    const uint32_t p = (uint32_t)w.huge_list[h];
     const uint32_t cc = (uint32_t)w.piece_cnt[p];
-    const uint32_t src = (uint32_t)w.piece_start[p], dst = (uint32_t)w.tok_off[p];
-    for (uint32_t k = blockIdx.x * 256 + threadIdx.x; k < cc; k += gridDim.x * 256) out_ids[dst + k] = w.tmp_ids[src + k];
+    const uint32_t nch = (cc + HUGE_CHUNK - 1) / HUGE_CHUNK;
+    uint32_t first = (blockIdx.x + gridDim.x - item % gridDim.x) % gridDim.x;  // my first chunk of this piece
+    item += nch;
+    if (first >= nch) continue;
+    const uint32_t u = p / EMIT_UNIT;
+    const uint32_t dst = block_reduce(w.blk_sum, (int)u, ~0u, red, &hi) + (uint32_t)w.tok_off[p];
+    const uint32_t src = (uint32_t)w.piece_start[p];
+    for (uint32_t ch = first; ch < nch; ch += gridDim.x) {
+      const uint32_t k1 = min(cc, (ch + 1) * HUGE_CHUNK);
+      for (uint32_t k = ch * HUGE_CHUNK + threadIdx.x; k < k1; k += EMIT_UNIT) out_ids[dst + k] = w.tmp_ids[src + k];
+    }
   }
 }
 
@@ -1011,10 +1091,6 @@ __global__ void k_check_offsets(const int64_t* __restrict__ offs, int nseq, int6
   int64_t o = offs[s];
   bool bad = (s == 0 && o != 0) || (s == nseq && o != n) || o < 0 || o > n || (s < nseq && offs[s + 1] < o);
   if (bad) atomicOr(&ctr[CTR_ERR], ERR_OFFSETS);
-}
-
-__device__ __forceinline__ int64_t err_code(uint32_t e) {
-  return (e & ERR_OFFSETS) ? -7 : (e & ERR_UTF8) ? -5 : 0;
 }
 
 __global__ void k_finish_count(const uint32_t* ctr, int which, int64_t* out) {
@@ -1053,44 +1129,39 @@ __global__ void k_write_zero_i32(int32_t* out) { *out = 0; }
 // ---------------------------------------------------------------- launchers
 
 static inline int ceil_div(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
+static inline int capped_grid(int64_t items, int per, int cap) {
+  const int g = ceil_div(items, per);
+  return g < 1 ? 1 : (g > cap ? cap : g);
+}
 
 hipError_t launch_pretokenize(const uint8_t* bytes, int64_t n, const int64_t* offs, int nseq, int pattern,
-                              const Work& w, int32_t* starts, hipStream_t st) {
+                              const Work& w, int32_t* starts, int64_t* out_np, hipStream_t st) {
   const int ntiles = ceil_div(n, TILE);
-  hipLaunchKernelGGL(k_zero, dim3(1), dim3(64), 0, st, w.ctr, (int)CTR_COUNT); prof_mark("k_zero", st);
-  if (offs) {
-    hipLaunchKernelGGL(k_check_offsets, dim3(ceil_div((int64_t)nseq + 1, 256)), dim3(256), 0, st, offs, nseq, n, w.ctr);
-    prof_mark("k_check_offsets", st);
-  }
   if (pattern == 1) {
-    hipLaunchKernelGGL(k_tile_summary, dim3(ntiles), dim3(PT_THREADS), 0, st, bytes, n, offs, nseq, w); prof_mark("k_tile_summary", st);
-    hipLaunchKernelGGL(k_pretok<1>, dim3(ntiles), dim3(PT_THREADS), 0, st, bytes, n, offs, nseq, ntiles, w); prof_mark("k_pretok<1>", st);
+    hipLaunchKernelGGL(k_tile_summary, dim3(ntiles), dim3(PT_THREADS), 0, st, bytes, n, offs, nseq, w);
+    prof_mark("k_tile_summary", st);
+    hipLaunchKernelGGL(k_pretok<1>, dim3(ntiles), dim3(PT_THREADS), 0, st, bytes, n, offs, nseq, ntiles, w);
+    prof_mark("k_pretok<1>", st);
   } else {
-    hipLaunchKernelGGL(k_pretok<0>, dim3(ntiles), dim3(PT_THREADS), 0, st, bytes, n, offs, nseq, ntiles, w); prof_mark("k_pretok<0>", st);
+    hipLaunchKernelGGL(k_pretok<0>, dim3(ntiles), dim3(PT_THREADS), 0, st, bytes, n, offs, nseq, ntiles, w);
+    prof_mark("k_pretok<0>", st);
   }
-  hipLaunchKernelGGL(k_compact, dim3(ntiles), dim3(PT_THREADS), 0, st, w, ntiles, n, starts); prof_mark("k_compact", st);
+  hipLaunchKernelGGL(k_compact, dim3(ntiles), dim3(PT_THREADS), 0, st, w, ntiles, n, starts, out_np);
+  prof_mark("k_compact", st);
   return hipGetLastError();
 }
 
 hipError_t launch_bpe_emit(const uint8_t* bytes, int64_t n, const Tables& tb, const Work& w, int32_t* out_ids,
-                           hipStream_t st) {
-  const int max_pieces = (int)n;
-  const int g_short = ceil_div(max_pieces, SHORT_THREADS);
-  hipLaunchKernelGGL(k_bpe_classify, dim3(g_short), dim3(SHORT_THREADS), 0, st, bytes, n, w, tb);
+                           int64_t* out_n, hipStream_t st) {
+  // grid-stride passes over at most n pieces
+  const int g = capped_grid(n, 256, GRID_CAP);
+  hipLaunchKernelGGL(k_bpe_classify, dim3(g), dim3(SHORT_THREADS), 0, st, bytes, n, w, tb);
   prof_mark("k_bpe_classify", st);
   // enough wavefronts to fill the chip; each one loops over work items
-  int g_merge = ceil_div(n, 256);
-  if (g_merge > 2048) g_merge = 2048;
+  const int g_merge = capped_grid(n, 256, 2048);
   hipLaunchKernelGGL(k_bpe_merge, dim3(g_merge), dim3(MERGE_THREADS), 0, st, bytes, w, tb); prof_mark("k_bpe_merge", st);
-  int g_long = ceil_div(n, LANE_CAP + 1);
-  if (g_long > 2048) g_long = 2048;
-  hipLaunchKernelGGL(k_bpe_long, dim3(g_long), dim3(64), 0, st, bytes, w, tb); prof_mark("k_bpe_long", st);
-  const int g_emit = ceil_div(max_pieces, EMIT_PER_BLOCK);
-  hipLaunchKernelGGL(k_emit_sums, dim3(g_emit), dim3(EMIT_THREADS), 0, st, w); prof_mark("k_emit_sums", st);
-  hipLaunchKernelGGL(k_emit, dim3(g_emit), dim3(EMIT_THREADS), 0, st, w, out_ids); prof_mark("k_emit", st);
-  int g_huge = ceil_div(n, 256 * 8);
-  if (g_huge > 1024) g_huge = 1024;
-  hipLaunchKernelGGL(k_copy_huge, dim3(g_huge), dim3(256), 0, st, w, out_ids); prof_mark("k_copy_huge", st);
+  hipLaunchKernelGGL(k_emit_sums, dim3(g), dim3(EMIT_UNIT), 0, st, w); prof_mark("k_emit_sums", st);
+  hipLaunchKernelGGL(k_emit, dim3(g), dim3(EMIT_UNIT), 0, st, w, out_ids, out_n); prof_mark("k_emit", st);
   return hipGetLastError();
 }
 
@@ -1120,7 +1191,7 @@ hipError_t launch_write_zero_i32(int32_t* out, hipStream_t st) {
 }
 
 hipError_t launch_zero_counters(const Work& w, hipStream_t st) {
-  hipLaunchKernelGGL(k_zero, dim3(1), dim3(64), 0, st, w.ctr, (int)CTR_COUNT); prof_mark("k_zero", st);
+  hipLaunchKernelGGL(k_zero, dim3(1), dim3(64), 0, st, w.ctr, (int)CTR_RESET_END); prof_mark("k_zero", st);
   return hipGetLastError();
 }
 
