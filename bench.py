@@ -37,10 +37,10 @@ def _sha(a):
     return hashlib.sha256(np.ascontiguousarray(a, dtype="<i4").tobytes()).hexdigest()
 
 
-# The BPE of short pieces is one stage of two kernels (classification with the
-# single-token table, then the merge loops of the rest); its roofline takes
-# both launches together.
-BPE_STAGE = "k_bpe_classify+k_bpe_merge"
+# Piece compaction with the first BPE step (single bytes, single-token table,
+# queues) and the merge loops of the rest form one stage of two kernels; its
+# roofline takes both launches together.
+BPE_STAGE = "k_compact+k_bpe_merge"
 
 
 def alg_bytes(kernel, n, P, T):
@@ -49,10 +49,9 @@ def alg_bytes(kernel, n, P, T):
         return n + n / 8            # text in, one start bit per byte out
     if kernel == "k_tile_summary":
         return n
-    if kernel == "k_compact":
-        return n / 8 + 4 * (P + 1)  # start bits in, piece offsets out
-    if kernel in (BPE_STAGE, "k_bpe_long"):
-        return 4 * (P + 1) + n + 4 * T + 4 * P  # offsets + piece bytes in, tokens + counts out
+    if kernel == BPE_STAGE:
+        # start bits in, piece offsets out; piece bytes in, tokens + counts out
+        return n / 8 + 4 * (P + 1) + n + 4 * T + 4 * P
     if kernel == "k_emit":
         return 12 * P + 8 * T       # counts, starts, tokens in; offsets, ids out
     if kernel == "k_emit_sums":
@@ -176,8 +175,8 @@ def run_workload(name, steps, warmup, graph=True, cpu=True, traffic=None):
     tt.profile(False)
     kern = {k: statistics.mean(v) for k, v in acc.items()}
     stage = dict(kern)
-    if "k_bpe_classify" in stage and "k_bpe_merge" in stage:
-        stage[BPE_STAGE] = stage.pop("k_bpe_classify") + stage.pop("k_bpe_merge")
+    if "k_compact" in stage and "k_bpe_merge" in stage:
+        stage[BPE_STAGE] = stage.pop("k_compact") + stage.pop("k_bpe_merge")
     start_np = tt.pretokenize(x, off)
     P = int(start_np.numel())
     dom = max(stage, key=stage.get)

@@ -25,7 +25,7 @@ struct State {
   int device = -1;
   uint32_t* d_byte_pair = nullptr;
   uint64_t* d_pair = nullptr;
-  CacheEntry* d_cache = nullptr;
+  CacheBucket* d_cache = nullptr;
   Tables tb{};
   void* d_ws = nullptr;
   int64_t ws_n = 0;     // bytes of input the workspace is sized for
@@ -129,9 +129,14 @@ size_t layout(int64_t n, char* base, Work* w) {
   t.blk_sum = (uint32_t*)take((nn / EMIT_UNIT + 2) * 4);
   t.long_list = (int32_t*)take((nn / (LANE_CAP + 1) + 2) * 4);
   t.huge_list = (int32_t*)take((nn / (HUGE_TOKENS + 1) + 2) * 4);
-  // a class-c queue holds pieces of at least 2, 9, 17, 33 bytes
-  const size_t qmin[4] = {2, 9, 17, 33};
-  for (int c = 0; c < 4; ++c) t.queue[c] = (uint32_t*)take((nn / qmin[c] + 2) * 4);
+  // a class-c sub-queue takes the pieces of at least QCLASS_MINLEN[c] bytes
+  // that start in every QGROUPS-th tile
+  const size_t tiles_per_group = (ntiles + QGROUPS - 1) / QGROUPS;
+  for (int c = 0; c < 4; ++c) {
+    t.qcap[c] = (uint32_t)(tiles_per_group * (TILE / QCLASS_MINLEN[c] + 1));
+    t.queue[c] = (uint32_t*)take((size_t)t.qcap[c] * QGROUPS * 4);
+  }
+  t.qctr = (uint32_t*)take(QGROUPS * QCTR_STRIDE * 4);
   t.ctr = (uint32_t*)take(CTR_COUNT * 4);
   if (w) *w = t;
   return off;
@@ -254,10 +259,11 @@ int tt_load_bpe(const int32_t* merges, const int32_t* ranks, int64_t n_merges, i
     std::vector<uint32_t> out = host_bpe(ids, rank);
     if (out.size() == 1 && out[0] == 256u + r) single.push_back((uint32_t)(256 + r));
   }
-  const uint64_t cache_n = std::max<uint64_t>(next_pow2(single.size() * 2 + 1), 1024);
-  const int cache_shift = 64 - log2_u64(cache_n);
-  std::vector<CacheEntry> cache(cache_n);
-  std::memset(cache.data(), 0, cache.size() * sizeof(CacheEntry));
+  // buckets of CACHE_SLOTS entries, load factor <= 1/2
+  const uint64_t cache_nb = std::max<uint64_t>(next_pow2((single.size() * 2 + CACHE_SLOTS - 1) / CACHE_SLOTS), 256);
+  const int cache_shift = 64 - log2_u64(cache_nb);
+  std::vector<CacheBucket> cache(cache_nb);
+  std::memset(cache.data(), 0, cache.size() * sizeof(CacheBucket));
   int cache_probe = 1;
   for (uint32_t t : single) {
     const auto& bs = tok[t];
@@ -267,14 +273,19 @@ int tt_load_bpe(const int32_t* merges, const int32_t* ranks, int64_t n_merges, i
       else w1 |= (uint64_t)bs[k] << (8 * (k - 8));
     }
     uint32_t h = cache_hash(w0, w1, (uint32_t)bs.size(), cache_shift);
-    for (int visited = 1;; ++visited, h = (uint32_t)((h + 1) & (cache_n - 1))) {
-      if (cache[h].meta == 0) {
-        cache[h].w0 = w0;
-        cache[h].w1 = w1;
-        cache[h].meta = (t << 5) | (uint32_t)bs.size();
+    for (int visited = 1;; ++visited, h = (uint32_t)((h + 1) & (cache_nb - 1))) {
+      CacheBucket& b = cache[h];
+      int slot = -1;
+      for (int s = 0; s < CACHE_SLOTS; ++s)
+        if ((b.meta[s] & ~CACHE_MORE) == 0) { slot = s; break; }
+      if (slot >= 0) {
+        b.w0[slot] = w0;
+        b.w1[slot] = w1;
+        b.meta[slot] |= (t << 5) | (uint32_t)bs.size();
         cache_probe = std::max(cache_probe, visited);
         break;
       }
+      b.meta[0] |= CACHE_MORE;  // the probe run goes on past this full bucket
     }
   }
 
@@ -298,7 +309,7 @@ int tt_load_bpe(const int32_t* merges, const int32_t* ranks, int64_t n_merges, i
   g.tb.pair_mask = (uint32_t)(pair_nb - 1);
   g.tb.pair_shift = pair_shift;
   g.tb.pair_probe = pair_probe;
-  g.tb.cache_mask = (uint32_t)(cache_n - 1);
+  g.tb.cache_mask = (uint32_t)(cache_nb - 1);
   g.tb.cache_shift = cache_shift;
   g.tb.cache_probe = cache_probe;
   g.tb.pattern = pattern_id;
@@ -324,7 +335,7 @@ int tt_encode(const uint8_t* dev_bytes, int64_t n, int32_t* out_ids, int64_t* ou
   if (n == 0) return launch_write_zeros(out_n, 1, stream) == hipSuccess ? TT_OK : TT_EHIP;
   if ((rc = ensure_workspace(n)) != TT_OK) return rc;
   prof_begin(stream);
-  if (launch_pretokenize(dev_bytes, n, nullptr, 1, g.pattern, g.w, g.w.piece_start, nullptr, stream) != hipSuccess ||
+  if (launch_pretokenize(dev_bytes, n, nullptr, 1, g.pattern, g.w, g.w.piece_start, nullptr, &g.tb, stream) != hipSuccess ||
       launch_bpe_emit(dev_bytes, n, g.tb, g.w, out_ids, out_n, stream) != hipSuccess)
     return TT_EHIP;
   return TT_OK;
@@ -348,7 +359,8 @@ int tt_encode_batch(const uint8_t* dev_bytes, int64_t n, const int64_t* dev_offs
     return TT_OK;
   }
   prof_begin(stream);
-  if (launch_pretokenize(dev_bytes, n, dev_offsets, n_seqs, g.pattern, g.w, g.w.piece_start, nullptr, stream) !=
+  if (launch_pretokenize(dev_bytes, n, dev_offsets, n_seqs, g.pattern, g.w, g.w.piece_start, nullptr, &g.tb,
+                         stream) !=
           hipSuccess ||
       launch_bpe_emit(dev_bytes, n, g.tb, g.w, out_ids, nullptr, stream) != hipSuccess ||
       launch_batch_offsets(dev_offsets, n_seqs, n, g.w, out_offsets, stream) != hipSuccess)
@@ -374,7 +386,7 @@ int tt_pretokenize(const uint8_t* dev_bytes, int64_t n, const int64_t* dev_offse
     return TT_OK;
   }
   prof_begin(stream);
-  if (launch_pretokenize(dev_bytes, n, dev_offsets, nseq, g.pattern, g.w, out_starts, out_np, stream) != hipSuccess)
+  if (launch_pretokenize(dev_bytes, n, dev_offsets, nseq, g.pattern, g.w, out_starts, out_np, nullptr, stream) != hipSuccess)
     return TT_EHIP;
   return TT_OK;
 }

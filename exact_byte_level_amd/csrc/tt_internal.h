@@ -49,13 +49,21 @@ __host__ __device__ inline uint32_t pair_bucket(uint64_t key, int shift) {
   return (uint32_t)((key * 0x9E3779B97F4A7C15ull) >> shift);
 }
 
-// Whole-pre-token cache entry (32 bytes): the piece bytes zero-padded into
-// w0/w1 (little endian), meta = (id << 5) | len, len in 2..16; meta 0 = empty.
+// Whole-pre-token table: buckets of CACHE_SLOTS entries in one 128-byte line
+// (struct of arrays).  Entry k holds the piece bytes zero-padded into w0[k] /
+// w1[k] (little endian) and meta[k] = (id << 5) | len, len in 2..16; a slot
+// with len 0 is empty.  Bit 31 of meta[0] is set if some key whose hash lands
+// in this bucket (or an earlier one of its probe run) was placed in a later
+// bucket: a lookup stops at the first bucket without it.
 constexpr int CACHE_MAXLEN = 16;
-struct alignas(32) CacheEntry {
-  uint64_t w0, w1;
-  uint32_t meta, pad0;
-  uint64_t pad1;
+constexpr int CACHE_SLOTS = 4;
+constexpr uint32_t CACHE_MORE = 1u << 31;
+struct alignas(128) CacheBucket {
+  uint32_t meta[CACHE_SLOTS];
+  uint32_t pad0[4];
+  uint64_t w0[CACHE_SLOTS];
+  uint64_t w1[CACHE_SLOTS];
+  uint64_t pad1[4];
 };
 __host__ __device__ inline uint32_t cache_hash(uint64_t w0, uint64_t w1, uint32_t len, int shift) {
   uint64_t h = (w0 ^ (uint64_t)len * 0xD6E8FEB86659FD93ull) * 0x9E3779B97F4A7C15ull;
@@ -69,13 +77,13 @@ __host__ __device__ inline uint32_t cache_hash(uint64_t w0, uint64_t w1, uint32_
 struct Tables {
   const uint32_t* byte_pair;    // [65536] rank of (x, y), x, y < 256, or RANK_NONE
   const uint64_t* pair_tab;     // [pair_nb * PAIR_SLOTS]
-  const CacheEntry* cache;      // [cache_n]
+  const CacheBucket* cache;     // [cache_nb]
   uint32_t pair_mask;           // pair_nb - 1
   int pair_shift;               // 64 - log2(pair_nb)
   int pair_probe;               // max buckets visited by any key
-  uint32_t cache_mask;          // cache_n - 1
-  int cache_shift;              // 64 - log2(cache_n)
-  int cache_probe;              // max slots visited by any key
+  uint32_t cache_mask;          // cache_nb - 1
+  int cache_shift;              // 64 - log2(cache_nb)
+  int cache_probe;              // max buckets visited by any lookup
   int pattern;
 };
 
@@ -89,12 +97,15 @@ enum : int {
   CTR_ERR = 2,           // ERR_* bits
   CTR_T = 4,             // tokens
   CTR_NHUGE = 5,         // pieces with more than HUGE_TOKENS tokens (huge_list)
-  CTR_Q = 6,             // CTR_Q + c: pieces queued in class c (<= 8, 16, 32, 64 bytes)
   CTR_RESET_END = 12,    // counters [0, CTR_RESET_END) are per call
   CTR_COUNT = 16
 };
 enum : uint32_t { ERR_UTF8 = 1u, ERR_OFFSETS = 2u };
 constexpr int TILE_ERR_SHIFT = 30;     // tile_cnt[t] bits 30-31: ERR_* bits of tile t
+
+constexpr int QGROUPS = 8;
+constexpr int QCTR_STRIDE = 32;          // words: 128 bytes
+constexpr int QCLASS_MINLEN[4] = {2, 9, 17, 33};
 
 struct Work {
   uint32_t* tile_fwd;    // [ntiles] forward run summary of each tile
@@ -109,7 +120,13 @@ struct Work {
   uint32_t* blk_sum;     // [n / EMIT_UNIT + 1] tokens of each emission unit
   int32_t* long_list;    // [n / (LANE_CAP + 1) + 1] pieces longer than LANE_CAP bytes
   int32_t* huge_list;    // [n / (HUGE_TOKENS + 1) + 1] pieces with more than HUGE_TOKENS tokens
-  uint32_t* queue[4];    // pieces for group BPE by class: <= 8 bytes [n/2], <= 16 [n/9], <= 32 [n/17], <= 64 [n/33]
+  // Pieces for group BPE by class c (<= 8, 16, 32, 64 bytes).  Tile t
+  // appends to sub-queue g = t % QGROUPS: queue[c] + g * qcap[c], with its
+  // count at qctr[g * QCTR_STRIDE + c] (one cache line per sub-queue group,
+  // so that appends from different groups do not meet at one atomic unit).
+  uint32_t* queue[4];
+  uint32_t qcap[4];
+  uint32_t* qctr;        // [QGROUPS * QCTR_STRIDE]
   uint32_t* ctr;         // [CTR_COUNT]
 };
 

@@ -8,13 +8,15 @@ namespace tt {
 // is on, records a HIP event on `st` after the named kernel's launch.
 void prof_mark(const char* name, hipStream_t st);
 
-// Pre-tokenize (validating the batch offsets, if any): piece starts (+
-// sentinel n) to `starts`, P and the error bits to w.ctr, the per-call
-// counters zeroed; *out_np = P or the error code if out_np is given.  n >= 1.
+// Pre-tokenize (validating the batch offsets, if any): the per-call counters
+// zeroed, piece starts (+ sentinel n) to `starts`, P and the error bits to
+// w.ctr; *out_np = P or the error code if out_np is given.  With tables `tb`,
+// also the first BPE step of every piece (single bytes, single-token table,
+// queues for the merge pass).  n >= 1.
 hipError_t launch_pretokenize(const uint8_t* bytes, int64_t n, const int64_t* offs, int nseq, int pattern,
-                              const Work& w, int32_t* starts, int64_t* out_np, hipStream_t st);
+                              const Work& w, int32_t* starts, int64_t* out_np, const Tables* tb, hipStream_t st);
 
-// BPE of every piece in w.piece_start, then token offsets and ids into out_ids;
+// BPE of the queued pieces, then token offsets and ids into out_ids;
 // the total goes to w.ctr[CTR_T] and, if out_n is given, T or the error code
 // to *out_n.
 hipError_t launch_bpe_emit(const uint8_t* bytes, int64_t n, const Tables& tb, const Work& w, int32_t* out_ids,

@@ -588,6 +588,11 @@ __global__ __launch_bounds__(PT_THREADS) void k_pretok(const uint8_t* __restrict
   __shared__ TileSmem sm;
   const int t = blockIdx.x;
   const int64_t t0 = (int64_t)t * TILE;
+  // no block of this pass uses the counters: reset them for the passes after
+  if (t == 0) {
+    if (threadIdx.x < CTR_RESET_END) w.ctr[threadIdx.x] = 0u;
+    for (int i = threadIdx.x; i < QGROUPS * QCTR_STRIDE; i += PT_THREADS) w.qctr[i] = 0u;
+  }
   const bool bad = load_tile(bytes, n, offs, nseq, t0, sm);
   bool bad_off = false;
   if (offs) {
@@ -634,41 +639,6 @@ __global__ __launch_bounds__(PT_THREADS) void k_pretok(const uint8_t* __restrict
   if (threadIdx.x == 0) w.tile_cnt[t] = cnt | (err << TILE_ERR_SHIFT);
 }
 
-// Pass 3: piece starts in order, from the counts of the tiles before and a
-// block scan of the start bits.  The last tile adds the sentinel n, sets P
-// and the error bits, zeroes the other per-call counters and, for a bare
-// pre-tokenization, writes P (or the error code) to *out_np.
-__global__ __launch_bounds__(PT_THREADS) void k_compact(Work w, int ntiles, int64_t n, int32_t* __restrict__ starts,
-                                                        int64_t* __restrict__ out_np) {
-  __shared__ uint32_t red[8];
-  const int t = blockIdx.x;
-  const uint32_t cmask = (1u << TILE_ERR_SHIFT) - 1u;
-  const bool last = t == ntiles - 1;
-  uint32_t hi;
-  // the last tile also folds its own count and error bits into the totals
-  const uint32_t base = block_reduce(w.tile_cnt, last ? t + 1 : t, cmask, red, &hi) -
-                        (last ? (w.tile_cnt[t] & cmask) : 0u);
-  uint32_t bits = w.flags[(int64_t)t * PT_THREADS + threadIdx.x];
-  uint32_t tot;
-  uint32_t pos = base + block_excl_sum(__popc(bits), red, &tot);
-  const int64_t p0 = (int64_t)t * TILE + (int64_t)PT_CHUNK * threadIdx.x;
-  while (bits) {
-    int k = __ffs(bits) - 1;
-    bits &= bits - 1;
-    starts[pos++] = (int32_t)(p0 + k);
-  }
-  if (last) {
-    const uint32_t e = (__syncthreads_or(hi & (ERR_UTF8 << TILE_ERR_SHIFT)) ? ERR_UTF8 : 0u) |
-                       (__syncthreads_or(hi & (ERR_OFFSETS << TILE_ERR_SHIFT)) ? ERR_OFFSETS : 0u);
-    const uint32_t P = base + tot;
-    if (threadIdx.x < CTR_RESET_END) w.ctr[threadIdx.x] = threadIdx.x == CTR_P ? P : threadIdx.x == CTR_ERR ? e : 0u;
-    if (threadIdx.x == 0) {
-      starts[P] = (int32_t)n;
-      if (out_np) *out_np = e ? err_code(e) : (int64_t)P;
-    }
-  }
-}
-
 // ----------------------------------------------------------------------- BPE
 
 // Rank of merging the adjacent pair (x, y), or RANK_NONE.
@@ -690,14 +660,26 @@ __device__ __forceinline__ uint32_t pair_rank(const Tables& tb, uint32_t x, uint
 }
 
 // Id of the single-token piece with these bytes (len 2..16), or RANK_NONE.
+// One 128-byte bucket per step (the second key word only for len > 8); the
+// walk ends at the first bucket that no key's probe run passed.
 __device__ __forceinline__ uint32_t cache_lookup(const Tables& tb, uint64_t w0, uint64_t w1, uint32_t len) {
   uint32_t h = cache_hash(w0, w1, len, tb.cache_shift);
   for (int i = 0; i < tb.cache_probe; ++i) {
-    const CacheEntry* e = tb.cache + h;
-    ulonglong2 a = *reinterpret_cast<const ulonglong2*>(e);
-    uint32_t meta = e->meta;
-    if (meta == 0) return RANK_NONE;
-    if ((meta & 31u) == len && a.x == w0 && a.y == w1) return meta >> 5;
+    const CacheBucket* b = tb.cache + h;
+    const uint4 mt = *reinterpret_cast<const uint4*>(b->meta);
+    const ulonglong2 a01 = *reinterpret_cast<const ulonglong2*>(&b->w0[0]);
+    const ulonglong2 a23 = *reinterpret_cast<const ulonglong2*>(&b->w0[2]);
+    ulonglong2 c01 = make_ulonglong2(0ull, 0ull), c23 = make_ulonglong2(0ull, 0ull);
+    if (len > 8) {
+      c01 = *reinterpret_cast<const ulonglong2*>(&b->w1[0]);
+      c23 = *reinterpret_cast<const ulonglong2*>(&b->w1[2]);
+    }
+    const uint32_t m0 = mt.x & ~CACHE_MORE;
+    if ((m0 & 31u) == len && a01.x == w0 && c01.x == w1) return (m0 >> 5) & ID_MASK;
+    if ((mt.y & 31u) == len && a01.y == w0 && c01.y == w1) return (mt.y >> 5) & ID_MASK;
+    if ((mt.z & 31u) == len && a23.x == w0 && c23.x == w1) return (mt.z >> 5) & ID_MASK;
+    if ((mt.w & 31u) == len && a23.y == w0 && c23.y == w1) return (mt.w >> 5) & ID_MASK;
+    if (!(mt.x & CACHE_MORE)) return RANK_NONE;
     h = (h + 1) & tb.cache_mask;
   }
   return RANK_NONE;
@@ -785,70 +767,122 @@ __device__ void group_bpe(const uint8_t* __restrict__ bytes, const Work& w, cons
   }
 }
 
-constexpr int SHORT_THREADS = 256;
-constexpr int STAGE_BYTES = 8192;  // text bytes of a unit's pieces staged in LDS
-
-// Pass 4: one thread per piece, 256 pieces per workgroup pass.  Single bytes
-// and pieces found in the single-token table finish here; pieces of up to
-// LANE_CAP bytes go to the global queue of their length class (<= 8, 16, 32,
-// 64 bytes) for k_bpe_merge, longer ones to the long list.  Queue slots are
-// reserved with one atomic per class and pass.
-__global__ __launch_bounds__(SHORT_THREADS) void k_bpe_classify(const uint8_t* __restrict__ bytes, int64_t n,
-                                                                Work w, Tables tb) {
-  __shared__ uint4 stage[STAGE_BYTES / 16];
+// Pass 3: piece starts in order, from the counts of the tiles before and a
+// block scan of the start bits.  The last tile adds the sentinel n and sets P
+// and the error bits; for a bare pre-tokenization it writes P (or the error
+// code) to *out_np.  With CLASSIFY, the tile then takes the first BPE step of
+// every piece that starts in it: single bytes and pieces found in the
+// single-token table finish here; pieces of up to LANE_CAP bytes go to the
+// global queue of their length class (<= 8, 16, 32, 64 bytes) for
+// k_bpe_merge, longer ones to the long list (one atomic per class and round
+// of 256 pieces reserves the slots).  The end of the tile's last piece is the
+// first start in a later tile, found from the tile counts and start bits.
+template <bool CLASSIFY>
+__global__ __launch_bounds__(PT_THREADS) void k_compact(const uint8_t* __restrict__ bytes, Work w, Tables tb,
+                                                        int ntiles, int64_t n, int32_t* __restrict__ starts,
+                                                        int64_t* __restrict__ out_np) {
+  __shared__ uint32_t red[8];
+  __shared__ int32_t sst[TILE + 1];
+  __shared__ uint4 stage[(TILE + CACHE_MAXLEN) / 16];
   __shared__ uint32_t qn[5], qbase[5];
-  __shared__ int32_t st_lo, st_n;
-  const uint32_t P = w.ctr[CTR_P];
-  const bool aligned = (reinterpret_cast<uintptr_t>(bytes) & 15u) == 0;
-  const uint8_t* sb = reinterpret_cast<const uint8_t*>(stage);
-  for (uint32_t p0 = blockIdx.x * SHORT_THREADS; p0 < P; p0 += gridDim.x * SHORT_THREADS) {
-    if (threadIdx.x < 5) qn[threadIdx.x] = 0;
+  const int t = blockIdx.x;
+  const int lane = (int)(threadIdx.x & 63u);
+  const uint32_t cmask = (1u << TILE_ERR_SHIFT) - 1u;
+  const bool last = t == ntiles - 1;
+  uint32_t hi;
+  // the last tile also folds its own count and error bits into the totals
+  const uint32_t base = block_reduce(w.tile_cnt, last ? t + 1 : t, cmask, red, &hi) -
+                        (last ? (w.tile_cnt[t] & cmask) : 0u);
+  uint32_t bits = w.flags[(int64_t)t * PT_THREADS + threadIdx.x];
+  uint32_t tot;
+  uint32_t lpos = block_excl_sum(__popc(bits), red, &tot);
+  uint32_t pos = base + lpos;
+  const int64_t t0 = (int64_t)t * TILE;
+  const int64_t p0 = t0 + (int64_t)PT_CHUNK * threadIdx.x;
+  while (bits) {
+    const int k = __ffs(bits) - 1;
+    bits &= bits - 1;
+    starts[pos++] = (int32_t)(p0 + k);
+    if (CLASSIFY) sst[lpos++] = (int32_t)(p0 + k);
+  }
+  if (last) {
+    const uint32_t e = (__syncthreads_or(hi & (ERR_UTF8 << TILE_ERR_SHIFT)) ? ERR_UTF8 : 0u) |
+                       (__syncthreads_or(hi & (ERR_OFFSETS << TILE_ERR_SHIFT)) ? ERR_OFFSETS : 0u);
+    const uint32_t P = base + tot;
     if (threadIdx.x == 0) {
-      // the pass's pieces cover one contiguous byte range; stage (a prefix of) it
-      const int32_t a = w.piece_start[p0];
-      const int32_t b = w.piece_start[min(P, p0 + SHORT_THREADS)];
-      const int32_t lo = a & ~15;
-      st_lo = lo;
-      st_n = min(b - lo, STAGE_BYTES);
+      w.ctr[CTR_P] = P;
+      w.ctr[CTR_ERR] = e;
+      starts[P] = (int32_t)n;
+      if (out_np) *out_np = e ? err_code(e) : (int64_t)P;
     }
-    __syncthreads();
-    const int32_t lo = st_lo, nst = st_n;
-    for (int i = threadIdx.x; i * 16 < nst; i += SHORT_THREADS) {
-      const int64_t g = (int64_t)lo + 16 * i;
-      uint4 v;
-      if (aligned && g + 16 <= n) {
-        v = *reinterpret_cast<const uint4*>(bytes + g);
-      } else {
-        uint32_t wv[4] = {0u, 0u, 0u, 0u};
-        for (int k = 0; k < 16; ++k)
-          if (g + k < n) wv[k >> 2] |= (uint32_t)bytes[g + k] << (8 * (k & 3));
-        v = make_uint4(wv[0], wv[1], wv[2], wv[3]);
+  }
+  if (!CLASSIFY || tot == 0) return;
+  {
+    // end of the last piece: the first start after this tile, else n (every
+    // wavefront runs the same search; the ballots keep it wave-uniform)
+    int32_t e = (int32_t)n;
+    for (int b = t + 1; b < ntiles; b += 64) {
+      const int bb = b + lane;
+      const uint64_t nz = __ballot(bb < ntiles && (w.tile_cnt[bb] & cmask) != 0u);
+      if (nz) {
+        const int f = b + __ffsll((unsigned long long)nz) - 1;
+        for (int q = 0; q < PT_THREADS; q += 64) {
+          const uint32_t fl = w.flags[(int64_t)f * PT_THREADS + q + lane];
+          const uint64_t fm = __ballot(fl != 0u);
+          if (fm) {
+            const int l = __ffsll((unsigned long long)fm) - 1;
+            const uint32_t flw = (uint32_t)__shfl((int)fl, l);
+            e = (int32_t)((int64_t)f * TILE + PT_CHUNK * (q + l) + __ffs(flw) - 1);
+            break;
+          }
+        }
+        break;
       }
-      stage[i] = v;
     }
-    __syncthreads();
-    const uint32_t p = p0 + threadIdx.x;
+    if (threadIdx.x == 0) sst[tot] = e;
+  }
+  // the tile's bytes plus CACHE_MAXLEN, for single bytes and table keys
+  const bool aligned = (reinterpret_cast<uintptr_t>(bytes) & 15u) == 0;
+  for (int i = threadIdx.x; i < (TILE + CACHE_MAXLEN) / 16; i += PT_THREADS) {
+    const int64_t g = t0 + 16 * i;
+    uint4 v;
+    if (aligned && g + 16 <= n) {
+      v = *reinterpret_cast<const uint4*>(bytes + g);
+    } else {
+      uint32_t wv[4] = {0u, 0u, 0u, 0u};
+      for (int k = 0; k < 16; ++k)
+        if (g + k < n) wv[k >> 2] |= (uint32_t)bytes[g + k] << (8 * (k & 3));
+      v = make_uint4(wv[0], wv[1], wv[2], wv[3]);
+    }
+    stage[i] = v;
+  }
+  if (threadIdx.x < 5) qn[threadIdx.x] = 0;
+  __syncthreads();
+  const uint8_t* sb = reinterpret_cast<const uint8_t*>(stage);
+  for (uint32_t k0 = 0; k0 < tot; k0 += PT_THREADS) {
+    const uint32_t k = k0 + threadIdx.x;
+    const uint32_t p = base + k;
     int cls = -1;
     uint32_t slot = 0;
-    if (p < P) {
-      const int32_t s = w.piece_start[p];
-      const int32_t len = w.piece_start[p + 1] - s;
-      const bool in_stage = s - lo + len <= nst;
+    if (k < tot) {
+      const int32_t s = sst[k];
+      const int32_t len = sst[k + 1] - s;
+      const int off = (int)(s - t0);
       if (len > LANE_CAP) {
         cls = 4;
       } else if (len == 1) {
-        w.tmp_ids[s] = in_stage ? sb[s - lo] : bytes[s];
+        w.tmp_ids[s] = sb[off];
         w.piece_cnt[p] = 1;
       } else {
         uint32_t hit = RANK_NONE;
         if (len <= CACHE_MAXLEN) {
           uint64_t w0 = 0, w1 = 0;
 #pragma unroll
-          for (int k = 0; k < CACHE_MAXLEN; ++k) {
-            if (k < len) {
-              const uint64_t b = in_stage ? sb[s - lo + k] : bytes[s + k];
-              if (k < 8) w0 |= b << (8 * k);
-              else w1 |= b << (8 * (k - 8));
+          for (int j = 0; j < CACHE_MAXLEN; ++j) {
+            if (j < len) {
+              const uint64_t by = sb[off + j];
+              if (j < 8) w0 |= by << (8 * j);
+              else w1 |= by << (8 * (j - 8));
             }
           }
           hit = cache_lookup(tb, w0, w1, (uint32_t)len);
@@ -865,13 +899,15 @@ __global__ __launch_bounds__(SHORT_THREADS) void k_bpe_classify(const uint8_t* _
     __syncthreads();
     if (threadIdx.x < 5) {
       const uint32_t c = qn[threadIdx.x];
-      qbase[threadIdx.x] = c ? atomicAdd(&w.ctr[threadIdx.x < 4 ? CTR_Q + threadIdx.x : CTR_NLONG], c) : 0u;
+      uint32_t* ctr = threadIdx.x < 4 ? &w.qctr[(t % QGROUPS) * QCTR_STRIDE + threadIdx.x] : &w.ctr[CTR_NLONG];
+      qbase[threadIdx.x] = c ? atomicAdd(ctr, c) : 0u;
     }
     __syncthreads();
     if (cls >= 0) {
-      uint32_t* q = cls < 4 ? w.queue[cls] : reinterpret_cast<uint32_t*>(w.long_list);
+      uint32_t* q = cls < 4 ? w.queue[cls] + (t % QGROUPS) * w.qcap[cls] : reinterpret_cast<uint32_t*>(w.long_list);
       q[qbase[cls] + slot] = p;
     }
+    if (threadIdx.x < 5) qn[threadIdx.x] = 0;
     __syncthreads();
   }
 }
@@ -975,24 +1011,43 @@ __device__ void long_bpe(const uint8_t* __restrict__ bytes, const Work& w, const
 // class branches are scalar.
 constexpr int MERGE_THREADS = 256;
 __global__ __launch_bounds__(MERGE_THREADS) void k_bpe_merge(const uint8_t* __restrict__ bytes, Work w, Tables tb) {
+  // pre[k]: work items before sub-queue k, k = (3 - class) * QGROUPS + group
+  // (classes longest first, sub-queues in order); pre[4 * QGROUPS] = all
+  constexpr int NQ = 4 * QGROUPS;
+  __shared__ uint32_t pre[NQ + 1];
+  if (threadIdx.x < 64) {
+    const int k = (int)threadIdx.x, c = 3 - k / QGROUPS, g = k % QGROUPS;
+    const uint32_t it = k < NQ ? (w.qctr[g * QCTR_STRIDE + c] + (8u >> c) - 1) >> (3 - c) : 0u;
+    uint32_t inc = it;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const uint32_t o = __shfl_up(inc, d);
+      if (k >= d) inc += o;
+    }
+    if (k <= NQ) pre[k] = inc - it;
+  }
+  __syncthreads();
   const uint32_t nl = w.ctr[CTR_NLONG];
-  const uint32_t n8 = w.ctr[CTR_Q + 0], n16 = w.ctr[CTR_Q + 1], n32 = w.ctr[CTR_Q + 2], n64 = w.ctr[CTR_Q + 3];
-  const uint32_t c64 = n64, c32 = (n32 + 1) / 2, c16 = (n16 + 3) / 4, c8 = (n8 + 7) / 8;
-  const uint32_t total = nl + c64 + c32 + c16 + c8;
+  const uint32_t total = nl + uniform(pre[NQ]);
   const uint32_t nwaves = gridDim.x * (MERGE_THREADS / 64);
   for (uint32_t t = uniform(blockIdx.x * (MERGE_THREADS / 64) + (threadIdx.x >> 6)); t < total; t += nwaves) {
-    uint32_t u = t;
-    if (u < nl) {
-      long_bpe(bytes, w, tb, uniform((uint32_t)w.long_list[u]));
-    } else if ((u -= nl) < c64) {
-      group_bpe<64>(bytes, w, tb, w.queue[3], (int)n64, (int)u);
-    } else if ((u -= c64) < c32) {
-      group_bpe<32>(bytes, w, tb, w.queue[2], (int)n32, (int)u);
-    } else if ((u -= c32) < c16) {
-      group_bpe<16>(bytes, w, tb, w.queue[1], (int)n16, (int)u);
-    } else {
-      group_bpe<8>(bytes, w, tb, w.queue[0], (int)n8, (int)(u - c16));
+    if (t < nl) {
+      long_bpe(bytes, w, tb, uniform((uint32_t)w.long_list[t]));
+      continue;
     }
+    const uint32_t u = t - nl;
+    uint32_t k = 0;
+#pragma unroll
+    for (uint32_t step = NQ / 2; step >= 1; step >>= 1)
+      if (uniform(pre[k + step]) <= u) k += step;
+    const uint32_t c = 3 - k / QGROUPS, g = k % QGROUPS;
+    const uint32_t item = u - uniform(pre[k]);
+    const uint32_t qn = w.qctr[g * QCTR_STRIDE + c];
+    const uint32_t* q = w.queue[c] + g * w.qcap[c];
+    if (c == 3) group_bpe<64>(bytes, w, tb, q, (int)qn, (int)item);
+    else if (c == 2) group_bpe<32>(bytes, w, tb, q, (int)qn, (int)item);
+    else if (c == 1) group_bpe<16>(bytes, w, tb, q, (int)qn, (int)item);
+    else group_bpe<8>(bytes, w, tb, q, (int)qn, (int)item);
   }
 }
 
@@ -1135,7 +1190,7 @@ static inline int capped_grid(int64_t items, int per, int cap) {
 }
 
 hipError_t launch_pretokenize(const uint8_t* bytes, int64_t n, const int64_t* offs, int nseq, int pattern,
-                              const Work& w, int32_t* starts, int64_t* out_np, hipStream_t st) {
+                              const Work& w, int32_t* starts, int64_t* out_np, const Tables* tb, hipStream_t st) {
   const int ntiles = ceil_div(n, TILE);
   if (pattern == 1) {
     hipLaunchKernelGGL(k_tile_summary, dim3(ntiles), dim3(PT_THREADS), 0, st, bytes, n, offs, nseq, w);
@@ -1146,20 +1201,23 @@ hipError_t launch_pretokenize(const uint8_t* bytes, int64_t n, const int64_t* of
     hipLaunchKernelGGL(k_pretok<0>, dim3(ntiles), dim3(PT_THREADS), 0, st, bytes, n, offs, nseq, ntiles, w);
     prof_mark("k_pretok<0>", st);
   }
-  hipLaunchKernelGGL(k_compact, dim3(ntiles), dim3(PT_THREADS), 0, st, w, ntiles, n, starts, out_np);
+  if (tb) {
+    hipLaunchKernelGGL(k_compact<true>, dim3(ntiles), dim3(PT_THREADS), 0, st, bytes, w, *tb, ntiles, n, starts, out_np);
+  } else {
+    hipLaunchKernelGGL(k_compact<false>, dim3(ntiles), dim3(PT_THREADS), 0, st, bytes, w, Tables{}, ntiles, n, starts,
+                       out_np);
+  }
   prof_mark("k_compact", st);
   return hipGetLastError();
 }
 
 hipError_t launch_bpe_emit(const uint8_t* bytes, int64_t n, const Tables& tb, const Work& w, int32_t* out_ids,
                            int64_t* out_n, hipStream_t st) {
-  // grid-stride passes over at most n pieces
-  const int g = capped_grid(n, 256, GRID_CAP);
-  hipLaunchKernelGGL(k_bpe_classify, dim3(g), dim3(SHORT_THREADS), 0, st, bytes, n, w, tb);
-  prof_mark("k_bpe_classify", st);
   // enough wavefronts to fill the chip; each one loops over work items
   const int g_merge = capped_grid(n, 256, 2048);
   hipLaunchKernelGGL(k_bpe_merge, dim3(g_merge), dim3(MERGE_THREADS), 0, st, bytes, w, tb); prof_mark("k_bpe_merge", st);
+  // grid-stride passes over at most n pieces
+  const int g = capped_grid(n, EMIT_UNIT, GRID_CAP);
   hipLaunchKernelGGL(k_emit_sums, dim3(g), dim3(EMIT_UNIT), 0, st, w); prof_mark("k_emit_sums", st);
   hipLaunchKernelGGL(k_emit, dim3(g), dim3(EMIT_UNIT), 0, st, w, out_ids, out_n); prof_mark("k_emit", st);
   return hipGetLastError();
