@@ -767,151 +767,6 @@ __device__ void group_bpe(const uint8_t* __restrict__ bytes, const Work& w, cons
   }
 }
 
-// Pass 3: piece starts in order, from the counts of the tiles before and a
-// block scan of the start bits.  The last tile adds the sentinel n and sets P
-// and the error bits; for a bare pre-tokenization it writes P (or the error
-// code) to *out_np.  With CLASSIFY, the tile then takes the first BPE step of
-// every piece that starts in it: single bytes and pieces found in the
-// single-token table finish here; pieces of up to LANE_CAP bytes go to the
-// global queue of their length class (<= 8, 16, 32, 64 bytes) for
-// k_bpe_merge, longer ones to the long list (one atomic per class and round
-// of 256 pieces reserves the slots).  The end of the tile's last piece is the
-// first start in a later tile, found from the tile counts and start bits.
-template <bool CLASSIFY>
-__global__ __launch_bounds__(PT_THREADS) void k_compact(const uint8_t* __restrict__ bytes, Work w, Tables tb,
-                                                        int ntiles, int64_t n, int32_t* __restrict__ starts,
-                                                        int64_t* __restrict__ out_np) {
-  __shared__ uint32_t red[8];
-  __shared__ int32_t sst[TILE + 1];
-  __shared__ uint4 stage[(TILE + CACHE_MAXLEN) / 16];
-  __shared__ uint32_t qn[5], qbase[5];
-  const int t = blockIdx.x;
-  const int lane = (int)(threadIdx.x & 63u);
-  const uint32_t cmask = (1u << TILE_ERR_SHIFT) - 1u;
-  const bool last = t == ntiles - 1;
-  uint32_t hi;
-  // the last tile also folds its own count and error bits into the totals
-  const uint32_t base = block_reduce(w.tile_cnt, last ? t + 1 : t, cmask, red, &hi) -
-                        (last ? (w.tile_cnt[t] & cmask) : 0u);
-  uint32_t bits = w.flags[(int64_t)t * PT_THREADS + threadIdx.x];
-  uint32_t tot;
-  uint32_t lpos = block_excl_sum(__popc(bits), red, &tot);
-  uint32_t pos = base + lpos;
-  const int64_t t0 = (int64_t)t * TILE;
-  const int64_t p0 = t0 + (int64_t)PT_CHUNK * threadIdx.x;
-  while (bits) {
-    const int k = __ffs(bits) - 1;
-    bits &= bits - 1;
-    starts[pos++] = (int32_t)(p0 + k);
-    if (CLASSIFY) sst[lpos++] = (int32_t)(p0 + k);
-  }
-  if (last) {
-    const uint32_t e = (__syncthreads_or(hi & (ERR_UTF8 << TILE_ERR_SHIFT)) ? ERR_UTF8 : 0u) |
-                       (__syncthreads_or(hi & (ERR_OFFSETS << TILE_ERR_SHIFT)) ? ERR_OFFSETS : 0u);
-    const uint32_t P = base + tot;
-    if (threadIdx.x == 0) {
-      w.ctr[CTR_P] = P;
-      w.ctr[CTR_ERR] = e;
-      starts[P] = (int32_t)n;
-      if (out_np) *out_np = e ? err_code(e) : (int64_t)P;
-    }
-  }
-  if (!CLASSIFY || tot == 0) return;
-  {
-    // end of the last piece: the first start after this tile, else n (every
-    // wavefront runs the same search; the ballots keep it wave-uniform)
-    int32_t e = (int32_t)n;
-    for (int b = t + 1; b < ntiles; b += 64) {
-      const int bb = b + lane;
-      const uint64_t nz = __ballot(bb < ntiles && (w.tile_cnt[bb] & cmask) != 0u);
-      if (nz) {
-        const int f = b + __ffsll((unsigned long long)nz) - 1;
-        for (int q = 0; q < PT_THREADS; q += 64) {
-          const uint32_t fl = w.flags[(int64_t)f * PT_THREADS + q + lane];
-          const uint64_t fm = __ballot(fl != 0u);
-          if (fm) {
-            const int l = __ffsll((unsigned long long)fm) - 1;
-            const uint32_t flw = (uint32_t)__shfl((int)fl, l);
-            e = (int32_t)((int64_t)f * TILE + PT_CHUNK * (q + l) + __ffs(flw) - 1);
-            break;
-          }
-        }
-        break;
-      }
-    }
-    if (threadIdx.x == 0) sst[tot] = e;
-  }
-  // the tile's bytes plus CACHE_MAXLEN, for single bytes and table keys
-  const bool aligned = (reinterpret_cast<uintptr_t>(bytes) & 15u) == 0;
-  for (int i = threadIdx.x; i < (TILE + CACHE_MAXLEN) / 16; i += PT_THREADS) {
-    const int64_t g = t0 + 16 * i;
-    uint4 v;
-    if (aligned && g + 16 <= n) {
-      v = *reinterpret_cast<const uint4*>(bytes + g);
-    } else {
-      uint32_t wv[4] = {0u, 0u, 0u, 0u};
-      for (int k = 0; k < 16; ++k)
-        if (g + k < n) wv[k >> 2] |= (uint32_t)bytes[g + k] << (8 * (k & 3));
-      v = make_uint4(wv[0], wv[1], wv[2], wv[3]);
-    }
-    stage[i] = v;
-  }
-  if (threadIdx.x < 5) qn[threadIdx.x] = 0;
-  __syncthreads();
-  const uint8_t* sb = reinterpret_cast<const uint8_t*>(stage);
-  for (uint32_t k0 = 0; k0 < tot; k0 += PT_THREADS) {
-    const uint32_t k = k0 + threadIdx.x;
-    const uint32_t p = base + k;
-    int cls = -1;
-    uint32_t slot = 0;
-    if (k < tot) {
-      const int32_t s = sst[k];
-      const int32_t len = sst[k + 1] - s;
-      const int off = (int)(s - t0);
-      if (len > LANE_CAP) {
-        cls = 4;
-      } else if (len == 1) {
-        w.tmp_ids[s] = sb[off];
-        w.piece_cnt[p] = 1;
-      } else {
-        uint32_t hit = RANK_NONE;
-        if (len <= CACHE_MAXLEN) {
-          uint64_t w0 = 0, w1 = 0;
-#pragma unroll
-          for (int j = 0; j < CACHE_MAXLEN; ++j) {
-            if (j < len) {
-              const uint64_t by = sb[off + j];
-              if (j < 8) w0 |= by << (8 * j);
-              else w1 |= by << (8 * (j - 8));
-            }
-          }
-          hit = cache_lookup(tb, w0, w1, (uint32_t)len);
-        }
-        if (hit != RANK_NONE) {
-          w.tmp_ids[s] = (int32_t)hit;
-          w.piece_cnt[p] = 1;
-        } else {
-          cls = len <= 8 ? 0 : len <= 16 ? 1 : len <= 32 ? 2 : 3;
-        }
-      }
-      if (cls >= 0) slot = atomicAdd(&qn[cls], 1u);
-    }
-    __syncthreads();
-    if (threadIdx.x < 5) {
-      const uint32_t c = qn[threadIdx.x];
-      uint32_t* ctr = threadIdx.x < 4 ? &w.qctr[(t % QGROUPS) * QCTR_STRIDE + threadIdx.x] : &w.ctr[CTR_NLONG];
-      qbase[threadIdx.x] = c ? atomicAdd(ctr, c) : 0u;
-    }
-    __syncthreads();
-    if (cls >= 0) {
-      uint32_t* q = cls < 4 ? w.queue[cls] + (t % QGROUPS) * w.qcap[cls] : reinterpret_cast<uint32_t*>(w.long_list);
-      q[qbase[cls] + slot] = p;
-    }
-    if (threadIdx.x < 5) qn[threadIdx.x] = 0;
-    __syncthreads();
-  }
-}
-
 __device__ __forceinline__ uint32_t wave_min(uint32_t x) {
 #pragma unroll
   for (int d = 32; d >= 1; d >>= 1) x = min(x, (uint32_t)__shfl_xor(x, d));
@@ -1000,6 +855,312 @@ __device__ void long_bpe(const uint8_t* __restrict__ bytes, const Work& w, const
   if (lane == 0) {
     w.piece_cnt[p] = m;
     if (m > HUGE_TOKENS) w.huge_list[atomicAdd(&w.ctr[CTR_NHUGE], 1u)] = (int32_t)p;
+  }
+}
+
+// Carry functions of the merge-start scan: bit 0 = carry out for carry in 0,
+// bit 1 = carry out for carry in 1.  compose(f, g) applies f, then g.
+constexpr uint32_t FN_ID = 2u;
+__device__ __forceinline__ uint32_t fn_compose(uint32_t f, uint32_t g) {
+  const uint32_t h0 = (f & 1u) ? (g >> 1) & 1u : g & 1u;
+  const uint32_t h1 = (f & 2u) ? (g >> 1) & 1u : g & 1u;
+  return h0 | (h1 << 1);
+}
+
+__device__ __forceinline__ uint32_t block_min(uint32_t x, uint32_t* red) {
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  x = wave_min(x);
+  if (lane == 0) red[wid] = x;
+  __syncthreads();
+  uint32_t r = RANK_NONE;
+  for (int v = 0; v < (int)(blockDim.x >> 6); ++v) r = min(r, red[v]);
+  __syncthreads();
+  return r;
+}
+
+constexpr int BIG_E = 8;                           // positions per thread and sweep step
+constexpr int BIG_STEP = 256 * BIG_E;              // positions per sweep step of the workgroup
+constexpr int BIG_LDS = BIG_STEP + 2 + (BIG_STEP + 2) / 32 + 1;  // skewed slots per staged array
+__device__ __forceinline__ int big_slot(int i) { return i + (i >> 5); }  // spreads BIG_E-strided reads over the banks
+
+// LDS of big_bpe: the staged ids and ranks of one sweep step plus scan space.
+struct BigSmem {
+  uint32_t id[BIG_LDS];
+  uint32_t rk[BIG_LDS];
+  uint32_t sh[16];
+};
+
+// Piece p = bytes [s, s + m), longer than BIG_BYTES, by one workgroup of 256
+// threads (s and m are the same in every thread): the
+// same exact global-minimum rounds as long_bpe.  A sweep step stages BIG_STEP
+// positions (and two more on the right) in LDS with coalesced loads; thread
+// t then takes the BIG_E contiguous positions t * BIG_E ... .  Inside a run of
+// equal pairs the merge starts alternate, so whether position k starts a
+// merge depends on the carry from k - 1: each thread evaluates its positions
+// for both carries and a block scan of the resulting carry functions picks
+// the right one.  A block prefix sum of the surviving positions places the
+// compacted ids; all reads of a step finish (barrier) before its writes,
+// which land at or left of the positions read.
+__device__ void big_bpe(const uint8_t* __restrict__ bytes, const Work& w, const Tables& tb, uint32_t p,
+                        int32_t s, int m, BigSmem& sm) {
+  const int tid = (int)threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  uint32_t* I = reinterpret_cast<uint32_t*>(w.tmp_ids) + s;
+  uint32_t* R = w.tmp_rank + s;
+  uint32_t rmin = RANK_NONE;
+  for (int base = 0; base < m; base += 256 * 8) {
+    uint32_t b0[8], b1[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int k = base + 256 * j + tid;
+      b0[j] = k < m ? bytes[s + k] : 0u;
+      b1[j] = k + 1 < m ? bytes[s + k + 1] : 0u;
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int k = base + 256 * j + tid;
+      if (k < m) {
+        const uint32_t r = k + 1 < m ? tb.byte_pair[(b0[j] << 8) | b1[j]] : RANK_NONE;
+        I[k] = b0[j];
+        R[k] = r;
+        rmin = min(rmin, r);
+      }
+    }
+  }
+  rmin = uniform(block_min(rmin, sm.sh + 8));
+  while (rmin != RANK_NONE) {
+    const uint32_t T = 256u + rmin;
+    uint32_t cin = 0, nmin = RANK_NONE;
+    int out = 0;
+    for (int base = 0; base < m; base += BIG_STEP) {
+      for (int i = tid; i < BIG_STEP + 2; i += 256) {
+        const int k = base + i;
+        sm.id[big_slot(i)] = k < m ? I[k] : 0u;
+        sm.rk[big_slot(i)] = k + 1 < m ? R[k] : RANK_NONE;
+      }
+      __syncthreads();
+      const int j0 = tid * BIG_E, k0 = base + j0;
+      uint32_t eq = 0;
+#pragma unroll
+      for (int j = 0; j < BIG_E + 2; ++j) eq |= (sm.rk[big_slot(j0 + j)] == rmin ? 1u : 0u) << j;
+      // merge starts of this thread's positions for carry in 0 (msA) and 1 (msB)
+      uint32_t msA = 0, msB = 0, a = 0, b = 1;
+#pragma unroll
+      for (int j = 0; j < BIG_E; ++j) {
+        const uint32_t e = (eq >> j) & 1u;
+        a = e & (a ^ 1u);
+        b = e & (b ^ 1u);
+        msA |= a << j;
+        msB |= b << j;
+      }
+      // carry into this thread: the step's carry through the functions of the threads before it
+      uint32_t inc = a | (b << 1);
+#pragma unroll
+      for (int d = 1; d < 64; d <<= 1) {
+        const uint32_t o = (uint32_t)__shfl_up((int)inc, d);
+        if (lane >= d) inc = fn_compose(o, inc);
+      }
+      if (lane == 63) sm.sh[wid] = inc;
+      __syncthreads();
+      uint32_t before = FN_ID;
+      for (int v = 0; v < wid; ++v) before = fn_compose(before, sm.sh[v]);
+      uint32_t exl = (uint32_t)__shfl_up((int)inc, 1);
+      if (lane == 0) exl = FN_ID;
+      before = fn_compose(before, exl);
+      const uint32_t tc = (cin ? (before >> 1) : before) & 1u;
+      const uint32_t ms = tc ? msB : msA;
+      const uint32_t lastms = (ms >> (BIG_E - 1)) & 1u;
+      const uint32_t msE = ((eq >> BIG_E) & 1u) & (lastms ^ 1u);
+      const uint32_t msE1 = ((eq >> (BIG_E + 1)) & 1u) & (msE ^ 1u);
+      const uint32_t msx = ms | (msE << BIG_E) | (msE1 << (BIG_E + 1));
+      const uint32_t prev = (ms << 1) | tc;  // bit j: a merge starts at position j - 1
+      uint32_t keep = 0;
+#pragma unroll
+      for (int j = 0; j < BIG_E; ++j)
+        if (k0 + j < m && !((prev >> j) & 1u)) keep |= 1u << j;
+      if (tid == 255) sm.sh[4] = lastms;
+      uint32_t tot;
+      int o = out + (int)block_excl_sum(__popc(keep), sm.sh + 8, &tot);
+      for (uint32_t kb = keep; kb; kb &= kb - 1) {
+        const int j = __ffs(kb) - 1;
+        const int k = k0 + j;
+        const bool m0 = (msx >> j) & 1u, m1 = (msx >> (j + 1)) & 1u, m2 = (msx >> (j + 2)) & 1u;
+        const uint32_t nid = m0 ? T : sm.id[big_slot(j0 + j)];
+        const bool has_next = m0 ? (k + 2 < m) : (k + 1 < m);
+        const uint32_t nxt = m0 ? (m2 ? T : sm.id[big_slot(j0 + j + 2)]) : (m1 ? T : sm.id[big_slot(j0 + j + 1)]);
+        uint32_t nr = RANK_NONE;
+        if (has_next) nr = (m0 || m1) ? pair_rank(tb, nid, nxt) : sm.rk[big_slot(j0 + j)];
+        I[o] = nid;
+        R[o] = nr;
+        ++o;
+        nmin = min(nmin, nr);
+      }
+      out += (int)tot;
+      cin = uniform(sm.sh[4]);
+      __syncthreads();  // the staged step is read; the next one may overwrite it
+    }
+    m = (int)uniform((uint32_t)out);
+    rmin = uniform(block_min(nmin, sm.sh + 8));
+  }
+  if (tid == 0) {
+    w.piece_cnt[p] = m;
+    if (m > HUGE_TOKENS) w.huge_list[atomicAdd(&w.ctr[CTR_NHUGE], 1u)] = (int32_t)p;
+  }
+}
+
+// Pass 3: piece starts in order, from the counts of the tiles before and a
+// block scan of the start bits.  The last tile adds the sentinel n and sets P
+// and the error bits; for a bare pre-tokenization it writes P (or the error
+// code) to *out_np.  With CLASSIFY, the tile then takes the first BPE step of
+// every piece that starts in it: single bytes and pieces found in the
+// single-token table finish here; pieces of up to LANE_CAP bytes go to the
+// global queue of their length class (<= 8, 16, 32, 64 bytes) for
+// k_bpe_merge, longer ones up to BIG_BYTES to the long list (one atomic per
+// class and round of 256 pieces reserves the slots).  The end of the tile's
+// last piece is the first start in a later tile, found from the tile counts
+// and start bits; if that piece is longer than BIG_BYTES (only the last one
+// can be), the tile's workgroup merges it (big_bpe).
+template <bool CLASSIFY>
+__global__ __launch_bounds__(PT_THREADS) void k_compact(const uint8_t* __restrict__ bytes, Work w, Tables tb,
+                                                        int ntiles, int64_t n, int32_t* __restrict__ starts,
+                                                        int64_t* __restrict__ out_np) {
+  __shared__ uint32_t red[8];
+  __shared__ int32_t sst[TILE + 1];
+  __shared__ uint4 stage[(TILE + CACHE_MAXLEN) / 16];
+  __shared__ uint32_t qn[5], qbase[5];
+  __shared__ BigSmem big;
+  const int t = blockIdx.x;
+  const int lane = (int)(threadIdx.x & 63u);
+  const uint32_t cmask = (1u << TILE_ERR_SHIFT) - 1u;
+  const bool last = t == ntiles - 1;
+  uint32_t hi;
+  // the last tile also folds its own count and error bits into the totals
+  const uint32_t base = block_reduce(w.tile_cnt, last ? t + 1 : t, cmask, red, &hi) -
+                        (last ? (w.tile_cnt[t] & cmask) : 0u);
+  uint32_t bits = w.flags[(int64_t)t * PT_THREADS + threadIdx.x];
+  uint32_t tot;
+  uint32_t lpos = block_excl_sum(__popc(bits), red, &tot);
+  uint32_t pos = base + lpos;
+  const int64_t t0 = (int64_t)t * TILE;
+  const int64_t p0 = t0 + (int64_t)PT_CHUNK * threadIdx.x;
+  while (bits) {
+    const int k = __ffs(bits) - 1;
+    bits &= bits - 1;
+    starts[pos++] = (int32_t)(p0 + k);
+    if (CLASSIFY) sst[lpos++] = (int32_t)(p0 + k);
+  }
+  if (last) {
+    const uint32_t e = (__syncthreads_or(hi & (ERR_UTF8 << TILE_ERR_SHIFT)) ? ERR_UTF8 : 0u) |
+                       (__syncthreads_or(hi & (ERR_OFFSETS << TILE_ERR_SHIFT)) ? ERR_OFFSETS : 0u);
+    const uint32_t P = base + tot;
+    if (threadIdx.x == 0) {
+      w.ctr[CTR_P] = P;
+      w.ctr[CTR_ERR] = e;
+      starts[P] = (int32_t)n;
+      if (out_np) *out_np = e ? err_code(e) : (int64_t)P;
+    }
+  }
+  if (!CLASSIFY || tot == 0) return;
+  {
+    // end of the last piece: the first start after this tile, else n (every
+    // wavefront runs the same search; the ballots keep it wave-uniform)
+    int32_t e = (int32_t)n;
+    for (int b = t + 1; b < ntiles; b += 64) {
+      const int bb = b + lane;
+      const uint64_t nz = __ballot(bb < ntiles && (w.tile_cnt[bb] & cmask) != 0u);
+      if (nz) {
+        const int f = b + __ffsll((unsigned long long)nz) - 1;
+        for (int q = 0; q < PT_THREADS; q += 64) {
+          const uint32_t fl = w.flags[(int64_t)f * PT_THREADS + q + lane];
+          const uint64_t fm = __ballot(fl != 0u);
+          if (fm) {
+            const int l = __ffsll((unsigned long long)fm) - 1;
+            const uint32_t flw = (uint32_t)__shfl((int)fl, l);
+            e = (int32_t)((int64_t)f * TILE + PT_CHUNK * (q + l) + __ffs(flw) - 1);
+            break;
+          }
+        }
+        break;
+      }
+    }
+    if (threadIdx.x == 0) sst[tot] = e;
+  }
+  // the tile's bytes plus CACHE_MAXLEN, for single bytes and table keys
+  const bool aligned = (reinterpret_cast<uintptr_t>(bytes) & 15u) == 0;
+  for (int i = threadIdx.x; i < (TILE + CACHE_MAXLEN) / 16; i += PT_THREADS) {
+    const int64_t g = t0 + 16 * i;
+    uint4 v;
+    if (aligned && g + 16 <= n) {
+      v = *reinterpret_cast<const uint4*>(bytes + g);
+    } else {
+      uint32_t wv[4] = {0u, 0u, 0u, 0u};
+      for (int k = 0; k < 16; ++k)
+        if (g + k < n) wv[k >> 2] |= (uint32_t)bytes[g + k] << (8 * (k & 3));
+      v = make_uint4(wv[0], wv[1], wv[2], wv[3]);
+    }
+    stage[i] = v;
+  }
+  if (threadIdx.x < 5) qn[threadIdx.x] = 0;
+  __syncthreads();
+  const uint8_t* sb = reinterpret_cast<const uint8_t*>(stage);
+  for (uint32_t k0 = 0; k0 < tot; k0 += PT_THREADS) {
+    const uint32_t k = k0 + threadIdx.x;
+    const uint32_t p = base + k;
+    int cls = -1;
+    uint32_t slot = 0;
+    if (k < tot) {
+      const int32_t s = sst[k];
+      const int32_t len = sst[k + 1] - s;
+      const int off = (int)(s - t0);
+      if (len > BIG_BYTES) {
+        // only a tile's last piece can be this long: the tile merges it below
+      } else if (len > LANE_CAP) {
+        cls = 4;
+      } else if (len == 1) {
+        w.tmp_ids[s] = sb[off];
+        w.piece_cnt[p] = 1;
+      } else {
+        uint32_t hit = RANK_NONE;
+        if (len <= CACHE_MAXLEN) {
+          uint64_t w0 = 0, w1 = 0;
+#pragma unroll
+          for (int j = 0; j < CACHE_MAXLEN; ++j) {
+            if (j < len) {
+              const uint64_t by = sb[off + j];
+              if (j < 8) w0 |= by << (8 * j);
+              else w1 |= by << (8 * (j - 8));
+            }
+          }
+          hit = cache_lookup(tb, w0, w1, (uint32_t)len);
+        }
+        if (hit != RANK_NONE) {
+          w.tmp_ids[s] = (int32_t)hit;
+          w.piece_cnt[p] = 1;
+        } else {
+          cls = len <= 8 ? 0 : len <= 16 ? 1 : len <= 32 ? 2 : 3;
+        }
+      }
+      if (cls >= 0) slot = atomicAdd(&qn[cls], 1u);
+    }
+    __syncthreads();
+    if (threadIdx.x < 5) {
+      const uint32_t c = qn[threadIdx.x];
+      uint32_t* ctr = threadIdx.x < 4 ? &w.qctr[(t % QGROUPS) * QCTR_STRIDE + threadIdx.x] : &w.ctr[CTR_NLONG];
+      qbase[threadIdx.x] = c ? atomicAdd(ctr, c) : 0u;
+    }
+    __syncthreads();
+    if (cls >= 0) {
+      uint32_t* q = cls < 4 ? w.queue[cls] + (t % QGROUPS) * w.qcap[cls] : reinterpret_cast<uint32_t*>(w.long_list);
+      q[qbase[cls] + slot] = p;
+    }
+    if (threadIdx.x < 5) qn[threadIdx.x] = 0;
+    __syncthreads();
+  }
+  {
+    // (the piece's end comes from this tile's search: the tile holding the
+    // next start may not have written it yet)
+    const int32_t ls = (int32_t)uniform((uint32_t)sst[tot - 1]);
+    const int32_t lm = (int32_t)uniform((uint32_t)sst[tot]) - ls;
+    if (lm > BIG_BYTES) big_bpe(bytes, w, tb, base + tot - 1, ls, lm, big);
   }
 }
 

@@ -210,6 +210,33 @@ def test_long_pieces_against_oracle():
             assert got == oracle_encode(text, v, GPT2)
 
 
+def test_pieces_over_two_kib_mixed_with_text():
+    # pieces longer than 2 KiB are merged by a whole workgroup (exact rounds
+    # with alternating merges inside runs of equal pairs); mix them with
+    # ordinary text so that every path runs in one call
+    rng = random.Random(44)
+    for name, pattern in (("c2", GPT2), ("c3", CL100K)):
+        v = load(name, pattern)
+        parts = []
+        for i in range(12):
+            parts.append(mix_text(3000, 900 + i))
+            kind = i % 4
+            k = rng.randint(2049, 12000)
+            if kind == 0:
+                parts.append(b" " * k + b"x")
+            elif kind == 1:
+                parts.append(b"9" * k if pattern == GPT2 else b"z" * k)
+            elif kind == 2:
+                parts.append(b" " + "".join(rng.choice("ab") for _ in range(k)).encode())
+            else:
+                parts.append(b"\n" + b"\t " * (k // 2) + b"q")
+        data = b"".join(parts)
+        say("pieces over 2 KiB: %d bytes pattern %d" % (len(data), pattern))
+        got = gpu_encode(data)
+        want = np.asarray(oracle_encode(data, v, pattern, {}), dtype=np.int32)
+        assert np.array_equal(got, want)
+
+
 def test_pipe_line_vocab_on_gpu():
     merges = np.asarray([(112, 105), (256, 112), (257, 101), (108, 105), (259, 110), (260, 101), (258, 261)],
                         dtype=np.int32)
