@@ -223,24 +223,26 @@ int tt_load_bpe(const int32_t* merges, const int32_t* ranks, int64_t n_merges, i
   for (size_t r = 0; r < M; ++r)
     if (mx[r] < 256 && my[r] < 256) byte_pair[(mx[r] << 8) | my[r]] = (uint32_t)r;
 
-  // pair-rank hash: buckets of PAIR_SLOTS entries, load factor <= 1/2
+  // pair-rank hash for pairs with an operand >= 256: buckets of PAIR_SLOTS
+  // entries, load factor <= 1/2
   const uint64_t pair_nb = std::max<uint64_t>(next_pow2((M + 1) / 2), 1024);
-  const int pair_shift = 64 - log2_u64(pair_nb);
-  std::vector<uint64_t> pair_tab(pair_nb * PAIR_SLOTS, PAIR_EMPTY);
+  const int pair_shift = 32 - log2_u64(pair_nb);
+  std::vector<uint64_t> pair_tab(pair_nb * PAIR_SLOTS, 0ull);
   int pair_probe = 1;
   for (size_t r = 0; r < M; ++r) {
-    uint64_t key = pair_key(mx[r], my[r]);
-    uint32_t b = pair_bucket(key, pair_shift);
+    if (mx[r] < 256 && my[r] < 256) continue;
+    uint32_t b = pair_bucket(mx[r], my[r], pair_shift);
     for (int visited = 1;; ++visited, b = (uint32_t)((b + 1) & (pair_nb - 1))) {
       uint64_t* bucket = &pair_tab[(size_t)b * PAIR_SLOTS];
       int slot = -1;
       for (int s = 0; s < PAIR_SLOTS; ++s)
-        if (bucket[s] == PAIR_EMPTY) { slot = s; break; }
+        if ((bucket[s] & ~PAIR_MORE) == 0) { slot = s; break; }
       if (slot >= 0) {
-        bucket[slot] = (key << ID_BITS) | r;
+        bucket[slot] |= (pair_key(mx[r], my[r]) << ID_BITS) | r;
         pair_probe = std::max(pair_probe, visited);
         break;
       }
+      bucket[0] |= PAIR_MORE;  // the probe run goes on past this full bucket
     }
   }
 

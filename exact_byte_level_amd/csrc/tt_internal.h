@@ -36,17 +36,25 @@ enum : uint32_t { LT_S = 1, LT_T = 2, LT_R = 3, LT_E = 4, LT_V = 5, LT_M = 6, LT
 
 // ------------------------------------------------------------------------- BPE
 constexpr uint32_t RANK_NONE = 0xFFFFFFFFu;
-constexpr uint64_t PAIR_EMPTY = ~0ull;
 constexpr int ID_BITS = 20;             // token ids < 2^20
 constexpr uint32_t ID_MASK = (1u << ID_BITS) - 1;
 constexpr int PAIR_SLOTS = 4;           // 32-byte buckets of four 8-byte entries
 
-// Pair-rank hash entry: (left << 40) | (right << 20) | rank.
+// Pair-rank table for pairs with an operand >= 256 (byte pairs have their own
+// direct table): entry (left << 40) | (right << 20) | rank, 0 = empty.  Bit 63
+// of a bucket's first entry is set if some key's probe run passed this bucket
+// (it was full): a lookup stops at the first bucket without it.
+constexpr uint64_t PAIR_MORE = 1ull << 63;
 __host__ __device__ inline uint64_t pair_key(uint32_t x, uint32_t y) {
   return ((uint64_t)x << ID_BITS) | (uint64_t)y;
 }
-__host__ __device__ inline uint32_t pair_bucket(uint64_t key, int shift) {
-  return (uint32_t)((key * 0x9E3779B97F4A7C15ull) >> shift);
+// Bucket of (x, y): 24-bit products (x, y < 2^20), an xor-shift and one
+// 32-bit product; shift = 32 - log2(buckets).
+__host__ __device__ inline uint32_t pair_bucket(uint32_t x, uint32_t y, int shift) {
+  uint32_t h = (uint32_t)(x * 0x9E3779u) ^ (uint32_t)(y * 0x7FEB35u);
+  h ^= h >> 13;
+  h *= 0x85EBCA6Bu;
+  return h >> shift;
 }
 
 // Whole-pre-token table: buckets of CACHE_SLOTS entries in one 128-byte line
@@ -79,7 +87,7 @@ struct Tables {
   const uint64_t* pair_tab;     // [pair_nb * PAIR_SLOTS]
   const CacheBucket* cache;     // [cache_nb]
   uint32_t pair_mask;           // pair_nb - 1
-  int pair_shift;               // 64 - log2(pair_nb)
+  int pair_shift;               // 32 - log2(pair_nb)
   int pair_probe;               // max buckets visited by any key
   uint32_t cache_mask;          // cache_nb - 1
   int cache_shift;              // 64 - log2(cache_nb)

@@ -641,22 +641,27 @@ __global__ __launch_bounds__(PT_THREADS) void k_pretok(const uint8_t* __restrict
 
 // ----------------------------------------------------------------------- BPE
 
-// Rank of merging the adjacent pair (x, y), or RANK_NONE.
+// Rank of merging the adjacent pair (x, y), or RANK_NONE.  Branch-free in
+// the common case: the byte-pair entry and the first bucket are loaded
+// together and the four slots compared with selects; further buckets only
+// while the bucket says a probe run went past it.
 __device__ __forceinline__ uint32_t pair_rank(const Tables& tb, uint32_t x, uint32_t y) {
-  if ((x | y) < 256u) return tb.byte_pair[(x << 8) | y];
-  const uint64_t key = pair_key(x, y);
-  uint32_t b = pair_bucket(key, tb.pair_shift);
+  const uint32_t bp = tb.byte_pair[((x & 255u) << 8) | (y & 255u)];
+  const uint64_t k20 = pair_key(x, y) << ID_BITS;
+  constexpr uint64_t LOW = ~PAIR_MORE;
+  uint32_t b = pair_bucket(x, y, tb.pair_shift);
+  uint32_t r = RANK_NONE;
   for (int i = 0; i < tb.pair_probe; ++i) {
-    const ulonglong2* bp = reinterpret_cast<const ulonglong2*>(tb.pair_tab + (size_t)b * PAIR_SLOTS);
-    ulonglong2 e0 = bp[0], e1 = bp[1];
-    if ((e0.x >> ID_BITS) == key) return (uint32_t)(e0.x & ID_MASK);
-    if ((e0.y >> ID_BITS) == key) return (uint32_t)(e0.y & ID_MASK);
-    if ((e1.x >> ID_BITS) == key) return (uint32_t)(e1.x & ID_MASK);
-    if ((e1.y >> ID_BITS) == key) return (uint32_t)(e1.y & ID_MASK);
-    if (e1.y == PAIR_EMPTY) return RANK_NONE;
+    const ulonglong2* q = reinterpret_cast<const ulonglong2*>(tb.pair_tab + (size_t)b * PAIR_SLOTS);
+    const ulonglong2 e0 = q[0], e1 = q[1];
+    r = ((e0.x & LOW) ^ k20) < (1ull << ID_BITS) ? (uint32_t)e0.x & ID_MASK : r;
+    r = (e0.y ^ k20) < (1ull << ID_BITS) ? (uint32_t)e0.y & ID_MASK : r;
+    r = (e1.x ^ k20) < (1ull << ID_BITS) ? (uint32_t)e1.x & ID_MASK : r;
+    r = (e1.y ^ k20) < (1ull << ID_BITS) ? (uint32_t)e1.y & ID_MASK : r;
+    if (r != RANK_NONE || !(e0.x & PAIR_MORE)) break;
     b = (b + 1) & tb.pair_mask;
   }
-  return RANK_NONE;
+  return (x | y) < 256u ? bp : r;
 }
 
 // Id of the single-token piece with these bytes (len 2..16), or RANK_NONE.
