@@ -5,13 +5,19 @@
 //         parallel from char classes, maximal same-class runs, the offset in a
 //         run, a few chars of context and run-level facts (k_tile_summary,
 //         k_pretok, k_compact);
-//   §4.2  BPE per piece, pieces independent, tiered by length: one lane per
-//         short piece (k_bpe_short), a cooperative exact merge loop for long
-//         ones (k_bpe_long); the whole-piece lookup of single-token pieces is
-//         the exact form of the vocabulary short-circuit the page mentions;
+//   §4.2  BPE per piece, pieces independent, tiered by length: the
+//         whole-piece lookup of single-token pieces (the exact form of the
+//         vocabulary short-circuit the page mentions) and queueing by length
+//         class in k_compact; group merges of up to 64-byte pieces, one byte
+//         position per lane, and exact global-minimum rounds for longer
+//         pieces, a wavefront each (k_bpe_merge) or, past 2 KiB, a workgroup
+//         each (big_bpe, run by the tile where the piece starts);
 //   §4.3  no host synchronisation between kernels: every size a kernel needs
 //         after the first is read on the device (grids are sized for the
 //         worst case and exit early), so the chain is graph-capturable.
+//
+// Passes of one encode: k_tile_summary (cl100k-style rules only), k_pretok,
+// k_compact, k_bpe_merge, k_emit_sums, k_emit.
 //
 // Hot-path data (all integer; no floating point, no MFMA):
 //   bytes   uint8[n]         caller's UTF-8 text
