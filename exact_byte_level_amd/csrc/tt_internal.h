@@ -124,7 +124,8 @@ struct Work {
   int32_t* piece_cnt;    // [n] tokens of each piece
   int32_t* tmp_ids;      // [n] tokens of the piece starting at byte s live at [s, s + cnt)
   uint32_t* tmp_rank;    // [n] pair ranks for the long-piece merge loop
-  int32_t* tok_off;      // [n + 1] token offset of each piece (first its offset inside its emission unit)
+  int32_t* tok_off;      // [n + 1] token offset of each piece; [P] = T
+  int32_t* tok_in;       // [n] token offset of each piece inside its emission unit
   uint32_t* blk_sum;     // [n / EMIT_UNIT + 1] tokens of each emission unit
   int32_t* long_list;    // [n / (LANE_CAP + 1) + 1] pieces of LANE_CAP + 1 .. BIG_BYTES bytes
   int32_t* huge_list;    // [n / (HUGE_TOKENS + 1) + 1] pieces with more than HUGE_TOKENS tokens

@@ -647,6 +647,22 @@ __global__ __launch_bounds__(PT_THREADS) void k_pretok(const uint8_t* __restrict
 
 // ----------------------------------------------------------------------- BPE
 
+// Rank in a bucket's four slots of the key k20 = pair_key(x, y) << ID_BITS,
+// or RANK_NONE.
+__device__ __forceinline__ uint32_t bucket_match(const ulonglong2& e0, const ulonglong2& e1, uint64_t k20) {
+  constexpr uint64_t LOW = ~PAIR_MORE;
+  uint32_t r = RANK_NONE;
+  r = ((e0.x & LOW) ^ k20) < (1ull << ID_BITS) ? (uint32_t)e0.x & ID_MASK : r;
+  r = (e0.y ^ k20) < (1ull << ID_BITS) ? (uint32_t)e0.y & ID_MASK : r;
+  r = (e1.x ^ k20) < (1ull << ID_BITS) ? (uint32_t)e1.x & ID_MASK : r;
+  r = (e1.y ^ k20) < (1ull << ID_BITS) ? (uint32_t)e1.y & ID_MASK : r;
+  return r;
+}
+
+__device__ __forceinline__ const ulonglong2* pair_bucket_ptr(const Tables& tb, uint32_t b) {
+  return reinterpret_cast<const ulonglong2*>(tb.pair_tab + (size_t)b * PAIR_SLOTS);
+}
+
 // Rank of merging the adjacent pair (x, y), or RANK_NONE.  Branch-free in
 // the common case: the byte-pair entry and the first bucket are loaded
 // together and the four slots compared with selects; further buckets only
@@ -654,16 +670,12 @@ __global__ __launch_bounds__(PT_THREADS) void k_pretok(const uint8_t* __restrict
 __device__ __forceinline__ uint32_t pair_rank(const Tables& tb, uint32_t x, uint32_t y) {
   const uint32_t bp = tb.byte_pair[((x & 255u) << 8) | (y & 255u)];
   const uint64_t k20 = pair_key(x, y) << ID_BITS;
-  constexpr uint64_t LOW = ~PAIR_MORE;
   uint32_t b = pair_bucket(x, y, tb.pair_shift);
   uint32_t r = RANK_NONE;
   for (int i = 0; i < tb.pair_probe; ++i) {
-    const ulonglong2* q = reinterpret_cast<const ulonglong2*>(tb.pair_tab + (size_t)b * PAIR_SLOTS);
+    const ulonglong2* q = pair_bucket_ptr(tb, b);
     const ulonglong2 e0 = q[0], e1 = q[1];
-    r = ((e0.x & LOW) ^ k20) < (1ull << ID_BITS) ? (uint32_t)e0.x & ID_MASK : r;
-    r = (e0.y ^ k20) < (1ull << ID_BITS) ? (uint32_t)e0.y & ID_MASK : r;
-    r = (e1.x ^ k20) < (1ull << ID_BITS) ? (uint32_t)e1.x & ID_MASK : r;
-    r = (e1.y ^ k20) < (1ull << ID_BITS) ? (uint32_t)e1.y & ID_MASK : r;
+    r = bucket_match(e0, e1, k20);
     if (r != RANK_NONE || !(e0.x & PAIR_MORE)) break;
     b = (b + 1) & tb.pair_mask;
   }
@@ -1177,9 +1189,9 @@ __global__ __launch_bounds__(PT_THREADS) void k_compact(const uint8_t* __restric
 
 // Pass 5: BPE of the queued pieces.  Work items are wavefront loads: one long
 // piece, one piece of <= 64 bytes, two of <= 32, four of <= 16 or eight of
-// <= 8, numbered longest class first and dealt round-robin to the wavefronts
-// of the grid, so the longest merge chains start first and spread over the
-// whole chip.  The item index is the same in every lane, so the loop and the
+// <= 8, numbered longest class first and dealt round-robin to the
+// wavefronts of the grid, so the longest merge chains start first and spread
+// over the whole chip.  The item index is the same in every lane, so the loop and the
 // class branches are scalar.
 constexpr int MERGE_THREADS = 256;
 __global__ __launch_bounds__(MERGE_THREADS) void k_bpe_merge(const uint8_t* __restrict__ bytes, Work w, Tables tb) {
@@ -1226,7 +1238,7 @@ __global__ __launch_bounds__(MERGE_THREADS) void k_bpe_merge(const uint8_t* __re
 // ------------------------------------------------------------------ emission
 
 // Pass 6: token count of each emission unit of 256 pieces, and each piece's
-// token offset inside its unit (in tok_off).
+// token offset inside its unit (tok_in).
 __global__ __launch_bounds__(EMIT_UNIT) void k_emit_sums(Work w) {
   __shared__ uint32_t red[8];
   const uint32_t P = w.ctr[CTR_P];
@@ -1235,7 +1247,7 @@ __global__ __launch_bounds__(EMIT_UNIT) void k_emit_sums(Work w) {
     const uint32_t c = p < P ? (uint32_t)w.piece_cnt[p] : 0u;
     uint32_t tot;
     const uint32_t e = block_excl_sum(c, red, &tot);
-    if (p < P) w.tok_off[p] = (int32_t)e;
+    if (p < P) w.tok_in[p] = (int32_t)e;
     if (threadIdx.x == 0) w.blk_sum[u] = tot;
   }
 }
@@ -1248,7 +1260,8 @@ constexpr uint32_t HUGE_CHUNK = 16384;  // tokens per grid work item of a huge p
 // wavefront.  Pieces with more tokens are cut into HUGE_CHUNK-token items
 // dealt round-robin to the workgroups.  The workgroup with the last unit
 // writes T (and tok_off[P]); *out_n, if given, gets T or the error code.
-__global__ __launch_bounds__(EMIT_UNIT) void k_emit(Work w, int32_t* __restrict__ out_ids, int64_t* __restrict__ out_n) {
+__global__ __launch_bounds__(EMIT_UNIT) void k_emit(Work w, int32_t* __restrict__ out_ids, int64_t* __restrict__ out_n,
+                                                    uint32_t cap) {
   __shared__ uint32_t red[8];
   const uint32_t P = w.ctr[CTR_P];
   const uint32_t nunits = (P + EMIT_UNIT - 1) / EMIT_UNIT;
@@ -1260,7 +1273,7 @@ __global__ __launch_bounds__(EMIT_UNIT) void k_emit(Work w, int32_t* __restrict_
     const bool live = p < P;
     const uint32_t c = live ? (uint32_t)w.piece_cnt[p] : 0u;
     const uint32_t src = live ? (uint32_t)w.piece_start[p] : 0u;
-    const uint32_t off = live ? base + (uint32_t)w.tok_off[p] : 0u;
+    const uint32_t off = live ? base + (uint32_t)w.tok_in[p] : 0u;
     if (live) {
       w.tok_off[p] = (int32_t)off;
       if (c <= 8) {
@@ -1297,10 +1310,12 @@ __global__ __launch_bounds__(EMIT_UNIT) void k_emit(Work w, int32_t* __restrict_
     item += nch;
     if (first >= nch) continue;
     const uint32_t u = p / EMIT_UNIT;
-    const uint32_t dst = block_reduce(w.blk_sum, (int)u, ~0u, red, &hi) + (uint32_t)w.tok_off[p];
+    // (tok_in, not tok_off: the piece's own workgroup may already have
+    // replaced its tok_off by the final offset)
+    const uint32_t dst = block_reduce(w.blk_sum, (int)u, ~0u, red, &hi) + (uint32_t)w.tok_in[p];
     const uint32_t src = (uint32_t)w.piece_start[p];
     for (uint32_t ch = first; ch < nch; ch += gridDim.x) {
-      const uint32_t k1 = min(cc, (ch + 1) * HUGE_CHUNK);
+      const uint32_t k1 = min(min(cc, (ch + 1) * HUGE_CHUNK), cap - min(cap, dst));  // never past the output
       for (uint32_t k = ch * HUGE_CHUNK + threadIdx.x; k < k1; k += EMIT_UNIT) out_ids[dst + k] = w.tmp_ids[src + k];
     }
   }
@@ -1391,7 +1406,7 @@ hipError_t launch_bpe_emit(const uint8_t* bytes, int64_t n, const Tables& tb, co
   // grid-stride passes over at most n pieces
   const int g = capped_grid(n, EMIT_UNIT, GRID_CAP);
   hipLaunchKernelGGL(k_emit_sums, dim3(g), dim3(EMIT_UNIT), 0, st, w); prof_mark("k_emit_sums", st);
-  hipLaunchKernelGGL(k_emit, dim3(g), dim3(EMIT_UNIT), 0, st, w, out_ids, out_n); prof_mark("k_emit", st);
+  hipLaunchKernelGGL(k_emit, dim3(g), dim3(EMIT_UNIT), 0, st, w, out_ids, out_n, (uint32_t)n); prof_mark("k_emit", st);
   return hipGetLastError();
 }
 
