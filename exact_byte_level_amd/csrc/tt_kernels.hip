@@ -32,8 +32,11 @@ namespace tt {
 
 // ------------------------------------------------------------ Unicode classes
 
-__device__ const uint8_t g_uni_l1[TT_UNI_L1_SIZE] = {TT_UNI_L1_DATA};
-__device__ const uint8_t g_uni_l2[TT_UNI_NBLOCKS * 64] = {TT_UNI_L2_DATA};
+// (sizes rounded up to 16 bytes so that workgroups stage them with 16-byte loads)
+constexpr int UNI_L1_PAD = (TT_UNI_L1_SIZE + 15) / 16 * 16;
+constexpr int UNI_L2_PAD = (TT_UNI_NBLOCKS * 64 + 15) / 16 * 16;
+alignas(16) __device__ const uint8_t g_uni_l1[UNI_L1_PAD] = {TT_UNI_L1_DATA};
+alignas(16) __device__ const uint8_t g_uni_l2[UNI_L2_PAD] = {TT_UNI_L2_DATA};
 
 struct AsciiTab {
   uint16_t v[128];
@@ -90,8 +93,8 @@ struct TileSmem {
   uint16_t code[CODE_SLOTS];
   uint16_t ascii[128];
   uint32_t bmap[BMAP_WORDS];
-  uint8_t l1[TT_UNI_L1_SIZE];
-  uint8_t l2[TT_UNI_NBLOCKS * 64];
+  alignas(16) uint8_t l1[UNI_L1_PAD];
+  alignas(16) uint8_t l2[UNI_L2_PAD];
   uint32_t red[8];
   int64_t seq_lo, seq_hi;
   uint32_t carry_fwd, carry_bwd;
@@ -173,9 +176,10 @@ __device__ __forceinline__ uint16_t decode_at(int64_t n, int64_t base, int j, co
 // one 16-byte load per thread (byte loads only at the text edges or for an
 // unaligned text), the sequence-boundary bitmap, the Unicode table if some byte
 // is non-ASCII, then the codes of positions [t0 - HALO, t0 + TILE + HALO).
-// Returns true if some char starting inside the tile is invalid UTF-8.
+// Returns true if some char starting inside the tile is invalid UTF-8;
+// *non_ascii (same in every thread) tells whether any staged byte is >= 0x80.
 __device__ bool load_tile(const uint8_t* __restrict__ bytes, int64_t n, const int64_t* __restrict__ offs,
-                          int nseq, int64_t t0, TileSmem& sm) {
+                          int nseq, int64_t t0, TileSmem& sm, bool* non_ascii = nullptr) {
   const int tid = threadIdx.x;
   const int64_t base = t0 - HALO;
   const bool aligned = (reinterpret_cast<uintptr_t>(bytes) & 15u) == 0;
@@ -208,6 +212,7 @@ __device__ bool load_tile(const uint8_t* __restrict__ bytes, int64_t n, const in
     }
   }
   const bool na = __syncthreads_or((hi_bits & 0x80808080u) != 0u);
+  if (non_ascii) *non_ascii = na;
   if (offs) {
     for (int64_t s = sm.seq_lo + tid; s < sm.seq_hi; s += PT_THREADS) {
       int64_t j = offs[s] - base;
@@ -218,8 +223,10 @@ __device__ bool load_tile(const uint8_t* __restrict__ bytes, int64_t n, const in
     if (j < (int64_t)BMAP_WORDS * 32) sm.bmap[j >> 5] |= 1u << (j & 31);
   }
   if (na) {
-    for (int i = tid; i < TT_UNI_L1_SIZE; i += PT_THREADS) sm.l1[i] = g_uni_l1[i];
-    for (int i = tid; i < TT_UNI_NBLOCKS * 64; i += PT_THREADS) sm.l2[i] = g_uni_l2[i];
+    for (int i = tid; i < UNI_L1_PAD / 16; i += PT_THREADS)
+      reinterpret_cast<uint4*>(sm.l1)[i] = reinterpret_cast<const uint4*>(g_uni_l1)[i];
+    for (int i = tid; i < UNI_L2_PAD / 16; i += PT_THREADS)
+      reinterpret_cast<uint4*>(sm.l2)[i] = reinterpret_cast<const uint4*>(g_uni_l2)[i];
   }
   __syncthreads();
   bool bad = false;
@@ -459,8 +466,11 @@ __device__ void tile_carries(const Work& w, int t, int ntiles, TileSmem& sm) {
 __device__ __forceinline__ uint32_t cat(const uint16_t* c, int j) { return c[cix(j)]; }
 
 // Previous char start before tile position j, or -1 at a sequence start.
+// With ASCII (no byte >= 0x80 in the staged span) every byte starts a char.
+template <bool ASCII>
 __device__ __forceinline__ int prev_char(const uint16_t* c, int j) {
   if (cat(c, j) & K_SEQ_START) return -1;
+  if (ASCII) return j - 1;
   int k = j - 1;
   while (k > 0 && cls_of(cat(c, k)) == C_CONT && k > j - 4) --k;
   return k;
@@ -468,20 +478,21 @@ __device__ __forceinline__ int prev_char(const uint16_t* c, int j) {
 
 // The apostrophe at q starts a piece: it is a one-char "other" run that no
 // space in front of it absorbs.
+template <bool ASCII>
 __device__ __forceinline__ bool ap_starts_piece(const uint16_t* c, int q) {
   uint32_t cq = cat(c, q);
   if (!(cq & K_AP)) return false;
   if (cq & K_SEQ_START) return true;
-  uint32_t cr = cat(c, prev_char(c, q));
+  uint32_t cr = cat(c, prev_char<ASCII>(c, q));
   return cls_of(cr) != C_O && !(cr & K_SP);
 }
 
 // Length (1 or 2) of a contraction suffix whose first letter is at a, or 0.
-template <int PAT>
+template <int PAT, bool ASCII>
 __device__ __forceinline__ int contraction_len(const uint16_t* c, int a) {
   uint32_t ca = cat(c, a);
   if (ca & K_SEQ_START) return 0;
-  if (!ap_starts_piece(c, prev_char(c, a))) return 0;
+  if (!ap_starts_piece<ASCII>(c, prev_char<ASCII>(c, a))) return 0;
   if (PAT == 0 && (ca & K_UPPER)) return 0;
   uint32_t lt = (ca >> K_LETTER_SHIFT) & 15u;
   if (lt == LT_S || lt == LT_T || lt == LT_M || lt == LT_D) return 1;
@@ -495,50 +506,52 @@ __device__ __forceinline__ int contraction_len(const uint16_t* c, int a) {
 }
 
 // Letter at j is the first letter after a contraction suffix.
-template <int PAT>
+template <int PAT, bool ASCII>
 __device__ __forceinline__ bool after_contraction(const uint16_t* c, int j) {
-  int a = prev_char(c, j);
+  int a = prev_char<ASCII>(c, j);
   if (a < 0) return false;
-  if (contraction_len<PAT>(c, a) == 1) return true;
-  int a2 = prev_char(c, a);
-  return a2 >= 0 && contraction_len<PAT>(c, a2) == 2;
+  if (contraction_len<PAT, ASCII>(c, a) == 1) return true;
+  int a2 = prev_char<ASCII>(c, a);
+  return a2 >= 0 && contraction_len<PAT, ASCII>(c, a2) == 2;
 }
 
+template <bool ASCII>
 __device__ __forceinline__ bool pred_gpt2(const uint16_t* c, int j) {
   uint32_t c0 = cat(c, j);
   if (c0 & K_SEQ_START) return true;
   uint32_t k0 = cls_of(c0);
-  int p1 = prev_char(c, j);
+  int p1 = prev_char<ASCII>(c, j);
   uint32_t c1 = cat(c, p1), k1 = cls_of(c1);
   if (is_w(k0)) {
     if (!is_w(k1)) return true;
     if (c0 & K_SEQ_LAST) return false;
-    return !is_w(cls_of(cat(c, j + clen(c0))));
+    return !is_w(cls_of(cat(c, j + (ASCII ? 1 : clen(c0)))));
   }
-  if (k1 == k0) return k0 == C_L && after_contraction<0>(c, j);
+  if (k1 == k0) return k0 == C_L && after_contraction<0, ASCII>(c, j);
   if (c1 & K_SP) return false;
-  if (k0 == C_L && contraction_len<0>(c, j) > 0) return false;
+  if (k0 == C_L && contraction_len<0, ASCII>(c, j) > 0) return false;
   return true;
 }
 
 // fwd_prev: forward run state at the previous char; fwd_here: at this char;
 // ends_run: the whitespace run through this char is followed by no CR/LF.
+template <bool ASCII>
 __device__ __forceinline__ bool pred_cl100k(const uint16_t* c, int j, uint32_t fwd_prev, uint32_t fwd_here,
                                             bool ends_run) {
   uint32_t c0 = cat(c, j);
   if (c0 & K_SEQ_START) return true;
   uint32_t k0 = cls_of(c0);
-  int p1 = prev_char(c, j);
+  int p1 = prev_char<ASCII>(c, j);
   uint32_t c1 = cat(c, p1), k1 = cls_of(c1);
   switch (k0) {
     case C_N:
       return k1 != C_N || ((fwd_here >> 8) & 3u) == 1u;
     case C_L:
-      if (k1 == C_L) return after_contraction<1>(c, j);
+      if (k1 == C_L) return after_contraction<1, ASCII>(c, j);
       if (k1 == C_WS) return false;
       if (k1 == C_O) {
         if (c1 & K_SEQ_START) return false;
-        uint32_t c2 = cat(c, prev_char(c, p1));
+        uint32_t c2 = cat(c, prev_char<ASCII>(c, p1));
         return !(cls_of(c2) != C_O && !(c2 & K_SP));
       }
       return true;
@@ -552,7 +565,7 @@ __device__ __forceinline__ bool pred_cl100k(const uint16_t* c, int j, uint32_t f
       if (!is_w(k1)) return true;
       if (k1 == C_WN) return ends_run || ((fwd_prev >> 5) & 7u) == C_O;
       if (c0 & K_SEQ_LAST) return false;
-      return !is_w(cls_of(cat(c, j + clen(c0))));
+      return !is_w(cls_of(cat(c, j + (ASCII ? 1 : clen(c0)))));
   }
   return false;
 }
@@ -599,7 +612,8 @@ __global__ __launch_bounds__(PT_THREADS) void k_pretok(const uint8_t* __restrict
     if (threadIdx.x < CTR_RESET_END) w.ctr[threadIdx.x] = 0u;
     for (int i = threadIdx.x; i < QGROUPS * QCTR_STRIDE; i += PT_THREADS) w.qctr[i] = 0u;
   }
-  const bool bad = load_tile(bytes, n, offs, nseq, t0, sm);
+  bool na;
+  const bool bad = load_tile(bytes, n, offs, nseq, t0, sm, &na);
   bool bad_off = false;
   if (offs) {
     for (int64_t q = (int64_t)t * PT_THREADS + threadIdx.x; q <= nseq; q += (int64_t)ntiles * PT_THREADS) {
@@ -610,10 +624,18 @@ __global__ __launch_bounds__(PT_THREADS) void k_pretok(const uint8_t* __restrict
   const int j0 = HALO + PT_CHUNK * threadIdx.x;
   uint32_t bits = 0;
   if (PAT == 0) {
+    if (na) {
 #pragma unroll
-    for (int k = 0; k < PT_CHUNK; ++k) {
-      uint32_t c = sm.code[cix(j0 + k)];
-      if (is_char(c) && pred_gpt2(sm.code, j0 + k)) bits |= 1u << k;
+      for (int k = 0; k < PT_CHUNK; ++k) {
+        uint32_t c = sm.code[cix(j0 + k)];
+        if (is_char(c) && pred_gpt2<false>(sm.code, j0 + k)) bits |= 1u << k;
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < PT_CHUNK; ++k) {
+        uint32_t c = sm.code[cix(j0 + k)];
+        if (is_char(c) && pred_gpt2<true>(sm.code, j0 + k)) bits |= 1u << k;
+      }
     }
   } else {
     tile_carries(w, t, ntiles, sm);
@@ -629,13 +651,25 @@ __global__ __launch_bounds__(PT_THREADS) void k_pretok(const uint8_t* __restrict
       }
     }
     uint32_t sf = FwdOp::combine(sm.carry_fwd, block_excl_fwd<FwdOp>(chunk_fwd(sm), sm.red, &tot));
+    if (na) {
 #pragma unroll
-    for (int k = 0; k < PT_CHUNK; ++k) {
-      uint32_t c = sm.code[cix(j0 + k)];
-      if (is_char(c)) {
-        uint32_t before = sf;
-        sf = FwdOp::combine(sf, FwdOp::elem(c));
-        if (pred_cl100k(sm.code, j0 + k, before, sf, (ends >> k) & 1u)) bits |= 1u << k;
+      for (int k = 0; k < PT_CHUNK; ++k) {
+        uint32_t c = sm.code[cix(j0 + k)];
+        if (is_char(c)) {
+          uint32_t before = sf;
+          sf = FwdOp::combine(sf, FwdOp::elem(c));
+          if (pred_cl100k<false>(sm.code, j0 + k, before, sf, (ends >> k) & 1u)) bits |= 1u << k;
+        }
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < PT_CHUNK; ++k) {
+        uint32_t c = sm.code[cix(j0 + k)];
+        if (is_char(c)) {
+          uint32_t before = sf;
+          sf = FwdOp::combine(sf, FwdOp::elem(c));
+          if (pred_cl100k<true>(sm.code, j0 + k, before, sf, (ends >> k) & 1u)) bits |= 1u << k;
+        }
       }
     }
   }
