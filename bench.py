@@ -54,8 +54,6 @@ def alg_bytes(kernel, n, P, T):
         return n / 8 + 4 * (P + 1) + n + 4 * T + 4 * P
     if kernel == "k_emit":
         return 12 * P + 8 * T       # counts, starts, tokens in; offsets, ids out
-    if kernel == "k_emit_sums":
-        return 4 * P
     return 0
 
 

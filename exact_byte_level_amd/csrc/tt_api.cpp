@@ -126,8 +126,8 @@ size_t layout(int64_t n, char* base, Work* w) {
   t.tmp_ids = (int32_t*)take(nn * 4);
   t.tmp_rank = (uint32_t*)take(nn * 4);
   t.tok_off = (int32_t*)take((nn + 1) * 4);
-  t.tok_in = (int32_t*)take(nn * 4);
-  t.blk_sum = (uint32_t*)take((nn / EMIT_UNIT + 2) * 4);
+  t.tile_tok = (uint32_t*)take(ntiles * 4);
+  t.tile_pbase = (uint32_t*)take(ntiles * 4);
   t.long_list = (int32_t*)take((nn / (LANE_CAP + 1) + 2) * 4);
   t.huge_list = (int32_t*)take((nn / (HUGE_TOKENS + 1) + 2) * 4);
   // a class-c sub-queue takes the pieces of at least QCLASS_MINLEN[c] bytes

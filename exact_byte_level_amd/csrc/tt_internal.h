@@ -125,8 +125,8 @@ struct Work {
   int32_t* tmp_ids;      // [n] tokens of the piece starting at byte s live at [s, s + cnt)
   uint32_t* tmp_rank;    // [n] pair ranks for the long-piece merge loop
   int32_t* tok_off;      // [n + 1] token offset of each piece; [P] = T
-  int32_t* tok_in;       // [n] token offset of each piece inside its emission unit
-  uint32_t* blk_sum;     // [n / EMIT_UNIT + 1] tokens of each emission unit
+  uint32_t* tile_tok;    // [ntiles] tokens of the pieces that start in each tile
+  uint32_t* tile_pbase;  // [ntiles] index of the first piece that starts in each tile
   int32_t* long_list;    // [n / (LANE_CAP + 1) + 1] pieces of LANE_CAP + 1 .. BIG_BYTES bytes
   int32_t* huge_list;    // [n / (HUGE_TOKENS + 1) + 1] pieces with more than HUGE_TOKENS tokens
   // Pieces for group BPE by class c (<= 8, 16, 32, 64 bytes).  Tile t
@@ -142,8 +142,7 @@ struct Work {
 // ------------------------------------------------------------- BPE tiers
 constexpr int LANE_CAP = 64;            // pieces up to this many bytes: group BPE in one wavefront
 constexpr int BIG_BYTES = 2048;         // longer pieces: merged by the workgroup of the tile they start in
-constexpr int EMIT_UNIT = 256;          // pieces per emission unit (one workgroup pass)
+constexpr int EMIT_THREADS = 256;       // emission workgroup (one tile's pieces)
 constexpr int HUGE_TOKENS = 64;         // pieces with more tokens are copied by the whole grid
-constexpr int GRID_CAP = 1024;          // workgroups of the grid-stride passes
 
 }  // namespace tt

@@ -17,7 +17,7 @@
 //         worst case and exit early), so the chain is graph-capturable.
 //
 // Passes of one encode: k_tile_summary (cl100k-style rules only), k_pretok,
-// k_compact, k_bpe_merge, k_emit_sums, k_emit.
+// k_compact, k_bpe_merge, k_emit.
 //
 // Hot-path data (all integer; no floating point, no MFMA):
 //   bytes   uint8[n]         caller's UTF-8 text
@@ -822,6 +822,24 @@ __device__ void group_bpe(const uint8_t* __restrict__ bytes, const Work& w, cons
     if (g < m) w.tmp_ids[s + g] = (int32_t)id;
     if (g == 0) w.piece_cnt[p] = m;
   }
+  // token counts into the tiles the pieces start in: the group leaders' tiles
+  // and counts are read into scalar registers and runs of equal tiles (the
+  // pieces are consecutive queue entries) summed, one atomic per run
+  const uint32_t tl = (valid && g == 0) ? (uint32_t)s / TILE : 0xFFFFFFFFu;
+  const uint32_t val = (valid && g == 0) ? (uint32_t)m : 0u;
+  uint32_t cur_t = 0xFFFFFFFFu, cur_sum = 0;
+#pragma unroll
+  for (int q = 0; q < 64 / G; ++q) {
+    const uint32_t tq = (uint32_t)__builtin_amdgcn_readlane((int)tl, q * G);
+    const uint32_t vq = (uint32_t)__builtin_amdgcn_readlane((int)val, q * G);
+    if (tq != cur_t) {
+      if (cur_t != 0xFFFFFFFFu && lane == 0) atomicAdd(&w.tile_tok[cur_t], cur_sum);
+      cur_t = tq;
+      cur_sum = 0;
+    }
+    cur_sum += vq;
+  }
+  if (cur_t != 0xFFFFFFFFu && lane == 0) atomicAdd(&w.tile_tok[cur_t], cur_sum);
 }
 
 __device__ __forceinline__ uint32_t wave_min(uint32_t x) {
@@ -911,6 +929,7 @@ __device__ void long_bpe(const uint8_t* __restrict__ bytes, const Work& w, const
   }
   if (lane == 0) {
     w.piece_cnt[p] = m;
+    atomicAdd(&w.tile_tok[s / TILE], (uint32_t)m);
     if (m > HUGE_TOKENS) w.huge_list[atomicAdd(&w.ctr[CTR_NHUGE], 1u)] = (int32_t)p;
   }
 }
@@ -958,8 +977,8 @@ struct BigSmem {
 // the right one.  A block prefix sum of the surviving positions places the
 // compacted ids; all reads of a step finish (barrier) before its writes,
 // which land at or left of the positions read.
-__device__ void big_bpe(const uint8_t* __restrict__ bytes, const Work& w, const Tables& tb, uint32_t p,
-                        int32_t s, int m, BigSmem& sm) {
+__device__ int big_bpe(const uint8_t* __restrict__ bytes, const Work& w, const Tables& tb, uint32_t p,
+                       int32_t s, int m, BigSmem& sm) {
   const int tid = (int)threadIdx.x, lane = tid & 63, wid = tid >> 6;
   uint32_t* I = reinterpret_cast<uint32_t*>(w.tmp_ids) + s;
   uint32_t* R = w.tmp_rank + s;
@@ -1062,6 +1081,7 @@ __device__ void big_bpe(const uint8_t* __restrict__ bytes, const Work& w, const 
     w.piece_cnt[p] = m;
     if (m > HUGE_TOKENS) w.huge_list[atomicAdd(&w.ctr[CTR_NHUGE], 1u)] = (int32_t)p;
   }
+  return m;
 }
 
 // Pass 3: piece starts in order, from the counts of the tiles before and a
@@ -1116,7 +1136,12 @@ __global__ __launch_bounds__(PT_THREADS) void k_compact(const uint8_t* __restric
       if (out_np) *out_np = e ? err_code(e) : (int64_t)P;
     }
   }
-  if (!CLASSIFY || tot == 0) return;
+  if (threadIdx.x == 0) w.tile_pbase[t] = base;
+  if (!CLASSIFY) return;
+  if (tot == 0) {
+    if (threadIdx.x == 0) w.tile_tok[t] = 0u;
+    return;
+  }
   {
     // end of the last piece: the first start after this tile, else n (every
     // wavefront runs the same search; the ballots keep it wave-uniform)
@@ -1159,6 +1184,7 @@ __global__ __launch_bounds__(PT_THREADS) void k_compact(const uint8_t* __restric
   if (threadIdx.x < 5) qn[threadIdx.x] = 0;
   __syncthreads();
   const uint8_t* sb = reinterpret_cast<const uint8_t*>(stage);
+  uint32_t fin = 0;  // pieces of one token finished here
   for (uint32_t k0 = 0; k0 < tot; k0 += PT_THREADS) {
     const uint32_t k = k0 + threadIdx.x;
     const uint32_t p = base + k;
@@ -1175,6 +1201,7 @@ __global__ __launch_bounds__(PT_THREADS) void k_compact(const uint8_t* __restric
       } else if (len == 1) {
         w.tmp_ids[s] = sb[off];
         w.piece_cnt[p] = 1;
+        ++fin;
       } else {
         uint32_t hit = RANK_NONE;
         if (len <= CACHE_MAXLEN) {
@@ -1192,6 +1219,7 @@ __global__ __launch_bounds__(PT_THREADS) void k_compact(const uint8_t* __restric
         if (hit != RANK_NONE) {
           w.tmp_ids[s] = (int32_t)hit;
           w.piece_cnt[p] = 1;
+          ++fin;
         } else {
           cls = len <= 8 ? 0 : len <= 16 ? 1 : len <= 32 ? 2 : 3;
         }
@@ -1217,7 +1245,10 @@ __global__ __launch_bounds__(PT_THREADS) void k_compact(const uint8_t* __restric
     // next start may not have written it yet)
     const int32_t ls = (int32_t)uniform((uint32_t)sst[tot - 1]);
     const int32_t lm = (int32_t)uniform((uint32_t)sst[tot]) - ls;
-    if (lm > BIG_BYTES) big_bpe(bytes, w, tb, base + tot - 1, ls, lm, big);
+    // tokens of the tile's finished pieces; merged pieces add theirs later
+    uint32_t tok = block_sum(fin, red);
+    if (lm > BIG_BYTES) tok += (uint32_t)big_bpe(bytes, w, tb, base + tot - 1, ls, lm, big);
+    if (threadIdx.x == 0) w.tile_tok[t] = tok;
   }
 }
 
@@ -1271,49 +1302,39 @@ __global__ __launch_bounds__(MERGE_THREADS) void k_bpe_merge(const uint8_t* __re
 
 // ------------------------------------------------------------------ emission
 
-// Pass 6: token count of each emission unit of 256 pieces, and each piece's
-// token offset inside its unit (tok_in).
-__global__ __launch_bounds__(EMIT_UNIT) void k_emit_sums(Work w) {
-  __shared__ uint32_t red[8];
-  const uint32_t P = w.ctr[CTR_P];
-  for (uint32_t u = blockIdx.x; u * EMIT_UNIT < P; u += gridDim.x) {
-    const uint32_t p = u * EMIT_UNIT + threadIdx.x;
-    const uint32_t c = p < P ? (uint32_t)w.piece_cnt[p] : 0u;
-    uint32_t tot;
-    const uint32_t e = block_excl_sum(c, red, &tot);
-    if (p < P) w.tok_in[p] = (int32_t)e;
-    if (threadIdx.x == 0) w.blk_sum[u] = tot;
-  }
-}
-
 constexpr uint32_t HUGE_CHUNK = 16384;  // tokens per grid work item of a huge piece
 
-// Pass 7: final token offsets (the counts of the earlier units plus the
-// offset inside the unit) and the copy of each piece's tokens into the
-// output: up to 8 tokens by the piece's own thread, up to HUGE_TOKENS by a
-// wavefront.  Pieces with more tokens are cut into HUGE_CHUNK-token items
-// dealt round-robin to the workgroups.  The workgroup with the last unit
-// writes T (and tok_off[P]); *out_n, if given, gets T or the error code.
-__global__ __launch_bounds__(EMIT_UNIT) void k_emit(Work w, int32_t* __restrict__ out_ids, int64_t* __restrict__ out_n,
-                                                    uint32_t cap) {
+// Pass 6, one workgroup per tile: the output offset of the tile's pieces (the
+// tokens of the tiles before it plus a block scan of their counts) and the
+// copy of their tokens: up to 8 by the piece's own thread, up to HUGE_TOKENS
+// by a wavefront.  Pieces with more tokens are cut into HUGE_CHUNK-token items
+// dealt round-robin to the workgroups, each of which works out the piece's
+// offset itself.  The last tile writes T (and tok_off[P]); *out_n, if given,
+// gets T or the error code.  No copy goes past cap (= n).
+__global__ __launch_bounds__(EMIT_THREADS) void k_emit(Work w, int ntiles, int32_t* __restrict__ out_ids,
+                                                       int64_t* __restrict__ out_n, uint32_t cap) {
   __shared__ uint32_t red[8];
-  const uint32_t P = w.ctr[CTR_P];
-  const uint32_t nunits = (P + EMIT_UNIT - 1) / EMIT_UNIT;
+  const int t = blockIdx.x;
   const int lane = (int)(threadIdx.x & 63u);
+  const uint32_t cmask = (1u << TILE_ERR_SHIFT) - 1u;
   uint32_t hi;
-  for (uint32_t u = blockIdx.x; u < nunits; u += gridDim.x) {
-    const uint32_t base = block_reduce(w.blk_sum, (int)u, ~0u, red, &hi);
-    const uint32_t p = u * EMIT_UNIT + threadIdx.x;
-    const bool live = p < P;
+  const uint32_t pbase = w.tile_pbase[t];
+  const uint32_t np = w.tile_cnt[t] & cmask;
+  uint32_t off0 = block_reduce(w.tile_tok, t, ~0u, red, &hi);
+  for (uint32_t k0 = 0; k0 < np; k0 += EMIT_THREADS) {
+    const uint32_t k = k0 + threadIdx.x;
+    const bool live = k < np;
+    const uint32_t p = pbase + k;
     const uint32_t c = live ? (uint32_t)w.piece_cnt[p] : 0u;
     const uint32_t src = live ? (uint32_t)w.piece_start[p] : 0u;
-    const uint32_t off = live ? base + (uint32_t)w.tok_in[p] : 0u;
+    uint32_t tot;
+    const uint32_t off = off0 + block_excl_sum(c, red, &tot);
     if (live) {
       w.tok_off[p] = (int32_t)off;
       if (c <= 8) {
 #pragma unroll
-        for (uint32_t k = 0; k < 8; ++k)
-          if (k < c) out_ids[off + k] = w.tmp_ids[src + k];
+        for (uint32_t j = 0; j < 8; ++j)
+          if (j < c) out_ids[off + j] = w.tmp_ids[src + j];
       }
     }
     uint64_t big = __ballot(live && c > 8 && c <= (uint32_t)HUGE_TOKENS);
@@ -1323,14 +1344,14 @@ __global__ __launch_bounds__(EMIT_UNIT) void k_emit(Work w, int32_t* __restrict_
       const uint32_t cs = __shfl(src, l), co = __shfl(off, l), cc = __shfl(c, l);
       if ((uint32_t)lane < cc) out_ids[co + lane] = w.tmp_ids[cs + lane];
     }
-    if (u == nunits - 1 && threadIdx.x == 0) {
-      const uint32_t T = base + w.blk_sum[u];
-      w.ctr[CTR_T] = T;
-      w.tok_off[P] = (int32_t)T;
-      if (out_n) {
-        const uint32_t e = w.ctr[CTR_ERR];
-        *out_n = e ? err_code(e) : (int64_t)T;
-      }
+    off0 += tot;
+  }
+  if (t == ntiles - 1 && threadIdx.x == 0) {
+    w.ctr[CTR_T] = off0;
+    w.tok_off[pbase + np] = (int32_t)off0;
+    if (out_n) {
+      const uint32_t e = w.ctr[CTR_ERR];
+      *out_n = e ? err_code(e) : (int64_t)off0;
     }
   }
   // huge pieces: work item i = (piece, chunk) goes to workgroup i mod grid
@@ -1343,14 +1364,15 @@ __global__ __launch_bounds__(EMIT_UNIT) void k_emit(Work w, int32_t* __restrict_
     uint32_t first = (blockIdx.x + gridDim.x - item % gridDim.x) % gridDim.x;  // my first chunk of this piece
     item += nch;
     if (first >= nch) continue;
-    const uint32_t u = p / EMIT_UNIT;
-    // (tok_in, not tok_off: the piece's own workgroup may already have
-    // replaced its tok_off by the final offset)
-    const uint32_t dst = block_reduce(w.blk_sum, (int)u, ~0u, red, &hi) + (uint32_t)w.tok_in[p];
+    // offset: tokens of the tiles before the piece's tile and of the pieces before it in its tile
     const uint32_t src = (uint32_t)w.piece_start[p];
+    const int tp = (int)(src / TILE);
+    const uint32_t pb = w.tile_pbase[tp];
+    const uint32_t dst = block_reduce(w.tile_tok, tp, ~0u, red, &hi) +
+                         block_reduce(reinterpret_cast<const uint32_t*>(w.piece_cnt) + pb, (int)(p - pb), ~0u, red, &hi);
     for (uint32_t ch = first; ch < nch; ch += gridDim.x) {
       const uint32_t k1 = min(min(cc, (ch + 1) * HUGE_CHUNK), cap - min(cap, dst));  // never past the output
-      for (uint32_t k = ch * HUGE_CHUNK + threadIdx.x; k < k1; k += EMIT_UNIT) out_ids[dst + k] = w.tmp_ids[src + k];
+      for (uint32_t k = ch * HUGE_CHUNK + threadIdx.x; k < k1; k += EMIT_THREADS) out_ids[dst + k] = w.tmp_ids[src + k];
     }
   }
 }
@@ -1437,10 +1459,9 @@ hipError_t launch_bpe_emit(const uint8_t* bytes, int64_t n, const Tables& tb, co
   // enough wavefronts to fill the chip; each one loops over work items
   const int g_merge = capped_grid(n, 256, 2048);
   hipLaunchKernelGGL(k_bpe_merge, dim3(g_merge), dim3(MERGE_THREADS), 0, st, bytes, w, tb); prof_mark("k_bpe_merge", st);
-  // grid-stride passes over at most n pieces
-  const int g = capped_grid(n, EMIT_UNIT, GRID_CAP);
-  hipLaunchKernelGGL(k_emit_sums, dim3(g), dim3(EMIT_UNIT), 0, st, w); prof_mark("k_emit_sums", st);
-  hipLaunchKernelGGL(k_emit, dim3(g), dim3(EMIT_UNIT), 0, st, w, out_ids, out_n, (uint32_t)n); prof_mark("k_emit", st);
+  const int ntiles = ceil_div(n, TILE);
+  hipLaunchKernelGGL(k_emit, dim3(ntiles), dim3(EMIT_THREADS), 0, st, w, ntiles, out_ids, out_n, (uint32_t)n);
+  prof_mark("k_emit", st);
   return hipGetLastError();
 }
 
