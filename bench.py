@@ -192,7 +192,12 @@ def run_workload(name, steps, warmup, graph=True, cpu=True, traffic=None):
         "kernel_ms": round(dom_ms, 5),
         "alg_bytes": int(a_bytes),
     }
-    if traffic and traffic.get("workload") == name and traffic.get("kernel") == dom:
+    # counters count only for the kernels they were taken on
+    src = os.path.join(ROOT, "exact_byte_level_amd", "csrc", "tt_kernels.hip")
+    with open(src, "rb") as f:
+        src_sha = hashlib.sha256(f.read()).hexdigest()
+    if (traffic and traffic.get("workload") == name and traffic.get("kernel") == dom
+            and traffic.get("kernel_source_sha256") == src_sha):
         roof["traffic"] = traffic.get("bytes")
 
     res = {

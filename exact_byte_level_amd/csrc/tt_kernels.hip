@@ -1109,15 +1109,26 @@ __global__ __launch_bounds__(PT_THREADS) void k_compact(const uint8_t* __restric
   const int lane = (int)(threadIdx.x & 63u);
   const uint32_t cmask = (1u << TILE_ERR_SHIFT) - 1u;
   const bool last = t == ntiles - 1;
+  const int64_t t0 = (int64_t)t * TILE;
+  // independent loads first, so that their latencies overlap: this tile's
+  // start bits, its bytes (+ CACHE_MAXLEN), the next tile's count and first
+  // start bits (where the last piece usually ends), and the first step of the
+  // prefix over the tile counts before it
+  uint32_t bits = w.flags[(int64_t)t * PT_THREADS + threadIdx.x];
+  const bool aligned = (reinterpret_cast<uintptr_t>(bytes) & 15u) == 0;
+  uint4 sv = make_uint4(0u, 0u, 0u, 0u);
+  const int64_t sg = t0 + 16 * (int64_t)threadIdx.x;
+  const bool stage_fast = CLASSIFY && aligned && threadIdx.x < (TILE + CACHE_MAXLEN) / 16 && sg + 16 <= n;
+  if (stage_fast) sv = *reinterpret_cast<const uint4*>(bytes + sg);
+  const uint32_t nc1 = (CLASSIFY && t + 1 + lane < ntiles) ? w.tile_cnt[t + 1 + lane] : 0u;
+  const uint32_t fl1 = (CLASSIFY && t + 1 < ntiles) ? w.flags[(int64_t)(t + 1) * PT_THREADS + lane] : 0u;
   uint32_t hi;
   // the last tile also folds its own count and error bits into the totals
   const uint32_t base = block_reduce(w.tile_cnt, last ? t + 1 : t, cmask, red, &hi) -
                         (last ? (w.tile_cnt[t] & cmask) : 0u);
-  uint32_t bits = w.flags[(int64_t)t * PT_THREADS + threadIdx.x];
   uint32_t tot;
   uint32_t lpos = block_excl_sum(__popc(bits), red, &tot);
   uint32_t pos = base + lpos;
-  const int64_t t0 = (int64_t)t * TILE;
   const int64_t p0 = t0 + (int64_t)PT_CHUNK * threadIdx.x;
   while (bits) {
     const int k = __ffs(bits) - 1;
@@ -1146,7 +1157,16 @@ __global__ __launch_bounds__(PT_THREADS) void k_compact(const uint8_t* __restric
     // end of the last piece: the first start after this tile, else n (every
     // wavefront runs the same search; the ballots keep it wave-uniform)
     int32_t e = (int32_t)n;
-    for (int b = t + 1; b < ntiles; b += 64) {
+    // usually the next tile has a start in its first 256 bytes
+    const uint64_t nz1 = __ballot((nc1 & cmask) != 0u);
+    const uint64_t fm1 = __ballot(fl1 != 0u);
+    const bool quick = (nz1 & 1ull) && fm1;
+    if (quick) {
+      const int l = __ffsll((unsigned long long)fm1) - 1;
+      const uint32_t flw = (uint32_t)__shfl((int)fl1, l);
+      e = (int32_t)((int64_t)(t + 1) * TILE + PT_CHUNK * l + __ffs(flw) - 1);
+    }
+    for (int b = t + 1; !quick && b < ntiles; b += 64) {
       const int bb = b + lane;
       const uint64_t nz = __ballot(bb < ntiles && (w.tile_cnt[bb] & cmask) != 0u);
       if (nz) {
@@ -1167,19 +1187,14 @@ __global__ __launch_bounds__(PT_THREADS) void k_compact(const uint8_t* __restric
     if (threadIdx.x == 0) sst[tot] = e;
   }
   // the tile's bytes plus CACHE_MAXLEN, for single bytes and table keys
-  const bool aligned = (reinterpret_cast<uintptr_t>(bytes) & 15u) == 0;
-  for (int i = threadIdx.x; i < (TILE + CACHE_MAXLEN) / 16; i += PT_THREADS) {
-    const int64_t g = t0 + 16 * i;
-    uint4 v;
-    if (aligned && g + 16 <= n) {
-      v = *reinterpret_cast<const uint4*>(bytes + g);
-    } else {
+  if (threadIdx.x < (TILE + CACHE_MAXLEN) / 16) {
+    if (!stage_fast) {
       uint32_t wv[4] = {0u, 0u, 0u, 0u};
       for (int k = 0; k < 16; ++k)
-        if (g + k < n) wv[k >> 2] |= (uint32_t)bytes[g + k] << (8 * (k & 3));
-      v = make_uint4(wv[0], wv[1], wv[2], wv[3]);
+        if (sg + k < n) wv[k >> 2] |= (uint32_t)bytes[sg + k] << (8 * (k & 3));
+      sv = make_uint4(wv[0], wv[1], wv[2], wv[3]);
     }
-    stage[i] = v;
+    stage[threadIdx.x] = sv;
   }
   if (threadIdx.x < 5) qn[threadIdx.x] = 0;
   __syncthreads();
