@@ -99,6 +99,10 @@ struct TileSmem {
   int64_t seq_lo, seq_hi;
   uint32_t carry_fwd, carry_bwd;
   int flag;
+  // plen[j]: byte length of the char that ends right before position j (0
+  // if unknown: no char start there, or the previous char begins outside the
+  // span); filled only when the tile has non-ASCII bytes
+  alignas(16) uint8_t plen[SPAN + 16];
 };
 
 __device__ __forceinline__ bool bmap_bit(const uint32_t* bm, int j) {
@@ -184,6 +188,7 @@ __device__ bool load_tile(const uint8_t* __restrict__ bytes, int64_t n, const in
   const int64_t base = t0 - HALO;
   const bool aligned = (reinterpret_cast<uintptr_t>(bytes) & 15u) == 0;
   for (int i = tid; i < BMAP_WORDS; i += PT_THREADS) sm.bmap[i] = 0;
+  for (int i = tid; i < (SPAN + 16) / 16; i += PT_THREADS) reinterpret_cast<uint4*>(sm.plen)[i] = make_uint4(0u, 0u, 0u, 0u);
   for (int i = tid; i < 128; i += PT_THREADS) sm.ascii[i] = g_ascii.v[i];
   uint32_t hi_bits = 0;
   for (int i = tid; i < RAW_WORDS; i += PT_THREADS) {
@@ -234,6 +239,7 @@ __device__ bool load_tile(const uint8_t* __restrict__ bytes, int64_t n, const in
     uint16_t c = decode_at(n, base, j, sm, na);
     sm.code[cix(j)] = c;
     if ((c & K_BAD) && j >= HALO && j < HALO + TILE) bad = true;
+    if (na && is_char(c)) sm.plen[j + clen(c)] = (uint8_t)clen(c);
   }
   __syncthreads();
   return bad;
@@ -468,9 +474,10 @@ __device__ __forceinline__ uint32_t cat(const uint16_t* c, int j) { return c[cix
 // Previous char start before tile position j, or -1 at a sequence start.
 // With ASCII (no byte >= 0x80 in the staged span) every byte starts a char.
 template <bool ASCII>
-__device__ __forceinline__ int prev_char(const uint16_t* c, int j) {
+__device__ __forceinline__ int prev_char(const uint16_t* c, const uint8_t* pl, int j) {
   if (cat(c, j) & K_SEQ_START) return -1;
   if (ASCII) return j - 1;
+  if (pl[j]) return j - pl[j];
   int k = j - 1;
   while (k > 0 && cls_of(cat(c, k)) == C_CONT && k > j - 4) --k;
   return k;
@@ -479,20 +486,20 @@ __device__ __forceinline__ int prev_char(const uint16_t* c, int j) {
 // The apostrophe at q starts a piece: it is a one-char "other" run that no
 // space in front of it absorbs.
 template <bool ASCII>
-__device__ __forceinline__ bool ap_starts_piece(const uint16_t* c, int q) {
+__device__ __forceinline__ bool ap_starts_piece(const uint16_t* c, const uint8_t* pl, int q) {
   uint32_t cq = cat(c, q);
   if (!(cq & K_AP)) return false;
   if (cq & K_SEQ_START) return true;
-  uint32_t cr = cat(c, prev_char<ASCII>(c, q));
+  uint32_t cr = cat(c, prev_char<ASCII>(c, pl, q));
   return cls_of(cr) != C_O && !(cr & K_SP);
 }
 
 // Length (1 or 2) of a contraction suffix whose first letter is at a, or 0.
 template <int PAT, bool ASCII>
-__device__ __forceinline__ int contraction_len(const uint16_t* c, int a) {
+__device__ __forceinline__ int contraction_len(const uint16_t* c, const uint8_t* pl, int a) {
   uint32_t ca = cat(c, a);
   if (ca & K_SEQ_START) return 0;
-  if (!ap_starts_piece<ASCII>(c, prev_char<ASCII>(c, a))) return 0;
+  if (!ap_starts_piece<ASCII>(c, pl, prev_char<ASCII>(c, pl, a))) return 0;
   if (PAT == 0 && (ca & K_UPPER)) return 0;
   uint32_t lt = (ca >> K_LETTER_SHIFT) & 15u;
   if (lt == LT_S || lt == LT_T || lt == LT_M || lt == LT_D) return 1;
@@ -507,51 +514,51 @@ __device__ __forceinline__ int contraction_len(const uint16_t* c, int a) {
 
 // Letter at j is the first letter after a contraction suffix.
 template <int PAT, bool ASCII>
-__device__ __forceinline__ bool after_contraction(const uint16_t* c, int j) {
-  int a = prev_char<ASCII>(c, j);
+__device__ __forceinline__ bool after_contraction(const uint16_t* c, const uint8_t* pl, int j) {
+  int a = prev_char<ASCII>(c, pl, j);
   if (a < 0) return false;
-  if (contraction_len<PAT, ASCII>(c, a) == 1) return true;
-  int a2 = prev_char<ASCII>(c, a);
-  return a2 >= 0 && contraction_len<PAT, ASCII>(c, a2) == 2;
+  if (contraction_len<PAT, ASCII>(c, pl, a) == 1) return true;
+  int a2 = prev_char<ASCII>(c, pl, a);
+  return a2 >= 0 && contraction_len<PAT, ASCII>(c, pl, a2) == 2;
 }
 
 template <bool ASCII>
-__device__ __forceinline__ bool pred_gpt2(const uint16_t* c, int j) {
+__device__ __forceinline__ bool pred_gpt2(const uint16_t* c, const uint8_t* pl, int j) {
   uint32_t c0 = cat(c, j);
   if (c0 & K_SEQ_START) return true;
   uint32_t k0 = cls_of(c0);
-  int p1 = prev_char<ASCII>(c, j);
+  int p1 = prev_char<ASCII>(c, pl, j);
   uint32_t c1 = cat(c, p1), k1 = cls_of(c1);
   if (is_w(k0)) {
     if (!is_w(k1)) return true;
     if (c0 & K_SEQ_LAST) return false;
     return !is_w(cls_of(cat(c, j + (ASCII ? 1 : clen(c0)))));
   }
-  if (k1 == k0) return k0 == C_L && after_contraction<0, ASCII>(c, j);
+  if (k1 == k0) return k0 == C_L && after_contraction<0, ASCII>(c, pl, j);
   if (c1 & K_SP) return false;
-  if (k0 == C_L && contraction_len<0, ASCII>(c, j) > 0) return false;
+  if (k0 == C_L && contraction_len<0, ASCII>(c, pl, j) > 0) return false;
   return true;
 }
 
 // fwd_prev: forward run state at the previous char; fwd_here: at this char;
 // ends_run: the whitespace run through this char is followed by no CR/LF.
 template <bool ASCII>
-__device__ __forceinline__ bool pred_cl100k(const uint16_t* c, int j, uint32_t fwd_prev, uint32_t fwd_here,
+__device__ __forceinline__ bool pred_cl100k(const uint16_t* c, const uint8_t* pl, int j, uint32_t fwd_prev, uint32_t fwd_here,
                                             bool ends_run) {
   uint32_t c0 = cat(c, j);
   if (c0 & K_SEQ_START) return true;
   uint32_t k0 = cls_of(c0);
-  int p1 = prev_char<ASCII>(c, j);
+  int p1 = prev_char<ASCII>(c, pl, j);
   uint32_t c1 = cat(c, p1), k1 = cls_of(c1);
   switch (k0) {
     case C_N:
       return k1 != C_N || ((fwd_here >> 8) & 3u) == 1u;
     case C_L:
-      if (k1 == C_L) return after_contraction<1, ASCII>(c, j);
+      if (k1 == C_L) return after_contraction<1, ASCII>(c, pl, j);
       if (k1 == C_WS) return false;
       if (k1 == C_O) {
         if (c1 & K_SEQ_START) return false;
-        uint32_t c2 = cat(c, prev_char<ASCII>(c, p1));
+        uint32_t c2 = cat(c, prev_char<ASCII>(c, pl, p1));
         return !(cls_of(c2) != C_O && !(c2 & K_SP));
       }
       return true;
@@ -628,13 +635,13 @@ __global__ __launch_bounds__(PT_THREADS) void k_pretok(const uint8_t* __restrict
 #pragma unroll
       for (int k = 0; k < PT_CHUNK; ++k) {
         uint32_t c = sm.code[cix(j0 + k)];
-        if (is_char(c) && pred_gpt2<false>(sm.code, j0 + k)) bits |= 1u << k;
+        if (is_char(c) && pred_gpt2<false>(sm.code, sm.plen, j0 + k)) bits |= 1u << k;
       }
     } else {
 #pragma unroll
       for (int k = 0; k < PT_CHUNK; ++k) {
         uint32_t c = sm.code[cix(j0 + k)];
-        if (is_char(c) && pred_gpt2<true>(sm.code, j0 + k)) bits |= 1u << k;
+        if (is_char(c) && pred_gpt2<true>(sm.code, sm.plen, j0 + k)) bits |= 1u << k;
       }
     }
   } else {
@@ -658,7 +665,7 @@ __global__ __launch_bounds__(PT_THREADS) void k_pretok(const uint8_t* __restrict
         if (is_char(c)) {
           uint32_t before = sf;
           sf = FwdOp::combine(sf, FwdOp::elem(c));
-          if (pred_cl100k<false>(sm.code, j0 + k, before, sf, (ends >> k) & 1u)) bits |= 1u << k;
+          if (pred_cl100k<false>(sm.code, sm.plen, j0 + k, before, sf, (ends >> k) & 1u)) bits |= 1u << k;
         }
       }
     } else {
@@ -668,7 +675,7 @@ __global__ __launch_bounds__(PT_THREADS) void k_pretok(const uint8_t* __restrict
         if (is_char(c)) {
           uint32_t before = sf;
           sf = FwdOp::combine(sf, FwdOp::elem(c));
-          if (pred_cl100k<true>(sm.code, j0 + k, before, sf, (ends >> k) & 1u)) bits |= 1u << k;
+          if (pred_cl100k<true>(sm.code, sm.plen, j0 + k, before, sf, (ends >> k) & 1u)) bits |= 1u << k;
         }
       }
     }
