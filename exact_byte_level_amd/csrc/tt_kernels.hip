@@ -178,12 +178,10 @@ __device__ __forceinline__ uint16_t decode_at(int64_t n, int64_t base, int j, co
 
 // Stage the tile in LDS: raw bytes of [t0 - HALO, t0 + TILE + HALO + 16) with
 // one 16-byte load per thread (byte loads only at the text edges or for an
-// unaligned text), the sequence-boundary bitmap, the Unicode table if some byte
-// is non-ASCII, then the codes of positions [t0 - HALO, t0 + TILE + HALO).
-// Returns true if some char starting inside the tile is invalid UTF-8;
-// *non_ascii (same in every thread) tells whether any staged byte is >= 0x80.
-__device__ bool load_tile(const uint8_t* __restrict__ bytes, int64_t n, const int64_t* __restrict__ offs,
-                          int nseq, int64_t t0, TileSmem& sm, bool* non_ascii = nullptr) {
+// unaligned text) and the sequence-boundary bitmap.  Returns (the same in
+// every thread) whether any staged byte is >= 0x80.
+__device__ bool stage_tile(const uint8_t* __restrict__ bytes, int64_t n, const int64_t* __restrict__ offs,
+                           int nseq, int64_t t0, TileSmem& sm) {
   const int tid = threadIdx.x;
   const int64_t base = t0 - HALO;
   const bool aligned = (reinterpret_cast<uintptr_t>(bytes) & 15u) == 0;
@@ -217,7 +215,6 @@ __device__ bool load_tile(const uint8_t* __restrict__ bytes, int64_t n, const in
     }
   }
   const bool na = __syncthreads_or((hi_bits & 0x80808080u) != 0u);
-  if (non_ascii) *non_ascii = na;
   if (offs) {
     for (int64_t s = sm.seq_lo + tid; s < sm.seq_hi; s += PT_THREADS) {
       int64_t j = offs[s] - base;
@@ -227,6 +224,14 @@ __device__ bool load_tile(const uint8_t* __restrict__ bytes, int64_t n, const in
     int64_t j = -base;
     if (j < (int64_t)BMAP_WORDS * 32) sm.bmap[j >> 5] |= 1u << (j & 31);
   }
+  return na;
+}
+
+// Codes of all SPAN positions (the Unicode table staged in LDS first if some
+// byte is non-ASCII), and for non-ASCII tiles the predecessor lengths.
+// Returns true if some char starting inside the tile is invalid UTF-8.
+__device__ bool decode_span(int64_t n, int64_t t0, bool na, TileSmem& sm) {
+  const int tid = threadIdx.x;
   if (na) {
     for (int i = tid; i < UNI_L1_PAD / 16; i += PT_THREADS)
       reinterpret_cast<uint4*>(sm.l1)[i] = reinterpret_cast<const uint4*>(g_uni_l1)[i];
@@ -236,13 +241,22 @@ __device__ bool load_tile(const uint8_t* __restrict__ bytes, int64_t n, const in
   __syncthreads();
   bool bad = false;
   for (int j = tid; j < SPAN; j += PT_THREADS) {
-    uint16_t c = decode_at(n, base, j, sm, na);
+    uint16_t c = decode_at(n, t0 - HALO, j, sm, na);
     sm.code[cix(j)] = c;
     if ((c & K_BAD) && j >= HALO && j < HALO + TILE) bad = true;
     if (na && is_char(c)) sm.plen[j + clen(c)] = (uint8_t)clen(c);
   }
   __syncthreads();
   return bad;
+}
+
+// The whole tile: stage, then decode every position.  *non_ascii (same in
+// every thread) tells whether any staged byte is >= 0x80.
+__device__ bool load_tile(const uint8_t* __restrict__ bytes, int64_t n, const int64_t* __restrict__ offs,
+                          int nseq, int64_t t0, TileSmem& sm, bool* non_ascii = nullptr) {
+  const bool na = stage_tile(bytes, n, offs, nseq, t0, sm);
+  if (non_ascii) *non_ascii = na;
+  return decode_span(n, t0, na, sm);
 }
 
 // ---------------------------------------------------- run-state scan operators
@@ -413,18 +427,50 @@ __device__ __forceinline__ uint32_t chunk_bwd(const TileSmem& sm) {
 // every tile, so that pass 2 can resolve runs that cross tiles (digit-group
 // phase, the last newline of a whitespace run, newlines absorbed after
 // punctuation) without a second look at distant bytes.
+constexpr int EDGE = 64;  // positions at each tile end decoded first
+
 __global__ __launch_bounds__(PT_THREADS) void k_tile_summary(const uint8_t* __restrict__ bytes, int64_t n,
                                                              const int64_t* __restrict__ offs, int nseq,
                                                              Work w) {
   __shared__ TileSmem sm;
   const int64_t t0 = (int64_t)blockIdx.x * TILE;
-  load_tile(bytes, n, offs, nseq, t0, sm);
-  uint32_t tf, tb;
-  block_excl_fwd<FwdOp>(chunk_fwd(sm), sm.red, &tf);
-  block_excl_bwd<BwdOp>(chunk_bwd(sm), sm.red, &tb);
+  const int lane = (int)(threadIdx.x & 63u), wid = (int)(threadIdx.x >> 6);
+  const bool na = stage_tile(bytes, n, offs, nseq, t0, sm);
+  __syncthreads();
+  // Usually the leading and the trailing run of a tile end within EDGE
+  // positions: then decoding those positions decides both summaries (the
+  // Unicode table is read from global memory for these few chars).
+  if (wid < 2) {
+    const int j = HALO + (wid == 0 ? lane : TILE - EDGE + lane);
+    const uint16_t c = decode_at(n, t0 - HALO, j, sm, false);
+    uint32_t v;
+    if (wid == 0) {
+      v = wave_incl_bwd<BwdOp>(is_char(c) ? BwdOp::elem(c) : BwdOp::IDENT, lane);
+      if (lane == 0) sm.red[0] = v;
+    } else {
+      v = wave_incl_fwd<FwdOp>(is_char(c) ? FwdOp::elem(c) : FwdOp::IDENT, lane);
+      if (lane == 63) sm.red[1] = v;
+    }
+  }
+  __syncthreads();
+  const uint32_t tb = sm.red[0], tf = sm.red[1];
+  const bool closed = (tb & 1u) && !(tb & 2u) && (tf & 1u) && !(tf & 2u);
+  __syncthreads();
+  if (closed) {
+    if (threadIdx.x == 0) {
+      w.tile_fwd[blockIdx.x] = tf;
+      w.tile_bwd[blockIdx.x] = tb;
+    }
+    return;
+  }
+  // a run reaches EDGE positions in from an end: decode and scan the whole tile
+  decode_span(n, t0, na, sm);
+  uint32_t af, ab;
+  block_excl_fwd<FwdOp>(chunk_fwd(sm), sm.red, &af);
+  block_excl_bwd<BwdOp>(chunk_bwd(sm), sm.red, &ab);
   if (threadIdx.x == 0) {
-    w.tile_fwd[blockIdx.x] = tf;
-    w.tile_bwd[blockIdx.x] = tb;
+    w.tile_fwd[blockIdx.x] = af;
+    w.tile_bwd[blockIdx.x] = ab;
   }
 }
 
