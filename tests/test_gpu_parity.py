@@ -133,6 +133,39 @@ def test_pretokenize_runs_crossing_tiles(pattern):
     assert gpu_starts(data, pattern, offs) == piece_starts_batch(data, offs, pattern)
 
 
+def _tile_edge_text(seed, tile=1024, ntiles=48):
+    # runs of 1..130 chars of each class placed across every tile boundary,
+    # contractions split by a boundary, and every other tile holding one
+    # 2-byte char (so that ASCII-only and mixed tiles alternate)
+    rng = random.Random(seed)
+    runs = [" ", "7", "x", ".", "\n", "\t", "'", "\r\n"]
+    out = bytearray()
+    for t in range(1, ntiles):
+        edge = t * tile
+        ch = rng.choice(runs)
+        k = rng.choice([1, 2, 3, 60, 63, 64, 65, 66, 70, 100, 130])
+        left = rng.randint(0, k)
+        while len(out) < edge - left * len(ch.encode()):
+            word = rng.choice(["ab", "don't", "we're", "x1", "Il", "9", "..", " ", "\n"])
+            out += word.encode()
+            if t % 2 and rng.random() < 0.02:
+                out += "é".encode()
+        out += (ch * k).encode()
+        out += rng.choice([b"'s", b"'LL", b"q", b"1", b"!", b" "])
+    return bytes(out)
+
+
+@pytest.mark.parametrize("pattern", [GPT2, CL100K])
+def test_runs_across_tile_edges(pattern):
+    data = _tile_edge_text(60 + pattern)
+    say("tile edges: %d bytes, pattern %d" % (len(data), pattern))
+    _, want = split_bytes(data, pattern)
+    assert gpu_starts(data, pattern) == want
+    v = load("c1", pattern)
+    got = gpu_encode(data)
+    assert np.array_equal(got, np.asarray(oracle_encode(data, v, pattern, {}), dtype=np.int32))
+
+
 # ------------------------------------------------------------- end to end
 
 def gpu_encode(data):
