@@ -38,7 +38,7 @@ constexpr int UNI_L2_PAD = (TT_UNI_NBLOCKS * 64 + 15) / 16 * 16;
 alignas(16) __device__ const uint8_t g_uni_l1[UNI_L1_PAD] = {TT_UNI_L1_DATA};
 alignas(16) __device__ const uint8_t g_uni_l2[UNI_L2_PAD] = {TT_UNI_L2_DATA};
 
-struct AsciiTab {
+struct alignas(16) AsciiTab {
   uint16_t v[128];
 };
 
@@ -91,7 +91,7 @@ __device__ __forceinline__ int cix(int j) { return j + 2 * (j >> 4); }
 struct TileSmem {
   uint4 raw[RAW_WORDS];   // bytes of positions [t0 - HALO, t0 - HALO + 16 * RAW_WORDS); 0 outside the text
   uint16_t code[CODE_SLOTS];
-  uint16_t ascii[128];
+  alignas(16) uint16_t ascii[128];
   uint32_t bmap[BMAP_WORDS];
   alignas(16) uint8_t l1[UNI_L1_PAD];
   alignas(16) uint8_t l2[UNI_L2_PAD];
@@ -187,7 +187,7 @@ __device__ bool stage_tile(const uint8_t* __restrict__ bytes, int64_t n, const i
   const bool aligned = (reinterpret_cast<uintptr_t>(bytes) & 15u) == 0;
   for (int i = tid; i < BMAP_WORDS; i += PT_THREADS) sm.bmap[i] = 0;
   for (int i = tid; i < (SPAN + 16) / 16; i += PT_THREADS) reinterpret_cast<uint4*>(sm.plen)[i] = make_uint4(0u, 0u, 0u, 0u);
-  for (int i = tid; i < 128; i += PT_THREADS) sm.ascii[i] = g_ascii.v[i];
+  if (tid < 16) reinterpret_cast<uint4*>(sm.ascii)[tid] = reinterpret_cast<const uint4*>(g_ascii.v)[tid];
   uint32_t hi_bits = 0;
   for (int i = tid; i < RAW_WORDS; i += PT_THREADS) {
     const int64_t g = base + 16 * (int64_t)i;
@@ -240,11 +240,29 @@ __device__ bool decode_span(int64_t n, int64_t t0, bool na, TileSmem& sm) {
   }
   __syncthreads();
   bool bad = false;
+  if (!na) {
+    // every byte is a one-byte char: class from the ASCII table, sequence
+    // edges from the bitmap (no invalid UTF-8 is possible)
+    const uint8_t* raw = reinterpret_cast<const uint8_t*>(sm.raw);
+    const int64_t base = t0 - HALO;
+    for (int j = tid; j < SPAN; j += PT_THREADS) {
+      const int64_t p = base + j;
+      uint32_t c = C_OUT;
+      if (p >= 0 && p < n) {
+        c = sm.ascii[raw[j]];
+        if (bmap_bit(sm.bmap, j)) c |= K_SEQ_START;
+        if (p + 1 >= n || bmap_bit(sm.bmap, j + 1)) c |= K_SEQ_LAST;
+      }
+      sm.code[cix(j)] = (uint16_t)c;
+    }
+    __syncthreads();
+    return false;
+  }
   for (int j = tid; j < SPAN; j += PT_THREADS) {
     uint16_t c = decode_at(n, t0 - HALO, j, sm, na);
     sm.code[cix(j)] = c;
     if ((c & K_BAD) && j >= HALO && j < HALO + TILE) bad = true;
-    if (na && is_char(c)) sm.plen[j + clen(c)] = (uint8_t)clen(c);
+    if (is_char(c)) sm.plen[j + clen(c)] = (uint8_t)clen(c);
   }
   __syncthreads();
   return bad;
