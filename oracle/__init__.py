@@ -17,7 +17,8 @@ What it follows (TokTier, arXiv:2607.29678v1, summary page):
 Modules
   pretok  -- the two ordered rule sets (GPT-2-style, cl100k-style) and split()
   bpe     -- classic lowest-rank-first merge loop, a heap/linked-list form with
-             the same semantics, the naive rank-order brute force, decode
+             the same semantics, the naive rank-order brute force, decode, and the
+             byte offset of every token
   train   -- the BPE trainer that learns merge tables from seeded corpora
   vocab   -- merge-table container and (de)serialisation
 

@@ -170,3 +170,35 @@ def encode_batch(data, offsets, vocab, pattern_id, memo=None):
 def decode(ids, vocab):
     """Bytes of a token sequence, UTF-8 decoded (strict)."""
     return b"".join(vocab.tok_bytes[i] for i in ids).decode("utf-8")
+
+
+def token_starts(ids, vocab, base=0):
+    """Byte offset where each token begins, plus the end: T + 1 values.
+
+    The device-side byte-offset export (TokTier summary page, §8 Path C and
+    Appendix E path C; §4.4 and §7 note that the pages' GPU path emits ids
+    only).  Token i covers bytes [starts[i], starts[i+1]) of the input: the
+    offsets are the running sum of the tokens' byte lengths, from ``base``.
+    """
+    starts = [base]
+    for i in ids:
+        starts.append(starts[-1] + len(vocab.tok_bytes[i]))
+    return starts
+
+
+def encode_offsets(data, offsets, vocab, pattern_id, memo=None):
+    """Ids and token starts of a text (offsets None) or a concatenated batch.
+
+    Returns (ids, starts, counts).  Starts are offsets into the whole buffer
+    ``data`` (a batch text s begins at offsets[s]); starts[T] = len(data).
+    counts is [T] for one text, else the per-text id offsets [B + 1].
+    """
+    if offsets is None:
+        ids = encode(data, vocab, pattern_id, memo)
+        return ids, token_starts(ids, vocab), [len(ids)]
+    ids, counts = encode_batch(data, offsets, vocab, pattern_id, memo)
+    starts = []
+    for s in range(len(offsets) - 1):
+        starts.extend(token_starts(ids[counts[s]:counts[s + 1]], vocab, offsets[s])[:-1])
+    starts.append(len(data))
+    return ids, starts, counts

@@ -3,7 +3,8 @@
 Calls only the seeded generators (``synth``) and the oracle (``oracle``).  For
 every workload it stores the byte and char counts, the number of pre-tokens P
 and a SHA-256 of their int32 byte offsets, the number of tokens T and a SHA-256
-of the int32 token ids (little endian), and for the batch workload the
+of the int32 token ids (little endian), a SHA-256 of the int32 byte offset
+of every token followed by the byte count, and for the batch workload the
 per-sequence token offsets.  The GPU tests compare against these digests.
 
     python tests/golden/make_golden.py [name ...]
@@ -20,7 +21,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(os.path.dirname(HERE))
 sys.path.insert(0, ROOT)
 
-from oracle.bpe import Vocab, encode, encode_batch  # noqa: E402
+from oracle.bpe import Vocab, encode, encode_batch, token_starts  # noqa: E402
 from oracle.pretok import piece_starts_batch, split_bytes  # noqa: E402
 from synth.text import WORKLOADS, workload  # noqa: E402
 
@@ -38,9 +39,13 @@ def golden(name):
         _, starts = split_bytes(data, pat)
         ids = encode(data, vocab, pat, memo)
         out_off = None
+        tstarts = token_starts(ids, vocab)
     else:
         starts = piece_starts_batch(data, offs.tolist(), pat)
         ids, out_off = encode_batch(data, offs.tolist(), vocab, pat, memo)
+        # a batch's texts are contiguous, so the running byte sum over all ids
+        # gives offsets into the whole buffer
+        tstarts = token_starts(ids, vocab)
     rec = {
         "bytes": len(data),
         "chars": len(data.decode("utf-8")),
@@ -50,6 +55,7 @@ def golden(name):
         "pieces_sha256": sha(starts),
         "tokens": len(ids),
         "ids_sha256": sha(ids),
+        "token_starts_sha256": sha(tstarts),
         "oracle_s": round(time.time() - t0, 1),
     }
     if out_off is not None:
