@@ -111,6 +111,29 @@ def run_workload(name, steps, warmup, graph=True, cpu=True, traffic=None):
     torch.cuda.synchronize()
     ms_per_step = e0.elapsed_time(e1) / steps
 
+    # byte-offset export: the same encode plus every token's byte start
+    # (tt_encode_offsets), checked against the oracle's digest, then timed
+    starts_buf = torch.empty(n + 1, dtype=torch.int32, device=dev)
+
+    def step_off():
+        tt.encode_offsets_into(x, off, out, starts_buf, cnt)
+
+    step_off()
+    torch.cuda.synchronize()
+    if int(cnt[-1].item()) != T or _sha(out[:T].cpu().numpy()) != _sha(ids):
+        raise RuntimeError("tt_encode_offsets ids differ from tt_encode's")
+    offsets_verified = None
+    if verified is not None and "token_starts_sha256" in exp:
+        offsets_verified = _sha(starts_buf[:T + 1].cpu().numpy()) == exp["token_starts_sha256"]
+        if not offsets_verified:
+            raise RuntimeError("GPU token offsets differ from the oracle digest for %s" % name)
+    e0.record(stream)
+    for _ in range(steps):
+        step_off()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    offsets_ms = e0.elapsed_time(e1) / steps
+
     # latency distribution: one event pair per encode
     lat = []
     for _ in range(steps):
@@ -213,6 +236,8 @@ def run_workload(name, steps, warmup, graph=True, cpu=True, traffic=None):
         "p99_ms": p99,
         "host_incl_p50_ms": host_p50,
         "graph_p50_ms": graph_p50,
+        "offsets_ms_per_step": offsets_ms,
+        "offsets_verified": offsets_verified,
         "kernels_ms": {k: round(v, 5) for k, v in sorted(kern.items(), key=lambda kv: -kv[1])},
         "roofline": roof,
         "verified": verified,
@@ -314,6 +339,8 @@ def main():
             "p99_ms": res["p99_ms"],
             "graph_p50_ms": res["graph_p50_ms"],
             "host_incl_p50_ms": res["host_incl_p50_ms"],
+            "with_byte_offsets_ms": res["offsets_ms_per_step"],
+            "byte_offsets_verified": res["offsets_verified"],
             "end_to_end_alg_GBps": (res["bytes"] + 4 * res["tokens"]) / (res["ms_per_step"] * 1e-3) / 1e9,
             "kernels_ms": res["kernels_ms"],
             "verified_against_oracle": res["verified"],

@@ -52,6 +52,7 @@ def lib():
         L.tt_encode.argtypes = [vp, i64, vp, vp, vp]
         L.tt_encode_batch.argtypes = [vp, i64, vp, i32, vp, vp, vp]
         L.tt_pretokenize.argtypes = [vp, i64, vp, i32, vp, vp, vp]
+        L.tt_encode_offsets.argtypes = [vp, i64, vp, i32, vp, vp, vp, vp]
         L.tt_char_class.argtypes = [ctypes.c_uint32]
         L.tt_profile.argtypes = [ctypes.c_int]
         L.tt_profile_read.argtypes = [ctypes.POINTER(ctypes.c_char_p), ctypes.POINTER(ctypes.c_float), ctypes.c_int]
@@ -59,8 +60,8 @@ def lib():
         L.tt_free.restype = None
         L.tt_strerror.argtypes = [ctypes.c_int]
         L.tt_strerror.restype = ctypes.c_char_p
-        for f in ("tt_load_bpe", "tt_reserve", "tt_encode", "tt_encode_batch", "tt_pretokenize", "tt_char_class",
-                  "tt_profile", "tt_profile_read"):
+        for f in ("tt_load_bpe", "tt_reserve", "tt_encode", "tt_encode_batch", "tt_pretokenize", "tt_encode_offsets",
+                  "tt_char_class", "tt_profile", "tt_profile_read"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -153,6 +154,39 @@ def pretokenize(data, offsets=None, stream=None):
     if p < 0:
         raise TTError(p, "tt_pretokenize")
     return starts[:p]
+
+
+def encode_offsets_into(data, offsets, out_ids, out_starts, out_counts, stream=None):
+    """Enqueue an encode with byte offsets into caller buffers (no sync)."""
+    n = data.numel()
+    rc = lib().tt_encode_offsets(data.data_ptr() if n else None, n,
+                                 None if offsets is None else offsets.data_ptr(),
+                                 1 if offsets is None else offsets.numel() - 1,
+                                 out_ids.data_ptr(), out_starts.data_ptr(), out_counts.data_ptr(), _stream(stream))
+    _check(rc, "tt_encode_offsets")
+
+
+def encode_offsets(data, offsets=None, stream=None):
+    """Token ids and byte starts of one text, or of a batch with int64 CUDA offsets.
+
+    Returns (ids, starts) for one text and (ids, starts, out_offsets) for a
+    batch: token i covers bytes [starts[i], starts[i+1]) of ``data`` (offsets
+    into the whole buffer) and starts[T] = n.
+    """
+    import torch
+    assert data.dtype == torch.uint8 and data.is_cuda and data.is_contiguous()
+    n = data.numel()
+    out = torch.empty(max(n, 1), dtype=torch.int32, device=data.device)
+    starts = torch.empty(n + 1, dtype=torch.int32, device=data.device)
+    cnt = torch.empty(1 if offsets is None else offsets.numel(), dtype=torch.int64, device=data.device)
+    encode_offsets_into(data, offsets, out, starts, cnt, stream)
+    c = cnt.cpu()
+    t = int(c[-1])
+    if t < 0:
+        raise TTError(t, "tt_encode_offsets")
+    if offsets is None:
+        return out[:t], starts[:t + 1]
+    return out[:t], starts[:t + 1], c
 
 
 def char_class(cp):

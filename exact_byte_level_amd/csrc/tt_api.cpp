@@ -26,6 +26,7 @@ struct State {
   uint32_t* d_byte_pair = nullptr;
   uint64_t* d_pair = nullptr;
   CacheBucket* d_cache = nullptr;
+  uint32_t* d_tok_len = nullptr;
   Tables tb{};
   void* d_ws = nullptr;
   int64_t ws_n = 0;     // bytes of input the workspace is sized for
@@ -94,6 +95,7 @@ void release_tables() {
   free_dev(g.d_byte_pair);
   free_dev(g.d_pair);
   free_dev(g.d_cache);
+  free_dev(g.d_tok_len);
   g.loaded = false;
 }
 
@@ -254,6 +256,10 @@ int tt_load_bpe(const int32_t* merges, const int32_t* ranks, int64_t n_merges, i
     tok[256 + r] = tok[mx[r]];
     tok[256 + r].insert(tok[256 + r].end(), tok[my[r]].begin(), tok[my[r]].end());
   }
+  // byte length of every token, for offset export: 2^ID_BITS entries so that
+  // any id masked to ID_BITS indexes inside the table
+  std::vector<uint32_t> tok_len((size_t)1 << ID_BITS, 0u);
+  for (size_t t = 0; t < tok.size(); ++t) tok_len[t] = (uint32_t)std::min<size_t>(tok[t].size(), 0xFFFFFFFFu);
   std::vector<uint32_t> single;
   for (size_t r = 0; r < M; ++r) {
     const auto& bs = tok[256 + r];
@@ -296,7 +302,7 @@ int tt_load_bpe(const int32_t* merges, const int32_t* ranks, int64_t n_merges, i
   release_tables();
   int rc;
   if ((rc = upload(&g.d_byte_pair, byte_pair)) != TT_OK || (rc = upload(&g.d_pair, pair_tab)) != TT_OK ||
-      (rc = upload(&g.d_cache, cache)) != TT_OK) {
+      (rc = upload(&g.d_cache, cache)) != TT_OK || (rc = upload(&g.d_tok_len, tok_len)) != TT_OK) {
     release_tables();
     return rc;
   }
@@ -309,6 +315,7 @@ int tt_load_bpe(const int32_t* merges, const int32_t* ranks, int64_t n_merges, i
   g.tb.byte_pair = g.d_byte_pair;
   g.tb.pair_tab = g.d_pair;
   g.tb.cache = g.d_cache;
+  g.tb.tok_len = g.d_tok_len;
   g.tb.pair_mask = (uint32_t)(pair_nb - 1);
   g.tb.pair_shift = pair_shift;
   g.tb.pair_probe = pair_probe;
@@ -339,7 +346,7 @@ int tt_encode(const uint8_t* dev_bytes, int64_t n, int32_t* out_ids, int64_t* ou
   if ((rc = ensure_workspace(n)) != TT_OK) return rc;
   prof_begin(stream);
   if (launch_pretokenize(dev_bytes, n, nullptr, 1, g.pattern, g.w, g.w.piece_start, nullptr, &g.tb, stream) != hipSuccess ||
-      launch_bpe_emit(dev_bytes, n, g.tb, g.w, out_ids, out_n, stream) != hipSuccess)
+      launch_bpe_emit(dev_bytes, n, g.tb, g.w, out_ids, out_n, nullptr, stream) != hipSuccess)
     return TT_EHIP;
   return TT_OK;
 }
@@ -365,7 +372,7 @@ int tt_encode_batch(const uint8_t* dev_bytes, int64_t n, const int64_t* dev_offs
   if (launch_pretokenize(dev_bytes, n, dev_offsets, n_seqs, g.pattern, g.w, g.w.piece_start, nullptr, &g.tb,
                          stream) !=
           hipSuccess ||
-      launch_bpe_emit(dev_bytes, n, g.tb, g.w, out_ids, nullptr, stream) != hipSuccess ||
+      launch_bpe_emit(dev_bytes, n, g.tb, g.w, out_ids, nullptr, nullptr, stream) != hipSuccess ||
       launch_batch_offsets(dev_offsets, n_seqs, n, g.w, out_offsets, stream) != hipSuccess)
     return TT_EHIP;
   return TT_OK;
@@ -390,6 +397,35 @@ int tt_pretokenize(const uint8_t* dev_bytes, int64_t n, const int64_t* dev_offse
   }
   prof_begin(stream);
   if (launch_pretokenize(dev_bytes, n, dev_offsets, nseq, g.pattern, g.w, out_starts, out_np, nullptr, stream) != hipSuccess)
+    return TT_EHIP;
+  return TT_OK;
+}
+
+int tt_encode_offsets(const uint8_t* dev_bytes, int64_t n, const int64_t* dev_offsets, int32_t n_seqs,
+                      int32_t* out_ids, int32_t* out_starts, int64_t* out_counts, hipStream_t stream) {
+  std::lock_guard<std::mutex> lock(g_mu);
+  if (n < 0 || !out_starts || !out_counts || (n > 0 && (!dev_bytes || !out_ids)) || (dev_offsets && n_seqs < 1))
+    return TT_EINVAL;
+  if (n >= TT_MAX_BYTES || n_seqs >= (int64_t)1 << 30) return TT_ETOOBIG;
+  int rc = check_stream_state();
+  if (rc != TT_OK) return rc;
+  if ((rc = ensure_workspace(n)) != TT_OK) return rc;
+  const int nseq = dev_offsets ? n_seqs : 1;
+  if (n == 0) {
+    if (launch_zero_counters(g.w, stream) != hipSuccess ||
+        (dev_offsets && launch_check_offsets(dev_offsets, nseq, n, g.w, stream) != hipSuccess) ||
+        launch_write_zero_i32(out_starts, stream) != hipSuccess ||
+        (dev_offsets && launch_write_zeros(out_counts, nseq, stream) != hipSuccess) ||
+        launch_finish_count(g.w, CTR_T, dev_offsets ? out_counts + nseq : out_counts, stream) != hipSuccess)
+      return TT_EHIP;
+    return TT_OK;
+  }
+  prof_begin(stream);
+  if (launch_pretokenize(dev_bytes, n, dev_offsets, nseq, g.pattern, g.w, g.w.piece_start, nullptr, &g.tb, stream) !=
+          hipSuccess ||
+      launch_bpe_emit(dev_bytes, n, g.tb, g.w, out_ids, dev_offsets ? nullptr : out_counts, out_starts, stream) !=
+          hipSuccess ||
+      (dev_offsets && launch_batch_offsets(dev_offsets, nseq, n, g.w, out_counts, stream) != hipSuccess))
     return TT_EHIP;
   return TT_OK;
 }

@@ -86,6 +86,7 @@ struct Tables {
   const uint32_t* byte_pair;    // [65536] rank of (x, y), x, y < 256, or RANK_NONE
   const uint64_t* pair_tab;     // [pair_nb * PAIR_SLOTS]
   const CacheBucket* cache;     // [cache_nb]
+  const uint32_t* tok_len;      // [2^ID_BITS] byte length of every token (0 past the vocabulary)
   uint32_t pair_mask;           // pair_nb - 1
   int pair_shift;               // 32 - log2(pair_nb)
   int pair_probe;               // max buckets visited by any key
@@ -123,7 +124,9 @@ struct Work {
   int32_t* piece_start;  // [n + 1]
   int32_t* piece_cnt;    // [n] tokens of each piece
   int32_t* tmp_ids;      // [n] tokens of the piece starting at byte s live at [s, s + cnt)
-  uint32_t* tmp_rank;    // [n] pair ranks for the long-piece merge loop
+  uint32_t* tmp_rank;    // [n] pair ranks for the long-piece merge loop; afterwards, for
+                         // offset export, the byte length of chunk k of a huge piece
+                         // starting at byte s at [s + k]
   int32_t* tok_off;      // [n + 1] token offset of each piece; [P] = T
   uint32_t* tile_tok;    // [ntiles] tokens of the pieces that start in each tile
   uint32_t* tile_pbase;  // [ntiles] index of the first piece that starts in each tile

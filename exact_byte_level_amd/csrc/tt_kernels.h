@@ -18,9 +18,10 @@ hipError_t launch_pretokenize(const uint8_t* bytes, int64_t n, const int64_t* of
 
 // BPE of the queued pieces, then token offsets and ids into out_ids;
 // the total goes to w.ctr[CTR_T] and, if out_n is given, T or the error code
-// to *out_n.
+// to *out_n.  If out_starts is given it receives the byte offset of every
+// token and, at [T], n.
 hipError_t launch_bpe_emit(const uint8_t* bytes, int64_t n, const Tables& tb, const Work& w, int32_t* out_ids,
-                           int64_t* out_n, hipStream_t st);
+                           int64_t* out_n, int32_t* out_starts, hipStream_t st);
 
 // *out = error code if any data error was flagged, else w.ctr[which].
 hipError_t launch_finish_count(const Work& w, int which, int64_t* out, hipStream_t st);

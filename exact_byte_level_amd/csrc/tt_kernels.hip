@@ -1390,6 +1390,39 @@ __global__ __launch_bounds__(MERGE_THREADS) void k_bpe_merge(const uint8_t* __re
 
 constexpr uint32_t HUGE_CHUNK = 16384;  // tokens per grid work item of a huge piece
 
+// Byte-offset export only: chunk k of a huge piece (tokens [k * HUGE_CHUNK,
+// (k + 1) * HUGE_CHUNK)) gets its byte length written to tmp_rank[s + k] (s =
+// the piece's first byte; the piece's ranks are dead by now and its byte
+// range is at least as long as its chunk count), for every chunk but the
+// last.  Items (piece, chunk) are dealt round-robin to the workgroups.
+__global__ __launch_bounds__(EMIT_THREADS) void k_chunk_sums(Work w, const uint32_t* __restrict__ tok_len) {
+  __shared__ uint32_t red[8];
+  const uint32_t nhuge = w.ctr[CTR_NHUGE];
+  uint32_t item = 0;
+  for (uint32_t h = 0; h < nhuge; ++h) {
+    const uint32_t p = (uint32_t)w.huge_list[h];
+    const uint32_t cc = (uint32_t)w.piece_cnt[p];
+    const uint32_t nit = (cc + HUGE_CHUNK - 1) / HUGE_CHUNK - 1;  // chunks before the last
+    const uint32_t first = (blockIdx.x + gridDim.x - item % gridDim.x) % gridDim.x;
+    item += nit;
+    if (first >= nit) continue;
+    const uint32_t src = (uint32_t)w.piece_start[p];
+    for (uint32_t ch = first; ch < nit; ch += gridDim.x) {
+      const int32_t* ids = w.tmp_ids + src + ch * HUGE_CHUNK;
+      uint32_t sum = 0;
+      for (uint32_t k0 = 0; k0 < HUGE_CHUNK; k0 += EMIT_THREADS * 8) {
+        uint32_t id[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) id[j] = (uint32_t)ids[k0 + EMIT_THREADS * j + threadIdx.x];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) sum += tok_len[id[j] & ID_MASK];
+      }
+      sum = block_sum(sum, red);
+      if (threadIdx.x == 0) w.tmp_rank[src + ch] = sum;
+    }
+  }
+}
+
 // Pass 6, one workgroup per tile: the output offset of the tile's pieces (the
 // tokens of the tiles before it plus a block scan of their counts) and the
 // copy of their tokens: up to 8 by the piece's own thread, up to HUGE_TOKENS
@@ -1397,8 +1430,18 @@ constexpr uint32_t HUGE_CHUNK = 16384;  // tokens per grid work item of a huge p
 // dealt round-robin to the workgroups, each of which works out the piece's
 // offset itself.  The last tile writes T (and tok_off[P]); *out_n, if given,
 // gets T or the error code.  No copy goes past cap (= n).
+//
+// OFFS: also the byte offset of every token (device-side offset export, the
+// summary page's Path C, §8 / Appendix E): a token's start is its piece's
+// first byte plus the byte lengths of the tokens before it in the piece -- a
+// running sum in the piece's thread, a wavefront scan, or for a huge piece a
+// workgroup scan that starts from the byte lengths of the earlier chunks
+// (k_chunk_sums).  out_starts[T] = cap.
+template <bool OFFS>
 __global__ __launch_bounds__(EMIT_THREADS) void k_emit(Work w, int ntiles, int32_t* __restrict__ out_ids,
-                                                       int64_t* __restrict__ out_n, uint32_t cap) {
+                                                       int64_t* __restrict__ out_n, uint32_t cap,
+                                                       int32_t* __restrict__ out_starts,
+                                                       const uint32_t* __restrict__ tok_len) {
   __shared__ uint32_t red[8];
   const int t = blockIdx.x;
   const int lane = (int)(threadIdx.x & 63u);
@@ -1418,9 +1461,17 @@ __global__ __launch_bounds__(EMIT_THREADS) void k_emit(Work w, int ntiles, int32
     if (live) {
       w.tok_off[p] = (int32_t)off;
       if (c <= 8) {
+        uint32_t at = src;
 #pragma unroll
         for (uint32_t j = 0; j < 8; ++j)
-          if (j < c) out_ids[off + j] = w.tmp_ids[src + j];
+          if (j < c) {
+            const int32_t id = w.tmp_ids[src + j];
+            out_ids[off + j] = id;
+            if (OFFS) {
+              out_starts[off + j] = (int32_t)at;
+              at += tok_len[(uint32_t)id & ID_MASK];
+            }
+          }
       }
     }
     uint64_t big = __ballot(live && c > 8 && c <= (uint32_t)HUGE_TOKENS);
@@ -1428,13 +1479,26 @@ __global__ __launch_bounds__(EMIT_THREADS) void k_emit(Work w, int ntiles, int32
       const int l = __ffsll((unsigned long long)big) - 1;
       big &= big - 1;
       const uint32_t cs = __shfl(src, l), co = __shfl(off, l), cc = __shfl(c, l);
-      if ((uint32_t)lane < cc) out_ids[co + lane] = w.tmp_ids[cs + lane];
+      const bool in = (uint32_t)lane < cc;
+      const int32_t id = in ? w.tmp_ids[cs + lane] : 0;
+      if (in) out_ids[co + lane] = id;
+      if (OFFS) {
+        const uint32_t len = in ? tok_len[(uint32_t)id & ID_MASK] : 0u;
+        uint32_t inc = len;
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+          const uint32_t o = __shfl_up(inc, d);
+          if (lane >= d) inc += o;
+        }
+        if (in) out_starts[co + lane] = (int32_t)(cs + inc - len);
+      }
     }
     off0 += tot;
   }
   if (t == ntiles - 1 && threadIdx.x == 0) {
     w.ctr[CTR_T] = off0;
     w.tok_off[pbase + np] = (int32_t)off0;
+    if (OFFS && off0 <= cap) out_starts[off0] = (int32_t)cap;
     if (out_n) {
       const uint32_t e = w.ctr[CTR_ERR];
       *out_n = e ? err_code(e) : (int64_t)off0;
@@ -1458,7 +1522,34 @@ __global__ __launch_bounds__(EMIT_THREADS) void k_emit(Work w, int ntiles, int32
                          block_reduce(reinterpret_cast<const uint32_t*>(w.piece_cnt) + pb, (int)(p - pb), ~0u, red, &hi);
     for (uint32_t ch = first; ch < nch; ch += gridDim.x) {
       const uint32_t k1 = min(min(cc, (ch + 1) * HUGE_CHUNK), cap - min(cap, dst));  // never past the output
-      for (uint32_t k = ch * HUGE_CHUNK + threadIdx.x; k < k1; k += EMIT_THREADS) out_ids[dst + k] = w.tmp_ids[src + k];
+      if (!OFFS) {
+        for (uint32_t k = ch * HUGE_CHUNK + threadIdx.x; k < k1; k += EMIT_THREADS) out_ids[dst + k] = w.tmp_ids[src + k];
+        continue;
+      }
+      // byte offset of the chunk's first token: the earlier chunks' lengths
+      uint32_t at = src + block_reduce(w.tmp_rank + src, (int)ch, ~0u, red, &hi);
+      for (uint32_t b0 = ch * HUGE_CHUNK; b0 < k1; b0 += EMIT_THREADS * 8) {
+        const uint32_t kb = b0 + 8u * threadIdx.x;  // 8 consecutive tokens per thread
+        int32_t id[8];
+        uint32_t len[8], sum = 0;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) id[j] = kb + j < k1 ? w.tmp_ids[src + kb + j] : 0;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          len[j] = kb + j < k1 ? tok_len[(uint32_t)id[j] & ID_MASK] : 0u;
+          sum += len[j];
+        }
+        uint32_t tot;
+        uint32_t a = at + block_excl_sum(sum, red, &tot);
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          if (kb + j < k1) {
+            out_ids[dst + kb + j] = id[j];
+            out_starts[dst + kb + j] = (int32_t)a;
+            a += len[j];
+          }
+        at += tot;
+      }
     }
   }
 }
@@ -1541,12 +1632,20 @@ hipError_t launch_pretokenize(const uint8_t* bytes, int64_t n, const int64_t* of
 }
 
 hipError_t launch_bpe_emit(const uint8_t* bytes, int64_t n, const Tables& tb, const Work& w, int32_t* out_ids,
-                           int64_t* out_n, hipStream_t st) {
+                           int64_t* out_n, int32_t* out_starts, hipStream_t st) {
   // enough wavefronts to fill the chip; each one loops over work items
   const int g_merge = capped_grid(n, 256, 2048);
   hipLaunchKernelGGL(k_bpe_merge, dim3(g_merge), dim3(MERGE_THREADS), 0, st, bytes, w, tb); prof_mark("k_bpe_merge", st);
   const int ntiles = ceil_div(n, TILE);
-  hipLaunchKernelGGL(k_emit, dim3(ntiles), dim3(EMIT_THREADS), 0, st, w, ntiles, out_ids, out_n, (uint32_t)n);
+  if (out_starts) {
+    hipLaunchKernelGGL(k_chunk_sums, dim3(capped_grid(n, HUGE_CHUNK, 1024)), dim3(EMIT_THREADS), 0, st, w, tb.tok_len);
+    prof_mark("k_chunk_sums", st);
+    hipLaunchKernelGGL(k_emit<true>, dim3(ntiles), dim3(EMIT_THREADS), 0, st, w, ntiles, out_ids, out_n, (uint32_t)n,
+                       out_starts, tb.tok_len);
+  } else {
+    hipLaunchKernelGGL(k_emit<false>, dim3(ntiles), dim3(EMIT_THREADS), 0, st, w, ntiles, out_ids, out_n, (uint32_t)n,
+                       nullptr, nullptr);
+  }
   prof_mark("k_emit", st);
   return hipGetLastError();
 }

@@ -128,6 +128,31 @@ int tt_encode_batch(const uint8_t* dev_bytes, int64_t n, const int64_t* dev_offs
 int tt_pretokenize(const uint8_t* dev_bytes, int64_t n, const int64_t* dev_offsets, int32_t n_seqs,
                    int32_t* out_starts, int64_t* out_np, hipStream_t stream);
 
+/* tt_encode_offsets -- token ids plus the byte span of every token: the
+ * device-side byte-offset export (TokTier summary page, Path C of §8 and of
+ * Appendix E; §4.4 and §7 note that the pages' GPU path emits ids only and
+ * falls back to the CPU when offsets are needed).
+ *
+ * dev_bytes, n, dev_offsets, n_seqs: as in tt_pretokenize (dev_offsets NULL
+ *              means one text of n bytes).
+ * out_ids      device int32[>= n]: the same ids tt_encode / tt_encode_batch
+ *              give.
+ * out_starts   device int32[>= n + 1]: token i covers bytes
+ *              [out_starts[i], out_starts[i+1]) of dev_bytes -- offsets into
+ *              the whole buffer, also for a batch -- and out_starts[T] = n.
+ *              Token byte spans never split a pre-token boundary but may
+ *              split a multi-byte char (byte-level tokens).
+ * out_counts   device int64: with dev_offsets NULL, [1] receiving T or
+ *              TT_EUTF8; else [n_seqs + 1] as out_offsets of tt_encode_batch.
+ *              On a data error out_ids and out_starts are unspecified.
+ * Same enqueue-only contract as tt_encode.  Each token's byte length comes
+ * from a table built by tt_load_bpe; the extra device work over tt_encode is
+ * one gather per token and, for a pre-token of more than 16,384 tokens, one
+ * extra read of its ids.
+ */
+int tt_encode_offsets(const uint8_t* dev_bytes, int64_t n, const int64_t* dev_offsets, int32_t n_seqs,
+                      int32_t* out_ids, int32_t* out_starts, int64_t* out_counts, hipStream_t stream);
+
 /* tt_char_class -- host query of the compiled Unicode class table:
  * 0 other, 1 letter (\p{L}), 2 number (\p{N}), 3 White_Space; -1 if cp is
  * not a Unicode scalar value.  No device work. */

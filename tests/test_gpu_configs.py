@@ -1,7 +1,7 @@
 """The five workloads at full size on the GPU, against stored oracle digests.
 
-tests/golden/expected.json holds, per workload, the oracle's pre-token offsets
-and token ids as SHA-256 digests (written by tests/golden/make_golden.py,
+tests/golden/expected.json holds, per workload, the oracle's pre-token offsets,
+token ids and token byte offsets as SHA-256 digests (written by tests/golden/make_golden.py,
 which calls only the oracle and the seeded generators).  The GPU output must
 match them bit for bit, in the same launch configuration bench.py times (one
 tt_encode per text, one tt_encode_batch for the 64-text batch).  On a
@@ -68,3 +68,23 @@ def test_workload_bit_exact(name):
     # a second run on the same buffers is identical (no state leaks between calls)
     again = tt.encode(x).cpu().numpy() if off is None else tt.encode_batch(x, off)[0].cpu().numpy()
     assert np.array_equal(again, ids)
+
+
+@pytest.mark.parametrize("name", ["c1", "c2", "c3", "c4", "c5a", "c5b", "c5c", "c5d"])
+def test_workload_offsets_bit_exact(name):
+    """tt_encode_offsets: the same ids, and every token's byte offset equal to
+    the oracle's running byte length (digest), at full size."""
+    exp = EXPECTED[name]
+    data, offs, pat, voc = workload(name)
+    print("offsets workload %s: %d bytes, pattern %d, vocab %s" % (name, len(data), pat, voc), flush=True)
+    tt.load(np.load(os.path.join(ROOT, "data", "vocab_%s.npy" % voc)), pattern_id=pat)
+    x = torch.frombuffer(bytearray(data), dtype=torch.uint8).cuda()
+    if offs is None:
+        ids, starts = tt.encode_offsets(x)
+    else:
+        ids, starts, cnt = tt.encode_offsets(x, torch.tensor(offs, dtype=torch.int64, device="cuda"))
+        assert cnt.tolist() == exp["out_offsets"]
+    ids, starts = ids.cpu().numpy(), starts.cpu().numpy()
+    assert len(ids) == exp["tokens"] and sha(ids) == exp["ids_sha256"]
+    assert len(starts) == exp["tokens"] + 1 and starts[-1] == len(data)
+    assert sha(starts) == exp["token_starts_sha256"]
