@@ -274,6 +274,67 @@ def run_workload(name, steps, warmup, graph=True, cpu=True, traffic=None):
     return res
 
 
+def run_session(steps, append_chars=1400):
+    """Incremental repair (tt_session_append) on the 1M-char text as the
+    session's context: host-inclusive latency of appends of ``append_chars``
+    chars (the pages' median interactive append), against a full
+    tt_encode_offsets of the same grown text; the session's tokens are checked
+    against that full encode."""
+    import numpy as np
+    import torch
+
+    import exact_byte_level_amd as tt
+    from synth.text import workload
+    from synth import mix_text
+
+    data, offs, pat, voc = workload("c2")
+    merges = np.load(os.path.join(ROOT, "data", "vocab_%s.npy" % voc))
+    tt.load(merges, pattern_id=pat)
+    extra = mix_text(append_chars * (steps + 8), 4321)
+    cap = len(data) + len(extra) + 16
+    tt.reserve(cap, 1)
+    s = tt.Session(cap)
+    x = torch.frombuffer(bytearray(data), dtype=torch.uint8).cuda()
+    ext = torch.frombuffer(bytearray(extra), dtype=torch.uint8).cuda()
+    s.reset(x)
+    lat, full, ways = [], [], {}
+    out = torch.empty(cap, dtype=torch.int32, device="cuda")
+    st = torch.empty(cap + 1, dtype=torch.int32, device="cuda")
+    cnt = torch.empty(1, dtype=torch.int64, device="cuda")
+    pos = 0
+    for k in range(steps + 3):
+        d = ext[pos:pos + append_chars]
+        pos += append_chars
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        info = s.append(d)
+        t1 = time.perf_counter()
+        ways[info["doublings"]] = ways.get(info["doublings"], 0) + 1
+        n, T = s.sizes()
+        text = s.text()
+        torch.cuda.synchronize()
+        t2 = time.perf_counter()
+        tt.encode_offsets_into(text, None, out, st, cnt)
+        int(cnt.item())
+        t3 = time.perf_counter()
+        if k >= 3:
+            lat.append((t1 - t0) * 1e3)
+            full.append((t3 - t2) * 1e3)
+    ok = (int(cnt.item()) == T and torch.equal(out[:T], s.ids()) and torch.equal(st[:T + 1], s.starts()))
+    if not ok:
+        raise RuntimeError("session tokens differ from a full encode")
+    s.close()
+    return {
+        "context_chars": len(data),
+        "append_chars": append_chars,
+        "appends": steps,
+        "append_p50_ms": statistics.median(lat),
+        "full_reencode_p50_ms": statistics.median(full),
+        "ways": {str(k): v for k, v in sorted(ways.items())},
+        "verified_against_full_encode": ok,
+    }
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -283,6 +344,7 @@ def main():
     ap.add_argument("--all", action="store_true", help="also bench every workload (lines on stderr)")
     ap.add_argument("--no-graph", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-session", action="store_true", help="skip the incremental-repair latency line")
     ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "traffic.json"),
                     help="measured HBM traffic of the dominant kernel (rocprofv3 PMC), if present")
     ap.add_argument("--copy-probe", type=int, default=0,
@@ -314,6 +376,7 @@ def main():
 
     res = run_workload(args.workload, args.steps, args.warmup, graph=not args.no_graph,
                        cpu=not args.no_cpu, traffic=traffic)
+    sess = run_session(min(args.steps, 50)) if args.workload == "c2" and not args.no_session else None
     chars_per_s = res["chars"] / (res["ms_per_step"] * 1e-3)
     line = {
         "metric": METRIC,
@@ -344,6 +407,7 @@ def main():
             "end_to_end_alg_GBps": (res["bytes"] + 4 * res["tokens"]) / (res["ms_per_step"] * 1e-3) / 1e9,
             "kernels_ms": res["kernels_ms"],
             "verified_against_oracle": res["verified"],
+            "session": sess,
             "parallelism": "single GPU",
         },
         "roofline": res["roofline"],

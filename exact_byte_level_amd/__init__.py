@@ -29,6 +29,7 @@ TT_EUTF8 = -5
 TT_ENOTLOADED = -6
 TT_EOFFSETS = -7
 TT_ETOOBIG = -8
+TT_ESTALE = -9
 
 _lib = None
 
@@ -53,6 +54,12 @@ def lib():
         L.tt_encode_batch.argtypes = [vp, i64, vp, i32, vp, vp, vp]
         L.tt_pretokenize.argtypes = [vp, i64, vp, i32, vp, vp, vp]
         L.tt_encode_offsets.argtypes = [vp, i64, vp, i32, vp, vp, vp, vp]
+        L.tt_session_create.argtypes = [i64, i64, vp]
+        L.tt_session_destroy.argtypes = [vp]
+        L.tt_session_reset.argtypes = [vp, vp, i64, vp]
+        L.tt_session_append.argtypes = [vp, vp, i64, vp, vp]
+        L.tt_session_view.argtypes = [vp, vp, vp, vp, vp, vp]
+        L.tt_session_read.argtypes = [vp, vp, vp, vp, vp]
         L.tt_char_class.argtypes = [ctypes.c_uint32]
         L.tt_profile.argtypes = [ctypes.c_int]
         L.tt_profile_read.argtypes = [ctypes.POINTER(ctypes.c_char_p), ctypes.POINTER(ctypes.c_float), ctypes.c_int]
@@ -61,7 +68,8 @@ def lib():
         L.tt_strerror.argtypes = [ctypes.c_int]
         L.tt_strerror.restype = ctypes.c_char_p
         for f in ("tt_load_bpe", "tt_reserve", "tt_encode", "tt_encode_batch", "tt_pretokenize", "tt_encode_offsets",
-                  "tt_char_class", "tt_profile", "tt_profile_read"):
+                  "tt_session_create", "tt_session_destroy", "tt_session_reset", "tt_session_append",
+                  "tt_session_view", "tt_session_read", "tt_char_class", "tt_profile", "tt_profile_read"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -187,6 +195,71 @@ def encode_offsets(data, offsets=None, stream=None):
     if offsets is None:
         return out[:t], starts[:t + 1]
     return out[:t], starts[:t + 1], c
+
+
+class Session:
+    """A growing text kept on the device with its ids and token byte starts;
+    appends are repaired from a tail window (tt_session_* in include/tt.h).
+
+        s = tt.Session(capacity=4 << 20)
+        s.reset(u8_cuda_tensor)
+        info = s.append(u8_cuda_delta)   # {'doublings': 0..5 or -1, ...}
+        ids, starts = s.ids(), s.starts()
+    """
+
+    def __init__(self, capacity, tail_bytes=0):
+        h = ctypes.c_void_p()
+        _check(lib().tt_session_create(int(capacity), int(tail_bytes), ctypes.byref(h)), "tt_session_create")
+        self._h = h
+
+    def close(self):
+        if self._h:
+            lib().tt_session_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def reset(self, data, stream=None):
+        n = data.numel()
+        _check(lib().tt_session_reset(self._h, data.data_ptr() if n else None, n, _stream(stream)),
+               "tt_session_reset")
+
+    def append(self, delta, stream=None):
+        """Append a uint8 CUDA tensor; returns how the tokens were repaired."""
+        info = (ctypes.c_int64 * 4)()
+        n = delta.numel()
+        _check(lib().tt_session_append(self._h, delta.data_ptr() if n else None, n, info, _stream(stream)),
+               "tt_session_append")
+        return {"doublings": int(info[0]), "window_bytes": int(info[1]), "splice": int(info[2]),
+                "tokens": int(info[3])}
+
+    def sizes(self):
+        n, t = ctypes.c_int64(), ctypes.c_int64()
+        _check(lib().tt_session_view(self._h, None, ctypes.byref(n), None, None, ctypes.byref(t)), "tt_session_view")
+        return n.value, t.value
+
+    def _read(self, which, stream=None):
+        import torch
+        n, t = self.sizes()
+        size, dtype = {"text": (n, torch.uint8), "ids": (t, torch.int32), "starts": (t + 1, torch.int32)}[which]
+        out = torch.empty(max(size, 1), dtype=dtype, device="cuda")
+        ptrs = [None, None, None]
+        ptrs[["text", "ids", "starts"].index(which)] = out.data_ptr()
+        _check(lib().tt_session_read(self._h, *ptrs, _stream(stream)), "tt_session_read")
+        return out[:size]
+
+    def text(self, stream=None):
+        return self._read("text", stream)
+
+    def ids(self, stream=None):
+        return self._read("ids", stream)
+
+    def starts(self, stream=None):
+        return self._read("starts", stream)
 
 
 def char_class(cp):

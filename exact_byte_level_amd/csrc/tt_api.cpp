@@ -1,6 +1,7 @@
 // tt_api.cpp -- C ABI of libtt: tokenizer loading, device tables, workspace,
 // and the enqueue-only encode entry points declared in include/tt.h.
 #include <algorithm>
+#include <new>
 #include <cstring>
 #include <mutex>
 #include <unordered_map>
@@ -22,6 +23,7 @@ struct State {
   bool loaded = false;
   int pattern = 0;
   int64_t n_merges = 0;
+  uint64_t generation = 0;  // bumped by every load and free: sessions keep the one they began with
   int device = -1;
   uint32_t* d_byte_pair = nullptr;
   uint64_t* d_pair = nullptr;
@@ -35,6 +37,10 @@ struct State {
 
 State g;
 std::mutex g_mu;
+
+constexpr int64_t SESSION_DEFAULT_TAIL = 2048;
+constexpr int64_t SESSION_MIN_TAIL = 64;
+constexpr int64_t SESSION_MAX_TAIL = (int64_t)1 << 24;
 
 // Per-kernel timing (measurement aid): events recorded after each launch.
 constexpr int PROF_CAP = 64;
@@ -92,6 +98,7 @@ std::vector<uint32_t> host_bpe(const std::vector<uint32_t>& in,
 }
 
 void release_tables() {
+  ++g.generation;
   free_dev(g.d_byte_pair);
   free_dev(g.d_pair);
   free_dev(g.d_cache);
@@ -184,6 +191,61 @@ int check_stream_state() {
   int dev = -1;
   if (hipGetDevice(&dev) != hipSuccess || dev != g.device) return TT_EINVAL;
   return TT_OK;
+}
+
+}  // namespace
+
+// A session's device-resident state: the text so far, its token ids and the
+// byte start of every token (plus the end), window scratch, and the repair
+// step's info block (device and pinned host copies).
+struct tt_session {
+  int64_t cap = 0;
+  int64_t tail = SESSION_DEFAULT_TAIL;
+  int64_t n = 0, T = 0;
+  uint64_t gen = 0;
+  bool valid = false;
+  uint8_t* text = nullptr;
+  int32_t* ids = nullptr;
+  int32_t* starts = nullptr;
+  int32_t* win_ids = nullptr;
+  int32_t* win_starts = nullptr;
+  int64_t* info_dev = nullptr;
+  int64_t* info_host = nullptr;
+  int64_t next_w0[SESSION_LEVELS] = {};
+};
+
+namespace {
+
+void session_release(tt_session* s) {
+  free_dev(s->text);
+  free_dev(s->ids);
+  free_dev(s->starts);
+  free_dev(s->win_ids);
+  free_dev(s->win_starts);
+  free_dev(s->info_dev);
+  if (s->info_host) (void)hipHostFree(s->info_host);
+  s->info_host = nullptr;
+}
+
+// Read the info block of the last step (one stream synchronisation).
+int session_read_info(tt_session* s, hipStream_t st) {
+  if (hipMemcpyAsync(s->info_host, s->info_dev, SI_COUNT * sizeof(int64_t), hipMemcpyDeviceToHost, st) != hipSuccess ||
+      hipStreamSynchronize(st) != hipSuccess)
+    return TT_EHIP;
+  return TT_OK;
+}
+
+void session_take_windows(tt_session* s) {
+  for (int k = 0; k < SESSION_LEVELS; ++k) s->next_w0[k] = s->info_host[SI_NEXT_W0 + k];
+}
+
+// Full encode of the session text [0, n) into the session arrays.
+int session_full(tt_session* s, int64_t n, hipStream_t st) {
+  if (launch_pretokenize(s->text, n, nullptr, 1, g.pattern, g.w, g.w.piece_start, nullptr, &g.tb, st) != hipSuccess ||
+      launch_bpe_emit(s->text, n, g.tb, g.w, s->ids, s->info_dev + SI_WIN_CNT, s->starts, st) != hipSuccess ||
+      launch_session_full(s->text, n, s->tail, g.w, s->info_dev, st) != hipSuccess)
+    return TT_EHIP;
+  return session_read_info(s, st);
 }
 
 }  // namespace
@@ -430,6 +492,161 @@ int tt_encode_offsets(const uint8_t* dev_bytes, int64_t n, const int64_t* dev_of
   return TT_OK;
 }
 
+int tt_session_create(int64_t capacity, int64_t tail_bytes, tt_session** out) {
+  std::lock_guard<std::mutex> lock(g_mu);
+  if (!out || capacity < 0 || tail_bytes < 0 || (tail_bytes && tail_bytes < SESSION_MIN_TAIL)) return TT_EINVAL;
+  if (capacity >= TT_MAX_BYTES || tail_bytes > SESSION_MAX_TAIL) return TT_ETOOBIG;
+  *out = nullptr;
+  int rc = check_stream_state();
+  if (rc != TT_OK) return rc;
+  if ((rc = ensure_workspace(capacity)) != TT_OK) return rc;
+  tt_session* s = new (std::nothrow) tt_session();
+  if (!s) return TT_ENOMEM;
+  s->cap = capacity;
+  s->tail = tail_bytes ? tail_bytes : SESSION_DEFAULT_TAIL;
+  const size_t c1 = (size_t)capacity + 1;
+  bool ok = hipMalloc((void**)&s->text, c1 + 16) == hipSuccess && hipMalloc((void**)&s->ids, c1 * 4) == hipSuccess &&
+            hipMalloc((void**)&s->starts, c1 * 4) == hipSuccess && hipMalloc((void**)&s->win_ids, c1 * 4) == hipSuccess &&
+            hipMalloc((void**)&s->win_starts, c1 * 4) == hipSuccess &&
+            hipMalloc((void**)&s->info_dev, SI_COUNT * sizeof(int64_t)) == hipSuccess &&
+            hipHostMalloc((void**)&s->info_host, SI_COUNT * sizeof(int64_t), hipHostMallocDefault) == hipSuccess;
+  if (!ok) {
+    (void)hipGetLastError();
+    session_release(s);
+    delete s;
+    return TT_ENOMEM;
+  }
+  *out = s;
+  return TT_OK;
+}
+
+int tt_session_destroy(tt_session* s) {
+  std::lock_guard<std::mutex> lock(g_mu);
+  if (!s) return TT_EINVAL;
+  (void)hipDeviceSynchronize();
+  session_release(s);
+  delete s;
+  return TT_OK;
+}
+
+int tt_session_reset(tt_session* s, const uint8_t* dev_bytes, int64_t n, hipStream_t stream) {
+  std::lock_guard<std::mutex> lock(g_mu);
+  if (!s || n < 0 || (n > 0 && !dev_bytes)) return TT_EINVAL;
+  if (n > s->cap) return TT_ETOOBIG;
+  int rc = check_stream_state();
+  if (rc != TT_OK) return rc;
+  s->valid = false;
+  s->n = s->T = 0;
+  if ((rc = ensure_workspace(std::max<int64_t>(n, 1))) != TT_OK) return rc;
+  prof_begin(stream);
+  if (n == 0) {
+    if (launch_write_zero_i32(s->starts, stream) != hipSuccess || hipStreamSynchronize(stream) != hipSuccess)
+      return TT_EHIP;
+    for (int k = 0; k < SESSION_LEVELS; ++k) s->next_w0[k] = 0;
+  } else {
+    if (hipMemcpyAsync(s->text, dev_bytes, (size_t)n, hipMemcpyDeviceToDevice, stream) != hipSuccess) return TT_EHIP;
+    if ((rc = session_full(s, n, stream)) != TT_OK) return rc;
+    if (s->info_host[SI_ERROR] != 0) return (int)s->info_host[SI_ERROR];
+    s->n = n;
+    s->T = s->info_host[SI_T];
+    session_take_windows(s);
+  }
+  s->gen = g.generation;
+  s->valid = true;
+  return TT_OK;
+}
+
+int tt_session_append(tt_session* s, const uint8_t* dev_delta, int64_t nd, int64_t* out_info, hipStream_t stream) {
+  std::lock_guard<std::mutex> lock(g_mu);
+  if (!s || nd < 0 || (nd > 0 && !dev_delta)) return TT_EINVAL;
+  int rc = check_stream_state();
+  if (rc != TT_OK) return rc;
+  if (!s->valid) return TT_EINVAL;
+  if (s->gen != g.generation) return TT_ESTALE;
+  if (nd > s->cap - s->n) return TT_ETOOBIG;
+  int64_t info[4] = {0, 0, -1, s->T};
+  if (nd == 0) {
+    if (out_info) std::memcpy(out_info, info, sizeof(info));
+    return TT_OK;
+  }
+  const int64_t n_old = s->n, n_new = s->n + nd;
+  if ((rc = ensure_workspace(n_new)) != TT_OK) return rc;
+  prof_begin(stream);
+  if (hipMemcpyAsync(s->text + n_old, dev_delta, (size_t)nd, hipMemcpyDeviceToDevice, stream) != hipSuccess)
+    return TT_EHIP;
+  int64_t prev = -1;
+  bool odd = false;
+  for (int k = 0; k < SESSION_LEVELS && !odd; ++k) {
+    const int64_t w0 = s->next_w0[k];
+    if (w0 == prev) continue;
+    prev = w0;
+    const int64_t nw = n_new - w0;
+    if (launch_pretokenize(s->text + w0, nw, nullptr, 1, g.pattern, g.w, g.w.piece_start, nullptr, &g.tb, stream) !=
+            hipSuccess ||
+        launch_bpe_emit(s->text + w0, nw, g.tb, g.w, s->win_ids, s->info_dev + SI_WIN_CNT, s->win_starts, stream) !=
+            hipSuccess ||
+        launch_splice(s->text, w0, n_old, n_new, g.pattern, s->tail, s->ids, s->starts, s->T, s->win_ids,
+                      s->win_starts, g.w, s->info_dev, stream) != hipSuccess)
+      return TT_EHIP;
+    if ((rc = session_read_info(s, stream)) != TT_OK) return rc;
+    const int64_t* h = s->info_host;
+    if (h[SI_ERROR] != 0) return (int)h[SI_ERROR];  // Δ rejected; the session is unchanged
+    if (h[SI_STATUS] == SS_SPLICED) {
+      s->n = n_new;
+      s->T = h[SI_T];
+      session_take_windows(s);
+      info[0] = k;
+      info[1] = nw;
+      info[2] = h[SI_P];
+      info[3] = s->T;
+      if (out_info) std::memcpy(out_info, info, sizeof(info));
+      return TT_OK;
+    }
+    odd = h[SI_STATUS] == SS_ODD;
+  }
+  // no window qualified: encode the whole text
+  if ((rc = session_full(s, n_new, stream)) != TT_OK) return rc;
+  if (s->info_host[SI_ERROR] != 0) {
+    s->valid = false;
+    return (int)s->info_host[SI_ERROR];
+  }
+  s->n = n_new;
+  s->T = s->info_host[SI_T];
+  session_take_windows(s);
+  info[0] = -1;
+  info[1] = n_new;
+  info[2] = 0;
+  info[3] = s->T;
+  if (out_info) std::memcpy(out_info, info, sizeof(info));
+  return TT_OK;
+}
+
+int tt_session_view(const tt_session* s, const uint8_t** text, int64_t* n, const int32_t** ids,
+                    const int32_t** starts, int64_t* T) {
+  std::lock_guard<std::mutex> lock(g_mu);
+  if (!s) return TT_EINVAL;
+  if (text) *text = s->text;
+  if (n) *n = s->n;
+  if (ids) *ids = s->ids;
+  if (starts) *starts = s->starts;
+  if (T) *T = s->T;
+  return TT_OK;
+}
+
+int tt_session_read(const tt_session* s, uint8_t* text_out, int32_t* ids_out, int32_t* starts_out,
+                    hipStream_t stream) {
+  std::lock_guard<std::mutex> lock(g_mu);
+  if (!s || !s->valid) return TT_EINVAL;
+  if ((text_out && s->n &&
+       hipMemcpyAsync(text_out, s->text, (size_t)s->n, hipMemcpyDeviceToDevice, stream) != hipSuccess) ||
+      (ids_out && s->T &&
+       hipMemcpyAsync(ids_out, s->ids, (size_t)s->T * 4, hipMemcpyDeviceToDevice, stream) != hipSuccess) ||
+      (starts_out &&
+       hipMemcpyAsync(starts_out, s->starts, (size_t)(s->T + 1) * 4, hipMemcpyDeviceToDevice, stream) != hipSuccess))
+    return TT_EHIP;
+  return TT_OK;
+}
+
 int tt_char_class(uint32_t cp) {
   if (cp > 0x10FFFF || (cp >= 0xD800 && cp <= 0xDFFF)) return -1;
   uint32_t hi = cp >> 8;
@@ -486,6 +703,7 @@ const char* tt_strerror(int code) {
     case TT_ENOTLOADED: return "no tokenizer loaded";
     case TT_EOFFSETS: return "invalid batch offsets";
     case TT_ETOOBIG: return "size beyond library limits";
+    case TT_ESTALE: return "tokenizer replaced since the session began";
     default: return "unknown error";
   }
 }

@@ -148,4 +148,21 @@ constexpr int BIG_BYTES = 2048;         // longer pieces: merged by the workgrou
 constexpr int EMIT_THREADS = 256;       // emission workgroup (one tile's pieces)
 constexpr int HUGE_TOKENS = 64;         // pieces with more tokens are copied by the whole grid
 
+// ------------------------------------------------------------- sessions
+constexpr int SESSION_LEVELS = 6;       // window sizes tail << 0 .. tail << 5 before a full encode
+// info[] of one repair step (device int64; the host reads it after the step)
+enum : int {
+  SI_STATUS = 0,   // SPLICED, FULL, NONE (no qualifying p in this window), ODD (bookkeeping mismatch)
+  SI_ERROR = 1,    // 0 or a negative TT_* data error code of the window encode
+  SI_T = 2,        // tokens of the whole text after the step
+  SI_P = 3,        // splice byte
+  SI_IOLD = 4,     // index of p among A's token starts
+  SI_IWIN = 5,     // index of p - w0 among W's token starts
+  SI_TWIN = 6,     // tokens of W
+  SI_NEXT_W0 = 7,  // [7, 7 + SESSION_LEVELS): window starts for the next append
+  SI_WIN_CNT = 14, // the window encode's count (T or error code)
+  SI_COUNT = 16
+};
+enum : int64_t { SS_NONE = 0, SS_SPLICED = 1, SS_FULL = 2, SS_ODD = 3 };
+
 }  // namespace tt

@@ -30,6 +30,18 @@ hipError_t launch_finish_count(const Work& w, int which, int64_t* out, hipStream
 hipError_t launch_batch_offsets(const int64_t* offs, int nseq, int64_t n, const Work& w, int64_t* out_off,
                                 hipStream_t st);
 
+// Incremental repair step after the window text[w0, n_new) was encoded into
+// win_ids / win_starts (count in info[SI_WIN_CNT]): choose the splice byte
+// and, if one qualifies, copy the window's tokens from it over ids / starts
+// (t_old tokens of text[0, n_old)).  Results and the next append's window
+// starts go to info (device int64[SI_COUNT]).
+hipError_t launch_splice(const uint8_t* text, int64_t w0, int64_t n_old, int64_t n_new, int pattern, int64_t tail,
+                         int32_t* ids, int32_t* starts, int64_t t_old, const int32_t* win_ids,
+                         const int32_t* win_starts, const Work& w, int64_t* info, hipStream_t st);
+// After a full encode of text[0, n) with its count in info[SI_WIN_CNT].
+hipError_t launch_session_full(const uint8_t* text, int64_t n, int64_t tail, const Work& w, int64_t* info,
+                               hipStream_t st);
+
 hipError_t launch_write_zeros(int64_t* out, int cnt, hipStream_t st);
 hipError_t launch_write_zero_i32(int32_t* out, hipStream_t st);
 hipError_t launch_zero_counters(const Work& w, hipStream_t st);

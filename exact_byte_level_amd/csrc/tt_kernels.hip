@@ -1554,6 +1554,188 @@ __global__ __launch_bounds__(EMIT_THREADS) void k_emit(Work w, int ntiles, int32
   }
 }
 
+// ------------------------------------------------------- incremental repair
+//
+// A session holds a text A (n_old bytes), its token ids and the byte start of
+// every token.  After Δ is appended, the window W = X[w0, n_new) of X = A + Δ
+// is encoded on its own, and X's tokens are A's tokens before a splice byte p
+// followed by W's tokens from p (TokTier summary page, §3.3 and the splicing
+// theorem of Appendix A.2).  p qualifies when
+//   (1) p is a pre-token start of W, with w0 + 16 <= p and p + 20 <= n_old;
+//   (2) cl100k-style rules only: the chars at p - 1 and p differ in class
+//       (letter / number / whitespace / other): a class-run start.
+// Why this is exact: every start decision of both rule sets reads at most 4
+// chars to the left (an apostrophe 3 chars back and the char before it) and
+// 4 to the right (16 bytes hold at least 4 chars; 20 bytes at least 5).  The
+// GPT-2-style rules read nothing else, so W's starts at or after p are X's,
+// and A's starts before p are X's.  The cl100k-style rules also read the
+// whole run they sit in (digit groups count from the run start, whitespace
+// runs look at their newlines and their end): from a run start p on, every
+// run lies inside W with its left neighbour inside W too, and every run
+// before p ends at or before p, inside A and at least 5 chars before A's end.
+// Pre-tokens are encoded independently (Appendix A.1), so equal pre-tokens
+// give equal tokens.  This is the pages' char-class synchronisation boundary,
+// with the two rule sets' exact reach in place of the generic matched-token
+// certificate.
+
+
+// class of the char starting at byte q (the text is valid UTF-8): 1 letter,
+// 2 number, 3 other, 4 whitespace
+__device__ uint32_t class4_at(const uint8_t* __restrict__ text, int64_t q) {
+  const uint32_t b0 = text[q];
+  if (b0 < 0x80u) {
+    const uint32_t c = cls_of(g_ascii.v[b0]);
+    return c == C_L ? 1u : c == C_N ? 2u : is_w(c) ? 4u : 3u;
+  }
+  uint32_t cp, len;
+  if (b0 < 0xE0u) { cp = b0 & 0x1Fu; len = 2; }
+  else if (b0 < 0xF0u) { cp = b0 & 0x0Fu; len = 3; }
+  else { cp = b0 & 0x07u; len = 4; }
+  for (uint32_t k = 1; k < len; ++k) cp = (cp << 6) | (text[q + k] & 0x3Fu);
+  const uint32_t hi = cp >> 8;
+  uint32_t u = 0;
+  if (hi < (uint32_t)TT_UNI_L1_SIZE) {
+    const uint32_t idx = (uint32_t)g_uni_l1[hi] * 64u + ((cp & 255u) >> 2);
+    u = (g_uni_l2[idx] >> ((cp & 3u) * 2u)) & 3u;
+  }
+  return u == 1u ? 1u : u == 2u ? 2u : u == 3u ? 4u : 3u;
+}
+
+// start of the char that ends right before byte q (q > 0)
+__device__ __forceinline__ int64_t prev_char_start(const uint8_t* __restrict__ text, int64_t q) {
+  int64_t s = q - 1;
+  for (int k = 0; k < 3 && s > 0 && (text[s] & 0xC0u) == 0x80u; ++k) --s;
+  return s;
+}
+
+// first index i in [0, cnt] with a[i] >= v
+__device__ __forceinline__ int64_t lower_bound_i32(const int32_t* __restrict__ a, int64_t cnt, int64_t v) {
+  int64_t lo = 0, hi = cnt;
+  while (lo < hi) {
+    const int64_t mid = (lo + hi) >> 1;
+    if ((int64_t)a[mid] < v) lo = mid + 1; else hi = mid;
+  }
+  return lo;
+}
+
+// window starts of the next append for a text of n bytes: char starts at or
+// before n - (tail << k), or 0
+__device__ void session_next_windows(const uint8_t* __restrict__ text, int64_t n, int64_t tail, int64_t* info) {
+  for (int k = 0; k < SESSION_LEVELS; ++k) {
+    int64_t s = n - (tail << k);
+    if (s <= 0) {
+      s = 0;
+    } else {
+      for (int j = 0; j < 3 && s > 0 && (text[s] & 0xC0u) == 0x80u; ++j) --s;
+    }
+    info[SI_NEXT_W0 + k] = s;
+  }
+}
+
+// One workgroup: pick the splice byte (the first qualifying pre-token start
+// of the window) and the token indices on both sides.
+__global__ __launch_bounds__(256) void k_splice_find(const uint8_t* __restrict__ text, int64_t w0, int64_t n_old,
+                                                     int pattern, const int32_t* __restrict__ starts, int64_t t_old,
+                                                     const int32_t* __restrict__ win_starts, Work w,
+                                                     int64_t* __restrict__ info) {
+  __shared__ uint32_t red[8];
+  const int64_t wc = info[SI_WIN_CNT];
+  const uint32_t err = w.ctr[CTR_ERR];
+  if (wc < 0 || err) {
+    if (threadIdx.x == 0) {
+      info[SI_STATUS] = SS_NONE;
+      info[SI_ERROR] = wc < 0 ? wc : err_code(err);
+    }
+    return;
+  }
+  const uint32_t P = w.ctr[CTR_P];
+  int64_t p = -1;
+  if (w0 == 0) {
+    p = 0;  // the window is the whole text
+  } else {
+    const int64_t lo = 16, hi = n_old - 20 - w0;  // window-relative range of p
+    // first piece starting at or after lo
+    uint32_t a = 0, b = P;
+    while (a < b) {
+      const uint32_t mid = (a + b) >> 1;
+      if ((int64_t)w.piece_start[mid] < lo) a = mid + 1; else b = mid;
+    }
+    for (uint32_t k0 = a; k0 < P; k0 += 256) {
+      const uint32_t k = k0 + threadIdx.x;
+      uint32_t best = 0xFFFFFFFFu;
+      const int64_t q = k < P ? (int64_t)w.piece_start[k] : hi + 1;
+      if (q <= hi) {
+        bool ok = true;
+        if (pattern == 1) {
+          const int64_t g = w0 + q;
+          ok = class4_at(text, g) != class4_at(text, prev_char_start(text, g));
+        }
+        if (ok) best = k;
+      }
+      best = block_min(best, red);
+      if (best != 0xFFFFFFFFu) {
+        p = w0 + (int64_t)w.piece_start[best];
+        break;
+      }
+      // no piece of this batch qualified; stop once the batch ran past hi
+      const int64_t last = (int64_t)w.piece_start[min(k0 + 255u, P - 1u)];
+      if (last > hi) break;
+    }
+  }
+  if (threadIdx.x != 0) return;
+  info[SI_ERROR] = 0;
+  info[SI_TWIN] = wc;
+  if (p < 0) {
+    info[SI_STATUS] = SS_NONE;
+    return;
+  }
+  const int64_t iw = lower_bound_i32(win_starts, wc, p - w0);
+  const int64_t io = lower_bound_i32(starts, t_old, p);
+  // p must start a token on both sides (it does whenever the reach argument
+  // holds; a mismatch falls back to a full encode)
+  const bool odd = iw > wc || win_starts[iw] != (int32_t)(p - w0) || io > t_old || starts[io] != (int32_t)p;
+  info[SI_STATUS] = odd ? SS_ODD : SS_SPLICED;
+  info[SI_P] = p;
+  info[SI_IOLD] = io;
+  info[SI_IWIN] = iw;
+  info[SI_T] = io + (wc - iw);
+}
+
+// The splice itself: W's tokens from p (ids, and starts shifted by w0) over
+// the session's arrays from A's token index of p; the end sentinel; the next
+// append's window starts.
+__global__ __launch_bounds__(256) void k_splice_copy(const uint8_t* __restrict__ text, int64_t w0, int64_t n_new,
+                                                     int64_t tail, int32_t* __restrict__ ids,
+                                                     int32_t* __restrict__ starts,
+                                                     const int32_t* __restrict__ win_ids,
+                                                     const int32_t* __restrict__ win_starts,
+                                                     int64_t* __restrict__ info) {
+  if (info[SI_STATUS] != SS_SPLICED) return;
+  const int64_t io = info[SI_IOLD], iw = info[SI_IWIN], wc = info[SI_TWIN];
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = iw + (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < wc; i += stride) {
+    ids[io + (i - iw)] = win_ids[i];
+    starts[io + (i - iw)] = (int32_t)(win_starts[i] + w0);
+  }
+  if (blockIdx.x == 0 && threadIdx.x == 0) {
+    starts[io + (wc - iw)] = (int32_t)n_new;
+    session_next_windows(text, n_new, tail, info);
+  }
+}
+
+// After a full encode of the session text into its own arrays (count in
+// info[SI_WIN_CNT]): status, T and the next append's window starts.
+__global__ void k_session_full(const uint8_t* __restrict__ text, int64_t n, int64_t tail, Work w,
+                               int64_t* __restrict__ info) {
+  const int64_t c = info[SI_WIN_CNT];
+  const uint32_t err = w.ctr[CTR_ERR];
+  info[SI_STATUS] = SS_FULL;
+  info[SI_ERROR] = c < 0 ? c : (err ? err_code(err) : 0);
+  info[SI_T] = c < 0 ? 0 : c;
+  info[SI_P] = 0;
+  session_next_windows(text, n, tail, info);
+}
+
 // ------------------------------------------------------------- small kernels
 
 __global__ void k_zero(uint32_t* ctr, int cnt) {
@@ -1677,6 +1859,25 @@ hipError_t launch_write_zero_i32(int32_t* out, hipStream_t st) {
 
 hipError_t launch_zero_counters(const Work& w, hipStream_t st) {
   hipLaunchKernelGGL(k_zero, dim3(1), dim3(64), 0, st, w.ctr, (int)CTR_RESET_END); prof_mark("k_zero", st);
+  return hipGetLastError();
+}
+
+hipError_t launch_splice(const uint8_t* text, int64_t w0, int64_t n_old, int64_t n_new, int pattern, int64_t tail,
+                         int32_t* ids, int32_t* starts, int64_t t_old, const int32_t* win_ids,
+                         const int32_t* win_starts, const Work& w, int64_t* info, hipStream_t st) {
+  hipLaunchKernelGGL(k_splice_find, dim3(1), dim3(256), 0, st, text, w0, n_old, pattern, starts, t_old, win_starts, w,
+                     info);
+  prof_mark("k_splice_find", st);
+  hipLaunchKernelGGL(k_splice_copy, dim3(capped_grid(n_new - w0, 4096, 1024)), dim3(256), 0, st, text, w0, n_new, tail,
+                     ids, starts, win_ids, win_starts, info);
+  prof_mark("k_splice_copy", st);
+  return hipGetLastError();
+}
+
+hipError_t launch_session_full(const uint8_t* text, int64_t n, int64_t tail, const Work& w, int64_t* info,
+                               hipStream_t st) {
+  hipLaunchKernelGGL(k_session_full, dim3(1), dim3(1), 0, st, text, n, tail, w, info);
+  prof_mark("k_session_full", st);
   return hipGetLastError();
 }
 

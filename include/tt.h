@@ -39,6 +39,7 @@ extern "C" {
 #define TT_ENOTLOADED -6  /* no tokenizer loaded */
 #define TT_EOFFSETS   -7  /* batch offsets not monotone / not ending at n (device-side) */
 #define TT_ETOOBIG    -8  /* size beyond the library's limits */
+#define TT_ESTALE     -9  /* tokenizer replaced since the session was reset (sessions below) */
 
 #define TT_PATTERN_GPT2   0  /* GPT-2-style rules: lower-case contractions, ' ?letters', ' ?digits',
                                 ' ?other', whitespace with the not-followed-by-non-space rule */
@@ -152,6 +153,67 @@ int tt_pretokenize(const uint8_t* dev_bytes, int64_t n, const int64_t* dev_offse
  */
 int tt_encode_offsets(const uint8_t* dev_bytes, int64_t n, const int64_t* dev_offsets, int32_t n_seqs,
                       int32_t* out_ids, int32_t* out_starts, int64_t* out_counts, hipStream_t stream);
+
+/* ---------------------------------------------------------------- sessions
+ *
+ * Incremental repair (TokTier summary page, §3.3, with the splicing theorem
+ * of Appendix A.2): a session keeps a growing text, its token ids and the byte
+ * start of every token in device memory.  After an append only a tail window
+ * (the last tail_bytes of the old text plus the appended bytes) is encoded,
+ * and its tokens are spliced in at a pre-token start that the old and the new
+ * tokenization provably share: at least 16 bytes into the window and 20 bytes
+ * before the old end, and for cl100k-style rules also a change of char class
+ * (letter / number / whitespace / other), the pages' synchronisation boundary.
+ * Without such a start the window doubles, up to 5 times (§3.3), then the
+ * whole text is encoded.  The result always equals a fresh encode of the
+ * whole text.  Sessions belong to the loaded tokenizer: after tt_load_bpe or
+ * tt_free a session must be reset (TT_ESTALE).  Session calls are
+ * host-synchronous (they wait for their stream) and serialised with every
+ * other call of the library.
+ */
+typedef struct tt_session tt_session;
+
+/* tt_session_create -- a session for texts of up to capacity bytes.
+ * tail_bytes: first window size behind the old end (0 = 2048; else
+ * 64 .. 2^24).  Allocates device memory for the text, ids, token starts and
+ * window scratch (17 bytes per byte of capacity) and sizes the shared
+ * workspace for capacity bytes.  Needs a loaded tokenizer.  *out receives the
+ * session.  Returns TT_OK, TT_EINVAL, TT_ETOOBIG, TT_ENOMEM, TT_EHIP or
+ * TT_ENOTLOADED. */
+int tt_session_create(int64_t capacity, int64_t tail_bytes, tt_session** out);
+
+/* tt_session_destroy -- synchronise the device and free the session. */
+int tt_session_destroy(tt_session* s);
+
+/* tt_session_reset -- start the session over with dev_bytes[0, n) (device,
+ * caller-owned, copied): a full encode, ids and byte starts kept in the
+ * session.  n <= capacity (else TT_ETOOBIG).  Invalid UTF-8 gives TT_EUTF8
+ * and leaves the session empty and unusable until the next reset. */
+int tt_session_reset(tt_session* s, const uint8_t* dev_bytes, int64_t n, hipStream_t stream);
+
+/* tt_session_append -- append dev_delta[0, nd) (device, caller-owned,
+ * copied) and repair the tokens.  If the text with the append would not be
+ * valid UTF-8 (including a char split across appends) the call returns
+ * TT_EUTF8 and the session keeps its previous text and tokens.
+ * out_info (host int64[4], may be NULL): [0] windows doubled before the splice
+ * (0..5), or -1 if the whole text was encoded; [1] bytes encoded by the last
+ * window; [2] splice byte; [3] tokens of the whole text.  nd == 0 changes
+ * nothing.  Returns TT_OK, TT_EINVAL (not reset), TT_ETOOBIG (capacity),
+ * TT_ESTALE, TT_EUTF8 or TT_EHIP. */
+int tt_session_append(tt_session* s, const uint8_t* dev_delta, int64_t nd, int64_t* out_info, hipStream_t stream);
+
+/* tt_session_view -- the session's device arrays, valid until the next call
+ * on the session: text uint8[n], ids int32[T], starts int32[T + 1] (token i
+ * covers bytes [starts[i], starts[i+1]); starts[T] = n).  Any output pointer
+ * may be NULL. */
+int tt_session_view(const tt_session* s, const uint8_t** text, int64_t* n, const int32_t** ids,
+                    const int32_t** starts, int64_t* T);
+
+/* tt_session_read -- enqueue device-to-device copies of the session's text
+ * (n bytes), ids (T) and token starts (T + 1) into caller buffers (device;
+ * any may be NULL).  Returns TT_OK, TT_EINVAL or TT_EHIP. */
+int tt_session_read(const tt_session* s, uint8_t* text_out, int32_t* ids_out, int32_t* starts_out,
+                    hipStream_t stream);
 
 /* tt_char_class -- host query of the compiled Unicode class table:
  * 0 other, 1 letter (\p{L}), 2 number (\p{N}), 3 White_Space; -1 if cp is
