@@ -787,6 +787,28 @@ __device__ __forceinline__ uint32_t pair_rank(const Tables& tb, uint32_t x, uint
   return (x | y) < 256u ? bp : r;
 }
 
+// Rank of a pair with an operand >= 256 (every pair next to a new token):
+// no byte-pair table, 24-bit products for the hash (exact: ids < 2^20), the
+// first bucket without a loop.
+__device__ __forceinline__ uint32_t pair_rank_new(const Tables& tb, uint32_t x, uint32_t y) {
+  uint32_t h = __umul24(x, 0x9E3779u) ^ __umul24(y, 0x7FEB35u);
+  h ^= h >> 13;
+  h *= 0x85EBCA6Bu;
+  uint32_t b = h >> tb.pair_shift;
+  const uint64_t k20 = pair_key(x, y) << ID_BITS;
+  const ulonglong2* q = pair_bucket_ptr(tb, b);
+  ulonglong2 e0 = q[0], e1 = q[1];
+  uint32_t r = bucket_match(e0, e1, k20);
+  for (int i = 1; r == RANK_NONE && (e0.x & PAIR_MORE) && i < tb.pair_probe; ++i) {
+    b = (b + 1) & tb.pair_mask;
+    q = pair_bucket_ptr(tb, b);
+    e0 = q[0];
+    e1 = q[1];
+    r = bucket_match(e0, e1, k20);
+  }
+  return r;
+}
+
 // Id of the single-token piece with these bytes (len 2..16), or RANK_NONE.
 // One 128-byte bucket per step (the second key word only for len > 8); the
 // walk ends at the first bucket that no key's probe run passed.
@@ -825,21 +847,32 @@ __device__ __forceinline__ uint32_t dpp(uint32_t x) {
 __device__ __forceinline__ uint32_t lane_up1(uint32_t x) { return dpp<0x130>(x); }
 
 // Minimum over each aligned group of G lanes (G = 8, 16, 32, 64): butterflies
-// inside a 16-lane row by DPP, then across rows by reading the row results.
+// inside a 16-lane row by DPP (folded into the min instructions), then across
+// rows by row broadcasts; G = 32 and 64 read the result from the last lane
+// of each half / of the wavefront.
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_all(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, CTRL, 0xF, 0xF, true);
+}
+template <int CTRL, int ROWS>
+__device__ __forceinline__ uint32_t dpp_rows(uint32_t old, uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_update_dpp((int)old, (int)x, CTRL, ROWS, 0xF, false);
+}
 template <int G>
 __device__ __forceinline__ uint32_t group_min(uint32_t x) {
-  x = min(x, dpp<0xB1>(x));
-  x = min(x, dpp<0x4E>(x));
-  x = min(x, dpp<0x141>(x));
-  if (G >= 16) x = min(x, dpp<0x140>(x));
+  x = min(x, dpp_all<0xB1>(x));
+  x = min(x, dpp_all<0x4E>(x));
+  x = min(x, dpp_all<0x141>(x));
+  if (G >= 16) x = min(x, dpp_all<0x140>(x));
   if (G == 32) {
-    const uint32_t r0 = (uint32_t)__builtin_amdgcn_readlane((int)x, 15), r1 = (uint32_t)__builtin_amdgcn_readlane((int)x, 31);
-    const uint32_t r2 = (uint32_t)__builtin_amdgcn_readlane((int)x, 47), r3 = (uint32_t)__builtin_amdgcn_readlane((int)x, 63);
-    x = ((threadIdx.x & 63u) < 32u) ? min(r0, r1) : min(r2, r3);
+    x = min(x, dpp_rows<0x142, 0xA>(x, x));  // rows 1, 3 += rows 0, 2
+    const uint32_t r0 = (uint32_t)__builtin_amdgcn_readlane((int)x, 31);
+    const uint32_t r1 = (uint32_t)__builtin_amdgcn_readlane((int)x, 63);
+    x = ((threadIdx.x & 63u) < 32u) ? r0 : r1;
   } else if (G == 64) {
-    const uint32_t r0 = (uint32_t)__builtin_amdgcn_readlane((int)x, 15), r1 = (uint32_t)__builtin_amdgcn_readlane((int)x, 31);
-    const uint32_t r2 = (uint32_t)__builtin_amdgcn_readlane((int)x, 47), r3 = (uint32_t)__builtin_amdgcn_readlane((int)x, 63);
-    x = min(min(r0, r1), min(r2, r3));
+    x = min(x, dpp_rows<0x142, 0xA>(x, x));
+    x = min(x, dpp_rows<0x143, 0xC>(x, x));  // rows 2, 3 += row 1
+    x = (uint32_t)__builtin_amdgcn_readlane((int)x, 63);
   }
   return x;
 }
@@ -881,7 +914,7 @@ __device__ void group_bpe(const uint8_t* __restrict__ bytes, const Work& w, cons
     const bool do_l = act && g == bk - 1;
     const bool do_r = act && g == bk && bk + 2 < m;
     uint32_t r = RANK_NONE;
-    if (do_l || do_r) r = pair_rank(tb, do_l ? id : nid, do_l ? nid : id2);
+    if (do_l || do_r) r = pair_rank_new(tb, do_l ? id : nid, do_l ? nid : id2);
     if (act) {
       const uint32_t nid_here = (g < bk) ? id : ((g == bk) ? nid : id1);
       rk = (g < bk - 1) ? rk : ((g == bk - 1 || g == bk) ? r : rk1);
@@ -983,7 +1016,7 @@ __device__ void long_bpe(const uint8_t* __restrict__ bytes, const Work& w, const
       const bool has_next = m0 ? (k + 2 < m) : (k + 1 < m);
       const uint32_t nxt = m0 ? (m2 ? T : id2) : (m1 ? T : id1);
       uint32_t nr = RANK_NONE;
-      if (keep && has_next) nr = (m0 || m1) ? pair_rank(tb, nid, nxt) : r0;
+      if (keep && has_next) nr = (m0 || m1) ? pair_rank_new(tb, nid, nxt) : r0;
       const uint64_t km = __ballot(keep);
       if (keep) {
         const int o = out + __popcll(km & lt_mask);
@@ -1345,7 +1378,7 @@ __global__ __launch_bounds__(PT_THREADS) void k_compact(const uint8_t* __restric
 // over the whole chip.  The item index is the same in every lane, so the loop and the
 // class branches are scalar.
 constexpr int MERGE_THREADS = 256;
-__global__ __launch_bounds__(MERGE_THREADS) void k_bpe_merge(const uint8_t* __restrict__ bytes, Work w, Tables tb) {
+__global__ __launch_bounds__(MERGE_THREADS) __attribute__((amdgpu_waves_per_eu(8, 8))) void k_bpe_merge(const uint8_t* __restrict__ bytes, Work w, Tables tb) {
   // pre[k]: work items before sub-queue k, k = (3 - class) * QGROUPS + group
   // (classes longest first, sub-queues in order); pre[4 * QGROUPS] = all
   constexpr int NQ = 4 * QGROUPS;
@@ -1365,7 +1398,10 @@ __global__ __launch_bounds__(MERGE_THREADS) void k_bpe_merge(const uint8_t* __re
   const uint32_t nl = w.ctr[CTR_NLONG];
   const uint32_t total = nl + uniform(pre[NQ]);
   const uint32_t nwaves = gridDim.x * (MERGE_THREADS / 64);
-  for (uint32_t t = uniform(blockIdx.x * (MERGE_THREADS / 64) + (threadIdx.x >> 6)); t < total; t += nwaves) {
+  const uint32_t wv = uniform(blockIdx.x * (MERGE_THREADS / 64) + (threadIdx.x >> 6));
+  // rounds of nwaves items, every other round dealt in reverse: the waves
+  // that drew the longest items in one round draw the shortest in the next
+  for (uint32_t rnd = 0, t = wv; t < total; ++rnd, t = rnd * nwaves + ((rnd & 1u) ? nwaves - 1u - wv : wv)) {
     if (t < nl) {
       long_bpe(bytes, w, tb, uniform((uint32_t)w.long_list[t]));
       continue;
