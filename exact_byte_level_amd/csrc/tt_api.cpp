@@ -288,27 +288,39 @@ int tt_load_bpe(const int32_t* merges, const int32_t* ranks, int64_t n_merges, i
   for (size_t r = 0; r < M; ++r)
     if (mx[r] < 256 && my[r] < 256) byte_pair[(mx[r] << 8) | my[r]] = (uint32_t)r;
 
-  // pair-rank hash for pairs with an operand >= 256: buckets of PAIR_SLOTS
-  // entries, load factor <= 1/2
-  const uint64_t pair_nb = std::max<uint64_t>(next_pow2((M + 1) / 2), 1024);
-  const int pair_shift = 32 - log2_u64(pair_nb);
-  std::vector<uint64_t> pair_tab(pair_nb * PAIR_SLOTS, 0ull);
-  int pair_probe = 1;
-  for (size_t r = 0; r < M; ++r) {
-    if (mx[r] < 256 && my[r] < 256) continue;
-    uint32_t b = pair_bucket(mx[r], my[r], pair_shift);
-    for (int visited = 1;; ++visited, b = (uint32_t)((b + 1) & (pair_nb - 1))) {
-      uint64_t* bucket = &pair_tab[(size_t)b * PAIR_SLOTS];
-      int slot = -1;
-      for (int s = 0; s < PAIR_SLOTS; ++s)
-        if ((bucket[s] & ~PAIR_MORE) == 0) { slot = s; break; }
-      if (slot >= 0) {
-        bucket[slot] |= (pair_key(mx[r], my[r]) << ID_BITS) | r;
-        pair_probe = std::max(pair_probe, visited);
-        break;
+  // pair-rank table for pairs with an operand >= 256: two-choice slots, load
+  // factor <= 0.45; a failed insertion doubles the table
+  size_t n_pairs = 0;
+  for (size_t r = 0; r < M; ++r) n_pairs += (mx[r] >= 256 || my[r] >= 256);
+  uint64_t pair_ns = std::max<uint64_t>(next_pow2((uint64_t)(n_pairs / 0.45) + 1), 1024);
+  std::vector<uint64_t> pair_tab;
+  int pair_shift = 0;
+  for (;;) {
+    pair_shift = 32 - log2_u64(pair_ns);
+    pair_tab.assign(pair_ns, 0ull);
+    bool ok = true;
+    for (size_t r = 0; r < M && ok; ++r) {
+      if (mx[r] < 256 && my[r] < 256) continue;
+      uint64_t cur = (pair_key(mx[r], my[r]) << ID_BITS) | r;
+      uint32_t h = pair_mix(mx[r], my[r]);
+      uint32_t pos = h >> pair_shift;
+      if (pair_tab[pos] != 0) {
+        const uint32_t alt = pair_alt(h) >> pair_shift;
+        if (pair_tab[alt] == 0) pos = alt;
       }
-      bucket[0] |= PAIR_MORE;  // the probe run goes on past this full bucket
+      ok = false;
+      for (int kick = 0; kick < 1000; ++kick) {
+        std::swap(cur, pair_tab[pos]);
+        if (cur == 0) { ok = true; break; }
+        // move the evicted entry to its other slot
+        const uint32_t ex = (uint32_t)(cur >> (2 * ID_BITS)), ey = (uint32_t)(cur >> ID_BITS) & ID_MASK;
+        const uint32_t eh = pair_mix(ex, ey);
+        const uint32_t p1 = eh >> pair_shift, p2 = pair_alt(eh) >> pair_shift;
+        pos = pos == p1 ? p2 : p1;
+      }
     }
+    if (ok) break;
+    pair_ns *= 2;
   }
 
   // whole-pre-token table: token t of 2..16 bytes whose own BPE is [t]
@@ -378,9 +390,7 @@ int tt_load_bpe(const int32_t* merges, const int32_t* ranks, int64_t n_merges, i
   g.tb.pair_tab = g.d_pair;
   g.tb.cache = g.d_cache;
   g.tb.tok_len = g.d_tok_len;
-  g.tb.pair_mask = (uint32_t)(pair_nb - 1);
   g.tb.pair_shift = pair_shift;
-  g.tb.pair_probe = pair_probe;
   g.tb.cache_mask = (uint32_t)(cache_nb - 1);
   g.tb.cache_shift = cache_shift;
   g.tb.cache_probe = cache_probe;

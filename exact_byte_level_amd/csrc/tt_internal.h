@@ -38,24 +38,23 @@ enum : uint32_t { LT_S = 1, LT_T = 2, LT_R = 3, LT_E = 4, LT_V = 5, LT_M = 6, LT
 constexpr uint32_t RANK_NONE = 0xFFFFFFFFu;
 constexpr int ID_BITS = 20;             // token ids < 2^20
 constexpr uint32_t ID_MASK = (1u << ID_BITS) - 1;
-constexpr int PAIR_SLOTS = 4;           // 32-byte buckets of four 8-byte entries
 
 // Pair-rank table for pairs with an operand >= 256 (byte pairs have their own
-// direct table): entry (left << 40) | (right << 20) | rank, 0 = empty.  Bit 63
-// of a bucket's first entry is set if some key's probe run passed this bucket
-// (it was full): a lookup stops at the first bucket without it.
-constexpr uint64_t PAIR_MORE = 1ull << 63;
+// direct table): a two-choice (cuckoo) table of 8-byte slots, entry
+// (left << 40) | (right << 20) | rank, 0 = empty.  A key sits in one of its
+// two slots, so a lookup is two independent loads and two compares.
 __host__ __device__ inline uint64_t pair_key(uint32_t x, uint32_t y) {
   return ((uint64_t)x << ID_BITS) | (uint64_t)y;
 }
-// Bucket of (x, y): 24-bit products (x, y < 2^20), an xor-shift and one
-// 32-bit product; shift = 32 - log2(buckets).
-__host__ __device__ inline uint32_t pair_bucket(uint32_t x, uint32_t y, int shift) {
+// 32-bit hash of (x, y): 24-bit products (exact for ids < 2^20), an
+// xor-shift and one 32-bit product.  Slot 1 = its top bits, slot 2 = the top
+// bits of its 16-bit rotation xor a constant (shift = 32 - log2(slots)).
+__host__ __device__ inline uint32_t pair_mix(uint32_t x, uint32_t y) {
   uint32_t h = (uint32_t)(x * 0x9E3779u) ^ (uint32_t)(y * 0x7FEB35u);
   h ^= h >> 13;
-  h *= 0x85EBCA6Bu;
-  return h >> shift;
+  return h * 0x85EBCA6Bu;
 }
+__host__ __device__ inline uint32_t pair_alt(uint32_t h) { return ((h >> 16) | (h << 16)) ^ 0x5BD1E995u; }
 
 // Whole-pre-token table: buckets of CACHE_SLOTS entries in one 128-byte line
 // (struct of arrays).  Entry k holds the piece bytes zero-padded into w0[k] /
@@ -84,12 +83,10 @@ __host__ __device__ inline uint32_t cache_hash(uint64_t w0, uint64_t w1, uint32_
 // Device-resident tables of the loaded tokenizer (passed by value).
 struct Tables {
   const uint32_t* byte_pair;    // [65536] rank of (x, y), x, y < 256, or RANK_NONE
-  const uint64_t* pair_tab;     // [pair_nb * PAIR_SLOTS]
+  const uint64_t* pair_tab;     // [2^(32 - pair_shift)] two-choice slots
   const CacheBucket* cache;     // [cache_nb]
   const uint32_t* tok_len;      // [2^ID_BITS] byte length of every token (0 past the vocabulary)
-  uint32_t pair_mask;           // pair_nb - 1
-  int pair_shift;               // 32 - log2(pair_nb)
-  int pair_probe;               // max buckets visited by any key
+  int pair_shift;               // 32 - log2(slots)
   uint32_t cache_mask;          // cache_nb - 1
   int cache_shift;              // 64 - log2(cache_nb)
   int cache_probe;              // max buckets visited by any lookup

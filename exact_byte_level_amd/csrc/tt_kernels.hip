@@ -754,59 +754,28 @@ __global__ __launch_bounds__(PT_THREADS) void k_pretok(const uint8_t* __restrict
 
 // Rank in a bucket's four slots of the key k20 = pair_key(x, y) << ID_BITS,
 // or RANK_NONE.
-__device__ __forceinline__ uint32_t bucket_match(const ulonglong2& e0, const ulonglong2& e1, uint64_t k20) {
-  constexpr uint64_t LOW = ~PAIR_MORE;
-  uint32_t r = RANK_NONE;
-  r = ((e0.x & LOW) ^ k20) < (1ull << ID_BITS) ? (uint32_t)e0.x & ID_MASK : r;
-  r = (e0.y ^ k20) < (1ull << ID_BITS) ? (uint32_t)e0.y & ID_MASK : r;
-  r = (e1.x ^ k20) < (1ull << ID_BITS) ? (uint32_t)e1.x & ID_MASK : r;
-  r = (e1.y ^ k20) < (1ull << ID_BITS) ? (uint32_t)e1.y & ID_MASK : r;
-  return r;
-}
-
-__device__ __forceinline__ const ulonglong2* pair_bucket_ptr(const Tables& tb, uint32_t b) {
-  return reinterpret_cast<const ulonglong2*>(tb.pair_tab + (size_t)b * PAIR_SLOTS);
-}
-
-// Rank of merging the adjacent pair (x, y), or RANK_NONE.  Branch-free in
-// the common case: the byte-pair entry and the first bucket are loaded
-// together and the four slots compared with selects; further buckets only
-// while the bucket says a probe run went past it.
-__device__ __forceinline__ uint32_t pair_rank(const Tables& tb, uint32_t x, uint32_t y) {
-  const uint32_t bp = tb.byte_pair[((x & 255u) << 8) | (y & 255u)];
-  const uint64_t k20 = pair_key(x, y) << ID_BITS;
-  uint32_t b = pair_bucket(x, y, tb.pair_shift);
-  uint32_t r = RANK_NONE;
-  for (int i = 0; i < tb.pair_probe; ++i) {
-    const ulonglong2* q = pair_bucket_ptr(tb, b);
-    const ulonglong2 e0 = q[0], e1 = q[1];
-    r = bucket_match(e0, e1, k20);
-    if (r != RANK_NONE || !(e0.x & PAIR_MORE)) break;
-    b = (b + 1) & tb.pair_mask;
-  }
-  return (x | y) < 256u ? bp : r;
-}
-
-// Rank of a pair with an operand >= 256 (every pair next to a new token):
-// no byte-pair table, 24-bit products for the hash (exact: ids < 2^20), the
-// first bucket without a loop.
+// Rank of a pair with an operand >= 256 (every pair next to a new token),
+// or RANK_NONE: its two slots loaded together, 24-bit products for the hash
+// (exact: ids < 2^20), 32-bit byte offsets from the table base.
 __device__ __forceinline__ uint32_t pair_rank_new(const Tables& tb, uint32_t x, uint32_t y) {
   uint32_t h = __umul24(x, 0x9E3779u) ^ __umul24(y, 0x7FEB35u);
   h ^= h >> 13;
   h *= 0x85EBCA6Bu;
-  uint32_t b = h >> tb.pair_shift;
+  const uint32_t s1 = h >> tb.pair_shift, s2 = pair_alt(h) >> tb.pair_shift;
+  const char* base = reinterpret_cast<const char*>(tb.pair_tab);
+  const uint64_t e1 = *reinterpret_cast<const uint64_t*>(base + (s1 << 3));
+  const uint64_t e2 = *reinterpret_cast<const uint64_t*>(base + (s2 << 3));
   const uint64_t k20 = pair_key(x, y) << ID_BITS;
-  const ulonglong2* q = pair_bucket_ptr(tb, b);
-  ulonglong2 e0 = q[0], e1 = q[1];
-  uint32_t r = bucket_match(e0, e1, k20);
-  for (int i = 1; r == RANK_NONE && (e0.x & PAIR_MORE) && i < tb.pair_probe; ++i) {
-    b = (b + 1) & tb.pair_mask;
-    q = pair_bucket_ptr(tb, b);
-    e0 = q[0];
-    e1 = q[1];
-    r = bucket_match(e0, e1, k20);
-  }
-  return r;
+  uint32_t r = (e1 ^ k20) < (1ull << ID_BITS) ? (uint32_t)e1 & ID_MASK : RANK_NONE;
+  return (e2 ^ k20) < (1ull << ID_BITS) ? (uint32_t)e2 & ID_MASK : r;
+}
+
+// Rank of merging the adjacent pair (x, y), or RANK_NONE: the byte-pair
+// table for two bytes, else the two-choice table (both loaded together).
+__device__ __forceinline__ uint32_t pair_rank(const Tables& tb, uint32_t x, uint32_t y) {
+  const uint32_t bp = tb.byte_pair[((x & 255u) << 8) | (y & 255u)];
+  const uint32_t r = pair_rank_new(tb, x, y);
+  return (x | y) < 256u ? bp : r;
 }
 
 // Id of the single-token piece with these bytes (len 2..16), or RANK_NONE.
@@ -844,7 +813,10 @@ __device__ __forceinline__ uint32_t dpp(uint32_t x) {
   return (uint32_t)__builtin_amdgcn_update_dpp((int)x, (int)x, CTRL, 0xF, 0xF, false);
 }
 
-__device__ __forceinline__ uint32_t lane_up1(uint32_t x) { return dpp<0x130>(x); }
+// Value of the next lane (wave_shl:1); the last lane reads 0.
+__device__ __forceinline__ uint32_t lane_up1(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x130, 0xF, 0xF, true);
+}
 
 // Minimum over each aligned group of G lanes (G = 8, 16, 32, 64): butterflies
 // inside a 16-lane row by DPP (folded into the min instructions), then across
@@ -854,9 +826,11 @@ template <int CTRL>
 __device__ __forceinline__ uint32_t dpp_all(uint32_t x) {
   return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, CTRL, 0xF, 0xF, true);
 }
+// x from another row into the rows of ROWS; the other rows read the identity
+// of min, so min(x, dpp_rows(x)) folds into one DPP min.
 template <int CTRL, int ROWS>
-__device__ __forceinline__ uint32_t dpp_rows(uint32_t old, uint32_t x) {
-  return (uint32_t)__builtin_amdgcn_update_dpp((int)old, (int)x, CTRL, ROWS, 0xF, false);
+__device__ __forceinline__ uint32_t dpp_rows(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_update_dpp((int)0xFFFFFFFFu, (int)x, CTRL, ROWS, 0xF, false);
 }
 template <int G>
 __device__ __forceinline__ uint32_t group_min(uint32_t x) {
@@ -865,13 +839,13 @@ __device__ __forceinline__ uint32_t group_min(uint32_t x) {
   x = min(x, dpp_all<0x141>(x));
   if (G >= 16) x = min(x, dpp_all<0x140>(x));
   if (G == 32) {
-    x = min(x, dpp_rows<0x142, 0xA>(x, x));  // rows 1, 3 += rows 0, 2
+    x = min(x, dpp_rows<0x142, 0xA>(x));  // rows 1, 3 += rows 0, 2
     const uint32_t r0 = (uint32_t)__builtin_amdgcn_readlane((int)x, 31);
     const uint32_t r1 = (uint32_t)__builtin_amdgcn_readlane((int)x, 63);
     x = ((threadIdx.x & 63u) < 32u) ? r0 : r1;
   } else if (G == 64) {
-    x = min(x, dpp_rows<0x142, 0xA>(x, x));
-    x = min(x, dpp_rows<0x143, 0xC>(x, x));  // rows 2, 3 += row 1
+    x = min(x, dpp_rows<0x142, 0xA>(x));
+    x = min(x, dpp_rows<0x143, 0xC>(x));  // rows 2, 3 += row 1
     x = (uint32_t)__builtin_amdgcn_readlane((int)x, 63);
   }
   return x;
