@@ -840,9 +840,7 @@ __device__ __forceinline__ uint32_t group_min(uint32_t x) {
   if (G >= 16) x = min(x, dpp_all<0x140>(x));
   if (G == 32) {
     x = min(x, dpp_rows<0x142, 0xA>(x));  // rows 1, 3 += rows 0, 2
-    const uint32_t r0 = (uint32_t)__builtin_amdgcn_readlane((int)x, 31);
-    const uint32_t r1 = (uint32_t)__builtin_amdgcn_readlane((int)x, 63);
-    x = ((threadIdx.x & 63u) < 32u) ? r0 : r1;
+    x = (uint32_t)__builtin_amdgcn_ds_swizzle((int)x, 0x3E0);  // every lane reads lane 31 of its half
   } else if (G == 64) {
     x = min(x, dpp_rows<0x142, 0xA>(x));
     x = min(x, dpp_rows<0x143, 0xC>(x));  // rows 2, 3 += row 1
@@ -876,15 +874,17 @@ __device__ void group_bpe(const uint8_t* __restrict__ bytes, const Work& w, cons
   }
   uint32_t id = (g < m) ? (uint32_t)bytes[s + g] : 0u;
   const uint32_t nx = lane_up1(id);
+  // rk is RANK_NONE wherever no pair starts (g + 1 >= m), so the key of such
+  // a lane, (RANK_NONE << 6) | g, lies above every real key (< 2^26)
   uint32_t rk = (g + 1 < m) ? tb.byte_pair[(id << 8) | (nx & 255u)] : RANK_NONE;
   for (;;) {
-    const uint32_t key = (g + 1 < m && rk != RANK_NONE) ? ((rk << 6) | (uint32_t)g) : 0xFFFFFFFFu;
-    const uint32_t kmin = group_min<G>(key);
-    const bool act = kmin != 0xFFFFFFFFu;
+    const uint32_t kmin = group_min<G>((rk << 6) | (uint32_t)g);
+    const bool act = kmin < (1u << 26);
     if (__ballot(act) == 0ull) break;
     const int bk = (int)(kmin & 63u);
     const uint32_t nid = 256u + (kmin >> 6);
-    const uint32_t id1 = lane_up1(id), id2 = lane_up1(id1), rk1 = lane_up1(rk);
+    const uint32_t id1 = lane_up1(id), id2 = lane_up1(id1), rs = lane_up1(rk);
+    const uint32_t rk1 = g == G - 1 ? RANK_NONE : rs;  // nothing enters from the next group
     const bool do_l = act && g == bk - 1;
     const bool do_r = act && g == bk && bk + 2 < m;
     uint32_t r = RANK_NONE;
