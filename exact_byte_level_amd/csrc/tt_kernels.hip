@@ -604,6 +604,78 @@ __device__ __forceinline__ bool pred_gpt2(const uint16_t* c, const uint8_t* pl, 
   return true;
 }
 
+// GPT-2-style start bits of a pure-ASCII tile, evaluated on 64-position masks
+// instead of position by position, straight from the staged bytes (no decode
+// pass: every byte is a char and its class comes from the ASCII table).  A
+// wavefront covers its 256 tile positions in windows of 64 lanes: lane i of
+// a window reads position P - 4 + i, so each mask holds the 4 positions
+// before the window's own 56 (bits 4..59) and 4 after -- the whole reach of
+// the rules (a contraction looks at most 4 chars back, the whitespace rule 1
+// char ahead).  Class tests become ballots and the rules 64-bit scalar
+// operations (X << 1 is "the char before", X >> 1 "the char after").  PLAIN:
+// the span holds no text edge and no sequence boundary, so every position is
+// a char and none starts or ends a sequence.  Returns the 4 start bits of
+// this thread's positions and sets *cnt to the wavefront's start count.
+template <bool PLAIN>
+__device__ __forceinline__ uint32_t gpt2_ascii_bits(const TileSmem& sm, int64_t n, int64_t t0, uint32_t* cnt) {
+  const int lane = (int)(threadIdx.x & 63u);
+  const int wbase = HALO + 256 * (int)(threadIdx.x >> 6);  // the wave's first tile position
+  const uint8_t* raw = reinterpret_cast<const uint8_t*>(sm.raw);
+  uint32_t mine = 0, total = 0;
+#pragma unroll
+  for (int q = 0; q < 5; ++q) {  // 5 windows of 56 cover 256 positions
+    const int P = wbase + 56 * q;
+    const int j = P - 4 + lane;  // < 16 * RAW_WORDS
+    uint32_t c = sm.ascii[raw[j] & 127u];
+    uint64_t CH = ~0ull, SS = 0ull, SL = 0ull;
+    if (!PLAIN) {
+      const int64_t p = t0 - HALO + j;
+      const bool in = p >= 0 && p < n;
+      if (!in) c = C_OUT;
+      CH = __ballot(in);
+      SS = __ballot(in && bmap_bit(sm.bmap, j));
+      SL = __ballot(in && (p + 1 >= n || bmap_bit(sm.bmap, j + 1)));
+    }
+    const uint32_t k = cls_of(c), lt = (c >> K_LETTER_SHIFT) & 15u;
+    const uint64_t W = __ballot(k == C_WS || k == C_WN);
+    const uint64_t L = __ballot(k == C_L);
+    const uint64_t N = __ballot(k == C_N);
+    const uint64_t O = __ballot(k == C_O);
+    const uint64_t SP = __ballot((c & K_SP) != 0u);
+    const uint64_t AP = __ballot((c & K_AP) != 0u);
+    uint64_t CLEN = 0ull, AFTER = 0ull;
+    if (AP) {
+      const bool low = k == C_L && !(c & K_UPPER);
+      const uint64_t C1 = __ballot(low && (lt == LT_S || lt == LT_T || lt == LT_M || lt == LT_D));
+      const uint64_t CRV = __ballot(low && (lt == LT_R || lt == LT_V));
+      const uint64_t CL = __ballot(low && lt == LT_L);
+      const uint64_t CE = __ballot(low && lt == LT_E);
+      // an apostrophe starts a piece: sequence start, or the char before it
+      // is neither "other" nor a space
+      const uint64_t APS = AP & (SS | ~((O | SP) << 1));
+      // contraction suffix of 1 or 2 lower-case letters starting here
+      const uint64_t PRE = ~SS & (APS << 1);
+      const uint64_t CLEN1 = PRE & C1;
+      const uint64_t CLEN2 = PRE & ~SL & ((CRV & (CE >> 1)) | (CL & (CL >> 1)));
+      CLEN = CLEN1 | CLEN2;
+      // first letter after a contraction suffix
+      AFTER = ~SS & ((CLEN1 << 1) | ((~SS & (CLEN2 << 1)) << 1));
+    }
+    const uint64_t SAME = (L & (L << 1)) | (N & (N << 1)) | (O & (O << 1)) | (W & (W << 1));
+    const uint64_t WB = W & (~(W << 1) | (~SL & ~(W >> 1)));
+    const uint64_t NB = ~W & ((SAME & L & AFTER) | (~SAME & ~(SP << 1) & ~(L & CLEN)));
+    uint64_t B = CH & (SS | WB | NB);
+    // own positions: bits 4..59 that are this wavefront's tile positions
+    const int own = min(56, min(wbase + 256, HALO + TILE) - P);
+    B = own > 0 ? (B >> 4) & ((1ull << own) - 1ull) : 0ull;
+    total += (uint32_t)__popcll(B);
+    const int rel = 4 * lane - 56 * q;  // this thread's first position in the window
+    if (rel >= 0 && rel < 56) mine = (uint32_t)(B >> rel) & 15u;
+  }
+  *cnt = total;
+  return mine;
+}
+
 // fwd_prev: forward run state at the previous char; fwd_here: at this char;
 // ends_run: the whitespace run through this char is followed by no CR/LF.
 template <bool ASCII>
@@ -683,8 +755,9 @@ __global__ __launch_bounds__(PT_THREADS) void k_pretok(const uint8_t* __restrict
     if (threadIdx.x < CTR_RESET_END) w.ctr[threadIdx.x] = 0u;
     for (int i = threadIdx.x; i < QGROUPS * QCTR_STRIDE; i += PT_THREADS) w.qctr[i] = 0u;
   }
-  bool na;
-  const bool bad = load_tile(bytes, n, offs, nseq, t0, sm, &na);
+  const bool na = stage_tile(bytes, n, offs, nseq, t0, sm);
+  // pure-ASCII tiles under GPT-2-style rules need no decode pass
+  const bool bad = (PAT == 0 && !na) ? false : decode_span(n, t0, na, sm);
   bool bad_off = false;
   if (offs) {
     for (int64_t q = (int64_t)t * PT_THREADS + threadIdx.x; q <= nseq; q += (int64_t)ntiles * PT_THREADS) {
@@ -694,18 +767,22 @@ __global__ __launch_bounds__(PT_THREADS) void k_pretok(const uint8_t* __restrict
   }
   const int j0 = HALO + PT_CHUNK * threadIdx.x;
   uint32_t bits = 0;
+  uint32_t cnt;
+  bool counted = false;
   if (PAT == 0) {
-    if (na) {
+    if (!na) {
+      uint32_t wc;
+      const bool plain = t0 - HALO >= 0 && t0 - HALO + 16 * RAW_WORDS <= n && (!offs || sm.seq_lo == sm.seq_hi);
+      bits = plain ? gpt2_ascii_bits<true>(sm, n, t0, &wc) : gpt2_ascii_bits<false>(sm, n, t0, &wc);
+      if ((threadIdx.x & 63u) == 0) sm.red[threadIdx.x >> 6] = wc;
+      __syncthreads();
+      cnt = sm.red[0] + sm.red[1] + sm.red[2] + sm.red[3];
+      counted = true;
+    } else if (na) {
 #pragma unroll
       for (int k = 0; k < PT_CHUNK; ++k) {
         uint32_t c = sm.code[cix(j0 + k)];
         if (is_char(c) && pred_gpt2<false>(sm.code, sm.plen, j0 + k)) bits |= 1u << k;
-      }
-    } else {
-#pragma unroll
-      for (int k = 0; k < PT_CHUNK; ++k) {
-        uint32_t c = sm.code[cix(j0 + k)];
-        if (is_char(c) && pred_gpt2<true>(sm.code, sm.plen, j0 + k)) bits |= 1u << k;
       }
     }
   } else {
@@ -745,7 +822,7 @@ __global__ __launch_bounds__(PT_THREADS) void k_pretok(const uint8_t* __restrict
     }
   }
   w.flags[(int64_t)t * PT_THREADS + threadIdx.x] = (uint16_t)bits;
-  const uint32_t cnt = block_sum(__popc(bits), sm.red);
+  if (!counted) cnt = block_sum(__popc(bits), sm.red);
   const uint32_t err = (__syncthreads_or(bad) ? ERR_UTF8 : 0u) | (__syncthreads_or(bad_off) ? ERR_OFFSETS : 0u);
   if (threadIdx.x == 0) w.tile_cnt[t] = cnt | (err << TILE_ERR_SHIFT);
 }
