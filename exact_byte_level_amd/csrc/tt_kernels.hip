@@ -224,6 +224,7 @@ __device__ bool stage_tile(const uint8_t* __restrict__ bytes, int64_t n, const i
     int64_t j = -base;
     if (j < (int64_t)BMAP_WORDS * 32) sm.bmap[j >> 5] |= 1u << (j & 31);
   }
+  __syncthreads();  // the bitmap is complete before any wavefront reads it
   return na;
 }
 
