@@ -32,7 +32,6 @@ namespace tt {
 
 // ------------------------------------------------------------ Unicode classes
 
-// (sizes rounded up to 16 bytes so that workgroups stage them with 16-byte loads)
 constexpr int UNI_L1_PAD = (TT_UNI_L1_SIZE + 15) / 16 * 16;
 constexpr int UNI_L2_PAD = (TT_UNI_NBLOCKS * 64 + 15) / 16 * 16;
 alignas(16) __device__ const uint8_t g_uni_l1[UNI_L1_PAD] = {TT_UNI_L1_DATA};
@@ -93,8 +92,6 @@ struct TileSmem {
   uint16_t code[CODE_SLOTS];
   alignas(16) uint16_t ascii[128];
   uint32_t bmap[BMAP_WORDS];
-  alignas(16) uint8_t l1[UNI_L1_PAD];
-  alignas(16) uint8_t l2[UNI_L2_PAD];
   uint32_t red[8];
   int64_t seq_lo, seq_hi;
   uint32_t carry_fwd, carry_bwd;
@@ -123,8 +120,7 @@ __device__ __forceinline__ int64_t lower_bound_i64(const int64_t* a, int64_t cnt
 // the raw bytes staged in LDS.  Validates UTF-8 as strict decoding does: no
 // overlong forms, no surrogates, nothing above U+10FFFF, no truncated or stray
 // continuation bytes, and no char crossing a sequence boundary.
-__device__ __forceinline__ uint16_t decode_at(int64_t n, int64_t base, int j, const TileSmem& sm,
-                                              bool table_in_lds) {
+__device__ __forceinline__ uint16_t decode_at(int64_t n, int64_t base, int j, const TileSmem& sm){
   const uint8_t* raw = reinterpret_cast<const uint8_t*>(sm.raw);
   int64_t p = base + j;
   if (p < 0 || p >= n) return (uint16_t)C_OUT;
@@ -158,9 +154,9 @@ __device__ __forceinline__ uint16_t decode_at(int64_t n, int64_t base, int j, co
     } else {
       uint32_t hi = cp >> 8, u = 0;
       if (hi < (uint32_t)TT_UNI_L1_SIZE) {
-        uint32_t blk = table_in_lds ? sm.l1[hi] : g_uni_l1[hi];
+        uint32_t blk = g_uni_l1[hi];
         uint32_t idx = blk * 64u + ((cp & 255u) >> 2);
-        uint32_t byte = table_in_lds ? sm.l2[idx] : g_uni_l2[idx];
+        uint32_t byte = g_uni_l2[idx];
         u = (byte >> ((cp & 3u) * 2u)) & 3u;
       }
       code = u == 1u ? C_L : u == 2u ? C_N : u == 3u ? C_WS : C_O;
@@ -228,18 +224,12 @@ __device__ bool stage_tile(const uint8_t* __restrict__ bytes, int64_t n, const i
   return na;
 }
 
-// Codes of all SPAN positions (the Unicode table staged in LDS first if some
-// byte is non-ASCII), and for non-ASCII tiles the predecessor lengths.
+// Codes of all SPAN positions (class tables of non-ASCII chars read from
+// global memory, where they stay cached), and for non-ASCII tiles the
+// predecessor lengths.
 // Returns true if some char starting inside the tile is invalid UTF-8.
 __device__ bool decode_span(int64_t n, int64_t t0, bool na, TileSmem& sm) {
   const int tid = threadIdx.x;
-  if (na) {
-    for (int i = tid; i < UNI_L1_PAD / 16; i += PT_THREADS)
-      reinterpret_cast<uint4*>(sm.l1)[i] = reinterpret_cast<const uint4*>(g_uni_l1)[i];
-    for (int i = tid; i < UNI_L2_PAD / 16; i += PT_THREADS)
-      reinterpret_cast<uint4*>(sm.l2)[i] = reinterpret_cast<const uint4*>(g_uni_l2)[i];
-  }
-  __syncthreads();
   bool bad = false;
   if (!na) {
     // every byte is a one-byte char: class from the ASCII table, sequence
@@ -260,7 +250,7 @@ __device__ bool decode_span(int64_t n, int64_t t0, bool na, TileSmem& sm) {
     return false;
   }
   for (int j = tid; j < SPAN; j += PT_THREADS) {
-    uint16_t c = decode_at(n, t0 - HALO, j, sm, na);
+    uint16_t c = decode_at(n, t0 - HALO, j, sm);
     sm.code[cix(j)] = c;
     if ((c & K_BAD) && j >= HALO && j < HALO + TILE) bad = true;
     if (is_char(c)) sm.plen[j + clen(c)] = (uint8_t)clen(c);
@@ -461,7 +451,7 @@ __global__ __launch_bounds__(PT_THREADS) void k_tile_summary(const uint8_t* __re
   // Unicode table is read from global memory for these few chars).
   if (wid < 2) {
     const int j = HALO + (wid == 0 ? lane : TILE - EDGE + lane);
-    const uint16_t c = decode_at(n, t0 - HALO, j, sm, false);
+    const uint16_t c = decode_at(n, t0 - HALO, j, sm);
     uint32_t v;
     if (wid == 0) {
       v = wave_incl_bwd<BwdOp>(is_char(c) ? BwdOp::elem(c) : BwdOp::IDENT, lane);
