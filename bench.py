@@ -30,6 +30,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "exact BPE encode throughput: chars/s and ms per 1M chars; % of HBM peak"
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
+VALU_CLOCK_GHZ = 2.4    # MI355X peak engine clock
 
 
 def _sha(a):
@@ -222,6 +223,17 @@ def run_workload(name, steps, warmup, graph=True, cpu=True, traffic=None):
     if (traffic and traffic.get("workload") == name and traffic.get("kernel") == dom
             and traffic.get("kernel_source_sha256") == src_sha):
         roof["traffic"] = traffic.get("bytes")
+    # what actually bounds the merge pass: VALU issue, from SQ_INSTS_VALU of a
+    # rocprofv3 counter pass on the same kernels (a wave64 VALU instruction
+    # holds a 16-lane SIMD for 4 cycles; 1024 SIMDs; the chip's 2.4 GHz peak
+    # clock, so the fraction is a lower bound when the clock runs below it)
+    sq_path = os.path.join(ROOT, "profiles", "sq.json")
+    if os.path.exists(sq_path) and "k_bpe_merge" in kern:
+        with open(sq_path) as f:
+            sq = json.load(f)
+        vi = sq.get("valu_insts", {}).get("k_bpe_merge")
+        if sq.get("workload") == name and sq.get("kernel_source_sha256") == src_sha and vi:
+            roof["merge_valu_issue_frac"] = round(vi * 4 / 1024 / (VALU_CLOCK_GHZ * 1e9) / (kern["k_bpe_merge"] * 1e-3), 3)
 
     res = {
         "name": name,
