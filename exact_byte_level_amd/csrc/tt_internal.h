@@ -127,6 +127,11 @@ struct Work {
   int32_t* tok_off;      // [n + 1] token offset of each piece; [P] = T
   uint32_t* tile_tok;    // [ntiles] tokens of the pieces that start in each tile
   uint32_t* tile_pbase;  // [ntiles] index of the first piece that starts in each tile
+  // Hand-over of a piece longer than BIG_BYTES between the tiles it covers,
+  // at the index of the tile holding its last byte (no two such pieces share
+  // one): the least pair rank of the piece and the arrival counter.
+  uint32_t* big_min;     // [ntiles]
+  int32_t* big_ctr;      // [ntiles]
   int32_t* long_list;    // [n / (LANE_CAP + 1) + 1] pieces of LANE_CAP + 1 .. BIG_BYTES bytes
   int32_t* huge_list;    // [n / (HUGE_TOKENS + 1) + 1] pieces with more than HUGE_TOKENS tokens
   // Pieces for group BPE by class c (<= 8, 16, 32, 64 bytes).  Tile t

@@ -11,7 +11,8 @@
 //         class in k_compact; group merges of up to 64-byte pieces, one byte
 //         position per lane, and exact global-minimum rounds for longer
 //         pieces, a wavefront each (k_bpe_merge) or, past 2 KiB, a workgroup
-//         each (big_bpe, run by the tile where the piece starts);
+//         each (big_merge, after every tile the piece covers has taken its
+//         share of the first round: big_share);
 //   §4.3  no host synchronisation between kernels: every size a kernel needs
 //         after the first is read on the device (grids are sized for the
 //         worst case and exit early), so the chain is graph-capturable.
@@ -815,7 +816,12 @@ __global__ __launch_bounds__(PT_THREADS) void k_pretok(const uint8_t* __restrict
   w.flags[(int64_t)t * PT_THREADS + threadIdx.x] = (uint16_t)bits;
   if (!counted) cnt = block_sum(__popc(bits), sm.red);
   const uint32_t err = (__syncthreads_or(bad) ? ERR_UTF8 : 0u) | (__syncthreads_or(bad_off) ? ERR_OFFSETS : 0u);
-  if (threadIdx.x == 0) w.tile_cnt[t] = cnt | (err << TILE_ERR_SHIFT);
+  if (threadIdx.x == 0) {
+    w.tile_cnt[t] = cnt | (err << TILE_ERR_SHIFT);
+    // reset for the long-piece hand-over of the next pass
+    w.big_min[t] = RANK_NONE;
+    w.big_ctr[t] = 0;
+  }
 }
 
 // ----------------------------------------------------------------------- BPE
@@ -1102,62 +1108,62 @@ __device__ __forceinline__ uint32_t block_min(uint32_t x, uint32_t* red) {
 
 constexpr int BIG_E = 8;                           // positions per thread and sweep step
 constexpr int BIG_STEP = 256 * BIG_E;              // positions per sweep step of the workgroup
+constexpr int SHARE_TILES = 9;  // tiles per share of a long piece's first round (prime to the 8 XCDs that
+                                // workgroups are dealt to in turn, so that shares spread over all of them)
 constexpr int BIG_LDS = BIG_STEP + 2 + (BIG_STEP + 2) / 32 + 1;  // skewed slots per staged array
 __device__ __forceinline__ int big_slot(int i) { return i + (i >> 5); }  // spreads BIG_E-strided reads over the banks
 
-// LDS of big_bpe: the staged ids and ranks of one sweep step plus scan space.
+// LDS of big_rounds: the staged ids and ranks of one sweep step plus scan space.
 struct BigSmem {
   uint32_t id[BIG_LDS];
   uint32_t rk[BIG_LDS];
   uint32_t sh[16];
 };
 
-// Piece p = bytes [s, s + m), longer than BIG_BYTES, by one workgroup of 256
-// threads (s and m are the same in every thread): the
-// same exact global-minimum rounds as long_bpe.  A sweep step stages BIG_STEP
-// positions (and two more on the right) in LDS with coalesced loads; thread
-// t then takes the BIG_E contiguous positions t * BIG_E ... .  Inside a run of
-// equal pairs the merge starts alternate, so whether position k starts a
-// merge depends on the carry from k - 1: each thread evaluates its positions
-// for both carries and a block scan of the resulting carry functions picks
-// the right one.  A block prefix sum of the surviving positions places the
-// compacted ids; all reads of a step finish (barrier) before its writes,
-// which land at or left of the positions read.
-__device__ int big_bpe(const uint8_t* __restrict__ bytes, const Work& w, const Tables& tb, uint32_t p,
-                       int32_t s, int m, BigSmem& sm) {
+// Word k of a uint32 array at base (uniform): 32-bit byte offsets let the
+// loads take the base from scalar registers.
+__device__ __forceinline__ uint32_t big_word(const uint32_t* base, uint32_t k) {
+  return *reinterpret_cast<const uint32_t*>(reinterpret_cast<const char*>(base) + k * 4u);
+}
+
+// Rounds 1, 2, ... of piece p = bytes [s, s + m), longer than BIG_BYTES, by
+// one workgroup of 256 threads (s, m and rmin, the least pair rank left by the
+// first round, are the same in every thread): the same exact global-minimum
+// rounds as long_bpe.  A sweep step's BIG_STEP positions (and two more on the
+// right) are staged in LDS with coalesced loads;
+// thread t then takes the BIG_E contiguous positions t * BIG_E ... .  Inside
+// a run of equal pairs the merge starts alternate, so whether position k
+// starts a merge depends on the carry from k - 1: each thread evaluates its
+// positions for both carries and a block scan of the resulting carry
+// functions picks the right one.  A block prefix sum of the surviving
+// positions places the compacted ids; a step writes only left of the next
+// step's positions, and all its LDS reads finish (barrier) before the next
+// step is staged.
+__device__ int big_rounds(const Work& w, const Tables& tb, uint32_t p, int32_t s, int m, uint32_t rmin,
+                          BigSmem& sm) {
   const int tid = (int)threadIdx.x, lane = tid & 63, wid = tid >> 6;
   uint32_t* I = reinterpret_cast<uint32_t*>(w.tmp_ids) + s;
   uint32_t* R = w.tmp_rank + s;
-  uint32_t rmin = RANK_NONE;
-  for (int base = 0; base < m; base += 256 * 8) {
-    uint32_t b0[8], b1[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int k = base + 256 * j + tid;
-      b0[j] = k < m ? bytes[s + k] : 0u;
-      b1[j] = k + 1 < m ? bytes[s + k + 1] : 0u;
-    }
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int k = base + 256 * j + tid;
-      if (k < m) {
-        const uint32_t r = k + 1 < m ? tb.byte_pair[(b0[j] << 8) | b1[j]] : RANK_NONE;
-        I[k] = b0[j];
-        R[k] = r;
-        rmin = min(rmin, r);
-      }
-    }
-  }
-  rmin = uniform(block_min(rmin, sm.sh + 8));
+  uint32_t lx = RANK_NONE, ly = RANK_NONE, lr = RANK_NONE;  // the last pair looked up and its rank
   while (rmin != RANK_NONE) {
     const uint32_t T = 256u + rmin;
     uint32_t cin = 0, nmin = RANK_NONE;
     int out = 0;
     for (int base = 0; base < m; base += BIG_STEP) {
-      for (int i = tid; i < BIG_STEP + 2; i += 256) {
-        const int k = base + i;
-        sm.id[big_slot(i)] = k < m ? I[k] : 0u;
-        sm.rk[big_slot(i)] = k + 1 < m ? R[k] : RANK_NONE;
+      uint32_t pid[BIG_E + 1], prk[BIG_E + 1];
+#pragma unroll
+      for (int j = 0; j <= BIG_E; ++j) {
+        const uint32_t k = (uint32_t)(base + tid + 256 * j);
+        const bool in = j < BIG_E || tid < 2;
+        pid[j] = in && (int)k < m ? big_word(I, k) : 0u;
+        prk[j] = in && (int)k + 1 < m ? big_word(R, k) : RANK_NONE;
+      }
+#pragma unroll
+      for (int j = 0; j <= BIG_E; ++j) {
+        if (j < BIG_E || tid < 2) {
+          sm.id[big_slot(tid + 256 * j)] = pid[j];
+          sm.rk[big_slot(tid + 256 * j)] = prk[j];
+        }
       }
       __syncthreads();
       const int j0 = tid * BIG_E, k0 = base + j0;
@@ -1210,7 +1216,17 @@ __device__ int big_bpe(const uint8_t* __restrict__ bytes, const Work& w, const T
         const bool has_next = m0 ? (k + 2 < m) : (k + 1 < m);
         const uint32_t nxt = m0 ? (m2 ? T : sm.id[big_slot(j0 + j + 2)]) : (m1 ? T : sm.id[big_slot(j0 + j + 1)]);
         uint32_t nr = RANK_NONE;
-        if (has_next) nr = (m0 || m1) ? pair_rank(tb, nid, nxt) : sm.rk[big_slot(j0 + j)];
+        if (has_next && (m0 || m1)) {
+          // (merged ids are never bytes; inside runs the same pair recurs)
+          if (nid != lx || nxt != ly) {
+            lx = nid;
+            ly = nxt;
+            lr = pair_rank_new(tb, nid, nxt);
+          }
+          nr = lr;
+        } else if (has_next) {
+          nr = sm.rk[big_slot(j0 + j)];
+        }
         I[o] = nid;
         R[o] = nr;
         ++o;
@@ -1230,6 +1246,129 @@ __device__ int big_bpe(const uint8_t* __restrict__ bytes, const Work& w, const T
   return m;
 }
 
+// The first round of a piece longer than BIG_BYTES on one share [a, b) of
+// it (the piece ends at e): every position holds its byte as id and the rank
+// of the byte pair it starts (none at the piece's last byte).  A thread takes
+// BIG_E contiguous positions per pass, its loads and lookups issued before
+// any is used.  Returns the least rank of the share, the same in every thread.
+__device__ uint32_t big_first_round(const uint8_t* __restrict__ bytes, const Work& w, const Tables& tb, int32_t a,
+                                    int32_t b, int32_t e, BigSmem& sm) {
+  uint32_t rmin = RANK_NONE;
+  for (int32_t k0 = a + BIG_E * (int32_t)threadIdx.x; k0 < b; k0 += BIG_E * PT_THREADS) {
+    uint32_t by[BIG_E + 1], r[BIG_E];
+#pragma unroll
+    for (int j = 0; j <= BIG_E; ++j) by[j] = k0 + j < e ? bytes[k0 + j] : 0u;
+#pragma unroll
+    for (int j = 0; j < BIG_E; ++j) r[j] = k0 + j + 1 < e ? tb.byte_pair[(by[j] << 8) | by[j + 1]] : RANK_NONE;
+#pragma unroll
+    for (int j = 0; j < BIG_E; ++j) {
+      if (k0 + j < b) {
+        w.tmp_ids[k0 + j] = (int32_t)by[j];
+        w.tmp_rank[k0 + j] = r[j];
+        rmin = min(rmin, r[j]);
+      }
+    }
+  }
+  return uniform(block_min(rmin, sm.sh + 8));
+}
+
+// A piece p = bytes [s, e) longer than BIG_BYTES spans several tiles.  In
+// each group of SHARE_TILES tiles it covers, the first of them takes the
+// first round on the group's share [a, b) (starting in tile t0 / TILE), so
+// that many workgroups write the piece's ids and ranks (groups rather than
+// single tiles, since each share ends in device-wide memory fences).  The tiles then meet at
+// the piece's counter without waiting for one another: each folds its least
+// rank into the piece's minimum and adds its share's length to the counter,
+// the tile holding s adding minus the piece's length on top.  Only the sum
+// over every share is zero, so the tile whose addition reads it has seen all
+// of them and merges the piece (big_merge, after the tile's other share, so
+// that a tile which merges one piece does not hold back the next one).
+// Returns that, the same in every thread.
+__device__ bool big_share(const uint8_t* __restrict__ bytes, const Work& w, const Tables& tb, int32_t s, int32_t e,
+                          int32_t a, int32_t b, int64_t t0, BigSmem& sm) {
+  const uint32_t rmin = big_first_round(bytes, w, tb, a, b, e, sm);
+  const int key = (e - 1) / TILE;
+  const int32_t delta = (b - a) - (s >= t0 ? e - s : 0);
+  __builtin_amdgcn_s_waitcnt(0);  // this wavefront's ids and ranks have reached the cache
+  __syncthreads();                // ... and every wavefront's
+  if (threadIdx.x == 0) {
+    atomicMin(&w.big_min[key], rmin);
+    __threadfence();  // the share and its minimum, device-wide, before the counter
+    const int32_t old = atomicAdd(&w.big_ctr[key], delta);
+    sm.sh[6] = old + delta == 0 ? 1u : 0u;
+  }
+  __syncthreads();
+  const bool last = uniform(sm.sh[6]) != 0u;
+  __syncthreads();  // sh[6] is read before a later share writes it
+  return last;
+}
+
+// The rounds of piece p = bytes [s, e) after big_share found every share of
+// its first round done; its token count goes to the tile where it starts.
+__device__ void big_merge(const Work& w, const Tables& tb, uint32_t p, int32_t s, int32_t e, BigSmem& sm) {
+  __threadfence();  // every share's ids and ranks, after the counter
+  const int key = (e - 1) / TILE;
+  const uint32_t r = uniform(__hip_atomic_load(&w.big_min[key], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+  const int cnt = big_rounds(w, tb, p, s, e - s, r, sm);
+  if (threadIdx.x == 0) atomicAdd(&w.tile_tok[s / TILE], (uint32_t)cnt);
+}
+
+// The last pre-token start before tile t (t >= 1; byte 0 always starts one),
+// from the tile counts and start bits; the same in every lane.
+__device__ int32_t last_start_before(const Work& w, int t, uint32_t cmask) {
+  const int lane = (int)(threadIdx.x & 63u);
+  for (int b = t - 1; b >= 0; b -= 64) {
+    const int bb = b - lane;
+    const uint64_t nz = __ballot(bb >= 0 && (w.tile_cnt[bb] & cmask) != 0u);
+    if (nz) {
+      const int f = b - (__ffsll((unsigned long long)nz) - 1);
+      for (int q = PT_THREADS - 64; q >= 0; q -= 64) {
+        const uint32_t fl = w.flags[(int64_t)f * PT_THREADS + q + lane];
+        const uint64_t fm = __ballot(fl != 0u);
+        if (fm) {
+          const int l = 63 - __clzll((long long)fm);
+          const uint32_t flw = (uint32_t)__shfl((int)fl, l);
+          return (int32_t)((int64_t)f * TILE + PT_CHUNK * (q + l) + 31 - __clz(flw));
+        }
+      }
+    }
+  }
+  return 0;
+}
+
+// The first pre-token start after tile t, else n; nc1 = the count of tile
+// t + 1 + lane and fl1 = the start bits of tile t + 1's thread lane, loaded
+// ahead.  Every wavefront runs the same search; the ballots keep it uniform.
+__device__ int32_t first_start_after(const Work& w, int t, int ntiles, int64_t n, uint32_t cmask, uint32_t nc1,
+                                     uint32_t fl1) {
+  const int lane = (int)(threadIdx.x & 63u);
+  // usually the next tile has a start in its first 256 bytes
+  const uint64_t nz1 = __ballot((nc1 & cmask) != 0u);
+  const uint64_t fm1 = __ballot(fl1 != 0u);
+  if ((nz1 & 1ull) && fm1) {
+    const int l = __ffsll((unsigned long long)fm1) - 1;
+    const uint32_t flw = (uint32_t)__shfl((int)fl1, l);
+    return (int32_t)((int64_t)(t + 1) * TILE + PT_CHUNK * l + __ffs(flw) - 1);
+  }
+  for (int b = t + 1; b < ntiles; b += 64) {
+    const int bb = b + lane;
+    const uint64_t nz = __ballot(bb < ntiles && (w.tile_cnt[bb] & cmask) != 0u);
+    if (nz) {
+      const int f = b + __ffsll((unsigned long long)nz) - 1;
+      for (int q = 0; q < PT_THREADS; q += 64) {
+        const uint32_t fl = w.flags[(int64_t)f * PT_THREADS + q + lane];
+        const uint64_t fm = __ballot(fl != 0u);
+        if (fm) {
+          const int l = __ffsll((unsigned long long)fm) - 1;
+          const uint32_t flw = (uint32_t)__shfl((int)fl, l);
+          return (int32_t)((int64_t)f * TILE + PT_CHUNK * (q + l) + __ffs(flw) - 1);
+        }
+      }
+    }
+  }
+  return (int32_t)n;
+}
+
 // Pass 3: piece starts in order, from the counts of the tiles before and a
 // block scan of the start bits.  The last tile adds the sentinel n and sets P
 // and the error bits; for a bare pre-tokenization it writes P (or the error
@@ -1240,17 +1379,25 @@ __device__ int big_bpe(const uint8_t* __restrict__ bytes, const Work& w, const T
 // k_bpe_merge, longer ones up to BIG_BYTES to the long list (one atomic per
 // class and round of 256 pieces reserves the slots).  The end of the tile's
 // last piece is the first start in a later tile, found from the tile counts
-// and start bits; if that piece is longer than BIG_BYTES (only the last one
-// can be), the tile's workgroup merges it (big_bpe).
+// and start bits.  A piece longer than BIG_BYTES (only the tile's last one
+// and the one its first bytes end can be) gets the tile's share of its first
+// round, and the last tile to take a share merges it (big_share, big_merge).
 template <bool CLASSIFY>
-__global__ __launch_bounds__(PT_THREADS) void k_compact(const uint8_t* __restrict__ bytes, Work w, Tables tb,
+__global__ __launch_bounds__(PT_THREADS) __attribute__((amdgpu_waves_per_eu(6))) void k_compact(const uint8_t* __restrict__ bytes, Work w, Tables tb,
                                                         int ntiles, int64_t n, int32_t* __restrict__ starts,
                                                         int64_t* __restrict__ out_np) {
+  // the piece starts and the staged bytes of the classification, and after
+  // it the LDS of big_rounds, in one place
+  constexpr size_t SST_BYTES = sizeof(int32_t) * (TILE + 4);
+  constexpr size_t CLS_BYTES = SST_BYTES + 16 * ((TILE + CACHE_MAXLEN) / 16);
+  constexpr size_t LDS_BYTES = CLS_BYTES > sizeof(BigSmem) ? CLS_BYTES : sizeof(BigSmem);
+  static_assert(SST_BYTES % 16 == 0, "staged bytes stay 16-byte aligned");
+  __shared__ __attribute__((aligned(16))) unsigned char lds[LDS_BYTES];
   __shared__ uint32_t red[8];
-  __shared__ int32_t sst[TILE + 1];
-  __shared__ uint4 stage[(TILE + CACHE_MAXLEN) / 16];
   __shared__ uint32_t qn[5], qbase[5];
-  __shared__ BigSmem big;
+  int32_t* sst = reinterpret_cast<int32_t*>(lds);                  // [TILE + 1]
+  uint4* stage = reinterpret_cast<uint4*>(lds + SST_BYTES);        // [(TILE + CACHE_MAXLEN) / 16]
+  BigSmem& big = *reinterpret_cast<BigSmem*>(lds);
   const int t = blockIdx.x;
   const int lane = (int)(threadIdx.x & 63u);
   const uint32_t cmask = (1u << TILE_ERR_SHIFT) - 1u;
@@ -1268,6 +1415,7 @@ __global__ __launch_bounds__(PT_THREADS) void k_compact(const uint8_t* __restric
   if (stage_fast) sv = *reinterpret_cast<const uint4*>(bytes + sg);
   const uint32_t nc1 = (CLASSIFY && t + 1 + lane < ntiles) ? w.tile_cnt[t + 1 + lane] : 0u;
   const uint32_t fl1 = (CLASSIFY && t + 1 < ntiles) ? w.flags[(int64_t)(t + 1) * PT_THREADS + lane] : 0u;
+  const uint32_t prev_cnt = (CLASSIFY && t > 0) ? w.tile_cnt[t - 1] : 1u;
   uint32_t hi;
   // the last tile also folds its own count and error bits into the totals
   const uint32_t base = block_reduce(w.tile_cnt, last ? t + 1 : t, cmask, red, &hi) -
@@ -1296,42 +1444,21 @@ __global__ __launch_bounds__(PT_THREADS) void k_compact(const uint8_t* __restric
   if (threadIdx.x == 0) w.tile_pbase[t] = base;
   if (!CLASSIFY) return;
   if (tot == 0) {
+    // the whole tile lies inside one piece: if it is longer than BIG_BYTES
+    // and this tile starts a group, take the group's share of its first round
     if (threadIdx.x == 0) w.tile_tok[t] = 0u;
+    if (t % SHARE_TILES == 0) {
+      const int32_t sp = last_start_before(w, t, cmask);
+      const int32_t ep = first_start_after(w, t, ntiles, n, cmask, nc1, fl1);
+      if (ep - sp > BIG_BYTES &&
+          big_share(bytes, w, tb, sp, ep, (int32_t)t0, (int32_t)min<int64_t>(ep, t0 + SHARE_TILES * TILE), t0, big))
+        big_merge(w, tb, base - 1, sp, ep, big);
+    }
     return;
   }
-  {
-    // end of the last piece: the first start after this tile, else n (every
-    // wavefront runs the same search; the ballots keep it wave-uniform)
-    int32_t e = (int32_t)n;
-    // usually the next tile has a start in its first 256 bytes
-    const uint64_t nz1 = __ballot((nc1 & cmask) != 0u);
-    const uint64_t fm1 = __ballot(fl1 != 0u);
-    const bool quick = (nz1 & 1ull) && fm1;
-    if (quick) {
-      const int l = __ffsll((unsigned long long)fm1) - 1;
-      const uint32_t flw = (uint32_t)__shfl((int)fl1, l);
-      e = (int32_t)((int64_t)(t + 1) * TILE + PT_CHUNK * l + __ffs(flw) - 1);
-    }
-    for (int b = t + 1; !quick && b < ntiles; b += 64) {
-      const int bb = b + lane;
-      const uint64_t nz = __ballot(bb < ntiles && (w.tile_cnt[bb] & cmask) != 0u);
-      if (nz) {
-        const int f = b + __ffsll((unsigned long long)nz) - 1;
-        for (int q = 0; q < PT_THREADS; q += 64) {
-          const uint32_t fl = w.flags[(int64_t)f * PT_THREADS + q + lane];
-          const uint64_t fm = __ballot(fl != 0u);
-          if (fm) {
-            const int l = __ffsll((unsigned long long)fm) - 1;
-            const uint32_t flw = (uint32_t)__shfl((int)fl, l);
-            e = (int32_t)((int64_t)f * TILE + PT_CHUNK * (q + l) + __ffs(flw) - 1);
-            break;
-          }
-        }
-        break;
-      }
-    }
-    if (threadIdx.x == 0) sst[tot] = e;
-  }
+  // end of the last piece: the first start after this tile, else n
+  const int32_t e_next = first_start_after(w, t, ntiles, n, cmask, nc1, fl1);
+  if (threadIdx.x == 0) sst[tot] = e_next;
   // the tile's bytes plus CACHE_MAXLEN, for single bytes and table keys
   if (threadIdx.x < (TILE + CACHE_MAXLEN) / 16) {
     if (!stage_fast) {
@@ -1401,16 +1528,28 @@ __global__ __launch_bounds__(PT_THREADS) void k_compact(const uint8_t* __restric
     if (threadIdx.x < 5) qn[threadIdx.x] = 0;
     __syncthreads();
   }
-  {
-    // (the piece's end comes from this tile's search: the tile holding the
-    // next start may not have written it yet)
-    const int32_t ls = (int32_t)uniform((uint32_t)sst[tot - 1]);
-    const int32_t lm = (int32_t)uniform((uint32_t)sst[tot]) - ls;
-    // tokens of the tile's finished pieces; merged pieces add theirs later
-    uint32_t tok = block_sum(fin, red);
-    if (lm > BIG_BYTES) tok += (uint32_t)big_bpe(bytes, w, tb, base + tot - 1, ls, lm, big);
-    if (threadIdx.x == 0) w.tile_tok[t] = tok;
+  // tokens of the tile's finished pieces; merged pieces add theirs later
+  const uint32_t tok = block_sum(fin, red);
+  if (threadIdx.x == 0) w.tile_tok[t] = tok;
+  // shares of pieces longer than BIG_BYTES: the bytes before the tile's first
+  // start end a piece that began before the tile (a share if the tile starts
+  // a group), which can be that long only if the tile before has no start;
+  // the tile's last piece can be too (its end comes from this tile's search:
+  // the tile holding the next start may not have written it yet)
+  const int32_t fs = (int32_t)uniform((uint32_t)sst[0]);
+  int32_t sp = 0;
+  bool head_last = false;
+  if (t % SHARE_TILES == 0 && t > 0 && fs > t0 && (prev_cnt & cmask) == 0u) {
+    sp = last_start_before(w, t, cmask);
+    if (fs - sp > BIG_BYTES) head_last = big_share(bytes, w, tb, sp, fs, (int32_t)t0, fs, t0, big);
   }
+  const int32_t ls = (int32_t)uniform((uint32_t)sst[tot - 1]);
+  const int32_t le = (int32_t)uniform((uint32_t)sst[tot]);
+  const int64_t gend = (int64_t)(t / SHARE_TILES + 1) * SHARE_TILES * TILE;
+  const bool tail_last =
+      le - ls > BIG_BYTES && big_share(bytes, w, tb, ls, le, ls, (int32_t)min<int64_t>(le, gend), t0, big);
+  if (head_last) big_merge(w, tb, base - 1, sp, fs, big);
+  if (tail_last) big_merge(w, tb, base + tot - 1, ls, le, big);
 }
 
 // Pass 5: BPE of the queued pieces.  Work items are wavefront loads: one long

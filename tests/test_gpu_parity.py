@@ -270,6 +270,59 @@ def test_pieces_over_two_kib_mixed_with_text():
         assert np.array_equal(got, want)
 
 
+# A piece longer than 2 KiB is set up by every group of 9 tiles (9 KiB) it
+# covers, each writing its share of the starting ids and pair ranks; the last
+# group to finish merges the piece.  These cases put long pieces' starts and
+# ends on and around tile and group edges, place long pieces next to each
+# other (so that one tile holds the end of one and the start of the next),
+# and run many merge rounds on one piece.
+GROUP = 9 * 1024
+
+
+def test_long_pieces_across_share_groups():
+    v = load("c3", CL100K)
+    cases = []
+    for pre in (0, 1, 1023, 1024, 1025, GROUP - 1, GROUP, GROUP + 1, 2 * GROUP - 2500):
+        for length in (2049, GROUP - 1, GROUP, GROUP + 1, 3 * GROUP + 5, 40_000):
+            head = (b"x" * (pre - 1) + b" ") if pre else b""
+            cases.append(head + b" " * length + b"y" + b"a" * (length // 3) + b"\n")
+    rng = random.Random(46)
+    parts = []
+    for i in range(10):
+        parts.append(rng.choice([b" ", b"a", b"-", b"7"]) * rng.randint(2049, 30_000))
+        if i % 3:
+            parts.append(code_text(rng.randint(1, 2000), 600 + i))
+    cases.append(b"".join(parts))
+    for k, data in enumerate(cases):
+        say("long pieces across share groups: case %d, %d bytes" % (k, len(data)))
+        got = gpu_encode(data)
+        want = np.asarray(oracle_encode(data, v, CL100K, {}), dtype=np.int32)
+        assert np.array_equal(got, want), k
+
+
+def test_long_random_piece_many_rounds():
+    # one 60,000-letter word: thousands of distinct merges, one round each
+    v = load("c2", GPT2)
+    rng = random.Random(47)
+    word = "".join(rng.choice("etaoinshrdlu") for _ in range(60_000)).encode()
+    for data in (word, b" " + word + b" " + word[:20_000]):
+        say("long random piece, %d bytes" % len(data))
+        assert gpu_encode(data).tolist() == oracle_encode(data, v, GPT2)
+
+
+def test_long_pieces_in_a_batch():
+    v = load("c3", CL100K)
+    texts = [b"a" * 2500, b"b" * 30_000, b"", b" " * 20_000 + b"x", code_text(3000, 48), b"c" * 2049,
+             b"d" * GROUP, b" " * (2 * GROUP) + b"\n"]
+    data = b"".join(texts)
+    offs = np.cumsum([0] + [len(t) for t in texts]).astype(np.int64)
+    say("batch of %d texts with long pieces, %d bytes" % (len(texts), len(data)))
+    ids, out_off = tt.encode_batch(dev(data), torch.tensor(offs, device="cuda"))
+    want, want_off = oracle_encode_batch(data, offs.tolist(), v, CL100K, {})
+    assert out_off.numpy().tolist() == want_off
+    assert np.array_equal(ids.cpu().numpy(), np.asarray(want, dtype=np.int32))
+
+
 def test_pipe_line_vocab_on_gpu():
     merges = np.asarray([(112, 105), (256, 112), (257, 101), (108, 105), (259, 110), (260, 101), (258, 261)],
                         dtype=np.int32)
