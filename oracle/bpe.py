@@ -20,6 +20,13 @@ Three implementations with the same semantics live here:
                  every left-to-right non-overlapping occurrence of merge r.  On
                  a consistent table (both operands of merge r have ids below
                  256 + r) it must agree with bpe_classic.
+
+The whole-word rule of the Llama family (same page, §4.2: with ignore_merges
+the whole pre-token is matched against the vocabulary first, and a match
+skips the merges) is the ``ignore_merges`` option of the encoders.  Reading:
+a piece whose bytes equal a vocabulary token becomes that one token; if
+several ids share those bytes, the smallest (the first to enter the
+vocabulary); any other piece goes through BPE as above.
 """
 import heapq
 
@@ -41,6 +48,17 @@ class Vocab:
         self.tok_bytes = [bytes([b]) for b in range(256)]
         for x, y in self.merges:
             self.tok_bytes.append(self.tok_bytes[x] + self.tok_bytes[y])
+        self._token_id = None
+
+    @property
+    def token_id(self):
+        """bytes -> the smallest id whose bytes they are (the vocabulary)."""
+        if self._token_id is None:
+            d = {}
+            for i, b in enumerate(self.tok_bytes):
+                d.setdefault(b, i)
+            self._token_id = d
+        return self._token_id
 
     @property
     def size(self):
@@ -131,38 +149,45 @@ def bpe_naive(ids, merges):
     return ids
 
 
-def bpe(piece, vocab):
-    """BPE of one pre-token (bytes).  Long pieces take the heap form."""
+def bpe(piece, vocab, ignore_merges=False):
+    """BPE of one pre-token (bytes).  Long pieces take the heap form.  With
+    ignore_merges, a piece that is a vocabulary token is that token."""
+    if ignore_merges:
+        t = vocab.token_id.get(bytes(piece))
+        if t is not None:
+            return [t]
     if len(piece) > 64:
         return bpe_heap(piece, vocab.rank)
     return bpe_classic(piece, vocab.rank)
 
 
-def encode(data, vocab, pattern_id, memo=None):
+def encode(data, vocab, pattern_id, memo=None, ignore_merges=False):
     """Token ids of UTF-8 ``data``: concatenation of the BPE of every piece.
 
     ``memo`` (optional dict) caches piece -> ids; BPE is a pure function of the
-    piece, so the memo never changes the result.
+    piece, so the memo never changes the result (the two modes use different
+    keys, so one memo may serve both).
     """
     pieces, _ = split_bytes(data, pattern_id)
     out = []
     for p in pieces:
         if memo is not None:
-            r = memo.get(p)
+            key = (1, p) if ignore_merges else p
+            r = memo.get(key)
             if r is None:
-                r = bpe(p, vocab)
-                memo[p] = r
+                r = bpe(p, vocab, ignore_merges)
+                memo[key] = r
             out.extend(r)
         else:
-            out.extend(bpe(p, vocab))
+            out.extend(bpe(p, vocab, ignore_merges))
     return out
 
 
-def encode_batch(data, offsets, vocab, pattern_id, memo=None):
+def encode_batch(data, offsets, vocab, pattern_id, memo=None, ignore_merges=False):
     """Per-sequence encode of a concatenated batch; returns (ids, out_offsets)."""
     ids, out_off = [], [0]
     for s in range(len(offsets) - 1):
-        ids.extend(encode(data[offsets[s]:offsets[s + 1]], vocab, pattern_id, memo))
+        ids.extend(encode(data[offsets[s]:offsets[s + 1]], vocab, pattern_id, memo, ignore_merges))
         out_off.append(len(ids))
     return ids, out_off
 
@@ -186,7 +211,7 @@ def token_starts(ids, vocab, base=0):
     return starts
 
 
-def encode_offsets(data, offsets, vocab, pattern_id, memo=None):
+def encode_offsets(data, offsets, vocab, pattern_id, memo=None, ignore_merges=False):
     """Ids and token starts of a text (offsets None) or a concatenated batch.
 
     Returns (ids, starts, counts).  Starts are offsets into the whole buffer
@@ -194,9 +219,9 @@ def encode_offsets(data, offsets, vocab, pattern_id, memo=None):
     counts is [T] for one text, else the per-text id offsets [B + 1].
     """
     if offsets is None:
-        ids = encode(data, vocab, pattern_id, memo)
+        ids = encode(data, vocab, pattern_id, memo, ignore_merges)
         return ids, token_starts(ids, vocab), [len(ids)]
-    ids, counts = encode_batch(data, offsets, vocab, pattern_id, memo)
+    ids, counts = encode_batch(data, offsets, vocab, pattern_id, memo, ignore_merges)
     starts = []
     for s in range(len(offsets) - 1):
         starts.extend(token_starts(ids[counts[s]:counts[s + 1]], vocab, offsets[s])[:-1])

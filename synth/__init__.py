@@ -14,3 +14,4 @@ from .text import (  # noqa: F401
     workload,
     WORKLOADS,
 )
+from .vocab import extend_merges, word_text  # noqa: F401
