@@ -49,6 +49,7 @@ def lib():
         L = ctypes.CDLL(LIB_PATH)
         vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32
         L.tt_load_bpe.argtypes = [vp, vp, i64, i32]
+        L.tt_load_bpe_ex.argtypes = [vp, vp, i64, i32, ctypes.c_uint32]
         L.tt_reserve.argtypes = [i64, i32]
         L.tt_encode.argtypes = [vp, i64, vp, vp, vp]
         L.tt_encode_batch.argtypes = [vp, i64, vp, i32, vp, vp, vp]
@@ -67,7 +68,7 @@ def lib():
         L.tt_free.restype = None
         L.tt_strerror.argtypes = [ctypes.c_int]
         L.tt_strerror.restype = ctypes.c_char_p
-        for f in ("tt_load_bpe", "tt_reserve", "tt_encode", "tt_encode_batch", "tt_pretokenize", "tt_encode_offsets",
+        for f in ("tt_load_bpe", "tt_load_bpe_ex", "tt_reserve", "tt_encode", "tt_encode_batch", "tt_pretokenize", "tt_encode_offsets",
                   "tt_session_create", "tt_session_destroy", "tt_session_reset", "tt_session_append",
                   "tt_session_view", "tt_session_read", "tt_char_class", "tt_profile", "tt_profile_read"):
             getattr(L, f).restype = ctypes.c_int
@@ -90,16 +91,20 @@ def _stream(stream):
     return ctypes.c_void_p(s.cuda_stream)
 
 
-def load(merges, ranks=None, pattern_id=PATTERN_GPT2):
+LOAD_IGNORE_MERGES = 1
+
+
+def load(merges, ranks=None, pattern_id=PATTERN_GPT2, ignore_merges=False):
     """Load a merge table: merges int32 [M, 2]; merge k makes id 256 + ranks[k]
-    (ranks defaults to 0..M-1, i.e. rows in rank order)."""
+    (ranks defaults to 0..M-1, i.e. rows in rank order).  ignore_merges turns
+    on the whole-word rule: a piece that is a vocabulary token becomes it."""
     m = np.ascontiguousarray(np.asarray(merges, dtype=np.int32).reshape(-1, 2))
     r = None if ranks is None else np.ascontiguousarray(np.asarray(ranks, dtype=np.int32).reshape(-1))
     if r is not None and len(r) != len(m):
         raise ValueError("ranks must have one entry per merge")
-    rc = lib().tt_load_bpe(m.ctypes.data if len(m) else None, None if r is None else r.ctypes.data,
-                           len(m), int(pattern_id))
-    _check(rc, "tt_load_bpe")
+    rc = lib().tt_load_bpe_ex(m.ctypes.data if len(m) else None, None if r is None else r.ctypes.data,
+                              len(m), int(pattern_id), LOAD_IGNORE_MERGES if ignore_merges else 0)
+    _check(rc, "tt_load_bpe_ex")
 
 
 def reserve(max_bytes, max_seqs=1):

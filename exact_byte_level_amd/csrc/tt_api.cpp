@@ -2,6 +2,7 @@
 // and the enqueue-only encode entry points declared in include/tt.h.
 #include <algorithm>
 #include <new>
+#include <string>
 #include <cstring>
 #include <mutex>
 #include <unordered_map>
@@ -29,6 +30,10 @@ struct State {
   uint64_t* d_pair = nullptr;
   CacheBucket* d_cache = nullptr;
   uint32_t* d_tok_len = nullptr;
+  uint64_t* d_word = nullptr;
+  uint32_t* d_tok_off = nullptr;
+  uint8_t* d_tok_bytes = nullptr;
+  bool ignore_merges = false;
   Tables tb{};
   void* d_ws = nullptr;
   int64_t ws_n = 0;     // bytes of input the workspace is sized for
@@ -103,6 +108,9 @@ void release_tables() {
   free_dev(g.d_pair);
   free_dev(g.d_cache);
   free_dev(g.d_tok_len);
+  free_dev(g.d_word);
+  free_dev(g.d_tok_off);
+  free_dev(g.d_tok_bytes);
   g.loaded = false;
 }
 
@@ -261,8 +269,15 @@ void tt::prof_mark(const char* name, hipStream_t st) {
 extern "C" {
 
 int tt_load_bpe(const int32_t* merges, const int32_t* ranks, int64_t n_merges, int32_t pattern_id) {
+  return tt_load_bpe_ex(merges, ranks, n_merges, pattern_id, 0u);
+}
+
+int tt_load_bpe_ex(const int32_t* merges, const int32_t* ranks, int64_t n_merges, int32_t pattern_id,
+                   uint32_t flags) {
   std::lock_guard<std::mutex> lock(g_mu);
   if (pattern_id != TT_PATTERN_GPT2 && pattern_id != TT_PATTERN_CL100K) return TT_EINVAL;
+  if (flags & ~(uint32_t)TT_LOAD_IGNORE_MERGES) return TT_EINVAL;
+  const bool whole = (flags & TT_LOAD_IGNORE_MERGES) != 0;
   if (n_merges < 0 || n_merges > TT_MAX_MERGES) return TT_EINVAL;
   if (n_merges > 0 && !merges) return TT_EINVAL;
   const size_t M = (size_t)n_merges;
@@ -336,13 +351,33 @@ int tt_load_bpe(const int32_t* merges, const int32_t* ranks, int64_t n_merges, i
   // any id masked to ID_BITS indexes inside the table
   std::vector<uint32_t> tok_len((size_t)1 << ID_BITS, 0u);
   for (size_t t = 0; t < tok.size(); ++t) tok_len[t] = (uint32_t)std::min<size_t>(tok[t].size(), 0xFFFFFFFFu);
-  std::vector<uint32_t> single;
-  for (size_t r = 0; r < M; ++r) {
-    const auto& bs = tok[256 + r];
-    if (bs.size() < 2 || bs.size() > (size_t)CACHE_MAXLEN) continue;
-    std::vector<uint32_t> ids(bs.begin(), bs.end());
-    std::vector<uint32_t> out = host_bpe(ids, rank);
-    if (out.size() == 1 && out[0] == 256u + r) single.push_back((uint32_t)(256 + r));
+  // whole-pre-token table: tokens of 2..16 bytes whose own BPE is
+  // themselves; with the whole-word rule, every token (the smallest id of
+  // each byte string), and the longer ones go to the whole-word table
+  std::vector<uint32_t> single, words;
+  size_t word_maxlen = 0;
+  if (whole) {
+    std::unordered_map<std::string, uint32_t> first;
+    first.reserve(tok.size() * 2);
+    for (size_t t = 256; t < tok.size(); ++t) {
+      const std::string key(tok[t].begin(), tok[t].end());
+      if (!first.emplace(key, (uint32_t)t).second) continue;  // a later id with the same bytes
+      if (tok[t].size() > (size_t)WORD_MAXLEN) return TT_ETABLE;
+      if (tok[t].size() <= (size_t)CACHE_MAXLEN) {
+        single.push_back((uint32_t)t);
+      } else {
+        words.push_back((uint32_t)t);
+        word_maxlen = std::max(word_maxlen, tok[t].size());
+      }
+    }
+  } else {
+    for (size_t r = 0; r < M; ++r) {
+      const auto& bs = tok[256 + r];
+      if (bs.size() < 2 || bs.size() > (size_t)CACHE_MAXLEN) continue;
+      std::vector<uint32_t> ids(bs.begin(), bs.end());
+      std::vector<uint32_t> out = host_bpe(ids, rank);
+      if (out.size() == 1 && out[0] == 256u + r) single.push_back((uint32_t)(256 + r));
+    }
   }
   // buckets of CACHE_SLOTS entries, load factor <= 1/2
   const uint64_t cache_nb = std::max<uint64_t>(next_pow2((single.size() * 2 + CACHE_SLOTS - 1) / CACHE_SLOTS), 256);
@@ -374,11 +409,48 @@ int tt_load_bpe(const int32_t* merges, const int32_t* ranks, int64_t n_merges, i
     }
   }
 
+  // whole-word table: open addressing, load factor <= 1/2; a token's bytes
+  // at tok_off[t] in tok_bytes
+  std::vector<uint64_t> word_tab;
+  std::vector<uint32_t> tok_off;
+  std::vector<uint8_t> tok_blob;
+  int word_probe = 0;
+  if (whole) {
+    const uint64_t ns = std::max<uint64_t>(next_pow2(words.size() * 2 + 1), 64);
+    word_tab.assign(ns, 0ull);
+    for (uint32_t t : words) {
+      const auto& bs = tok[t];
+      uint64_t h = word_hash_init((uint32_t)bs.size());
+      for (size_t k = 0; k < bs.size(); k += 8) {
+        uint64_t wd = 0;
+        for (size_t j = 0; j < 8 && k + j < bs.size(); ++j) wd |= (uint64_t)bs[k + j] << (8 * j);
+        h = word_hash_step(h, wd);
+      }
+      const uint64_t e = (h >> 32 << 32) | ((uint64_t)bs.size() << ID_BITS) | t;
+      uint64_t pos = h & (ns - 1);
+      int run = 1;
+      while (word_tab[pos] != 0) {
+        pos = (pos + 1) & (ns - 1);
+        ++run;
+      }
+      word_tab[pos] = e;
+      word_probe = std::max(word_probe, run);
+    }
+    tok_off.resize(tok.size() + 1);
+    for (size_t t = 0; t < tok.size(); ++t) {
+      tok_off[t] = (uint32_t)tok_blob.size();
+      tok_blob.insert(tok_blob.end(), tok[t].begin(), tok[t].end());
+    }
+    tok_off[tok.size()] = (uint32_t)tok_blob.size();
+  }
+
   if (hipDeviceSynchronize() != hipSuccess) return TT_EHIP;
   release_tables();
   int rc;
   if ((rc = upload(&g.d_byte_pair, byte_pair)) != TT_OK || (rc = upload(&g.d_pair, pair_tab)) != TT_OK ||
-      (rc = upload(&g.d_cache, cache)) != TT_OK || (rc = upload(&g.d_tok_len, tok_len)) != TT_OK) {
+      (rc = upload(&g.d_cache, cache)) != TT_OK || (rc = upload(&g.d_tok_len, tok_len)) != TT_OK ||
+      (whole && ((rc = upload(&g.d_word, word_tab)) != TT_OK || (rc = upload(&g.d_tok_off, tok_off)) != TT_OK ||
+                 (rc = upload(&g.d_tok_bytes, tok_blob)) != TT_OK))) {
     release_tables();
     return rc;
   }
@@ -397,6 +469,13 @@ int tt_load_bpe(const int32_t* merges, const int32_t* ranks, int64_t n_merges, i
   g.tb.cache_shift = cache_shift;
   g.tb.cache_probe = cache_probe;
   g.tb.pattern = pattern_id;
+  g.tb.word_tab = g.d_word;
+  g.tb.tok_off = g.d_tok_off;
+  g.tb.tok_bytes = g.d_tok_bytes;
+  g.tb.word_mask = whole ? (uint32_t)(word_tab.size() - 1) : 0u;
+  g.tb.word_probe = word_probe;
+  g.tb.word_maxlen = whole ? (int)std::max<size_t>(word_maxlen, (size_t)CACHE_MAXLEN) : 0;
+  g.ignore_merges = whole;
   g.loaded = true;
   return TT_OK;
 }

@@ -81,6 +81,18 @@ __host__ __device__ inline uint32_t cache_hash(uint64_t w0, uint64_t w1, uint32_
 }
 
 // Device-resident tables of the loaded tokenizer (passed by value).
+// Whole-word table (the whole-word rule, for pieces longer than
+// CACHE_MAXLEN bytes): open addressing over entries
+// hash << 32 | length << ID_BITS | id (0 = empty), the hash over the piece's
+// bytes read as little-endian 8-byte words (the last one zero-padded); a hit
+// is confirmed against the token's bytes.
+constexpr int WORD_MAXLEN = 2048;  // longest token the rule serves
+__host__ __device__ inline uint64_t word_hash_init(uint32_t len) { return 0x9E3779B97F4A7C15ull * ((uint64_t)len + 1); }
+__host__ __device__ inline uint64_t word_hash_step(uint64_t h, uint64_t word) {
+  h = (h ^ word) * 0xFF51AFD7ED558CCDull;
+  return h ^ (h >> 32);
+}
+
 struct Tables {
   const uint32_t* byte_pair;    // [65536] rank of (x, y), x, y < 256, or RANK_NONE
   const uint64_t* pair_tab;     // [2^(32 - pair_shift)] two-choice slots
@@ -91,6 +103,14 @@ struct Tables {
   int cache_shift;              // 64 - log2(cache_nb)
   int cache_probe;              // max buckets visited by any lookup
   int pattern;
+  // whole-word rule (word_maxlen > 0): every token of 2..16 bytes is in the
+  // cache, longer ones in word_tab
+  const uint64_t* word_tab;     // [word_mask + 1]
+  const uint32_t* tok_off;      // [vocabulary + 1] offset of each token's bytes in tok_bytes
+  const uint8_t* tok_bytes;     // every token's bytes, back to back
+  uint32_t word_mask;
+  int word_probe;               // longest probe run in word_tab
+  int word_maxlen;              // longest token with the rule on, else 0
 };
 
 // Device workspace of one encode.

@@ -852,6 +852,32 @@ __device__ __forceinline__ uint32_t pair_rank(const Tables& tb, uint32_t x, uint
   return (x | y) < 256u ? bp : r;
 }
 
+// The whole-word rule for a piece of len bytes at p, CACHE_MAXLEN < len <=
+// tb.word_maxlen: the id of the token with exactly these bytes, or
+// RANK_NONE.  Linear probing ends at an empty slot; a slot whose hash and
+// length match is confirmed against the token's bytes.
+__device__ uint32_t word_lookup(const Tables& tb, const uint8_t* __restrict__ p, uint32_t len) {
+  uint64_t h = word_hash_init(len);
+  for (uint32_t k = 0; k < len; k += 8) {
+    uint64_t wd = 0;
+    for (uint32_t j = 0; j < 8 && k + j < len; ++j) wd |= (uint64_t)p[k + j] << (8 * j);
+    h = word_hash_step(h, wd);
+  }
+  const uint64_t key = (h >> 32 << 32) | ((uint64_t)len << ID_BITS);
+  uint32_t slot = (uint32_t)h & tb.word_mask;
+  for (int i = 0; i < tb.word_probe; ++i, slot = (slot + 1) & tb.word_mask) {
+    const uint64_t e = tb.word_tab[slot];
+    if (e == 0) break;
+    if ((e & ~(uint64_t)ID_MASK) != key) continue;
+    const uint32_t id = (uint32_t)e & ID_MASK;
+    const uint8_t* q = tb.tok_bytes + tb.tok_off[id];
+    bool same = true;
+    for (uint32_t k = 0; k < len && same; ++k) same = p[k] == q[k];
+    if (same) return id;
+  }
+  return RANK_NONE;
+}
+
 // Id of the single-token piece with these bytes (len 2..16), or RANK_NONE.
 // One 128-byte bucket per step (the second key word only for len > 8); the
 // walk ends at the first bucket that no key's probe run passed.
@@ -1415,7 +1441,6 @@ __global__ __launch_bounds__(PT_THREADS) __attribute__((amdgpu_waves_per_eu(6)))
   if (stage_fast) sv = *reinterpret_cast<const uint4*>(bytes + sg);
   const uint32_t nc1 = (CLASSIFY && t + 1 + lane < ntiles) ? w.tile_cnt[t + 1 + lane] : 0u;
   const uint32_t fl1 = (CLASSIFY && t + 1 < ntiles) ? w.flags[(int64_t)(t + 1) * PT_THREADS + lane] : 0u;
-  const uint32_t prev_cnt = (CLASSIFY && t > 0) ? w.tile_cnt[t - 1] : 1u;
   uint32_t hi;
   // the last tile also folds its own count and error bits into the totals
   const uint32_t base = block_reduce(w.tile_cnt, last ? t + 1 : t, cmask, red, &hi) -
@@ -1482,7 +1507,15 @@ __global__ __launch_bounds__(PT_THREADS) __attribute__((amdgpu_waves_per_eu(6)))
       const int32_t s = sst[k];
       const int32_t len = sst[k + 1] - s;
       const int off = (int)(s - t0);
-      if (len > BIG_BYTES) {
+      // the whole-word rule, for pieces longer than the cache's keys
+      const uint32_t word = len > CACHE_MAXLEN && len <= tb.word_maxlen
+                                ? word_lookup(tb, bytes + s, (uint32_t)len)
+                                : RANK_NONE;
+      if (word != RANK_NONE) {
+        w.tmp_ids[s] = (int32_t)word;
+        w.piece_cnt[p] = 1;
+        ++fin;
+      } else if (len > BIG_BYTES) {
         // only a tile's last piece can be this long: the tile merges it below
       } else if (len > LANE_CAP) {
         cls = 4;
@@ -1539,7 +1572,7 @@ __global__ __launch_bounds__(PT_THREADS) __attribute__((amdgpu_waves_per_eu(6)))
   const int32_t fs = (int32_t)uniform((uint32_t)sst[0]);
   int32_t sp = 0;
   bool head_last = false;
-  if (t % SHARE_TILES == 0 && t > 0 && fs > t0 && (prev_cnt & cmask) == 0u) {
+  if (t % SHARE_TILES == 0 && t > 0 && fs > t0 && (w.tile_cnt[t - 1] & cmask) == 0u) {
     sp = last_start_before(w, t, cmask);
     if (fs - sp > BIG_BYTES) head_last = big_share(bytes, w, tb, sp, fs, (int32_t)t0, fs, t0, big);
   }
@@ -2021,7 +2054,8 @@ hipError_t launch_pretokenize(const uint8_t* bytes, int64_t n, const int64_t* of
     prof_mark("k_pretok<0>", st);
   }
   if (tb) {
-    hipLaunchKernelGGL(k_compact<true>, dim3(ntiles), dim3(PT_THREADS), 0, st, bytes, w, *tb, ntiles, n, starts, out_np);
+    hipLaunchKernelGGL(k_compact<true>, dim3(ntiles), dim3(PT_THREADS), 0, st, bytes, w, *tb, ntiles, n, starts,
+                       out_np);
   } else {
     hipLaunchKernelGGL(k_compact<false>, dim3(ntiles), dim3(PT_THREADS), 0, st, bytes, w, Tables{}, ntiles, n, starts,
                        out_np);

@@ -72,6 +72,29 @@ extern "C" {
  */
 int tt_load_bpe(const int32_t* merges, const int32_t* ranks, int64_t n_merges, int32_t pattern_id);
 
+/* Option of tt_load_bpe_ex: the whole-word rule of the Llama family
+ * (ignore_merges; TokTier summary page, §4.2: the whole pre-token is first
+ * matched against the vocabulary, and a match skips the merges).  A piece
+ * whose bytes are those of a token becomes that one token (the smallest id
+ * if several tokens have the same bytes); any other piece is merged as
+ * usual.  Tables learned by BPE training have no token that its own BPE
+ * fails to reach, so there the rule changes nothing; it matters for tables
+ * that do. */
+#define TT_LOAD_IGNORE_MERGES 1u
+
+/* tt_load_bpe_ex -- tt_load_bpe with options.
+ *
+ * flags      0 (same as tt_load_bpe) or TT_LOAD_IGNORE_MERGES.  With the
+ *            rule, every token of 2..16 bytes goes into the whole-pre-token
+ *            cache and longer tokens into a hashed whole-word table whose
+ *            hits are confirmed byte by byte; tokens longer than 2048 bytes
+ *            are not supported (TT_ETABLE).
+ * Other arguments, effects and return values as tt_load_bpe; unknown flag
+ * bits give TT_EINVAL.
+ */
+int tt_load_bpe_ex(const int32_t* merges, const int32_t* ranks, int64_t n_merges, int32_t pattern_id,
+                   uint32_t flags);
+
 /* tt_reserve -- size the device workspace for inputs of up to max_bytes
  * bytes and up to max_seqs batch sequences, so that later encodes do no
  * allocation (required before capturing an encode into a HIP graph).

@@ -28,7 +28,7 @@ def _declared():
 
 def test_exports_every_declared_symbol():
     names = _declared()
-    assert names == sorted(["tt_load_bpe", "tt_reserve", "tt_encode", "tt_encode_batch", "tt_pretokenize", "tt_encode_offsets",
+    assert names == sorted(["tt_load_bpe", "tt_load_bpe_ex", "tt_reserve", "tt_encode", "tt_encode_batch", "tt_pretokenize", "tt_encode_offsets",
                             "tt_session_create", "tt_session_destroy", "tt_session_reset", "tt_session_append",
                             "tt_session_view", "tt_session_read",
                             "tt_char_class", "tt_profile", "tt_profile_read", "tt_free", "tt_strerror"])
@@ -71,6 +71,12 @@ def test_load_rejects_bad_tables_without_device():
     assert load([(97, 98), (98, 99)], ranks=[0, 2]) == tt.TT_ETABLE
     assert load([(97, 257), (98, 99)], ranks=[1, 0]) == tt.TT_ETABLE  # 257 = rank 1 itself
     assert lib.tt_load_bpe(None, None, -1, 0) == tt.TT_EINVAL
+    m = np.ascontiguousarray(np.asarray([(97, 98)], dtype=np.int32))
+    assert lib.tt_load_bpe_ex(m.ctypes.data, None, 1, 0, 2) == tt.TT_EINVAL  # unknown flag
+    # with the whole-word rule, a token longer than 2048 bytes is refused:
+    # a, aa, aaaa, ... up to 4096 letters
+    chain = np.ascontiguousarray(np.asarray([(97, 97)] + [(256 + i, 256 + i) for i in range(11)], dtype=np.int32))
+    assert lib.tt_load_bpe_ex(chain.ctypes.data, None, len(chain), 0, tt.LOAD_IGNORE_MERGES) == tt.TT_ETABLE
 
 
 def test_encode_rejects_bad_arguments():
