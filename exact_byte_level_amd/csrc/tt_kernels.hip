@@ -1614,9 +1614,13 @@ __global__ __launch_bounds__(MERGE_THREADS) __attribute__((amdgpu_waves_per_eu(8
   const uint32_t nwaves = gridDim.x * (MERGE_THREADS / 64);
   const uint32_t wv = uniform(blockIdx.x * (MERGE_THREADS / 64) + (threadIdx.x >> 6));
   // rounds of nwaves items, every other round dealt in reverse: the waves
-  // that drew the longest items in one round draw the shortest in the next
+  // that drew the longest items in one round draw the shortest in the next.
+  // A wavefront's issue priority follows its item's length class, so that
+  // the SIMDs favour the longest merge chains (the kernel's critical path)
+  // over the short items that fill in around them.
   for (uint32_t rnd = 0, t = wv; t < total; ++rnd, t = rnd * nwaves + ((rnd & 1u) ? nwaves - 1u - wv : wv)) {
     if (t < nl) {
+      __builtin_amdgcn_s_setprio(3);
       long_bpe(bytes, w, tb, uniform((uint32_t)w.long_list[t]));
       continue;
     }
@@ -1629,10 +1633,19 @@ __global__ __launch_bounds__(MERGE_THREADS) __attribute__((amdgpu_waves_per_eu(8
     const uint32_t item = u - uniform(pre[k]);
     const uint32_t qn = w.qctr[g * QCTR_STRIDE + c];
     const uint32_t* q = w.queue[c] + g * w.qcap[c];
-    if (c == 3) group_bpe<64>(bytes, w, tb, q, (int)qn, (int)item);
-    else if (c == 2) group_bpe<32>(bytes, w, tb, q, (int)qn, (int)item);
-    else if (c == 1) group_bpe<16>(bytes, w, tb, q, (int)qn, (int)item);
-    else group_bpe<8>(bytes, w, tb, q, (int)qn, (int)item);
+    if (c == 3) {
+      __builtin_amdgcn_s_setprio(3);
+      group_bpe<64>(bytes, w, tb, q, (int)qn, (int)item);
+    } else if (c == 2) {
+      __builtin_amdgcn_s_setprio(2);
+      group_bpe<32>(bytes, w, tb, q, (int)qn, (int)item);
+    } else if (c == 1) {
+      __builtin_amdgcn_s_setprio(1);
+      group_bpe<16>(bytes, w, tb, q, (int)qn, (int)item);
+    } else {
+      __builtin_amdgcn_s_setprio(0);
+      group_bpe<8>(bytes, w, tb, q, (int)qn, (int)item);
+    }
   }
 }
 
