@@ -375,10 +375,28 @@ __device__ uint32_t block_excl_bwd(uint32_t x, uint32_t* red, uint32_t* total) {
   return Op::combine(exc, post);
 }
 
+// Butterfly step inside each half of the wavefront: lane l reads lane l ^ d
+// (d < 32).  ds_swizzle takes the pattern as an immediate, so a kernel with
+// many reductions keeps no per-lane address registers alive for them.
+template <int D>
+__device__ __forceinline__ uint32_t swz_xor(uint32_t x) {
+  static_assert(D > 0 && D < 32, "within a half");
+  return (uint32_t)__builtin_amdgcn_ds_swizzle((int)x, 0x1F | (D << 10));
+}
+
+// Sum over the wavefront, the same in every lane.
+__device__ __forceinline__ uint32_t wave_sum(uint32_t x) {
+  x += swz_xor<16>(x);
+  x += swz_xor<8>(x);
+  x += swz_xor<4>(x);
+  x += swz_xor<2>(x);
+  x += swz_xor<1>(x);
+  return (uint32_t)__builtin_amdgcn_readlane((int)x, 0) + (uint32_t)__builtin_amdgcn_readlane((int)x, 32);
+}
+
 __device__ __forceinline__ uint32_t block_sum(uint32_t x, uint32_t* red) {
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-#pragma unroll
-  for (int d = 32; d >= 1; d >>= 1) x += __shfl_xor(x, d);
+  x = wave_sum(x);
   if (lane == 0) red[wid] = x;
   __syncthreads();
   uint32_t t = 0;
@@ -1021,9 +1039,12 @@ __device__ void group_bpe(const uint8_t* __restrict__ bytes, const Work& w, cons
 }
 
 __device__ __forceinline__ uint32_t wave_min(uint32_t x) {
-#pragma unroll
-  for (int d = 32; d >= 1; d >>= 1) x = min(x, (uint32_t)__shfl_xor(x, d));
-  return x;
+  x = min(x, swz_xor<16>(x));
+  x = min(x, swz_xor<8>(x));
+  x = min(x, swz_xor<4>(x));
+  x = min(x, swz_xor<2>(x));
+  x = min(x, swz_xor<1>(x));
+  return min((uint32_t)__builtin_amdgcn_readlane((int)x, 0), (uint32_t)__builtin_amdgcn_readlane((int)x, 32));
 }
 
 // Merge starts of one 64-position chunk: ms[k] = eq[k] && !ms[k-1], ms[-1] =
