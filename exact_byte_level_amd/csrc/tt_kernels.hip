@@ -316,24 +316,50 @@ struct BwdOp {
   }
 };
 
+// Sum as a scan operator.
+struct SumOp {
+  static constexpr uint32_t IDENT = 0;
+  __device__ static __forceinline__ uint32_t combine(uint32_t a, uint32_t b) { return a + b; }
+};
+
+// Ordered scans over a wavefront by DPP (operand modifiers of the combining
+// VALU instruction: no LDS round trip and no per-lane address registers).
+// dpp_id reads another lane's x by dpp_ctrl CTRL in the rows of ROWS; lanes
+// without a source, or outside ROWS, read id.  Controls: 0x111.. row shift
+// right by 1.., 0x101.. row shift left, 0x142 / 0x143 row broadcast of lane
+// 15 / 31, 0x138 / 0x130 wavefront shift right / left by one lane.
+template <int CTRL, int ROWS = 0xF>
+__device__ __forceinline__ uint32_t dpp_id(uint32_t id, uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_update_dpp((int)id, (int)x, CTRL, ROWS, 0xF, false);
+}
+
+// Inclusive left-to-right scan: Kogge-Stone inside each 16-lane row, then
+// the rows before by broadcasts (lane 15 of a row into rows 1 and 3, then
+// lane 31 into rows 2 and 3).
 template <class Op>
-__device__ __forceinline__ uint32_t wave_incl_fwd(uint32_t x, int lane) {
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    uint32_t o = __shfl_up(x, d);
-    if (lane >= d) x = Op::combine(o, x);
-  }
+__device__ __forceinline__ uint32_t wave_incl_fwd(uint32_t x, int) {
+  x = Op::combine(dpp_id<0x111>(Op::IDENT, x), x);
+  x = Op::combine(dpp_id<0x112>(Op::IDENT, x), x);
+  x = Op::combine(dpp_id<0x114>(Op::IDENT, x), x);
+  x = Op::combine(dpp_id<0x118>(Op::IDENT, x), x);
+  x = Op::combine(dpp_id<0x142, 0xA>(Op::IDENT, x), x);
+  x = Op::combine(dpp_id<0x143, 0xC>(Op::IDENT, x), x);
   return x;
 }
 
+// Inclusive right-to-left scan: Kogge-Stone inside each row, then the totals
+// of the rows after (their first lanes, read into scalars).
 template <class Op>
 __device__ __forceinline__ uint32_t wave_incl_bwd(uint32_t x, int lane) {
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    uint32_t o = __shfl_down(x, d);
-    if (lane + d < 64) x = Op::combine(x, o);
-  }
-  return x;
+  x = Op::combine(x, dpp_id<0x101>(Op::IDENT, x));
+  x = Op::combine(x, dpp_id<0x102>(Op::IDENT, x));
+  x = Op::combine(x, dpp_id<0x104>(Op::IDENT, x));
+  x = Op::combine(x, dpp_id<0x108>(Op::IDENT, x));
+  const uint32_t r3 = (uint32_t)__builtin_amdgcn_readlane((int)x, 48);
+  const uint32_t p2 = Op::combine((uint32_t)__builtin_amdgcn_readlane((int)x, 32), r3);
+  const uint32_t p1 = Op::combine((uint32_t)__builtin_amdgcn_readlane((int)x, 16), p2);
+  const int row = lane >> 4;
+  return Op::combine(x, row == 0 ? p1 : row == 1 ? p2 : row == 2 ? r3 : Op::IDENT);
 }
 
 // Exclusive ordered scan over the PT_THREADS threads of a block (left to
@@ -342,8 +368,7 @@ template <class Op>
 __device__ uint32_t block_excl_fwd(uint32_t x, uint32_t* red, uint32_t* total) {
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   uint32_t inc = wave_incl_fwd<Op>(x, lane);
-  uint32_t exc = __shfl_up(inc, 1);
-  if (lane == 0) exc = Op::IDENT;
+  uint32_t exc = dpp_id<0x138>(Op::IDENT, inc);
   if (lane == 63) red[wid] = inc;
   __syncthreads();
   uint32_t pre = Op::IDENT, tot = Op::IDENT;
@@ -361,8 +386,7 @@ template <class Op>
 __device__ uint32_t block_excl_bwd(uint32_t x, uint32_t* red, uint32_t* total) {
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   uint32_t inc = wave_incl_bwd<Op>(x, lane);
-  uint32_t exc = __shfl_down(inc, 1);
-  if (lane == 63) exc = Op::IDENT;
+  uint32_t exc = dpp_id<0x130>(Op::IDENT, inc);
   if (lane == 0) red[wid] = inc;
   __syncthreads();
   uint32_t post = Op::IDENT, tot = Op::IDENT;
@@ -408,12 +432,7 @@ __device__ __forceinline__ uint32_t block_sum(uint32_t x, uint32_t* red) {
 // Exclusive prefix sum over the block; *total receives the block sum.
 __device__ __forceinline__ uint32_t block_excl_sum(uint32_t x, uint32_t* red, uint32_t* total) {
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-  uint32_t inc = x;
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    uint32_t o = __shfl_up(inc, d);
-    if (lane >= d) inc += o;
-  }
+  const uint32_t inc = wave_incl_fwd<SumOp>(x, lane);
   if (lane == 63) red[wid] = inc;
   __syncthreads();
   uint32_t pre = 0, tot = 0;
@@ -1141,6 +1160,10 @@ __device__ __forceinline__ uint32_t fn_compose(uint32_t f, uint32_t g) {
   const uint32_t h1 = (f & 2u) ? (g >> 1) & 1u : g & 1u;
   return h0 | (h1 << 1);
 }
+struct FnOp {
+  static constexpr uint32_t IDENT = FN_ID;
+  __device__ static __forceinline__ uint32_t combine(uint32_t f, uint32_t g) { return fn_compose(f, g); }
+};
 
 __device__ __forceinline__ uint32_t block_min(uint32_t x, uint32_t* red) {
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
@@ -1228,19 +1251,12 @@ __device__ int big_rounds(const Work& w, const Tables& tb, uint32_t p, int32_t s
         msB |= b << j;
       }
       // carry into this thread: the step's carry through the functions of the threads before it
-      uint32_t inc = a | (b << 1);
-#pragma unroll
-      for (int d = 1; d < 64; d <<= 1) {
-        const uint32_t o = (uint32_t)__shfl_up((int)inc, d);
-        if (lane >= d) inc = fn_compose(o, inc);
-      }
+      const uint32_t inc = wave_incl_fwd<FnOp>(a | (b << 1), lane);
       if (lane == 63) sm.sh[wid] = inc;
       __syncthreads();
       uint32_t before = FN_ID;
       for (int v = 0; v < wid; ++v) before = fn_compose(before, sm.sh[v]);
-      uint32_t exl = (uint32_t)__shfl_up((int)inc, 1);
-      if (lane == 0) exl = FN_ID;
-      before = fn_compose(before, exl);
+      before = fn_compose(before, dpp_id<0x138>(FN_ID, inc));
       const uint32_t tc = (cin ? (before >> 1) : before) & 1u;
       const uint32_t ms = tc ? msB : msA;
       const uint32_t lastms = (ms >> (BIG_E - 1)) & 1u;
@@ -1621,12 +1637,7 @@ __global__ __launch_bounds__(MERGE_THREADS) __attribute__((amdgpu_waves_per_eu(8
   if (threadIdx.x < 64) {
     const int k = (int)threadIdx.x, c = 3 - k / QGROUPS, g = k % QGROUPS;
     const uint32_t it = k < NQ ? (w.qctr[g * QCTR_STRIDE + c] + (8u >> c) - 1) >> (3 - c) : 0u;
-    uint32_t inc = it;
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-      const uint32_t o = __shfl_up(inc, d);
-      if (k >= d) inc += o;
-    }
+    const uint32_t inc = wave_incl_fwd<SumOp>(it, k);
     if (k <= NQ) pre[k] = inc - it;
   }
   __syncthreads();
@@ -1768,12 +1779,7 @@ __global__ __launch_bounds__(EMIT_THREADS) void k_emit(Work w, int ntiles, int32
       if (in) out_ids[co + lane] = id;
       if (OFFS) {
         const uint32_t len = in ? tok_len[(uint32_t)id & ID_MASK] : 0u;
-        uint32_t inc = len;
-#pragma unroll
-        for (int d = 1; d < 64; d <<= 1) {
-          const uint32_t o = __shfl_up(inc, d);
-          if (lane >= d) inc += o;
-        }
+        const uint32_t inc = wave_incl_fwd<SumOp>(len, lane);
         if (in) out_starts[co + lane] = (int32_t)(cs + inc - len);
       }
     }
