@@ -333,6 +333,14 @@ __device__ __forceinline__ uint32_t dpp_id(uint32_t id, uint32_t x) {
   return (uint32_t)__builtin_amdgcn_update_dpp((int)id, (int)x, CTRL, ROWS, 0xF, false);
 }
 
+// Op with its operands swapped (a scan over lanes whose text order runs from
+// the last lane to the first).
+template <class Op>
+struct RevOp {
+  static constexpr uint32_t IDENT = Op::IDENT;
+  __device__ static __forceinline__ uint32_t combine(uint32_t a, uint32_t b) { return Op::combine(b, a); }
+};
+
 // Inclusive left-to-right scan: Kogge-Stone inside each 16-lane row, then
 // the rows before by broadcasts (lane 15 of a row into rows 1 and 3, then
 // lane 31 into rows 2 and 3).
@@ -529,14 +537,10 @@ __device__ void tile_carries(const Work& w, int t, int ntiles, TileSmem& sm) {
     uint32_t acc = FwdOp::IDENT;
     for (int b = t - 1; b >= 0; b -= 64) {
       int j = b - lane;
-      uint32_t v = j >= 0 ? w.tile_fwd[j] : FwdOp::IDENT;
-#pragma unroll
-      for (int d = 1; d < 64; d <<= 1) {
-        uint32_t o = __shfl_down(v, d);
-        if (lane + d < 64) v = FwdOp::combine(o, v);
-      }
-      v = __shfl(v, 0);
-      acc = uniform(FwdOp::combine(v, acc));
+      // lane 0 is the tile next to t: the lanes run right to left in the text
+      const uint32_t v = j >= 0 ? w.tile_fwd[j] : FwdOp::IDENT;
+      const uint32_t all = (uint32_t)__builtin_amdgcn_readlane((int)wave_incl_bwd<RevOp<FwdOp>>(v, lane), 0);
+      acc = uniform(FwdOp::combine(all, acc));
       if ((acc & 1u) && !(acc & 2u)) break;
     }
     if (lane == 0) sm.carry_fwd = acc;
@@ -544,14 +548,9 @@ __device__ void tile_carries(const Work& w, int t, int ntiles, TileSmem& sm) {
     uint32_t acc = BwdOp::IDENT;
     for (int b = t + 1; b < ntiles; b += 64) {
       int j = b + lane;
-      uint32_t v = j < ntiles ? w.tile_bwd[j] : BwdOp::IDENT;
-#pragma unroll
-      for (int d = 1; d < 64; d <<= 1) {
-        uint32_t o = __shfl_down(v, d);
-        if (lane + d < 64) v = BwdOp::combine(v, o);
-      }
-      v = __shfl(v, 0);
-      acc = uniform(BwdOp::combine(acc, v));
+      const uint32_t v = j < ntiles ? w.tile_bwd[j] : BwdOp::IDENT;
+      const uint32_t all = (uint32_t)__builtin_amdgcn_readlane((int)wave_incl_bwd<BwdOp>(v, lane), 0);
+      acc = uniform(BwdOp::combine(acc, all));
       if ((acc & 1u) && !(acc & 2u)) break;
     }
     if (lane == 0) sm.carry_bwd = acc;
@@ -1390,7 +1389,7 @@ __device__ int32_t last_start_before(const Work& w, int t, uint32_t cmask) {
         const uint64_t fm = __ballot(fl != 0u);
         if (fm) {
           const int l = 63 - __clzll((long long)fm);
-          const uint32_t flw = (uint32_t)__shfl((int)fl, l);
+          const uint32_t flw = (uint32_t)__builtin_amdgcn_readlane((int)fl, l);
           return (int32_t)((int64_t)f * TILE + PT_CHUNK * (q + l) + 31 - __clz(flw));
         }
       }
@@ -1410,7 +1409,7 @@ __device__ int32_t first_start_after(const Work& w, int t, int ntiles, int64_t n
   const uint64_t fm1 = __ballot(fl1 != 0u);
   if ((nz1 & 1ull) && fm1) {
     const int l = __ffsll((unsigned long long)fm1) - 1;
-    const uint32_t flw = (uint32_t)__shfl((int)fl1, l);
+    const uint32_t flw = (uint32_t)__builtin_amdgcn_readlane((int)fl1, l);
     return (int32_t)((int64_t)(t + 1) * TILE + PT_CHUNK * l + __ffs(flw) - 1);
   }
   for (int b = t + 1; b < ntiles; b += 64) {
@@ -1423,7 +1422,7 @@ __device__ int32_t first_start_after(const Work& w, int t, int ntiles, int64_t n
         const uint64_t fm = __ballot(fl != 0u);
         if (fm) {
           const int l = __ffsll((unsigned long long)fm) - 1;
-          const uint32_t flw = (uint32_t)__shfl((int)fl, l);
+          const uint32_t flw = (uint32_t)__builtin_amdgcn_readlane((int)fl, l);
           return (int32_t)((int64_t)f * TILE + PT_CHUNK * (q + l) + __ffs(flw) - 1);
         }
       }
@@ -1773,7 +1772,9 @@ __global__ __launch_bounds__(EMIT_THREADS) void k_emit(Work w, int ntiles, int32
     while (big) {
       const int l = __ffsll((unsigned long long)big) - 1;
       big &= big - 1;
-      const uint32_t cs = __shfl(src, l), co = __shfl(off, l), cc = __shfl(c, l);
+      const uint32_t cs = (uint32_t)__builtin_amdgcn_readlane((int)src, l);
+      const uint32_t co = (uint32_t)__builtin_amdgcn_readlane((int)off, l);
+      const uint32_t cc = (uint32_t)__builtin_amdgcn_readlane((int)c, l);
       const bool in = (uint32_t)lane < cc;
       const int32_t id = in ? w.tmp_ids[cs + lane] : 0;
       if (in) out_ids[co + lane] = id;
