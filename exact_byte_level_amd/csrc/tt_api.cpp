@@ -147,6 +147,9 @@ size_t layout(int64_t n, char* base, Work* w) {
   t.tile_pbase = (uint32_t*)take(ntiles * 4);
   t.big_min = (uint32_t*)take(ntiles * 4);
   t.big_ctr = (int32_t*)take(ntiles * 4);
+  t.sb_cnt = (uint32_t*)take((ntiles / SB_TILES + 2) * 4);
+  t.sb_err = (uint32_t*)take((ntiles / SB_TILES + 2) * 4);
+  t.sb_tok = (uint32_t*)take((ntiles / SB_TILES + 2) * 4);
   t.long_list = (int32_t*)take((nn / (LANE_CAP + 1) + 2) * 4);
   t.huge_list = (int32_t*)take((nn / (HUGE_TOKENS + 1) + 2) * 4);
   // a class-c sub-queue takes the pieces of at least QCLASS_MINLEN[c] bytes

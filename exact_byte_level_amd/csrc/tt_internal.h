@@ -152,6 +152,13 @@ struct Work {
   // one): the least pair rank of the piece and the arrival counter.
   uint32_t* big_min;     // [ntiles]
   int32_t* big_ctr;      // [ntiles]
+  // Inputs of more than SB_MIN_TILES tiles: sums over each run of SB_TILES
+  // tiles of their piece counts (and the OR of their error bits) and of
+  // their token counts, so that a tile's prefix reads O(1) cache lines per
+  // thread instead of every tile before it (the kernels' SB instantiations).
+  uint32_t* sb_cnt;      // [ntiles / SB_TILES + 1]
+  uint32_t* sb_err;      // [ntiles / SB_TILES + 1]
+  uint32_t* sb_tok;      // [ntiles / SB_TILES + 1]
   int32_t* long_list;    // [n / (LANE_CAP + 1) + 1] pieces of LANE_CAP + 1 .. BIG_BYTES bytes
   int32_t* huge_list;    // [n / (HUGE_TOKENS + 1) + 1] pieces with more than HUGE_TOKENS tokens
   // Pieces for group BPE by class c (<= 8, 16, 32, 64 bytes).  Tile t
@@ -163,6 +170,9 @@ struct Work {
   uint32_t* qctr;        // [QGROUPS * QCTR_STRIDE]
   uint32_t* ctr;         // [CTR_COUNT]
 };
+
+constexpr int SB_TILES = 2048;          // tiles per super-block of the two-level tile prefix
+constexpr int SB_MIN_TILES = 16384;     // inputs above this many tiles use it
 
 // ------------------------------------------------------------- BPE tiers
 constexpr int LANE_CAP = 64;            // pieces up to this many bytes: group BPE in one wavefront

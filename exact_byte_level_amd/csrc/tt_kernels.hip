@@ -768,6 +768,42 @@ __device__ uint32_t block_reduce(const uint32_t* __restrict__ a, int cnt, uint32
   return block_sum(sum, red);
 }
 
+// Sum of (a[i] & mask), i < cnt, for a tile prefix (a = tile_cnt or
+// tile_tok), with *hi = this thread's OR of (a[i] & ~mask).  With the
+// super-block sums (SB: sb_sum and sb_or, which may be null), the whole runs of
+// SB_TILES tiles before cnt come from their sums and only the partial run is
+// read tile by tile.
+template <bool SB>
+__device__ __forceinline__ uint32_t tile_prefix(const uint32_t* __restrict__ a, const uint32_t* __restrict__ sb_sum,
+                                                const uint32_t* __restrict__ sb_or, int cnt, uint32_t mask,
+                                                uint32_t* red, uint32_t* hi) {
+  if (!SB || cnt < SB_TILES) return block_reduce(a, cnt, mask, red, hi);
+  const int j = cnt / SB_TILES;
+  uint32_t h0, h1, h2 = 0;
+  const uint32_t s0 = block_reduce(sb_sum, j, ~0u, red, &h0);
+  const uint32_t s1 = block_reduce(a + (int64_t)j * SB_TILES, cnt - j * SB_TILES, mask, red, &h1);
+  if (sb_or) block_reduce(sb_or, j, 0u, red, &h2);  // mask 0: the sum is 0, *hi the OR
+  *hi = h1 | h2;
+  return s0 + s1;
+}
+
+// Super-block j: the sum of (a[i] & mask) and the OR of (a[i] & ~mask) over
+// tiles [j * SB_TILES, (j + 1) * SB_TILES) (or_out may be null).
+__global__ __launch_bounds__(256) void k_sb_sums(const uint32_t* __restrict__ a, int ntiles, uint32_t mask,
+                                                 uint32_t* __restrict__ sum_out, uint32_t* __restrict__ or_out) {
+  __shared__ uint32_t red[8];
+  const int lo = (int)blockIdx.x * SB_TILES;
+  uint32_t hi;
+  const uint32_t sum = block_reduce(a + lo, min(SB_TILES, ntiles - lo), mask, red, &hi);
+  uint32_t orv = 0;
+  for (int b = 0; b < 32; ++b)
+    if ((~mask >> b) & 1u) orv |= __syncthreads_or((hi >> b) & 1u) ? 1u << b : 0u;
+  if (threadIdx.x == 0) {
+    sum_out[blockIdx.x] = sum;
+    if (or_out) or_out[blockIdx.x] = orv;
+  }
+}
+
 // Pass 2: pre-token start bits of every byte of a tile and the tile count,
 // with the tile's error bits (invalid UTF-8; for a batch, the validity of a
 // share of the offsets) above TILE_ERR_SHIFT.
@@ -1444,7 +1480,7 @@ __device__ int32_t first_start_after(const Work& w, int t, int ntiles, int64_t n
 // and start bits.  A piece longer than BIG_BYTES (only the tile's last one
 // and the one its first bytes end can be) gets the tile's share of its first
 // round, and the last tile to take a share merges it (big_share, big_merge).
-template <bool CLASSIFY>
+template <bool CLASSIFY, bool SB>
 __global__ __launch_bounds__(PT_THREADS) __attribute__((amdgpu_waves_per_eu(6))) void k_compact(const uint8_t* __restrict__ bytes, Work w, Tables tb,
                                                         int ntiles, int64_t n, int32_t* __restrict__ starts,
                                                         int64_t* __restrict__ out_np) {
@@ -1479,7 +1515,7 @@ __global__ __launch_bounds__(PT_THREADS) __attribute__((amdgpu_waves_per_eu(6)))
   const uint32_t fl1 = (CLASSIFY && t + 1 < ntiles) ? w.flags[(int64_t)(t + 1) * PT_THREADS + lane] : 0u;
   uint32_t hi;
   // the last tile also folds its own count and error bits into the totals
-  const uint32_t base = block_reduce(w.tile_cnt, last ? t + 1 : t, cmask, red, &hi) -
+  const uint32_t base = tile_prefix<SB>(w.tile_cnt, w.sb_cnt, w.sb_err, last ? t + 1 : t, cmask, red, &hi) -
                         (last ? (w.tile_cnt[t] & cmask) : 0u);
   uint32_t tot;
   uint32_t lpos = block_excl_sum(__popc(bits), red, &tot);
@@ -1731,7 +1767,7 @@ __global__ __launch_bounds__(EMIT_THREADS) void k_chunk_sums(Work w, const uint3
 // running sum in the piece's thread, a wavefront scan, or for a huge piece a
 // workgroup scan that starts from the byte lengths of the earlier chunks
 // (k_chunk_sums).  out_starts[T] = cap.
-template <bool OFFS>
+template <bool OFFS, bool SB>
 __global__ __launch_bounds__(EMIT_THREADS) void k_emit(Work w, int ntiles, int32_t* __restrict__ out_ids,
                                                        int64_t* __restrict__ out_n, uint32_t cap,
                                                        int32_t* __restrict__ out_starts,
@@ -1743,7 +1779,7 @@ __global__ __launch_bounds__(EMIT_THREADS) void k_emit(Work w, int ntiles, int32
   uint32_t hi;
   const uint32_t pbase = w.tile_pbase[t];
   const uint32_t np = w.tile_cnt[t] & cmask;
-  uint32_t off0 = block_reduce(w.tile_tok, t, ~0u, red, &hi);
+  uint32_t off0 = tile_prefix<SB>(w.tile_tok, w.sb_tok, nullptr, t, ~0u, red, &hi);
   for (uint32_t k0 = 0; k0 < np; k0 += EMIT_THREADS) {
     const uint32_t k = k0 + threadIdx.x;
     const bool live = k < np;
@@ -1809,7 +1845,7 @@ __global__ __launch_bounds__(EMIT_THREADS) void k_emit(Work w, int ntiles, int32
     const uint32_t src = (uint32_t)w.piece_start[p];
     const int tp = (int)(src / TILE);
     const uint32_t pb = w.tile_pbase[tp];
-    const uint32_t dst = block_reduce(w.tile_tok, tp, ~0u, red, &hi) +
+    const uint32_t dst = tile_prefix<SB>(w.tile_tok, w.sb_tok, nullptr, tp, ~0u, red, &hi) +
                          block_reduce(reinterpret_cast<const uint32_t*>(w.piece_cnt) + pb, (int)(p - pb), ~0u, red, &hi);
     for (uint32_t ch = first; ch < nch; ch += gridDim.x) {
       const uint32_t k1 = min(min(cc, (ch + 1) * HUGE_CHUNK), cap - min(cap, dst));  // never past the output
@@ -2094,13 +2130,21 @@ hipError_t launch_pretokenize(const uint8_t* bytes, int64_t n, const int64_t* of
     hipLaunchKernelGGL(k_pretok<0>, dim3(ntiles), dim3(PT_THREADS), 0, st, bytes, n, offs, nseq, ntiles, w);
     prof_mark("k_pretok<0>", st);
   }
-  if (tb) {
-    hipLaunchKernelGGL(k_compact<true>, dim3(ntiles), dim3(PT_THREADS), 0, st, bytes, w, *tb, ntiles, n, starts,
-                       out_np);
-  } else {
-    hipLaunchKernelGGL(k_compact<false>, dim3(ntiles), dim3(PT_THREADS), 0, st, bytes, w, Tables{}, ntiles, n, starts,
-                       out_np);
+  // large inputs: the two-level tile prefix (sums of the tile counts per
+  // super-block first); smaller ones sum the tile counts directly
+  const bool sb = ntiles > SB_MIN_TILES;
+  if (sb) {
+    hipLaunchKernelGGL(k_sb_sums, dim3(ceil_div(ntiles, SB_TILES)), dim3(256), 0, st, w.tile_cnt, ntiles,
+                       (1u << TILE_ERR_SHIFT) - 1u, w.sb_cnt, w.sb_err);
+    prof_mark("k_sb_sums", st);
   }
+  const dim3 g(ntiles), b(PT_THREADS);
+  if (tb && sb) hipLaunchKernelGGL((k_compact<true, true>), g, b, 0, st, bytes, w, *tb, ntiles, n, starts, out_np);
+  if (tb && !sb) hipLaunchKernelGGL((k_compact<true, false>), g, b, 0, st, bytes, w, *tb, ntiles, n, starts, out_np);
+  if (!tb && sb)
+    hipLaunchKernelGGL((k_compact<false, true>), g, b, 0, st, bytes, w, Tables{}, ntiles, n, starts, out_np);
+  if (!tb && !sb)
+    hipLaunchKernelGGL((k_compact<false, false>), g, b, 0, st, bytes, w, Tables{}, ntiles, n, starts, out_np);
   prof_mark("k_compact", st);
   return hipGetLastError();
 }
@@ -2111,14 +2155,28 @@ hipError_t launch_bpe_emit(const uint8_t* bytes, int64_t n, const Tables& tb, co
   const int g_merge = capped_grid(n, 256, 2048);
   hipLaunchKernelGGL(k_bpe_merge, dim3(g_merge), dim3(MERGE_THREADS), 0, st, bytes, w, tb); prof_mark("k_bpe_merge", st);
   const int ntiles = ceil_div(n, TILE);
+  const bool sb = ntiles > SB_MIN_TILES;  // the two-level tile prefix, as in pre-tokenization
+  if (sb) {
+    hipLaunchKernelGGL(k_sb_sums, dim3(ceil_div(ntiles, SB_TILES)), dim3(256), 0, st, w.tile_tok, ntiles, ~0u,
+                       w.sb_tok, nullptr);
+    prof_mark("k_sb_sums", st);
+  }
+  const dim3 g(ntiles), b(EMIT_THREADS);
   if (out_starts) {
     hipLaunchKernelGGL(k_chunk_sums, dim3(capped_grid(n, HUGE_CHUNK, 1024)), dim3(EMIT_THREADS), 0, st, w, tb.tok_len);
     prof_mark("k_chunk_sums", st);
-    hipLaunchKernelGGL(k_emit<true>, dim3(ntiles), dim3(EMIT_THREADS), 0, st, w, ntiles, out_ids, out_n, (uint32_t)n,
-                       out_starts, tb.tok_len);
+    if (sb)
+      hipLaunchKernelGGL((k_emit<true, true>), g, b, 0, st, w, ntiles, out_ids, out_n, (uint32_t)n, out_starts,
+                         tb.tok_len);
+    else
+      hipLaunchKernelGGL((k_emit<true, false>), g, b, 0, st, w, ntiles, out_ids, out_n, (uint32_t)n, out_starts,
+                         tb.tok_len);
   } else {
-    hipLaunchKernelGGL(k_emit<false>, dim3(ntiles), dim3(EMIT_THREADS), 0, st, w, ntiles, out_ids, out_n, (uint32_t)n,
-                       nullptr, nullptr);
+    if (sb)
+      hipLaunchKernelGGL((k_emit<false, true>), g, b, 0, st, w, ntiles, out_ids, out_n, (uint32_t)n, nullptr, nullptr);
+    else
+      hipLaunchKernelGGL((k_emit<false, false>), g, b, 0, st, w, ntiles, out_ids, out_n, (uint32_t)n, nullptr,
+                         nullptr);
   }
   prof_mark("k_emit", st);
   return hipGetLastError();
