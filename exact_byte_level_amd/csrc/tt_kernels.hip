@@ -1411,24 +1411,59 @@ __device__ void big_merge(const Work& w, const Tables& tb, uint32_t p, int32_t s
   if (threadIdx.x == 0) atomicAdd(&w.tile_tok[s / TILE], (uint32_t)cnt);
 }
 
+// The last tile before t with a pre-token start, scanning tiles [lo, t)
+// down 64 at a time, or -1; the same in every lane.
+__device__ __forceinline__ int last_tile_in(const Work& w, int lo, int t, uint32_t cmask) {
+  const int lane = (int)(threadIdx.x & 63u);
+  for (int b = t - 1; b >= lo; b -= 64) {
+    const int bb = b - lane;
+    const uint64_t nz = __ballot(bb >= lo && (w.tile_cnt[bb] & cmask) != 0u);
+    if (nz) return b - (__ffsll((unsigned long long)nz) - 1);
+  }
+  return -1;
+}
+
+// The first tile in (t, hi) with a pre-token start, or hi.
+__device__ __forceinline__ int first_tile_in(const Work& w, int t, int hi, uint32_t cmask) {
+  const int lane = (int)(threadIdx.x & 63u);
+  for (int b = t + 1; b < hi; b += 64) {
+    const int bb = b + lane;
+    const uint64_t nz = __ballot(bb < hi && (w.tile_cnt[bb] & cmask) != 0u);
+    if (nz) return b + __ffsll((unsigned long long)nz) - 1;
+  }
+  return hi;
+}
+
 // The last pre-token start before tile t (t >= 1; byte 0 always starts one),
-// from the tile counts and start bits; the same in every lane.
+// from the tile counts and start bits; the same in every lane.  With SB the
+// search skips whole runs of SB_TILES tiles without a start (their sums are
+// zero), so its length does not grow with the input.
+template <bool SB>
 __device__ int32_t last_start_before(const Work& w, int t, uint32_t cmask) {
   const int lane = (int)(threadIdx.x & 63u);
-  for (int b = t - 1; b >= 0; b -= 64) {
-    const int bb = b - lane;
-    const uint64_t nz = __ballot(bb >= 0 && (w.tile_cnt[bb] & cmask) != 0u);
-    if (nz) {
-      const int f = b - (__ffsll((unsigned long long)nz) - 1);
-      for (int q = PT_THREADS - 64; q >= 0; q -= 64) {
-        const uint32_t fl = w.flags[(int64_t)f * PT_THREADS + q + lane];
-        const uint64_t fm = __ballot(fl != 0u);
-        if (fm) {
-          const int l = 63 - __clzll((long long)fm);
-          const uint32_t flw = (uint32_t)__builtin_amdgcn_readlane((int)fl, l);
-          return (int32_t)((int64_t)f * TILE + PT_CHUNK * (q + l) + 31 - __clz(flw));
-        }
+  int f;
+  if (SB) {
+    const int r0 = t / SB_TILES * SB_TILES;
+    f = last_tile_in(w, r0, t, cmask);
+    if (f < 0) {
+      int j = -1;
+      for (int b = t / SB_TILES - 1; b >= 0 && j < 0; b -= 64) {
+        const uint64_t nz = __ballot(b - lane >= 0 && w.sb_cnt[b - lane] != 0u);
+        if (nz) j = b - (__ffsll((unsigned long long)nz) - 1);
       }
+      f = j < 0 ? -1 : last_tile_in(w, j * SB_TILES, (j + 1) * SB_TILES, cmask);
+    }
+  } else {
+    f = last_tile_in(w, 0, t, cmask);
+  }
+  if (f < 0) return 0;
+  for (int q = PT_THREADS - 64; q >= 0; q -= 64) {
+    const uint32_t fl = w.flags[(int64_t)f * PT_THREADS + q + lane];
+    const uint64_t fm = __ballot(fl != 0u);
+    if (fm) {
+      const int l = 63 - __clzll((long long)fm);
+      const uint32_t flw = (uint32_t)__builtin_amdgcn_readlane((int)fl, l);
+      return (int32_t)((int64_t)f * TILE + PT_CHUNK * (q + l) + 31 - __clz(flw));
     }
   }
   return 0;
@@ -1437,6 +1472,8 @@ __device__ int32_t last_start_before(const Work& w, int t, uint32_t cmask) {
 // The first pre-token start after tile t, else n; nc1 = the count of tile
 // t + 1 + lane and fl1 = the start bits of tile t + 1's thread lane, loaded
 // ahead.  Every wavefront runs the same search; the ballots keep it uniform.
+// With SB it skips whole runs of SB_TILES tiles without a start.
+template <bool SB>
 __device__ int32_t first_start_after(const Work& w, int t, int ntiles, int64_t n, uint32_t cmask, uint32_t nc1,
                                      uint32_t fl1) {
   const int lane = (int)(threadIdx.x & 63u);
@@ -1448,20 +1485,30 @@ __device__ int32_t first_start_after(const Work& w, int t, int ntiles, int64_t n
     const uint32_t flw = (uint32_t)__builtin_amdgcn_readlane((int)fl1, l);
     return (int32_t)((int64_t)(t + 1) * TILE + PT_CHUNK * l + __ffs(flw) - 1);
   }
-  for (int b = t + 1; b < ntiles; b += 64) {
-    const int bb = b + lane;
-    const uint64_t nz = __ballot(bb < ntiles && (w.tile_cnt[bb] & cmask) != 0u);
-    if (nz) {
-      const int f = b + __ffsll((unsigned long long)nz) - 1;
-      for (int q = 0; q < PT_THREADS; q += 64) {
-        const uint32_t fl = w.flags[(int64_t)f * PT_THREADS + q + lane];
-        const uint64_t fm = __ballot(fl != 0u);
-        if (fm) {
-          const int l = __ffsll((unsigned long long)fm) - 1;
-          const uint32_t flw = (uint32_t)__builtin_amdgcn_readlane((int)fl, l);
-          return (int32_t)((int64_t)f * TILE + PT_CHUNK * (q + l) + __ffs(flw) - 1);
-        }
+  int f;
+  if (SB) {
+    const int r1 = min(ntiles, (t / SB_TILES + 1) * SB_TILES);
+    f = first_tile_in(w, t, r1, cmask);
+    if (f >= r1) {
+      const int nsb = (ntiles + SB_TILES - 1) / SB_TILES;
+      int j = nsb;
+      for (int b = t / SB_TILES + 1; b < nsb && j >= nsb; b += 64) {
+        const uint64_t nz = __ballot(b + lane < nsb && w.sb_cnt[b + lane] != 0u);
+        if (nz) j = b + __ffsll((unsigned long long)nz) - 1;
       }
+      f = j >= nsb ? ntiles : first_tile_in(w, j * SB_TILES - 1, min(ntiles, (j + 1) * SB_TILES), cmask);
+    }
+  } else {
+    f = first_tile_in(w, t, ntiles, cmask);
+  }
+  if (f >= ntiles) return (int32_t)n;
+  for (int q = 0; q < PT_THREADS; q += 64) {
+    const uint32_t fl = w.flags[(int64_t)f * PT_THREADS + q + lane];
+    const uint64_t fm = __ballot(fl != 0u);
+    if (fm) {
+      const int l = __ffsll((unsigned long long)fm) - 1;
+      const uint32_t flw = (uint32_t)__builtin_amdgcn_readlane((int)fl, l);
+      return (int32_t)((int64_t)f * TILE + PT_CHUNK * (q + l) + __ffs(flw) - 1);
     }
   }
   return (int32_t)n;
@@ -1545,8 +1592,8 @@ __global__ __launch_bounds__(PT_THREADS) __attribute__((amdgpu_waves_per_eu(6)))
     // and this tile starts a group, take the group's share of its first round
     if (threadIdx.x == 0) w.tile_tok[t] = 0u;
     if (t % SHARE_TILES == 0) {
-      const int32_t sp = last_start_before(w, t, cmask);
-      const int32_t ep = first_start_after(w, t, ntiles, n, cmask, nc1, fl1);
+      const int32_t sp = last_start_before<SB>(w, t, cmask);
+      const int32_t ep = first_start_after<SB>(w, t, ntiles, n, cmask, nc1, fl1);
       if (ep - sp > BIG_BYTES &&
           big_share(bytes, w, tb, sp, ep, (int32_t)t0, (int32_t)min<int64_t>(ep, t0 + SHARE_TILES * TILE), t0, big))
         big_merge(w, tb, base - 1, sp, ep, big);
@@ -1554,7 +1601,7 @@ __global__ __launch_bounds__(PT_THREADS) __attribute__((amdgpu_waves_per_eu(6)))
     return;
   }
   // end of the last piece: the first start after this tile, else n
-  const int32_t e_next = first_start_after(w, t, ntiles, n, cmask, nc1, fl1);
+  const int32_t e_next = first_start_after<SB>(w, t, ntiles, n, cmask, nc1, fl1);
   if (threadIdx.x == 0) sst[tot] = e_next;
   // the tile's bytes plus CACHE_MAXLEN, for single bytes and table keys
   if (threadIdx.x < (TILE + CACHE_MAXLEN) / 16) {
@@ -1645,7 +1692,7 @@ __global__ __launch_bounds__(PT_THREADS) __attribute__((amdgpu_waves_per_eu(6)))
   int32_t sp = 0;
   bool head_last = false;
   if (t % SHARE_TILES == 0 && t > 0 && fs > t0 && (w.tile_cnt[t - 1] & cmask) == 0u) {
-    sp = last_start_before(w, t, cmask);
+    sp = last_start_before<SB>(w, t, cmask);
     if (fs - sp > BIG_BYTES) head_last = big_share(bytes, w, tb, sp, fs, (int32_t)t0, fs, t0, big);
   }
   const int32_t ls = (int32_t)uniform((uint32_t)sst[tot - 1]);

@@ -1,4 +1,5 @@
-"""Inputs at the library's size limit (TT_MAX_BYTES - 1 bytes, 1 GiB) on the GPU.
+"""Inputs at the library's size limit (TT_MAX_BYTES - 1 bytes, 1 GiB) on the GPU,
+and a 64 MiB single pre-token.
 
 The text is K copies of a 1 MB mix whose end and start meet at a pre-token
 boundary (checked with the oracle: the encode of two copies is the encode of
@@ -17,7 +18,7 @@ pytestmark = pytest.mark.gpu
 
 import exact_byte_level_amd as tt  # noqa: E402
 from oracle.bpe import Vocab, encode as oracle_encode  # noqa: E402
-from oracle.pretok import GPT2  # noqa: E402
+from oracle.pretok import CL100K, GPT2  # noqa: E402
 from synth import mix_text  # noqa: E402
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
@@ -57,6 +58,36 @@ def test_largest_input_bit_exact():
     want = torch.tensor(one, dtype=torch.int32, device="cuda")
     assert bool((got == want).all())
     del ids, got, x
+    torch.cuda.empty_cache()
+
+
+def test_giant_piece_in_a_large_input():
+    # one pre-token of 64 MiB + a ragged tail of letters: its first round is
+    # shared over thousands of tile groups, the searches for its ends cross
+    # dozens of runs of 2,048 tiles, and its merges run on one workgroup.
+    # Closed forms: with a+a, aa+aa, ... up to a^(2^K) the ids are the binary
+    # expansion of the length; with a trained table that has no aa merge, the
+    # bytes themselves.
+    length = (64 << 20) + 12_345
+    x = torch.full((length,), 97, dtype=torch.uint8, device="cuda")
+    K = 12
+    merges = np.asarray([(97, 97)] + [(256 + i, 256 + i) for i in range(K - 1)], dtype=np.int32)
+    tt.load(merges, pattern_id=CL100K)
+    say("giant piece: %d letters, doubling-chain table" % length)
+    ids = tt.encode(x)
+    torch.cuda.synchronize()
+    rem = length & ((1 << K) - 1)
+    tail = [97 if bit == 0 else 256 + bit - 1 for bit in range(K - 1, -1, -1) if rem & (1 << bit)]
+    head = length >> K
+    assert ids.numel() == head + len(tail)
+    assert bool((ids[:head] == 256 + K - 1).all())
+    assert ids[head:].cpu().tolist() == tail
+    tt.load(np.load(os.path.join(ROOT, "data", "vocab_c3.npy")), pattern_id=CL100K)
+    say("giant piece: %d letters, trained table without aa" % length)
+    ids = tt.encode(x)
+    torch.cuda.synchronize()
+    assert ids.numel() == length and bool((ids == 97).all())
+    del ids, x
     torch.cuda.empty_cache()
 
 
