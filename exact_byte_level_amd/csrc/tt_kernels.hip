@@ -1250,11 +1250,17 @@ __device__ int big_rounds(const Work& w, const Tables& tb, uint32_t p, int32_t s
   uint32_t* I = reinterpret_cast<uint32_t*>(w.tmp_ids) + s;
   uint32_t* R = w.tmp_rank + s;
   uint32_t lx = RANK_NONE, ly = RANK_NONE, lr = RANK_NONE;  // the last pair looked up and its rank
+  int first = 0;  // a position at or before the first pair of rank rmin
   while (rmin != RANK_NONE) {
     const uint32_t T = 256u + rmin;
     uint32_t cin = 0, nmin = RANK_NONE;
-    int out = 0;
-    for (int base = 0; base < m; base += BIG_STEP) {
+    int nfirst = 0x7FFFFFFF;  // where this thread's least new rank first occurs
+    // the steps before the one holding the pair just before the first pair
+    // of rank rmin merge nothing, move nothing and keep their ranks: the
+    // sweep starts there, with carry 0
+    const int base0 = max(first - 1, 0) / BIG_STEP * BIG_STEP;
+    int out = base0;
+    for (int base = base0; base < m; base += BIG_STEP) {
       uint32_t pid[BIG_E + 1], prk[BIG_E + 1];
 #pragma unroll
       for (int j = 0; j <= BIG_E; ++j) {
@@ -1327,15 +1333,28 @@ __device__ int big_rounds(const Work& w, const Tables& tb, uint32_t p, int32_t s
         }
         I[o] = nid;
         R[o] = nr;
+        if (nr < nmin) {
+          nmin = nr;
+          nfirst = o;
+        }
         ++o;
-        nmin = min(nmin, nr);
       }
       out += (int)tot;
       cin = uniform(sm.sh[4]);
       __syncthreads();  // the staged step is read; the next one may overwrite it
     }
     m = (int)uniform((uint32_t)out);
+    // the ranks of the skipped steps count for the next minimum (and come
+    // before every rewritten position)
+    for (int k = tid; k < base0; k += 256) {
+      const uint32_t r = R[k];
+      if (r < nmin || (r == nmin && k < nfirst)) {
+        nmin = r;
+        nfirst = k;
+      }
+    }
     rmin = uniform(block_min(nmin, sm.sh + 8));
+    first = (int)uniform(block_min(nmin == rmin ? (uint32_t)nfirst : 0x7FFFFFFFu, sm.sh + 8));
   }
   if (tid == 0) {
     w.piece_cnt[p] = m;
