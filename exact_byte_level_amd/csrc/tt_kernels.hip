@@ -1231,6 +1231,20 @@ __device__ __forceinline__ uint32_t big_word(const uint32_t* base, uint32_t k) {
   return *reinterpret_cast<const uint32_t*>(reinterpret_cast<const char*>(base) + k * 4u);
 }
 
+// This thread's share of sweep step base (positions base + tid + 256 j, and
+// two more on the right in threads 0 and 1): ids, and ranks of the pairs
+// they start (none past the end).
+__device__ __forceinline__ void big_load_step(const uint32_t* I, const uint32_t* R, int base, int m, int tid,
+                                              uint32_t (&pid)[BIG_E + 1], uint32_t (&prk)[BIG_E + 1]) {
+#pragma unroll
+  for (int j = 0; j <= BIG_E; ++j) {
+    const uint32_t k = (uint32_t)(base + tid + 256 * j);
+    const bool in = j < BIG_E || tid < 2;
+    pid[j] = in && (int)k < m ? big_word(I, k) : 0u;
+    prk[j] = in && (int)k + 1 < m ? big_word(R, k) : RANK_NONE;
+  }
+}
+
 // Rounds 1, 2, ... of piece p = bytes [s, s + m), longer than BIG_BYTES, by
 // one workgroup of 256 threads (s, m and rmin, the least pair rank left by the
 // first round, are the same in every thread): the same exact global-minimum
@@ -1260,15 +1274,11 @@ __device__ int big_rounds(const Work& w, const Tables& tb, uint32_t p, int32_t s
     // sweep starts there, with carry 0
     const int base0 = max(first - 1, 0) / BIG_STEP * BIG_STEP;
     int out = base0;
+    // the loads of step base + BIG_STEP are issued while step base is worked
+    // on: a step writes only below its own end, never into the next step
+    uint32_t pid[BIG_E + 1], prk[BIG_E + 1];
+    big_load_step(I, R, base0, m, tid, pid, prk);
     for (int base = base0; base < m; base += BIG_STEP) {
-      uint32_t pid[BIG_E + 1], prk[BIG_E + 1];
-#pragma unroll
-      for (int j = 0; j <= BIG_E; ++j) {
-        const uint32_t k = (uint32_t)(base + tid + 256 * j);
-        const bool in = j < BIG_E || tid < 2;
-        pid[j] = in && (int)k < m ? big_word(I, k) : 0u;
-        prk[j] = in && (int)k + 1 < m ? big_word(R, k) : RANK_NONE;
-      }
 #pragma unroll
       for (int j = 0; j <= BIG_E; ++j) {
         if (j < BIG_E || tid < 2) {
@@ -1277,6 +1287,7 @@ __device__ int big_rounds(const Work& w, const Tables& tb, uint32_t p, int32_t s
         }
       }
       __syncthreads();
+      if (base + BIG_STEP < m) big_load_step(I, R, base + BIG_STEP, m, tid, pid, prk);
       const int j0 = tid * BIG_E, k0 = base + j0;
       uint32_t eq = 0;
 #pragma unroll
@@ -1346,11 +1357,18 @@ __device__ int big_rounds(const Work& w, const Tables& tb, uint32_t p, int32_t s
     m = (int)uniform((uint32_t)out);
     // the ranks of the skipped steps count for the next minimum (and come
     // before every rewritten position)
-    for (int k = tid; k < base0; k += 256) {
-      const uint32_t r = R[k];
-      if (r < nmin || (r == nmin && k < nfirst)) {
-        nmin = r;
-        nfirst = k;
+    // (eight loads in flight per thread)
+    for (int k0 = tid; k0 < base0; k0 += 256 * 8) {
+      uint32_t r[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) r[u] = k0 + 256 * u < base0 ? big_word(R, (uint32_t)(k0 + 256 * u)) : RANK_NONE;
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int k = k0 + 256 * u;
+        if (r[u] < nmin || (r[u] == nmin && k < nfirst)) {
+          nmin = r[u];
+          nfirst = k;
+        }
       }
     }
     rmin = uniform(block_min(nmin, sm.sh + 8));
