@@ -93,6 +93,8 @@ class ShadowVerifier:
         self._checked = 0
         self._texts = 0
         self._mismatches = 0
+        self._errors = 0
+        self.last_error = ""
         self._q = queue.Queue(maxsize=max(1, int(max_pending)))
         self._closed = False
         self._worker = threading.Thread(target=self._run, name="tt-shadow", daemon=True)
@@ -175,6 +177,10 @@ class ShadowVerifier:
                 if ev is not None:
                     ev.synchronize()
                 self._check(call, *[None if p is None else _to_numpy(p) for p in parts])
+            except Exception as e:  # noqa: BLE001 - the thread must outlive a failing hook or write
+                with self._lock:
+                    self._errors += 1
+                    self.last_error = "%s: %s" % (type(e).__name__, e)
             finally:
                 self._q.task_done()
 
@@ -232,10 +238,14 @@ class ShadowVerifier:
 
     def stats(self):
         """Counts so far: calls seen, calls sampled, sampled calls dropped
-        (queue full), calls checked, texts checked, texts that mismatched."""
+        (queue full), calls checked, texts checked, texts that mismatched, and
+        checks that failed in the verifier itself (a raising ``on_mismatch``
+        hook, an unwritable ``quarantine_dir``; the last one is kept in
+        ``last_error``)."""
         with self._lock:
             return {"calls": self._calls, "sampled": self._sampled, "dropped": self._dropped,
-                    "checked": self._checked, "texts": self._texts, "mismatches": self._mismatches}
+                    "checked": self._checked, "texts": self._texts, "mismatches": self._mismatches,
+                    "errors": self._errors}
 
     def close(self):
         """Run the queued checks, then stop the background thread."""

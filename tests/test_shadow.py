@@ -231,3 +231,16 @@ def test_rate_zero_checks_nothing():
         assert sv.stats()["sampled"] == 0 and sv.quarantine == []
     with pytest.raises(ValueError):
         ShadowVerifier(lambda b: [], rate=1.5)
+
+
+def test_failing_hook_does_not_stop_the_checks():
+    def hook(sample):
+        raise OSError("disk full")
+
+    with ShadowVerifier(lambda b: [1], rate=1.0, on_mismatch=hook, encoder=lambda d: _ids([2])) as sv:
+        for _ in range(3):
+            sv.encode(_u8(b"a"))
+        sv.drain()
+        st = sv.stats()
+    assert st["checked"] == 3 and st["mismatches"] == 3
+    assert st["errors"] == 3 and "disk full" in sv.last_error and len(sv.quarantine) == 3
