@@ -1274,11 +1274,9 @@ __device__ int big_rounds(const Work& w, const Tables& tb, uint32_t p, int32_t s
     // sweep starts there, with carry 0
     const int base0 = max(first - 1, 0) / BIG_STEP * BIG_STEP;
     int out = base0;
-    // the loads of step base + BIG_STEP are issued while step base is worked
-    // on: a step writes only below its own end, never into the next step
-    uint32_t pid[BIG_E + 1], prk[BIG_E + 1];
-    big_load_step(I, R, base0, m, tid, pid, prk);
     for (int base = base0; base < m; base += BIG_STEP) {
+      uint32_t pid[BIG_E + 1], prk[BIG_E + 1];
+      big_load_step(I, R, base, m, tid, pid, prk);
 #pragma unroll
       for (int j = 0; j <= BIG_E; ++j) {
         if (j < BIG_E || tid < 2) {
@@ -1287,11 +1285,18 @@ __device__ int big_rounds(const Work& w, const Tables& tb, uint32_t p, int32_t s
         }
       }
       __syncthreads();
-      if (base + BIG_STEP < m) big_load_step(I, R, base + BIG_STEP, m, tid, pid, prk);
       const int j0 = tid * BIG_E, k0 = base + j0;
+      // this thread's ids and ranks (and the two ids after them), read once:
+      // the loads' latency hides behind the scans below
+      uint32_t own_id[BIG_E + 2], own_rk[BIG_E + 2];
+#pragma unroll
+      for (int j = 0; j < BIG_E + 2; ++j) {
+        own_id[j] = sm.id[big_slot(j0 + j)];
+        own_rk[j] = sm.rk[big_slot(j0 + j)];
+      }
       uint32_t eq = 0;
 #pragma unroll
-      for (int j = 0; j < BIG_E + 2; ++j) eq |= (sm.rk[big_slot(j0 + j)] == rmin ? 1u : 0u) << j;
+      for (int j = 0; j < BIG_E + 2; ++j) eq |= (own_rk[j] == rmin ? 1u : 0u) << j;
       // merge starts of this thread's positions for carry in 0 (msA) and 1 (msB)
       uint32_t msA = 0, msB = 0, a = 0, b = 1;
 #pragma unroll
@@ -1323,13 +1328,14 @@ __device__ int big_rounds(const Work& w, const Tables& tb, uint32_t p, int32_t s
       if (tid == 255) sm.sh[4] = lastms;
       uint32_t tot;
       int o = out + (int)block_excl_sum(__popc(keep), sm.sh + 8, &tot);
-      for (uint32_t kb = keep; kb; kb &= kb - 1) {
-        const int j = __ffs(kb) - 1;
+#pragma unroll
+      for (int j = 0; j < BIG_E; ++j) {
+        if (!((keep >> j) & 1u)) continue;
         const int k = k0 + j;
         const bool m0 = (msx >> j) & 1u, m1 = (msx >> (j + 1)) & 1u, m2 = (msx >> (j + 2)) & 1u;
-        const uint32_t nid = m0 ? T : sm.id[big_slot(j0 + j)];
+        const uint32_t nid = m0 ? T : own_id[j];
         const bool has_next = m0 ? (k + 2 < m) : (k + 1 < m);
-        const uint32_t nxt = m0 ? (m2 ? T : sm.id[big_slot(j0 + j + 2)]) : (m1 ? T : sm.id[big_slot(j0 + j + 1)]);
+        const uint32_t nxt = m0 ? (m2 ? T : own_id[j + 2]) : (m1 ? T : own_id[j + 1]);
         uint32_t nr = RANK_NONE;
         if (has_next && (m0 || m1)) {
           // (merged ids are never bytes; inside runs the same pair recurs)
@@ -1340,7 +1346,7 @@ __device__ int big_rounds(const Work& w, const Tables& tb, uint32_t p, int32_t s
           }
           nr = lr;
         } else if (has_next) {
-          nr = sm.rk[big_slot(j0 + j)];
+          nr = own_rk[j];
         }
         I[o] = nid;
         R[o] = nr;
