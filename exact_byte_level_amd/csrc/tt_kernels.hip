@@ -1286,8 +1286,8 @@ __device__ int big_rounds(const Work& w, const Tables& tb, uint32_t p, int32_t s
       }
       __syncthreads();
       const int j0 = tid * BIG_E, k0 = base + j0;
-      // this thread's ids and ranks (and the two ids after them), read once:
-      // the loads' latency hides behind the scans below
+      // this thread's ids and ranks and the two after them, read once (the
+      // ids are needed only after the scans below, which hide their latency)
       uint32_t own_id[BIG_E + 2], own_rk[BIG_E + 2];
 #pragma unroll
       for (int j = 0; j < BIG_E + 2; ++j) {
