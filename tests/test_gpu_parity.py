@@ -310,6 +310,24 @@ def test_long_random_piece_many_rounds():
         assert gpu_encode(data).tolist() == oracle_encode(data, v, GPT2)
 
 
+@pytest.mark.parametrize("letters", [100_000, 300_000])
+def test_long_random_words_timed_sizes(letters):
+    # the random-letter words whose encode times are reported (seed 5, the
+    # 12-letter alphabet, 50K merges), bit-exact at full length, and one in a
+    # cl100k-style text between other words
+    v = load("c2", GPT2)
+    rng = random.Random(5)
+    word = "".join(rng.choice("etaoinshrdlu") for _ in range(letters)).encode()
+    say("random word of %d letters" % letters)
+    got = gpu_encode(word)
+    want = np.asarray(oracle_encode(word, v, GPT2), dtype=np.int32)
+    assert np.array_equal(got, want)
+    v3 = load("c3", CL100K)
+    data = b"begin " + word[: letters // 3] + b" end\n" + mix_text(20_000, 49)
+    say("random word of %d letters in a cl100k-style text" % (letters // 3))
+    assert np.array_equal(gpu_encode(data), np.asarray(oracle_encode(data, v3, CL100K, {}), dtype=np.int32))
+
+
 def test_long_pieces_in_a_batch():
     v = load("c3", CL100K)
     texts = [b"a" * 2500, b"b" * 30_000, b"", b" " * 20_000 + b"x", code_text(3000, 48), b"c" * 2049,
