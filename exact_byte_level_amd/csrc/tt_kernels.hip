@@ -1808,7 +1808,8 @@ __global__ __launch_bounds__(MERGE_THREADS) __attribute__((amdgpu_waves_per_eu(8
 
 // ------------------------------------------------------------------ emission
 
-constexpr uint32_t HUGE_CHUNK = 16384;  // tokens per grid work item of a huge piece
+constexpr uint32_t HUGE_CHUNK = 4096;  // tokens per grid work item of a huge piece
+static_assert(HUGE_CHUNK % (EMIT_THREADS * 8) == 0, "a chunk is whole passes of 8 tokens per thread");
 
 // Byte-offset export only: chunk k of a huge piece (tokens [k * HUGE_CHUNK,
 // (k + 1) * HUGE_CHUNK)) gets its byte length written to tmp_rank[s + k] (s =
@@ -1940,7 +1941,20 @@ __global__ __launch_bounds__(EMIT_THREADS) void k_emit(Work w, int ntiles, int32
     for (uint32_t ch = first; ch < nch; ch += gridDim.x) {
       const uint32_t k1 = min(min(cc, (ch + 1) * HUGE_CHUNK), cap - min(cap, dst));  // never past the output
       if (!OFFS) {
-        for (uint32_t k = ch * HUGE_CHUNK + threadIdx.x; k < k1; k += EMIT_THREADS) out_ids[dst + k] = w.tmp_ids[src + k];
+        // eight loads in flight per thread, then their stores
+        for (uint32_t k0 = ch * HUGE_CHUNK; k0 < k1; k0 += EMIT_THREADS * 8) {
+          int32_t v[8];
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            const uint32_t k = k0 + EMIT_THREADS * j + threadIdx.x;
+            v[j] = k < k1 ? w.tmp_ids[src + k] : 0;
+          }
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            const uint32_t k = k0 + EMIT_THREADS * j + threadIdx.x;
+            if (k < k1) out_ids[dst + k] = v[j];
+          }
+        }
         continue;
       }
       // byte offset of the chunk's first token: the earlier chunks' lengths

@@ -171,7 +171,7 @@ int tt_pretokenize(const uint8_t* dev_bytes, int64_t n, const int64_t* dev_offse
  *              On a data error out_ids and out_starts are unspecified.
  * Same enqueue-only contract as tt_encode.  Each token's byte length comes
  * from a table built by tt_load_bpe; the extra device work over tt_encode is
- * one gather per token and, for a pre-token of more than 16,384 tokens, one
+ * one gather per token and, for a pre-token of more than 4,096 tokens, one
  * extra read of its ids.
  */
 int tt_encode_offsets(const uint8_t* dev_bytes, int64_t n, const int64_t* dev_offsets, int32_t n_seqs,

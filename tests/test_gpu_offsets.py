@@ -4,7 +4,7 @@ TokTier summary page, Path C of §8 and Appendix E: the GPU returns each
 token's byte span along with its id.  Every case compares the ids and the T+1
 byte offsets with oracle.bpe.encode_offsets element by element, and the ids
 with tt_encode's.  The cases cover every copy path of the emission kernel
-(pieces of <= 8 tokens, of <= 64, and longer pieces cut into 16,384-token
+(pieces of <= 8 tokens, of <= 64, and longer pieces cut into 4,096-token
 chunks, with chunk counts around the chunk edges), batches with empty texts,
 multi-byte text, no merges, and the data errors.
 """
@@ -24,7 +24,7 @@ from synth import code_text, mix_text  # noqa: E402
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
-CHUNK = 16384  # tokens per work item of a long piece in the emission kernel
+CHUNK = 4096  # tokens per work item of a long piece in the emission kernel
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -100,7 +100,8 @@ def test_offsets_batch_with_empty_texts():
     check(b"".join(texts), v, CL100K, offs)
 
 
-@pytest.mark.parametrize("run", [8, 9, 64, 65, CHUNK - 1, CHUNK, CHUNK + 1, 2 * CHUNK, 2 * CHUNK + 5, 3 * CHUNK + 100])
+@pytest.mark.parametrize("run", [8, 9, 64, 65, CHUNK - 1, CHUNK, CHUNK + 1, 2 * CHUNK, 2 * CHUNK + 5, 3 * CHUNK + 100,
+                                 16 * CHUNK + 7])
 def test_offsets_copy_paths_and_chunk_edges(run):
     # with the c3 vocabulary "aa" is no merge, so a run of r letters a is one
     # pre-token of r one-byte tokens: r picks the copy path
