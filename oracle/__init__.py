@@ -15,12 +15,14 @@ What it follows (TokTier, arXiv:2607.29678v1, summary page):
     from tok(A+B)).
 
 Modules
-  pretok  -- the two ordered rule sets (GPT-2-style, cl100k-style) and split()
-  bpe     -- classic lowest-rank-first merge loop, a heap/linked-list form with
-             the same semantics, the naive rank-order brute force, decode, and the
-             byte offset of every token
+  pretok  -- the ordered rule sets and split(); split_bytes() (byte offsets of
+             the pieces of one text) and piece_starts_batch() (a batch of
+             independent texts)
+  bpe     -- the merge-table container Vocab, the classic lowest-rank-first
+             merge loop, a heap/linked-list form with the same semantics, the
+             naive rank-order brute force, encode / encode_batch, decode, and
+             the byte offset of every token
   train   -- the BPE trainer that learns merge tables from seeded corpora
-  vocab   -- merge-table container and (de)serialisation
 
 Parity status: every function here is pinned by ``tests/test_oracle_*.py``
 (worked examples, brute force against independent formulations, closed forms,

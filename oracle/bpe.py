@@ -64,14 +64,6 @@ class Vocab:
     def size(self):
         return 256 + len(self.merges)
 
-    @classmethod
-    def from_abi(cls, merges, ranks):
-        """Build from the (merges[k], ranks[k]) form: merge k makes 256+ranks[k]."""
-        order = sorted(range(len(ranks)), key=lambda k: int(ranks[k]))
-        if [int(ranks[k]) for k in order] != list(range(len(ranks))):
-            raise ValueError("ranks must be a permutation of 0..M-1")
-        return cls([tuple(merges[k]) for k in order])
-
 
 def bpe_classic(ids, rank):
     """Textbook lowest-rank-first merge loop (leftmost on equal pairs)."""

@@ -18,7 +18,7 @@ import re
 import pytest
 import regex
 
-from oracle.pretok import CL100K, GPT2, PATTERNS, WHITESPACE_CPS, split, split_bytes
+from oracle.pretok import CL100K, GPT2, PATTERNS, WHITESPACE_CPS, piece_starts_batch, split, split_bytes
 from runsplit import piece_starts
 
 EXAMPLES = [
@@ -141,3 +141,60 @@ def test_split_bytes_offsets_and_invalid_utf8():
     for bad in (b"\xff", b"a\x80", b"\xc3", b"\xed\xa0\x80", b"\xc0\xaf", b"\xf4\x90\x80\x80"):
         with pytest.raises(UnicodeDecodeError):
             split_bytes(bad, GPT2)
+
+
+# A batch is a list of independent fresh texts (TokTier summary page, Appendix
+# A.1: the pipeline runs per text; the batch workload's texts are fresh
+# sessions), so piece starts restart at every text and no piece crosses a text
+# end.  Expected starts written by hand, as byte offsets into the
+# concatenation; each text's reading:
+#   0  "ab "   -> "ab" | " "      (the space ends its text: the lookahead rule
+#                                  sees end-of-text; run on into text 2 it
+#                                  would have joined "cd" as " cd")
+#   1  ""      -> nothing
+#   2  "cd"    -> "cd"
+#   3  "é1"    -> "é" (2 bytes) | "1"
+#   4  "  x"   -> " " | " x"
+#   5  "中 "   -> "中" (3 bytes) | " "
+#   6  "1234"  -> GPT-2-style one digit run; cl100k-style "123" | "4"
+BATCH_TEXTS = ["ab ", "", "cd", "é1", "  x", "中 ", "1234"]
+BATCH_STARTS = {
+    GPT2: [0, 2, 3, 5, 7, 8, 9, 11, 14, 15],
+    CL100K: [0, 2, 3, 5, 7, 8, 9, 11, 14, 15, 18],
+}
+
+
+def _batch(texts):
+    data, offs = b"", [0]
+    for t in texts:
+        data += t.encode()
+        offs.append(len(data))
+    return data, offs
+
+
+@pytest.mark.parametrize("pattern_id", [GPT2, CL100K])
+def test_piece_starts_batch_hand_worked(pattern_id):
+    data, offs = _batch(BATCH_TEXTS)
+    assert offs == [0, 3, 3, 5, 8, 11, 15, 19]
+    assert piece_starts_batch(data, offs, pattern_id) == BATCH_STARTS[pattern_id]
+    # the same bytes split as one text: the space of text 0 joins "cd", so no
+    # piece starts at byte 3
+    whole = _starts(split(data.decode(), pattern_id))
+    assert 3 not in [len(data.decode()[:i].encode()) for i in whole]
+
+
+@pytest.mark.parametrize("pattern_id", [GPT2, CL100K])
+def test_piece_starts_batch_random_against_run_decomposition(pattern_id):
+    """Random batches (empty texts, texts ending in whitespace, multibyte chars)
+    against the regex-free run decomposition, applied text by text and shifted
+    by each text's byte offset."""
+    rng = random.Random(31 + pattern_id)
+    for _ in range(400):
+        texts = ["".join(rng.choice(ALPHA2) for _ in range(rng.choice([0, 0, 1, 3, 9, 25])))
+                 for _ in range(rng.randint(1, 8))]
+        data, offs = _batch(texts)
+        want = []
+        for s, t in enumerate(texts):
+            for ci in piece_starts(t, pattern_id):
+                want.append(offs[s] + len(t[:ci].encode()))
+        assert piece_starts_batch(data, offs, pattern_id) == want, texts
