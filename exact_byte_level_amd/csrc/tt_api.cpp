@@ -37,6 +37,7 @@ struct State {
   Tables tb{};
   void* d_ws = nullptr;
   int64_t ws_n = 0;     // bytes of input the workspace is sized for
+  bool ws_fixed = false;  // set by tt_reserve: the workspace is never reallocated
   Work w{};
 };
 
@@ -112,6 +113,7 @@ void release_tables() {
   free_dev(g.d_tok_off);
   free_dev(g.d_tok_bytes);
   g.loaded = false;
+  g.ws_fixed = false;  // graphs captured under a reservation hold the old tables
 }
 
 void release_workspace() {
@@ -119,6 +121,7 @@ void release_workspace() {
   g.d_ws = nullptr;
   g.ws_n = 0;
   g.w = Work{};
+  g.ws_fixed = false;
 }
 
 size_t align_up(size_t v) { return (v + 255) & ~(size_t)255; }
@@ -165,9 +168,12 @@ size_t layout(int64_t n, char* base, Work* w) {
   return off;
 }
 
-// Make the workspace large enough for n input bytes (synchronises if it grows).
+// Make the workspace large enough for n input bytes (synchronises if it
+// grows).  A reserved workspace is never reallocated: graphs captured after
+// tt_reserve hold its address.
 int ensure_workspace(int64_t n) {
   if (n <= g.ws_n && g.d_ws) return TT_OK;
+  if (g.ws_fixed) return TT_ETOOBIG;
   int64_t want = std::max<int64_t>(n, (int64_t)1 << 16);
   want = (want + TILE - 1) / TILE * TILE;
   if (hipDeviceSynchronize() != hipSuccess) return TT_EHIP;
@@ -489,7 +495,10 @@ int tt_reserve(int64_t max_bytes, int32_t max_seqs) {
   if (max_bytes >= TT_MAX_BYTES) return TT_ETOOBIG;
   int rc = check_stream_state();
   if (rc != TT_OK) return rc;
-  return ensure_workspace(max_bytes);
+  g.ws_fixed = false;
+  if ((rc = ensure_workspace(max_bytes)) != TT_OK) return rc;
+  g.ws_fixed = true;
+  return TT_OK;
 }
 
 int tt_encode(const uint8_t* dev_bytes, int64_t n, int32_t* out_ids, int64_t* out_n, hipStream_t stream) {

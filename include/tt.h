@@ -38,7 +38,7 @@ extern "C" {
 #define TT_EUTF8      -5  /* input is not valid UTF-8 (device-side data error) */
 #define TT_ENOTLOADED -6  /* no tokenizer loaded */
 #define TT_EOFFSETS   -7  /* batch offsets not monotone / not ending at n (device-side) */
-#define TT_ETOOBIG    -8  /* size beyond the library's limits */
+#define TT_ETOOBIG    -8  /* size beyond the library's limits or the tt_reserve size */
 #define TT_ESTALE     -9  /* tokenizer replaced since the session was reset (sessions below) */
 
 #define TT_PATTERN_GPT2   0  /* GPT-2-style rules: lower-case contractions, ' ?letters', ' ?digits',
@@ -55,6 +55,12 @@ extern "C" {
 
 /* tt_load_bpe -- load a byte-level BPE merge table and a rule set.
  *
+ * Defines the reference tokenizer every encode must equal id for id
+ * (TokTier summary page, §1.3: outputs identical to the reference
+ * tokenizer, never an approximation): the rule set is the pre-tokenizer G and
+ * the merge table the per-piece BPE E of the factorisation F = E* o G
+ * (Appendix A.1).
+ *
  * merges     host int32[n_merges][2]: (left id, right id) of merge k.
  * ranks      host int32[n_merges]: rank of merge k, a permutation of
  *            0..n_merges-1; merge k makes token id 256 + ranks[k].  May be
@@ -68,6 +74,8 @@ extern "C" {
  * copied; the caller may free them on return.  Builds the device pair-rank
  * tables and the whole-pre-token cache (each token whose own BPE is itself),
  * synchronises the device, and replaces any previously loaded tokenizer.
+ * The old tables are freed, so a HIP graph captured before the call must not
+ * be replayed after it; the call also ends any tt_reserve (see there).
  * Returns TT_OK, TT_EINVAL, TT_ETABLE, TT_ENOMEM or TT_EHIP.
  */
 int tt_load_bpe(const int32_t* merges, const int32_t* ranks, int64_t n_merges, int32_t pattern_id);
@@ -96,14 +104,29 @@ int tt_load_bpe_ex(const int32_t* merges, const int32_t* ranks, int64_t n_merges
                    uint32_t flags);
 
 /* tt_reserve -- size the device workspace for inputs of up to max_bytes
- * bytes and up to max_seqs batch sequences, so that later encodes do no
- * allocation (required before capturing an encode into a HIP graph).
- * Without it, an encode that needs more workspace grows it, which
- * synchronises the device.  Returns TT_OK, TT_EINVAL, TT_ETOOBIG, TT_ENOMEM,
- * TT_EHIP or TT_ENOTLOADED. */
+ * bytes and up to max_seqs batch sequences, and fix it there.
+ *
+ * The pages' single-request path sizes its buffers ahead in buckets so that
+ * the host never reads a count to size a kernel and the whole chain can run
+ * as one captured graph (TokTier summary page, §4.3); this call is that
+ * bucket.  Without a reservation an encode that needs more workspace grows it
+ * (which synchronises the device and frees the old buffer).  After
+ * tt_reserve the workspace is never reallocated: an encode, batch,
+ * pretokenize or session that needs more than max_bytes returns TT_ETOOBIG
+ * instead, so a HIP graph captured after the call stays valid.  The
+ * reservation (and every graph captured under it) ends at the next
+ * tt_reserve, tt_load_bpe / tt_load_bpe_ex or tt_free; a later tt_reserve may
+ * resize.  Returns TT_OK, TT_EINVAL, TT_ETOOBIG, TT_ENOMEM, TT_EHIP or
+ * TT_ENOTLOADED. */
 int tt_reserve(int64_t max_bytes, int32_t max_seqs);
 
 /* tt_encode -- token ids of one text.
+ *
+ * Exact fresh-session tokenization of one text on the GPU (TokTier summary
+ * page, §4): pre-tokenization by run decomposition (§4.1), BPE of every
+ * pre-token (§4.2), ids as a raw device array with no host synchronisation
+ * inside the call (§4.3) and no byte offsets (§4.4; tt_encode_offsets adds
+ * them).
  *
  * dev_bytes  device uint8[n]: the UTF-8 text (caller-owned).
  * n          0 .. TT_MAX_BYTES-1.
@@ -115,12 +138,17 @@ int tt_reserve(int64_t max_bytes, int32_t max_seqs);
  *
  * Enqueues only: no host synchronisation, no allocation once the workspace is
  * large enough (see tt_reserve), graph-capturable.  n == 0 gives *out_n = 0.
- * Returns TT_OK, TT_EINVAL, TT_ETOOBIG, TT_ENOMEM, TT_EHIP or TT_ENOTLOADED.
+ * Returns TT_OK, TT_EINVAL, TT_ETOOBIG (also: n above a tt_reserve),
+ * TT_ENOMEM, TT_EHIP or TT_ENOTLOADED.
  */
 int tt_encode(const uint8_t* dev_bytes, int64_t n, int32_t* out_ids, int64_t* out_n,
               hipStream_t stream);
 
 /* tt_encode_batch -- token ids of n_seqs independent texts in one call.
+ *
+ * Each text is a fresh session tokenized on its own (the factorisation of
+ * TokTier summary page, Appendix A.1, applied text by text), all of them in
+ * one enqueue-only launch chain (§4.3).
  *
  * dev_bytes    device uint8[n]: the texts, concatenated.
  * n            total bytes; must equal dev_offsets[n_seqs].
@@ -257,10 +285,13 @@ int tt_profile(int enable);
  * is off, or TT_EHIP. */
 int tt_profile_read(const char** names, float* ms, int cap);
 
-/* tt_free -- release the tokenizer tables and the workspace (synchronises). */
+/* tt_free -- release the tokenizer tables and the workspace (synchronises);
+ * ends any tt_reserve and invalidates captured graphs.  Housekeeping: no
+ * passage of the pages defines it. */
 void tt_free(void);
 
-/* tt_strerror -- static description of a TT_* code. */
+/* tt_strerror -- static description of a TT_* code.  Housekeeping: no
+ * passage of the pages defines it. */
 const char* tt_strerror(int code);
 
 #ifdef __cplusplus

@@ -157,3 +157,42 @@ def test_graph_replays_of_offsets():
         assert np.array_equal(out[:T].cpu().numpy(), np.asarray(wi, dtype=np.int32)), k
         assert np.array_equal(starts[:T + 1].cpu().numpy(), np.asarray(ws, dtype=np.int32)), k
         eager_noise(k)
+
+
+def test_reserved_workspace_is_never_reallocated():
+    """After tt_reserve the workspace stays where a captured graph points: a
+    larger encode or session is refused (TT_ETOOBIG) rather than served by a
+    new allocation, and the graph still replays correctly afterwards.  The
+    reservation ends at the next tt_reserve or tt_load_bpe."""
+    v = setup("c1", GPT2)
+    say("reserve: graph captured under a %d-byte reservation, larger calls refused" % (4 * N))
+    x = torch.empty(N, dtype=torch.uint8, device="cuda")
+    out = torch.empty(N, dtype=torch.int32, device="cuda")
+    out_n = torch.empty(1, dtype=torch.int64, device="cuda")
+    x.copy_(torch.frombuffer(bytearray(text_of(4)), dtype=torch.uint8))
+    g = capture(lambda: tt.encode_into(x, out, out_n))
+    big_text = mix_text(6 * N, 77)
+    big = torch.frombuffer(bytearray(big_text), dtype=torch.uint8).cuda()
+    with pytest.raises(tt.TTError) as ei:
+        tt.encode(big)
+    assert ei.value.code == tt.TT_ETOOBIG
+    with pytest.raises(tt.TTError) as ei:
+        tt.Session(6 * N)
+    assert ei.value.code == tt.TT_ETOOBIG
+    t = text_of(40)
+    x.copy_(torch.frombuffer(bytearray(t), dtype=torch.uint8))
+    g.replay()
+    torch.cuda.synchronize()
+    want = oracle_encode(t, v, GPT2)
+    T = int(out_n.item())
+    assert T == len(want)
+    assert np.array_equal(out[:T].cpu().numpy(), np.asarray(want, dtype=np.int32))
+    # a new reservation may resize; a new load ends the reservation
+    tt.reserve(8 * N, 1)
+    want_big = np.asarray(oracle_encode(big_text, v, GPT2), dtype=np.int32)
+    assert np.array_equal(tt.encode(big).cpu().numpy(), want_big)
+    v = setup("c1", GPT2)  # reserves 4 * N again
+    with pytest.raises(tt.TTError):
+        tt.encode(big)
+    tt.load(np.load(os.path.join(ROOT, "data", "vocab_c1.npy")), pattern_id=GPT2)
+    assert np.array_equal(tt.encode(big).cpu().numpy(), want_big)
