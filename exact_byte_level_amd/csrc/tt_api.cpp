@@ -168,14 +168,20 @@ size_t layout(int64_t n, char* base, Work* w) {
   return off;
 }
 
+// Input bytes a workspace for n bytes is sized for: n rounded up to whole
+// tiles, at least 64 KiB.
+int64_t workspace_size(int64_t n) {
+  const int64_t want = std::max<int64_t>(n, (int64_t)1 << 16);
+  return (want + TILE - 1) / TILE * TILE;
+}
+
 // Make the workspace large enough for n input bytes (synchronises if it
 // grows).  A reserved workspace is never reallocated: graphs captured after
 // tt_reserve hold its address.
 int ensure_workspace(int64_t n) {
   if (n <= g.ws_n && g.d_ws) return TT_OK;
   if (g.ws_fixed) return TT_ETOOBIG;
-  int64_t want = std::max<int64_t>(n, (int64_t)1 << 16);
-  want = (want + TILE - 1) / TILE * TILE;
+  const int64_t want = workspace_size(n);
   if (hipDeviceSynchronize() != hipSuccess) return TT_EHIP;
   release_workspace();
   size_t bytes = layout(want, nullptr, nullptr);
@@ -495,7 +501,13 @@ int tt_reserve(int64_t max_bytes, int32_t max_seqs) {
   if (max_bytes >= TT_MAX_BYTES) return TT_ETOOBIG;
   int rc = check_stream_state();
   if (rc != TT_OK) return rc;
+  // the workspace takes exactly the reserved size (a larger one left by
+  // earlier calls is given back), so that the limit is the one asked for
   g.ws_fixed = false;
+  if (g.d_ws && g.ws_n != workspace_size(max_bytes)) {
+    if (hipDeviceSynchronize() != hipSuccess) return TT_EHIP;
+    release_workspace();
+  }
   if ((rc = ensure_workspace(max_bytes)) != TT_OK) return rc;
   g.ws_fixed = true;
   return TT_OK;

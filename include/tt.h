@@ -110,10 +110,12 @@ int tt_load_bpe_ex(const int32_t* merges, const int32_t* ranks, int64_t n_merges
  * the host never reads a count to size a kernel and the whole chain can run
  * as one captured graph (TokTier summary page, §4.3); this call is that
  * bucket.  Without a reservation an encode that needs more workspace grows it
- * (which synchronises the device and frees the old buffer).  After
- * tt_reserve the workspace is never reallocated: an encode, batch,
- * pretokenize or session that needs more than max_bytes returns TT_ETOOBIG
- * instead, so a HIP graph captured after the call stays valid.  The
+ * (which synchronises the device and frees the old buffer).  tt_reserve
+ * sizes the workspace for exactly max_bytes, rounded up to a multiple of
+ * 1 KiB and to at least 64 KiB (freeing a larger one left by earlier calls),
+ * and from then on never reallocates it: an encode, batch, pretokenize or
+ * session that needs more returns TT_ETOOBIG instead, so a HIP graph
+ * captured after the call stays valid.  The
  * reservation (and every graph captured under it) ends at the next
  * tt_reserve, tt_load_bpe / tt_load_bpe_ex or tt_free; a later tt_reserve may
  * resize.  Returns TT_OK, TT_EINVAL, TT_ETOOBIG, TT_ENOMEM, TT_EHIP or
