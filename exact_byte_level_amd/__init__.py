@@ -52,6 +52,7 @@ def lib():
         L.tt_load_bpe_ex.argtypes = [vp, vp, i64, i32, ctypes.c_uint32]
         L.tt_reserve.argtypes = [i64, i32]
         L.tt_encode.argtypes = [vp, i64, vp, vp, vp]
+        L.tt_encode_noalloc.argtypes = [vp, i64, vp, vp, vp]
         L.tt_encode_batch.argtypes = [vp, i64, vp, i32, vp, vp, vp]
         L.tt_pretokenize.argtypes = [vp, i64, vp, i32, vp, vp, vp]
         L.tt_encode_offsets.argtypes = [vp, i64, vp, i32, vp, vp, vp, vp]
@@ -68,7 +69,7 @@ def lib():
         L.tt_free.restype = None
         L.tt_strerror.argtypes = [ctypes.c_int]
         L.tt_strerror.restype = ctypes.c_char_p
-        for f in ("tt_load_bpe", "tt_load_bpe_ex", "tt_reserve", "tt_encode", "tt_encode_batch", "tt_pretokenize", "tt_encode_offsets",
+        for f in ("tt_load_bpe", "tt_load_bpe_ex", "tt_reserve", "tt_encode", "tt_encode_noalloc", "tt_encode_batch", "tt_pretokenize", "tt_encode_offsets",
                   "tt_session_create", "tt_session_destroy", "tt_session_reset", "tt_session_append",
                   "tt_session_view", "tt_session_read", "tt_char_class", "tt_profile", "tt_profile_read"):
             getattr(L, f).restype = ctypes.c_int
@@ -129,6 +130,18 @@ def encode(data, stream=None):
     if t < 0:
         raise TTError(t, "tt_encode")
     return out[:t]
+
+
+NOALLOC_MAX_BYTES = 1 << 21
+
+
+def encode_noalloc_into(data, out_ids, out_n, stream=None):
+    """tt_encode_noalloc: as encode_into, but the library allocates nothing
+    (a fixed per-device scratch array; inputs up to NOALLOC_MAX_BYTES)."""
+    n = data.numel()
+    rc = lib().tt_encode_noalloc(data.data_ptr() if n else None, n, out_ids.data_ptr(), out_n.data_ptr(),
+                                 _stream(stream))
+    _check(rc, "tt_encode_noalloc")
 
 
 def encode_batch_into(data, offsets, out_ids, out_offsets, stream=None):

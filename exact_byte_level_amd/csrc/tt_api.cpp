@@ -469,7 +469,10 @@ int tt_load_bpe_ex(const int32_t* merges, const int32_t* ranks, int64_t n_merges
     release_tables();
     return rc;
   }
-  if (hipGetDevice(&g.device) != hipSuccess) {
+  // the device address of the no-alloc scratch array, looked up once here
+  void* scratch_ptr = nullptr;
+  if (hipGetDevice(&g.device) != hipSuccess || scratch_address(&scratch_ptr) != hipSuccess) {
+    (void)hipGetLastError();
     release_tables();
     return TT_EHIP;
   }
@@ -524,6 +527,26 @@ int tt_encode(const uint8_t* dev_bytes, int64_t n, int32_t* out_ids, int64_t* ou
   prof_begin(stream);
   if (launch_pretokenize(dev_bytes, n, nullptr, 1, g.pattern, g.w, g.w.piece_start, nullptr, &g.tb, stream) != hipSuccess ||
       launch_bpe_emit(dev_bytes, n, g.tb, g.w, out_ids, out_n, nullptr, stream) != hipSuccess)
+    return TT_EHIP;
+  return TT_OK;
+}
+
+int tt_encode_noalloc(const uint8_t* dev_bytes, int64_t n, int32_t* out_ids, int64_t* out_n, hipStream_t stream) {
+  std::lock_guard<std::mutex> lock(g_mu);
+  if (n < 0 || !out_n || (n > 0 && (!dev_bytes || !out_ids))) return TT_EINVAL;
+  if (n > TT_NOALLOC_MAX_BYTES) return TT_ETOOBIG;
+  int rc = check_stream_state();
+  if (rc != TT_OK) return rc;
+  void* base = nullptr;  // the scratch array's device address (never its host-side name)
+  if (scratch_address(&base) != hipSuccess) return TT_EHIP;
+  if (n == 0) return launch_write_zeros(out_n, 1, stream) == hipSuccess ? TT_OK : TT_EHIP;
+  const int64_t want = (n + TILE - 1) / TILE * TILE;
+  if (layout(want, nullptr, nullptr) > NOALLOC_SCRATCH_BYTES) return TT_ETOOBIG;
+  Work w{};
+  layout(want, static_cast<char*>(base), &w);
+  prof_begin(stream);
+  if (launch_pretokenize(dev_bytes, n, nullptr, 1, g.pattern, w, w.piece_start, nullptr, &g.tb, stream) != hipSuccess ||
+      launch_bpe_emit(dev_bytes, n, g.tb, w, out_ids, out_n, nullptr, stream) != hipSuccess)
     return TT_EHIP;
   return TT_OK;
 }

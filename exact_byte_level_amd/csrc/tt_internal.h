@@ -180,6 +180,13 @@ constexpr int BIG_BYTES = 2048;         // longer pieces: merged by the workgrou
 constexpr int EMIT_THREADS = 256;       // emission workgroup (one tile's pieces)
 constexpr int HUGE_TOKENS = 64;         // pieces with more tokens are copied by the whole grid
 
+// ------------------------------------------------------------- no-alloc encode
+// tt_encode_noalloc carves its workspace out of one fixed device array of
+// NOALLOC_SCRATCH_BYTES (the layout of an input of TT_NOALLOC_MAX_BYTES bytes
+// needs about 23.5 bytes per input byte, 47 MiB at 2 MiB).
+constexpr size_t NOALLOC_SCRATCH_BYTES = (size_t)48 << 20;
+constexpr int NOALLOC_MAX_DEVICES = 64;
+
 // ------------------------------------------------------------- sessions
 constexpr int SESSION_LEVELS = 6;       // window sizes tail << 0 .. tail << 5 before a full encode
 // info[] of one repair step (device int64; the host reads it after the step)

@@ -42,6 +42,11 @@ hipError_t launch_splice(const uint8_t* text, int64_t w0, int64_t n_old, int64_t
 hipError_t launch_session_full(const uint8_t* text, int64_t n, int64_t tail, const Work& w, int64_t* info,
                                hipStream_t st);
 
+// Device address of the fixed scratch array of the no-alloc encode on the
+// current device: looked up with hipGetSymbolAddress on the first call per
+// device, then kept.  Allocates nothing.
+hipError_t scratch_address(void** out);
+
 hipError_t launch_write_zeros(int64_t* out, int cnt, hipStream_t st);
 hipError_t launch_write_zero_i32(int32_t* out, hipStream_t st);
 hipError_t launch_zero_counters(const Work& w, hipStream_t st);

@@ -2214,6 +2214,31 @@ __global__ void k_write_zero_i64(int64_t* out, int cnt) {
 
 __global__ void k_write_zero_i32(int32_t* out) { *out = 0; }
 
+// ------------------------------------------------------- fixed scratch array
+// The workspace of tt_encode_noalloc, for callers that cannot allocate: one
+// array per device, held from module load until the process ends.  Host code
+// never passes the array's name to a kernel (on the host it is a stand-in,
+// not a device address); it looks up the device address once per device and
+// passes that.
+static __device__ __align__(256) unsigned char scratch[NOALLOC_SCRATCH_BYTES];
+static void* scratch_dev[NOALLOC_MAX_DEVICES];  // looked-up address per device, null until then
+
+hipError_t scratch_address(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= NOALLOC_MAX_DEVICES) return hipErrorInvalidDevice;
+  if (!scratch_dev[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    scratch_dev[dev] = p;
+  }
+  *out = scratch_dev[dev];
+  return hipSuccess;
+}
+
 // ---------------------------------------------------------------- launchers
 
 static inline int ceil_div(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }

@@ -146,6 +146,27 @@ int tt_reserve(int64_t max_bytes, int32_t max_seqs);
 int tt_encode(const uint8_t* dev_bytes, int64_t n, int32_t* out_ids, int64_t* out_n,
               hipStream_t stream);
 
+/* Largest input of tt_encode_noalloc. */
+#define TT_NOALLOC_MAX_BYTES ((int64_t)1 << 21)
+
+/* tt_encode_noalloc -- tt_encode for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc).
+ *
+ * Arguments, output and enqueue-only contract as tt_encode, with n at most
+ * TT_NOALLOC_MAX_BYTES (2 MiB; larger gives TT_ETOOBIG before any device
+ * work).  The call allocates nothing, ever: instead of the library's
+ * workspace it uses a fixed 48 MiB device array that every GPU the library
+ * is loaded on holds until the process ends, looked up once per device.
+ * Every call on one GPU shares that array, which keeps the last call's
+ * contents (the kernels reset what they need), so two calls that overlap in
+ * time on one GPU race, as do a no-alloc call and any other encode.  The
+ * merge tables still come from tt_load_bpe.  Returns TT_OK, TT_EINVAL,
+ * TT_ETOOBIG, TT_EHIP or TT_ENOTLOADED.
+ */
+int tt_encode_noalloc(const uint8_t* dev_bytes, int64_t n, int32_t* out_ids, int64_t* out_n,
+                      hipStream_t stream);
+
 /* tt_encode_batch -- token ids of n_seqs independent texts in one call.
  *
  * Each text is a fresh session tokenized on its own (the factorisation of

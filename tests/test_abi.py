@@ -28,7 +28,7 @@ def _declared():
 
 def test_exports_every_declared_symbol():
     names = _declared()
-    assert names == sorted(["tt_load_bpe", "tt_load_bpe_ex", "tt_reserve", "tt_encode", "tt_encode_batch", "tt_pretokenize", "tt_encode_offsets",
+    assert names == sorted(["tt_load_bpe", "tt_load_bpe_ex", "tt_reserve", "tt_encode", "tt_encode_noalloc", "tt_encode_batch", "tt_pretokenize", "tt_encode_offsets",
                             "tt_session_create", "tt_session_destroy", "tt_session_reset", "tt_session_append",
                             "tt_session_view", "tt_session_read",
                             "tt_char_class", "tt_profile", "tt_profile_read", "tt_free", "tt_strerror"])
