@@ -1,23 +1,39 @@
 """Benchmark: exact BPE encode throughput on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c2] [--all]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c2] [--only]
+    python bench.py --summarize DIR --workload NAME   (rocprofv3 output -> profiles/)
 
 One step = one full encode (pre-tokenization, BPE of every pre-token, token-id
-emission) of the workload's text, which is already resident in HBM.  Prints
-one JSON line: chars/s (value), ms per step and per 1M chars, the roofline of
-the dominant kernel (per-kernel HIP events recorded on the launch stream), and
-the CPU oracle timed on a bounded sample on this host as a reported baseline.
+emission) of the workload's text, already resident in HBM.  The timed region
+is exactly K steps, each between its own pair of HIP events on the launch
+stream with a synchronisation after it, so every step is a single-request
+latency; the headline is chars / p50 of those K latencies.  Prints one JSON
+line with the headline workload's figures, the roofline of its dominant
+kernel, every other workload's figures under config.workloads, and the CPU
+oracle timed on this host as a reported baseline.
 
-Workloads (seeded, synthetic; the default is the 1,000,000-char single text
-the headline metric is quoted on):
-  c1  64 KiB ASCII code-like text, GPT-2-style rules, 4,096 merges
-  c2  1,000,000-char code/log mix, GPT-2-style rules, 50,000 merges
-  c3  1,000,000-char mix with 5 % multibyte chars, cl100k-style, 100,000 merges
-  c4  64 log-normal fresh texts (~8M chars) in one batch call
+Workloads (seeded, synthetic; the headline is the 1,000,000-char single text):
+  c1   64 KiB ASCII code-like text, GPT-2-style rules, 4,096 merges
+  c2   1,000,000-char code/log mix, GPT-2-style rules, 50,000 merges
+  c3   1,000,000-char mix with 5 % multibyte chars, cl100k-style, 100,000 merges
+  c4   64 log-normal fresh texts (~8M chars) in one batch call
   c5a..c5d adversarial 1,000,000-char texts (one giant piece, 100K-digit runs,
-      50K-space runs, alternating letter/punctuation)
+       50K-space runs, alternating letter/punctuation)
+  w100k one 100,000-letter random word (a long piece with many distinct merges)
+Each is checked against the oracle's stored digests before it is timed.
+
+Roofline (per workload, for the kernel with the largest live event time):
+  alg_bytes = n + 4T (+ 16 (B + 1) for a batch): the text read once and the
+  ids written once, the per-encode algorithmic bytes of the method; the HBM
+  fraction is alg_bytes / kernel time / 8 TB/s.  The kernels are bound by
+  VALU issue and dependent probe latency, not by HBM: where a rocprofv3
+  counter pass of the same kernel source is stored (profiles/counters.json),
+  the VALU issue fraction is SQ_INSTS_VALU x 4 cycles / 1024 SIMDs / 2.4 GHz /
+  kernel time, and `bound` says which fraction is the larger.
 """
 import argparse
+import csv
+import glob
 import hashlib
 import json
 import os
@@ -29,8 +45,16 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "exact BPE encode throughput: chars/s and ms per 1M chars; % of HBM peak"
-HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
-VALU_CLOCK_GHZ = 2.4    # MI355X peak engine clock
+HEADLINE = "c2"
+ALL_WORKLOADS = ["c1", "c2", "c3", "c4", "c5a", "c5b", "c5c", "c5d", "w100k"]
+HBM_PEAK_GBS = 8000.0   # MI355X HBM3E, published
+CLOCK_GHZ = 2.4         # MI355X peak engine clock (one clock for every figure here)
+SIMDS = 256 * 4         # 256 CUs x 4 SIMDs
+# a wave64 VALU instruction occupies a 16-lane SIMD for 4 cycles
+VALU_PEAK_GINST = SIMDS * CLOCK_GHZ / 4  # 614.4 G wave-instructions/s
+COUNTERS = os.path.join(ROOT, "profiles", "counters.json")
+KERNEL_SRC = os.path.join(ROOT, "exact_byte_level_amd", "csrc", "tt_kernels.hip")
+PRETOK_KERNELS = ("k_tile_summary", "k_pretok<0>", "k_pretok<1>")
 
 
 def _sha(a):
@@ -38,27 +62,36 @@ def _sha(a):
     return hashlib.sha256(np.ascontiguousarray(a, dtype="<i4").tobytes()).hexdigest()
 
 
-# Piece compaction with the first BPE step (single bytes, single-token table,
-# queues) and the merge loops of the rest form one stage of two kernels; its
-# roofline takes both launches together.
-BPE_STAGE = "k_compact+k_bpe_merge"
+def kernel_source_sha():
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
 
 
-def alg_bytes(kernel, n, P, T):
-    """Bytes a kernel must move at least once (inputs read + outputs written)."""
-    if kernel.startswith("k_pretok"):
-        return n + n / 8            # text in, one start bit per byte out
-    if kernel == "k_tile_summary":
-        return n
-    if kernel == BPE_STAGE:
-        # start bits in, piece offsets out; piece bytes in, tokens + counts out
-        return n / 8 + 4 * (P + 1) + n + 4 * T + 4 * P
-    if kernel == "k_emit":
-        return 12 * P + 8 * T       # counts, starts, tokens in; offsets, ids out
-    return 0
+def _base_name(k):
+    """Kernel name without template arguments and namespace (profiler names)."""
+    k = k.split("(")[0].replace("void ", "").replace("tt::", "").strip()
+    return k
 
 
-def run_workload(name, steps, warmup, graph=True, cpu=True, traffic=None):
+def load_counters():
+    """Stored counter summaries whose kernel source matches this tree, by workload."""
+    if not os.path.exists(COUNTERS):
+        return {}
+    with open(COUNTERS) as f:
+        c = json.load(f)
+    if c.get("kernel_source_sha256") != kernel_source_sha():
+        return {}
+    return c.get("workloads", {})
+
+
+def pct(sorted_vals, q):
+    return sorted_vals[min(len(sorted_vals) - 1, int(round(q * (len(sorted_vals) - 1))))]
+
+
+# ------------------------------------------------------------------ GPU side
+
+def measure(name, steps, warmup, graph=True, detail=False, counters=None):
+    """Time one workload; returns a dict of its figures (verified first)."""
     import numpy as np
     import torch
 
@@ -77,6 +110,7 @@ def run_workload(name, steps, warmup, graph=True, cpu=True, traffic=None):
     out = torch.empty(n, dtype=torch.int32, device=dev)
     cnt = torch.empty(nseq + 1 if offs is not None else 1, dtype=torch.int64, device=dev)
     off = None if offs is None else torch.tensor(offs, dtype=torch.int64, device=dev)
+    stream = torch.cuda.current_stream()
 
     def step():
         if off is None:
@@ -84,81 +118,56 @@ def run_workload(name, steps, warmup, graph=True, cpu=True, traffic=None):
         else:
             tt.encode_batch_into(x, off, out, cnt)
 
-    for _ in range(warmup):
+    t0 = time.perf_counter()
+    step()
+    torch.cuda.synchronize()
+    first_ms = (time.perf_counter() - t0) * 1e3
+    # slow workloads (a long piece of many rounds) take fewer steps
+    k = steps if first_ms < 5.0 else max(3, min(steps, int(2000.0 / first_ms)))
+    for _ in range(warmup if first_ms < 5.0 else min(warmup, 2)):
         step()
     torch.cuda.synchronize()
     T = int(cnt[-1].item())
     if T < 0:
-        raise RuntimeError("encode reported error %d" % T)
+        raise RuntimeError("%s: encode reported error %d" % (name, T))
     ids = out[:T].cpu().numpy()
-    gold_path = os.path.join(ROOT, "tests", "golden", "expected.json")
-    verified = None
-    if os.path.exists(gold_path):
-        with open(gold_path) as f:
-            exp = json.load(f).get(name)
-        if exp:
-            verified = exp["tokens"] == T and exp["ids_sha256"] == _sha(ids)
-            if not verified:
-                raise RuntimeError("GPU ids differ from the oracle digest for %s" % name)
+    with open(os.path.join(ROOT, "tests", "golden", "expected.json")) as f:
+        exp = json.load(f)[name]
+    if exp["tokens"] != T or exp["ids_sha256"] != _sha(ids):
+        raise RuntimeError("GPU ids differ from the oracle digest for %s" % name)
 
-    # timed region: exactly `steps` encodes, events on the launch stream
-    stream = torch.cuda.current_stream()
+    # the timed region: exactly k steps, each a single-request latency
     torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for _ in range(steps):
-        step()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    ms_per_step = e0.elapsed_time(e1) / steps
-
-    # byte-offset export: the same encode plus every token's byte start
-    # (tt_encode_offsets), checked against the oracle's digest, then timed
-    starts_buf = torch.empty(n + 1, dtype=torch.int32, device=dev)
-
-    def step_off():
-        tt.encode_offsets_into(x, off, out, starts_buf, cnt)
-
-    step_off()
-    torch.cuda.synchronize()
-    if int(cnt[-1].item()) != T or _sha(out[:T].cpu().numpy()) != _sha(ids):
-        raise RuntimeError("tt_encode_offsets ids differ from tt_encode's")
-    offsets_verified = None
-    if verified is not None and "token_starts_sha256" in exp:
-        offsets_verified = _sha(starts_buf[:T + 1].cpu().numpy()) == exp["token_starts_sha256"]
-        if not offsets_verified:
-            raise RuntimeError("GPU token offsets differ from the oracle digest for %s" % name)
-    e0.record(stream)
-    for _ in range(steps):
-        step_off()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    offsets_ms = e0.elapsed_time(e1) / steps
-
-    # latency distribution: one event pair per encode
     lat = []
-    for _ in range(steps):
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(k)]
+    for a, b in evs:
         a.record(stream)
         step()
         b.record(stream)
         b.synchronize()
-        lat.append(a.elapsed_time(b))
-    lat.sort()
-    p50 = statistics.median(lat)
-    p99 = lat[min(len(lat) - 1, int(round(0.99 * (len(lat) - 1))))]
+    lat = sorted(a.elapsed_time(b) for a, b in evs)
+    p50, p99 = statistics.median(lat), pct(lat, 0.99)
 
-    # host-inclusive latency: encode plus the D2H read of the count
-    t_host = []
-    for _ in range(min(steps, 50)):
-        t0 = time.perf_counter()
+    # k encodes queued back to back (a stream of requests): mean per encode
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(k):
         step()
-        int(cnt[-1].item())
-        t_host.append((time.perf_counter() - t0) * 1e3)
-    host_p50 = statistics.median(t_host)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    b2b_ms = e0.elapsed_time(e1) / k
 
-    # HIP graph replay of one captured encode
-    graph_p50 = None
+    res = {
+        "desc": WORKLOADS[name][2],
+        "chars": chars, "bytes": n, "tokens": T, "seqs": nseq, "steps": k,
+        "p50_ms": p50, "p99_ms": p99,
+        "chars_per_s": chars / (p50 * 1e-3),
+        "ms_per_1M_chars": p50 * 1e6 / chars,
+        "back_to_back_mean_ms": b2b_ms,
+        "verified_against_oracle": True,
+    }
+
+    # HIP graph replay of one captured encode (the pages' single-request mode)
     if graph:
         try:
             g = torch.cuda.CUDAGraph()
@@ -171,124 +180,110 @@ def run_workload(name, steps, warmup, graph=True, cpu=True, traffic=None):
             with torch.cuda.graph(g):
                 step()
             torch.cuda.synchronize()
-            glat = []
-            for _ in range(steps):
+            gl = []
+            for _ in range(k):
                 a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
                 a.record(stream)
                 g.replay()
                 b.record(stream)
                 b.synchronize()
-                glat.append(a.elapsed_time(b))
-            gT = int(cnt[-1].item())
-            if gT != T or _sha(out[:T].cpu().numpy()) != _sha(ids):
+                gl.append(a.elapsed_time(b))
+            if int(cnt[-1].item()) != T or _sha(out[:T].cpu().numpy()) != _sha(ids):
                 raise RuntimeError("graph replay result differs")
-            graph_p50 = statistics.median(glat)
-        except Exception as ex:  # graph capture is optional context
-            print("graph mode skipped: %r" % (ex,), file=sys.stderr)
+            gl.sort()
+            res["graph_p50_ms"] = statistics.median(gl)
+            res["graph_p99_ms"] = pct(gl, 0.99)
+            del g
+        except Exception as ex:  # graph capture is context, not the headline
+            print("graph mode skipped for %s: %r" % (name, ex), file=sys.stderr)
 
-    # per-kernel durations from events recorded after each launch
+    if detail:
+        # host-inclusive latency: encode plus the D2H read of the count
+        th = []
+        for _ in range(min(k, 50)):
+            t0 = time.perf_counter()
+            step()
+            int(cnt[-1].item())
+            th.append((time.perf_counter() - t0) * 1e3)
+        res["host_incl_p50_ms"] = statistics.median(th)
+        # byte-offset export: the same ids plus every token's byte start
+        starts_buf = torch.empty(n + 1, dtype=torch.int32, device=dev)
+
+        def step_off():
+            tt.encode_offsets_into(x, off, out, starts_buf, cnt)
+
+        step_off()
+        torch.cuda.synchronize()
+        if int(cnt[-1].item()) != T or _sha(out[:T].cpu().numpy()) != _sha(ids):
+            raise RuntimeError("tt_encode_offsets ids differ from tt_encode's")
+        if _sha(starts_buf[:T + 1].cpu().numpy()) != exp["token_starts_sha256"]:
+            raise RuntimeError("GPU token offsets differ from the oracle digest for %s" % name)
+        ol = []
+        for _ in range(k):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            step_off()
+            b.record(stream)
+            b.synchronize()
+            ol.append(a.elapsed_time(b))
+        res["with_byte_offsets_p50_ms"] = statistics.median(ol)
+        res["byte_offsets_verified"] = True
+
+    # per-kernel durations, live: an event after each launch (tt_profile), k steps
     tt.profile(True)
     acc = {}
-    nprof = max(10, min(steps, 50))
-    for _ in range(nprof):
+    for _ in range(k):
         step()
-        for k, ms in tt.profile_read():
-            acc.setdefault(k, []).append(ms)
+        for kn, ms in tt.profile_read():
+            acc.setdefault(kn, []).append(ms)
     tt.profile(False)
-    kern = {k: statistics.mean(v) for k, v in acc.items()}
-    stage = dict(kern)
-    if "k_compact" in stage and "k_bpe_merge" in stage:
-        stage[BPE_STAGE] = stage.pop("k_compact") + stage.pop("k_bpe_merge")
-    start_np = tt.pretokenize(x, off)
-    P = int(start_np.numel())
-    dom = max(stage, key=stage.get)
-    dom_ms = stage[dom]
-    a_bytes = alg_bytes(dom, n, P, T)
-    achieved = a_bytes / (dom_ms * 1e-3) / 1e9
+    kern_us = {kn: 1e3 * statistics.mean(v) for kn, v in acc.items()}
+    res["kernels_us"] = {kn: round(v, 2) for kn, v in sorted(kern_us.items(), key=lambda kv: -kv[1])}
+    pre_us = sum(v for kn, v in kern_us.items() if kn in PRETOK_KERNELS)
+    bpe_us = sum(v for kn, v in kern_us.items() if kn not in PRETOK_KERNELS)
+    res["stage_split"] = {
+        "pretokenize_us": round(pre_us, 2),
+        "pretokenize_GBps": round(n / (pre_us * 1e-6) / 1e9, 1) if pre_us else None,
+        "bpe_and_emit_us": round(bpe_us, 2),
+        "bpe_and_emit_GBps": round(n / (bpe_us * 1e-6) / 1e9, 1) if bpe_us else None,
+    }
+    res["roofline"] = roofline(name, n, T, nseq if off is not None else 0, kern_us, counters or {})
+    return res
+
+
+def roofline(name, n, T, nseq, kern_us, counters):
+    dom = max(kern_us, key=kern_us.get)
+    t_us = kern_us[dom]
+    alg = n + 4 * T + (16 * (nseq + 1) if nseq else 0)
+    achieved = alg / (t_us * 1e-6) / 1e9
     roof = {
-        "bound": "hbm",
+        "bound": "alu",
         "kernel": dom,
         "achieved": round(achieved, 3),
         "peak": HBM_PEAK_GBS,
         "unit": "GB/s",
         "frac": achieved / HBM_PEAK_GBS,
         "traffic": None,
-        "kernel_ms": round(dom_ms, 5),
-        "alg_bytes": int(a_bytes),
+        "alg_bytes": alg,
+        "kernel_us_live": round(t_us, 2),
+        "clock_ghz": CLOCK_GHZ,
     }
-    # counters count only for the kernels they were taken on
-    src = os.path.join(ROOT, "exact_byte_level_amd", "csrc", "tt_kernels.hip")
-    with open(src, "rb") as f:
-        src_sha = hashlib.sha256(f.read()).hexdigest()
-    if (traffic and traffic.get("workload") == name and traffic.get("kernel") == dom
-            and traffic.get("kernel_source_sha256") == src_sha):
-        roof["traffic"] = traffic.get("bytes")
-    # what actually bounds the merge pass: VALU issue, from SQ_INSTS_VALU of a
-    # rocprofv3 counter pass on the same kernels (a wave64 VALU instruction
-    # holds a 16-lane SIMD for 4 cycles; 1024 SIMDs; the chip's 2.4 GHz peak
-    # clock, so the fraction is a lower bound when the clock runs below it)
-    sq_path = os.path.join(ROOT, "profiles", "sq.json")
-    if os.path.exists(sq_path) and "k_bpe_merge" in kern:
-        with open(sq_path) as f:
-            sq = json.load(f)
-        vi = sq.get("valu_insts", {}).get("k_bpe_merge")
-        if sq.get("workload") == name and sq.get("kernel_source_sha256") == src_sha and vi:
-            roof["merge_valu_issue_frac"] = round(vi * 4 / 1024 / (VALU_CLOCK_GHZ * 1e9) / (kern["k_bpe_merge"] * 1e-3), 3)
-
-    res = {
-        "name": name,
-        "desc": WORKLOADS[name][2],
-        "bytes": n,
-        "chars": chars,
-        "pieces": P,
-        "tokens": T,
-        "seqs": nseq,
-        "ms_per_step": ms_per_step,
-        "p50_ms": p50,
-        "p99_ms": p99,
-        "host_incl_p50_ms": host_p50,
-        "graph_p50_ms": graph_p50,
-        "offsets_ms_per_step": offsets_ms,
-        "offsets_verified": offsets_verified,
-        "kernels_ms": {k: round(v, 5) for k, v in sorted(kern.items(), key=lambda kv: -kv[1])},
-        "roofline": roof,
-        "verified": verified,
-    }
-
-    if cpu:
-        from oracle.bpe import Vocab, encode as oracle_encode
-        v = Vocab(merges)
-        # bounded sample: the whole text, or the
-        # first texts of the batch up to ~4 MB
-        if offs is None:
-            parts, desc = [data], "the whole text"
-        else:
-            parts, tot = [], 0
-            for s in range(nseq):
-                seg = data[offs[s]:offs[s + 1]]
-                if tot + len(seg) > 4_000_000 and parts:
-                    break
-                parts.append(seg)
-                tot += len(seg)
-            desc = "first %d of %d texts (%d bytes)" % (len(parts), nseq, sum(len(p) for p in parts))
-        c_chars = sum(len(p.decode("utf-8")) for p in parts)
-        # the sample again and again until about 10 s of CPU work; the median run counts
-        runs, t_all = [], time.perf_counter()
-        while not runs or (time.perf_counter() - t_all < 10.0 and len(runs) < 25):
-            t0 = time.perf_counter()
-            for p in parts:
-                oracle_encode(p, v, pat)
-            runs.append(time.perf_counter() - t0)
-        dt = statistics.median(runs)
-        res["cpu_baseline"] = {
-            "value": c_chars / dt,
-            "unit": "chars/s",
-            "cores": 1,
-            "kind": "oracle",
-            "sample": "%s, %d chars; median of %d runs, %.2f s each, %.1f s in all (plain Python oracle, one "
-                      "thread, no piece memo)" % (desc, c_chars, len(runs), dt, sum(runs)),
-        }
-    return res
+    c = counters.get(name, {})
+    base = _base_name(dom)
+    rp = c.get("avg_us", {}).get(base)
+    if rp:
+        roof["kernel_us_rocprof"] = rp
+        roof["frac_rocprof"] = alg / (rp * 1e-6) / 1e9 / HBM_PEAK_GBS
+    tr = c.get("hbm_bytes", {}).get(base)
+    if tr is not None:
+        roof["traffic"] = int(tr)
+    vi = c.get("valu_insts", {}).get(base)
+    if vi:
+        valu = vi / (t_us * 1e-6) / 1e9
+        roof["valu"] = {"insts": int(vi), "achieved": round(valu, 1), "peak": VALU_PEAK_GINST,
+                        "unit": "G wave64 VALU instructions/s", "frac": round(valu / VALU_PEAK_GINST, 3)}
+        roof["bound"] = "alu" if valu / VALU_PEAK_GINST > achieved / HBM_PEAK_GBS else "hbm"
+    return roof
 
 
 def run_session(steps, append_chars=1400):
@@ -352,26 +347,242 @@ def run_session(steps, append_chars=1400):
     }
 
 
+# ------------------------------------------------------------------ CPU side
+# The oracle timed on this host's cores.  It runs before anything touches the
+# GPU, in forked worker processes (fork only: no program is replaced).
+
+def host_info():
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    allowed = sorted(os.sched_getaffinity(0))
+    return {"nproc": os.cpu_count(), "cpus_allowed": len(allowed), "cpu_model": model}, allowed
+
+
+# Inputs of the CPU runs, prepared in the parent before the workers fork
+# (each worker then reads them from its copy of the parent's memory).
+_CPU = {}
+
+
+def _cpu_input(name):
+    import numpy as np
+    from oracle.bpe import Vocab
+    from synth.text import workload
+    if name not in _CPU:
+        data, offs, pat, voc = workload(name)
+        _CPU[name] = (data, offs, pat, Vocab(np.load(os.path.join(ROOT, "data", "vocab_%s.npy" % voc))))
+    return _CPU[name]
+
+
+def _oracle_job(args):
+    """Worker: (workload, core, runs) -> per-run seconds of the split alone and
+    of the whole encode, after one warm-up run."""
+    name, core, runs = args
+    from oracle.bpe import encode
+    from oracle.pretok import split_bytes
+    os.sched_setaffinity(0, {core})
+    data, _, pat, v = _CPU[name]
+    split_s, total_s = [], []
+    for _ in range(runs + 1):
+        t0 = time.perf_counter()
+        split_bytes(data, pat)
+        t1 = time.perf_counter()
+        encode(data, v, pat)
+        t2 = time.perf_counter()
+        split_s.append(t1 - t0)
+        total_s.append(t2 - t1)
+    return split_s[1:], total_s[1:]
+
+
+def _batch_text_job(args):
+    """Worker of the all-cores batch run: encode text s of the batch."""
+    name, s = args
+    from oracle.bpe import encode
+    data, offs, pat, v = _CPU[name]
+    encode(data[offs[s]:offs[s + 1]], v, pat)
+
+
+def cpu_baseline(runs=3):
+    import multiprocessing as mp
+    info, allowed = host_info()
+    ctx = mp.get_context("fork")
+    core = allowed[-1]
+    data, _, _, _ = _cpu_input(HEADLINE)
+    chars = len(data.decode("utf-8"))
+    with ctx.Pool(1) as pool:
+        split_s, total_s = pool.map(_oracle_job, [(HEADLINE, core, runs)])[0]
+    t_all = statistics.median(total_s)
+    t_split = statistics.median(split_s)
+    res = {
+        "value": chars / t_all,
+        "unit": "chars/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": "the whole %s text (%d chars): plain Python oracle (regex split + classic merge loop, no piece "
+                  "memo), one process pinned to core %d, 1 warm-up + %d timed runs, median" % (
+                      HEADLINE, chars, core, runs),
+        "host": info,
+        "pinned_core": core,
+        "encode_s": round(t_all, 4),
+        "split_s": round(t_split, 4),
+        "bpe_s": round(t_all - t_split, 4),
+    }
+    # the 64-text batch on all allowed cores (a process per core, at most 16),
+    # texts handed out largest first
+    name = "c4"
+    data, offs, _, _ = _cpu_input(name)
+    bchars = len(data.decode("utf-8"))
+    workers = min(16, len(allowed))
+    nseq = len(offs) - 1
+    jobs = [(name, s) for s in sorted(range(nseq), key=lambda s: -(offs[s + 1] - offs[s]))]
+    times = []
+    with ctx.Pool(workers) as pool:
+        for r in range(runs + 1):
+            t0 = time.perf_counter()
+            pool.map(_batch_text_job, jobs, chunksize=1)
+            if r:
+                times.append(time.perf_counter() - t0)
+    tb = statistics.median(times)
+    res["batch_all_cores"] = {
+        "workload": name, "chars": bchars, "workers": workers, "s": round(tb, 3),
+        "chars_per_s": bchars / tb,
+        "sample": "the whole 64-text batch, one text per task over %d worker processes, 1 warm-up + %d timed runs, "
+                  "median" % (workers, runs),
+    }
+    return res
+
+
+# ------------------------------------------------------- profile summaries
+
+def summarize(outdir, name):
+    """Read rocprofv3 CSV output under outdir (a kernel-trace run and counter
+    runs of `bench.py --only --workload name`) and write
+    profiles/<name>_kernels.md plus this workload's entry of
+    profiles/counters.json."""
+    src_sha = kernel_source_sha()
+    stats = {}
+    for p in glob.glob(os.path.join(outdir, "**", "*kernel_stats.csv"), recursive=True):
+        with open(p) as f:
+            for row in csv.DictReader(f):
+                stats[row["Name"]] = row
+    pmc = {}
+    for p in glob.glob(os.path.join(outdir, "**", "*counter_collection.csv"), recursive=True):
+        with open(p) as f:
+            for row in csv.DictReader(f):
+                key = (row["Kernel_Name"], row["Counter_Name"])
+                pmc.setdefault(key, {})
+                d = row.get("Dispatch_Id") or row.get("Correlation_Id")
+                pmc[key][d] = pmc[key].get(d, 0.0) + float(row["Counter_Value"])
+
+    def avg(kname, counter):
+        v = pmc.get((kname, counter))
+        return (sum(v.values()) / len(v), len(v)) if v else (None, 0)
+
+    copy = [k for k in {k for k, _ in pmc} if "copyBuffer" in k]
+    fetch_scale = write_scale = None
+    if copy:
+        fk, _ = avg(copy[0], "FETCH_SIZE")
+        wk, _ = avg(copy[0], "WRITE_SIZE")
+        probe_kib = 64 * 1024.0
+        fetch_scale = probe_kib / fk if fk else None
+        write_scale = probe_kib / wk if wk else None
+    kernels = sorted({k for k in stats} | {k for k, _ in pmc if "copyBuffer" not in k})
+    entry = {"avg_us": {}, "hbm_bytes": {}, "valu_insts": {}}
+    rows = []
+    for k in kernels:
+        base = _base_name(k)
+        st = stats.get(k)
+        avg_us = float(st["AverageNs"]) / 1e3 if st else None
+        fk, nd = avg(k, "FETCH_SIZE")
+        wk, _ = avg(k, "WRITE_SIZE")
+        vi, _ = avg(k, "SQ_INSTS_VALU")
+        hbm = None
+        if fk is not None and wk is not None and fetch_scale and write_scale:
+            hbm = 1024.0 * (fk * fetch_scale + wk * write_scale)
+        if avg_us is not None and "copyBuffer" not in k:
+            entry["avg_us"][base] = round(avg_us, 3)
+        if hbm is not None:
+            entry["hbm_bytes"][base] = round(hbm)
+        if vi is not None:
+            entry["valu_insts"][base] = round(vi)
+        rows.append((k, st, avg_us, fk, wk, hbm, vi))
+    cur = {"kernel_source_sha256": src_sha, "workloads": {}}
+    if os.path.exists(COUNTERS):
+        with open(COUNTERS) as f:
+            old = json.load(f)
+        if old.get("kernel_source_sha256") == src_sha:
+            cur = old
+    cur["workloads"][name] = entry
+    with open(COUNTERS, "w") as f:
+        json.dump(cur, f, indent=1, sort_keys=True)
+    from synth.text import WORKLOADS
+    lines = ["# Kernels of one encode: %s (%s)" % (name, WORKLOADS[name][2]), "",
+             "rocprofv3 on one MI355X, run from /tmp (`<repo>` is the repository root); each counter in its own run:", "",
+             "    rocprofv3 --kernel-trace --stats -f csv -d <out>/trace -o run -- python3 <repo>/bench.py --only "
+             "--workload %s --steps 50 --warmup 5 --no-cpu --no-graph" % name]
+    for c in ("FETCH_SIZE", "WRITE_SIZE", "SQ_INSTS_VALU"):
+        lines.append("    timeout -s KILL 150 rocprofv3 --pmc %s -f csv -d <out>/%s -o %s -- python3 <repo>/bench.py "
+                     "--only --workload %s --steps 5 --warmup 2 --no-cpu --no-graph --copy-probe 64" % (c, c, c, name))
+    lines += ["", "    python3 bench.py --summarize <out> --workload %s" % name, ""]
+    if fetch_scale:
+        lines.append("Calibration: a 64 MiB device-to-device copy reads FETCH_SIZE %.1f KiB and WRITE_SIZE %.1f KiB per "
+                     "dispatch, so fetch counts are scaled by %.4f and write counts by %.4f." % (
+                         64 * 1024 / fetch_scale, 64 * 1024 / write_scale, fetch_scale, write_scale))
+        lines.append("")
+    lines += ["| kernel | calls | avg us | min us | max us | FETCH KiB | WRITE KiB | HBM bytes (scaled) | SQ_INSTS_VALU | "
+              "VALU issue frac at %.1f GHz |" % CLOCK_GHZ,
+              "|---|---|---|---|---|---|---|---|---|---|"]
+    for k, st, avg_us, fk, wk, hbm, vi in rows:
+        if "copyBuffer" in k:
+            continue
+        frac = vi * 4 / SIMDS / (CLOCK_GHZ * 1e3) / avg_us if (vi and avg_us) else None
+        lines.append("| %s | %s | %s | %s | %s | %s | %s | %s | %s | %s |" % (
+            _base_name(k), st["Calls"] if st else "-", "%.2f" % avg_us if avg_us else "-",
+            "%.2f" % (float(st["MinNs"]) / 1e3) if st else "-", "%.2f" % (float(st["MaxNs"]) / 1e3) if st else "-",
+            "%.1f" % fk if fk is not None else "-", "%.1f" % wk if wk is not None else "-",
+            "%d" % hbm if hbm is not None else "-", "%d" % vi if vi is not None else "-",
+            "%.3f" % frac if frac else "-"))
+    lines += ["", "Kernel source: tt_kernels.hip sha256 %s." % src_sha, ""]
+    path = os.path.join(ROOT, "profiles", "%s_kernels.md" % name)
+    with open(path, "w") as f:
+        f.write("\n".join(lines))
+    print(path)
+
+
+# ---------------------------------------------------------------------- main
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="c2")
-    ap.add_argument("--all", action="store_true", help="also bench every workload (lines on stderr)")
+    ap.add_argument("--workload", default=HEADLINE)
+    ap.add_argument("--only", action="store_true", help="time only --workload (no other workloads, no session)")
     ap.add_argument("--no-graph", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-session", action="store_true", help="skip the incremental-repair latency line")
-    ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "traffic.json"),
-                    help="measured HBM traffic of the dominant kernel (rocprofv3 PMC), if present")
     ap.add_argument("--copy-probe", type=int, default=0,
-                    help="also run a plain device copy of this many MiB (counter calibration)")
+                    help="first run a plain device copy of this many MiB (counter calibration)")
+    ap.add_argument("--summarize", metavar="DIR", help="summarise rocprofv3 CSV output of --workload into profiles/")
     args = ap.parse_args()
 
+    if args.summarize:
+        summarize(args.summarize, args.workload)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py: this path runs on one GPU only (no sharding or collectives are built); "
               "run with --gpus 1", file=sys.stderr)
         sys.exit(2)
+
+    # the CPU oracle first: its worker processes are forked before anything
+    # touches the GPU
+    cpu = None if args.no_cpu else cpu_baseline()
 
     import torch
     if not torch.cuda.is_available():
@@ -379,69 +590,54 @@ def main():
         sys.exit(2)
     torch.cuda.set_device(0)
 
-    traffic = None
-    if os.path.exists(args.traffic):
-        with open(args.traffic) as f:
-            traffic = json.load(f)
-
     if args.copy_probe:
         src = torch.empty(args.copy_probe << 20, dtype=torch.uint8, device="cuda")
         dst = torch.empty_like(src)
         for _ in range(3):
             dst.copy_(src)
         torch.cuda.synchronize()
+        del src, dst
 
-    res = run_workload(args.workload, args.steps, args.warmup, graph=not args.no_graph,
-                       cpu=not args.no_cpu, traffic=traffic)
-    sess = run_session(min(args.steps, 50)) if args.workload == "c2" and not args.no_session else None
-    chars_per_s = res["chars"] / (res["ms_per_step"] * 1e-3)
+    counters = load_counters()
+    head = measure(args.workload, args.steps, args.warmup, graph=not args.no_graph, detail=not args.only,
+                   counters=counters)
+    others = {}
+    if not args.only:
+        for name in ALL_WORKLOADS:
+            if name == args.workload:
+                continue
+            r = measure(name, args.steps, args.warmup, graph=not args.no_graph, counters=counters)
+            others[name] = r
+            print("%s: p50 %.4f ms, %.3g chars/s, graph p50 %s ms" % (
+                name, r["p50_ms"], r["chars_per_s"], "%.4f" % r["graph_p50_ms"] if "graph_p50_ms" in r else "-"),
+                file=sys.stderr, flush=True)
+    sess = run_session(min(args.steps, 50)) if args.workload == "c2" and not args.no_session and not args.only \
+        else None
+
+    config = {"workload": "%s: %s" % (args.workload, head["desc"])}
+    config.update({k: v for k, v in head.items() if k not in ("desc", "roofline")})
+    config["session"] = sess
+    config["workloads"] = {k: {kk: vv for kk, vv in v.items() if kk not in ("kernels_us",)} for k, v in others.items()}
+    config["parallelism"] = "single GPU"
     line = {
         "metric": METRIC,
-        "value": chars_per_s,
+        "value": head["chars_per_s"],
         "unit": "chars/s",
         "n_gpus": 1,
-        "steps": args.steps,
+        "steps": head["steps"],
         "warmup": args.warmup,
-        "ms_per_step": res["ms_per_step"],
+        "ms_per_step": head["p50_ms"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "int32",
         "data": "synthetic",
-        "config": {
-            "workload": "%s: %s" % (res["name"], res["desc"]),
-            "chars": res["chars"],
-            "bytes": res["bytes"],
-            "pieces": res["pieces"],
-            "tokens": res["tokens"],
-            "ms_per_1M_chars": res["ms_per_step"] * 1e6 / res["chars"],
-            "p50_ms": res["p50_ms"],
-            "p99_ms": res["p99_ms"],
-            "graph_p50_ms": res["graph_p50_ms"],
-            "host_incl_p50_ms": res["host_incl_p50_ms"],
-            "with_byte_offsets_ms": res["offsets_ms_per_step"],
-            "byte_offsets_verified": res["offsets_verified"],
-            "end_to_end_alg_GBps": (res["bytes"] + 4 * res["tokens"]) / (res["ms_per_step"] * 1e-3) / 1e9,
-            "kernels_ms": res["kernels_ms"],
-            "verified_against_oracle": res["verified"],
-            "session": sess,
-            "parallelism": "single GPU",
-        },
-        "roofline": res["roofline"],
+        "config": config,
+        "roofline": head["roofline"],
     }
-    if "cpu_baseline" in res:
-        line["cpu_baseline"] = res["cpu_baseline"]
+    if cpu:
+        line["cpu_baseline"] = cpu
     print(json.dumps(line), flush=True)
-
-    if args.all:
-        from synth.text import WORKLOADS
-        for name in WORKLOADS:
-            if name == args.workload:
-                continue
-            r = run_workload(name, args.steps, args.warmup, graph=not args.no_graph, cpu=False, traffic=traffic)
-            r["chars_per_s"] = r["chars"] / (r["ms_per_step"] * 1e-3)
-            r["ms_per_1M_chars"] = r["ms_per_step"] * 1e6 / r["chars"]
-            print(json.dumps(r), file=sys.stderr, flush=True)
 
 
 if __name__ == "__main__":

@@ -11,6 +11,7 @@ from .text import (  # noqa: F401
     mix_text,
     batch_texts,
     adversarial_text,
+    random_word,
     workload,
     WORKLOADS,
 )

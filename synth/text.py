@@ -8,6 +8,8 @@ log-normal batch of fresh texts, and four adversarial texts.
 """
 import math
 
+import random
+
 import numpy as np
 
 ASCII_PUNCT = "!\"#$%&'()*+,-./:;<=>?@[\\]^_`{|}~"
@@ -271,6 +273,7 @@ WORKLOADS = {
     "c5b": (1, "c3", "100,000-digit runs, cl100k-style rules"),
     "c5c": (1, "c3", "50,000-space runs with a trailing non-space, cl100k-style rules"),
     "c5d": (1, "c3", "alternating letter/punctuation, cl100k-style rules"),
+    "w100k": (0, "c2", "one 100,000-letter random word (12 letters), GPT-2-style rules, 50,000 merges"),
 }
 
 
@@ -288,7 +291,16 @@ def workload(name):
         return data, off, pat, voc
     if name.startswith("c5"):
         return adversarial_text(name[2]), None, pat, voc
+    if name == "w100k":
+        return random_word(100_000, 5), None, pat, voc
     raise ValueError(name)
+
+
+def random_word(n_letters, seed, alphabet="etaoinshrdlu"):
+    """One pre-token of ``n_letters`` letters drawn uniformly (Python's seeded
+    ``random``): a long piece with thousands of distinct merges."""
+    rng = random.Random(seed)
+    return "".join(rng.choice(alphabet) for _ in range(n_letters)).encode()
 
 
 # Training corpora for the three vocabularies: (generator, size, seed, rules, M).
