@@ -30,6 +30,8 @@ struct State {
   uint64_t* d_pair = nullptr;
   CacheBucket* d_cache = nullptr;
   uint32_t* d_tok_len = nullptr;
+  uint64_t* d_kids = nullptr;
+  RunChunk* d_runs = nullptr;
   uint64_t* d_word = nullptr;
   uint32_t* d_tok_off = nullptr;
   uint8_t* d_tok_bytes = nullptr;
@@ -109,6 +111,8 @@ void release_tables() {
   free_dev(g.d_pair);
   free_dev(g.d_cache);
   free_dev(g.d_tok_len);
+  free_dev(g.d_kids);
+  free_dev(g.d_runs);
   free_dev(g.d_word);
   free_dev(g.d_tok_off);
   free_dev(g.d_tok_bytes);
@@ -148,8 +152,9 @@ size_t layout(int64_t n, char* base, Work* w) {
   t.tok_off = (int32_t*)take((nn + 1) * 4);
   t.tile_tok = (uint32_t*)take(ntiles * 4);
   t.tile_pbase = (uint32_t*)take(ntiles * 4);
-  t.big_min = (uint32_t*)take(ntiles * 4);
-  t.big_ctr = (int32_t*)take(ntiles * 4);
+  t.big_fail = (int32_t*)take(ntiles * 4);
+  t.huge_hc = (uint32_t*)take(ntiles * 2 * 4);
+  t.fall_list = (int32_t*)take((nn / BIG_BYTES + 2) * 4);
   t.sb_cnt = (uint32_t*)take((ntiles / SB_TILES + 2) * 4);
   t.sb_err = (uint32_t*)take((ntiles / SB_TILES + 2) * 4);
   t.sb_tok = (uint32_t*)take((ntiles / SB_TILES + 2) * 4);
@@ -366,6 +371,24 @@ int tt_load_bpe_ex(const int32_t* merges, const int32_t* ranks, int64_t n_merges
   // any id masked to ID_BITS indexes inside the table
   std::vector<uint32_t> tok_len((size_t)1 << ID_BITS, 0u);
   for (size_t t = 0; t < tok.size(); ++t) tok_len[t] = (uint32_t)std::min<size_t>(tok[t].size(), 0xFFFFFFFFu);
+  // operands of every merge, for the token-pair compatibility walk of the
+  // long-piece stitching (one entry even for an empty table)
+  std::vector<uint64_t> kids(std::max<size_t>(M, 1), 0ull);
+  for (size_t r = 0; r < M; ++r) kids[r] = (uint64_t)mx[r] | ((uint64_t)my[r] << 32);
+  // the encoding of RUN_BYTES copies of each byte value (host classic loop)
+  std::vector<RunChunk> runs(256);
+  for (uint32_t b = 0; b < 256; ++b) {
+    std::vector<uint32_t> out = host_bpe(std::vector<uint32_t>(RUN_BYTES, b), rank);
+    RunChunk& rc = runs[b];
+    std::memset(&rc, 0, sizeof(rc));
+    rc.cnt = (uint32_t)out.size();
+    uint32_t at = 0;
+    for (size_t k = 0; k < out.size(); ++k) {
+      rc.id[k] = out[k];
+      rc.pos[k] = (uint8_t)at;
+      at += (uint32_t)tok[out[k]].size();
+    }
+  }
   // whole-pre-token table: tokens of 2..16 bytes whose own BPE is
   // themselves; with the whole-word rule, every token (the smallest id of
   // each byte string), and the longer ones go to the whole-word table
@@ -464,6 +487,7 @@ int tt_load_bpe_ex(const int32_t* merges, const int32_t* ranks, int64_t n_merges
   int rc;
   if ((rc = upload(&g.d_byte_pair, byte_pair)) != TT_OK || (rc = upload(&g.d_pair, pair_tab)) != TT_OK ||
       (rc = upload(&g.d_cache, cache)) != TT_OK || (rc = upload(&g.d_tok_len, tok_len)) != TT_OK ||
+      (rc = upload(&g.d_kids, kids)) != TT_OK || (rc = upload(&g.d_runs, runs)) != TT_OK ||
       (whole && ((rc = upload(&g.d_word, word_tab)) != TT_OK || (rc = upload(&g.d_tok_off, tok_off)) != TT_OK ||
                  (rc = upload(&g.d_tok_bytes, tok_blob)) != TT_OK))) {
     release_tables();
@@ -482,6 +506,8 @@ int tt_load_bpe_ex(const int32_t* merges, const int32_t* ranks, int64_t n_merges
   g.tb.pair_tab = g.d_pair;
   g.tb.cache = g.d_cache;
   g.tb.tok_len = g.d_tok_len;
+  g.tb.kids = g.d_kids;
+  g.tb.runs = g.d_runs;
   g.tb.pair_shift = pair_shift;
   g.tb.cache_mask = (uint32_t)(cache_nb - 1);
   g.tb.cache_shift = cache_shift;

@@ -93,11 +93,23 @@ __host__ __device__ inline uint64_t word_hash_step(uint64_t h, uint64_t word) {
   return h ^ (h >> 32);
 }
 
+// The classic encoding of RUN_BYTES copies of one byte value: token count,
+// ids, and the byte offset of each token (a stitched chunk that is a run of
+// one byte takes it from here instead of merging).
+constexpr int RUN_BYTES = 32;
+struct RunChunk {
+  uint32_t cnt;
+  uint32_t id[RUN_BYTES];
+  uint8_t pos[RUN_BYTES];
+};
+
 struct Tables {
   const uint32_t* byte_pair;    // [65536] rank of (x, y), x, y < 256, or RANK_NONE
   const uint64_t* pair_tab;     // [2^(32 - pair_shift)] two-choice slots
   const CacheBucket* cache;     // [cache_nb]
   const uint32_t* tok_len;      // [2^ID_BITS] byte length of every token (0 past the vocabulary)
+  const uint64_t* kids;         // [merges] operands of the merge of rank r: left | right << 32
+  const struct RunChunk* runs;  // [256] the encoding of RUN_BYTES copies of each byte
   int pair_shift;               // 32 - log2(slots)
   uint32_t cache_mask;          // cache_nb - 1
   int cache_shift;              // 64 - log2(cache_nb)
@@ -123,6 +135,7 @@ enum : int {
   CTR_ERR = 2,           // ERR_* bits
   CTR_T = 4,             // tokens
   CTR_NHUGE = 5,         // pieces with more than HUGE_TOKENS tokens (huge_list)
+  CTR_NFALL = 6,         // pieces longer than BIG_BYTES whose stitching failed (fall_list)
   CTR_RESET_END = 12,    // counters [0, CTR_RESET_END) are per call
   CTR_COUNT = 16
 };
@@ -147,11 +160,15 @@ struct Work {
   int32_t* tok_off;      // [n + 1] token offset of each piece; [P] = T
   uint32_t* tile_tok;    // [ntiles] tokens of the pieces that start in each tile
   uint32_t* tile_pbase;  // [ntiles] index of the first piece that starts in each tile
-  // Hand-over of a piece longer than BIG_BYTES between the tiles it covers,
-  // at the index of the tile holding its last byte (no two such pieces share
-  // one): the least pair rank of the piece and the arrival counter.
-  uint32_t* big_min;     // [ntiles]
-  int32_t* big_ctr;      // [ntiles]
+  // Pieces longer than BIG_BYTES (stitched in k_compact): at the index of the
+  // tile holding the piece's last byte (no two such pieces share one), 1 once
+  // some tile found a boundary it could not repair; reset by k_pretok.
+  int32_t* big_fail;     // [ntiles]
+  // Tokens of stitched pieces that start in each tile: [2t] for the piece
+  // that covers the tile's first byte, [2t + 1] for the piece that starts in
+  // the tile (both included in tile_tok[t]).
+  uint32_t* huge_hc;     // [2 * ntiles]
+  int32_t* fall_list;    // [n / BIG_BYTES + 1] pieces whose stitching failed
   // Inputs of more than SB_MIN_TILES tiles: sums over each run of SB_TILES
   // tiles of their piece counts (and the OR of their error bits) and of
   // their token counts, so that a tile's prefix reads O(1) cache lines per

@@ -890,9 +890,8 @@ __global__ __launch_bounds__(PT_THREADS) void k_pretok(const uint8_t* __restrict
   const uint32_t err = (__syncthreads_or(bad) ? ERR_UTF8 : 0u) | (__syncthreads_or(bad_off) ? ERR_OFFSETS : 0u);
   if (threadIdx.x == 0) {
     w.tile_cnt[t] = cnt | (err << TILE_ERR_SHIFT);
-    // reset for the long-piece hand-over of the next pass
-    w.big_min[t] = RANK_NONE;
-    w.big_ctr[t] = 0;
+    // reset for the long-piece stitching of the next pass
+    w.big_fail[t] = 0;
   }
 }
 
@@ -1021,14 +1020,45 @@ __device__ __forceinline__ uint32_t group_min(uint32_t x) {
   return x;
 }
 
-// Classic BPE of 64 / G pieces at once, one piece per aligned group of G
-// lanes and one byte position per lane (piece length <= G).  Each step takes
+// The classic merge loop on 64 / G sequences at once, one per aligned group
+// of G lanes: lane g of a group holds token g of its sequence (id, and with
+// TRACK its first byte's offset pos), rk the rank of the pair (token g,
+// token g + 1) or RANK_NONE, m the sequence's token count.  Each step takes
 // the group minimum of (rank << 6 | position) -- the lowest rank, leftmost
 // among equal pairs, exactly the classic choice -- merges that pair, shifts
-// the positions right of it one lane left, and the two lanes next to the new
-// token probe the pair-rank table (both probes in flight together).  The loop
-// runs while any group of the wavefront still has a merge (ballot: a
-// wave-uniform exit around the shuffles).  Tokens go to tmp_ids[s, s + cnt).
+// the tokens right of it one lane left, and the two lanes next to the new
+// token probe the pair-rank table (both probes in flight together).  The
+// loop runs while any group of the wavefront still has a merge (ballot: a
+// wave-uniform exit around the DPP moves).
+template <int G, bool TRACK>
+__device__ __forceinline__ void group_merge_loop(const Tables& tb, uint32_t& id, uint32_t& rk, uint32_t& pos, int& m) {
+  const int g = (int)(threadIdx.x & 63u) & (G - 1);
+  for (;;) {
+    const uint32_t kmin = group_min<G>((rk << 6) | (uint32_t)g);
+    const bool act = kmin < (1u << 26);
+    if (__ballot(act) == 0ull) break;
+    const int bk = (int)(kmin & 63u);
+    const uint32_t nid = 256u + (kmin >> 6);
+    const uint32_t id1 = lane_up1(id), id2 = lane_up1(id1), rs = lane_up1(rk);
+    const uint32_t pos1 = TRACK ? lane_up1(pos) : 0u;
+    const uint32_t rk1 = g == G - 1 ? RANK_NONE : rs;  // nothing enters from the next group
+    const bool do_l = act && g == bk - 1;
+    const bool do_r = act && g == bk && bk + 2 < m;
+    uint32_t r = RANK_NONE;
+    if (do_l || do_r) r = pair_rank_new(tb, do_l ? id : nid, do_l ? nid : id2);
+    if (act) {
+      const uint32_t nid_here = (g < bk) ? id : ((g == bk) ? nid : id1);
+      rk = (g < bk - 1) ? rk : ((g == bk - 1 || g == bk) ? r : rk1);
+      id = nid_here;
+      if (TRACK && g > bk) pos = pos1;
+      --m;
+    }
+  }
+}
+
+// Classic BPE of up to 64 / G queued pieces (queue entries chunk * (64 / G)
+// ...), one per aligned group of G lanes, one byte position per lane (piece
+// length <= G).  Tokens go to tmp_ids[s, s + cnt).
 template <int G>
 __device__ void group_bpe(const uint8_t* __restrict__ bytes, const Work& w, const Tables& tb,
                           const uint32_t* queue, int qn, int chunk) {
@@ -1049,25 +1079,8 @@ __device__ void group_bpe(const uint8_t* __restrict__ bytes, const Work& w, cons
   // rk is RANK_NONE wherever no pair starts (g + 1 >= m), so the key of such
   // a lane, (RANK_NONE << 6) | g, lies above every real key (< 2^26)
   uint32_t rk = (g + 1 < m) ? tb.byte_pair[(id << 8) | (nx & 255u)] : RANK_NONE;
-  for (;;) {
-    const uint32_t kmin = group_min<G>((rk << 6) | (uint32_t)g);
-    const bool act = kmin < (1u << 26);
-    if (__ballot(act) == 0ull) break;
-    const int bk = (int)(kmin & 63u);
-    const uint32_t nid = 256u + (kmin >> 6);
-    const uint32_t id1 = lane_up1(id), id2 = lane_up1(id1), rs = lane_up1(rk);
-    const uint32_t rk1 = g == G - 1 ? RANK_NONE : rs;  // nothing enters from the next group
-    const bool do_l = act && g == bk - 1;
-    const bool do_r = act && g == bk && bk + 2 < m;
-    uint32_t r = RANK_NONE;
-    if (do_l || do_r) r = pair_rank_new(tb, do_l ? id : nid, do_l ? nid : id2);
-    if (act) {
-      const uint32_t nid_here = (g < bk) ? id : ((g == bk) ? nid : id1);
-      rk = (g < bk - 1) ? rk : ((g == bk - 1 || g == bk) ? r : rk1);
-      id = nid_here;
-      --m;
-    }
-  }
+  uint32_t pos = 0;
+  group_merge_loop<G, false>(tb, id, rk, pos, m);
   if (valid) {
     if (g < m) w.tmp_ids[s + g] = (int32_t)id;
     if (g == 0) w.piece_cnt[p] = m;
@@ -1213,8 +1226,6 @@ __device__ __forceinline__ uint32_t block_min(uint32_t x, uint32_t* red) {
 
 constexpr int BIG_E = 8;                           // positions per thread and sweep step
 constexpr int BIG_STEP = 256 * BIG_E;              // positions per sweep step of the workgroup
-constexpr int SHARE_TILES = 9;  // tiles per share of a long piece's first round (prime to the 8 XCDs that
-                                // workgroups are dealt to in turn, so that shares spread over all of them)
 constexpr int BIG_LDS = BIG_STEP + 2 + (BIG_STEP + 2) / 32 + 1;  // skewed slots per staged array
 __device__ __forceinline__ int big_slot(int i) { return i + (i >> 5); }  // spreads BIG_E-strided reads over the banks
 
@@ -1231,33 +1242,20 @@ __device__ __forceinline__ uint32_t big_word(const uint32_t* base, uint32_t k) {
   return *reinterpret_cast<const uint32_t*>(reinterpret_cast<const char*>(base) + k * 4u);
 }
 
-// This thread's share of sweep step base (positions base + tid + 256 j, and
-// two more on the right in threads 0 and 1): ids, and ranks of the pairs
-// they start (none past the end).
-__device__ __forceinline__ void big_load_step(const uint32_t* I, const uint32_t* R, int base, int m, int tid,
-                                              uint32_t (&pid)[BIG_E + 1], uint32_t (&prk)[BIG_E + 1]) {
-#pragma unroll
-  for (int j = 0; j <= BIG_E; ++j) {
-    const uint32_t k = (uint32_t)(base + tid + 256 * j);
-    const bool in = j < BIG_E || tid < 2;
-    pid[j] = in && (int)k < m ? big_word(I, k) : 0u;
-    prk[j] = in && (int)k + 1 < m ? big_word(R, k) : RANK_NONE;
-  }
-}
-
-// Rounds 1, 2, ... of piece p = bytes [s, s + m), longer than BIG_BYTES, by
-// one workgroup of 256 threads (s, m and rmin, the least pair rank left by the
-// first round, are the same in every thread): the same exact global-minimum
-// rounds as long_bpe.  A sweep step's BIG_STEP positions (and two more on the
-// right) are staged in LDS with coalesced loads;
-// thread t then takes the BIG_E contiguous positions t * BIG_E ... .  Inside
-// a run of equal pairs the merge starts alternate, so whether position k
-// starts a merge depends on the carry from k - 1: each thread evaluates its
-// positions for both carries and a block scan of the resulting carry
-// functions picks the right one.  A block prefix sum of the surviving
-// positions places the compacted ids; a step writes only left of the next
-// step's positions, and all its LDS reads finish (barrier) before the next
-// step is staged.
+// Rounds 1, 2, ... of piece p = bytes [s, s + m) by one workgroup of 256
+// threads (s, m and rmin, the least pair rank left by the first round, are
+// the same in every thread): exact global-minimum rounds, as long_bpe, for a
+// piece whose stitching failed.  A sweep step's BIG_STEP positions (and two
+// more on the right) are staged in LDS with coalesced loads; thread t then
+// takes the BIG_E contiguous positions t * BIG_E ... .  Inside a run of equal
+// pairs the merge starts alternate, so whether position k starts a merge
+// depends on the carry from k - 1: each thread evaluates its positions for
+// both carries and a block scan of the resulting carry functions picks the
+// right one.  A block prefix sum of the surviving positions places the
+// compacted ids; a step writes only left of the next step's positions, and
+// all its LDS reads finish (barrier) before the next step is staged.  The
+// staged ids and ranks are read from LDS where they are used, which keeps the
+// code small enough in registers to live in the merge kernel.
 __device__ int big_rounds(const Work& w, const Tables& tb, uint32_t p, int32_t s, int m, uint32_t rmin,
                           BigSmem& sm) {
   const int tid = (int)threadIdx.x, lane = tid & 63, wid = tid >> 6;
@@ -1275,31 +1273,19 @@ __device__ int big_rounds(const Work& w, const Tables& tb, uint32_t p, int32_t s
     const int base0 = max(first - 1, 0) / BIG_STEP * BIG_STEP;
     int out = base0;
     for (int base = base0; base < m; base += BIG_STEP) {
-      uint32_t pid[BIG_E + 1], prk[BIG_E + 1];
-      big_load_step(I, R, base, m, tid, pid, prk);
-#pragma unroll
       for (int j = 0; j <= BIG_E; ++j) {
         if (j < BIG_E || tid < 2) {
-          sm.id[big_slot(tid + 256 * j)] = pid[j];
-          sm.rk[big_slot(tid + 256 * j)] = prk[j];
+          const uint32_t k = (uint32_t)(base + tid + 256 * j);
+          sm.id[big_slot(tid + 256 * j)] = (int)k < m ? big_word(I, k) : 0u;
+          sm.rk[big_slot(tid + 256 * j)] = (int)k + 1 < m ? big_word(R, k) : RANK_NONE;
         }
       }
       __syncthreads();
       const int j0 = tid * BIG_E, k0 = base + j0;
-      // this thread's ids and ranks and the two after them, read once (the
-      // ids are needed only after the scans below, which hide their latency)
-      uint32_t own_id[BIG_E + 2], own_rk[BIG_E + 2];
-#pragma unroll
-      for (int j = 0; j < BIG_E + 2; ++j) {
-        own_id[j] = sm.id[big_slot(j0 + j)];
-        own_rk[j] = sm.rk[big_slot(j0 + j)];
-      }
       uint32_t eq = 0;
-#pragma unroll
-      for (int j = 0; j < BIG_E + 2; ++j) eq |= (own_rk[j] == rmin ? 1u : 0u) << j;
+      for (int j = 0; j < BIG_E + 2; ++j) eq |= (sm.rk[big_slot(j0 + j)] == rmin ? 1u : 0u) << j;
       // merge starts of this thread's positions for carry in 0 (msA) and 1 (msB)
       uint32_t msA = 0, msB = 0, a = 0, b = 1;
-#pragma unroll
       for (int j = 0; j < BIG_E; ++j) {
         const uint32_t e = (eq >> j) & 1u;
         a = e & (a ^ 1u);
@@ -1322,20 +1308,18 @@ __device__ int big_rounds(const Work& w, const Tables& tb, uint32_t p, int32_t s
       const uint32_t msx = ms | (msE << BIG_E) | (msE1 << (BIG_E + 1));
       const uint32_t prev = (ms << 1) | tc;  // bit j: a merge starts at position j - 1
       uint32_t keep = 0;
-#pragma unroll
       for (int j = 0; j < BIG_E; ++j)
         if (k0 + j < m && !((prev >> j) & 1u)) keep |= 1u << j;
       if (tid == 255) sm.sh[4] = lastms;
       uint32_t tot;
       int o = out + (int)block_excl_sum(__popc(keep), sm.sh + 8, &tot);
-#pragma unroll
       for (int j = 0; j < BIG_E; ++j) {
         if (!((keep >> j) & 1u)) continue;
         const int k = k0 + j;
         const bool m0 = (msx >> j) & 1u, m1 = (msx >> (j + 1)) & 1u, m2 = (msx >> (j + 2)) & 1u;
-        const uint32_t nid = m0 ? T : own_id[j];
+        const uint32_t nid = m0 ? T : sm.id[big_slot(j0 + j)];
         const bool has_next = m0 ? (k + 2 < m) : (k + 1 < m);
-        const uint32_t nxt = m0 ? (m2 ? T : own_id[j + 2]) : (m1 ? T : own_id[j + 1]);
+        const uint32_t nxt = m0 ? (m2 ? T : sm.id[big_slot(j0 + j + 2)]) : (m1 ? T : sm.id[big_slot(j0 + j + 1)]);
         uint32_t nr = RANK_NONE;
         if (has_next && (m0 || m1)) {
           // (merged ids are never bytes; inside runs the same pair recurs)
@@ -1346,7 +1330,7 @@ __device__ int big_rounds(const Work& w, const Tables& tb, uint32_t p, int32_t s
           }
           nr = lr;
         } else if (has_next) {
-          nr = own_rk[j];
+          nr = sm.rk[big_slot(j0 + j)];
         }
         I[o] = nid;
         R[o] = nr;
@@ -1363,18 +1347,11 @@ __device__ int big_rounds(const Work& w, const Tables& tb, uint32_t p, int32_t s
     m = (int)uniform((uint32_t)out);
     // the ranks of the skipped steps count for the next minimum (and come
     // before every rewritten position)
-    // (eight loads in flight per thread)
-    for (int k0 = tid; k0 < base0; k0 += 256 * 8) {
-      uint32_t r[8];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) r[u] = k0 + 256 * u < base0 ? big_word(R, (uint32_t)(k0 + 256 * u)) : RANK_NONE;
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int k = k0 + 256 * u;
-        if (r[u] < nmin || (r[u] == nmin && k < nfirst)) {
-          nmin = r[u];
-          nfirst = k;
-        }
+    for (int k = tid; k < base0; k += 256) {
+      const uint32_t r = big_word(R, (uint32_t)k);
+      if (r < nmin || (r == nmin && k < nfirst)) {
+        nmin = r;
+        nfirst = k;
       }
     }
     rmin = uniform(block_min(nmin, sm.sh + 8));
@@ -1413,55 +1390,280 @@ __device__ uint32_t big_first_round(const uint8_t* __restrict__ bytes, const Wor
   return uniform(block_min(rmin, sm.sh + 8));
 }
 
-// A piece p = bytes [s, e) longer than BIG_BYTES spans several tiles.  In
-// each group of SHARE_TILES tiles it covers, the first of them takes the
-// first round on the group's share [a, b) (starting in tile t0 / TILE), so
-// that many workgroups write the piece's ids and ranks (groups rather than
-// single tiles, since each share ends in device-wide memory fences).  The tiles then meet at
-// the piece's counter without waiting for one another: each folds its least
-// rank into the piece's minimum and adds its share's length to the counter,
-// the tile holding s adding minus the piece's length on top.  Only the sum
-// over every share is zero, so the tile whose addition reads it has seen all
-// of them and merges the piece (big_merge, after the tile's other share, so
-// that a tile which merges one piece does not hold back the next one).
-// Returns that, the same in every thread.
-__device__ bool big_share(const uint8_t* __restrict__ bytes, const Work& w, const Tables& tb, int32_t s, int32_t e,
-                          int32_t a, int32_t b, int64_t t0, BigSmem& sm) {
-  const uint32_t rmin = big_first_round(bytes, w, tb, a, b, e, sm);
-  const int key = (e - 1) / TILE;
-  const int32_t delta = (b - a) - (s >= t0 ? e - s : 0);
-  __builtin_amdgcn_s_waitcnt(0);  // this wavefront's ids and ranks have reached the cache
-  __syncthreads();                // ... and every wavefront's
-  if (threadIdx.x == 0) {
-    atomicMin(&w.big_min[key], rmin);
-    __threadfence();  // the share and its minimum, device-wide, before the counter
-    const int32_t old = atomicAdd(&w.big_ctr[key], delta);
-    sm.sh[6] = old + delta == 0 ? 1u : 0u;
+
+// ------------------------------------------------------------- stitched BPE
+//
+// A piece longer than BIG_BYTES is cut into chunks of SCH bytes counted from
+// its first byte.  Every chunk is encoded on its own; two adjacent chunks
+// join as they are when their edge tokens are compatible (tokens_compatible:
+// the classic loop on the two tokens' bytes gives back the two tokens).  A
+// token sequence whose every adjacent pair is compatible, built from tokens
+// that are each their own encoding, is the classic encoding of its bytes, so
+// joined chunks are exact.  Where two chunks do not join, a window -- the
+// last k tokens of the left chunk and the first k of the right one -- is
+// encoded again, and it replaces them if its own edge tokens are compatible
+// with the chunk tokens next to it; k doubles up to SK_MAX.  A window takes at
+// most (cnt - 1) / 2 tokens of a chunk with a boundary on its other side too,
+// so the two windows of one chunk never meet and every adjacent pair of the
+// result has been checked.  A boundary that no window within these limits
+// repairs makes the piece fall back to exact global-minimum rounds
+// (big_fallback, in k_bpe_merge).
+//
+// Each tile the piece covers encodes the chunks that overlap it and their
+// two neighbours, and decides the boundaries between them; a boundary shared
+// by two tiles is decided by both, from the same two chunks, the same way.
+// The result stays sparse: the id of each token at its first byte in
+// tmp_ids, -1 at every other byte of the piece; k_emit compacts it.
+constexpr int SCH = RUN_BYTES;           // bytes per chunk
+constexpr int SCH_MAX = TILE / SCH + 3;  // chunks a tile's region and its two neighbours can touch
+constexpr int SWIN = 64;                 // longest window, bytes
+constexpr int SWIN_TOK = 32;             // most tokens a window's encoding may have
+constexpr int SK_MAX = 8;                // largest window half, tokens per side
+
+struct StitchSmem {
+  uint32_t tok[SCH_MAX][SCH];    // tokens of each chunk
+  uint32_t win[SCH_MAX][SWIN_TOK];  // window tokens of boundary b (between chunks b and b + 1)
+  int32_t wstart[SCH_MAX];       // first byte of each window
+  uint32_t list[SCH_MAX];        // boundaries whose windows are encoded in this pass
+  uint32_t red[8];
+  uint32_t nlist, nopen, nfail;
+  uint8_t pos[SCH_MAX][SCH];     // byte offset of each chunk token in its chunk
+  uint8_t wpos[SCH_MAX][SWIN_TOK];  // byte offset of each window token in its window
+  uint8_t cnt[SCH_MAX];          // tokens per chunk
+  uint8_t wcnt[SCH_MAX];         // window tokens
+  uint8_t wlen[SCH_MAX];         // window bytes
+  uint8_t kb[SCH_MAX];           // window half of each boundary (0: the chunks join as they are)
+  uint8_t state[SCH_MAX];        // 0 joined, 1 open, 2 beyond the limits
+};
+
+// Can token b follow token a in a BPE result: does the classic loop on
+// bytes(a) + bytes(b) give exactly [a, b]?  The loop builds a and b from
+// their operands.  At any moment the pair across the junction is (x, y), x on
+// a's right spine (a, right(a), right(right(a)), ...) and y on b's left spine.
+// It gets merged if it has a merge whose rank is below the rank that consumes
+// x (an equal rank is this same pair further left, which goes first) and not
+// above the rank that consumes y (an equal rank is this same pair further
+// right, which goes after).  The walk visits the junction pairs from the last
+// one, (a, b), back to the two edge bytes: of the two current tokens the one
+// made later (the higher rank) steps down to its operand at the junction.
+__device__ bool tokens_compatible(const Tables& tb, uint32_t a, uint32_t b) {
+  uint32_t x = a, y = b, cx = RANK_NONE, cy = RANK_NONE;
+  for (int it = 0; it < 4 * SCH; ++it) {  // at most depth(a) + depth(b) <= 2 (SWIN - 1) steps
+    const uint32_t r = pair_rank(tb, x, y);
+    if (r != RANK_NONE && r < cx && r <= cy) return false;
+    if (x >= 256u && (y < 256u || x > y)) {
+      cx = x - 256u;
+      x = (uint32_t)(tb.kids[cx] >> 32);
+    } else if (y >= 256u) {
+      cy = y - 256u;
+      y = (uint32_t)tb.kids[cy] & ID_MASK;
+    } else {
+      return true;
+    }
   }
-  __syncthreads();
-  const bool last = uniform(sm.sh[6]) != 0u;
-  __syncthreads();  // sh[6] is read before a later share writes it
-  return last;
+  return false;  // not reached for tokens of at most SWIN bytes; refusing only costs the fallback
 }
 
-// The rounds of piece p = bytes [s, e) after big_share found every share of
-// its first round done; its token count goes to the tile where it starts.
-__device__ void big_merge(const Work& w, const Tables& tb, uint32_t p, int32_t s, int32_t e, BigSmem& sm) {
-  __threadfence();  // every share's ids and ranks, after the counter
-  const int key = (e - 1) / TILE;
-  const uint32_t r = uniform(__hip_atomic_load(&w.big_min[key], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-  const int cnt = big_rounds(w, tb, p, s, e - s, r, sm);
-  if (threadIdx.x == 0) atomicAdd(&w.tile_tok[s / TILE], (uint32_t)cnt);
+// The stitched encoding of piece [s, e) on the region [a, b) of the tile at
+// t0 (all the same in every thread): the region's ids at their token starts
+// (-1 elsewhere) into ids_out[a, b).  Returns the number of tokens that start
+// in the region, or -1 if some boundary needs a window beyond the limits
+// (then nothing is written).
+__device__ int stitch_region(const uint8_t* __restrict__ bytes, const Tables& tb, int32_t* __restrict__ ids_out,
+                             int32_t s, int32_t e, int32_t a, int32_t b, int64_t t0, StitchSmem& sm) {
+  const int tid = (int)threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int nc = (e - s + SCH - 1) / SCH;
+  const int klo = (a - s) / SCH, khi = (b - 1 - s) / SCH;
+  const int c0 = max(klo - 1, 0), c1 = min(khi + 1, nc - 1);
+  const int nch = c1 - c0 + 1, nb = nch - 1;
+  // 1. each chunk on its own, two per wavefront and pass
+  for (int q = 0; q < nch; q += 8) {
+    const int i = q + 2 * wid + (lane >> 5), g = lane & 31;
+    const int32_t cs = s + (c0 + i) * SCH;
+    const int len = i < nch ? min(SCH, e - cs) : 0;
+    uint32_t id = g < len ? (uint32_t)bytes[cs + g] : 0u;
+    const uint32_t nx = lane_up1(id);
+    uint32_t rk = g + 1 < len ? tb.byte_pair[(id << 8) | (nx & 255u)] : RANK_NONE;
+    uint32_t pos = (uint32_t)g;
+    int m = len;
+    // a whole chunk of one byte value: its encoding from the run table
+    const uint32_t first = lane < 32 ? (uint32_t)__builtin_amdgcn_readlane((int)id, 0)
+                                     : (uint32_t)__builtin_amdgcn_readlane((int)id, 32);
+    const uint64_t same = __ballot(id == first);
+    if (len == SCH && ((same >> (lane & 32)) & 0xFFFFFFFFull) == 0xFFFFFFFFull) {
+      const RunChunk& rc = tb.runs[id];
+      m = (int)rc.cnt;
+      id = g < m ? rc.id[g] : 0u;
+      pos = g < m ? rc.pos[g] : 0u;
+      rk = RANK_NONE;
+    }
+    group_merge_loop<32, true>(tb, id, rk, pos, m);
+    if (i < nch) {
+      if (g < m) {
+        sm.tok[i][g] = id;
+        sm.pos[i][g] = (uint8_t)pos;
+      }
+      if (g == 0) sm.cnt[i] = (uint8_t)m;
+    }
+  }
+  if (tid == 0) {
+    sm.nopen = 0u;
+    sm.nfail = 0u;
+  }
+  __syncthreads();
+  // 2. the boundaries: join where the edge tokens are compatible
+  if (tid < nb) {
+    const bool ok = tokens_compatible(tb, sm.tok[tid][sm.cnt[tid] - 1], sm.tok[tid + 1][0]);
+    sm.kb[tid] = 0;
+    sm.wcnt[tid] = 0;
+    sm.state[tid] = ok ? 0 : 1;
+    if (!ok) atomicAdd(&sm.nopen, 1u);
+  }
+  __syncthreads();
+  for (int k = 1; k <= SK_MAX && uniform(sm.nopen) != 0u; k *= 2) {
+    if (tid == 0) sm.nlist = 0u;
+    __syncthreads();
+    if (tid < nb && sm.state[tid] == 1) {
+      const int p = sm.cnt[tid], q = sm.cnt[tid + 1];
+      // a chunk with a boundary on its other side as well gives a window at
+      // most (cnt - 1) / 2 tokens; the piece's first and last chunks all of theirs
+      const int kl = c0 + tid > 0 ? (p - 1) / 2 : p;
+      const int kr = c0 + tid + 1 < nc - 1 ? (q - 1) / 2 : q;
+      const int32_t cs0 = s + (c0 + tid) * SCH, cs1 = cs0 + SCH;
+      int32_t ws = 0, we = 0;
+      bool fit = k <= kl && k <= kr;
+      if (fit) {
+        ws = cs0 + sm.pos[tid][p - k];
+        we = k < q ? cs1 + sm.pos[tid + 1][k] : min(cs1 + SCH, e);
+        fit = we - ws <= SWIN;
+      }
+      if (!fit) {
+        sm.state[tid] = 2;
+        atomicAdd(&sm.nfail, 1u);
+      } else {
+        sm.kb[tid] = (uint8_t)k;
+        sm.wstart[tid] = ws;
+        sm.wlen[tid] = (uint8_t)(we - ws);
+        sm.list[atomicAdd(&sm.nlist, 1u)] = (uint32_t)tid;
+      }
+    }
+    __syncthreads();
+    if (uniform(sm.nfail) != 0u) break;
+    // the windows, one per wavefront and pass
+    const int nl = (int)uniform(sm.nlist);
+    for (int q = wid; q < nl; q += 4) {
+      const int bb = (int)uniform(sm.list[q]);
+      const int32_t ws = (int32_t)uniform((uint32_t)sm.wstart[bb]);
+      const int wl = (int)uniform(sm.wlen[bb]);
+      uint32_t id = lane < wl ? (uint32_t)bytes[ws + lane] : 0u;
+      const uint32_t nx = lane_up1(id);
+      uint32_t rk = lane + 1 < wl ? tb.byte_pair[(id << 8) | (nx & 255u)] : RANK_NONE;
+      uint32_t pos = (uint32_t)lane;
+      int m = wl;
+      group_merge_loop<64, true>(tb, id, rk, pos, m);
+      if (lane < m && lane < SWIN_TOK) {
+        sm.win[bb][lane] = id;
+        sm.wpos[bb][lane] = (uint8_t)pos;
+      }
+      if (lane == 0) sm.wcnt[bb] = (uint8_t)m;
+    }
+    __syncthreads();
+    // the window's edge tokens against the chunk tokens next to it
+    if (tid < nb && sm.state[tid] == 1 && sm.wcnt[tid] > SWIN_TOK) {
+      sm.state[tid] = 2;  // more window tokens than kept: beyond the limits
+      atomicAdd(&sm.nfail, 1u);
+    }
+    if (tid < nb && sm.state[tid] == 1) {
+      const int kk = sm.kb[tid], p = sm.cnt[tid], q = sm.cnt[tid + 1], wc = sm.wcnt[tid];
+      const bool okl = p - kk < 1 || tokens_compatible(tb, sm.tok[tid][p - kk - 1], sm.win[tid][0]);
+      const bool okr = kk >= q || tokens_compatible(tb, sm.win[tid][wc - 1], sm.tok[tid + 1][kk]);
+      if (okl && okr) {
+        sm.state[tid] = 0;
+        atomicSub(&sm.nopen, 1u);
+      }
+    }
+    __syncthreads();
+  }
+  if (uniform(sm.nopen) != 0u) return -1;
+  // 3. the region's image: each final token's id at its first byte, -1 at
+  // the others (the barrier orders the two stores of a byte)
+  for (int32_t j = a + tid; j < b; j += PT_THREADS) ids_out[j] = -1;
+  __syncthreads();
+  uint32_t mine = 0;
+  for (int k = tid; k < nch * SCH; k += PT_THREADS) {
+    const int i = k / SCH, j = k % SCH;
+    const int head = i > 0 ? sm.kb[i - 1] : 0, tail = i < nb ? sm.kb[i] : 0;
+    if (j >= head && j < (int)sm.cnt[i] - tail) {
+      const int32_t at = s + (c0 + i) * SCH + sm.pos[i][j];
+      if (at >= a && at < b) {
+        ids_out[at] = (int32_t)sm.tok[i][j];
+        ++mine;
+      }
+    }
+  }
+  for (int k = tid; k < nb * SWIN_TOK; k += PT_THREADS) {
+    const int bb = k / SWIN_TOK, j = k % SWIN_TOK;
+    if (sm.kb[bb] && j < sm.wcnt[bb]) {
+      const int32_t at = sm.wstart[bb] + sm.wpos[bb][j];
+      if (at >= a && at < b) {
+        ids_out[at] = (int32_t)sm.win[bb][j];
+        ++mine;
+      }
+    }
+  }
+  return (int)block_sum(mine, sm.red);
+}
+
+// stitch_region for piece p, with the failure hand-off: the first tile to
+// find a boundary it cannot repair lists the piece for the fallback rounds
+// (its other tiles' sparse output is then overwritten there).  Returns the
+// tokens that start in the region, 0 on failure.
+__device__ uint32_t stitch_piece(const uint8_t* __restrict__ bytes, const Work& w, const Tables& tb, uint32_t p,
+                                 int32_t s, int32_t e, int32_t a, int32_t b, int64_t t0, StitchSmem& sm) {
+  const int c = stitch_region(bytes, tb, w.tmp_ids, s, e, a, b, t0, sm);
+  if (c >= 0) return (uint32_t)c;
+  if (threadIdx.x == 0 && atomicCAS(&w.big_fail[(e - 1) / TILE], 0, 1) == 0)
+    w.fall_list[atomicAdd(&w.ctr[CTR_NFALL], 1u)] = (int32_t)p;
+  return 0u;
+}
+
+// Fallback for a piece whose stitching failed: the exact global-minimum
+// rounds by the whole workgroup (first round from the bytes, then
+// big_rounds), ids contiguous in tmp_ids[s, s + m).  The piece's tokens then
+// count in the tile it starts in, and the stitched counts its tiles posted to
+// tile_tok are taken back.
+__device__ void big_fallback(const uint8_t* __restrict__ bytes, const Work& w, const Tables& tb, uint32_t p,
+                             BigSmem& sm) {
+  const int32_t s = (int32_t)uniform((uint32_t)w.piece_start[p]);
+  const int32_t e = (int32_t)uniform((uint32_t)w.piece_start[p + 1]);
+  const uint32_t rmin = big_first_round(bytes, w, tb, s, e, e, sm);
+  const int m = big_rounds(w, tb, p, s, e - s, rmin, sm);
+  const int ts = s / TILE, te = (e - 1) / TILE;
+  for (int t = ts + (int)threadIdx.x; t <= te; t += (int)blockDim.x) {
+    uint32_t* hc = &w.huge_hc[t == ts ? 2 * t + 1 : 2 * t];
+    const uint32_t add = (t == ts ? (uint32_t)m : 0u) - *hc;  // modulo 2^32: a subtraction
+    *hc = 0u;  // no stitched tokens of this piece remain in the tile
+    if (add) atomicAdd(&w.tile_tok[t], add);
+  }
 }
 
 // The last tile before t with a pre-token start, scanning tiles [lo, t)
-// down 64 at a time, or -1; the same in every lane.
+// down 512 at a time (8 loads in flight per lane), or -1; the same in every
+// lane.
 __device__ __forceinline__ int last_tile_in(const Work& w, int lo, int t, uint32_t cmask) {
   const int lane = (int)(threadIdx.x & 63u);
-  for (int b = t - 1; b >= lo; b -= 64) {
-    const int bb = b - lane;
-    const uint64_t nz = __ballot(bb >= lo && (w.tile_cnt[bb] & cmask) != 0u);
-    if (nz) return b - (__ffsll((unsigned long long)nz) - 1);
+  for (int b = t - 1; b >= lo; b -= 512) {
+    uint32_t v[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int bb = b - 64 * k - lane;
+      v[k] = bb >= lo ? w.tile_cnt[bb] & cmask : 0u;
+    }
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const uint64_t nz = __ballot(v[k] != 0u);
+      if (nz) return b - 64 * k - (__ffsll((unsigned long long)nz) - 1);
+    }
   }
   return -1;
 }
@@ -1469,10 +1671,18 @@ __device__ __forceinline__ int last_tile_in(const Work& w, int lo, int t, uint32
 // The first tile in (t, hi) with a pre-token start, or hi.
 __device__ __forceinline__ int first_tile_in(const Work& w, int t, int hi, uint32_t cmask) {
   const int lane = (int)(threadIdx.x & 63u);
-  for (int b = t + 1; b < hi; b += 64) {
-    const int bb = b + lane;
-    const uint64_t nz = __ballot(bb < hi && (w.tile_cnt[bb] & cmask) != 0u);
-    if (nz) return b + __ffsll((unsigned long long)nz) - 1;
+  for (int b = t + 1; b < hi; b += 512) {
+    uint32_t v[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int bb = b + 64 * k + lane;
+      v[k] = bb < hi ? w.tile_cnt[bb] & cmask : 0u;
+    }
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const uint64_t nz = __ballot(v[k] != 0u);
+      if (nz) return b + 64 * k + __ffsll((unsigned long long)nz) - 1;
+    }
   }
   return hi;
 }
@@ -1578,14 +1788,14 @@ __global__ __launch_bounds__(PT_THREADS) __attribute__((amdgpu_waves_per_eu(6)))
   // it the LDS of big_rounds, in one place
   constexpr size_t SST_BYTES = sizeof(int32_t) * (TILE + 4);
   constexpr size_t CLS_BYTES = SST_BYTES + 16 * ((TILE + CACHE_MAXLEN) / 16);
-  constexpr size_t LDS_BYTES = CLS_BYTES > sizeof(BigSmem) ? CLS_BYTES : sizeof(BigSmem);
+  constexpr size_t LDS_BYTES = CLS_BYTES > sizeof(StitchSmem) ? CLS_BYTES : sizeof(StitchSmem);
   static_assert(SST_BYTES % 16 == 0, "staged bytes stay 16-byte aligned");
   __shared__ __attribute__((aligned(16))) unsigned char lds[LDS_BYTES];
   __shared__ uint32_t red[8];
   __shared__ uint32_t qn[5], qbase[5];
   int32_t* sst = reinterpret_cast<int32_t*>(lds);                  // [TILE + 1]
   uint4* stage = reinterpret_cast<uint4*>(lds + SST_BYTES);        // [(TILE + CACHE_MAXLEN) / 16]
-  BigSmem& big = *reinterpret_cast<BigSmem*>(lds);
+  StitchSmem& st = *reinterpret_cast<StitchSmem*>(lds);
   const int t = blockIdx.x;
   const int lane = (int)(threadIdx.x & 63u);
   const uint32_t cmask = (1u << TILE_ERR_SHIFT) - 1u;
@@ -1631,15 +1841,17 @@ __global__ __launch_bounds__(PT_THREADS) __attribute__((amdgpu_waves_per_eu(6)))
   if (threadIdx.x == 0) w.tile_pbase[t] = base;
   if (!CLASSIFY) return;
   if (tot == 0) {
-    // the whole tile lies inside one piece: if it is longer than BIG_BYTES
-    // and this tile starts a group, take the group's share of its first round
-    if (threadIdx.x == 0) w.tile_tok[t] = 0u;
-    if (t % SHARE_TILES == 0) {
-      const int32_t sp = last_start_before<SB>(w, t, cmask);
-      const int32_t ep = first_start_after<SB>(w, t, ntiles, n, cmask, nc1, fl1);
-      if (ep - sp > BIG_BYTES &&
-          big_share(bytes, w, tb, sp, ep, (int32_t)t0, (int32_t)min<int64_t>(ep, t0 + SHARE_TILES * TILE), t0, big))
-        big_merge(w, tb, base - 1, sp, ep, big);
+    // the whole tile lies inside one piece; if it is longer than BIG_BYTES,
+    // this tile's part of its stitched encoding
+    const int32_t sp = last_start_before<SB>(w, t, cmask);
+    const int32_t ep = first_start_after<SB>(w, t, ntiles, n, cmask, nc1, fl1);
+    uint32_t hh = 0;
+    if (ep - sp > BIG_BYTES)
+      hh = stitch_piece(bytes, w, tb, base - 1, sp, ep, (int32_t)t0, (int32_t)min<int64_t>(ep, t0 + TILE), t0, st);
+    if (threadIdx.x == 0) {
+      w.tile_tok[t] = hh;
+      w.huge_hc[2 * t] = hh;
+      w.huge_hc[2 * t + 1] = 0u;
     }
     return;
   }
@@ -1678,7 +1890,7 @@ __global__ __launch_bounds__(PT_THREADS) __attribute__((amdgpu_waves_per_eu(6)))
         w.piece_cnt[p] = 1;
         ++fin;
       } else if (len > BIG_BYTES) {
-        // only a tile's last piece can be this long: the tile merges it below
+        // only a tile's last piece can be this long: the tile stitches it below
       } else if (len > LANE_CAP) {
         cls = 4;
       } else if (len == 1) {
@@ -1725,26 +1937,29 @@ __global__ __launch_bounds__(PT_THREADS) __attribute__((amdgpu_waves_per_eu(6)))
   }
   // tokens of the tile's finished pieces; merged pieces add theirs later
   const uint32_t tok = block_sum(fin, red);
-  if (threadIdx.x == 0) w.tile_tok[t] = tok;
-  // shares of pieces longer than BIG_BYTES: the bytes before the tile's first
-  // start end a piece that began before the tile (a share if the tile starts
-  // a group), which can be that long only if the tile before has no start;
-  // the tile's last piece can be too (its end comes from this tile's search:
-  // the tile holding the next start may not have written it yet)
+  // pieces longer than BIG_BYTES, stitched (this tile's part of each): the
+  // bytes before the tile's first start end a piece that began before the
+  // tile (that long only if the tile before has no start), and the tile's
+  // last piece (its end comes from this tile's search)
   const int32_t fs = (int32_t)uniform((uint32_t)sst[0]);
-  int32_t sp = 0;
-  bool head_last = false;
-  if (t % SHARE_TILES == 0 && t > 0 && fs > t0 && (w.tile_cnt[t - 1] & cmask) == 0u) {
-    sp = last_start_before<SB>(w, t, cmask);
-    if (fs - sp > BIG_BYTES) head_last = big_share(bytes, w, tb, sp, fs, (int32_t)t0, fs, t0, big);
-  }
   const int32_t ls = (int32_t)uniform((uint32_t)sst[tot - 1]);
   const int32_t le = (int32_t)uniform((uint32_t)sst[tot]);
-  const int64_t gend = (int64_t)(t / SHARE_TILES + 1) * SHARE_TILES * TILE;
-  const bool tail_last =
-      le - ls > BIG_BYTES && big_share(bytes, w, tb, ls, le, ls, (int32_t)min<int64_t>(le, gend), t0, big);
-  if (head_last) big_merge(w, tb, base - 1, sp, fs, big);
-  if (tail_last) big_merge(w, tb, base + tot - 1, ls, le, big);
+  __syncthreads();  // the classification's LDS is read; the stitching reuses it
+  uint32_t hh = 0, ht = 0;
+  if (t > 0 && fs > t0 && (w.tile_cnt[t - 1] & cmask) == 0u) {
+    const int32_t sp = last_start_before<SB>(w, t, cmask);
+    if (fs - sp > BIG_BYTES) hh = stitch_piece(bytes, w, tb, base - 1, sp, fs, (int32_t)t0, fs, t0, st);
+  }
+  if (le - ls > BIG_BYTES) {
+    // count 0 marks the sparse layout (a fallback writes its real count)
+    if (threadIdx.x == 0) w.piece_cnt[base + tot - 1] = 0;
+    ht = stitch_piece(bytes, w, tb, base + tot - 1, ls, le, ls, (int32_t)min<int64_t>(le, t0 + TILE), t0, st);
+  }
+  if (threadIdx.x == 0) {
+    w.tile_tok[t] = tok + hh + ht;
+    w.huge_hc[2 * t] = hh;
+    w.huge_hc[2 * t + 1] = ht;
+  }
 }
 
 // Pass 5: BPE of the queued pieces.  Work items are wavefront loads: one long
@@ -1759,6 +1974,11 @@ __global__ __launch_bounds__(MERGE_THREADS) __attribute__((amdgpu_waves_per_eu(8
   // (classes longest first, sub-queues in order); pre[4 * QGROUPS] = all
   constexpr int NQ = 4 * QGROUPS;
   __shared__ uint32_t pre[NQ + 1];
+  __shared__ BigSmem big;  // LDS of the fallback rounds
+  // pieces whose stitching failed: exact rounds, a whole workgroup each, first
+  const uint32_t nfall = w.ctr[CTR_NFALL];
+  for (uint32_t f = blockIdx.x; f < nfall; f += gridDim.x)
+    big_fallback(bytes, w, tb, uniform((uint32_t)w.fall_list[f]), big);
   if (threadIdx.x < 64) {
     const int k = (int)threadIdx.x, c = 3 - k / QGROUPS, g = k % QGROUPS;
     const uint32_t it = k < NQ ? (w.qctr[g * QCTR_STRIDE + c] + (8u >> c) - 1) >> (3 - c) : 0u;
@@ -1844,6 +2064,35 @@ __global__ __launch_bounds__(EMIT_THREADS) void k_chunk_sums(Work w, const uint3
   }
 }
 
+// The tokens of a stitched piece that start in [a, b) (inside one tile; their
+// ids sit at their first byte in tmp_ids, -1 at the other bytes), in byte
+// order to out_ids[off ...) (and with OFFS their first bytes to out_starts),
+// never past cap.  Returns their number, the same in every thread.
+template <bool OFFS>
+__device__ uint32_t emit_sparse(const Work& w, int32_t a, int32_t b, uint32_t off, uint32_t cap,
+                                int32_t* __restrict__ out_ids, int32_t* __restrict__ out_starts, uint32_t* red) {
+  const int32_t j0 = a + 4 * (int32_t)threadIdx.x;  // 4 bytes per thread: b - a <= TILE
+  int32_t v[4];
+  uint32_t c = 0;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    v[k] = j0 + k < b ? w.tmp_ids[j0 + k] : -1;
+    c += v[k] >= 0 ? 1u : 0u;
+  }
+  uint32_t tot;
+  uint32_t o = off + block_excl_sum(c, red, &tot);
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    if (v[k] < 0) continue;
+    if (o < cap) {
+      out_ids[o] = v[k];
+      if (OFFS) out_starts[o] = j0 + k;
+    }
+    ++o;
+  }
+  return tot;
+}
+
 // Pass 6, one workgroup per tile: the output offset of the tile's pieces (the
 // tokens of the tiles before it plus a block scan of their counts) and the
 // copy of their tokens: up to 8 by the piece's own thread, up to HUGE_TOKENS
@@ -1870,7 +2119,16 @@ __global__ __launch_bounds__(EMIT_THREADS) void k_emit(Work w, int ntiles, int32
   uint32_t hi;
   const uint32_t pbase = w.tile_pbase[t];
   const uint32_t np = w.tile_cnt[t] & cmask;
+  const uint32_t hh = uniform(w.huge_hc[2 * t]), ht = uniform(w.huge_hc[2 * t + 1]);
   uint32_t off0 = tile_prefix<SB>(w.tile_tok, w.sb_tok, nullptr, t, ~0u, red, &hi);
+  const int32_t t0 = t * TILE;
+  const int32_t tend = (int32_t)min(cap, (uint32_t)(t0 + TILE));
+  // a stitched piece that began before the tile: its tokens that start here
+  // come first (a nonzero stitched count marks it; a fallback zeroes it)
+  if (hh) {
+    const int32_t pe = np ? (int32_t)uniform((uint32_t)w.piece_start[pbase]) : tend;
+    off0 += emit_sparse<OFFS>(w, t0, pe, off0, cap, out_ids, out_starts, red);
+  }
   for (uint32_t k0 = 0; k0 < np; k0 += EMIT_THREADS) {
     const uint32_t k = k0 + threadIdx.x;
     const bool live = k < np;
@@ -1913,6 +2171,11 @@ __global__ __launch_bounds__(EMIT_THREADS) void k_emit(Work w, int ntiles, int32
     }
     off0 += tot;
   }
+  // the tile's last piece, if stitched: its tokens that start in the tile
+  if (ht) {
+    const int32_t ls = (int32_t)uniform((uint32_t)w.piece_start[pbase + np - 1]);
+    off0 += emit_sparse<OFFS>(w, ls, tend, off0, cap, out_ids, out_starts, red);
+  }
   if (t == ntiles - 1 && threadIdx.x == 0) {
     w.ctr[CTR_T] = off0;
     w.tok_off[pbase + np] = (int32_t)off0;
@@ -1936,7 +2199,9 @@ __global__ __launch_bounds__(EMIT_THREADS) void k_emit(Work w, int ntiles, int32
     const uint32_t src = (uint32_t)w.piece_start[p];
     const int tp = (int)(src / TILE);
     const uint32_t pb = w.tile_pbase[tp];
-    const uint32_t dst = tile_prefix<SB>(w.tile_tok, w.sb_tok, nullptr, tp, ~0u, red, &hi) +
+    // (plus the tokens of a stitched piece that began before that tile and
+    // start in it: they come before the tile's own pieces)
+    const uint32_t dst = tile_prefix<SB>(w.tile_tok, w.sb_tok, nullptr, tp, ~0u, red, &hi) + w.huge_hc[2 * tp] +
                          block_reduce(reinterpret_cast<const uint32_t*>(w.piece_cnt) + pb, (int)(p - pb), ~0u, red, &hi);
     for (uint32_t ch = first; ch < nch; ch += gridDim.x) {
       const uint32_t k1 = min(min(cc, (ch + 1) * HUGE_CHUNK), cap - min(cap, dst));  // never past the output
