@@ -94,9 +94,16 @@ struct TileSmem {
   alignas(16) uint16_t ascii[128];
   uint32_t bmap[BMAP_WORDS];
   uint32_t red[8];
+  uint64_t bsw[6][17];   // cl100k-style rules: bit planes of the span's chars (64 per entry)
+  uint32_t cbits[34];    // their start bits by char (tiles with non-ASCII bytes)
   int64_t seq_lo, seq_hi;
   uint32_t carry_fwd, carry_bwd;
   int flag;
+  // cl100k-style rules: the span's chars in order (codes) and their
+  // positions, and the tile's start bits
+  uint32_t cc[SPAN];
+  uint16_t cpos[SPAN];
+  uint32_t sbits[TILE / 32];
   // plen[j]: byte length of the char that ends right before position j (0
   // if unknown: no char start there, or the previous char begins outside the
   // span); filled only when the tile has non-ASCII bytes
@@ -153,12 +160,11 @@ __device__ __forceinline__ uint16_t decode_at(int64_t n, int64_t base, int j, co
       len = 1;
       code = C_O | K_BAD;
     } else {
+      // (block numbers below 4 are single-class blocks: the number is the class)
       uint32_t hi = cp >> 8, u = 0;
       if (hi < (uint32_t)TT_UNI_L1_SIZE) {
-        uint32_t blk = g_uni_l1[hi];
-        uint32_t idx = blk * 64u + ((cp & 255u) >> 2);
-        uint32_t byte = g_uni_l2[idx];
-        u = (byte >> ((cp & 3u) * 2u)) & 3u;
+        const uint32_t blk = g_uni_l1[hi];
+        u = blk < 4u ? blk : (g_uni_l2[blk * 64u + ((cp & 255u) >> 2)] >> ((cp & 3u) * 2u)) & 3u;
       }
       code = u == 1u ? C_L : u == 2u ? C_N : u == 3u ? C_WS : C_O;
     }
@@ -225,9 +231,84 @@ __device__ bool stage_tile(const uint8_t* __restrict__ bytes, int64_t n, const i
   return na;
 }
 
-// Codes of all SPAN positions (class tables of non-ASCII chars read from
-// global memory, where they stay cached), and for non-ASCII tiles the
-// predecessor lengths.
+
+// decode_at for the four contiguous span positions j .. j + 3 (j a multiple
+// of 4), from two staged words (the bytes up to j + 7) and the sequence-start
+// bits of j .. j + 7 held in registers: the same codes, with the LDS reads of
+// the lead and continuation bytes issued together instead of one after
+// another.  Writes the codes and the predecessor lengths; returns whether a
+// char starting at one of the tile's own positions is invalid.
+__device__ __forceinline__ bool decode4(int64_t n, int64_t base, int j, TileSmem& sm) {
+  const uint32_t* raw32 = reinterpret_cast<const uint32_t*>(sm.raw);
+  const uint64_t wb = (uint64_t)raw32[j >> 2] | ((uint64_t)raw32[(j >> 2) + 1] << 32);
+  const int sh = j & 31;
+  const uint32_t b0w = sm.bmap[j >> 5], b1w = sm.bmap[(j >> 5) + 1];
+  const uint32_t bm = sh ? (b0w >> sh) | (b1w << (32 - sh)) : b0w;  // bit i: a sequence starts at j + i
+  bool bad_own = false;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int64_t p = base + j + k;
+    const uint32_t b0 = (uint32_t)(wb >> (8 * k)) & 255u;
+    const bool start = (bm >> k) & 1u;
+    uint32_t code;
+    int len = 1;
+    bool bad = false;
+    if (p < 0 || p >= n) {
+      sm.code[cix(j + k)] = (uint16_t)C_OUT;
+      continue;
+    }
+    if ((b0 & 0xC0u) == 0x80u) {
+      code = C_CONT | (start ? K_BAD : 0u);
+      sm.code[cix(j + k)] = (uint16_t)code;
+      if (start && j + k >= HALO && j + k < HALO + TILE) bad_own = true;
+      continue;
+    }
+    if (b0 < 0x80u) {
+      code = sm.ascii[b0];
+    } else {
+      uint32_t cp = 0;
+      if (b0 >= 0xC2u && b0 <= 0xDFu) { len = 2; cp = b0 & 0x1Fu; }
+      else if (b0 >= 0xE0u && b0 <= 0xEFu) { len = 3; cp = b0 & 0x0Fu; }
+      else if (b0 >= 0xF0u && b0 <= 0xF4u) { len = 4; cp = b0 & 0x07u; }
+      else { bad = true; }
+#pragma unroll
+      for (int i = 1; i < 4; ++i) {
+        if (i >= len || bad) continue;
+        const uint32_t bk = (uint32_t)(wb >> (8 * (k + i))) & 255u;
+        if (p + i >= n || ((bm >> (k + i)) & 1u) || (bk & 0xC0u) != 0x80u) { bad = true; continue; }
+        if (i == 1 && ((b0 == 0xE0u && bk < 0xA0u) || (b0 == 0xEDu && bk > 0x9Fu) ||
+                       (b0 == 0xF0u && bk < 0x90u) || (b0 == 0xF4u && bk > 0x8Fu))) { bad = true; continue; }
+        cp = (cp << 6) | (bk & 0x3Fu);
+      }
+      if (bad) {
+        len = 1;
+        code = C_O | K_BAD;
+      } else {
+        // (block numbers below 4 are single-class blocks: the number is the class)
+        uint32_t hi = cp >> 8, u = 0;
+        if (hi < (uint32_t)TT_UNI_L1_SIZE) {
+          const uint32_t blk = g_uni_l1[hi];
+          u = blk < 4u ? blk : (g_uni_l2[blk * 64u + ((cp & 255u) >> 2)] >> ((cp & 3u) * 2u)) & 3u;
+        }
+        code = u == 1u ? C_L : u == 2u ? C_N : u == 3u ? C_WS : C_O;
+      }
+    }
+    // a continuation byte right after a complete char is stray
+    const bool last = p + len >= n || ((bm >> (k + len)) & 1u);
+    if (!last && !bad && (((uint32_t)(wb >> (8 * (k + len))) & 0xC0u) == 0x80u)) code |= K_BAD;
+    code |= (uint32_t)(len - 1) << K_LEN_SHIFT;
+    if (start) code |= K_SEQ_START;
+    if (last) code |= K_SEQ_LAST;
+    sm.code[cix(j + k)] = (uint16_t)code;
+    sm.plen[j + k + len] = (uint8_t)len;
+    if ((code & K_BAD) && j + k >= HALO && j + k < HALO + TILE) bad_own = true;
+  }
+  return bad_own;
+}
+
+// Codes of all SPAN positions (non-ASCII chars classed from the two-level
+// Unicode table in global memory, where it stays cached), and for non-ASCII
+// tiles the predecessor lengths.
 // Returns true if some char starting inside the tile is invalid UTF-8.
 __device__ bool decode_span(int64_t n, int64_t t0, bool na, TileSmem& sm) {
   const int tid = threadIdx.x;
@@ -250,12 +331,10 @@ __device__ bool decode_span(int64_t n, int64_t t0, bool na, TileSmem& sm) {
     __syncthreads();
     return false;
   }
-  for (int j = tid; j < SPAN; j += PT_THREADS) {
-    uint16_t c = decode_at(n, t0 - HALO, j, sm);
-    sm.code[cix(j)] = c;
-    if ((c & K_BAD) && j >= HALO && j < HALO + TILE) bad = true;
-    if (is_char(c)) sm.plen[j + clen(c)] = (uint8_t)clen(c);
-  }
+  // four contiguous positions per thread: positions 0 .. 1023, and threads
+  // 0 .. 7 the last 32 of the span as well
+  bad = decode4(n, t0 - HALO, PT_CHUNK * tid, sm);
+  if (tid < (SPAN - PT_CHUNK * PT_THREADS) / PT_CHUNK) bad |= decode4(n, t0 - HALO, PT_CHUNK * (PT_THREADS + tid), sm);
   __syncthreads();
   return bad;
 }
@@ -407,6 +486,28 @@ __device__ uint32_t block_excl_bwd(uint32_t x, uint32_t* red, uint32_t* total) {
   return Op::combine(exc, post);
 }
 
+// The two run-state scans of a tile in one pass: the exclusive forward scan
+// of fx (left to right) and the exclusive backward scan of bx (right to
+// left) over the block, with one barrier.  red needs 8 words.
+__device__ __forceinline__ void block_excl_fwd_bwd(uint32_t fx, uint32_t bx, uint32_t* red, uint32_t* ef,
+                                                   uint32_t* eb) {
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const uint32_t incf = wave_incl_fwd<FwdOp>(fx, lane);
+  const uint32_t incb = wave_incl_bwd<BwdOp>(bx, lane);
+  const uint32_t excf = dpp_id<0x138>(FwdOp::IDENT, incf);
+  const uint32_t excb = dpp_id<0x130>(BwdOp::IDENT, incb);
+  if (lane == 63) red[wid] = incf;
+  if (lane == 0) red[4 + wid] = incb;
+  __syncthreads();
+  uint32_t pre = FwdOp::IDENT, post = BwdOp::IDENT;
+  for (int v = 0; v < PT_THREADS / 64; ++v) {
+    if (v < wid) pre = FwdOp::combine(pre, red[v]);
+  }
+  for (int v = PT_THREADS / 64 - 1; v > wid; --v) post = BwdOp::combine(red[4 + v], post);
+  *ef = FwdOp::combine(pre, excf);
+  *eb = BwdOp::combine(excb, post);
+}
+
 // Butterfly step inside each half of the wavefront: lane l reads lane l ^ d
 // (d < 32).  ds_swizzle takes the pattern as an immediate, so a kernel with
 // many reductions keeps no per-lane address registers alive for them.
@@ -491,7 +592,6 @@ __global__ __launch_bounds__(PT_THREADS) void k_tile_summary(const uint8_t* __re
   const int64_t t0 = (int64_t)blockIdx.x * TILE;
   const int lane = (int)(threadIdx.x & 63u), wid = (int)(threadIdx.x >> 6);
   const bool na = stage_tile(bytes, n, offs, nseq, t0, sm);
-  __syncthreads();
   // Usually the leading and the trailing run of a tile end within EDGE
   // positions: then decoding those positions decides both summaries (the
   // Unicode table is read from global memory for these few chars).
@@ -741,6 +841,247 @@ __device__ __forceinline__ bool pred_cl100k(const uint16_t* c, const uint8_t* pl
   return false;
 }
 
+
+// cl100k-style start bits, bit-sliced.  The span's chars in order (char
+// index x; own chars [c_lo, e)) are held as bit planes: lane l of a wavefront
+// holds bits i = 0..31 of word l, char x = c_lo - 32 + 32 l + i (word 0: the
+// chars before the own ones; then the own chars and the right context), so
+// one VALU instruction evaluates a rule at up to 1088 positions.  The rules
+// read at most four chars back and one ahead, except three facts that a
+// whole run decides: a digit starts a group iff its offset in its digit run
+// is a multiple of 3; a whitespace char after a CR/LF starts a piece iff its
+// run of non-CR/LF whitespace is not followed by a CR/LF, or the CR/LF run
+// before it follows an "other" char (which absorbed the CR/LFs).  Runs are
+// spread over words with carry chains (a fill by addition, its carries
+// between words from two ballots); runs that cross the tile's ends take the
+// tile's forward and backward run states.
+constexpr int BS_WORDS = 34;            // 1088 chars: 32 before, 1024 own, 32 after
+constexpr int BS_CHUNKS = BS_WORDS / 2;  // 64-char ballot chunks
+constexpr int BS_PLANES = 6;            // class-index bits 0..3, sequence start, sequence last
+
+// Class index of a char code: 0 no char; letters 1 plain, 2 s/t/m/d, 3 r/v,
+// 4 l, 5 e (either case: the contraction letters); 8 digit; 9 other,
+// 10 apostrophe; 12 whitespace, 13 space; 14 CR/LF.
+__device__ __forceinline__ uint32_t cl_index(uint32_t code) {
+  constexpr uint64_t LTAB = 1ull | 2ull << 4 | 2ull << 8 | 3ull << 12 | 5ull << 16 | 3ull << 20 | 2ull << 24 |
+                            4ull << 28 | 2ull << 32;  // by letter type 0..8
+  constexpr uint32_t CTAB = 8u << (4 * C_N) | 9u << (4 * C_O) | 12u << (4 * C_WS) | 14u << (4 * C_WN);
+  const uint32_t k = cls_of(code), lt = (code >> K_LETTER_SHIFT) & 15u;
+  if (k == C_L) return (uint32_t)(LTAB >> (4 * lt)) & 15u;
+  return ((CTAB >> (4 * k)) & 15u) + ((code >> 10) & 1u) + ((code >> 11) & 1u);  // + K_SP, + K_AP
+}
+
+// x from the char S places before / after (bits shifted in across words).
+template <int S>
+__device__ __forceinline__ uint32_t bs_up(uint32_t x) {
+  return __builtin_amdgcn_alignbit(x, dpp_id<0x138>(0u, x), 32 - S);
+}
+template <int S>
+__device__ __forceinline__ uint32_t bs_dn(uint32_t x) {
+  return __builtin_amdgcn_alignbit(dpp_id<0x130>(0u, x), x, S);
+}
+
+// Bits of R reached from a seed of S going up through contiguous bits of R,
+// across words.  S lies in R, at most one seed per block of R.
+__device__ __forceinline__ uint32_t bs_fill_up(uint32_t R, uint32_t S, int lane) {
+  const uint32_t sum = R + S;
+  const uint64_t G = __ballot(sum < R);                  // carry out of the word
+  const uint64_t P = G | __ballot(sum == 0xFFFFFFFFu);   // carry out given a carry in
+  const uint64_t C = (G + P) ^ G ^ P;                    // carry into each word
+  return R & ~(R + S + ((uint32_t)(C >> lane) & 1u));
+}
+
+// The same going down (seeds at the blocks' tops): the fill on reversed bits,
+// with the carries between words running from the last word to the first.
+__device__ __forceinline__ uint32_t bs_fill_down(uint32_t R, uint32_t S, int lane) {
+  const uint32_t r = __builtin_bitreverse32(R), s = __builtin_bitreverse32(S);
+  const uint32_t sum = r + s;
+  const uint64_t G = __builtin_bitreverse64(__ballot(sum < r));
+  const uint64_t P = G | __builtin_bitreverse64(__ballot(sum == 0xFFFFFFFFu));
+  const uint64_t C = (G + P) ^ G ^ P;
+  return __builtin_bitreverse32(r & ~(r + s + ((uint32_t)(C >> (63 - lane)) & 1u)));
+}
+
+// Bits of this lane's word with char index in [lo, hi).
+__device__ __forceinline__ uint32_t bs_range(int x0, int lo, int hi) {
+  const int a = min(max(lo - x0, 0), 32), b = min(max(hi - x0, 0), 32);
+  const uint32_t ma = a >= 32 ? 0u : ~0u << a;
+  const uint32_t mb = b >= 32 ? ~0u : ~(~0u << b);
+  return ma & mb;
+}
+
+// Start bits of this lane's word (one wavefront; lanes >= BS_WORDS hold no
+// chars).  lf: forward run state of the chars before c_lo; rb: backward run
+// state of the chars from e on.
+__device__ uint32_t cl_word_bits(const uint32_t* pl, int lane, int c_lo, int e, uint32_t lf, uint32_t rb) {
+  const uint32_t b0 = pl[0], b1 = pl[1], b2 = pl[2], b3 = pl[3], SS = pl[4], SL = pl[5];
+  const int x0 = c_lo - 32 + 32 * lane;
+  const uint32_t CH = b0 | b1 | b2 | b3;
+  const uint32_t L = ~b3 & (b0 | b1 | b2);
+  const uint32_t N = b3 & ~b2 & ~b1 & ~b0;
+  const uint32_t O = b3 & ~b2 & (b0 ^ b1);
+  const uint32_t AP = b3 & ~b2 & b1 & ~b0;
+  const uint32_t W = b3 & b2, WS = W & ~b1, SP = WS & b0, WN = W & b1;
+  // digits at offset 0 mod 3 in their run: fill each run with its start's
+  // residue (mod 3) of the char index
+  // X0: the span's first char, whose predecessor is not seen (a run start
+  // only if a sequence starts there)
+  const uint32_t X0 = bs_range(x0, 0, 1);
+  const uint32_t Np = bs_up<1>(N);
+  const uint32_t RSN = N & (~Np | SS) & ~(X0 & ~SS);
+  const uint32_t Q = N & ~RSN;
+  const int base = ((x0 % 3) + 3) % 3;
+  const uint32_t P0 = 0x49249249u;
+  const uint32_t M0 = P0 << ((3 - base) % 3), M1 = P0 << ((4 - base) % 3), M2 = P0 << ((5 - base) % 3);
+  uint32_t S0 = RSN & M0, S1 = RSN & M1;
+  if ((lf & 1u) && ((lf >> 2) & 7u) == C_N) {
+    // the digit run that reaches c_lo, if it began before the span: its
+    // start's residue, seeded at the span's first char
+    const int r0 = (((c_lo - (int)((lf >> 8) & 3u)) % 3) + 3) % 3;
+    if (r0 == 0) S0 |= N & X0;
+    if (r0 == 1) S1 |= N & X0;
+  }
+  const uint32_t F0 = bs_fill_up(Q, bs_up<1>(S0) & Q, lane) | S0;
+  const uint32_t F1 = bs_fill_up(Q, bs_up<1>(S1) & Q, lane) | S1;
+  const uint32_t F2 = N & ~F0 & ~F1;
+  const uint32_t NPH = (F0 & M0) | (F1 & M1) | (F2 & M2);
+  // whitespace runs followed by a CR/LF, spread down from the run's top (runs
+  // cut at e; one that goes on past e takes the backward state there)
+  const uint32_t lim = bs_range(x0, -(1 << 20), e);
+  uint32_t FW = WS & bs_dn<1>(WN) & ~SL & lim;
+  const bool rb_ws_nl = (rb & 1u) && ((rb >> 2) & 7u) == C_WS && ((rb >> 5) & 7u) == C_WN;
+  if (rb_ws_nl) FW |= WS & bs_dn<1>(WS) & ~SL & bs_range(x0, e - 1, e);
+  const uint32_t ENDS = WS & ~bs_fill_down(WS & ~SL & lim, FW, lane);
+  // CR/LF runs right after an "other" char
+  const uint32_t RN = WN & ~SS;
+  uint32_t SN = RN & ~bs_up<1>(WN) & bs_up<1>(O);
+  if ((lf & 1u) && ((lf >> 2) & 7u) == C_WN && ((lf >> 5) & 7u) == C_O) SN |= RN & X0;
+  const uint32_t ABSO = bs_fill_up(RN, SN, lane);
+  // contractions (ASCII letters, either case): the letter after a suffix of
+  // one or two letters that follows a piece-starting apostrophe starts a piece
+  const uint32_t OSp = bs_up<1>(O | SP);
+  uint32_t AFTER = 0u;
+  if (__ballot(AP != 0u)) {
+    const uint32_t C1 = ~b3 & ~b2 & b1 & ~b0, RV = ~b3 & ~b2 & b1 & b0;
+    const uint32_t LL = ~b3 & b2 & ~b1 & ~b0, E = ~b3 & b2 & ~b1 & b0;
+    const uint32_t APS = AP & (SS | ~OSp);
+    const uint32_t PRE = ~SS & bs_up<1>(APS);
+    const uint32_t CLEN1 = PRE & C1;
+    const uint32_t CLEN2 = PRE & ~SL & ((RV & bs_dn<1>(E)) | (LL & bs_dn<1>(LL)));
+    AFTER = ~SS & (bs_up<1>(CLEN1) | bs_up<1>(~SS & bs_up<1>(CLEN2)));
+  }
+  const uint32_t Lp = bs_up<1>(L), Op = bs_up<1>(O), WSp = bs_up<1>(WS), Wp = bs_up<1>(W);
+  const uint32_t WNp = bs_up<1>(WN), SSp = bs_up<1>(SS), SPp = bs_up<1>(SP);
+  const uint32_t BN = N & (~Np | NPH);
+  const uint32_t BL = L & ((Lp & AFTER) | (~Lp & ~WSp & ~Op) | (Op & ~SSp & bs_up<1>(OSp)));
+  const uint32_t BO = O & ~Op & ~SPp;
+  const uint32_t BWN = WN & ~Wp & ~Op;
+  const uint32_t BWS = WS & (~Wp | (WNp & (ENDS | bs_up<1>(ABSO))) | (WSp & ~SL & ~bs_dn<1>(W)));
+  return CH & (SS | BN | BL | BO | BWN | BWS) & bs_range(x0, c_lo, e);
+}
+
+// The tile's cl100k-style start bits: this thread's 4 (its positions
+// HALO + 4 tid ...) and, in *cnt, the tile's count (the same in every thread).
+// The tile's carries (sm.carry_fwd / carry_bwd) must be set.
+template <bool ASCII>
+__device__ uint32_t cl100k_bits(TileSmem& sm, int64_t n, int64_t t0, uint32_t* cnt) {
+  const int tid = (int)threadIdx.x, lane = tid & 63, wid = (int)uniform((uint32_t)tid >> 6);
+  int c_lo = HALO, n_own = TILE, nc = SPAN;
+  if (!ASCII) {
+    // the span's chars in order: left halo, own, right halo
+    const int j0 = HALO + PT_CHUNK * tid;
+    uint32_t own = 0;
+#pragma unroll
+    for (int k = 0; k < PT_CHUNK; ++k) own += is_char(sm.code[cix(j0 + k)]) ? 1u : 0u;
+    uint32_t n_o;
+    const uint32_t own_base = block_excl_sum(own, sm.red, &n_o);
+    // the halos, lanes 0..15 the left one and 16..31 the right one (every
+    // wavefront counts them, so all agree on the indices; wavefront 0 writes them)
+    const int hj = lane < HALO ? lane : TILE + lane;
+    const bool hc = lane < 2 * HALO && is_char(sm.code[cix(hj)]);
+    const uint64_t hm = __ballot(hc);
+    const uint32_t n_left = (uint32_t)__popcll(hm & 0xFFFFull);
+    c_lo = (int)uniform(n_left);
+    n_own = (int)uniform(n_o);
+    nc = c_lo + n_own + (int)__popcll(hm & 0xFFFF0000ull);
+    uint32_t at = n_left + own_base;
+#pragma unroll
+    for (int k = 0; k < PT_CHUNK; ++k) {
+      const uint32_t c = sm.code[cix(j0 + k)];
+      if (is_char(c)) {
+        sm.cc[at] = c;
+        sm.cpos[at] = (uint16_t)(j0 + k);
+        ++at;
+      }
+    }
+    if (wid == 0 && hc) {
+      const uint32_t below = (uint32_t)__popcll(hm & ((1ull << lane) - 1ull));
+      const uint32_t idx = lane < HALO ? below : (uint32_t)(c_lo + n_own) + below - n_left;
+      sm.cc[idx] = sm.code[cix(hj)];
+      sm.cpos[idx] = (uint16_t)hj;
+    }
+    if (tid < TILE / 32) sm.sbits[tid] = 0u;
+    __syncthreads();
+  }
+  // bit planes, 64 chars per ballot, chunks dealt to the wavefronts
+  for (int c = wid; c < BS_CHUNKS; c += PT_THREADS / 64) {
+    const int x = c_lo - 32 + 64 * c + lane;
+    uint32_t code = C_OUT;
+    if (ASCII) {
+      const int64_t p = t0 - HALO + x;
+      if (x >= 0 && x < SPAN && p >= 0 && p < n) {
+        code = sm.ascii[reinterpret_cast<const uint8_t*>(sm.raw)[x] & 127u];
+        if (bmap_bit(sm.bmap, x)) code |= K_SEQ_START;
+        if (p + 1 >= n || bmap_bit(sm.bmap, x + 1)) code |= K_SEQ_LAST;
+      }
+    } else if (x >= 0 && x < nc) {
+      code = sm.cc[x];
+    }
+    const uint32_t idx = cl_index(code);
+    uint64_t m[BS_PLANES];
+    m[0] = __ballot(idx & 1u);
+    m[1] = __ballot(idx & 2u);
+    m[2] = __ballot(idx & 4u);
+    m[3] = __ballot(idx & 8u);
+    m[4] = __ballot(idx != 0u && (code & K_SEQ_START));
+    m[5] = __ballot(idx != 0u && (code & K_SEQ_LAST));
+    if (lane == 0) {
+#pragma unroll
+      for (int k = 0; k < BS_PLANES; ++k) sm.bsw[k][c] = m[k];
+    }
+  }
+  __syncthreads();
+  if (wid == 0) {
+    uint32_t pl[BS_PLANES];
+#pragma unroll
+    for (int k = 0; k < BS_PLANES; ++k)
+      pl[k] = lane < BS_WORDS ? reinterpret_cast<const uint32_t*>(sm.bsw[k])[lane] : 0u;
+    const uint32_t B = cl_word_bits(pl, lane, c_lo, c_lo + n_own, uniform(sm.carry_fwd), uniform(sm.carry_bwd));
+    const uint32_t tot = wave_incl_fwd<SumOp>((uint32_t)__popc(B), lane);
+    if (lane == 63) sm.red[0] = tot;
+    if (ASCII) {
+      if (lane >= 1 && lane <= TILE / 32) sm.sbits[lane - 1] = B;
+    } else if (lane < BS_WORDS) {
+      sm.cbits[lane] = B;
+    }
+  }
+  __syncthreads();
+  *cnt = sm.red[0];
+  if (!ASCII) {
+    // own char o sits at word 1 + o / 32: its start bit goes to its byte position
+#pragma unroll
+    for (int k = 0; k < PT_CHUNK; ++k) {
+      const int o = PT_CHUNK * tid + k;
+      if (o < n_own && ((sm.cbits[1 + (o >> 5)] >> (o & 31)) & 1u)) {
+        const int p = (int)sm.cpos[c_lo + o] - HALO;
+        atomicOr(&sm.sbits[p >> 5], 1u << (p & 31));
+      }
+    }
+    __syncthreads();
+  }
+  return (sm.sbits[tid >> 3] >> ((tid & 7) * PT_CHUNK)) & 15u;
+}
+
 __device__ __forceinline__ int64_t err_code(uint32_t e) {
   return (e & ERR_OFFSETS) ? -7 : (e & ERR_UTF8) ? -5 : 0;
 }
@@ -820,8 +1161,8 @@ __global__ __launch_bounds__(PT_THREADS) void k_pretok(const uint8_t* __restrict
     for (int i = threadIdx.x; i < QGROUPS * QCTR_STRIDE; i += PT_THREADS) w.qctr[i] = 0u;
   }
   const bool na = stage_tile(bytes, n, offs, nseq, t0, sm);
-  // pure-ASCII tiles under GPT-2-style rules need no decode pass
-  const bool bad = (PAT == 0 && !na) ? false : decode_span(n, t0, na, sm);
+  // pure-ASCII tiles need no decode pass (their masks come from the bytes)
+  const bool bad = na ? decode_span(n, t0, na, sm) : false;
   bool bad_off = false;
   if (offs) {
     for (int64_t q = (int64_t)t * PT_THREADS + threadIdx.x; q <= nseq; q += (int64_t)ntiles * PT_THREADS) {
@@ -851,39 +1192,8 @@ __global__ __launch_bounds__(PT_THREADS) void k_pretok(const uint8_t* __restrict
     }
   } else {
     tile_carries(w, t, ntiles, sm);
-    uint32_t tot;
-    uint32_t sb = BwdOp::combine(block_excl_bwd<BwdOp>(chunk_bwd(sm), sm.red, &tot), sm.carry_bwd);
-    uint32_t ends = 0;
-#pragma unroll
-    for (int k = PT_CHUNK - 1; k >= 0; --k) {
-      uint32_t c = sm.code[cix(j0 + k)];
-      if (is_char(c)) {
-        sb = BwdOp::combine(BwdOp::elem(c), sb);
-        if (((sb >> 5) & 7u) != C_WN) ends |= 1u << k;
-      }
-    }
-    uint32_t sf = FwdOp::combine(sm.carry_fwd, block_excl_fwd<FwdOp>(chunk_fwd(sm), sm.red, &tot));
-    if (na) {
-#pragma unroll
-      for (int k = 0; k < PT_CHUNK; ++k) {
-        uint32_t c = sm.code[cix(j0 + k)];
-        if (is_char(c)) {
-          uint32_t before = sf;
-          sf = FwdOp::combine(sf, FwdOp::elem(c));
-          if (pred_cl100k<false>(sm.code, sm.plen, j0 + k, before, sf, (ends >> k) & 1u)) bits |= 1u << k;
-        }
-      }
-    } else {
-#pragma unroll
-      for (int k = 0; k < PT_CHUNK; ++k) {
-        uint32_t c = sm.code[cix(j0 + k)];
-        if (is_char(c)) {
-          uint32_t before = sf;
-          sf = FwdOp::combine(sf, FwdOp::elem(c));
-          if (pred_cl100k<true>(sm.code, sm.plen, j0 + k, before, sf, (ends >> k) & 1u)) bits |= 1u << k;
-        }
-      }
-    }
+    bits = na ? cl100k_bits<false>(sm, n, t0, &cnt) : cl100k_bits<true>(sm, n, t0, &cnt);
+    counted = true;
   }
   w.flags[(int64_t)t * PT_THREADS + threadIdx.x] = (uint16_t)bits;
   if (!counted) cnt = block_sum(__popc(bits), sm.red);
