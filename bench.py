@@ -608,9 +608,9 @@ def main():
                 continue
             r = measure(name, args.steps, args.warmup, graph=not args.no_graph, counters=counters)
             others[name] = r
-            print("%s: p50 %.4f ms, %.3g chars/s, graph p50 %s ms" % (
-                name, r["p50_ms"], r["chars_per_s"], "%.4f" % r["graph_p50_ms"] if "graph_p50_ms" in r else "-"),
-                file=sys.stderr, flush=True)
+            print("%s: p50 %.4f ms, %.3g chars/s, graph p50 %s ms, kernels (us) %s" % (
+                name, r["p50_ms"], r["chars_per_s"], "%.4f" % r["graph_p50_ms"] if "graph_p50_ms" in r else "-",
+                r.get("kernels_us")), file=sys.stderr, flush=True)
     sess = run_session(min(args.steps, 50)) if args.workload == "c2" and not args.no_session and not args.only \
         else None
 

@@ -144,6 +144,7 @@ size_t layout(int64_t n, char* base, Work* w) {
   t.tile_fwd = (uint32_t*)take(ntiles * 4);
   t.tile_bwd = (uint32_t*)take(ntiles * 4);
   t.tile_cnt = (uint32_t*)take(ntiles * 4);
+  t.codes = (uint8_t*)take(ntiles * TILE + 64);
   t.flags = (uint16_t*)take(ntiles * PT_THREADS * 2);
   t.piece_start = (int32_t*)take((nn + 1) * 4);
   t.piece_cnt = (int32_t*)take(nn * 4);

@@ -99,9 +99,10 @@ struct TileSmem {
   int64_t seq_lo, seq_hi;
   uint32_t carry_fwd, carry_bwd;
   int flag;
-  // cl100k-style rules: the span's chars in order (codes) and their
-  // positions, and the tile's start bits
-  uint32_t cc[SPAN];
+  // cl100k-style rules: the span's code bytes (by position), its chars in
+  // order (code bytes) and their positions, and the tile's start bits
+  alignas(16) uint8_t cb[SPAN + 16];
+  alignas(16) uint8_t cc[SPAN + 16];
   uint16_t cpos[SPAN];
   uint32_t sbits[TILE / 32];
   // plen[j]: byte length of the char that ends right before position j (0
@@ -232,76 +233,84 @@ __device__ bool stage_tile(const uint8_t* __restrict__ bytes, int64_t n, const i
 }
 
 
+// decode_at for four contiguous positions p0 .. p0 + 3 held in registers: wb
+// the bytes p0 .. p0 + 7 (0 past the text), bm bit i: a sequence starts at
+// p0 + i.  The same codes, computed without branches: byte kinds from the
+// count of leading one bits, the continuation bytes of a lead checked
+// together as one word, the code point assembled from all four payloads and
+// shifted to the char's length; then the table blocks and class bits of the
+// four are loaded together, so a thread waits for two global loads, not
+// eight.  len[k]: byte length of the char at p0 + k (0 if none starts there).
+__device__ __forceinline__ void decode4_regs(uint64_t wb, uint32_t bm, int64_t p0, int64_t n, const uint16_t* ascii,
+                                             uint32_t code[4], int len_out[4]) {
+  uint32_t cp[4];
+  bool tab[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int64_t p = p0 + k;
+    const uint32_t w4 = (uint32_t)(wb >> (8 * k));  // bytes p .. p + 3
+    const uint32_t b0 = w4 & 255u, b1 = (w4 >> 8) & 255u;
+    const uint32_t ones = (uint32_t)__clz(~(b0 << 24));  // leading one bits of b0
+    const bool start = (bm >> k) & 1u;
+    const bool in = p >= 0 && p < n;
+    const bool ascii_b = ones == 0u, cont = ones == 1u;
+    const bool lead = ones - 2u <= 2u && b0 >= 0xC2u && b0 <= 0xF4u;
+    const uint32_t len = lead ? ones : 1u;
+    const uint32_t need = (0xFFFFFFFFu >> (32u - 8u * len)) & ~0xFFu;  // the continuation bytes
+    const bool conts = (((w4 & 0xC0C0C000u) ^ 0x80808000u) & need) == 0u;
+    const bool seq_ok = ((bm >> (k + 1)) & ((1u << (len - 1u)) - 1u)) == 0u;
+    const bool second = !((b0 == 0xE0u && b1 < 0xA0u) || (b0 == 0xEDu && b1 > 0x9Fu) || (b0 == 0xF0u && b1 < 0x90u) ||
+                          (b0 == 0xF4u && b1 > 0x8Fu));
+    const bool good_mb = lead && conts && seq_ok && p + (int64_t)len <= n && second;
+    const bool bad_lead = !ascii_b && !cont && !good_mb;
+    const uint32_t clen = bad_lead ? 1u : len;
+    const uint32_t full = ((b0 & (0x7Fu >> ones)) << 18) | (((w4 >> 8) & 0x3Fu) << 12) | (((w4 >> 16) & 0x3Fu) << 6) |
+                          ((w4 >> 24) & 0x3Fu);
+    cp[k] = full >> (6u * (4u - len));
+    tab[k] = in && good_mb && (cp[k] >> 8) < (uint32_t)TT_UNI_L1_SIZE;  // else class 0 (other)
+    // a continuation byte right after a complete char is stray
+    const bool last = p + (int64_t)clen >= n || ((bm >> (k + clen)) & 1u);
+    const bool stray = !last && !bad_lead && (((uint32_t)(wb >> (8 * (k + clen))) & 0xC0u) == 0x80u);
+    uint32_t c = ascii_b ? (uint32_t)ascii[b0 & 127u] : bad_lead ? (C_O | K_BAD) : 0u;
+    c |= ((clen - 1u) << K_LEN_SHIFT) | (start ? K_SEQ_START : 0u) | (last ? K_SEQ_LAST : 0u) | (stray ? K_BAD : 0u);
+    code[k] = !in ? (uint32_t)C_OUT : cont ? (C_CONT | (start ? K_BAD : 0u)) : c;
+    len_out[k] = in && !cont ? (int)clen : 0;
+  }
+  // class of the multibyte chars: block numbers below 4 are single-class
+  // blocks (the number is the class)
+  uint32_t blk[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) blk[k] = tab[k] ? (uint32_t)g_uni_l1[cp[k] >> 8] : 0u;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    if (cls_of(code[k]) == 0u) {
+      // a valid multibyte char (class bits still 0)
+      const uint32_t u = !tab[k] ? 0u : blk[k] < 4u ? blk[k]
+                       : (g_uni_l2[blk[k] * 64u + ((cp[k] & 255u) >> 2)] >> ((cp[k] & 3u) * 2u)) & 3u;
+      code[k] |= u == 1u ? C_L : u == 2u ? C_N : u == 3u ? C_WS : C_O;
+    }
+  }
+}
+
 // decode_at for the four contiguous span positions j .. j + 3 (j a multiple
-// of 4), from two staged words (the bytes up to j + 7) and the sequence-start
-// bits of j .. j + 7 held in registers: the same codes, with the LDS reads of
-// the lead and continuation bytes issued together instead of one after
-// another.  Writes the codes and the predecessor lengths; returns whether a
-// char starting at one of the tile's own positions is invalid.
+// of 4) of a staged tile: writes the codes and the predecessor lengths;
+// returns whether a char starting at one of the tile's own positions is
+// invalid.
 __device__ __forceinline__ bool decode4(int64_t n, int64_t base, int j, TileSmem& sm) {
   const uint32_t* raw32 = reinterpret_cast<const uint32_t*>(sm.raw);
   const uint64_t wb = (uint64_t)raw32[j >> 2] | ((uint64_t)raw32[(j >> 2) + 1] << 32);
   const int sh = j & 31;
   const uint32_t b0w = sm.bmap[j >> 5], b1w = sm.bmap[(j >> 5) + 1];
   const uint32_t bm = sh ? (b0w >> sh) | (b1w << (32 - sh)) : b0w;  // bit i: a sequence starts at j + i
+  uint32_t code[4];
+  int len[4];
+  decode4_regs(wb, bm, base + j, n, sm.ascii, code, len);
   bool bad_own = false;
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
-    const int64_t p = base + j + k;
-    const uint32_t b0 = (uint32_t)(wb >> (8 * k)) & 255u;
-    const bool start = (bm >> k) & 1u;
-    uint32_t code;
-    int len = 1;
-    bool bad = false;
-    if (p < 0 || p >= n) {
-      sm.code[cix(j + k)] = (uint16_t)C_OUT;
-      continue;
-    }
-    if ((b0 & 0xC0u) == 0x80u) {
-      code = C_CONT | (start ? K_BAD : 0u);
-      sm.code[cix(j + k)] = (uint16_t)code;
-      if (start && j + k >= HALO && j + k < HALO + TILE) bad_own = true;
-      continue;
-    }
-    if (b0 < 0x80u) {
-      code = sm.ascii[b0];
-    } else {
-      uint32_t cp = 0;
-      if (b0 >= 0xC2u && b0 <= 0xDFu) { len = 2; cp = b0 & 0x1Fu; }
-      else if (b0 >= 0xE0u && b0 <= 0xEFu) { len = 3; cp = b0 & 0x0Fu; }
-      else if (b0 >= 0xF0u && b0 <= 0xF4u) { len = 4; cp = b0 & 0x07u; }
-      else { bad = true; }
-#pragma unroll
-      for (int i = 1; i < 4; ++i) {
-        if (i >= len || bad) continue;
-        const uint32_t bk = (uint32_t)(wb >> (8 * (k + i))) & 255u;
-        if (p + i >= n || ((bm >> (k + i)) & 1u) || (bk & 0xC0u) != 0x80u) { bad = true; continue; }
-        if (i == 1 && ((b0 == 0xE0u && bk < 0xA0u) || (b0 == 0xEDu && bk > 0x9Fu) ||
-                       (b0 == 0xF0u && bk < 0x90u) || (b0 == 0xF4u && bk > 0x8Fu))) { bad = true; continue; }
-        cp = (cp << 6) | (bk & 0x3Fu);
-      }
-      if (bad) {
-        len = 1;
-        code = C_O | K_BAD;
-      } else {
-        // (block numbers below 4 are single-class blocks: the number is the class)
-        uint32_t hi = cp >> 8, u = 0;
-        if (hi < (uint32_t)TT_UNI_L1_SIZE) {
-          const uint32_t blk = g_uni_l1[hi];
-          u = blk < 4u ? blk : (g_uni_l2[blk * 64u + ((cp & 255u) >> 2)] >> ((cp & 3u) * 2u)) & 3u;
-        }
-        code = u == 1u ? C_L : u == 2u ? C_N : u == 3u ? C_WS : C_O;
-      }
-    }
-    // a continuation byte right after a complete char is stray
-    const bool last = p + len >= n || ((bm >> (k + len)) & 1u);
-    if (!last && !bad && (((uint32_t)(wb >> (8 * (k + len))) & 0xC0u) == 0x80u)) code |= K_BAD;
-    code |= (uint32_t)(len - 1) << K_LEN_SHIFT;
-    if (start) code |= K_SEQ_START;
-    if (last) code |= K_SEQ_LAST;
-    sm.code[cix(j + k)] = (uint16_t)code;
-    sm.plen[j + k + len] = (uint8_t)len;
-    if ((code & K_BAD) && j + k >= HALO && j + k < HALO + TILE) bad_own = true;
+    sm.code[cix(j + k)] = (uint16_t)code[k];
+    if (len[k]) sm.plen[j + k + len[k]] = (uint8_t)len[k];
+    if ((code[k] & K_BAD) && j + k >= HALO && j + k < HALO + TILE) bad_own = true;
   }
   return bad_own;
 }
@@ -579,79 +588,159 @@ __device__ __forceinline__ uint32_t chunk_bwd(const TileSmem& sm) {
   return s;
 }
 
-// Pass 1 (cl100k-style rules only): forward and backward run summaries of
-// every tile, so that pass 2 can resolve runs that cross tiles (digit-group
-// phase, the last newline of a whitespace run, newlines absorbed after
-// punctuation) without a second look at distant bytes.
-constexpr int EDGE = 64;  // positions at each tile end decoded first
+// Class index of a char code: 0 no char; letters 1 plain, 2 s/t/m/d, 3 r/v,
+// 4 l, 5 e (either case: the contraction letters); 8 digit; 9 other,
+// 10 apostrophe; 12 whitespace, 13 space; 14 CR/LF.
+__device__ __forceinline__ uint32_t cl_index(uint32_t code) {
+  constexpr uint64_t LTAB = 1ull | 2ull << 4 | 2ull << 8 | 3ull << 12 | 5ull << 16 | 3ull << 20 | 2ull << 24 |
+                            4ull << 28 | 2ull << 32;  // by letter type 0..8
+  constexpr uint32_t CTAB = 8u << (4 * C_N) | 9u << (4 * C_O) | 12u << (4 * C_WS) | 14u << (4 * C_WN);
+  const uint32_t k = cls_of(code), lt = (code >> K_LETTER_SHIFT) & 15u;
+  if (k == C_L) return (uint32_t)(LTAB >> (4 * lt)) & 15u;
+  return ((CTAB >> (4 * k)) & 15u) + ((code >> 10) & 1u) + ((code >> 11) & 1u);  // + K_SP, + K_AP
+}
 
+// Code byte of a text byte for the cl100k-style rules (written by
+// k_tile_summary, read by k_pretok): bits 0-3 the class index of the char
+// starting there (0: no char starts there), bit 4 a sequence starts with that
+// char, bit 5 its sequence ends with it, bit 7 invalid UTF-8 starts there.
+constexpr uint32_t CB_SS = 1u << 4, CB_SL = 1u << 5, CB_BAD = 1u << 7;
+
+__device__ __forceinline__ uint32_t code_byte(uint32_t code) {
+  return cl_index(code) | ((code & K_SEQ_START) ? CB_SS : 0u) | ((code & K_SEQ_LAST) ? CB_SL : 0u) |
+         ((code & K_BAD) ? CB_BAD : 0u);
+}
+
+// First index s in [0, cnt) with a[s] >= v (cnt if none), by one wavefront:
+// 64 probes per step, so a step narrows the range 64-fold.
+__device__ int64_t wave_lower_bound(const int64_t* __restrict__ a, int64_t cnt, int64_t v, int lane) {
+  int64_t lo = 0, hi = cnt;  // the answer lies in [lo, hi]
+  while (hi > lo) {
+    const int64_t step = (hi - lo + 63) / 64;
+    const int64_t q = lo + step * lane;
+    const uint64_t m = __ballot(q < hi && a[q] < v);  // lanes 0 .. c - 1 (a is sorted)
+    const int64_t c = __popcll(m);
+    if (c == 0) return lo;
+    const int64_t lo2 = lo + step * (c - 1) + 1;
+    hi = min(hi, lo + step * c);
+    lo = lo2;
+  }
+  return lo;
+}
+
+// Pass 1 (cl100k-style rules only): decode the tile (4 bytes per thread),
+// write one code byte per text byte, and the tile's forward and backward run
+// summaries, so that pass 2 can resolve runs that cross tiles (digit-group
+// phase, the last newline of a whitespace run, newlines absorbed after
+// punctuation) without a second look at distant bytes, and classify its span
+// without decoding it again.
 __global__ __launch_bounds__(PT_THREADS) void k_tile_summary(const uint8_t* __restrict__ bytes, int64_t n,
                                                              const int64_t* __restrict__ offs, int nseq,
                                                              Work w) {
-  __shared__ TileSmem sm;
-  const int64_t t0 = (int64_t)blockIdx.x * TILE;
-  const int lane = (int)(threadIdx.x & 63u), wid = (int)(threadIdx.x >> 6);
-  const bool na = stage_tile(bytes, n, offs, nseq, t0, sm);
-  // Usually the leading and the trailing run of a tile end within EDGE
-  // positions: then decoding those positions decides both summaries (the
-  // Unicode table is read from global memory for these few chars).
-  if (wid < 2) {
-    const int j = HALO + (wid == 0 ? lane : TILE - EDGE + lane);
-    const uint16_t c = decode_at(n, t0 - HALO, j, sm);
-    uint32_t v;
+  __shared__ uint16_t ascii[128];
+  __shared__ uint32_t sbm[TILE / 32 + 2];  // sequence starts in [t0, t0 + TILE + 64)
+  __shared__ uint32_t red[8];
+  const int tid = (int)threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int t = blockIdx.x;
+  const int64_t t0 = (int64_t)t * TILE;
+  if (tid < 64) reinterpret_cast<uint32_t*>(ascii)[tid] = reinterpret_cast<const uint32_t*>(g_ascii.v)[tid];
+  if (tid < TILE / 32 + 2) sbm[tid] = 0u;
+  // this thread's 4 bytes and the 4 after them
+  const int64_t q = t0 + PT_CHUNK * tid;
+  uint32_t d0 = 0u, d1 = 0u;
+  if ((reinterpret_cast<uintptr_t>(bytes) & 3u) == 0 && q + 8 <= n) {
+    d0 = *reinterpret_cast<const uint32_t*>(bytes + q);
+    d1 = *reinterpret_cast<const uint32_t*>(bytes + q + 4);
+  } else {
+    for (int k = 0; k < 8; ++k)
+      if (q + k < n) (k < 4 ? d0 : d1) |= (uint32_t)bytes[q + k] << (8 * (k & 3));
+  }
+  __syncthreads();
+  if (offs) {
     if (wid == 0) {
-      v = wave_incl_bwd<BwdOp>(is_char(c) ? BwdOp::elem(c) : BwdOp::IDENT, lane);
-      if (lane == 0) sm.red[0] = v;
-    } else {
-      v = wave_incl_fwd<FwdOp>(is_char(c) ? FwdOp::elem(c) : FwdOp::IDENT, lane);
-      if (lane == 63) sm.red[1] = v;
+      const int64_t lo = wave_lower_bound(offs, (int64_t)nseq + 1, t0, lane);
+      const int64_t hi = wave_lower_bound(offs, (int64_t)nseq + 1, t0 + TILE + 64, lane);
+      for (int64_t s = lo + lane; s < hi; s += 64) {
+        const int j = (int)(offs[s] - t0);
+        atomicOr(&sbm[j >> 5], 1u << (j & 31));
+      }
     }
+  } else if (t0 == 0 && tid == 0) {
+    sbm[0] = 1u;
   }
   __syncthreads();
-  const uint32_t tb = sm.red[0], tf = sm.red[1];
-  const bool closed = (tb & 1u) && !(tb & 2u) && (tf & 1u) && !(tf & 2u);
-  __syncthreads();
-  if (closed) {
-    if (threadIdx.x == 0) {
-      w.tile_fwd[blockIdx.x] = tf;
-      w.tile_bwd[blockIdx.x] = tb;
-    }
-    return;
+  const int sh = (PT_CHUNK * tid) & 31;
+  const uint32_t sw0 = sbm[(PT_CHUNK * tid) >> 5], sw1 = sbm[((PT_CHUNK * tid) >> 5) + 1];
+  const uint32_t bm = sh ? (sw0 >> sh) | (sw1 << (32 - sh)) : sw0;  // bit i: a sequence starts at q + i
+  uint32_t code[4];
+  int len[4];
+  decode4_regs((uint64_t)d0 | ((uint64_t)d1 << 32), bm, q, n, ascii, code, len);
+  uint32_t out = 0u, fv = FwdOp::IDENT, bv = BwdOp::IDENT;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    out |= code_byte(code[k]) << (8 * k);
+    if (is_char(code[k])) fv = FwdOp::combine(fv, FwdOp::elem(code[k]));
   }
-  // a run reaches EDGE positions in from an end: decode and scan the whole tile
-  decode_span(n, t0, na, sm);
-  uint32_t af, ab;
-  block_excl_fwd<FwdOp>(chunk_fwd(sm), sm.red, &af);
-  block_excl_bwd<BwdOp>(chunk_bwd(sm), sm.red, &ab);
-  if (threadIdx.x == 0) {
-    w.tile_fwd[blockIdx.x] = af;
-    w.tile_bwd[blockIdx.x] = ab;
+#pragma unroll
+  for (int k = 3; k >= 0; --k)
+    if (is_char(code[k])) bv = BwdOp::combine(BwdOp::elem(code[k]), bv);
+  *reinterpret_cast<uint32_t*>(w.codes + q) = out;
+  const uint32_t wf = wave_incl_fwd<FwdOp>(fv, lane);
+  const uint32_t wb = wave_incl_bwd<BwdOp>(bv, lane);
+  if (lane == 63) red[wid] = wf;
+  if (lane == 0) red[4 + wid] = wb;
+  __syncthreads();
+  if (tid == 0) {
+    w.tile_fwd[t] = FwdOp::combine(FwdOp::combine(red[0], red[1]), FwdOp::combine(red[2], red[3]));
+    w.tile_bwd[t] = BwdOp::combine(BwdOp::combine(red[4], red[5]), BwdOp::combine(red[6], red[7]));
   }
 }
 
 // Combine the summaries of all tiles left of `t` (wave 0) / right of `t`
-// (wave 1), 64 tiles per step, stopping once the run is closed.
+// (wave 1), stopping once the run is closed: first the 64 nearest tiles (one
+// per lane; usually a run closes there), then 8 per lane, 512 per step.
 __device__ void tile_carries(const Work& w, int t, int ntiles, TileSmem& sm) {
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  constexpr int PER = 8;
   if (wid == 0) {
     uint32_t acc = FwdOp::IDENT;
-    for (int b = t - 1; b >= 0; b -= 64) {
-      int j = b - lane;
-      // lane 0 is the tile next to t: the lanes run right to left in the text
-      const uint32_t v = j >= 0 ? w.tile_fwd[j] : FwdOp::IDENT;
+    int b = t - 1, per = 1;
+    while (b >= 0) {
+      // lane 0 holds the tiles next to t: the lanes run right to left in the text
+      uint32_t x[PER];
+#pragma unroll
+      for (int i = 0; i < PER; ++i) {
+        const int j = b - per * lane - i;
+        x[i] = i < per && j >= 0 ? w.tile_fwd[j] : FwdOp::IDENT;
+      }
+      uint32_t v = FwdOp::IDENT;
+#pragma unroll
+      for (int i = PER - 1; i >= 0; --i) v = FwdOp::combine(v, x[i]);
       const uint32_t all = (uint32_t)__builtin_amdgcn_readlane((int)wave_incl_bwd<RevOp<FwdOp>>(v, lane), 0);
       acc = uniform(FwdOp::combine(all, acc));
       if ((acc & 1u) && !(acc & 2u)) break;
+      b -= 64 * per;
+      per = PER;
     }
     if (lane == 0) sm.carry_fwd = acc;
   } else if (wid == 1) {
     uint32_t acc = BwdOp::IDENT;
-    for (int b = t + 1; b < ntiles; b += 64) {
-      int j = b + lane;
-      const uint32_t v = j < ntiles ? w.tile_bwd[j] : BwdOp::IDENT;
+    int b = t + 1, per = 1;
+    while (b < ntiles) {
+      uint32_t x[PER];
+#pragma unroll
+      for (int i = 0; i < PER; ++i) {
+        const int j = b + per * lane + i;
+        x[i] = i < per && j < ntiles ? w.tile_bwd[j] : BwdOp::IDENT;
+      }
+      uint32_t v = BwdOp::IDENT;
+#pragma unroll
+      for (int i = 0; i < PER; ++i) v = BwdOp::combine(v, x[i]);
       const uint32_t all = (uint32_t)__builtin_amdgcn_readlane((int)wave_incl_bwd<BwdOp>(v, lane), 0);
       acc = uniform(BwdOp::combine(acc, all));
       if ((acc & 1u) && !(acc & 2u)) break;
+      b += 64 * per;
+      per = PER;
     }
     if (lane == 0) sm.carry_bwd = acc;
   }
@@ -859,18 +948,6 @@ constexpr int BS_WORDS = 34;            // 1088 chars: 32 before, 1024 own, 32 a
 constexpr int BS_CHUNKS = BS_WORDS / 2;  // 64-char ballot chunks
 constexpr int BS_PLANES = 6;            // class-index bits 0..3, sequence start, sequence last
 
-// Class index of a char code: 0 no char; letters 1 plain, 2 s/t/m/d, 3 r/v,
-// 4 l, 5 e (either case: the contraction letters); 8 digit; 9 other,
-// 10 apostrophe; 12 whitespace, 13 space; 14 CR/LF.
-__device__ __forceinline__ uint32_t cl_index(uint32_t code) {
-  constexpr uint64_t LTAB = 1ull | 2ull << 4 | 2ull << 8 | 3ull << 12 | 5ull << 16 | 3ull << 20 | 2ull << 24 |
-                            4ull << 28 | 2ull << 32;  // by letter type 0..8
-  constexpr uint32_t CTAB = 8u << (4 * C_N) | 9u << (4 * C_O) | 12u << (4 * C_WS) | 14u << (4 * C_WN);
-  const uint32_t k = cls_of(code), lt = (code >> K_LETTER_SHIFT) & 15u;
-  if (k == C_L) return (uint32_t)(LTAB >> (4 * lt)) & 15u;
-  return ((CTAB >> (4 * k)) & 15u) + ((code >> 10) & 1u) + ((code >> 11) & 1u);  // + K_SP, + K_AP
-}
-
 // x from the char S places before / after (bits shifted in across words).
 template <int S>
 __device__ __forceinline__ uint32_t bs_up(uint32_t x) {
@@ -980,25 +1057,54 @@ __device__ uint32_t cl_word_bits(const uint32_t* pl, int lane, int c_lo, int e, 
   return CH & (SS | BN | BL | BO | BWN | BWS) & bs_range(x0, c_lo, e);
 }
 
+// Stage the span's code bytes (k_tile_summary's; none before the text or at
+// or past its end).  Returns, the same in every thread, whether some position
+// of the span inside the text starts no char (then the chars are compacted
+// before the bit planes are taken); *bad: an own position starts invalid
+// UTF-8.
+__device__ bool stage_codes(int64_t n, int64_t t0, const Work& w, TileSmem& sm, bool* bad) {
+  bool gap = false, b = false;
+  for (int i = threadIdx.x; i < SPAN / 4; i += PT_THREADS) {
+    const int64_t p = t0 - HALO + 4 * (int64_t)i;
+    uint32_t v = 0u, in = 0u;
+    if (p >= 0 && p < n) {
+      v = *reinterpret_cast<const uint32_t*>(w.codes + p);
+      in = p + 4 <= n ? ~0u : (1u << (8 * (n - p))) - 1u;  // bytes inside the text
+      v &= in;
+    }
+    // a byte inside the text whose class index is 0 (set the others' low bit)
+    const uint32_t nib = (v & 0x0F0F0F0Fu) | (~in & 0x01010101u);
+    gap |= ((nib - 0x01010101u) & ~nib & 0x80808080u) != 0u;
+    if (i >= HALO / 4 && i < (HALO + TILE) / 4) b |= (v & 0x80808080u) != 0u;
+    reinterpret_cast<uint32_t*>(sm.cb)[i] = v;
+  }
+  *bad = __syncthreads_or(b);
+  return __syncthreads_or(gap);
+}
+
 // The tile's cl100k-style start bits: this thread's 4 (its positions
-// HALO + 4 tid ...) and, in *cnt, the tile's count (the same in every thread).
-// The tile's carries (sm.carry_fwd / carry_bwd) must be set.
-template <bool ASCII>
-__device__ uint32_t cl100k_bits(TileSmem& sm, int64_t n, int64_t t0, uint32_t* cnt) {
+// HALO + 4 tid ...) and, in *cnt, the tile's count (the same in every
+// thread).  The code bytes are staged and the tile's carries (sm.carry_fwd /
+// carry_bwd) set.  DIRECT: every span position inside the text starts a
+// char, so char x is span position x; else the chars are compacted first.
+template <bool DIRECT>
+__device__ uint32_t cl100k_bits(TileSmem& sm, uint32_t* cnt) {
   const int tid = (int)threadIdx.x, lane = tid & 63, wid = (int)uniform((uint32_t)tid >> 6);
   int c_lo = HALO, n_own = TILE, nc = SPAN;
-  if (!ASCII) {
+  const uint8_t* chars = sm.cb;
+  if (!DIRECT) {
     // the span's chars in order: left halo, own, right halo
     const int j0 = HALO + PT_CHUNK * tid;
+    const uint32_t v = reinterpret_cast<const uint32_t*>(sm.cb)[j0 >> 2];
     uint32_t own = 0;
 #pragma unroll
-    for (int k = 0; k < PT_CHUNK; ++k) own += is_char(sm.code[cix(j0 + k)]) ? 1u : 0u;
+    for (int k = 0; k < PT_CHUNK; ++k) own += ((v >> (8 * k)) & 15u) ? 1u : 0u;
     uint32_t n_o;
     const uint32_t own_base = block_excl_sum(own, sm.red, &n_o);
     // the halos, lanes 0..15 the left one and 16..31 the right one (every
     // wavefront counts them, so all agree on the indices; wavefront 0 writes them)
     const int hj = lane < HALO ? lane : TILE + lane;
-    const bool hc = lane < 2 * HALO && is_char(sm.code[cix(hj)]);
+    const bool hc = lane < 2 * HALO && (sm.cb[hj] & 15u) != 0u;
     const uint64_t hm = __ballot(hc);
     const uint32_t n_left = (uint32_t)__popcll(hm & 0xFFFFull);
     c_lo = (int)uniform(n_left);
@@ -1007,9 +1113,9 @@ __device__ uint32_t cl100k_bits(TileSmem& sm, int64_t n, int64_t t0, uint32_t* c
     uint32_t at = n_left + own_base;
 #pragma unroll
     for (int k = 0; k < PT_CHUNK; ++k) {
-      const uint32_t c = sm.code[cix(j0 + k)];
-      if (is_char(c)) {
-        sm.cc[at] = c;
+      const uint32_t c = (v >> (8 * k)) & 255u;
+      if (c & 15u) {
+        sm.cc[at] = (uint8_t)c;
         sm.cpos[at] = (uint16_t)(j0 + k);
         ++at;
       }
@@ -1017,34 +1123,25 @@ __device__ uint32_t cl100k_bits(TileSmem& sm, int64_t n, int64_t t0, uint32_t* c
     if (wid == 0 && hc) {
       const uint32_t below = (uint32_t)__popcll(hm & ((1ull << lane) - 1ull));
       const uint32_t idx = lane < HALO ? below : (uint32_t)(c_lo + n_own) + below - n_left;
-      sm.cc[idx] = sm.code[cix(hj)];
+      sm.cc[idx] = sm.cb[hj];
       sm.cpos[idx] = (uint16_t)hj;
     }
     if (tid < TILE / 32) sm.sbits[tid] = 0u;
     __syncthreads();
+    chars = sm.cc;
   }
   // bit planes, 64 chars per ballot, chunks dealt to the wavefronts
   for (int c = wid; c < BS_CHUNKS; c += PT_THREADS / 64) {
     const int x = c_lo - 32 + 64 * c + lane;
-    uint32_t code = C_OUT;
-    if (ASCII) {
-      const int64_t p = t0 - HALO + x;
-      if (x >= 0 && x < SPAN && p >= 0 && p < n) {
-        code = sm.ascii[reinterpret_cast<const uint8_t*>(sm.raw)[x] & 127u];
-        if (bmap_bit(sm.bmap, x)) code |= K_SEQ_START;
-        if (p + 1 >= n || bmap_bit(sm.bmap, x + 1)) code |= K_SEQ_LAST;
-      }
-    } else if (x >= 0 && x < nc) {
-      code = sm.cc[x];
-    }
-    const uint32_t idx = cl_index(code);
+    const uint32_t b = x >= 0 && x < nc ? chars[x] : 0u;
+    const uint32_t idx = b & 15u;
     uint64_t m[BS_PLANES];
     m[0] = __ballot(idx & 1u);
     m[1] = __ballot(idx & 2u);
     m[2] = __ballot(idx & 4u);
     m[3] = __ballot(idx & 8u);
-    m[4] = __ballot(idx != 0u && (code & K_SEQ_START));
-    m[5] = __ballot(idx != 0u && (code & K_SEQ_LAST));
+    m[4] = __ballot(idx != 0u && (b & CB_SS));
+    m[5] = __ballot(idx != 0u && (b & CB_SL));
     if (lane == 0) {
 #pragma unroll
       for (int k = 0; k < BS_PLANES; ++k) sm.bsw[k][c] = m[k];
@@ -1059,7 +1156,7 @@ __device__ uint32_t cl100k_bits(TileSmem& sm, int64_t n, int64_t t0, uint32_t* c
     const uint32_t B = cl_word_bits(pl, lane, c_lo, c_lo + n_own, uniform(sm.carry_fwd), uniform(sm.carry_bwd));
     const uint32_t tot = wave_incl_fwd<SumOp>((uint32_t)__popc(B), lane);
     if (lane == 63) sm.red[0] = tot;
-    if (ASCII) {
+    if (DIRECT) {
       if (lane >= 1 && lane <= TILE / 32) sm.sbits[lane - 1] = B;
     } else if (lane < BS_WORDS) {
       sm.cbits[lane] = B;
@@ -1067,7 +1164,7 @@ __device__ uint32_t cl100k_bits(TileSmem& sm, int64_t n, int64_t t0, uint32_t* c
   }
   __syncthreads();
   *cnt = sm.red[0];
-  if (!ASCII) {
+  if (!DIRECT) {
     // own char o sits at word 1 + o / 32: its start bit goes to its byte position
 #pragma unroll
     for (int k = 0; k < PT_CHUNK; ++k) {
@@ -1160,9 +1257,6 @@ __global__ __launch_bounds__(PT_THREADS) void k_pretok(const uint8_t* __restrict
     if (threadIdx.x < CTR_RESET_END) w.ctr[threadIdx.x] = 0u;
     for (int i = threadIdx.x; i < QGROUPS * QCTR_STRIDE; i += PT_THREADS) w.qctr[i] = 0u;
   }
-  const bool na = stage_tile(bytes, n, offs, nseq, t0, sm);
-  // pure-ASCII tiles need no decode pass (their masks come from the bytes)
-  const bool bad = na ? decode_span(n, t0, na, sm) : false;
   bool bad_off = false;
   if (offs) {
     for (int64_t q = (int64_t)t * PT_THREADS + threadIdx.x; q <= nseq; q += (int64_t)ntiles * PT_THREADS) {
@@ -1170,11 +1264,20 @@ __global__ __launch_bounds__(PT_THREADS) void k_pretok(const uint8_t* __restrict
       bad_off |= (q == 0 && o != 0) || (q == nseq && o != n) || o < 0 || o > n || (q < nseq && offs[q + 1] < o);
     }
   }
-  const int j0 = HALO + PT_CHUNK * threadIdx.x;
   uint32_t bits = 0;
   uint32_t cnt;
-  bool counted = false;
-  if (PAT == 0) {
+  bool counted = false, bad;
+  if (PAT == 1) {
+    // cl100k-style rules: classes from the code bytes of the summary pass
+    const bool gap = stage_codes(n, t0, w, sm, &bad);
+    tile_carries(w, t, ntiles, sm);
+    bits = gap ? cl100k_bits<false>(sm, &cnt) : cl100k_bits<true>(sm, &cnt);
+    counted = true;
+  } else {
+    const bool na = stage_tile(bytes, n, offs, nseq, t0, sm);
+    // pure-ASCII tiles need no decode pass (their masks come from the bytes)
+    bad = na ? decode_span(n, t0, na, sm) : false;
+    const int j0 = HALO + PT_CHUNK * threadIdx.x;
     if (!na) {
       uint32_t wc;
       const bool plain = t0 - HALO >= 0 && t0 - HALO + 16 * RAW_WORDS <= n && (!offs || sm.seq_lo == sm.seq_hi);
@@ -1183,17 +1286,13 @@ __global__ __launch_bounds__(PT_THREADS) void k_pretok(const uint8_t* __restrict
       __syncthreads();
       cnt = sm.red[0] + sm.red[1] + sm.red[2] + sm.red[3];
       counted = true;
-    } else if (na) {
+    } else {
 #pragma unroll
       for (int k = 0; k < PT_CHUNK; ++k) {
         uint32_t c = sm.code[cix(j0 + k)];
         if (is_char(c) && pred_gpt2<false>(sm.code, sm.plen, j0 + k)) bits |= 1u << k;
       }
     }
-  } else {
-    tile_carries(w, t, ntiles, sm);
-    bits = na ? cl100k_bits<false>(sm, n, t0, &cnt) : cl100k_bits<true>(sm, n, t0, &cnt);
-    counted = true;
   }
   w.flags[(int64_t)t * PT_THREADS + threadIdx.x] = (uint16_t)bits;
   if (!counted) cnt = block_sum(__popc(bits), sm.red);
