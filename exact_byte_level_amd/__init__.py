@@ -30,6 +30,7 @@ TT_ENOTLOADED = -6
 TT_EOFFSETS = -7
 TT_ETOOBIG = -8
 TT_ESTALE = -9
+TT_EUNSUPPORTED = -10
 
 _lib = None
 

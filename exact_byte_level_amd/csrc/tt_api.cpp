@@ -18,7 +18,7 @@ namespace {
 using namespace tt;
 
 const uint8_t h_uni_l1[TT_UNI_L1_SIZE] = {TT_UNI_L1_DATA};
-const uint8_t h_uni_l2[TT_UNI_NBLOCKS * 64] = {TT_UNI_L2_DATA};
+const uint8_t h_uni_l2[TT_UNI_NBLOCKS * 128] = {TT_UNI_L2_DATA};
 
 struct State {
   bool loaded = false;
@@ -145,6 +145,7 @@ size_t layout(int64_t n, char* base, Work* w) {
   t.tile_bwd = (uint32_t*)take(ntiles * 4);
   t.tile_cnt = (uint32_t*)take(ntiles * 4);
   t.codes = (uint8_t*)take(ntiles * TILE + 64);
+  t.tile_tail = (uint32_t*)take(ntiles * 4);
   t.flags = (uint16_t*)take(ntiles * PT_THREADS * 2);
   t.piece_start = (int32_t*)take((nn + 1) * 4);
   t.piece_cnt = (int32_t*)take(nn * 4);
@@ -296,7 +297,8 @@ int tt_load_bpe(const int32_t* merges, const int32_t* ranks, int64_t n_merges, i
 int tt_load_bpe_ex(const int32_t* merges, const int32_t* ranks, int64_t n_merges, int32_t pattern_id,
                    uint32_t flags) {
   std::lock_guard<std::mutex> lock(g_mu);
-  if (pattern_id != TT_PATTERN_GPT2 && pattern_id != TT_PATTERN_CL100K) return TT_EINVAL;
+  if (pattern_id != TT_PATTERN_GPT2 && pattern_id != TT_PATTERN_CL100K && pattern_id != TT_PATTERN_O200K)
+    return TT_EINVAL;
   if (flags & ~(uint32_t)TT_LOAD_IGNORE_MERGES) return TT_EINVAL;
   const bool whole = (flags & TT_LOAD_IGNORE_MERGES) != 0;
   if (n_merges < 0 || n_merges > TT_MAX_MERGES) return TT_EINVAL;
@@ -698,6 +700,7 @@ int tt_session_reset(tt_session* s, const uint8_t* dev_bytes, int64_t n, hipStre
   std::lock_guard<std::mutex> lock(g_mu);
   if (!s || n < 0 || (n > 0 && !dev_bytes)) return TT_EINVAL;
   if (n > s->cap) return TT_ETOOBIG;
+  if (g.loaded && g.pattern == TT_PATTERN_O200K) return TT_EINVAL;  // no splice rule for these rules
   int rc = check_stream_state();
   if (rc != TT_OK) return rc;
   s->valid = false;
@@ -728,6 +731,7 @@ int tt_session_append(tt_session* s, const uint8_t* dev_delta, int64_t nd, int64
   if (rc != TT_OK) return rc;
   if (!s->valid) return TT_EINVAL;
   if (s->gen != g.generation) return TT_ESTALE;
+  if (g.pattern == TT_PATTERN_O200K) return TT_EINVAL;
   if (nd > s->cap - s->n) return TT_ETOOBIG;
   int64_t info[4] = {0, 0, -1, s->T};
   if (nd == 0) {
@@ -816,8 +820,8 @@ int tt_char_class(uint32_t cp) {
   if (cp > 0x10FFFF || (cp >= 0xD800 && cp <= 0xDFFF)) return -1;
   uint32_t hi = cp >> 8;
   if (hi >= (uint32_t)TT_UNI_L1_SIZE) return 0;
-  uint32_t byte = h_uni_l2[h_uni_l1[hi] * 64u + ((cp & 255u) >> 2)];
-  return (int)((byte >> ((cp & 3u) * 2u)) & 3u);
+  uint32_t byte = h_uni_l2[h_uni_l1[hi] * 128u + ((cp & 255u) >> 1)];
+  return (int)((byte >> ((cp & 1u) * 4u)) & 15u);
 }
 
 int tt_profile(int enable) {
@@ -869,6 +873,7 @@ const char* tt_strerror(int code) {
     case TT_EOFFSETS: return "invalid batch offsets";
     case TT_ETOOBIG: return "size beyond library limits";
     case TT_ESTALE: return "tokenizer replaced since the session began";
+    case TT_EUNSUPPORTED: return "input case not decided by the o200k-style GPU rules";
     default: return "unknown error";
   }
 }

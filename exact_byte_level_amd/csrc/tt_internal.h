@@ -32,6 +32,8 @@ constexpr uint32_t K_SP = 1u << 10;
 constexpr uint32_t K_AP = 1u << 11;
 constexpr uint32_t K_BAD = 1u << 12;
 constexpr int K_LEN_SHIFT = 13;
+constexpr uint32_t K_SLASH = 1u << 15;  // '/'
+constexpr int K_FINE_SHIFT = 16;        // 32-bit codes: the Unicode class of a multibyte char (4 bits)
 enum : uint32_t { LT_S = 1, LT_T = 2, LT_R = 3, LT_E = 4, LT_V = 5, LT_M = 6, LT_L = 7, LT_D = 8 };
 
 // ------------------------------------------------------------------------- BPE
@@ -139,8 +141,8 @@ enum : int {
   CTR_RESET_END = 12,    // counters [0, CTR_RESET_END) are per call
   CTR_COUNT = 16
 };
-enum : uint32_t { ERR_UTF8 = 1u, ERR_OFFSETS = 2u };
-constexpr int TILE_ERR_SHIFT = 30;     // tile_cnt[t] bits 30-31: ERR_* bits of tile t
+enum : uint32_t { ERR_UTF8 = 1u, ERR_OFFSETS = 2u, ERR_UNSUP = 4u };
+constexpr int TILE_ERR_SHIFT = 29;     // tile_cnt[t] bits 29-31: ERR_* bits of tile t
 
 constexpr int QGROUPS = 8;
 constexpr int QCTR_STRIDE = 32;          // words: 128 bytes
@@ -150,7 +152,8 @@ struct Work {
   uint32_t* tile_fwd;    // [ntiles] forward run summary of each tile
   uint32_t* tile_bwd;    // [ntiles] backward run summary
   uint32_t* tile_cnt;    // [ntiles] pre-token starts of each tile | error bits << TILE_ERR_SHIFT
-  uint8_t* codes;        // [(ntiles + 1) * TILE] cl100k-style rules: one code byte per text byte
+  uint8_t* codes;        // [(ntiles + 1) * TILE] cl100k/o200k-style rules: one code byte per text byte
+  uint32_t* tile_tail;   // [ntiles] o200k-style rules: CR/LF/'/' tail summary of each tile
   uint16_t* flags;       // [ntiles * PT_THREADS] start bits of each thread's PT_CHUNK bytes
   int32_t* piece_start;  // [n + 1]
   int32_t* piece_cnt;    // [n] tokens of each piece

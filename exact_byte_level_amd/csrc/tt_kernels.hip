@@ -34,9 +34,15 @@ namespace tt {
 // ------------------------------------------------------------ Unicode classes
 
 constexpr int UNI_L1_PAD = (TT_UNI_L1_SIZE + 15) / 16 * 16;
-constexpr int UNI_L2_PAD = (TT_UNI_NBLOCKS * 64 + 15) / 16 * 16;
+constexpr int UNI_L2_PAD = TT_UNI_NBLOCKS * 128;
 alignas(16) __device__ const uint8_t g_uni_l1[UNI_L1_PAD] = {TT_UNI_L1_DATA};
 alignas(16) __device__ const uint8_t g_uni_l2[UNI_L2_PAD] = {TT_UNI_L2_DATA};
+
+// Unicode class (the table's 4-bit value) -> the char class of the rules.
+constexpr uint32_t UNI_SINGLE = 9;  // single-class blocks 0..8
+__device__ __forceinline__ uint32_t uni_cls(uint32_t u) {
+  return u - 1u < 3u ? C_L : u == 5u ? C_N : u == 6u ? C_WS : C_O;
+}
 
 struct alignas(16) AsciiTab {
   uint16_t v[128];
@@ -59,6 +65,8 @@ constexpr uint16_t ascii_code(int c) {
     code = (uint16_t)(C_WS | (c == ' ' ? K_SP : 0));
   } else if (c == '\'') {
     code = (uint16_t)(C_O | K_AP);
+  } else if (c == '/') {
+    code = (uint16_t)(C_O | K_SLASH);
   }
   return code;
 }
@@ -94,10 +102,10 @@ struct TileSmem {
   alignas(16) uint16_t ascii[128];
   uint32_t bmap[BMAP_WORDS];
   uint32_t red[8];
-  uint64_t bsw[6][17];   // cl100k-style rules: bit planes of the span's chars (64 per entry)
+  uint64_t bsw[7][17];   // cl100k/o200k-style rules: bit planes of the span's chars (64 per entry)
   uint32_t cbits[34];    // their start bits by char (tiles with non-ASCII bytes)
   int64_t seq_lo, seq_hi;
-  uint32_t carry_fwd, carry_bwd;
+  uint32_t carry_fwd, carry_bwd, carry_tail;
   int flag;
   // cl100k-style rules: the span's code bytes (by position), its chars in
   // order (code bytes) and their positions, and the tile's start bits
@@ -123,61 +131,6 @@ __device__ __forceinline__ int64_t lower_bound_i64(const int64_t* a, int64_t cnt
     if (a[mid] < v) lo = mid + 1; else hi = mid;
   }
   return lo;
-}
-
-// Decode the char starting at tile position j (global position base + j) from
-// the raw bytes staged in LDS.  Validates UTF-8 as strict decoding does: no
-// overlong forms, no surrogates, nothing above U+10FFFF, no truncated or stray
-// continuation bytes, and no char crossing a sequence boundary.
-__device__ __forceinline__ uint16_t decode_at(int64_t n, int64_t base, int j, const TileSmem& sm){
-  const uint8_t* raw = reinterpret_cast<const uint8_t*>(sm.raw);
-  int64_t p = base + j;
-  if (p < 0 || p >= n) return (uint16_t)C_OUT;
-  uint32_t b0 = raw[j];
-  bool start = bmap_bit(sm.bmap, j);
-  if ((b0 & 0xC0u) == 0x80u) return (uint16_t)(C_CONT | (start ? K_BAD : 0u));
-  uint32_t code;
-  int len = 1;
-  bool bad = false;
-  if (b0 < 0x80u) {
-    code = sm.ascii[b0];
-  } else {
-    uint32_t cp = 0;
-    if (b0 >= 0xC2u && b0 <= 0xDFu) { len = 2; cp = b0 & 0x1Fu; }
-    else if (b0 >= 0xE0u && b0 <= 0xEFu) { len = 3; cp = b0 & 0x0Fu; }
-    else if (b0 >= 0xF0u && b0 <= 0xF4u) { len = 4; cp = b0 & 0x07u; }
-    else { bad = true; }
-    for (int k = 1; k < len && !bad; ++k) {
-      if (p + k >= n || bmap_bit(sm.bmap, j + k)) { bad = true; break; }
-      uint32_t bk = raw[j + k];
-      if ((bk & 0xC0u) != 0x80u) { bad = true; break; }
-      if (k == 1) {
-        if ((b0 == 0xE0u && bk < 0xA0u) || (b0 == 0xEDu && bk > 0x9Fu) ||
-            (b0 == 0xF0u && bk < 0x90u) || (b0 == 0xF4u && bk > 0x8Fu)) { bad = true; break; }
-      }
-      cp = (cp << 6) | (bk & 0x3Fu);
-    }
-    if (bad) {
-      len = 1;
-      code = C_O | K_BAD;
-    } else {
-      // (block numbers below 4 are single-class blocks: the number is the class)
-      uint32_t hi = cp >> 8, u = 0;
-      if (hi < (uint32_t)TT_UNI_L1_SIZE) {
-        const uint32_t blk = g_uni_l1[hi];
-        u = blk < 4u ? blk : (g_uni_l2[blk * 64u + ((cp & 255u) >> 2)] >> ((cp & 3u) * 2u)) & 3u;
-      }
-      code = u == 1u ? C_L : u == 2u ? C_N : u == 3u ? C_WS : C_O;
-    }
-  }
-  // a continuation byte right after a complete char is stray
-  int64_t e = p + len;
-  bool last = e >= n || bmap_bit(sm.bmap, j + len);
-  if (!last && !bad && (raw[j + len] & 0xC0u) == 0x80u) code |= K_BAD;
-  code |= (uint32_t)(len - 1) << K_LEN_SHIFT;
-  if (start) code |= K_SEQ_START;
-  if (last) code |= K_SEQ_LAST;
-  return (uint16_t)code;
 }
 
 // Stage the tile in LDS: raw bytes of [t0 - HALO, t0 + TILE + HALO + 16) with
@@ -276,8 +229,8 @@ __device__ __forceinline__ void decode4_regs(uint64_t wb, uint32_t bm, int64_t p
     code[k] = !in ? (uint32_t)C_OUT : cont ? (C_CONT | (start ? K_BAD : 0u)) : c;
     len_out[k] = in && !cont ? (int)clen : 0;
   }
-  // class of the multibyte chars: block numbers below 4 are single-class
-  // blocks (the number is the class)
+  // class of the multibyte chars: block numbers below UNI_SINGLE are
+  // single-class blocks (the number is the class)
   uint32_t blk[4];
 #pragma unroll
   for (int k = 0; k < 4; ++k) blk[k] = tab[k] ? (uint32_t)g_uni_l1[cp[k] >> 8] : 0u;
@@ -285,9 +238,9 @@ __device__ __forceinline__ void decode4_regs(uint64_t wb, uint32_t bm, int64_t p
   for (int k = 0; k < 4; ++k) {
     if (cls_of(code[k]) == 0u) {
       // a valid multibyte char (class bits still 0)
-      const uint32_t u = !tab[k] ? 0u : blk[k] < 4u ? blk[k]
-                       : (g_uni_l2[blk[k] * 64u + ((cp[k] & 255u) >> 2)] >> ((cp[k] & 3u) * 2u)) & 3u;
-      code[k] |= u == 1u ? C_L : u == 2u ? C_N : u == 3u ? C_WS : C_O;
+      const uint32_t u = !tab[k] ? 0u : blk[k] < UNI_SINGLE ? blk[k]
+                       : (g_uni_l2[blk[k] * 128u + ((cp[k] & 255u) >> 1)] >> ((cp[k] & 1u) * 4u)) & 15u;
+      code[k] |= uni_cls(u) | (u << K_FINE_SHIFT);
     }
   }
 }
@@ -361,12 +314,17 @@ __device__ bool load_tile(const uint8_t* __restrict__ bytes, int64_t n, const in
 // Forward state of a range of chars, for the trailing run:
 //   bit 0 has chars, bit 1 open (the run reaches the range start and no
 //   sequence starts there), bits 2-4 class, bits 5-7 class of the char before
-//   the run (C_NONE at a sequence start), bits 8-9 run length mod 3.
+//   the run (C_NONE at a sequence start), bits 8-9 run length mod 3, bit 10
+//   the char before the run is an ASCII letter that can end a contraction
+//   suffix (s t m d e l, either case), bit 11 the range's last char is one.
 struct FwdOp {
   static constexpr uint32_t IDENT = 0;
+  static constexpr uint32_t CB_CL = 1u << 10, LAST_CL = 1u << 11;
   __device__ static __forceinline__ uint32_t elem(uint32_t code) {
     uint32_t open = (code & K_SEQ_START) ? 0u : 2u;
-    return 1u | open | (cls_of(code) << 2) | (1u << 8);
+    const uint32_t lt = (code >> K_LETTER_SHIFT) & 15u;  // 0 unless an ASCII letter
+    const bool cl = (0x1D6u >> lt) & 1u;                 // LT_S T E M L D
+    return 1u | open | (cls_of(code) << 2) | (1u << 8) | (cl ? LAST_CL : 0u);
   }
   __device__ static __forceinline__ uint32_t combine(uint32_t a, uint32_t b) {
     if (!(b & 1u)) return a;
@@ -375,11 +333,45 @@ struct FwdOp {
       uint32_t ca = (a >> 2) & 7u, cb = (b >> 2) & 7u;
       if (ca == cb) {
         uint32_t len = (((a >> 8) & 3u) + ((b >> 8) & 3u)) % 3u;
-        return (a & 0xFFu) | (len << 8);
+        return (a & (0xFFu | CB_CL)) | (len << 8) | (b & LAST_CL);
       }
-      return 1u | (cb << 2) | (ca << 5) | (b & 0x300u);
+      return 1u | (cb << 2) | (ca << 5) | (b & 0x300u) | ((a & LAST_CL) ? CB_CL : 0u) | (b & LAST_CL);
     }
     return b;
+  }
+};
+
+// Forward state for the o200k-style CR/LF/'/' tails, of the trailing run of
+// tail chars (CR, LF, '/'; none starts a sequence inside the run): bit 0 has
+// chars, bit 1 open (the whole range is that run), bit 2 active (a tail
+// starts in the run: a CR/LF right after an "other" char), bit 3 the range's
+// first char is CR/LF and starts no sequence, bit 4 its last char is
+// "other", bit 5 its last char is a tail char, bits 6-11 distance from the
+// range end back to the first tail start of the run (saturating at 63),
+// bits 12-17 the number of chars (saturating at 63).
+struct TailOp {
+  static constexpr uint32_t IDENT = 0;
+  static constexpr uint32_t SAT = 63;
+  __device__ static __forceinline__ uint32_t elem(uint32_t code) {
+    const uint32_t k = cls_of(code);
+    const bool r = k == C_WN || (code & K_SLASH), ss = (code & K_SEQ_START) != 0u;
+    return 1u | (r && !ss ? 2u : 0u) | (k == C_WN && !ss ? 8u : 0u) | (k == C_O ? 16u : 0u) | (r ? 32u : 0u) |
+           (1u << 12);
+  }
+  __device__ static __forceinline__ uint32_t combine(uint32_t a, uint32_t b) {
+    if (!(b & 1u)) return a;
+    if (!(a & 1u)) return b;
+    const uint32_t len = min(SAT, ((a >> 12) & SAT) + ((b >> 12) & SAT));
+    uint32_t r = 1u | (a & 8u) | (b & 48u) | (len << 12);
+    if (b & 2u) {
+      const bool a_act = (a & 32u) && (a & 4u), seed = (b & 8u) && (a & 16u);
+      const uint32_t blen = (b >> 12) & SAT;
+      const uint32_t d = a_act ? min(SAT, ((a >> 6) & SAT) + blen) : seed ? blen : ((b >> 6) & SAT);
+      r |= (a & b & 2u) | ((a_act || seed || (b & 4u)) ? 4u : 0u) | (d << 6);
+    } else {
+      r |= (b & 4u) | (b & (SAT << 6));
+    }
+    return r;
   }
 };
 
@@ -604,11 +596,44 @@ __device__ __forceinline__ uint32_t cl_index(uint32_t code) {
 // k_tile_summary, read by k_pretok): bits 0-3 the class index of the char
 // starting there (0: no char starts there), bit 4 a sequence starts with that
 // char, bit 5 its sequence ends with it, bit 7 invalid UTF-8 starts there.
-constexpr uint32_t CB_SS = 1u << 4, CB_SL = 1u << 5, CB_BAD = 1u << 7;
+constexpr uint32_t CB_IDX = 31u, CB_SS = 1u << 5, CB_SL = 1u << 6, CB_BAD = 1u << 7;
 
+// Class index of a char code under the o200k-style rules (5 bits): 0 no
+// char; 1 digit, 2 other, 3 apostrophe, 4 '/', 5 whitespace, 6 space, 7
+// CR/LF; letter-type chars 16 | (lower case ? 8 : 0) | t, where t is the
+// contraction letter type of an ASCII letter (0 none, 1 s/t/m/d, 2 r/v, 3 l,
+// 4 e), and 23 for Lm and Lo letters and marks (either case).
+__device__ __forceinline__ uint32_t o2_index(uint32_t code) {
+  constexpr uint64_t TTAB = 0ull | 1ull << 4 | 1ull << 8 | 2ull << 12 | 4ull << 16 | 2ull << 20 | 1ull << 24 |
+                            3ull << 28 | 1ull << 32;  // by letter type 0..8
+  const uint32_t k = cls_of(code), fine = (code >> K_FINE_SHIFT) & 15u;
+  const bool mb = ((code >> K_LEN_SHIFT) & 3u) != 0u;  // a multibyte char
+  if (k == C_L || (mb && k == C_O && fine == 4u)) {
+    if (mb) return fine == 1u ? 16u : fine == 2u ? 24u : 23u;
+    const uint32_t lt = (code >> K_LETTER_SHIFT) & 15u;
+    return 16u | ((code & K_UPPER) ? 0u : 8u) | ((uint32_t)(TTAB >> (4 * lt)) & 15u);
+  }
+  if (k == C_N) return 1u;
+  if (k == C_O) return (code & K_AP) ? 3u : (code & K_SLASH) ? 4u : 2u;
+  if (k == C_WS) return (code & K_SP) ? 6u : 5u;
+  return k == C_WN ? 7u : 0u;
+}
+
+// The code with its class as the o200k-style run summaries see it: marks
+// are letters, and letters split into three classes (upper case C_L2U, lower
+// case C_L, Lm/Lo/marks C_L2B) so that a run of one case is one run.
+constexpr uint32_t C_L2U = 6u, C_L2B = 7u;
+__device__ __forceinline__ uint32_t o2_sum_code(uint32_t code) {
+  const uint32_t idx = o2_index(code);
+  if (!(idx & 16u)) return code;
+  const uint32_t c = (idx & 8u) ? C_L : (idx & 7u) == 7u ? C_L2B : C_L2U;
+  return (code & ~7u) | c;
+}
+
+template <int PAT>
 __device__ __forceinline__ uint32_t code_byte(uint32_t code) {
-  return cl_index(code) | ((code & K_SEQ_START) ? CB_SS : 0u) | ((code & K_SEQ_LAST) ? CB_SL : 0u) |
-         ((code & K_BAD) ? CB_BAD : 0u);
+  return (PAT == 2 ? o2_index(code) : cl_index(code)) | ((code & K_SEQ_START) ? CB_SS : 0u) |
+         ((code & K_SEQ_LAST) ? CB_SL : 0u) | ((code & K_BAD) ? CB_BAD : 0u);
 }
 
 // First index s in [0, cnt) with a[s] >= v (cnt if none), by one wavefront:
@@ -634,12 +659,13 @@ __device__ int64_t wave_lower_bound(const int64_t* __restrict__ a, int64_t cnt, 
 // phase, the last newline of a whitespace run, newlines absorbed after
 // punctuation) without a second look at distant bytes, and classify its span
 // without decoding it again.
+template <int PAT>
 __global__ __launch_bounds__(PT_THREADS) void k_tile_summary(const uint8_t* __restrict__ bytes, int64_t n,
                                                              const int64_t* __restrict__ offs, int nseq,
                                                              Work w) {
   __shared__ uint16_t ascii[128];
   __shared__ uint32_t sbm[TILE / 32 + 2];  // sequence starts in [t0, t0 + TILE + 64)
-  __shared__ uint32_t red[8];
+  __shared__ uint32_t red[12];
   const int tid = (int)threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int t = blockIdx.x;
   const int64_t t0 = (int64_t)t * TILE;
@@ -675,53 +701,75 @@ __global__ __launch_bounds__(PT_THREADS) void k_tile_summary(const uint8_t* __re
   uint32_t code[4];
   int len[4];
   decode4_regs((uint64_t)d0 | ((uint64_t)d1 << 32), bm, q, n, ascii, code, len);
-  uint32_t out = 0u, fv = FwdOp::IDENT, bv = BwdOp::IDENT;
+  uint32_t out = 0u, fv = FwdOp::IDENT, bv = BwdOp::IDENT, tv = TailOp::IDENT;
+  bool ch[4];
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
-    out |= code_byte(code[k]) << (8 * k);
-    if (is_char(code[k])) fv = FwdOp::combine(fv, FwdOp::elem(code[k]));
+    out |= code_byte<PAT>(code[k]) << (8 * k);
+    ch[k] = is_char(code[k]);
+    // o200k-style summaries see marks as letters and letters by case (class
+    // values 6 and 7 included)
+    if (PAT == 2) code[k] = o2_sum_code(code[k]);
+    if (ch[k]) {
+      fv = FwdOp::combine(fv, FwdOp::elem(code[k]));
+      if (PAT == 2) tv = TailOp::combine(tv, TailOp::elem(code[k]));
+    }
   }
 #pragma unroll
   for (int k = 3; k >= 0; --k)
-    if (is_char(code[k])) bv = BwdOp::combine(BwdOp::elem(code[k]), bv);
+    if (ch[k]) bv = BwdOp::combine(BwdOp::elem(code[k]), bv);
   *reinterpret_cast<uint32_t*>(w.codes + q) = out;
   const uint32_t wf = wave_incl_fwd<FwdOp>(fv, lane);
   const uint32_t wb = wave_incl_bwd<BwdOp>(bv, lane);
   if (lane == 63) red[wid] = wf;
   if (lane == 0) red[4 + wid] = wb;
+  if (PAT == 2) {
+    const uint32_t wt = wave_incl_fwd<TailOp>(tv, lane);
+    if (lane == 63) red[8 + wid] = wt;
+  }
   __syncthreads();
   if (tid == 0) {
     w.tile_fwd[t] = FwdOp::combine(FwdOp::combine(red[0], red[1]), FwdOp::combine(red[2], red[3]));
     w.tile_bwd[t] = BwdOp::combine(BwdOp::combine(red[4], red[5]), BwdOp::combine(red[6], red[7]));
+    if (PAT == 2) w.tile_tail[t] = TailOp::combine(TailOp::combine(red[8], red[9]), TailOp::combine(red[10], red[11]));
   }
 }
 
-// Combine the summaries of all tiles left of `t` (wave 0) / right of `t`
-// (wave 1), stopping once the run is closed: first the 64 nearest tiles (one
-// per lane; usually a run closes there), then 8 per lane, 512 per step.
+// Combine the summaries of all tiles left of `t` (Op over src, wavefronts 0
+// and 2) / right of `t` (wavefront 1), stopping once the run is closed: first
+// the 64 nearest tiles (one per lane; usually a run closes there), then 8 per
+// lane, 512 per step.
+template <class Op>
+__device__ __forceinline__ uint32_t look_back(const uint32_t* __restrict__ src, int t, int lane) {
+  constexpr int PER = 8;
+  uint32_t acc = Op::IDENT;
+  int b = t - 1, per = 1;
+  while (b >= 0) {
+    // lane 0 holds the tiles next to t: the lanes run right to left in the text
+    uint32_t x[PER];
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int j = b - per * lane - i;
+      x[i] = i < per && j >= 0 ? src[j] : Op::IDENT;
+    }
+    uint32_t v = Op::IDENT;
+#pragma unroll
+    for (int i = PER - 1; i >= 0; --i) v = Op::combine(v, x[i]);
+    const uint32_t all = (uint32_t)__builtin_amdgcn_readlane((int)wave_incl_bwd<RevOp<Op>>(v, lane), 0);
+    acc = uniform(Op::combine(all, acc));
+    if ((acc & 1u) && !(acc & 2u)) break;
+    b -= 64 * per;
+    per = PER;
+  }
+  return acc;
+}
+
+template <int PAT>
 __device__ void tile_carries(const Work& w, int t, int ntiles, TileSmem& sm) {
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   constexpr int PER = 8;
   if (wid == 0) {
-    uint32_t acc = FwdOp::IDENT;
-    int b = t - 1, per = 1;
-    while (b >= 0) {
-      // lane 0 holds the tiles next to t: the lanes run right to left in the text
-      uint32_t x[PER];
-#pragma unroll
-      for (int i = 0; i < PER; ++i) {
-        const int j = b - per * lane - i;
-        x[i] = i < per && j >= 0 ? w.tile_fwd[j] : FwdOp::IDENT;
-      }
-      uint32_t v = FwdOp::IDENT;
-#pragma unroll
-      for (int i = PER - 1; i >= 0; --i) v = FwdOp::combine(v, x[i]);
-      const uint32_t all = (uint32_t)__builtin_amdgcn_readlane((int)wave_incl_bwd<RevOp<FwdOp>>(v, lane), 0);
-      acc = uniform(FwdOp::combine(all, acc));
-      if ((acc & 1u) && !(acc & 2u)) break;
-      b -= 64 * per;
-      per = PER;
-    }
+    const uint32_t acc = look_back<FwdOp>(w.tile_fwd, t, lane);
     if (lane == 0) sm.carry_fwd = acc;
   } else if (wid == 1) {
     uint32_t acc = BwdOp::IDENT;
@@ -743,6 +791,9 @@ __device__ void tile_carries(const Work& w, int t, int ntiles, TileSmem& sm) {
       per = PER;
     }
     if (lane == 0) sm.carry_bwd = acc;
+  } else if (wid == 2 && PAT == 2) {
+    const uint32_t acc = look_back<TailOp>(w.tile_tail, t, lane);
+    if (lane == 0) sm.carry_tail = acc;
   }
   __syncthreads();
 }
@@ -946,7 +997,6 @@ __device__ __forceinline__ bool pred_cl100k(const uint16_t* c, const uint8_t* pl
 // tile's forward and backward run states.
 constexpr int BS_WORDS = 34;            // 1088 chars: 32 before, 1024 own, 32 after
 constexpr int BS_CHUNKS = BS_WORDS / 2;  // 64-char ballot chunks
-constexpr int BS_PLANES = 6;            // class-index bits 0..3, sequence start, sequence last
 
 // x from the char S places before / after (bits shifted in across words).
 template <int S>
@@ -990,15 +1040,14 @@ __device__ __forceinline__ uint32_t bs_range(int x0, int lo, int hi) {
 // Start bits of this lane's word (one wavefront; lanes >= BS_WORDS hold no
 // chars).  lf: forward run state of the chars before c_lo; rb: backward run
 // state of the chars from e on.
-__device__ uint32_t cl_word_bits(const uint32_t* pl, int lane, int c_lo, int e, uint32_t lf, uint32_t rb) {
-  const uint32_t b0 = pl[0], b1 = pl[1], b2 = pl[2], b3 = pl[3], SS = pl[4], SL = pl[5];
+// The three run facts shared by the cl100k- and o200k-style rules, for this
+// lane's word: NPH digits at offset 0 mod 3 in their digit run, ENDS
+// whitespace chars whose whitespace run is not followed by a CR/LF, ABSO
+// CR/LF chars of a CR/LF run that follows an "other" char.
+__device__ __forceinline__ void run_facts(uint32_t N, uint32_t WS, uint32_t WN, uint32_t O, uint32_t SS, uint32_t SL,
+                                          int lane, int c_lo, int e, uint32_t lf, uint32_t rb, uint32_t* nph,
+                                          uint32_t* ends, uint32_t* abso) {
   const int x0 = c_lo - 32 + 32 * lane;
-  const uint32_t CH = b0 | b1 | b2 | b3;
-  const uint32_t L = ~b3 & (b0 | b1 | b2);
-  const uint32_t N = b3 & ~b2 & ~b1 & ~b0;
-  const uint32_t O = b3 & ~b2 & (b0 ^ b1);
-  const uint32_t AP = b3 & ~b2 & b1 & ~b0;
-  const uint32_t W = b3 & b2, WS = W & ~b1, SP = WS & b0, WN = W & b1;
   // digits at offset 0 mod 3 in their run: fill each run with its start's
   // residue (mod 3) of the char index
   // X0: the span's first char, whose predecessor is not seen (a run start
@@ -1021,19 +1070,32 @@ __device__ uint32_t cl_word_bits(const uint32_t* pl, int lane, int c_lo, int e, 
   const uint32_t F0 = bs_fill_up(Q, bs_up<1>(S0) & Q, lane) | S0;
   const uint32_t F1 = bs_fill_up(Q, bs_up<1>(S1) & Q, lane) | S1;
   const uint32_t F2 = N & ~F0 & ~F1;
-  const uint32_t NPH = (F0 & M0) | (F1 & M1) | (F2 & M2);
+  *nph = (F0 & M0) | (F1 & M1) | (F2 & M2);
   // whitespace runs followed by a CR/LF, spread down from the run's top (runs
   // cut at e; one that goes on past e takes the backward state there)
   const uint32_t lim = bs_range(x0, -(1 << 20), e);
   uint32_t FW = WS & bs_dn<1>(WN) & ~SL & lim;
   const bool rb_ws_nl = (rb & 1u) && ((rb >> 2) & 7u) == C_WS && ((rb >> 5) & 7u) == C_WN;
   if (rb_ws_nl) FW |= WS & bs_dn<1>(WS) & ~SL & bs_range(x0, e - 1, e);
-  const uint32_t ENDS = WS & ~bs_fill_down(WS & ~SL & lim, FW, lane);
+  *ends = WS & ~bs_fill_down(WS & ~SL & lim, FW, lane);
   // CR/LF runs right after an "other" char
   const uint32_t RN = WN & ~SS;
   uint32_t SN = RN & ~bs_up<1>(WN) & bs_up<1>(O);
   if ((lf & 1u) && ((lf >> 2) & 7u) == C_WN && ((lf >> 5) & 7u) == C_O) SN |= RN & X0;
-  const uint32_t ABSO = bs_fill_up(RN, SN, lane);
+  *abso = bs_fill_up(RN, SN, lane);
+}
+
+__device__ uint32_t cl_word_bits(const uint32_t* pl, int lane, int c_lo, int e, uint32_t lf, uint32_t rb) {
+  const uint32_t b0 = pl[0], b1 = pl[1], b2 = pl[2], b3 = pl[3], SS = pl[4], SL = pl[5];
+  const int x0 = c_lo - 32 + 32 * lane;
+  const uint32_t CH = b0 | b1 | b2 | b3;
+  const uint32_t L = ~b3 & (b0 | b1 | b2);
+  const uint32_t N = b3 & ~b2 & ~b1 & ~b0;
+  const uint32_t O = b3 & ~b2 & (b0 ^ b1);
+  const uint32_t AP = b3 & ~b2 & b1 & ~b0;
+  const uint32_t W = b3 & b2, WS = W & ~b1, SP = WS & b0, WN = W & b1;
+  uint32_t NPH, ENDS, ABSO;
+  run_facts(N, WS, WN, O, SS, SL, lane, c_lo, e, lf, rb, &NPH, &ENDS, &ABSO);
   // contractions (ASCII letters, either case): the letter after a suffix of
   // one or two letters that follows a piece-starting apostrophe starts a piece
   const uint32_t OSp = bs_up<1>(O | SP);
@@ -1049,7 +1111,7 @@ __device__ uint32_t cl_word_bits(const uint32_t* pl, int lane, int c_lo, int e, 
   }
   const uint32_t Lp = bs_up<1>(L), Op = bs_up<1>(O), WSp = bs_up<1>(WS), Wp = bs_up<1>(W);
   const uint32_t WNp = bs_up<1>(WN), SSp = bs_up<1>(SS), SPp = bs_up<1>(SP);
-  const uint32_t BN = N & (~Np | NPH);
+  const uint32_t BN = N & (~bs_up<1>(N) | NPH);
   const uint32_t BL = L & ((Lp & AFTER) | (~Lp & ~WSp & ~Op) | (Op & ~SSp & bs_up<1>(OSp)));
   const uint32_t BO = O & ~Op & ~SPp;
   const uint32_t BWN = WN & ~Wp & ~Op;
@@ -1073,7 +1135,7 @@ __device__ bool stage_codes(int64_t n, int64_t t0, const Work& w, TileSmem& sm, 
       v &= in;
     }
     // a byte inside the text whose class index is 0 (set the others' low bit)
-    const uint32_t nib = (v & 0x0F0F0F0Fu) | (~in & 0x01010101u);
+    const uint32_t nib = (v & 0x1F1F1F1Fu) | (~in & 0x01010101u);
     gap |= ((nib - 0x01010101u) & ~nib & 0x80808080u) != 0u;
     if (i >= HALO / 4 && i < (HALO + TILE) / 4) b |= (v & 0x80808080u) != 0u;
     reinterpret_cast<uint32_t*>(sm.cb)[i] = v;
@@ -1082,13 +1144,115 @@ __device__ bool stage_codes(int64_t n, int64_t t0, const Work& w, TileSmem& sm, 
   return __syncthreads_or(gap);
 }
 
+// o200k-style start bits of this lane's word (one wavefront; the planes are
+// the five class-index bits, sequence start, sequence last).  lf, rb: the
+// forward / backward run states (o200k-style classes) before c_lo and from
+// e on; tl: the tail state before c_lo.  *unsup (the same in every lane):
+// the word's outcome depends on a contraction chain or on a word restart
+// that lies before the span, which these carries do not hold.
+__device__ uint32_t o2_word_bits(const uint32_t* pl, int lane, int c_lo, int e, uint32_t lf, uint32_t rb, uint32_t tl,
+                                 bool* unsup) {
+  const uint32_t b0 = pl[0], b1 = pl[1], b2 = pl[2], b3 = pl[3], b4 = pl[4], SS = pl[5], SL = pl[6];
+  const int x0 = c_lo - 32 + 32 * lane;
+  const uint32_t CH = b0 | b1 | b2 | b3 | b4;
+  const uint32_t LI = b4, NL = ~b4 & CH;
+  const uint32_t LW = b4 & b3;                        // lower case
+  const uint32_t BT = b4 & ~b3 & b2 & b1 & b0;        // Lm, Lo, marks
+  const uint32_t UC = b4 & ~b3 & ~(b2 & b1 & b0);     // upper case
+  const uint32_t C1 = b4 & ~b2 & ~b1 & b0, RV = b4 & ~b2 & b1 & ~b0, LL = b4 & ~b2 & b1 & b0, E = b4 & b2 & ~b1 & ~b0;
+  const uint32_t N = NL & ~b2 & ~b1 & b0;
+  const uint32_t O = NL & ((~b2 & b1) | (b2 & ~b1 & ~b0));
+  const uint32_t AP = NL & ~b2 & b1 & b0;
+  const uint32_t SLASH = NL & b2 & ~b1 & ~b0;
+  const uint32_t WS = NL & b2 & (b1 ^ b0), SP = NL & b2 & b1 & ~b0, WN = NL & b2 & b1 & b0;
+  const uint32_t W = WS | WN;
+  const uint32_t X0 = bs_range(x0, 0, 1);
+  uint32_t NPH, ENDS, ABSO;
+  run_facts(N, WS, WN, O, SS, SL, lane, c_lo, e, lf, rb, &NPH, &ENDS, &ABSO);
+  // tails: CR/LF right after an "other" char, then CR, LF and '/' chars
+  const uint32_t RT = (WN | SLASH) & ~SS;
+  uint32_t ST = WN & bs_up<1>(O) & ~SS;
+  if ((tl & 1u) && (tl & 32u) && (tl & 4u)) {
+    // the tail through c_lo - 1 started d chars before c_lo (at the span's
+    // first char if that lies before the span)
+    const int xs = max(c_lo - (int)((tl >> 6) & 63u), 0);
+    ST |= RT & bs_range(x0, xs, xs + 1);
+  }
+  const uint32_t TAIL = bs_fill_up(RT, ST, lane) | ST;
+  // contractions: an apostrophe after a letter, with a contraction shape
+  // after it, attaches to the word before it
+  const uint32_t SSn = bs_dn<1>(SS), SSn2 = bs_dn<2>(SS);
+  const uint32_t CS1 = AP & bs_dn<1>(C1) & ~SSn;
+  const uint32_t CS2 = AP & ~SSn & ~SSn2 & ((bs_dn<1>(RV) & bs_dn<2>(E)) | (bs_dn<1>(LL) & bs_dn<2>(LL)));
+  const uint32_t CAND = (CS1 | CS2) & bs_up<1>(LI) & ~SS;
+  const uint32_t LINK = bs_up<2>(CS1) | bs_up<3>(CS2);  // right after a contraction shape: a chain
+  const uint32_t ATT = CAND & ~LINK;
+  const uint32_t IC = bs_up<1>(ATT) | bs_up<2>(ATT & CS2);  // letters of an attached contraction
+  const uint32_t AFTER = LI & ~SS & (bs_up<2>(ATT & CS1) | bs_up<3>(ATT & CS2));
+  // case rules inside a letter run: PREVW, the last cased char of the word
+  // before this char is lower case (Lm/Lo/marks carry it; a restart after a
+  // contraction cuts it)
+  const uint32_t RB = BT & ~AFTER & ~SS;
+  uint32_t SB = RB & bs_up<1>(LW);
+  bool amb = false;
+  if ((lf & 1u) && ((lf >> 2) & 7u) == C_L2B && ((lf >> 5) & 7u) == C_L) {
+    // an Lm/Lo/mark run that began before the span, after a lower-case letter
+    SB |= RB & X0;
+    // ... which might be a contraction's last letter (then the run restarts
+    // the word): undecided if the run covers the whole left context
+    amb = (lf & FwdOp::CB_CL) != 0u;
+  }
+  const uint32_t LWB = bs_fill_up(RB, SB, lane);
+  const uint32_t PREVW = bs_up<1>(LW | LWB);
+  // ALLU: upper-case chars from which only upper-case chars follow to the
+  // letter run's end (runs cut at e; one that goes on past e takes rb)
+  const uint32_t lim = bs_range(x0, -(1 << 20), e);
+  uint32_t SU = UC & ~SS & (SL | ~bs_dn<1>(LI)) & lim;
+  const bool rb_u_end = (rb & 1u) && ((rb >> 2) & 7u) == C_L2U && ((rb >> 5) & 7u) != C_L &&
+                        ((rb >> 5) & 7u) != C_L2B;
+  if (rb_u_end) SU |= UC & bs_dn<1>(UC) & ~SL & bs_range(x0, e - 1, e);
+  const uint32_t ALLU = bs_fill_down(((UC & ~SS & ~SL) | SU) & lim, SU, lane);
+  const uint32_t RULEA = UC & PREVW;
+  const uint32_t RULEB = UC & bs_up<1>(BT) & ~PREVW & ALLU;
+  const uint32_t Lp = bs_up<1>(LI), Op = bs_up<1>(O), TAILp = bs_up<1>(TAIL), SSp = bs_up<1>(SS);
+  const uint32_t BL_IN = LI & Lp & ~IC & (AFTER | RULEA | RULEB);
+  const uint32_t BL_ST = LI & ~Lp & ~bs_up<1>(WS) & ~IC &
+                         (~Op | TAILp | (~SSp & (bs_up<2>(O & ~TAIL) | bs_up<2>(SP))));
+  const uint32_t BN = N & (~bs_up<1>(N) | NPH);
+  const uint32_t BO = O & ~TAIL & ~bs_up<1>(SP) & (~Op | TAILp) & ~(Lp & ATT);
+  const uint32_t Wp = bs_up<1>(W);
+  const uint32_t BWN = WN & ~Wp & ~Op;
+  const uint32_t BWS = WS & (~Wp | (bs_up<1>(WN) & (ENDS | bs_up<1>(ABSO))) | (bs_up<1>(WS) & ~SL & ~bs_dn<1>(W)));
+  const uint32_t own = bs_range(x0, c_lo, e);
+  // undecided cases: a contraction chain near the own chars, or an upper-case
+  // own char whose word may restart before the span
+  const uint32_t near = bs_range(x0, c_lo - 4, e + 4);
+  const bool chain = __ballot((CAND & LINK & near) != 0u) != 0ull;
+  bool restart = false;
+  if (amb) {
+    // the run from the span's first char reaches the first own upper-case
+    // char that takes PREVW from it
+    const uint32_t notb = CH & ~BT;
+    const uint64_t m = __ballot(notb != 0u);
+    const int l1 = m ? __ffsll((unsigned long long)m) - 1 : 64;
+    const uint32_t w1 = (uint32_t)__builtin_amdgcn_readlane((int)notb, l1 < 64 ? l1 : 0);
+    const uint32_t u1 = (uint32_t)__builtin_amdgcn_readlane((int)UC, l1 < 64 ? l1 : 0);
+    const int first = l1 < 64 ? c_lo - 32 + 32 * l1 + (__ffs((int)w1) - 1) : (1 << 20);
+    restart = first >= c_lo && first < e && ((u1 >> (first - (c_lo - 32 + 32 * l1))) & 1u);
+  }
+  *unsup = chain || restart;
+  return CH & (SS | BN | BL_IN | BL_ST | BO | BWN | BWS) & own;
+}
+
 // The tile's cl100k-style start bits: this thread's 4 (its positions
 // HALO + 4 tid ...) and, in *cnt, the tile's count (the same in every
 // thread).  The code bytes are staged and the tile's carries (sm.carry_fwd /
 // carry_bwd) set.  DIRECT: every span position inside the text starts a
 // char, so char x is span position x; else the chars are compacted first.
-template <bool DIRECT>
-__device__ uint32_t cl100k_bits(TileSmem& sm, uint32_t* cnt) {
+template <int PAT, bool DIRECT>
+__device__ uint32_t pat_bits(TileSmem& sm, uint32_t* cnt, bool* unsup) {
+  constexpr int NPL = PAT == 2 ? 7 : 6;  // class-index bits, sequence start, sequence last
+  constexpr int NIDX = NPL - 2;
   const int tid = (int)threadIdx.x, lane = tid & 63, wid = (int)uniform((uint32_t)tid >> 6);
   int c_lo = HALO, n_own = TILE, nc = SPAN;
   const uint8_t* chars = sm.cb;
@@ -1098,13 +1262,13 @@ __device__ uint32_t cl100k_bits(TileSmem& sm, uint32_t* cnt) {
     const uint32_t v = reinterpret_cast<const uint32_t*>(sm.cb)[j0 >> 2];
     uint32_t own = 0;
 #pragma unroll
-    for (int k = 0; k < PT_CHUNK; ++k) own += ((v >> (8 * k)) & 15u) ? 1u : 0u;
+    for (int k = 0; k < PT_CHUNK; ++k) own += ((v >> (8 * k)) & CB_IDX) ? 1u : 0u;
     uint32_t n_o;
     const uint32_t own_base = block_excl_sum(own, sm.red, &n_o);
     // the halos, lanes 0..15 the left one and 16..31 the right one (every
     // wavefront counts them, so all agree on the indices; wavefront 0 writes them)
     const int hj = lane < HALO ? lane : TILE + lane;
-    const bool hc = lane < 2 * HALO && (sm.cb[hj] & 15u) != 0u;
+    const bool hc = lane < 2 * HALO && (sm.cb[hj] & CB_IDX) != 0u;
     const uint64_t hm = __ballot(hc);
     const uint32_t n_left = (uint32_t)__popcll(hm & 0xFFFFull);
     c_lo = (int)uniform(n_left);
@@ -1114,7 +1278,7 @@ __device__ uint32_t cl100k_bits(TileSmem& sm, uint32_t* cnt) {
 #pragma unroll
     for (int k = 0; k < PT_CHUNK; ++k) {
       const uint32_t c = (v >> (8 * k)) & 255u;
-      if (c & 15u) {
+      if (c & CB_IDX) {
         sm.cc[at] = (uint8_t)c;
         sm.cpos[at] = (uint16_t)(j0 + k);
         ++at;
@@ -1134,28 +1298,31 @@ __device__ uint32_t cl100k_bits(TileSmem& sm, uint32_t* cnt) {
   for (int c = wid; c < BS_CHUNKS; c += PT_THREADS / 64) {
     const int x = c_lo - 32 + 64 * c + lane;
     const uint32_t b = x >= 0 && x < nc ? chars[x] : 0u;
-    const uint32_t idx = b & 15u;
-    uint64_t m[BS_PLANES];
-    m[0] = __ballot(idx & 1u);
-    m[1] = __ballot(idx & 2u);
-    m[2] = __ballot(idx & 4u);
-    m[3] = __ballot(idx & 8u);
-    m[4] = __ballot(idx != 0u && (b & CB_SS));
-    m[5] = __ballot(idx != 0u && (b & CB_SL));
+    const uint32_t idx = b & CB_IDX;
+    uint64_t m[NPL];
+#pragma unroll
+    for (int k = 0; k < NIDX; ++k) m[k] = __ballot((idx >> k) & 1u);
+    m[NIDX] = __ballot(idx != 0u && (b & CB_SS));
+    m[NIDX + 1] = __ballot(idx != 0u && (b & CB_SL));
     if (lane == 0) {
 #pragma unroll
-      for (int k = 0; k < BS_PLANES; ++k) sm.bsw[k][c] = m[k];
+      for (int k = 0; k < NPL; ++k) sm.bsw[k][c] = m[k];
     }
   }
   __syncthreads();
   if (wid == 0) {
-    uint32_t pl[BS_PLANES];
+    uint32_t pl[NPL];
 #pragma unroll
-    for (int k = 0; k < BS_PLANES; ++k)
+    for (int k = 0; k < NPL; ++k)
       pl[k] = lane < BS_WORDS ? reinterpret_cast<const uint32_t*>(sm.bsw[k])[lane] : 0u;
-    const uint32_t B = cl_word_bits(pl, lane, c_lo, c_lo + n_own, uniform(sm.carry_fwd), uniform(sm.carry_bwd));
+    bool uns = false;
+    const uint32_t B = PAT == 2 ? o2_word_bits(pl, lane, c_lo, c_lo + n_own, uniform(sm.carry_fwd),
+                                               uniform(sm.carry_bwd), uniform(sm.carry_tail), &uns)
+                                : cl_word_bits(pl, lane, c_lo, c_lo + n_own, uniform(sm.carry_fwd),
+                                               uniform(sm.carry_bwd));
     const uint32_t tot = wave_incl_fwd<SumOp>((uint32_t)__popc(B), lane);
     if (lane == 63) sm.red[0] = tot;
+    if (lane == 0) sm.red[1] = uns ? 1u : 0u;
     if (DIRECT) {
       if (lane >= 1 && lane <= TILE / 32) sm.sbits[lane - 1] = B;
     } else if (lane < BS_WORDS) {
@@ -1164,6 +1331,7 @@ __device__ uint32_t cl100k_bits(TileSmem& sm, uint32_t* cnt) {
   }
   __syncthreads();
   *cnt = sm.red[0];
+  *unsup = sm.red[1] != 0u;
   if (!DIRECT) {
     // own char o sits at word 1 + o / 32: its start bit goes to its byte position
 #pragma unroll
@@ -1180,7 +1348,7 @@ __device__ uint32_t cl100k_bits(TileSmem& sm, uint32_t* cnt) {
 }
 
 __device__ __forceinline__ int64_t err_code(uint32_t e) {
-  return (e & ERR_OFFSETS) ? -7 : (e & ERR_UTF8) ? -5 : 0;
+  return (e & ERR_OFFSETS) ? -7 : (e & ERR_UTF8) ? -5 : (e & ERR_UNSUP) ? -10 : 0;
 }
 
 // Sum over i < cnt of (a[i] & mask) by the whole workgroup of 256 threads:
@@ -1266,12 +1434,13 @@ __global__ __launch_bounds__(PT_THREADS) void k_pretok(const uint8_t* __restrict
   }
   uint32_t bits = 0;
   uint32_t cnt;
-  bool counted = false, bad;
-  if (PAT == 1) {
-    // cl100k-style rules: classes from the code bytes of the summary pass
+  bool counted = false, bad, unsup = false;
+  if (PAT != 0) {
+    // cl100k- and o200k-style rules: classes from the code bytes of the
+    // summary pass
     const bool gap = stage_codes(n, t0, w, sm, &bad);
-    tile_carries(w, t, ntiles, sm);
-    bits = gap ? cl100k_bits<false>(sm, &cnt) : cl100k_bits<true>(sm, &cnt);
+    tile_carries<PAT>(w, t, ntiles, sm);
+    bits = gap ? pat_bits<PAT, false>(sm, &cnt, &unsup) : pat_bits<PAT, true>(sm, &cnt, &unsup);
     counted = true;
   } else {
     const bool na = stage_tile(bytes, n, offs, nseq, t0, sm);
@@ -1296,7 +1465,8 @@ __global__ __launch_bounds__(PT_THREADS) void k_pretok(const uint8_t* __restrict
   }
   w.flags[(int64_t)t * PT_THREADS + threadIdx.x] = (uint16_t)bits;
   if (!counted) cnt = block_sum(__popc(bits), sm.red);
-  const uint32_t err = (__syncthreads_or(bad) ? ERR_UTF8 : 0u) | (__syncthreads_or(bad_off) ? ERR_OFFSETS : 0u);
+  const uint32_t err = (__syncthreads_or(bad) ? ERR_UTF8 : 0u) | (__syncthreads_or(bad_off) ? ERR_OFFSETS : 0u) |
+                       (unsup ? ERR_UNSUP : 0u);
   if (threadIdx.x == 0) {
     w.tile_cnt[t] = cnt | (err << TILE_ERR_SHIFT);
     // reset for the long-piece stitching of the next pass
@@ -2238,7 +2408,8 @@ __global__ __launch_bounds__(PT_THREADS) __attribute__((amdgpu_waves_per_eu(6)))
   }
   if (last) {
     const uint32_t e = (__syncthreads_or(hi & (ERR_UTF8 << TILE_ERR_SHIFT)) ? ERR_UTF8 : 0u) |
-                       (__syncthreads_or(hi & (ERR_OFFSETS << TILE_ERR_SHIFT)) ? ERR_OFFSETS : 0u);
+                       (__syncthreads_or(hi & (ERR_OFFSETS << TILE_ERR_SHIFT)) ? ERR_OFFSETS : 0u) |
+                       (__syncthreads_or(hi & (ERR_UNSUP << TILE_ERR_SHIFT)) ? ERR_UNSUP : 0u);
     const uint32_t P = base + tot;
     if (threadIdx.x == 0) {
       w.ctr[CTR_P] = P;
@@ -2700,10 +2871,11 @@ __device__ uint32_t class4_at(const uint8_t* __restrict__ text, int64_t q) {
   const uint32_t hi = cp >> 8;
   uint32_t u = 0;
   if (hi < (uint32_t)TT_UNI_L1_SIZE) {
-    const uint32_t idx = (uint32_t)g_uni_l1[hi] * 64u + ((cp & 255u) >> 2);
-    u = (g_uni_l2[idx] >> ((cp & 3u) * 2u)) & 3u;
+    const uint32_t blk = g_uni_l1[hi];
+    u = blk < UNI_SINGLE ? blk : (g_uni_l2[blk * 128u + ((cp & 255u) >> 1)] >> ((cp & 1u) * 4u)) & 15u;
   }
-  return u == 1u ? 1u : u == 2u ? 2u : u == 3u ? 4u : 3u;
+  const uint32_t c = uni_cls(u);
+  return c == C_L ? 1u : c == C_N ? 2u : c == C_WS ? 4u : 3u;
 }
 
 // start of the char that ends right before byte q (q > 0)
@@ -2925,10 +3097,15 @@ hipError_t launch_pretokenize(const uint8_t* bytes, int64_t n, const int64_t* of
                               const Work& w, int32_t* starts, int64_t* out_np, const Tables* tb, hipStream_t st) {
   const int ntiles = ceil_div(n, TILE);
   if (pattern == 1) {
-    hipLaunchKernelGGL(k_tile_summary, dim3(ntiles), dim3(PT_THREADS), 0, st, bytes, n, offs, nseq, w);
+    hipLaunchKernelGGL(k_tile_summary<1>, dim3(ntiles), dim3(PT_THREADS), 0, st, bytes, n, offs, nseq, w);
     prof_mark("k_tile_summary", st);
     hipLaunchKernelGGL(k_pretok<1>, dim3(ntiles), dim3(PT_THREADS), 0, st, bytes, n, offs, nseq, ntiles, w);
     prof_mark("k_pretok<1>", st);
+  } else if (pattern == 2) {
+    hipLaunchKernelGGL(k_tile_summary<2>, dim3(ntiles), dim3(PT_THREADS), 0, st, bytes, n, offs, nseq, w);
+    prof_mark("k_tile_summary", st);
+    hipLaunchKernelGGL(k_pretok<2>, dim3(ntiles), dim3(PT_THREADS), 0, st, bytes, n, offs, nseq, ntiles, w);
+    prof_mark("k_pretok<2>", st);
   } else {
     hipLaunchKernelGGL(k_pretok<0>, dim3(ntiles), dim3(PT_THREADS), 0, st, bytes, n, offs, nseq, ntiles, w);
     prof_mark("k_pretok<0>", st);

@@ -40,6 +40,10 @@ extern "C" {
 #define TT_EOFFSETS   -7  /* batch offsets not monotone / not ending at n (device-side) */
 #define TT_ETOOBIG    -8  /* size beyond the library's limits or the tt_reserve size */
 #define TT_ESTALE     -9  /* tokenizer replaced since the session was reset (sessions below) */
+#define TT_EUNSUPPORTED -10 /* o200k-style rules: the input holds a case the GPU rules do not
+                              decide (device-side): back-to-back contraction suffixes, or an
+                              upper-case letter after a run of Lm/Lo/marks that crosses a tile
+                              start right after a letter that can end a contraction */
 
 #define TT_PATTERN_GPT2   0  /* GPT-2-style rules: lower-case contractions, ' ?letters', ' ?digits',
                                 ' ?other', whitespace with the not-followed-by-non-space rule */
@@ -47,6 +51,12 @@ extern "C" {
                                 with one optional non-letter/digit/newline prefix, 1-3 digit
                                 groups, punctuation absorbing following CR/LF, whitespace up to
                                 the last CR/LF, then the lookahead rule */
+#define TT_PATTERN_O200K  2  /* o200k-style rules: words split by case (upper-type Lu/Lt/Lm/Lo/marks,
+                                lower-type Ll/Lm/Lo/marks) with one optional non-letter/mark/digit/
+                                newline prefix and an attached ASCII case-insensitive contraction,
+                                1-3 digit groups, punctuation absorbing CR, LF and '/', whitespace
+                                up to the last CR/LF run, then the lookahead rule.  Sessions
+                                (incremental repair) are not offered under these rules. */
 
 /* Maximum merges: ids must fit in 20 bits. */
 #define TT_MAX_MERGES (1048576 - 256)
@@ -66,7 +76,7 @@ extern "C" {
  *            0..n_merges-1; merge k makes token id 256 + ranks[k].  May be
  *            NULL, meaning ranks[k] = k.
  * n_merges   0 .. TT_MAX_MERGES.  0 means ids are the UTF-8 bytes.
- * pattern_id TT_PATTERN_GPT2 or TT_PATTERN_CL100K.
+ * pattern_id TT_PATTERN_GPT2, TT_PATTERN_CL100K or TT_PATTERN_O200K.
  *
  * The table must be consistent: both operands of the merge of rank r are ids
  * below 256 + r (every table learned by BPE training is), and no pair may
@@ -290,8 +300,10 @@ int tt_session_read(const tt_session* s, uint8_t* text_out, int32_t* ids_out, in
                     hipStream_t stream);
 
 /* tt_char_class -- host query of the compiled Unicode class table:
- * 0 other, 1 letter (\p{L}), 2 number (\p{N}), 3 White_Space; -1 if cp is
- * not a Unicode scalar value.  No device work. */
+ * 0 other, 1 upper/title-case letter (Lu, Lt), 2 lower-case letter (Ll),
+ * 3 modifier/other letter (Lm, Lo), 4 mark (\p{M}), 5 number (\p{N}),
+ * 6 White_Space, 7 punctuation (\p{P}), 8 symbol (\p{S}); -1 if cp is not
+ * a Unicode scalar value.  No device work. */
 int tt_char_class(uint32_t cp);
 
 /* tt_profile -- per-kernel timing of later calls (a measurement aid).

@@ -38,6 +38,7 @@ O_CLASS = "[^" + _W + "\\p{L}\\p{N}]"  # neither whitespace, letter nor digit
 
 GPT2 = 0
 CL100K = 1
+O200K = 2
 
 # GPT-2-style, alternatives in priority order:
 #   G1 apostrophe contraction (lower case only)
@@ -70,7 +71,36 @@ _CL100K_RULES = [
     W_CLASS + "+",
 ]
 
-RULES = {GPT2: _GPT2_RULES, CL100K: _CL100K_RULES}
+# o200k-style, alternatives in priority order.  Letters are split by case:
+# "upper-type" chars are Lu, Lt, Lm, Lo and combining marks, "lower-type"
+# chars Ll, Lm, Lo and marks (so modifier/other letters and marks go with
+# either case).  Reading: marks count as letter-type chars only, never as
+# "other" chars, so neither the optional leading char nor the "other" run
+# takes one.
+#   Q1 one optional char that is not CR/LF/letter/mark/digit, upper-type
+#      chars, then one or more lower-type chars, then an optional contraction
+#      (ASCII case-insensitive, attached to the word)
+#   Q2 the same with one or more upper-type chars, then lower-type chars
+#   Q3 one to three digits
+#   Q4 optional space, "other" run, then any CR, LF and '/' chars
+#   Q5 whitespace up to and including the last CR/LF run of the whitespace run
+#   Q6 whitespace not followed by a non-whitespace char   Q7 whitespace
+_UPPER_T = "[\\p{Lu}\\p{Lt}\\p{Lm}\\p{Lo}\\p{M}]"
+_LOWER_T = "[\\p{Ll}\\p{Lm}\\p{Lo}\\p{M}]"
+_LEAD = "[^\\r\\n\\p{L}\\p{M}\\p{N}]?"
+_O_CLASS_M = "[^" + _W + "\\p{L}\\p{M}\\p{N}]"
+_CONTRACTION = "(?:'(?:[sS]|[tT]|[rR][eE]|[vV][eE]|[mM]|[lL][lL]|[dD]))?"
+_O200K_RULES = [
+    _LEAD + _UPPER_T + "*" + _LOWER_T + "+" + _CONTRACTION,
+    _LEAD + _UPPER_T + "+" + _LOWER_T + "*" + _CONTRACTION,
+    "\\p{N}{1,3}",
+    " ?" + _O_CLASS_M + "+[\\r\\n/]*",
+    W_CLASS + "*[\\r\\n]+",
+    W_CLASS + "+(?!" + NOT_W_CLASS + ")",
+    W_CLASS + "+",
+]
+
+RULES = {GPT2: _GPT2_RULES, CL100K: _CL100K_RULES, O200K: _O200K_RULES}
 PATTERNS = {k: "|".join(v) for k, v in RULES.items()}
 _COMPILED = {k: regex.compile(v, regex.VERSION0) for k, v in PATTERNS.items()}
 

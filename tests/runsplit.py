@@ -9,6 +9,8 @@ the rule tables (no regex engine); tests check it equals the regex split on
 every short string over a class-covering alphabet.
 
 Classes: L letters, N digits, WN = CR/LF, WS = other whitespace, O the rest.
+The o200k-style set (pattern 2) splits letters further by case: U (Lu, Lt),
+LW (Ll), B (Lm, Lo and combining marks, which go with either case).
 """
 import regex
 
@@ -31,12 +33,35 @@ def char_class(ch):
     return O
 
 
+_LU = regex.compile(r"[\p{Lu}\p{Lt}]")
+_LL = regex.compile(r"\p{Ll}")
+_LB = regex.compile(r"[\p{Lm}\p{Lo}\p{M}]")
+U, LW, B = "U", "LW", "B"
+
+
+def char_class2(ch):
+    """o200k-style classes: U, LW, B (letter-type), N, WS, WN, O."""
+    c = char_class(ch)
+    if c in (WN, WS, N):
+        return c
+    if _LU.match(ch):
+        return U
+    if _LL.match(ch):
+        return LW
+    if _LB.match(ch):
+        return B
+    return O
+
+
 def _is_w(c):
     return c in (WS, WN)
 
 
 def piece_starts(text, pattern_id):
-    """Char indices where a pre-token starts (pattern 0 GPT-2-style, 1 cl100k)."""
+    """Char indices where a pre-token starts (pattern 0 GPT-2-style, 1
+    cl100k-style, 2 o200k-style)."""
+    if pattern_id == 2:
+        return _o200k_starts(text)
     n = len(text)
     cls = [char_class(ch) for ch in text]
     run_start = [0] * n
@@ -125,6 +150,120 @@ def piece_starts(text, pattern_id):
                     b = 1 if (ends_run or absorbed) else 0
                 else:
                     b = 1 if (i + 1 < n and not _is_w(cls[i + 1])) else 0
+        if b:
+            starts.append(i)
+    return starts
+
+
+def _o200k_starts(text):
+    """o200k-style starts.  Letter-type chars (U, LW, B) form letter blocks;
+    inside one, a new word starts at an upper-case char U when the last cased
+    char of the current word is lower-case (rule A), or when it follows a B
+    char, no lower-case char precedes it in the word and only upper-case
+    chars follow it to the block's end (rule B: the lower-type run must take
+    at least one char, so it takes the last B and leaves the upper-case tail).
+    A contraction after a word belongs to it; the char after the contraction
+    starts a word.  An "other" char followed by CR/LF starts a tail of CR, LF
+    and '/' chars that belongs to its piece."""
+    n = len(text)
+    cls = [char_class2(ch) for ch in text]
+    li = [c in (U, LW, B) for c in cls]
+    # tails: CR/LF right after an "other" char, then CR, LF and '/' chars
+    tail = [False] * n
+    for i in range(1, n):
+        if cls[i] == WN and cls[i - 1] == O:
+            tail[i] = True
+        elif tail[i - 1] and (cls[i] == WN or text[i] == "/"):
+            tail[i] = True
+    # contractions attached to the word before them; after[i]: a word
+    # restarts.  The apostrophe right after an attached contraction cannot
+    # attach (no word ends there): along back-to-back contractions attachment
+    # alternates.
+    def shape(a):
+        one = text[a + 1] if a + 1 < n else ""
+        two = text[a + 1:a + 3]
+        if one.isascii() and one.lower() in ("s", "t", "m", "d"):
+            return 1
+        if len(two) == 2 and two.isascii() and two.lower() in ("re", "ve", "ll"):
+            return 2
+        return 0
+
+    contr = [0] * n
+    after = [False] * n
+    in_contr = [False] * n
+    for a in range(1, n - 1):
+        if text[a] == "'" and li[a - 1]:
+            m = shape(a)
+            prev_attached = any(a - k - 1 >= 0 and contr[a - k - 1] == k for k in (1, 2))
+            if m and not prev_attached:
+                contr[a] = m
+                for k in range(1, m + 1):
+                    in_contr[a + k] = True
+                if a + m + 1 < n:
+                    after[a + m + 1] = True
+    run_start = [0] * n
+    for i in range(1, n):
+        run_start[i] = run_start[i - 1] if cls[i] == cls[i - 1] else i
+    wrun_end = [n] * n
+    for i in range(n - 2, -1, -1):
+        wrun_end[i] = wrun_end[i + 1] if (_is_w(cls[i]) and _is_w(cls[i + 1]) and
+                                          (cls[i] == WS) == (cls[i + 1] == WS)) else i + 1
+
+    def prev_cased_lower(i):
+        # the last cased char of the current word before i is lower-case
+        k = i - 1
+        while k >= 0 and cls[k] == B and not after[k]:
+            k -= 1
+        return k >= 0 and cls[k] == LW
+
+    def only_upper_to_end(i):
+        k = i
+        while k < n and cls[k] == U:
+            k += 1
+        return k == n or not li[k]
+
+    starts = [0] if n else []
+    for i in range(1, n):
+        c, p = cls[i], cls[i - 1]
+        if c == N:
+            b = p != N or (i - run_start[i]) % 3 == 0
+        elif c == WN:
+            b = not (_is_w(p) or p == O)
+        elif c == WS:
+            if not _is_w(p):
+                b = True
+            elif p == WN:
+                s = run_start[i - 1]
+                ends_run = wrun_end[i] == n or not _is_w(cls[wrun_end[i]])
+                b = ends_run or (s > 0 and cls[s - 1] == O)
+            else:
+                b = i + 1 < n and not _is_w(cls[i + 1])
+        elif c == O:
+            if tail[i]:
+                b = False
+            elif text[i - 1] == " ":
+                b = False
+            elif p == O:
+                b = tail[i - 1]
+            elif li[i - 1] and contr[i]:
+                b = False
+            else:
+                b = True
+        else:  # letter-type
+            if in_contr[i]:
+                b = False
+            elif li[i - 1]:
+                b = after[i] or (c == U and prev_cased_lower(i)) or \
+                    (c == U and p == B and not prev_cased_lower(i) and only_upper_to_end(i))
+            elif p == WS:
+                b = False
+            elif p == O:
+                if tail[i - 1]:
+                    b = True
+                else:
+                    b = i >= 2 and ((cls[i - 2] == O and not tail[i - 2]) or text[i - 2] == " ")
+            else:
+                b = True
         if b:
             starts.append(i)
     return starts

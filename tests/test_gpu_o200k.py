@@ -1,0 +1,200 @@
+"""o200k-style rules on the GPU (tt_pretokenize and tt_encode through the C ABI)
+against the CPU oracle, bit for bit.
+
+Brute force over every string of length <= 5 of a class-covering alphabet
+(both cases, an Lo letter, a combining mark, '/', contraction letters), random
+multibyte strings, runs that cross tiles for each fact carried between tiles
+(digit groups, whitespace before CR/LF, CR/LF after "other" chars, CR/LF/'/'
+tails, upper-case runs to the end of a word, Lm/Lo runs after a lower-case
+letter), and a 1M-char encode.  Inputs holding back-to-back contraction
+suffixes (whose attachment alternates along the chain) are the one case the
+GPU rules leave undecided: the call reports TT_EUNSUPPORTED, never a wrong
+split.
+"""
+import itertools
+import os
+import random
+import re
+
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+import exact_byte_level_amd as tt  # noqa: E402
+from oracle.bpe import Vocab, encode as oracle_encode  # noqa: E402
+from oracle.pretok import O200K, piece_starts_batch, split_bytes  # noqa: E402
+from synth import mix_text  # noqa: E402
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+# an apostrophe after a letter or mark with a contraction shape after it,
+# right after another contraction shape
+_SHAPE = "(?:[sStTmMdD]|[rRvV][eE]|[lL][lL])"
+CHAIN = re.compile("'" + _SHAPE + "'" + _SHAPE)
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _device():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    torch.cuda.set_device(0)
+    yield
+    torch.cuda.synchronize()
+
+
+def dev(data):
+    return torch.frombuffer(bytearray(data), dtype=torch.uint8).cuda() if len(data) else torch.empty(
+        0, dtype=torch.uint8, device="cuda")
+
+
+def load(name="c3"):
+    merges = np.load(os.path.join(ROOT, "data", "vocab_%s.npy" % name))
+    tt.load(merges, pattern_id=O200K)
+    return Vocab(merges)
+
+
+def batch(strings):
+    data, offs = b"", [0]
+    for s in strings:
+        data += s.encode()
+        offs.append(len(data))
+    return data, offs
+
+
+def gpu_starts(data, offsets=None):
+    off = None if offsets is None else torch.tensor(offsets, dtype=torch.int64, device="cuda")
+    return tt.pretokenize(dev(data), off).cpu().numpy().tolist()
+
+
+def check_batch(strings):
+    """GPU starts of the batch equal the oracle's; on a difference, name the
+    first string where they part."""
+    data, offs = batch(strings)
+    got, want = gpu_starts(data, offs), piece_starts_batch(data, offs, O200K)
+    if got == want:
+        return
+    k = next((i for i, (a, b) in enumerate(zip(got, want)) if a != b), min(len(got), len(want)))
+    pos = min(got[k] if k < len(got) else len(data), want[k] if k < len(want) else len(data))
+    s = int(np.searchsorted(np.asarray(offs), pos, side="right")) - 1
+    raise AssertionError("first difference in string %d %r: gpu %s oracle %s" % (
+        s, strings[s], [x - offs[s] for x in got if offs[s] <= x < offs[s + 1]],
+        [x - offs[s] for x in want if offs[s] <= x < offs[s + 1]]))
+
+
+ALPHA = ["a", "A", "s", "S", "r", "e", "ª", "́", "1", ".", "/", "'", " ", "\n"]
+
+
+def test_every_short_string():
+    load()
+    strings = ["".join(t) for n in range(6) for t in itertools.product(ALPHA, repeat=n)]
+    strings = [s for s in strings if not CHAIN.search(s)]
+    say("o200k brute force: %d strings" % len(strings))
+    check_batch(strings)
+
+
+ALPHA2 = ALPHA + list("lLvVmMdDtTEéÉ中\U0001f600") + [
+    "　", "\xa0", "2", "²", "_", "(", "\t", "\r", "ǅ", "ʰ", "कि", "İ", "ß"]
+
+
+def test_random_multibyte_strings():
+    load()
+    rng = random.Random(91)
+    strings = []
+    while len(strings) < 40_000:
+        s = "".join(rng.choice(ALPHA2) for _ in range(rng.randint(0, 40)))
+        if not CHAIN.search(s):
+            strings.append(s)
+    say("o200k random batch: %d strings" % len(strings))
+    check_batch(strings)
+
+
+LONG_RUNS = [
+    "a" + "1" * 20_000 + "x" + "2" * 4_097,                 # digit groups
+    ".\n" + "\n" * 9_000 + " " * 9_000 + "z",             # CR/LF after "other", whitespace
+    "x" + " " * 8_191 + "\n" + " " * 8_193,               # whitespace run ending in CR/LF
+    "*/\n" + "/" * 5_000 + "x",                           # a tail of '/' across tiles
+    "a.\n" + "/\n" * 3_000 + ".b",                        # interleaved tail
+    "q" + "/" * 4_000 + "\n" + "y",                       # '/' in the "other" run, then a tail
+    "x" + "A" * 5_000 + "b" + "C" * 3_000 + ".",          # upper-case runs: to the word end or not
+    "x" + "中" * 3_000 + "A" + "中" * 2_000 + "Bc",  # Lo runs after a lower-case letter
+    "X" + "ª" * 3_000 + "AB",                        # Lo run after upper case, upper tail
+    "́" * 4_000 + "AB" + "ª" * 2_000 + "C",     # marks run
+    "it's" + "b" * 6_000 + "'re" + "c" * 3,                # contractions around a long word
+]
+
+
+def test_runs_crossing_tiles():
+    load()
+    for text in LONG_RUNS:
+        data = text.encode()
+        say("o200k long runs: %d bytes" % len(data))
+        _, want = split_bytes(data, O200K)
+        assert gpu_starts(data) == want
+    check_batch(LONG_RUNS)
+
+
+def _tile_edge_text(seed, tile=1024, ntiles=48):
+    rng = random.Random(seed)
+    runs = [" ", "7", "x", "X", ".", "\n", "\t", "'", "\r\n", "/", "ª", "́", "\n/"]
+    out = bytearray()
+    for t in range(1, ntiles):
+        edge = t * tile
+        ch = rng.choice(runs)
+        k = rng.choice([1, 2, 3, 15, 16, 17, 31, 32, 33, 60, 64, 70, 130])
+        left = rng.randint(0, k)
+        while len(out) < edge - left * len(ch.encode()):
+            word = rng.choice(["ab", "don't", "we're", "x1", "Il", "HTMLParser", "9", "..", " ", "\n", "a/b",
+                               "Été", "CamelCase"])
+            out += word.encode()
+        out += (ch * k).encode()
+        out += rng.choice([b"'s", b"'LL", b"q", b"Q", b"1", b"!", b" ", b"/", b"\n"])
+    return bytes(out)
+
+
+def test_runs_across_tile_edges():
+    data = _tile_edge_text(77)
+    assert not CHAIN.search(data.decode())
+    v = load("c1")
+    say("o200k tile edges: %d bytes" % len(data))
+    _, want = split_bytes(data, O200K)
+    assert gpu_starts(data) == want
+    got = tt.encode(dev(data)).cpu().numpy()
+    assert np.array_equal(got, np.asarray(oracle_encode(data, v, O200K, {}), dtype=np.int32))
+
+
+def test_encode_mix_1m():
+    v = load("c3")
+    data = mix_text(1_000_000, 203, multibyte=True)
+    say("o200k encode: %d bytes" % len(data))
+    got = tt.encode(dev(data)).cpu().numpy()
+    want = np.asarray(oracle_encode(data, v, O200K, {}), dtype=np.int32)
+    assert np.array_equal(got, want)
+
+
+def test_contraction_chain_is_reported_unsupported():
+    load()
+    for text in ["a's's", "it's'll go", "x" * 3000 + "'d've"]:
+        say("o200k chain: %r" % text[-12:])
+        with pytest.raises(tt.TTError) as ei:
+            tt.encode(dev(text.encode()))
+        assert ei.value.code == tt.TT_EUNSUPPORTED
+    # a lone contraction and a quote after one are decided
+    for text in ["it's", "'it's'", "rock'n'roll"]:
+        v = load()
+        got = tt.encode(dev(text.encode())).cpu().numpy()
+        assert np.array_equal(got, np.asarray(oracle_encode(text.encode(), v, O200K, {}), dtype=np.int32))
+
+
+def test_sessions_are_refused():
+    load()
+    s = tt.Session(1024) if hasattr(tt, "Session") else None
+    if s is None:
+        pytest.skip("no session binding")
+    with pytest.raises(tt.TTError) as ei:
+        s.reset(dev(b"hello world"))
+    assert ei.value.code == tt.TT_EINVAL

@@ -18,7 +18,7 @@ import re
 import pytest
 import regex
 
-from oracle.pretok import CL100K, GPT2, PATTERNS, WHITESPACE_CPS, piece_starts_batch, split, split_bytes
+from oracle.pretok import CL100K, GPT2, O200K, PATTERNS, WHITESPACE_CPS, piece_starts_batch, split, split_bytes
 from runsplit import piece_starts
 
 EXAMPLES = [
@@ -55,6 +55,31 @@ def test_worked_examples(text, gpt2, cl100k):
     assert split(text, CL100K) == cl100k
 
 
+# o200k-style, worked by hand from its rule table (Q1..Q7):
+EXAMPLES_O200K = [
+    ("HelloWorld", ["Hello", "World"]),        # Q1 ends at the upper-case W after lower-case o
+    ("HTMLParser", ["HTMLParser"]),            # upper-type run, then the lower-type run
+    ("aBcD", ["a", "Bc", "D"]),                # D: no lower-case char after it, Q2
+    ("ABªCD", ["ABª", "CD"]),                  # lower-type run takes only the last Lo char
+    ("don't stop", ["don't", " stop"]),        # the contraction stays with its word
+    ("AB'S", ["AB'S"]),                        # Q2 + contraction, case-insensitive
+    ("it'sªBc", ["it's", "ªBc"]),              # a word restarts after the contraction
+    ("a's's", ["a's", "'s"]),                  # no word ends at the second apostrophe
+    ("a's's's", ["a's", "'s's"]),              # ... so attachment alternates
+    ("a/\n/b", ["a", "/\n/", "b"]),            # Q4: "other" run, then CR/LF and '/'
+    (".\n/.b", [".\n/", ".b"]),                # the tail ends; '.' leads the next word
+    ("..\u0301a", ["..", "\u0301a"]),          # marks are letter-type, not "other"
+    (" 12345", [" ", "123", "45"]),
+    ("x\n \n  y", ["x", "\n \n", " ", " y"]),
+    ("\u00c9t\u00e9 2024!\n", ["\u00c9t\u00e9", " ", "202", "4", "!\n"]),
+]
+
+
+@pytest.mark.parametrize("text,pieces", EXAMPLES_O200K)
+def test_worked_examples_o200k(text, pieces):
+    assert split(text, O200K) == pieces
+
+
 def _starts(pieces):
     out, pos = [], 0
     for p in pieces:
@@ -79,6 +104,27 @@ def test_exhaustive_short_strings_against_run_decomposition(pattern_id):
 
 ALPHA2 = ALPHA + list("lLvVmdDtTEé中😀") + ["　", "\xa0", "2", "²", "_", "(", "\x0b", "٣"]
 
+# o200k-style: both cases, an Lo letter, a combining mark, '/', contractions
+ALPHA_O = ["a", "A", "s", "S", "r", "e", "\u00aa", "\u0301", "1", ".", "/", "'", " ", "\n"]
+ALPHA_O2 = ALPHA2 + ["\u00aa", "\u0301", "\u01c5", "\u02b0", "/", "\u00c9", "\u0915\u093f"]
+
+
+def test_exhaustive_short_strings_o200k():
+    bad = []
+    for length in range(6):
+        for tup in itertools.product(ALPHA_O, repeat=length):
+            s = "".join(tup)
+            if _starts(split(s, O200K)) != piece_starts(s, O200K):
+                bad.append(s)
+    assert bad == []
+
+
+def test_random_strings_o200k():
+    rng = random.Random(17)
+    for _ in range(30_000):
+        s = "".join(rng.choice(ALPHA_O2) for _ in range(rng.randint(6, 30)))
+        assert _starts(split(s, O200K)) == piece_starts(s, O200K), repr(s)
+
 
 @pytest.mark.parametrize("pattern_id", [GPT2, CL100K])
 def test_random_strings_against_run_decomposition(pattern_id):
@@ -92,7 +138,7 @@ def test_long_runs_against_run_decomposition():
     texts = ["a" + "1" * 1000 + "x", ".\n" * 3 + "\n" * 500 + " " * 700 + "z", " " * 999 + "7",
              "\t" * 5 + "\n" + " " * 400, "x" + "٣" * 11 + "2" * 7]
     for t in texts:
-        for pat in (GPT2, CL100K):
+        for pat in (GPT2, CL100K, O200K):
             assert _starts(split(t, pat)) == piece_starts(t, pat)
 
 
@@ -121,6 +167,19 @@ def test_cl100k_pattern_under_oniguruma_matches_regex_module():
         s = "".join(rng.choice(HF_ALPHA) for _ in range(rng.randint(1, 40)))
         hf = [a for _, (a, _) in sp.pre_tokenize_str(s)]
         assert _starts(split(s, CL100K)) == hf, repr(s)
+
+
+def test_o200k_pattern_under_oniguruma_matches_regex_module():
+    tk = pytest.importorskip("tokenizers")
+    pat = re.sub(r"\\(?:x([0-9a-f]{2})|u([0-9a-f]{4}))", lambda m: "\\x{%s}" % (m.group(1) or m.group(2)),
+                 PATTERNS[O200K])
+    sp = tk.pre_tokenizers.Split(tk.Regex(pat), behavior="isolated")
+    rng = random.Random(7)
+    alpha = HF_ALPHA + ["\u00aa", "\u0301", "/", "\u00c9", "'", "S", "R", "E"]
+    for _ in range(5000):
+        s = "".join(rng.choice(alpha) for _ in range(rng.randint(1, 40)))
+        hf = [a for _, (a, _) in sp.pre_tokenize_str(s)]
+        assert _starts(split(s, O200K)) == hf, repr(s)
 
 
 def test_whitespace_set_is_unicode_white_space():
@@ -161,6 +220,7 @@ BATCH_TEXTS = ["ab ", "", "cd", "é1", "  x", "中 ", "1234"]
 BATCH_STARTS = {
     GPT2: [0, 2, 3, 5, 7, 8, 9, 11, 14, 15],
     CL100K: [0, 2, 3, 5, 7, 8, 9, 11, 14, 15, 18],
+    O200K: [0, 2, 3, 5, 7, 8, 9, 11, 14, 15, 18],  # as cl100k-style: no case or tail rule applies
 }
 
 
@@ -172,7 +232,7 @@ def _batch(texts):
     return data, offs
 
 
-@pytest.mark.parametrize("pattern_id", [GPT2, CL100K])
+@pytest.mark.parametrize("pattern_id", [GPT2, CL100K, O200K])
 def test_piece_starts_batch_hand_worked(pattern_id):
     data, offs = _batch(BATCH_TEXTS)
     assert offs == [0, 3, 3, 5, 8, 11, 15, 19]
@@ -183,7 +243,7 @@ def test_piece_starts_batch_hand_worked(pattern_id):
     assert 3 not in [len(data.decode()[:i].encode()) for i in whole]
 
 
-@pytest.mark.parametrize("pattern_id", [GPT2, CL100K])
+@pytest.mark.parametrize("pattern_id", [GPT2, CL100K, O200K])
 def test_piece_starts_batch_random_against_run_decomposition(pattern_id):
     """Random batches (empty texts, texts ending in whitespace, multibyte chars)
     against the regex-free run decomposition, applied text by text and shifted
