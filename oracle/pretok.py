@@ -39,6 +39,7 @@ O_CLASS = "[^" + _W + "\\p{L}\\p{N}]"  # neither whitespace, letter nor digit
 GPT2 = 0
 CL100K = 1
 O200K = 2
+DEEPSEEK = 3
 
 # GPT-2-style, alternatives in priority order:
 #   G1 apostrophe contraction (lower case only)
@@ -100,9 +101,54 @@ _O200K_RULES = [
     W_CLASS + "+",
 ]
 
+# DeepSeek-style: three splits in a row, each cutting every piece the one
+# before left and keeping both what it matched and what lay between matches
+# as pieces ("isolated" splitting):
+#   S1 digit groups of one to three
+#   S2 runs of CJK unified ideographs (U+4E00..U+9FA5), hiragana and katakana
+#      (U+3040..U+30FF)
+#   S3 the rule set below, on each piece by itself (a piece's end is the
+#      end of text for the lookahead); chars no rule takes stay pieces
+#   D1 an ASCII punctuation or symbol char, then ASCII letters
+#   D2 one optional char that is not CR/LF/letter/punctuation/symbol, then
+#      letters and marks
+#   D3 optional space, a punctuation/symbol run, then any CR/LF chars
+#   D4 whitespace up to and including the last CR/LF run
+#   D5 whitespace not followed by a non-whitespace char   D6 whitespace
+_ASCII_PS = "[!-/:-@\\[-`{-~]"
+_DEEPSEEK_STAGES = [
+    "\\p{N}{1,3}",
+    "[\\u4e00-\\u9fa5\\u3040-\\u30ff]+",
+    "|".join([
+        _ASCII_PS + "[A-Za-z]+",
+        "[^\\r\\n\\p{L}\\p{P}\\p{S}]?[\\p{L}\\p{M}]+",
+        " ?[\\p{P}\\p{S}]+[\\r\\n]*",
+        W_CLASS + "*[\\r\\n]+",
+        W_CLASS + "+(?!" + NOT_W_CLASS + ")",
+        W_CLASS + "+",
+    ]),
+]
+
 RULES = {GPT2: _GPT2_RULES, CL100K: _CL100K_RULES, O200K: _O200K_RULES}
 PATTERNS = {k: "|".join(v) for k, v in RULES.items()}
 _COMPILED = {k: regex.compile(v, regex.VERSION0) for k, v in PATTERNS.items()}
+_STAGES = {DEEPSEEK: [regex.compile(p, regex.VERSION0) for p in _DEEPSEEK_STAGES]}
+
+
+def _isolate(pieces, rx):
+    """One isolating split: every match and every non-empty stretch between
+    matches (or before the first / after the last) becomes a piece."""
+    out = []
+    for p in pieces:
+        pos = 0
+        for m in rx.finditer(p):
+            if m.start() > pos:
+                out.append(p[pos:m.start()])
+            out.append(m.group())
+            pos = m.end()
+        if pos < len(p):
+            out.append(p[pos:])
+    return out
 
 
 def split(text, pattern_id):
@@ -111,7 +157,12 @@ def split(text, pattern_id):
     Plain left-to-right ``finditer``: each match starts where the previous one
     ended.  The rule sets match every char, so the pieces tile the text.
     """
-    pieces = [m.group() for m in _COMPILED[pattern_id].finditer(text)]
+    if pattern_id in _STAGES:
+        pieces = [text] if text else []
+        for rx in _STAGES[pattern_id]:
+            pieces = _isolate(pieces, rx)
+    else:
+        pieces = [m.group() for m in _COMPILED[pattern_id].finditer(text)]
     if "".join(pieces) != text or any(p == "" for p in pieces):
         raise AssertionError("rule set did not tile the text")
     return pieces

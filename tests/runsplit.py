@@ -59,9 +59,11 @@ def _is_w(c):
 
 def piece_starts(text, pattern_id):
     """Char indices where a pre-token starts (pattern 0 GPT-2-style, 1
-    cl100k-style, 2 o200k-style)."""
+    cl100k-style, 2 o200k-style, 3 DeepSeek-style)."""
     if pattern_id == 2:
         return _o200k_starts(text)
+    if pattern_id == 3:
+        return _deepseek_starts(text)
     n = len(text)
     cls = [char_class(ch) for ch in text]
     run_start = [0] * n
@@ -264,6 +266,106 @@ def _o200k_starts(text):
                     b = i >= 2 and ((cls[i - 2] == O and not tail[i - 2]) or text[i - 2] == " ")
             else:
                 b = True
+        if b:
+            starts.append(i)
+    return starts
+
+
+_LM = regex.compile(r"[\p{L}\p{M}]")
+_PS = regex.compile(r"[\p{P}\p{S}]")
+LM, PS = "LM", "PS"
+
+
+def char_class3(ch):
+    """DeepSeek-style classes: LM (letters and marks), PS (punctuation and
+    symbols), N, WS, WN, O (the rest)."""
+    c = char_class(ch)
+    if c in (WN, WS, N):
+        return c
+    if _LM.match(ch):
+        return LM
+    if _PS.match(ch):
+        return PS
+    return O
+
+
+def _deepseek_starts(text):
+    """DeepSeek-style starts.  Digit groups and CJK/kana runs cut the text
+    into segments first (each starts a piece, and a segment's end is the end
+    of text for the rules inside it).  Inside a segment: an ASCII
+    punctuation/symbol char that starts a piece and is followed by ASCII
+    letters takes those letters (D1); otherwise letters and marks form words
+    with one optional leading char (whitespace, "other"); punctuation and
+    symbols form runs (with one leading space) that take the CR/LF chars after
+    them; whitespace follows the same rules as cl100k-style; "other" chars
+    no rule takes are pieces of their own, joined while they follow each other."""
+    n = len(text)
+    cls = [char_class3(ch) for ch in text]
+    cjk = [0x4E00 <= ord(ch) <= 0x9FA5 or 0x3040 <= ord(ch) <= 0x30FF for ch in text]
+    al = [ch.isascii() and ch.isalpha() for ch in text]
+    ap1 = [ch.isascii() and bool(_PS.match(ch)) for ch in text]
+    seg = [False] * n
+    dig = 0
+    for i in range(n):
+        if cls[i] == N:
+            dig = dig + 1 if i > 0 and cls[i - 1] == N else 0
+            seg[i] = dig % 3 == 0
+        else:
+            seg[i] = i == 0 or cls[i - 1] == N or cjk[i] != cjk[i - 1]
+    if n:
+        seg[0] = True
+    same = [i > 0 and not seg[i] for i in range(n)]  # i - 1 lies in i's segment
+
+    def nxt(i):  # class of the next char of the segment, or None
+        return cls[i + 1] if i + 1 < n and same[i + 1] else None
+
+    d1s = [ap1[i] and i + 1 < n and same[i + 1] and al[i + 1] and
+           (not same[i] or (cls[i - 1] != PS and text[i - 1] != " ")) for i in range(n)]
+    d1l = [False] * n
+    for i in range(n):
+        d1l[i] = al[i] and same[i] and (d1s[i - 1] or d1l[i - 1])
+    wrun_end = [n] * n  # end of the whitespace run of the same kind (WS or WN) in the segment
+    for i in range(n - 1, -1, -1):
+        if i + 1 < n and same[i + 1] and cls[i + 1] == cls[i]:
+            wrun_end[i] = wrun_end[i + 1]
+        else:
+            wrun_end[i] = i + 1
+    run_start = [0] * n
+    for i in range(n):
+        run_start[i] = run_start[i - 1] if same[i] and cls[i] == cls[i - 1] else i
+
+    starts = []
+    for i in range(n):
+        if seg[i]:
+            starts.append(i)
+            continue
+        c, p = cls[i], cls[i - 1]
+        if c == N:
+            b = False
+        elif c == LM:
+            if p == LM:
+                b = d1l[i - 1] and not al[i]
+            elif p == PS:
+                b = not (d1s[i - 1] and al[i])
+            else:
+                b = p == WN
+        elif c == PS:
+            b = p != PS and text[i - 1] != " "
+        elif c == WN:
+            b = not (_is_w(p) or p == PS)
+        elif c == WS:
+            if not _is_w(p):
+                b = True
+            elif p == WN:
+                e = wrun_end[i]
+                ends_run = e == n or not same[e] or not _is_w(cls[e])
+                s0 = run_start[i - 1]
+                b = ends_run or (same[s0] and cls[s0 - 1] == PS)
+            else:
+                q = nxt(i)
+                b = q is not None and not _is_w(q)
+        else:  # O
+            b = p != O or nxt(i) == LM
         if b:
             starts.append(i)
     return starts

@@ -18,7 +18,8 @@ import re
 import pytest
 import regex
 
-from oracle.pretok import CL100K, GPT2, O200K, PATTERNS, WHITESPACE_CPS, piece_starts_batch, split, split_bytes
+from oracle.pretok import (CL100K, DEEPSEEK, GPT2, O200K, PATTERNS, WHITESPACE_CPS, _DEEPSEEK_STAGES,
+                           piece_starts_batch, split, split_bytes)
 from runsplit import piece_starts
 
 EXAMPLES = [
@@ -80,6 +81,30 @@ def test_worked_examples_o200k(text, pieces):
     assert split(text, O200K) == pieces
 
 
+# DeepSeek-style, worked by hand from its three splits (S1 digits, S2 CJK and
+# kana runs, S3 rules D1..D6 on every piece by itself):
+EXAMPLES_DEEPSEEK = [
+    ("Hello world", ["Hello", " world"]),      # D2 with a leading space
+    (".abc\u00e9", [".abc", "\u00e9"]),          # D1 takes ASCII letters only
+    ("_foo_bar", ["_foo", "_bar"]),            # '_' is ASCII punctuation: D1 twice
+    ("\u20acfoo", ["\u20ac", "foo"]),            # a non-ASCII symbol is a D3 run
+    ("x1234567y", ["x", "123", "456", "7", "y"]),
+    ("\u4e2d\u6587abc", ["\u4e2d\u6587", "abc"]),   # S2 cuts the CJK run out
+    ("\u3042\u30fb\u3044", ["\u3042", "\u30fb", "\u3044"]),  # S3 splits inside a kana run
+    (" .a", [" .", "a"]),                      # D3 takes the space; 'a' stands alone
+    ("\t.a", ["\t", ".a"]),
+    ("a\x00\x01b", ["a", "\x00", "\x01b"]),     # no rule takes \x00; \x01 leads a word
+    ("foo()\n\n  bar", ["foo", "()\n\n", " ", " bar"]),
+    ("a  1", ["a", "  ", "1"]),                # the segment ends at the digit
+    ("don't", ["don", "'t"]),
+]
+
+
+@pytest.mark.parametrize("text,pieces", EXAMPLES_DEEPSEEK)
+def test_worked_examples_deepseek(text, pieces):
+    assert split(text, DEEPSEEK) == pieces
+
+
 def _starts(pieces):
     out, pos = [], 0
     for p in pieces:
@@ -119,6 +144,29 @@ def test_exhaustive_short_strings_o200k():
     assert bad == []
 
 
+ALPHA_D = ["a", "A", "\u00e9", "\u0301", "1", "\u4e2d", "\u3042", "\u30fb", ".", "_", "\u20ac", " ", "\t", "\n",
+           "\x00"]
+ALPHA_D2 = ALPHA_D + list("sSzZ09$'(") + ["\u6587", "\u309b", "\u30fc", "\u30a2", "\u30a0", "\u00b2", "\u0663", "\r",
+                                        "\xa0", "\u200b", "\ue000", "\U0001f600", "\u01c5"]
+
+
+def test_exhaustive_short_strings_deepseek():
+    bad = []
+    for length in range(5):
+        for tup in itertools.product(ALPHA_D, repeat=length):
+            s = "".join(tup)
+            if _starts(split(s, DEEPSEEK)) != piece_starts(s, DEEPSEEK):
+                bad.append(s)
+    assert bad == []
+
+
+def test_random_strings_deepseek():
+    rng = random.Random(19)
+    for _ in range(30_000):
+        s = "".join(rng.choice(ALPHA_D2) for _ in range(rng.randint(6, 30)))
+        assert _starts(split(s, DEEPSEEK)) == piece_starts(s, DEEPSEEK), repr(s)
+
+
 def test_random_strings_o200k():
     rng = random.Random(17)
     for _ in range(30_000):
@@ -138,7 +186,7 @@ def test_long_runs_against_run_decomposition():
     texts = ["a" + "1" * 1000 + "x", ".\n" * 3 + "\n" * 500 + " " * 700 + "z", " " * 999 + "7",
              "\t" * 5 + "\n" + " " * 400, "x" + "٣" * 11 + "2" * 7]
     for t in texts:
-        for pat in (GPT2, CL100K, O200K):
+        for pat in (GPT2, CL100K, O200K, DEEPSEEK):
             assert _starts(split(t, pat)) == piece_starts(t, pat)
 
 
@@ -182,6 +230,21 @@ def test_o200k_pattern_under_oniguruma_matches_regex_module():
         assert _starts(split(s, O200K)) == hf, repr(s)
 
 
+def test_deepseek_splits_under_oniguruma_match_regex_module():
+    tk = pytest.importorskip("tokenizers")
+
+    def onig(p):
+        return re.sub(r"\\(?:x([0-9a-f]{2})|u([0-9a-f]{4}))", lambda m: "\\x{%s}" % (m.group(1) or m.group(2)), p)
+    seq = tk.pre_tokenizers.Sequence([tk.pre_tokenizers.Split(tk.Regex(onig(p)), behavior="isolated")
+                                      for p in _DEEPSEEK_STAGES])
+    rng = random.Random(8)
+    alpha = HF_ALPHA + ["\u3042", "\u30fb", "\u20ac", "$", "\x01"]
+    for _ in range(5000):
+        s = "".join(rng.choice(alpha) for _ in range(rng.randint(1, 40)))
+        hf = [a for _, (a, _) in seq.pre_tokenize_str(s)]
+        assert _starts(split(s, DEEPSEEK)) == hf, repr(s)
+
+
 def test_whitespace_set_is_unicode_white_space():
     s = regex.compile(r"\s")
     got = [cp for cp in range(0x110000) if not 0xD800 <= cp <= 0xDFFF and s.match(chr(cp))]
@@ -221,6 +284,7 @@ BATCH_STARTS = {
     GPT2: [0, 2, 3, 5, 7, 8, 9, 11, 14, 15],
     CL100K: [0, 2, 3, 5, 7, 8, 9, 11, 14, 15, 18],
     O200K: [0, 2, 3, 5, 7, 8, 9, 11, 14, 15, 18],  # as cl100k-style: no case or tail rule applies
+    DEEPSEEK: [0, 2, 3, 5, 7, 8, 9, 11, 14, 15, 18],  # "中" is its own run piece either way
 }
 
 
@@ -232,7 +296,7 @@ def _batch(texts):
     return data, offs
 
 
-@pytest.mark.parametrize("pattern_id", [GPT2, CL100K, O200K])
+@pytest.mark.parametrize("pattern_id", [GPT2, CL100K, O200K, DEEPSEEK])
 def test_piece_starts_batch_hand_worked(pattern_id):
     data, offs = _batch(BATCH_TEXTS)
     assert offs == [0, 3, 3, 5, 8, 11, 15, 19]
@@ -243,7 +307,7 @@ def test_piece_starts_batch_hand_worked(pattern_id):
     assert 3 not in [len(data.decode()[:i].encode()) for i in whole]
 
 
-@pytest.mark.parametrize("pattern_id", [GPT2, CL100K, O200K])
+@pytest.mark.parametrize("pattern_id", [GPT2, CL100K, O200K, DEEPSEEK])
 def test_piece_starts_batch_random_against_run_decomposition(pattern_id):
     """Random batches (empty texts, texts ending in whitespace, multibyte chars)
     against the regex-free run decomposition, applied text by text and shifted
