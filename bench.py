@@ -22,6 +22,8 @@ Workloads (seeded, synthetic; the headline is the 1,000,000-char single text):
   w100k one 100,000-letter random word (a long piece with many distinct merges)
   o2   the c3 text under the o200k-style rules (case-split words, attached
        contractions, CR/LF/'/' tails)
+  ds   the c3 text under the DeepSeek-style rules (digit groups and CJK runs cut
+       out first)
 Each is checked against the oracle's stored digests before it is timed.
 
 Roofline (per workload, for the kernel with the largest live event time):
@@ -48,7 +50,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "exact BPE encode throughput: chars/s and ms per 1M chars; % of HBM peak"
 HEADLINE = "c2"
-ALL_WORKLOADS = ["c1", "c2", "c3", "c4", "c5a", "c5b", "c5c", "c5d", "w100k", "o2"]
+ALL_WORKLOADS = ["c1", "c2", "c3", "c4", "c5a", "c5b", "c5c", "c5d", "w100k", "o2", "ds"]
 HBM_PEAK_GBS = 8000.0   # MI355X HBM3E, published
 CLOCK_GHZ = 2.4         # MI355X peak engine clock (one clock for every figure here)
 SIMDS = 256 * 4         # 256 CUs x 4 SIMDs
@@ -56,7 +58,7 @@ SIMDS = 256 * 4         # 256 CUs x 4 SIMDs
 VALU_PEAK_GINST = SIMDS * CLOCK_GHZ / 4  # 614.4 G wave-instructions/s
 COUNTERS = os.path.join(ROOT, "profiles", "counters.json")
 KERNEL_SRC = os.path.join(ROOT, "exact_byte_level_amd", "csrc", "tt_kernels.hip")
-PRETOK_KERNELS = ("k_tile_summary", "k_pretok<0>", "k_pretok<1>", "k_pretok<2>")
+PRETOK_KERNELS = ("k_tile_summary", "k_pretok<0>", "k_pretok<1>", "k_pretok<2>", "k_pretok<3>")
 
 
 def _sha(a):

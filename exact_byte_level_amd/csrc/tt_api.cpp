@@ -297,8 +297,7 @@ int tt_load_bpe(const int32_t* merges, const int32_t* ranks, int64_t n_merges, i
 int tt_load_bpe_ex(const int32_t* merges, const int32_t* ranks, int64_t n_merges, int32_t pattern_id,
                    uint32_t flags) {
   std::lock_guard<std::mutex> lock(g_mu);
-  if (pattern_id != TT_PATTERN_GPT2 && pattern_id != TT_PATTERN_CL100K && pattern_id != TT_PATTERN_O200K)
-    return TT_EINVAL;
+  if (pattern_id < TT_PATTERN_GPT2 || pattern_id > TT_PATTERN_DEEPSEEK) return TT_EINVAL;
   if (flags & ~(uint32_t)TT_LOAD_IGNORE_MERGES) return TT_EINVAL;
   const bool whole = (flags & TT_LOAD_IGNORE_MERGES) != 0;
   if (n_merges < 0 || n_merges > TT_MAX_MERGES) return TT_EINVAL;
@@ -700,7 +699,7 @@ int tt_session_reset(tt_session* s, const uint8_t* dev_bytes, int64_t n, hipStre
   std::lock_guard<std::mutex> lock(g_mu);
   if (!s || n < 0 || (n > 0 && !dev_bytes)) return TT_EINVAL;
   if (n > s->cap) return TT_ETOOBIG;
-  if (g.loaded && g.pattern == TT_PATTERN_O200K) return TT_EINVAL;  // no splice rule for these rules
+  if (g.loaded && g.pattern >= TT_PATTERN_O200K) return TT_EINVAL;  // no splice rule for these rules
   int rc = check_stream_state();
   if (rc != TT_OK) return rc;
   s->valid = false;
@@ -731,7 +730,7 @@ int tt_session_append(tt_session* s, const uint8_t* dev_delta, int64_t nd, int64
   if (rc != TT_OK) return rc;
   if (!s->valid) return TT_EINVAL;
   if (s->gen != g.generation) return TT_ESTALE;
-  if (g.pattern == TT_PATTERN_O200K) return TT_EINVAL;
+  if (g.pattern >= TT_PATTERN_O200K) return TT_EINVAL;
   if (nd > s->cap - s->n) return TT_ETOOBIG;
   int64_t info[4] = {0, 0, -1, s->T};
   if (nd == 0) {

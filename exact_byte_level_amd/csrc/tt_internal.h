@@ -33,7 +33,9 @@ constexpr uint32_t K_AP = 1u << 11;
 constexpr uint32_t K_BAD = 1u << 12;
 constexpr int K_LEN_SHIFT = 13;
 constexpr uint32_t K_SLASH = 1u << 15;  // '/'
-constexpr int K_FINE_SHIFT = 16;        // 32-bit codes: the Unicode class of a multibyte char (4 bits)
+constexpr int K_FINE_SHIFT = 16;        // 32-bit codes: the Unicode class of a multibyte char (4 bits),
+                                        // 7 for ASCII punctuation and symbols
+constexpr uint32_t K_CJK = 1u << 20;    // 32-bit codes: a CJK ideograph (U+4E00..U+9FA5) or kana (U+3040..U+30FF)
 enum : uint32_t { LT_S = 1, LT_T = 2, LT_R = 3, LT_E = 4, LT_V = 5, LT_M = 6, LT_L = 7, LT_D = 8 };
 
 // ------------------------------------------------------------------------- BPE

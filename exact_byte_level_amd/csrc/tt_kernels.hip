@@ -225,6 +225,8 @@ __device__ __forceinline__ void decode4_regs(uint64_t wb, uint32_t bm, int64_t p
     const bool last = p + (int64_t)clen >= n || ((bm >> (k + clen)) & 1u);
     const bool stray = !last && !bad_lead && (((uint32_t)(wb >> (8 * (k + clen))) & 0xC0u) == 0x80u);
     uint32_t c = ascii_b ? (uint32_t)ascii[b0 & 127u] : bad_lead ? (C_O | K_BAD) : 0u;
+    // printable ASCII that is not a letter, digit or space: punctuation or a symbol
+    if (ascii_b && b0 - 0x21u < 0x5Eu && cls_of(c) == C_O) c |= 7u << K_FINE_SHIFT;
     c |= ((clen - 1u) << K_LEN_SHIFT) | (start ? K_SEQ_START : 0u) | (last ? K_SEQ_LAST : 0u) | (stray ? K_BAD : 0u);
     code[k] = !in ? (uint32_t)C_OUT : cont ? (C_CONT | (start ? K_BAD : 0u)) : c;
     len_out[k] = in && !cont ? (int)clen : 0;
@@ -241,6 +243,7 @@ __device__ __forceinline__ void decode4_regs(uint64_t wb, uint32_t bm, int64_t p
       const uint32_t u = !tab[k] ? 0u : blk[k] < UNI_SINGLE ? blk[k]
                        : (g_uni_l2[blk[k] * 128u + ((cp[k] & 255u) >> 1)] >> ((cp[k] & 1u) * 4u)) & 15u;
       code[k] |= uni_cls(u) | (u << K_FINE_SHIFT);
+      if (cp[k] - 0x4E00u <= 0x9FA5u - 0x4E00u || cp[k] - 0x3040u <= 0x30FFu - 0x3040u) code[k] |= K_CJK;
     }
   }
 }
@@ -630,10 +633,39 @@ __device__ __forceinline__ uint32_t o2_sum_code(uint32_t code) {
   return (code & ~7u) | c;
 }
 
+// Class index of a char code under the DeepSeek-style rules (5 bits): bits
+// 0-3 1 digit, 2 other, 3 whitespace, 4 space, 5 CR/LF, 6 ASCII
+// punctuation or symbol, 7 other punctuation or symbol, 8 ASCII letter, 9
+// other letter or mark; bit 4 a CJK ideograph or kana; 0 no char.
+__device__ __forceinline__ uint32_t ds_index(uint32_t code) {
+  const uint32_t k = cls_of(code), fine = (code >> K_FINE_SHIFT) & 15u;
+  const bool mb = ((code >> K_LEN_SHIFT) & 3u) != 0u;  // a multibyte char
+  uint32_t c;
+  if (k == C_N) c = 1u;
+  else if (k == C_WS) c = (code & K_SP) ? 4u : 3u;
+  else if (k == C_WN) c = 5u;
+  else if (k == C_L || (mb && fine == 4u)) c = mb ? 9u : 8u;
+  else if (k == C_O && (fine == 7u || fine == 8u)) c = mb ? 7u : 6u;
+  else if (k == C_O) c = 2u;
+  else return 0u;
+  return c | ((code & K_CJK) ? 16u : 0u);
+}
+
+// The code with its class as the DeepSeek-style run summaries see it:
+// ASCII letters C_L2U, ASCII punctuation/symbols C_L2B, other
+// punctuation/symbols C_O, other letters, marks, "other" chars and every CJK
+// char C_L.
+__device__ __forceinline__ uint32_t ds_sum_code(uint32_t code) {
+  const uint32_t idx = ds_index(code), c4 = idx & 15u;
+  if (!idx || c4 == 1u || c4 == 3u || c4 == 4u || c4 == 5u) return code;  // digits, whitespace
+  const uint32_t c = (idx & 16u) ? C_L : c4 == 8u ? C_L2U : c4 == 6u ? C_L2B : c4 == 7u ? C_O : C_L;
+  return (code & ~7u) | c;
+}
+
 template <int PAT>
 __device__ __forceinline__ uint32_t code_byte(uint32_t code) {
-  return (PAT == 2 ? o2_index(code) : cl_index(code)) | ((code & K_SEQ_START) ? CB_SS : 0u) |
-         ((code & K_SEQ_LAST) ? CB_SL : 0u) | ((code & K_BAD) ? CB_BAD : 0u);
+  return (PAT == 3 ? ds_index(code) : PAT == 2 ? o2_index(code) : cl_index(code)) |
+         ((code & K_SEQ_START) ? CB_SS : 0u) | ((code & K_SEQ_LAST) ? CB_SL : 0u) | ((code & K_BAD) ? CB_BAD : 0u);
 }
 
 // First index s in [0, cnt) with a[s] >= v (cnt if none), by one wavefront:
@@ -710,6 +742,7 @@ __global__ __launch_bounds__(PT_THREADS) void k_tile_summary(const uint8_t* __re
     // o200k-style summaries see marks as letters and letters by case (class
     // values 6 and 7 included)
     if (PAT == 2) code[k] = o2_sum_code(code[k]);
+    if (PAT == 3) code[k] = ds_sum_code(code[k]);
     if (ch[k]) {
       fv = FwdOp::combine(fv, FwdOp::elem(code[k]));
       if (PAT == 2) tv = TailOp::combine(tv, TailOp::elem(code[k]));
@@ -1044,9 +1077,10 @@ __device__ __forceinline__ uint32_t bs_range(int x0, int lo, int hi) {
 // lane's word: NPH digits at offset 0 mod 3 in their digit run, ENDS
 // whitespace chars whose whitespace run is not followed by a CR/LF, ABSO
 // CR/LF chars of a CR/LF run that follows an "other" char.
+// o_cls: the summary classes that count as "other" for the CR/LF carry.
 __device__ __forceinline__ void run_facts(uint32_t N, uint32_t WS, uint32_t WN, uint32_t O, uint32_t SS, uint32_t SL,
                                           int lane, int c_lo, int e, uint32_t lf, uint32_t rb, uint32_t* nph,
-                                          uint32_t* ends, uint32_t* abso) {
+                                          uint32_t* ends, uint32_t* abso, uint32_t o_cls = 1u << C_O) {
   const int x0 = c_lo - 32 + 32 * lane;
   // digits at offset 0 mod 3 in their run: fill each run with its start's
   // residue (mod 3) of the char index
@@ -1081,7 +1115,7 @@ __device__ __forceinline__ void run_facts(uint32_t N, uint32_t WS, uint32_t WN, 
   // CR/LF runs right after an "other" char
   const uint32_t RN = WN & ~SS;
   uint32_t SN = RN & ~bs_up<1>(WN) & bs_up<1>(O);
-  if ((lf & 1u) && ((lf >> 2) & 7u) == C_WN && ((lf >> 5) & 7u) == C_O) SN |= RN & X0;
+  if ((lf & 1u) && ((lf >> 2) & 7u) == C_WN && ((o_cls >> ((lf >> 5) & 7u)) & 1u)) SN |= RN & X0;
   *abso = bs_fill_up(RN, SN, lane);
 }
 
@@ -1244,6 +1278,65 @@ __device__ uint32_t o2_word_bits(const uint32_t* pl, int lane, int c_lo, int e, 
   return CH & (SS | BN | BL_IN | BL_ST | BO | BWN | BWS) & own;
 }
 
+// DeepSeek-style start bits of this lane's word (one wavefront; the planes
+// are the five class-index bits, sequence start, sequence last).  Digit
+// groups and CJK/kana runs cut segments first: SEG marks a segment's first
+// char, SEGL its last; inside, the rules see segment ends as text ends.
+// lf, rb: the forward / backward run states (DeepSeek-style classes) before
+// c_lo and from e on.  *unsup (the same in every lane): an ASCII-letter run
+// that covers the whole left context after an ASCII punctuation char is
+// followed by another letter or mark among the own chars, and whether the
+// punctuation char took the run lies before the span.
+__device__ uint32_t ds_word_bits(const uint32_t* pl, int lane, int c_lo, int e, uint32_t lf, uint32_t rb,
+                                 bool* unsup) {
+  const uint32_t b0 = pl[0], b1 = pl[1], b2 = pl[2], b3 = pl[3], CJK = pl[4], SS = pl[5], SL = pl[6];
+  const int x0 = c_lo - 32 + 32 * lane;
+  const uint32_t CH = b0 | b1 | b2 | b3;
+  auto eq = [&](uint32_t v) {
+    return ((v & 1u) ? b0 : ~b0) & ((v & 2u) ? b1 : ~b1) & ((v & 4u) ? b2 : ~b2) & ((v & 8u) ? b3 : ~b3);
+  };
+  const uint32_t N = eq(1u), O = eq(2u), WSn = eq(3u), SP = eq(4u), WN = eq(5u), AP1 = eq(6u), PSn = eq(7u);
+  const uint32_t AL = eq(8u), LMn = eq(9u);
+  const uint32_t WS = WSn | SP, W = WS | WN, PS = AP1 | PSn, LM = AL | LMn;
+  // digit groups first: NPH from the shared run facts needs sequence starts
+  // only; then segment starts and ends
+  uint32_t NPH, ENDS0, ABSO0;
+  run_facts(N, WS, WN, PS, SS, SL, lane, c_lo, e, lf, rb, &NPH, &ENDS0, &ABSO0);
+  const uint32_t Np = bs_up<1>(N);
+  const uint32_t SEG = CH & (SS | (N & (~Np | NPH)) | (~N & Np) | (CJK ^ bs_up<1>(CJK)));
+  const uint32_t SEGL = CH & (SL | bs_dn<1>(SEG));
+  // whitespace facts again, inside segments
+  uint32_t NPH2, ENDS, ABSO;
+  run_facts(N, WS, WN, PS, SEG, SEGL, lane, c_lo, e, lf, rb, &NPH2, &ENDS, &ABSO, (1u << C_O) | (1u << C_L2B));
+  // D1: an ASCII punctuation char that starts a piece and has ASCII letters
+  // after it takes them
+  const uint32_t D1S = AP1 & bs_dn<1>(AL) & ~bs_dn<1>(SEG) & (SEG | ~(bs_up<1>(PS) | bs_up<1>(SP)));
+  const uint32_t RA = AL & ~SEG;
+  const uint32_t D1L = bs_fill_up(RA, RA & bs_up<1>(D1S), lane);
+  const uint32_t BLM = LM & ((bs_up<1>(LM) & bs_up<1>(D1L) & ~AL) | (bs_up<1>(PS) & ~(bs_up<1>(D1S) & AL)) |
+                             bs_up<1>(WN));
+  const uint32_t BPS = PS & ~bs_up<1>(PS) & ~bs_up<1>(SP);
+  const uint32_t BWN = WN & ~bs_up<1>(W) & ~bs_up<1>(PS);
+  const uint32_t BWS = WS & (~bs_up<1>(W) | (bs_up<1>(WN) & (ENDS | bs_up<1>(ABSO))) |
+                             (bs_up<1>(WS) & ~SEGL & ~bs_dn<1>(W)));
+  const uint32_t BO = O & (~bs_up<1>(O) | (bs_dn<1>(LM) & ~SEGL));
+  // undecided: the ASCII-letter run through c_lo - 1 began before the span
+  // right after an ASCII punctuation char, and an own letter or mark that
+  // is not an ASCII letter follows it
+  bool amb = false;
+  if ((lf & 1u) && ((lf >> 2) & 7u) == C_L2U && ((lf >> 5) & 7u) == C_L2B) {
+    const uint32_t nota = CH & ~AL;
+    const uint64_t m = __ballot(nota != 0u);
+    const int l1 = m ? __ffsll((unsigned long long)m) - 1 : 64;
+    const uint32_t w1 = (uint32_t)__builtin_amdgcn_readlane((int)nota, l1 < 64 ? l1 : 0);
+    const uint32_t m1 = (uint32_t)__builtin_amdgcn_readlane((int)LMn, l1 < 64 ? l1 : 0);
+    const int first = l1 < 64 ? c_lo - 32 + 32 * l1 + (__ffs((int)w1) - 1) : (1 << 20);
+    amb = first >= c_lo && first < e && ((m1 >> (first - (c_lo - 32 + 32 * l1))) & 1u);
+  }
+  *unsup = amb;
+  return CH & (SEG | BLM | BPS | BWN | BWS | BO) & bs_range(x0, c_lo, e);
+}
+
 // The tile's cl100k-style start bits: this thread's 4 (its positions
 // HALO + 4 tid ...) and, in *cnt, the tile's count (the same in every
 // thread).  The code bytes are staged and the tile's carries (sm.carry_fwd /
@@ -1251,7 +1344,7 @@ __device__ uint32_t o2_word_bits(const uint32_t* pl, int lane, int c_lo, int e, 
 // char, so char x is span position x; else the chars are compacted first.
 template <int PAT, bool DIRECT>
 __device__ uint32_t pat_bits(TileSmem& sm, uint32_t* cnt, bool* unsup) {
-  constexpr int NPL = PAT == 2 ? 7 : 6;  // class-index bits, sequence start, sequence last
+  constexpr int NPL = PAT >= 2 ? 7 : 6;  // class-index bits, sequence start, sequence last
   constexpr int NIDX = NPL - 2;
   const int tid = (int)threadIdx.x, lane = tid & 63, wid = (int)uniform((uint32_t)tid >> 6);
   int c_lo = HALO, n_own = TILE, nc = SPAN;
@@ -1316,7 +1409,9 @@ __device__ uint32_t pat_bits(TileSmem& sm, uint32_t* cnt, bool* unsup) {
     for (int k = 0; k < NPL; ++k)
       pl[k] = lane < BS_WORDS ? reinterpret_cast<const uint32_t*>(sm.bsw[k])[lane] : 0u;
     bool uns = false;
-    const uint32_t B = PAT == 2 ? o2_word_bits(pl, lane, c_lo, c_lo + n_own, uniform(sm.carry_fwd),
+    const uint32_t B = PAT == 3 ? ds_word_bits(pl, lane, c_lo, c_lo + n_own, uniform(sm.carry_fwd),
+                                               uniform(sm.carry_bwd), &uns)
+                     : PAT == 2 ? o2_word_bits(pl, lane, c_lo, c_lo + n_own, uniform(sm.carry_fwd),
                                                uniform(sm.carry_bwd), uniform(sm.carry_tail), &uns)
                                 : cl_word_bits(pl, lane, c_lo, c_lo + n_own, uniform(sm.carry_fwd),
                                                uniform(sm.carry_bwd));
@@ -3106,6 +3201,11 @@ hipError_t launch_pretokenize(const uint8_t* bytes, int64_t n, const int64_t* of
     prof_mark("k_tile_summary", st);
     hipLaunchKernelGGL(k_pretok<2>, dim3(ntiles), dim3(PT_THREADS), 0, st, bytes, n, offs, nseq, ntiles, w);
     prof_mark("k_pretok<2>", st);
+  } else if (pattern == 3) {
+    hipLaunchKernelGGL(k_tile_summary<3>, dim3(ntiles), dim3(PT_THREADS), 0, st, bytes, n, offs, nseq, w);
+    prof_mark("k_tile_summary", st);
+    hipLaunchKernelGGL(k_pretok<3>, dim3(ntiles), dim3(PT_THREADS), 0, st, bytes, n, offs, nseq, ntiles, w);
+    prof_mark("k_pretok<3>", st);
   } else {
     hipLaunchKernelGGL(k_pretok<0>, dim3(ntiles), dim3(PT_THREADS), 0, st, bytes, n, offs, nseq, ntiles, w);
     prof_mark("k_pretok<0>", st);

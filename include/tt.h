@@ -40,10 +40,12 @@ extern "C" {
 #define TT_EOFFSETS   -7  /* batch offsets not monotone / not ending at n (device-side) */
 #define TT_ETOOBIG    -8  /* size beyond the library's limits or the tt_reserve size */
 #define TT_ESTALE     -9  /* tokenizer replaced since the session was reset (sessions below) */
-#define TT_EUNSUPPORTED -10 /* o200k-style rules: the input holds a case the GPU rules do not
-                              decide (device-side): back-to-back contraction suffixes, or an
-                              upper-case letter after a run of Lm/Lo/marks that crosses a tile
-                              start right after a letter that can end a contraction */
+#define TT_EUNSUPPORTED -10 /* o200k/DeepSeek-style rules: the input holds a case the GPU rules
+                              do not decide (device-side).  o200k: back-to-back contraction
+                              suffixes, or an upper-case letter after a run of Lm/Lo/marks that
+                              crosses a tile start right after a letter that can end a
+                              contraction.  DeepSeek: a letter or mark after a run of ASCII
+                              letters that crosses a tile start right after ASCII punctuation */
 
 #define TT_PATTERN_GPT2   0  /* GPT-2-style rules: lower-case contractions, ' ?letters', ' ?digits',
                                 ' ?other', whitespace with the not-followed-by-non-space rule */
@@ -57,6 +59,13 @@ extern "C" {
                                 1-3 digit groups, punctuation absorbing CR, LF and '/', whitespace
                                 up to the last CR/LF run, then the lookahead rule.  Sessions
                                 (incremental repair) are not offered under these rules. */
+#define TT_PATTERN_DEEPSEEK 3 /* DeepSeek-style rules: digit groups of 1-3 and runs of CJK ideographs
+                                and kana cut out first; then on each piece by itself: ASCII
+                                punctuation followed by ASCII letters, letters/marks with one
+                                optional non-CR/LF/letter/punctuation/symbol prefix, ' ?'
+                                punctuation/symbol runs absorbing CR/LF, whitespace up to the
+                                last CR/LF run, the lookahead rule; other chars stand alone.
+                                Sessions are not offered under these rules. */
 
 /* Maximum merges: ids must fit in 20 bits. */
 #define TT_MAX_MERGES (1048576 - 256)
@@ -76,7 +85,7 @@ extern "C" {
  *            0..n_merges-1; merge k makes token id 256 + ranks[k].  May be
  *            NULL, meaning ranks[k] = k.
  * n_merges   0 .. TT_MAX_MERGES.  0 means ids are the UTF-8 bytes.
- * pattern_id TT_PATTERN_GPT2, TT_PATTERN_CL100K or TT_PATTERN_O200K.
+ * pattern_id TT_PATTERN_GPT2, TT_PATTERN_CL100K, TT_PATTERN_O200K or TT_PATTERN_DEEPSEEK.
  *
  * The table must be consistent: both operands of the merge of rank r are ids
  * below 256 + r (every table learned by BPE training is), and no pair may

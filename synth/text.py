@@ -275,6 +275,7 @@ WORKLOADS = {
     "c5d": (1, "c3", "alternating letter/punctuation, cl100k-style rules"),
     "w100k": (0, "c2", "one 100,000-letter random word (12 letters), GPT-2-style rules, 50,000 merges"),
     "o2": (2, "c3", "1,000,000-char mix with 5% multibyte, o200k-style rules, 100,000 merges"),
+    "ds": (3, "c3", "1,000,000-char mix with 5% multibyte, DeepSeek-style rules, 100,000 merges"),
 }
 
 
@@ -294,7 +295,7 @@ def workload(name):
         return adversarial_text(name[2]), None, pat, voc
     if name == "w100k":
         return random_word(100_000, 5), None, pat, voc
-    if name == "o2":
+    if name in ("o2", "ds"):
         return mix_text(1_000_000, 103, multibyte=True), None, pat, voc
     raise ValueError(name)
 

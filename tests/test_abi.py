@@ -68,7 +68,7 @@ def test_load_rejects_bad_tables_without_device():
         r = None if ranks is None else np.ascontiguousarray(np.asarray(ranks, dtype=np.int32))
         return lib.tt_load_bpe(m.ctypes.data, None if r is None else r.ctypes.data, len(m), pattern)
 
-    assert load([(97, 98)], pattern=3) == tt.TT_EINVAL
+    assert load([(97, 98)], pattern=4) == tt.TT_EINVAL
     assert load([(97, 256)]) == tt.TT_ETABLE              # operand made later
     assert load([(97, 98), (97, 98)]) == tt.TT_ETABLE     # duplicate pair
     assert load([(97, 98), (98, 99)], ranks=[0, 0]) == tt.TT_ETABLE  # ranks not a permutation

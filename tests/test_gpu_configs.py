@@ -46,7 +46,7 @@ def _first_diff(got, data, offs, pat, voc):
     return "GPU %d tokens, oracle %d; first difference at %s" % (len(got), len(want), d[0] if len(d) else k)
 
 
-@pytest.mark.parametrize("name", ["c1", "c2", "c3", "c4", "c5a", "c5b", "c5c", "c5d", "w100k", "o2"])
+@pytest.mark.parametrize("name", ["c1", "c2", "c3", "c4", "c5a", "c5b", "c5c", "c5d", "w100k", "o2", "ds"])
 def test_workload_bit_exact(name):
     exp = EXPECTED[name]
     data, offs, pat, voc = workload(name)
@@ -70,7 +70,7 @@ def test_workload_bit_exact(name):
     assert np.array_equal(again, ids)
 
 
-@pytest.mark.parametrize("name", ["c1", "c2", "c3", "c4", "c5a", "c5b", "c5c", "c5d", "w100k", "o2"])
+@pytest.mark.parametrize("name", ["c1", "c2", "c3", "c4", "c5a", "c5b", "c5c", "c5d", "w100k", "o2", "ds"])
 def test_workload_offsets_bit_exact(name):
     """tt_encode_offsets: the same ids, and every token's byte offset equal to
     the oracle's running byte length (digest), at full size."""
