@@ -652,13 +652,14 @@ __device__ __forceinline__ uint32_t ds_index(uint32_t code) {
 }
 
 // The code with its class as the DeepSeek-style run summaries see it:
-// ASCII letters C_L2U, ASCII punctuation/symbols C_L2B, other
-// punctuation/symbols C_O, other letters, marks, "other" chars and every CJK
-// char C_L.
-__device__ __forceinline__ uint32_t ds_sum_code(uint32_t code) {
+// ASCII letters C_L2U; ASCII punctuation/symbols that can start a D1 piece
+// (d1: no punctuation, symbol or space of its segment before it) C_L2B; other
+// punctuation/symbols C_O; other letters, marks, "other" chars and every
+// CJK char C_L.
+__device__ __forceinline__ uint32_t ds_sum_code(uint32_t code, bool d1) {
   const uint32_t idx = ds_index(code), c4 = idx & 15u;
   if (!idx || c4 == 1u || c4 == 3u || c4 == 4u || c4 == 5u) return code;  // digits, whitespace
-  const uint32_t c = (idx & 16u) ? C_L : c4 == 8u ? C_L2U : c4 == 6u ? C_L2B : c4 == 7u ? C_O : C_L;
+  const uint32_t c = (idx & 16u) ? C_L : c4 == 8u ? C_L2U : c4 == 6u ? (d1 ? C_L2B : C_O) : c4 == 7u ? C_O : C_L;
   return (code & ~7u) | c;
 }
 
@@ -696,13 +697,14 @@ __global__ __launch_bounds__(PT_THREADS) void k_tile_summary(const uint8_t* __re
                                                              const int64_t* __restrict__ offs, int nseq,
                                                              Work w) {
   __shared__ uint16_t ascii[128];
-  __shared__ uint32_t sbm[TILE / 32 + 2];  // sequence starts in [t0, t0 + TILE + 64)
+  __shared__ uint32_t sbm[TILE / 32 + 3];  // sequence starts in [t0 - 32, t0 + TILE + 64)
   __shared__ uint32_t red[12];
+  __shared__ uint32_t cbl[(4 + TILE) / 4];  // DeepSeek-style: code bytes of [t0 - 4, t0 + TILE)
   const int tid = (int)threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int t = blockIdx.x;
   const int64_t t0 = (int64_t)t * TILE;
   if (tid < 64) reinterpret_cast<uint32_t*>(ascii)[tid] = reinterpret_cast<const uint32_t*>(g_ascii.v)[tid];
-  if (tid < TILE / 32 + 2) sbm[tid] = 0u;
+  if (tid < TILE / 32 + 3) sbm[tid] = 0u;
   // this thread's 4 bytes and the 4 after them
   const int64_t q = t0 + PT_CHUNK * tid;
   uint32_t d0 = 0u, d1 = 0u;
@@ -716,33 +718,63 @@ __global__ __launch_bounds__(PT_THREADS) void k_tile_summary(const uint8_t* __re
   __syncthreads();
   if (offs) {
     if (wid == 0) {
-      const int64_t lo = wave_lower_bound(offs, (int64_t)nseq + 1, t0, lane);
+      const int64_t lo = wave_lower_bound(offs, (int64_t)nseq + 1, t0 - 32, lane);
       const int64_t hi = wave_lower_bound(offs, (int64_t)nseq + 1, t0 + TILE + 64, lane);
       for (int64_t s = lo + lane; s < hi; s += 64) {
-        const int j = (int)(offs[s] - t0);
+        const int j = (int)(offs[s] - (t0 - 32));
         atomicOr(&sbm[j >> 5], 1u << (j & 31));
       }
     }
   } else if (t0 == 0 && tid == 0) {
-    sbm[0] = 1u;
+    sbm[1] = 1u;
   }
   __syncthreads();
   const int sh = (PT_CHUNK * tid) & 31;
-  const uint32_t sw0 = sbm[(PT_CHUNK * tid) >> 5], sw1 = sbm[((PT_CHUNK * tid) >> 5) + 1];
+  const uint32_t sw0 = sbm[1 + ((PT_CHUNK * tid) >> 5)], sw1 = sbm[2 + ((PT_CHUNK * tid) >> 5)];
   const uint32_t bm = sh ? (sw0 >> sh) | (sw1 << (32 - sh)) : sw0;  // bit i: a sequence starts at q + i
   uint32_t code[4];
   int len[4];
   decode4_regs((uint64_t)d0 | ((uint64_t)d1 << 32), bm, q, n, ascii, code, len);
   uint32_t out = 0u, fv = FwdOp::IDENT, bv = BwdOp::IDENT, tv = TailOp::IDENT;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) out |= code_byte<PAT>(code[k]) << (8 * k);
+  bool cap[4] = {false, false, false, false};
+  if (PAT == 3) {
+    // whether each ASCII punctuation char may start a D1 piece: look at the
+    // char before it (through the code bytes of the tile and of the 4 bytes
+    // before it)
+    cbl[1 + tid] = out;
+    if (tid == 0) {
+      uint32_t pc[4] = {0u, 0u, 0u, 0u};
+      int pl[4];
+      if (t0 >= 4) {
+        uint32_t pb = 0u;
+        for (int k = 0; k < 4; ++k) pb |= (uint32_t)bytes[t0 - 4 + k] << (8 * k);
+        decode4_regs((uint64_t)pb | ((uint64_t)d0 << 32), (sbm[0] >> 28) | (sbm[1] << 4), t0 - 4, n, ascii, pc, pl);
+      }
+      cbl[0] = code_byte<PAT>(pc[0]) | (code_byte<PAT>(pc[1]) << 8) | (code_byte<PAT>(pc[2]) << 16) |
+               (code_byte<PAT>(pc[3]) << 24);
+    }
+    __syncthreads();
+    const uint8_t* cb8 = reinterpret_cast<const uint8_t*>(cbl);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      if ((ds_index(code[k]) & 31u) != 6u) continue;
+      int j = 4 + PT_CHUNK * tid + k - 1;
+      for (int s = 0; s < 3 && j > 0 && (cb8[j] & CB_IDX) == 0u; ++s) --j;
+      const uint32_t pidx = cb8[j] & CB_IDX, pc4 = pidx & 15u;
+      cap[k] = (code[k] & K_SEQ_START) || pidx == 0u || (pidx & 16u) ||
+              !(pc4 == 4u || pc4 == 6u || pc4 == 7u);
+    }
+  }
   bool ch[4];
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
-    out |= code_byte<PAT>(code[k]) << (8 * k);
     ch[k] = is_char(code[k]);
     // o200k-style summaries see marks as letters and letters by case (class
     // values 6 and 7 included)
     if (PAT == 2) code[k] = o2_sum_code(code[k]);
-    if (PAT == 3) code[k] = ds_sum_code(code[k]);
+    if (PAT == 3) code[k] = ds_sum_code(code[k], cap[k]);
     if (ch[k]) {
       fv = FwdOp::combine(fv, FwdOp::elem(code[k]));
       if (PAT == 2) tv = TailOp::combine(tv, TailOp::elem(code[k]));
@@ -1283,12 +1315,8 @@ __device__ uint32_t o2_word_bits(const uint32_t* pl, int lane, int c_lo, int e, 
 // groups and CJK/kana runs cut segments first: SEG marks a segment's first
 // char, SEGL its last; inside, the rules see segment ends as text ends.
 // lf, rb: the forward / backward run states (DeepSeek-style classes) before
-// c_lo and from e on.  *unsup (the same in every lane): an ASCII-letter run
-// that covers the whole left context after an ASCII punctuation char is
-// followed by another letter or mark among the own chars, and whether the
-// punctuation char took the run lies before the span.
-__device__ uint32_t ds_word_bits(const uint32_t* pl, int lane, int c_lo, int e, uint32_t lf, uint32_t rb,
-                                 bool* unsup) {
+// c_lo and from e on.
+__device__ uint32_t ds_word_bits(const uint32_t* pl, int lane, int c_lo, int e, uint32_t lf, uint32_t rb) {
   const uint32_t b0 = pl[0], b1 = pl[1], b2 = pl[2], b3 = pl[3], CJK = pl[4], SS = pl[5], SL = pl[6];
   const int x0 = c_lo - 32 + 32 * lane;
   const uint32_t CH = b0 | b1 | b2 | b3;
@@ -1312,7 +1340,10 @@ __device__ uint32_t ds_word_bits(const uint32_t* pl, int lane, int c_lo, int e, 
   // after it takes them
   const uint32_t D1S = AP1 & bs_dn<1>(AL) & ~bs_dn<1>(SEG) & (SEG | ~(bs_up<1>(PS) | bs_up<1>(SP)));
   const uint32_t RA = AL & ~SEG;
-  const uint32_t D1L = bs_fill_up(RA, RA & bs_up<1>(D1S), lane);
+  uint32_t SA = RA & bs_up<1>(D1S);
+  // an ASCII-letter run that began before the span right after a D1 start
+  if ((lf & 1u) && ((lf >> 2) & 7u) == C_L2U && ((lf >> 5) & 7u) == C_L2B) SA |= RA & bs_range(x0, 0, 1);
+  const uint32_t D1L = bs_fill_up(RA, SA, lane);
   const uint32_t BLM = LM & ((bs_up<1>(LM) & bs_up<1>(D1L) & ~AL) | (bs_up<1>(PS) & ~(bs_up<1>(D1S) & AL)) |
                              bs_up<1>(WN));
   const uint32_t BPS = PS & ~bs_up<1>(PS) & ~bs_up<1>(SP);
@@ -1320,20 +1351,6 @@ __device__ uint32_t ds_word_bits(const uint32_t* pl, int lane, int c_lo, int e, 
   const uint32_t BWS = WS & (~bs_up<1>(W) | (bs_up<1>(WN) & (ENDS | bs_up<1>(ABSO))) |
                              (bs_up<1>(WS) & ~SEGL & ~bs_dn<1>(W)));
   const uint32_t BO = O & (~bs_up<1>(O) | (bs_dn<1>(LM) & ~SEGL));
-  // undecided: the ASCII-letter run through c_lo - 1 began before the span
-  // right after an ASCII punctuation char, and an own letter or mark that
-  // is not an ASCII letter follows it
-  bool amb = false;
-  if ((lf & 1u) && ((lf >> 2) & 7u) == C_L2U && ((lf >> 5) & 7u) == C_L2B) {
-    const uint32_t nota = CH & ~AL;
-    const uint64_t m = __ballot(nota != 0u);
-    const int l1 = m ? __ffsll((unsigned long long)m) - 1 : 64;
-    const uint32_t w1 = (uint32_t)__builtin_amdgcn_readlane((int)nota, l1 < 64 ? l1 : 0);
-    const uint32_t m1 = (uint32_t)__builtin_amdgcn_readlane((int)LMn, l1 < 64 ? l1 : 0);
-    const int first = l1 < 64 ? c_lo - 32 + 32 * l1 + (__ffs((int)w1) - 1) : (1 << 20);
-    amb = first >= c_lo && first < e && ((m1 >> (first - (c_lo - 32 + 32 * l1))) & 1u);
-  }
-  *unsup = amb;
   return CH & (SEG | BLM | BPS | BWN | BWS | BO) & bs_range(x0, c_lo, e);
 }
 
@@ -1410,7 +1427,7 @@ __device__ uint32_t pat_bits(TileSmem& sm, uint32_t* cnt, bool* unsup) {
       pl[k] = lane < BS_WORDS ? reinterpret_cast<const uint32_t*>(sm.bsw[k])[lane] : 0u;
     bool uns = false;
     const uint32_t B = PAT == 3 ? ds_word_bits(pl, lane, c_lo, c_lo + n_own, uniform(sm.carry_fwd),
-                                               uniform(sm.carry_bwd), &uns)
+                                               uniform(sm.carry_bwd))
                      : PAT == 2 ? o2_word_bits(pl, lane, c_lo, c_lo + n_own, uniform(sm.carry_fwd),
                                                uniform(sm.carry_bwd), uniform(sm.carry_tail), &uns)
                                 : cl_word_bits(pl, lane, c_lo, c_lo + n_own, uniform(sm.carry_fwd),

@@ -6,10 +6,7 @@ Brute force over every string of length <= 5 of a class-covering alphabet
 middle dot, ASCII and other punctuation/symbols, whitespace, a control char),
 random multibyte strings, runs that cross tiles (digit groups, whitespace
 before CR/LF, CR/LF after punctuation, CJK runs, ASCII-letter runs after
-punctuation), tile edges and a 1M-char encode.  One case stays undecided by
-the GPU rules and is reported as TT_EUNSUPPORTED: an ASCII-letter run that
-covers a whole tile's left context right after ASCII punctuation, followed by
-a non-ASCII letter or mark.
+punctuation), tile edges and a 1M-char encode.
 """
 import itertools
 import os
@@ -158,14 +155,14 @@ def test_encode_mix_1m():
     assert np.array_equal(got, np.asarray(oracle_encode(data, v, DEEPSEEK, {}), dtype=np.int32))
 
 
-def test_undecided_case_is_reported():
-    load()
-    text = "x" * 1000 + "." + "a" * 100 + "é"   # the letter run covers the left context of tile 1
-    with pytest.raises(tt.TTError) as ei:
-        tt.encode(dev(text.encode()))
-    assert ei.value.code == tt.TT_EUNSUPPORTED
-    # the same letters after a space are decided
+def test_letter_run_after_punctuation_across_a_tile_start():
+    # an ASCII-letter run after '_' / '.' that covers a whole tile's left
+    # context, then a non-ASCII letter: the punctuation char's piece is
+    # decided from the summary pass, before or after a space
     v = load()
-    text = "x" * 1000 + " " + "a" * 100 + "é"
-    got = tt.encode(dev(text.encode())).cpu().numpy()
-    assert np.array_equal(got, np.asarray(oracle_encode(text.encode(), v, DEEPSEEK, {}), dtype=np.int32))
+    for pre in ("x" * 1000 + ".", "x" * 1000 + " .", "x" * 999 + "._", "\u4e2d" * 300 + "_"):
+        for k in (20, 100, 1500):
+            text = pre + "a" * k + "\u00e9b"
+            got = tt.encode(dev(text.encode())).cpu().numpy()
+            want = np.asarray(oracle_encode(text.encode(), v, DEEPSEEK, {}), dtype=np.int32)
+            assert np.array_equal(got, want), (pre[-3:], k)
