@@ -10,18 +10,20 @@
 //         vocabulary short-circuit the page mentions) and queueing by length
 //         class in k_compact; group merges of up to 64-byte pieces, one byte
 //         position per lane, and exact global-minimum rounds for longer
-//         pieces, a wavefront each (k_bpe_merge) or, past 2 KiB, a workgroup
-//         each (big_merge, after every tile the piece covers has taken its
-//         share of the first round: big_share);
+//         pieces, a wavefront each (k_bpe_merge); past 2 KiB, 32-byte chunks
+//         encoded alone and stitched at compatible token pairs by every tile
+//         the piece covers (stitch_piece, in k_compact), with the exact
+//         rounds by one workgroup as the fallback (big_fallback);
 //   §4.3  no host synchronisation between kernels: every size a kernel needs
 //         after the first is read on the device (grids are sized for the
 //         worst case and exit early), so the chain is graph-capturable.
 //
-// Passes of one encode: k_tile_summary (cl100k-style rules only), k_pretok,
-// k_compact, k_bpe_merge, k_emit.
+// Passes of one encode: k_tile_summary (every rule set but GPT-2 style),
+// k_pretok, k_compact, k_bpe_merge, k_emit.
 //
 // Hot-path data (all integer; no floating point, no MFMA):
 //   bytes   uint8[n]         caller's UTF-8 text
+//   codes   uint8[n]         one code byte per text byte (class index, run flags)
 //   flags   uint16 per 4 B   pre-token start bits
 //   starts  int32[P + 1]     piece byte offsets + sentinel n
 //   tmp_ids int32[n]         tokens of the piece starting at byte s at [s, s+cnt)
@@ -186,7 +188,7 @@ __device__ bool stage_tile(const uint8_t* __restrict__ bytes, int64_t n, const i
 }
 
 
-// decode_at for four contiguous positions p0 .. p0 + 3 held in registers: wb
+// UTF-8 decode of four contiguous positions p0 .. p0 + 3 held in registers: wb
 // the bytes p0 .. p0 + 7 (0 past the text), bm bit i: a sequence starts at
 // p0 + i.  The same codes, computed without branches: byte kinds from the
 // count of leading one bits, the continuation bytes of a lead checked
@@ -248,7 +250,7 @@ __device__ __forceinline__ void decode4_regs(uint64_t wb, uint32_t bm, int64_t p
   }
 }
 
-// decode_at for the four contiguous span positions j .. j + 3 (j a multiple
+// decode4_regs for the four contiguous span positions j .. j + 3 (j a multiple
 // of 4) of a staged tile: writes the codes and the predecessor lengths;
 // returns whether a char starting at one of the tile's own positions is
 // invalid.
@@ -2469,8 +2471,8 @@ __device__ int32_t first_start_after(const Work& w, int t, int ntiles, int64_t n
 // class and round of 256 pieces reserves the slots).  The end of the tile's
 // last piece is the first start in a later tile, found from the tile counts
 // and start bits.  A piece longer than BIG_BYTES (only the tile's last one
-// and the one its first bytes end can be) gets the tile's share of its first
-// round, and the last tile to take a share merges it (big_share, big_merge).
+// and the one its first bytes end can be) is stitched here, each tile doing
+// the stretch of it that lies in the tile (stitch_piece).
 template <bool CLASSIFY, bool SB>
 __global__ __launch_bounds__(PT_THREADS) __attribute__((amdgpu_waves_per_eu(6))) void k_compact(const uint8_t* __restrict__ bytes, Work w, Tables tb,
                                                         int ntiles, int64_t n, int32_t* __restrict__ starts,

@@ -4,8 +4,8 @@ TokTier summary page, §3.2 and Appendix A.1: GPT-style tokenization first cuts
 the text into pre-tokens with an ordered regex (leftmost alternative that
 matches wins, greedy quantifiers with backtracking), then encodes each piece on
 its own.  The pages name the rule families but never print the patterns, so
-the two rule sets below are this project's renderings of the feature lists it
-was given:
+the four rule sets below are this project's renderings of the families' known
+features:
 
   pattern 0, GPT-2-style: contractions (lower case), letters, digits,
   punctuation, whitespace with the "not followed by a non-space" lookahead.
@@ -14,6 +14,13 @@ was given:
   with one optional leading non-letter/non-digit/non-newline char, digit groups
   of one to three, punctuation that swallows the CR/LF chars after it,
   whitespace up to the last CR/LF, then the lookahead rule.
+
+  pattern 2, o200k-style: words split by letter case, contractions attached
+  to the word, digit groups, "other" runs with CR/LF/'/' tails, whitespace
+  rules as cl100k-style.
+
+  pattern 3, DeepSeek-style: digit groups and CJK/kana runs cut out first, then
+  punctuation/letter/whitespace rules on every piece by itself.
 
 Character sets (pinned by tests against the ``regex`` module's own classes):
   L  = \\p{L}    N = \\p{N}    (Unicode tables of the ``regex`` module)
