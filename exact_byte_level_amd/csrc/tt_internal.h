@@ -53,8 +53,9 @@ __host__ __device__ inline uint64_t pair_key(uint32_t x, uint32_t y) {
 // 32-bit hash of (x, y): 24-bit products (exact for ids < 2^20), an
 // xor-shift and one 32-bit product.  Slot 1 = its top bits, slot 2 = the top
 // bits of its 16-bit rotation xor a constant (shift = 32 - log2(slots)).
+constexpr uint32_t PAIR_MUL_X = 0x9E3779u, PAIR_MUL_Y = 0x7FEB35u;
 __host__ __device__ inline uint32_t pair_mix(uint32_t x, uint32_t y) {
-  uint32_t h = (uint32_t)(x * 0x9E3779u) ^ (uint32_t)(y * 0x7FEB35u);
+  uint32_t h = (uint32_t)(x * PAIR_MUL_X) ^ (uint32_t)(y * PAIR_MUL_Y);
   h ^= h >> 13;
   return h * 0x85EBCA6Bu;
 }

@@ -1608,6 +1608,21 @@ __device__ __forceinline__ uint32_t pair_rank_new(const Tables& tb, uint32_t x, 
   return (e2 ^ k20) < (1ull << ID_BITS) ? (uint32_t)e2 & ID_MASK : r;
 }
 
+// pair_rank_new with the two 24-bit products already combined:
+// hp = (x * PAIR_MUL_X) ^ (y * PAIR_MUL_Y) (so that a product shared by
+// several lookups is formed once).
+__device__ __forceinline__ uint32_t pair_rank_mixed(const Tables& tb, uint32_t hp, uint32_t x, uint32_t y) {
+  uint32_t h = hp ^ (hp >> 13);
+  h *= 0x85EBCA6Bu;
+  const uint32_t s1 = h >> tb.pair_shift, s2 = pair_alt(h) >> tb.pair_shift;
+  const char* base = reinterpret_cast<const char*>(tb.pair_tab);
+  const uint64_t e1 = *reinterpret_cast<const uint64_t*>(base + (s1 << 3));
+  const uint64_t e2 = *reinterpret_cast<const uint64_t*>(base + (s2 << 3));
+  const uint64_t k20 = pair_key(x, y) << ID_BITS;
+  uint32_t r = (e1 ^ k20) < (1ull << ID_BITS) ? (uint32_t)e1 & ID_MASK : RANK_NONE;
+  return (e2 ^ k20) < (1ull << ID_BITS) ? (uint32_t)e2 & ID_MASK : r;
+}
+
 // Rank of merging the adjacent pair (x, y), or RANK_NONE: the byte-pair
 // table for two bytes, else the two-choice table (both loaded together).
 __device__ __forceinline__ uint32_t pair_rank(const Tables& tb, uint32_t x, uint32_t y) {
@@ -1681,8 +1696,12 @@ __device__ __forceinline__ uint32_t dpp(uint32_t x) {
 __device__ __forceinline__ uint32_t lane_up1(uint32_t x) {
   return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x130, 0xF, 0xF, true);
 }
+// Value of the previous lane (wave_shr:1); lane 0 reads 0.
+__device__ __forceinline__ uint32_t lane_dn1(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x138, 0xF, 0xF, true);
+}
 
-// Minimum over each aligned group of G lanes (G = 8, 16, 32, 64): butterflies
+// Minimum over each aligned group of G lanes (G = 2 ... 64): butterflies
 // inside a 16-lane row by DPP (folded into the min instructions), then across
 // rows by row broadcasts; G = 32 and 64 read the result from the last lane
 // of each half / of the wavefront.
@@ -1699,8 +1718,8 @@ __device__ __forceinline__ uint32_t dpp_rows(uint32_t x) {
 template <int G>
 __device__ __forceinline__ uint32_t group_min(uint32_t x) {
   x = min(x, dpp_all<0xB1>(x));
-  x = min(x, dpp_all<0x4E>(x));
-  x = min(x, dpp_all<0x141>(x));
+  if (G >= 4) x = min(x, dpp_all<0x4E>(x));
+  if (G >= 8) x = min(x, dpp_all<0x141>(x));
   if (G >= 16) x = min(x, dpp_all<0x140>(x));
   if (G == 32) {
     x = min(x, dpp_rows<0x142, 0xA>(x));  // rows 1, 3 += rows 0, 2
@@ -1781,6 +1800,139 @@ __device__ void group_bpe(const uint8_t* __restrict__ bytes, const Work& w, cons
   // token counts into the tiles the pieces start in: the group leaders' tiles
   // and counts are read into scalar registers and runs of equal tiles (the
   // pieces are consecutive queue entries) summed, one atomic per run
+  const uint32_t tl = (valid && g == 0) ? (uint32_t)s / TILE : 0xFFFFFFFFu;
+  const uint32_t val = (valid && g == 0) ? (uint32_t)m : 0u;
+  uint32_t cur_t = 0xFFFFFFFFu, cur_sum = 0;
+#pragma unroll
+  for (int q = 0; q < 64 / G; ++q) {
+    const uint32_t tq = (uint32_t)__builtin_amdgcn_readlane((int)tl, q * G);
+    const uint32_t vq = (uint32_t)__builtin_amdgcn_readlane((int)val, q * G);
+    if (tq != cur_t) {
+      if (cur_t != 0xFFFFFFFFu && lane == 0) atomicAdd(&w.tile_tok[cur_t], cur_sum);
+      cur_t = tq;
+      cur_sum = 0;
+    }
+    cur_sum += vq;
+  }
+  if (cur_t != 0xFFFFFFFFu && lane == 0) atomicAdd(&w.tile_tok[cur_t], cur_sum);
+}
+
+// The classic merge loop with four token slots per lane: 64 / G sequences at
+// once, one per aligned group of G lanes, token p of a sequence in slot p % 4
+// of lane p / 4 of its group (sequences of up to 4 G tokens).  id[k] and
+// rk[k] are the token in slot k and the rank of the pair it starts (RANK_NONE
+// where no pair starts: at the sequence's last token and after it); m is the
+// sequence's token count.  Each step: the group minimum of (rank << 6 |
+// position) -- the lowest rank, leftmost among equal pairs, the classic
+// choice -- then the tokens after the merged pair move one position left
+// (slot k takes slot k + 1, the last slot the next lane's first), the merged
+// pair's slot takes the new id, and the pairs on both sides of it get their
+// ranks from the pair table: the lane holding the token before the pair
+// probes (left, new) and the lane holding the pair probes (new, right), both
+// probes of a step in flight together.  Every lane of a wavefront issues the
+// step once for all four of its slots, which is what makes more than one
+// slot per lane pay: a step costs a wavefront about twice as many
+// instructions as with one slot per lane, for four times the positions.
+template <int G>
+__device__ __forceinline__ uint32_t group_rev(uint32_t x) {  // lane g reads lane G - 1 - g of its group
+  return G == 2 ? dpp_all<0xB1>(x) : G == 4 ? dpp_all<0x1B>(x) : G == 8 ? dpp_all<0x141>(x) : dpp_all<0x140>(x);
+}
+
+template <int G>
+__device__ __forceinline__ void group_merge4(const Tables& tb, uint32_t (&id)[4], uint32_t (&rk)[4], int& m) {
+  static_assert(G == 2 || G == 4 || G == 8 || G == 16, "groups within one DPP row");
+  const int g = (int)(threadIdx.x & 63u) & (G - 1);
+  const uint32_t pb = 4u * (uint32_t)g;
+  const bool first = g == 0, last = g == G - 1;
+  for (;;) {
+    const uint32_t k0 = (rk[0] << 6) | pb, k1 = (rk[1] << 6) | (pb + 1u);
+    const uint32_t k2 = (rk[2] << 6) | (pb + 2u), k3 = (rk[3] << 6) | (pb + 3u);
+    const uint32_t kmin = group_min<G>(min(min(k0, k1), min(k2, k3)));
+    const bool act = kmin < (1u << 26);
+    if (__ballot(act) == 0ull) break;
+    const int bk = (int)(kmin & 63u);
+    const uint32_t nid = 256u + (kmin >> 6);
+    // slot of the pair's left token if it is in this lane; a group with
+    // nothing left to merge keeps every slot (lb past the lane)
+    const int lb = act ? bk - (int)pb : 127;
+    const uint32_t n0 = lane_up1(id[0]), r0 = lane_up1(rk[0]);
+    const uint32_t rn = last ? RANK_NONE : r0;  // nothing enters from the next group
+    const uint32_t rv3 = group_rev<G>(id[3]), dn3 = lane_dn1(id[3]);
+    const uint32_t p3 = first ? rv3 : dn3;  // the cyclically previous lane's last token
+    // One probe per lane: the lane holding the token before the pair probes
+    // (that token, new); the lane holding the token three after the pair's
+    // left one (lane 0 of the group if that is past the group) probes (new,
+    // token after the pair).  No lane has both roles.
+    const bool do_l = lb >= 1 && lb <= 4;
+    const bool do_r = act && bk + 2 < m && ((lb >= -3 && lb <= 0) || (first && bk + 3 >= 4 * G));
+    // x = id[lb - 1] (lb in 1..4), y = id[lb + 2] (lb in -2..0) else p3: selects on
+    // the bits of the slot number
+    const uint32_t a = (uint32_t)(lb - 1), b = (uint32_t)(lb + 2);
+    const uint32_t xl = (a & 1u) ? id[1] : id[0], xh = (a & 1u) ? id[3] : id[2];
+    const uint32_t x = (a & 2u) ? xh : xl;
+    const uint32_t yl = (b & 1u) ? id[1] : id[0];
+    const uint32_t y = b < 2u ? yl : (b == 2u ? id[2] : p3);
+    const uint32_t px = do_l ? x : nid, py = do_l ? nid : y;
+    uint32_t res = RANK_NONE;
+    if (do_l || do_r) res = pair_rank_new(tb, px, py);
+    // the right probe's result belongs to the lane holding the pair: the
+    // prober itself (pair at slot 0) or the cyclically previous lane
+    const uint32_t rvr = group_rev<G>(res), upr = lane_up1(res);
+    const uint32_t rnx = last ? rvr : upr;
+    const uint32_t rl = res, rr = lb == 0 ? res : rnx;
+    const bool e0 = lb == 0, e1 = lb == 1, e2 = lb == 2, e3 = lb == 3, e4 = lb == 4;
+    const bool t0 = lb > 0, t1 = lb > 1, t2 = lb > 2, t3 = lb > 3, t4 = lb > 4;
+    const uint32_t i0 = e0 ? nid : t0 ? id[0] : id[1];
+    const uint32_t i1 = e1 ? nid : t1 ? id[1] : id[2];
+    const uint32_t i2 = e2 ? nid : t2 ? id[2] : id[3];
+    const uint32_t i3 = e3 ? nid : t3 ? id[3] : n0;
+    const uint32_t q0 = e0 ? rr : e1 ? rl : t1 ? rk[0] : rk[1];
+    const uint32_t q1 = e1 ? rr : e2 ? rl : t2 ? rk[1] : rk[2];
+    const uint32_t q2 = e2 ? rr : e3 ? rl : t3 ? rk[2] : rk[3];
+    const uint32_t q3 = e3 ? rr : e4 ? rl : t4 ? rk[3] : rn;
+    id[0] = i0; id[1] = i1; id[2] = i2; id[3] = i3;
+    rk[0] = q0; rk[1] = q1; rk[2] = q2; rk[3] = q3;
+    m -= act ? 1 : 0;
+  }
+}
+
+// Classic BPE of up to 64 / G queued pieces of at most 4 G bytes (queue
+// entries chunk * (64 / G) ...), one per aligned group of G lanes, four byte
+// positions per lane.  Tokens go to tmp_ids[s, s + cnt); the pieces' token
+// counts are added to the tiles they start in, one atomic per run of pieces
+// in one tile.
+template <int G>
+__device__ void group_bpe4(const uint8_t* __restrict__ bytes, const Work& w, const Tables& tb,
+                           const uint32_t* queue, int qn, int chunk) {
+  const int lane = (int)(threadIdx.x & 63u);
+  const int g = lane & (G - 1);
+  const int qi = chunk * (64 / G) + lane / G;
+  const bool valid = qi < qn;
+  uint32_t p = 0;
+  int32_t s = 0;
+  int m = 0;
+  if (valid) {
+    p = queue[qi];
+    s = w.piece_start[p];
+    m = w.piece_start[p + 1] - s;
+  }
+  const int pb = 4 * g;
+  uint32_t id[4], rk[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) id[k] = pb + k < m ? (uint32_t)bytes[s + pb + k] : 0u;
+  const uint32_t n0 = lane_up1(id[0]);
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const uint32_t nx = k < 3 ? id[k + 1] : n0;
+    rk[k] = pb + k + 1 < m ? tb.byte_pair[(id[k] << 8) | nx] : RANK_NONE;
+  }
+  group_merge4<G>(tb, id, rk, m);
+  if (valid) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      if (pb + k < m) w.tmp_ids[s + pb + k] = (int32_t)id[k];
+    if (g == 0) w.piece_cnt[p] = m;
+  }
   const uint32_t tl = (valid && g == 0) ? (uint32_t)s / TILE : 0xFFFFFFFFu;
   const uint32_t val = (valid && g == 0) ? (uint32_t)m : 0u;
   uint32_t cur_t = 0xFFFFFFFFu, cur_sum = 0;
@@ -2675,7 +2827,14 @@ __global__ __launch_bounds__(MERGE_THREADS) __attribute__((amdgpu_waves_per_eu(8
     big_fallback(bytes, w, tb, uniform((uint32_t)w.fall_list[f]), big);
   if (threadIdx.x < 64) {
     const int k = (int)threadIdx.x, c = 3 - k / QGROUPS, g = k % QGROUPS;
-    const uint32_t it = k < NQ ? (w.qctr[g * QCTR_STRIDE + c] + (8u >> c) - 1) >> (3 - c) : 0u;
+    // work items: a 33-64 byte piece alone (its merge chain is the kernel's
+    // critical path: one token slot per lane keeps its steps short); 32 / 16
+    // / 8 shorter pieces together, four token slots per lane
+    uint32_t it = 0u;
+    if (k < NQ) {
+      const uint32_t qk = w.qctr[g * QCTR_STRIDE + c];
+      it = c == 3 ? qk : (qk + (32u >> c) - 1) >> (5 - c);
+    }
     const uint32_t inc = wave_incl_fwd<SumOp>(it, k);
     if (k <= NQ) pre[k] = inc - it;
   }
@@ -2709,13 +2868,13 @@ __global__ __launch_bounds__(MERGE_THREADS) __attribute__((amdgpu_waves_per_eu(8
       group_bpe<64>(bytes, w, tb, q, (int)qn, (int)item);
     } else if (c == 2) {
       __builtin_amdgcn_s_setprio(2);
-      group_bpe<32>(bytes, w, tb, q, (int)qn, (int)item);
+      group_bpe4<8>(bytes, w, tb, q, (int)qn, (int)item);
     } else if (c == 1) {
       __builtin_amdgcn_s_setprio(1);
-      group_bpe<16>(bytes, w, tb, q, (int)qn, (int)item);
+      group_bpe4<4>(bytes, w, tb, q, (int)qn, (int)item);
     } else {
       __builtin_amdgcn_s_setprio(0);
-      group_bpe<8>(bytes, w, tb, q, (int)qn, (int)item);
+      group_bpe4<2>(bytes, w, tb, q, (int)qn, (int)item);
     }
   }
 }
