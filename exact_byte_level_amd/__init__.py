@@ -87,10 +87,25 @@ def _check(rc, where):
         raise TTError(rc, where)
 
 
-def _stream(stream):
+_RAW_STREAM = None
+
+
+def _stream(stream, dev=None):
+    """The HIP stream to enqueue on: the given torch stream, else the current
+    stream of device dev (the data's device).  The current stream is read as
+    a raw handle: building a torch Stream object for it costs a few
+    microseconds, which a single request would wait for on the GPU."""
+    global _RAW_STREAM
+    if stream is not None:
+        return ctypes.c_void_p(stream.cuda_stream)
     import torch
-    s = stream if stream is not None else torch.cuda.current_stream()
-    return ctypes.c_void_p(s.cuda_stream)
+    if _RAW_STREAM is None:
+        _RAW_STREAM = getattr(torch._C, "_cuda_getCurrentRawStream", False)
+    if dev is None:
+        dev = torch.cuda.current_device()
+    if _RAW_STREAM:
+        return ctypes.c_void_p(_RAW_STREAM(dev))
+    return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
 
 
 LOAD_IGNORE_MERGES = 1
@@ -116,7 +131,8 @@ def reserve(max_bytes, max_seqs=1):
 def encode_into(data, out_ids, out_n, stream=None):
     """Enqueue an encode of a uint8 CUDA tensor into caller buffers (no sync)."""
     n = data.numel()
-    rc = lib().tt_encode(data.data_ptr() if n else None, n, out_ids.data_ptr(), out_n.data_ptr(), _stream(stream))
+    rc = lib().tt_encode(data.data_ptr() if n else None, n, out_ids.data_ptr(), out_n.data_ptr(),
+                         _stream(stream, data.device.index))
     _check(rc, "tt_encode")
 
 
@@ -141,14 +157,14 @@ def encode_noalloc_into(data, out_ids, out_n, stream=None):
     (a fixed per-device scratch array; inputs up to NOALLOC_MAX_BYTES)."""
     n = data.numel()
     rc = lib().tt_encode_noalloc(data.data_ptr() if n else None, n, out_ids.data_ptr(), out_n.data_ptr(),
-                                 _stream(stream))
+                                 _stream(stream, data.device.index))
     _check(rc, "tt_encode_noalloc")
 
 
 def encode_batch_into(data, offsets, out_ids, out_offsets, stream=None):
     n = data.numel()
     rc = lib().tt_encode_batch(data.data_ptr() if n else None, n, offsets.data_ptr(), offsets.numel() - 1,
-                               out_ids.data_ptr(), out_offsets.data_ptr(), _stream(stream))
+                               out_ids.data_ptr(), out_offsets.data_ptr(), _stream(stream, data.device.index))
     _check(rc, "tt_encode_batch")
 
 
@@ -175,7 +191,7 @@ def pretokenize(data, offsets=None, stream=None):
     rc = lib().tt_pretokenize(data.data_ptr() if n else None, n,
                               None if offsets is None else offsets.data_ptr(),
                               1 if offsets is None else offsets.numel() - 1,
-                              starts.data_ptr(), out_np.data_ptr(), _stream(stream))
+                              starts.data_ptr(), out_np.data_ptr(), _stream(stream, data.device.index))
     _check(rc, "tt_pretokenize")
     p = int(out_np.item())
     if p < 0:
@@ -189,7 +205,8 @@ def encode_offsets_into(data, offsets, out_ids, out_starts, out_counts, stream=N
     rc = lib().tt_encode_offsets(data.data_ptr() if n else None, n,
                                  None if offsets is None else offsets.data_ptr(),
                                  1 if offsets is None else offsets.numel() - 1,
-                                 out_ids.data_ptr(), out_starts.data_ptr(), out_counts.data_ptr(), _stream(stream))
+                                 out_ids.data_ptr(), out_starts.data_ptr(), out_counts.data_ptr(),
+                                 _stream(stream, data.device.index))
     _check(rc, "tt_encode_offsets")
 
 
