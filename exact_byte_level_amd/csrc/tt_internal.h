@@ -207,8 +207,8 @@ constexpr int HUGE_TOKENS = 64;         // pieces with more tokens are copied by
 // ------------------------------------------------------------- no-alloc encode
 // tt_encode_noalloc carves its workspace out of one fixed device array of
 // NOALLOC_SCRATCH_BYTES (the layout of an input of TT_NOALLOC_MAX_BYTES bytes
-// needs about 23.5 bytes per input byte, 47 MiB at 2 MiB).
-constexpr size_t NOALLOC_SCRATCH_BYTES = (size_t)48 << 20;
+// needs about 24.5 bytes per input byte, 49 MiB at 2 MiB).
+constexpr size_t NOALLOC_SCRATCH_BYTES = (size_t)52 << 20;
 constexpr int NOALLOC_MAX_DEVICES = 64;
 
 // ------------------------------------------------------------- sessions

@@ -337,7 +337,8 @@ struct FwdOp {
     if (b & 2u) {
       uint32_t ca = (a >> 2) & 7u, cb = (b >> 2) & 7u;
       if (ca == cb) {
-        uint32_t len = (((a >> 8) & 3u) + ((b >> 8) & 3u)) % 3u;
+        uint32_t len = ((a >> 8) & 3u) + ((b >> 8) & 3u);  // each < 3: the sum mod 3 by one subtraction
+        len -= len >= 3u ? 3u : 0u;
         return (a & (0xFFu | CB_CL)) | (len << 8) | (b & LAST_CL);
       }
       return 1u | (cb << 2) | (ca << 5) | (b & 0x300u) | ((a & LAST_CL) ? CB_CL : 0u) | (b & LAST_CL);
@@ -611,17 +612,19 @@ constexpr uint32_t CB_IDX = 31u, CB_SS = 1u << 5, CB_SL = 1u << 6, CB_BAD = 1u <
 __device__ __forceinline__ uint32_t o2_index(uint32_t code) {
   constexpr uint64_t TTAB = 0ull | 1ull << 4 | 1ull << 8 | 2ull << 12 | 4ull << 16 | 2ull << 20 | 1ull << 24 |
                             3ull << 28 | 1ull << 32;  // by letter type 0..8
+  // selects from the weakest case to the strongest (flat: no branches)
   const uint32_t k = cls_of(code), fine = (code >> K_FINE_SHIFT) & 15u;
   const bool mb = ((code >> K_LEN_SHIFT) & 3u) != 0u;  // a multibyte char
-  if (k == C_L || (mb && k == C_O && fine == 4u)) {
-    if (mb) return fine == 1u ? 16u : fine == 2u ? 24u : 23u;
-    const uint32_t lt = (code >> K_LETTER_SHIFT) & 15u;
-    return 16u | ((code & K_UPPER) ? 0u : 8u) | ((uint32_t)(TTAB >> (4 * lt)) & 15u);
-  }
-  if (k == C_N) return 1u;
-  if (k == C_O) return (code & K_AP) ? 3u : (code & K_SLASH) ? 4u : 2u;
-  if (k == C_WS) return (code & K_SP) ? 6u : 5u;
-  return k == C_WN ? 7u : 0u;
+  const uint32_t lt = (code >> K_LETTER_SHIFT) & 15u;
+  const uint32_t ascii_l = 16u | ((code & K_UPPER) ? 0u : 8u) | ((uint32_t)(TTAB >> (4 * lt)) & 15u);
+  const uint32_t mb_l = fine == 1u ? 16u : fine == 2u ? 24u : 23u;
+  uint32_t c = 0u;
+  c = k == C_WN ? 7u : c;
+  c = k == C_WS ? ((code & K_SP) ? 6u : 5u) : c;
+  c = k == C_O ? ((code & K_AP) ? 3u : (code & K_SLASH) ? 4u : 2u) : c;
+  c = k == C_N ? 1u : c;
+  c = (k == C_L) | (mb & (k == C_O) & (fine == 4u)) ? (mb ? mb_l : ascii_l) : c;
+  return c;
 }
 
 // The code with its class as the o200k-style run summaries see it: marks
@@ -640,17 +643,17 @@ __device__ __forceinline__ uint32_t o2_sum_code(uint32_t code) {
 // punctuation or symbol, 7 other punctuation or symbol, 8 ASCII letter, 9
 // other letter or mark; bit 4 a CJK ideograph or kana; 0 no char.
 __device__ __forceinline__ uint32_t ds_index(uint32_t code) {
+  // selects from the weakest case to the strongest (flat: no branches)
   const uint32_t k = cls_of(code), fine = (code >> K_FINE_SHIFT) & 15u;
   const bool mb = ((code >> K_LEN_SHIFT) & 3u) != 0u;  // a multibyte char
-  uint32_t c;
-  if (k == C_N) c = 1u;
-  else if (k == C_WS) c = (code & K_SP) ? 4u : 3u;
-  else if (k == C_WN) c = 5u;
-  else if (k == C_L || (mb && fine == 4u)) c = mb ? 9u : 8u;
-  else if (k == C_O && (fine == 7u || fine == 8u)) c = mb ? 7u : 6u;
-  else if (k == C_O) c = 2u;
-  else return 0u;
-  return c | ((code & K_CJK) ? 16u : 0u);
+  uint32_t c = 0u;
+  c = k == C_O ? 2u : c;
+  c = (k == C_O) & ((fine == 7u) | (fine == 8u)) ? (mb ? 7u : 6u) : c;
+  c = (k == C_L) | (mb & (fine == 4u)) ? (mb ? 9u : 8u) : c;
+  c = k == C_WN ? 5u : c;
+  c = k == C_WS ? ((code & K_SP) ? 4u : 3u) : c;
+  c = k == C_N ? 1u : c;
+  return c ? c | ((code & K_CJK) ? 16u : 0u) : 0u;
 }
 
 // The code with its class as the DeepSeek-style run summaries see it:
@@ -660,9 +663,13 @@ __device__ __forceinline__ uint32_t ds_index(uint32_t code) {
 // CJK char C_L.
 __device__ __forceinline__ uint32_t ds_sum_code(uint32_t code, bool d1) {
   const uint32_t idx = ds_index(code), c4 = idx & 15u;
-  if (!idx || c4 == 1u || c4 == 3u || c4 == 4u || c4 == 5u) return code;  // digits, whitespace
-  const uint32_t c = (idx & 16u) ? C_L : c4 == 8u ? C_L2U : c4 == 6u ? (d1 ? C_L2B : C_O) : c4 == 7u ? C_O : C_L;
-  return (code & ~7u) | c;
+  const bool keep = (idx == 0u) | (c4 == 1u) | (c4 - 3u <= 2u);  // no char, digits, whitespace
+  uint32_t c = C_L;
+  c = c4 == 7u ? C_O : c;
+  c = c4 == 6u ? (d1 ? C_L2B : C_O) : c;
+  c = c4 == 8u ? C_L2U : c;
+  c = (idx & 16u) ? C_L : c;
+  return keep ? code : (code & ~7u) | c;
 }
 
 template <int PAT>
@@ -707,6 +714,15 @@ __global__ __launch_bounds__(PT_THREADS) void k_tile_summary(const uint8_t* __re
   const int64_t t0 = (int64_t)t * TILE;
   if (tid < 64) reinterpret_cast<uint32_t*>(ascii)[tid] = reinterpret_cast<const uint32_t*>(g_ascii.v)[tid];
   if (tid < TILE / 32 + 3) sbm[tid] = 0u;
+  // DeepSeek-style: thread 0 also loads the 4 bytes before the tile (the
+  // chars its punctuation test looks back at), in flight with the tile
+  uint32_t pre4 = 0u;
+  if (PAT == 3 && tid == 0 && t0 >= 4) {
+    if ((reinterpret_cast<uintptr_t>(bytes) & 3u) == 0)
+      pre4 = *reinterpret_cast<const uint32_t*>(bytes + t0 - 4);
+    else
+      for (int k = 0; k < 4; ++k) pre4 |= (uint32_t)bytes[t0 - 4 + k] << (8 * k);
+  }
   // this thread's 4 bytes and the 4 after them
   const int64_t q = t0 + PT_CHUNK * tid;
   uint32_t d0 = 0u, d1 = 0u;
@@ -743,30 +759,31 @@ __global__ __launch_bounds__(PT_THREADS) void k_tile_summary(const uint8_t* __re
   bool cap[4] = {false, false, false, false};
   if (PAT == 3) {
     // whether each ASCII punctuation char may start a D1 piece: look at the
-    // char before it (through the code bytes of the tile and of the 4 bytes
-    // before it)
-    cbl[1 + tid] = out;
-    if (tid == 0) {
-      uint32_t pc[4] = {0u, 0u, 0u, 0u};
+    // char before it.  Thread 0 also decodes the 4 bytes before the tile;
+    // each thread then reads the previous thread's 4 code bytes and finds,
+    // in the 8-byte window, the nearest char start among the 3 bytes before
+    // each of its own (else the 4th byte back: a char is at most 4 bytes).
+    uint32_t pcw = 0u;
+    if (tid == 0 && t0 >= 4) {
+      uint32_t pc[4];
       int pl[4];
-      if (t0 >= 4) {
-        uint32_t pb = 0u;
-        for (int k = 0; k < 4; ++k) pb |= (uint32_t)bytes[t0 - 4 + k] << (8 * k);
-        decode4_regs((uint64_t)pb | ((uint64_t)d0 << 32), (sbm[0] >> 28) | (sbm[1] << 4), t0 - 4, n, ascii, pc, pl);
-      }
-      cbl[0] = code_byte<PAT>(pc[0]) | (code_byte<PAT>(pc[1]) << 8) | (code_byte<PAT>(pc[2]) << 16) |
-               (code_byte<PAT>(pc[3]) << 24);
+      decode4_regs((uint64_t)pre4 | ((uint64_t)d0 << 32), (sbm[0] >> 28) | (sbm[1] << 4), t0 - 4, n, ascii, pc, pl);
+      pcw = code_byte<PAT>(pc[0]) | (code_byte<PAT>(pc[1]) << 8) | (code_byte<PAT>(pc[2]) << 16) |
+            (code_byte<PAT>(pc[3]) << 24);
     }
+    cbl[1 + tid] = out;
+    if (tid == 0) cbl[0] = pcw;
     __syncthreads();
-    const uint8_t* cb8 = reinterpret_cast<const uint8_t*>(cbl);
+    const uint64_t win = (uint64_t)cbl[tid] | ((uint64_t)out << 32);
+    // bit 8 i + 7: window byte i starts a char (class index bits nonzero)
+    const uint64_t starts = ((win & 0x1F1F1F1F1F1F1F1Full) + 0x7F7F7F7F7F7F7F7Full) & 0x8080808080808080ull;
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-      if ((ds_index(code[k]) & 31u) != 6u) continue;
-      int j = 4 + PT_CHUNK * tid + k - 1;
-      for (int s = 0; s < 3 && j > 0 && (cb8[j] & CB_IDX) == 0u; ++s) --j;
-      const uint32_t pidx = cb8[j] & CB_IDX, pc4 = pidx & 15u;
-      cap[k] = (code[k] & K_SEQ_START) || pidx == 0u || (pidx & 16u) ||
-              !(pc4 == 4u || pc4 == 6u || pc4 == 7u);
+      const uint64_t m = starts & (0xFFFFFFull << (8 * (k + 1)));  // window bytes k + 1 .. k + 3
+      const int pos = m ? (63 - __clzll((long long)m)) >> 3 : k;
+      const uint32_t pidx = (uint32_t)(win >> (8 * pos)) & CB_IDX, pc4 = pidx & 15u;
+      cap[k] = (ds_index(code[k]) & 31u) == 6u &&
+               ((code[k] & K_SEQ_START) || pidx == 0u || (pidx & 16u) || !(pc4 == 4u || pc4 == 6u || pc4 == 7u));
     }
   }
   bool ch[4];

@@ -173,7 +173,7 @@ int tt_encode(const uint8_t* dev_bytes, int64_t n, int32_t* out_ids, int64_t* ou
  * Arguments, output and enqueue-only contract as tt_encode, with n at most
  * TT_NOALLOC_MAX_BYTES (2 MiB; larger gives TT_ETOOBIG before any device
  * work).  The call allocates nothing, ever: instead of the library's
- * workspace it uses a fixed 48 MiB device array that every GPU the library
+ * workspace it uses a fixed 52 MiB device array that every GPU the library
  * is loaded on holds until the process ends, looked up once per device.
  * Every call on one GPU shares that array, which keeps the last call's
  * contents (the kernels reset what they need), so two calls that overlap in

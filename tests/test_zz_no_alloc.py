@@ -5,7 +5,7 @@ instead of the library's workspace.  Two calls in a row on each rule set, the
 second with a smaller input (so it reuses the array with the first call's
 contents still in it), must give exactly tt_encode's ids; the smaller one is
 also checked against the oracle.  The texts hold pieces longer than 2 KiB, so
-the long-piece hand-over counters kept in the array are exercised too.
+the long-piece stitching slots kept in the array are exercised too.
 """
 import os
 import random
@@ -67,6 +67,24 @@ def test_noalloc_equals_encode_on_two_calls(pattern, voc):
         assert np.array_equal(out[:T].cpu().numpy(), want), k
         if t is small:
             assert np.array_equal(want, np.asarray(oracle_encode(t, v, pattern), dtype=np.int32))
+
+
+def test_noalloc_at_the_size_limit():
+    # an input of exactly the maximum size fits the scratch array
+    merges = np.load(os.path.join(ROOT, "data", "vocab_c2.npy"))
+    tt.load(merges, pattern_id=GPT2)
+    t = text_of(2_200_000, 64, False)[: tt.NOALLOC_MAX_BYTES]
+    assert len(t) == tt.NOALLOC_MAX_BYTES
+    say("noalloc: %d bytes (the limit)" % len(t))
+    x = torch.frombuffer(bytearray(t), dtype=torch.uint8).cuda()
+    want = tt.encode(x).cpu().numpy()
+    out = torch.full((len(t),), -7, dtype=torch.int32, device="cuda")
+    out_n = torch.full((1,), -99, dtype=torch.int64, device="cuda")
+    tt.encode_noalloc_into(x, out, out_n)
+    torch.cuda.synchronize()
+    T = int(out_n.item())
+    assert T == len(want)
+    assert np.array_equal(out[:T].cpu().numpy(), want)
 
 
 def test_noalloc_limits_and_empty_input():
