@@ -160,11 +160,12 @@ size_t layout(int64_t n, char* base, Work* w) {
   t.sb_cnt = (uint32_t*)take((ntiles / SB_TILES + 2) * 4);
   t.sb_err = (uint32_t*)take((ntiles / SB_TILES + 2) * 4);
   t.sb_tok = (uint32_t*)take((ntiles / SB_TILES + 2) * 4);
-  t.long_list = (int32_t*)take((nn / (LANE_CAP + 1) + 2) * 4);
-  t.huge_list = (int32_t*)take((nn / (HUGE_TOKENS + 1) + 2) * 4);
   // a class-c sub-queue takes the pieces of at least QCLASS_MINLEN[c] bytes
-  // that start in every QGROUPS-th tile
+  // that start in every QGROUPS-th tile (long pieces: LANE_CAP + 1 bytes)
   const size_t tiles_per_group = (ntiles + QGROUPS - 1) / QGROUPS;
+  t.lcap = (uint32_t)(tiles_per_group * (TILE / (LANE_CAP + 1) + 1));
+  t.long_list = (int32_t*)take((size_t)t.lcap * QGROUPS * 4);
+  t.huge_list = (int32_t*)take((nn / (HUGE_TOKENS + 1) + 2) * 4);
   for (int c = 0; c < 4; ++c) {
     t.qcap[c] = (uint32_t)(tiles_per_group * (TILE / QCLASS_MINLEN[c] + 1));
     t.queue[c] = (uint32_t*)take((size_t)t.qcap[c] * QGROUPS * 4);

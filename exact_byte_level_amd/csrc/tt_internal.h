@@ -136,7 +136,7 @@ struct Tables {
 // and zeroes the other per-call counters.
 enum : int {
   CTR_P = 0,             // pieces
-  CTR_NLONG = 1,         // pieces longer than LANE_CAP bytes (long_list)
+  CTR_NLONG = 1,         // (unused: long pieces are counted per queue group, qctr[g][4])
   CTR_ERR = 2,           // ERR_* bits
   CTR_T = 4,             // tokens
   CTR_NHUGE = 5,         // pieces with more than HUGE_TOKENS tokens (huge_list)
@@ -183,14 +183,17 @@ struct Work {
   uint32_t* sb_cnt;      // [ntiles / SB_TILES + 1]
   uint32_t* sb_err;      // [ntiles / SB_TILES + 1]
   uint32_t* sb_tok;      // [ntiles / SB_TILES + 1]
-  int32_t* long_list;    // [n / (LANE_CAP + 1) + 1] pieces of LANE_CAP + 1 .. BIG_BYTES bytes
+  int32_t* long_list;    // [QGROUPS][lcap] pieces of LANE_CAP + 1 .. BIG_BYTES bytes, by tile mod QGROUPS
   int32_t* huge_list;    // [n / (HUGE_TOKENS + 1) + 1] pieces with more than HUGE_TOKENS tokens
   // Pieces for group BPE by class c (<= 8, 16, 32, 64 bytes).  Tile t
   // appends to sub-queue g = t % QGROUPS: queue[c] + g * qcap[c], with its
   // count at qctr[g * QCTR_STRIDE + c] (one cache line per sub-queue group,
-  // so that appends from different groups do not meet at one atomic unit).
+  // so that appends from different groups do not meet at one atomic unit);
+  // pieces of LANE_CAP + 1 .. BIG_BYTES bytes to long_list + g * lcap,
+  // counted at qctr[g * QCTR_STRIDE + 4].
   uint32_t* queue[4];
   uint32_t qcap[4];
+  uint32_t lcap;
   uint32_t* qctr;        // [QGROUPS * QCTR_STRIDE]
   uint32_t* ctr;         // [CTR_COUNT]
 };

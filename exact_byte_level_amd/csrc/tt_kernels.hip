@@ -2787,12 +2787,13 @@ __global__ __launch_bounds__(PT_THREADS) __attribute__((amdgpu_waves_per_eu(6)))
     __syncthreads();
     if (threadIdx.x < 5) {
       const uint32_t c = qn[threadIdx.x];
-      uint32_t* ctr = threadIdx.x < 4 ? &w.qctr[(t % QGROUPS) * QCTR_STRIDE + threadIdx.x] : &w.ctr[CTR_NLONG];
+      uint32_t* ctr = &w.qctr[(t % QGROUPS) * QCTR_STRIDE + threadIdx.x];
       qbase[threadIdx.x] = c ? atomicAdd(ctr, c) : 0u;
     }
     __syncthreads();
     if (cls >= 0) {
-      uint32_t* q = cls < 4 ? w.queue[cls] + (t % QGROUPS) * w.qcap[cls] : reinterpret_cast<uint32_t*>(w.long_list);
+      uint32_t* q = cls < 4 ? w.queue[cls] + (t % QGROUPS) * w.qcap[cls]
+                            : reinterpret_cast<uint32_t*>(w.long_list) + (t % QGROUPS) * w.lcap;
       q[qbase[cls] + slot] = p;
     }
     if (threadIdx.x < 5) qn[threadIdx.x] = 0;
@@ -2826,60 +2827,62 @@ __global__ __launch_bounds__(PT_THREADS) __attribute__((amdgpu_waves_per_eu(6)))
 }
 
 // Pass 5: BPE of the queued pieces.  Work items are wavefront loads: one long
-// piece, one piece of <= 64 bytes, two of <= 32, four of <= 16 or eight of
-// <= 8, numbered longest class first and dealt round-robin to the
-// wavefronts of the grid, so the longest merge chains start first and spread
-// over the whole chip.  The item index is the same in every lane, so the loop and the
-// class branches are scalar.
+// piece, one piece of 33-64 bytes, eight of <= 32, sixteen of <= 16 or
+// thirty-two of <= 8, numbered longest class first and dealt round-robin to
+// the wavefronts (of the XCD that compacted their tiles, for queued pieces),
+// so the longest merge chains start first.  The item index is the same in
+// every lane, so the loop and the class branches are scalar.
 constexpr int MERGE_THREADS = 256;
 __global__ __launch_bounds__(MERGE_THREADS) __attribute__((amdgpu_waves_per_eu(8, 8))) void k_bpe_merge(const uint8_t* __restrict__ bytes, Work w, Tables tb) {
-  // pre[k]: work items before sub-queue k, k = (3 - class) * QGROUPS + group
-  // (classes longest first, sub-queues in order); pre[4 * QGROUPS] = all
-  constexpr int NQ = 4 * QGROUPS;
-  __shared__ uint32_t pre[NQ + 1];
+  __shared__ uint32_t pre[6];
   __shared__ BigSmem big;  // LDS of the fallback rounds
   // pieces whose stitching failed: exact rounds, a whole workgroup each, first
   const uint32_t nfall = w.ctr[CTR_NFALL];
   for (uint32_t f = blockIdx.x; f < nfall; f += gridDim.x)
     big_fallback(bytes, w, tb, uniform((uint32_t)w.fall_list[f]), big);
-  if (threadIdx.x < 64) {
-    const int k = (int)threadIdx.x, c = 3 - k / QGROUPS, g = k % QGROUPS;
-    // work items: a 33-64 byte piece alone (its merge chain is the kernel's
-    // critical path: one token slot per lane keeps its steps short); 32 / 16
-    // / 8 shorter pieces together, four token slots per lane
-    uint32_t it = 0u;
-    if (k < NQ) {
-      const uint32_t qk = w.qctr[g * QCTR_STRIDE + c];
-      it = c == 3 ? qk : (qk + (32u >> c) - 1) >> (5 - c);
-    }
-    const uint32_t inc = wave_incl_fwd<SumOp>(it, k);
-    if (k <= NQ) pre[k] = inc - it;
+  const uint32_t wid = threadIdx.x >> 6;
+  // the workgroups of group x = blockIdx mod QGROUPS take sub-queue x, the
+  // pieces of the tiles t = x mod QGROUPS.  Workgroups are dealt to the 8
+  // XCDs in turn, so these are the XCD that compacted those tiles and will
+  // emit them: the pieces' starts, bytes and output ids stay in one L2.
+  // (The grid has at least QGROUPS workgroups.)
+  const uint32_t x = blockIdx.x % QGROUPS;
+  const uint32_t nwx = (gridDim.x - x + QGROUPS - 1) / QGROUPS * (MERGE_THREADS / 64);
+  const uint32_t wx = uniform((blockIdx.x / QGROUPS) * (MERGE_THREADS / 64) + wid);
+  // work items per class, longest first: a long piece (65 bytes .. BIG_BYTES,
+  // exact rounds by the wavefront) or a 33-64 byte piece alone (their merge
+  // chains are the kernel's critical path: one token slot per lane keeps the
+  // steps short); 32 / 16 / 8 shorter pieces together, four token slots per
+  // lane.  pre[i]: items before class 4 - i.
+  if (threadIdx.x < 5) {
+    const uint32_t c = 4u - threadIdx.x;
+    const uint32_t qk = w.qctr[x * QCTR_STRIDE + c];
+    pre[threadIdx.x + 1] = c >= 3u ? qk : (qk + (32u >> c) - 1) >> (5 - c);
   }
   __syncthreads();
-  const uint32_t nl = w.ctr[CTR_NLONG];
-  const uint32_t total = nl + uniform(pre[NQ]);
-  const uint32_t nwaves = gridDim.x * (MERGE_THREADS / 64);
-  const uint32_t wv = uniform(blockIdx.x * (MERGE_THREADS / 64) + (threadIdx.x >> 6));
-  // rounds of nwaves items, every other round dealt in reverse: the waves
-  // that drew the longest items in one round draw the shortest in the next.
-  // A wavefront's issue priority follows its item's length class, so that
-  // the SIMDs favour the longest merge chains (the kernel's critical path)
-  // over the short items that fill in around them.
-  for (uint32_t rnd = 0, t = wv; t < total; ++rnd, t = rnd * nwaves + ((rnd & 1u) ? nwaves - 1u - wv : wv)) {
-    if (t < nl) {
+  if (threadIdx.x == 0) {
+    pre[0] = 0u;
+    for (int i = 1; i <= 5; ++i) pre[i] += pre[i - 1];
+  }
+  __syncthreads();
+  const uint32_t total = uniform(pre[5]);
+  // rounds of nwx items, every other round dealt in reverse: the waves that
+  // drew the longest items in one round draw the shortest in the next.  A
+  // wavefront's issue priority follows its item's length class, so that the
+  // SIMDs favour the longest merge chains over the short items that fill in
+  // around them.
+  for (uint32_t rnd = 0, u = wx; u < total; ++rnd, u = rnd * nwx + ((rnd & 1u) ? nwx - 1u - wx : wx)) {
+    const uint32_t i = u < uniform(pre[1]) ? 0u : u < uniform(pre[2]) ? 1u : u < uniform(pre[3]) ? 2u
+                     : u < uniform(pre[4]) ? 3u : 4u;
+    const uint32_t c = 4u - i;
+    const uint32_t item = u - uniform(pre[i]);
+    if (c == 4) {
       __builtin_amdgcn_s_setprio(3);
-      long_bpe(bytes, w, tb, uniform((uint32_t)w.long_list[t]));
+      long_bpe(bytes, w, tb, uniform((uint32_t)w.long_list[x * w.lcap + item]));
       continue;
     }
-    const uint32_t u = t - nl;
-    uint32_t k = 0;
-#pragma unroll
-    for (uint32_t step = NQ / 2; step >= 1; step >>= 1)
-      if (uniform(pre[k + step]) <= u) k += step;
-    const uint32_t c = 3 - k / QGROUPS, g = k % QGROUPS;
-    const uint32_t item = u - uniform(pre[k]);
-    const uint32_t qn = w.qctr[g * QCTR_STRIDE + c];
-    const uint32_t* q = w.queue[c] + g * w.qcap[c];
+    const uint32_t qn = w.qctr[x * QCTR_STRIDE + c];
+    const uint32_t* q = w.queue[c] + x * w.qcap[c];
     if (c == 3) {
       __builtin_amdgcn_s_setprio(3);
       group_bpe<64>(bytes, w, tb, q, (int)qn, (int)item);
@@ -3427,7 +3430,7 @@ hipError_t launch_pretokenize(const uint8_t* bytes, int64_t n, const int64_t* of
 hipError_t launch_bpe_emit(const uint8_t* bytes, int64_t n, const Tables& tb, const Work& w, int32_t* out_ids,
                            int64_t* out_n, int32_t* out_starts, hipStream_t st) {
   // enough wavefronts to fill the chip; each one loops over work items
-  const int g_merge = capped_grid(n, 256, 2048);
+  const int g_merge = max(QGROUPS, capped_grid(n, 256, 2048));  // every queue group has workgroups
   hipLaunchKernelGGL(k_bpe_merge, dim3(g_merge), dim3(MERGE_THREADS), 0, st, bytes, w, tb); prof_mark("k_bpe_merge", st);
   const int ntiles = ceil_div(n, TILE);
   const bool sb = ntiles > SB_MIN_TILES;  // the two-level tile prefix, as in pre-tokenization
