@@ -27,7 +27,7 @@ struct State {
   uint64_t generation = 0;  // bumped by every load and free: sessions keep the one they began with
   int device = -1;
   uint32_t* d_byte_pair = nullptr;
-  uint64_t* d_pair = nullptr;
+  uint32_t* d_pair = nullptr;
   CacheBucket* d_cache = nullptr;
   uint32_t* d_tok_len = nullptr;
   uint64_t* d_kids = nullptr;
@@ -328,39 +328,75 @@ int tt_load_bpe_ex(const int32_t* merges, const int32_t* ranks, int64_t n_merges
   for (size_t r = 0; r < M; ++r)
     if (mx[r] < 256 && my[r] < 256) byte_pair[(mx[r] << 8) | my[r]] = (uint32_t)r;
 
-  // pair-rank table for pairs with an operand >= 256: two-choice slots, load
-  // factor <= 0.45; a failed insertion doubles the table
+  // pair-rank table for pairs with an operand >= 256: two-choice buckets of
+  // two slots in 256 partitions, load factor <= 0.8; a failed insertion
+  // doubles the table
   size_t n_pairs = 0;
   for (size_t r = 0; r < M; ++r) n_pairs += (mx[r] >= 256 || my[r] >= 256);
-  uint64_t pair_ns = std::max<uint64_t>(next_pow2((uint64_t)(n_pairs / 0.45) + 1), 1024);
-  std::vector<uint64_t> pair_tab;
+  // ids below 2^v: slot keys x << (32 - v) | y >> p with 2^p partitions
+  int v_bits = 16;
+  while (v_bits < ID_BITS && ((uint64_t)1 << v_bits) < 256 + (uint64_t)M) ++v_bits;
+  const int kshift = 32 - v_bits, pbits = 2 * v_bits - 32;
+  const uint32_t pmask = (1u << pbits) - 1u;
+  uint64_t pair_nb = std::max<uint64_t>(next_pow2((uint64_t)(n_pairs / 1.6) + 1), 1024);  // buckets
+  std::vector<uint32_t> pair_tab;  // 4 words per bucket: key 0, rank 0, key 1, rank 1
   int pair_shift = 0;
   for (;;) {
-    pair_shift = 32 - log2_u64(pair_ns);
-    pair_tab.assign(pair_ns, 0ull);
+    pair_shift = 32 - (log2_u64(pair_nb) - pbits);
+    pair_tab.assign(pair_nb * 4, 0u);
+    for (uint64_t i = 0; i < pair_nb * 2; ++i) pair_tab[2 * i + 1] = RANK_NONE;
+    // the two buckets of a pair
+    auto buckets = [&](uint32_t x, uint32_t y, uint64_t* b1, uint64_t* b2) {
+      const uint32_t h = pair_mix(x, y), part = (x ^ y) & pmask;
+      *b1 = ((uint64_t)(h >> pair_shift) << pbits) | part;
+      *b2 = ((uint64_t)(pair_alt(h) >> pair_shift) << pbits) | part;
+    };
     bool ok = true;
+    uint64_t lcg = 0x9E3779B97F4A7C15ull;  // eviction choices (fixed seed: the table is reproducible)
     for (size_t r = 0; r < M && ok; ++r) {
       if (mx[r] < 256 && my[r] < 256) continue;
-      uint64_t cur = (pair_key(mx[r], my[r]) << ID_BITS) | r;
-      uint32_t h = pair_mix(mx[r], my[r]);
-      uint32_t pos = h >> pair_shift;
-      if (pair_tab[pos] != 0) {
-        const uint32_t alt = pair_alt(h) >> pair_shift;
-        if (pair_tab[alt] == 0) pos = alt;
-      }
+      uint32_t cx = mx[r], cy = my[r], crank = (uint32_t)r;
       ok = false;
-      for (int kick = 0; kick < 1000; ++kick) {
-        std::swap(cur, pair_tab[pos]);
-        if (cur == 0) { ok = true; break; }
-        // move the evicted entry to its other slot
-        const uint32_t ex = (uint32_t)(cur >> (2 * ID_BITS)), ey = (uint32_t)(cur >> ID_BITS) & ID_MASK;
-        const uint32_t eh = pair_mix(ex, ey);
-        const uint32_t p1 = eh >> pair_shift, p2 = pair_alt(eh) >> pair_shift;
-        pos = pos == p1 ? p2 : p1;
+      uint64_t b1, b2;
+      buckets(cx, cy, &b1, &b2);
+      uint64_t b = b1;
+      for (int kick = 0; kick < 2000; ++kick) {
+        // a free slot in either bucket
+        int free_slot = -1;
+        uint64_t fb = 0;
+        for (uint64_t cand : {b1, b2}) {
+          for (int sl = 0; sl < 2 && free_slot < 0; ++sl)
+            if (pair_tab[cand * 4 + 2 * sl] == 0u) {
+              free_slot = sl;
+              fb = cand;
+            }
+          if (free_slot >= 0) break;
+        }
+        if (free_slot >= 0) {
+          pair_tab[fb * 4 + 2 * free_slot] = pair_slot_key(cx, cy, kshift, pbits);
+          pair_tab[fb * 4 + 2 * free_slot + 1] = crank;
+          ok = true;
+          break;
+        }
+        // evict a slot of bucket b (alternating buckets along the walk) and
+        // move its key to that key's other bucket
+        lcg = lcg * 6364136223846793005ull + 1442695040888963407ull;
+        const int sl = (int)(lcg >> 63);
+        const uint32_t ek = pair_tab[b * 4 + 2 * sl], er = pair_tab[b * 4 + 2 * sl + 1];
+        pair_tab[b * 4 + 2 * sl] = pair_slot_key(cx, cy, kshift, pbits);
+        pair_tab[b * 4 + 2 * sl + 1] = crank;
+        cx = ek >> kshift;
+        cy = ((ek & ((1u << kshift) - 1u)) << pbits) | (((uint32_t)b ^ cx) & pmask);
+        crank = er;
+        uint64_t e1, e2;
+        buckets(cx, cy, &e1, &e2);
+        b1 = e1;
+        b2 = e2;
+        b = (b == e1) ? e2 : e1;  // the evicted key goes to its other bucket
       }
     }
     if (ok) break;
-    pair_ns *= 2;
+    pair_nb *= 2;
   }
 
   // whole-pre-token table: token t of 2..16 bytes whose own BPE is [t]
@@ -506,12 +542,14 @@ int tt_load_bpe_ex(const int32_t* merges, const int32_t* ranks, int64_t n_merges
   g.pattern = pattern_id;
   g.n_merges = n_merges;
   g.tb.byte_pair = g.d_byte_pair;
-  g.tb.pair_tab = g.d_pair;
+  g.tb.pair_tab = reinterpret_cast<const uint4*>(g.d_pair);
   g.tb.cache = g.d_cache;
   g.tb.tok_len = g.d_tok_len;
   g.tb.kids = g.d_kids;
   g.tb.runs = g.d_runs;
   g.tb.pair_shift = pair_shift;
+  g.tb.pair_kshift = kshift;
+  g.tb.pair_pbits = pbits;
   g.tb.cache_mask = (uint32_t)(cache_nb - 1);
   g.tb.cache_shift = cache_shift;
   g.tb.cache_probe = cache_probe;

@@ -43,16 +43,26 @@ constexpr uint32_t RANK_NONE = 0xFFFFFFFFu;
 constexpr int ID_BITS = 20;             // token ids < 2^20
 constexpr uint32_t ID_MASK = (1u << ID_BITS) - 1;
 
-// Pair-rank table for pairs with an operand >= 256 (byte pairs have their own
-// direct table): a two-choice (cuckoo) table of 8-byte slots, entry
-// (left << 40) | (right << 20) | rank, 0 = empty.  A key sits in one of its
-// two slots, so a lookup is two independent loads and two compares.
+// 40-bit key of the pair (x, y) (host-side maps).
 __host__ __device__ inline uint64_t pair_key(uint32_t x, uint32_t y) {
   return ((uint64_t)x << ID_BITS) | (uint64_t)y;
 }
+// Pair-rank table for pairs with an operand >= 256 (byte pairs have their own
+// direct table): a two-choice (cuckoo) table of 16-byte buckets of two slots
+// {key, rank}.  With ids below 2^v (v >= 16 chosen at load time from the
+// vocabulary), the 32-bit slot key is (x << (32 - v)) | (y >> p), p = 2 v -
+// 32, and the buckets are split into 2^p partitions by (x ^ y) mod 2^p: a
+// pair's two buckets lie in its partition, so the partition restores the low
+// bits of y that the key drops.  A slot is then 8 bytes and the table holds
+// up to 0.8 keys per slot.  Empty slots are {0, RANK_NONE} (no key of the
+// table is 0: one of its ids is >= 256).  A lookup is two independent
+// 16-byte loads and four compares.
+__host__ __device__ inline uint32_t pair_slot_key(uint32_t x, uint32_t y, int kshift, int pbits) {
+  return (x << kshift) | (y >> pbits);
+}
 // 32-bit hash of (x, y): 24-bit products (exact for ids < 2^20), an
-// xor-shift and one 32-bit product.  Slot 1 = its top bits, slot 2 = the top
-// bits of its 16-bit rotation xor a constant (shift = 32 - log2(slots)).
+// xor-shift and one 32-bit product; bucket choice 1 = its top bits, choice 2
+// = the top bits of its 16-bit rotation xor a constant.
 constexpr uint32_t PAIR_MUL_X = 0x9E3779u, PAIR_MUL_Y = 0x7FEB35u;
 __host__ __device__ inline uint32_t pair_mix(uint32_t x, uint32_t y) {
   uint32_t h = (uint32_t)(x * PAIR_MUL_X) ^ (uint32_t)(y * PAIR_MUL_Y);
@@ -110,12 +120,14 @@ struct RunChunk {
 
 struct Tables {
   const uint32_t* byte_pair;    // [65536] rank of (x, y), x, y < 256, or RANK_NONE
-  const uint64_t* pair_tab;     // [2^(32 - pair_shift)] two-choice slots
+  const uint4* pair_tab;        // [2^(32 - pair_shift + pair_pbits)] two-choice buckets of two {key, rank} slots
   const CacheBucket* cache;     // [cache_nb]
   const uint32_t* tok_len;      // [2^ID_BITS] byte length of every token (0 past the vocabulary)
   const uint64_t* kids;         // [merges] operands of the merge of rank r: left | right << 32
   const struct RunChunk* runs;  // [256] the encoding of RUN_BYTES copies of each byte
-  int pair_shift;               // 32 - log2(slots)
+  int pair_shift;               // 32 - (log2(buckets) - pair_pbits): hash bits above the partition
+  int pair_kshift;              // 32 - v (slot key: x << pair_kshift | y >> pair_pbits)
+  int pair_pbits;               // p = 2 v - 32: partitions 2^p
   uint32_t cache_mask;          // cache_nb - 1
   int cache_shift;              // 64 - log2(cache_nb)
   int cache_probe;              // max buckets visited by any lookup

@@ -1607,37 +1607,26 @@ __global__ __launch_bounds__(PT_THREADS) void k_pretok(const uint8_t* __restrict
 
 // ----------------------------------------------------------------------- BPE
 
-// Rank in a bucket's four slots of the key k20 = pair_key(x, y) << ID_BITS,
-// or RANK_NONE.
 // Rank of a pair with an operand >= 256 (every pair next to a new token),
-// or RANK_NONE: its two slots loaded together, 24-bit products for the hash
-// (exact: ids < 2^20), 32-bit byte offsets from the table base.
+// or RANK_NONE: its two buckets loaded together (16 bytes each), four slot
+// keys compared; 24-bit products for the hash (exact: ids < 2^20), 32-bit
+// byte offsets from the table base.
 __device__ __forceinline__ uint32_t pair_rank_new(const Tables& tb, uint32_t x, uint32_t y) {
-  uint32_t h = __umul24(x, 0x9E3779u) ^ __umul24(y, 0x7FEB35u);
+  uint32_t h = __umul24(x, PAIR_MUL_X) ^ __umul24(y, PAIR_MUL_Y);
   h ^= h >> 13;
   h *= 0x85EBCA6Bu;
-  const uint32_t s1 = h >> tb.pair_shift, s2 = pair_alt(h) >> tb.pair_shift;
+  // byte offset of the partition in a row of 2^p buckets
+  const uint32_t part = ((x ^ y) & ((1u << tb.pair_pbits) - 1u)) << 4;
+  const int rs = tb.pair_pbits + 4;
+  const uint32_t o1 = ((h >> tb.pair_shift) << rs) | part, o2 = ((pair_alt(h) >> tb.pair_shift) << rs) | part;
   const char* base = reinterpret_cast<const char*>(tb.pair_tab);
-  const uint64_t e1 = *reinterpret_cast<const uint64_t*>(base + (s1 << 3));
-  const uint64_t e2 = *reinterpret_cast<const uint64_t*>(base + (s2 << 3));
-  const uint64_t k20 = pair_key(x, y) << ID_BITS;
-  uint32_t r = (e1 ^ k20) < (1ull << ID_BITS) ? (uint32_t)e1 & ID_MASK : RANK_NONE;
-  return (e2 ^ k20) < (1ull << ID_BITS) ? (uint32_t)e2 & ID_MASK : r;
-}
-
-// pair_rank_new with the two 24-bit products already combined:
-// hp = (x * PAIR_MUL_X) ^ (y * PAIR_MUL_Y) (so that a product shared by
-// several lookups is formed once).
-__device__ __forceinline__ uint32_t pair_rank_mixed(const Tables& tb, uint32_t hp, uint32_t x, uint32_t y) {
-  uint32_t h = hp ^ (hp >> 13);
-  h *= 0x85EBCA6Bu;
-  const uint32_t s1 = h >> tb.pair_shift, s2 = pair_alt(h) >> tb.pair_shift;
-  const char* base = reinterpret_cast<const char*>(tb.pair_tab);
-  const uint64_t e1 = *reinterpret_cast<const uint64_t*>(base + (s1 << 3));
-  const uint64_t e2 = *reinterpret_cast<const uint64_t*>(base + (s2 << 3));
-  const uint64_t k20 = pair_key(x, y) << ID_BITS;
-  uint32_t r = (e1 ^ k20) < (1ull << ID_BITS) ? (uint32_t)e1 & ID_MASK : RANK_NONE;
-  return (e2 ^ k20) < (1ull << ID_BITS) ? (uint32_t)e2 & ID_MASK : r;
+  const uint4 e1 = *reinterpret_cast<const uint4*>(base + o1);
+  const uint4 e2 = *reinterpret_cast<const uint4*>(base + o2);
+  const uint32_t k = pair_slot_key(x, y, tb.pair_kshift, tb.pair_pbits);
+  uint32_t r = e1.x == k ? e1.y : RANK_NONE;
+  r = e1.z == k ? e1.w : r;
+  r = e2.x == k ? e2.y : r;
+  return e2.z == k ? e2.w : r;
 }
 
 // Rank of merging the adjacent pair (x, y), or RANK_NONE: the byte-pair
