@@ -1844,8 +1844,9 @@ __device__ __forceinline__ uint32_t group_rev(uint32_t x) {  // lane g reads lan
   return G == 2 ? dpp_all<0xB1>(x) : G == 4 ? dpp_all<0x1B>(x) : G == 8 ? dpp_all<0x141>(x) : dpp_all<0x140>(x);
 }
 
-template <int G>
-__device__ __forceinline__ void group_merge4(const Tables& tb, uint32_t (&id)[4], uint32_t (&rk)[4], int& m) {
+template <int G, bool TRACK = false>
+__device__ __forceinline__ void group_merge4(const Tables& tb, uint32_t (&id)[4], uint32_t (&rk)[4], int& m,
+                                             uint32_t (&pos)[4]) {
   static_assert(G == 2 || G == 4 || G == 8 || G == 16, "groups within one DPP row");
   const int g = (int)(threadIdx.x & 63u) & (G - 1);
   const uint32_t pb = 4u * (uint32_t)g;
@@ -1896,6 +1897,14 @@ __device__ __forceinline__ void group_merge4(const Tables& tb, uint32_t (&id)[4]
     const uint32_t q1 = e1 ? rr : e2 ? rl : t2 ? rk[1] : rk[2];
     const uint32_t q2 = e2 ? rr : e3 ? rl : t3 ? rk[2] : rk[3];
     const uint32_t q3 = e3 ? rr : e4 ? rl : t4 ? rk[3] : rn;
+    if (TRACK) {  // byte offsets move with the tokens; the new token keeps its left token's
+      // slot k keeps its offset while k <= lb, else takes slot k + 1's
+      const uint32_t pn = lane_up1(pos[0]);
+      pos[0] = lb >= 0 ? pos[0] : pos[1];
+      pos[1] = t0 ? pos[1] : pos[2];
+      pos[2] = t1 ? pos[2] : pos[3];
+      pos[3] = t2 ? pos[3] : pn;
+    }
     id[0] = i0; id[1] = i1; id[2] = i2; id[3] = i3;
     rk[0] = q0; rk[1] = q1; rk[2] = q2; rk[3] = q3;
     m -= act ? 1 : 0;
@@ -1932,7 +1941,8 @@ __device__ void group_bpe4(const uint8_t* __restrict__ bytes, const Work& w, con
     const uint32_t nx = k < 3 ? id[k + 1] : n0;
     rk[k] = pb + k + 1 < m ? tb.byte_pair[(id[k] << 8) | nx] : RANK_NONE;
   }
-  group_merge4<G>(tb, id, rk, m);
+  uint32_t pos[4];
+  group_merge4<G>(tb, id, rk, m, pos);
   if (valid) {
 #pragma unroll
     for (int k = 0; k < 4; ++k)
@@ -2297,11 +2307,17 @@ struct StitchSmem {
 // right, which goes after).  The walk visits the junction pairs from the last
 // one, (a, b), back to the two edge bytes: of the two current tokens the one
 // made later (the higher rank) steps down to its operand at the junction.
+//
+// The path of the walk does not depend on the ranks it finds, only its
+// verdict does, so the loop runs to the end of the path without an early
+// exit: each step's pair probe is then in flight with the child-id load of
+// the next step instead of before it.
 __device__ bool tokens_compatible(const Tables& tb, uint32_t a, uint32_t b) {
   uint32_t x = a, y = b, cx = RANK_NONE, cy = RANK_NONE;
+  bool bad = false;
   for (int it = 0; it < 4 * SCH; ++it) {  // at most depth(a) + depth(b) <= 2 (SWIN - 1) steps
     const uint32_t r = pair_rank(tb, x, y);
-    if (r != RANK_NONE && r < cx && r <= cy) return false;
+    bad |= r != RANK_NONE && r < cx && r <= cy;
     if (x >= 256u && (y < 256u || x > y)) {
       cx = x - 256u;
       x = (uint32_t)(tb.kids[cx] >> 32);
@@ -2309,7 +2325,7 @@ __device__ bool tokens_compatible(const Tables& tb, uint32_t a, uint32_t b) {
       cy = y - 256u;
       y = (uint32_t)tb.kids[cy] & ID_MASK;
     } else {
-      return true;
+      return !bad;
     }
   }
   return false;  // not reached for tokens of at most SWIN bytes; refusing only costs the fallback
@@ -2327,33 +2343,47 @@ __device__ int stitch_region(const uint8_t* __restrict__ bytes, const Tables& tb
   const int klo = (a - s) / SCH, khi = (b - 1 - s) / SCH;
   const int c0 = max(klo - 1, 0), c1 = min(khi + 1, nc - 1);
   const int nch = c1 - c0 + 1, nb = nch - 1;
-  // 1. each chunk on its own, two per wavefront and pass
-  for (int q = 0; q < nch; q += 8) {
-    const int i = q + 2 * wid + (lane >> 5), g = lane & 31;
+  // 1. each chunk on its own, eight per wavefront and pass: groups of 8
+  // lanes, four byte positions per lane
+  for (int q = 0; q < nch; q += 32) {
+    const int i = q + 8 * wid + (lane >> 3), g = lane & 7, pb = 4 * g;
     const int32_t cs = s + (c0 + i) * SCH;
     const int len = i < nch ? min(SCH, e - cs) : 0;
-    uint32_t id = g < len ? (uint32_t)bytes[cs + g] : 0u;
-    const uint32_t nx = lane_up1(id);
-    uint32_t rk = g + 1 < len ? tb.byte_pair[(id << 8) | (nx & 255u)] : RANK_NONE;
-    uint32_t pos = (uint32_t)g;
-    int m = len;
-    // a whole chunk of one byte value: its encoding from the run table
-    const uint32_t first = lane < 32 ? (uint32_t)__builtin_amdgcn_readlane((int)id, 0)
-                                     : (uint32_t)__builtin_amdgcn_readlane((int)id, 32);
-    const uint64_t same = __ballot(id == first);
-    if (len == SCH && ((same >> (lane & 32)) & 0xFFFFFFFFull) == 0xFFFFFFFFull) {
-      const RunChunk& rc = tb.runs[id];
-      m = (int)rc.cnt;
-      id = g < m ? rc.id[g] : 0u;
-      pos = g < m ? rc.pos[g] : 0u;
-      rk = RANK_NONE;
+    uint32_t id[4], rk[4], pos[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      id[k] = pb + k < len ? (uint32_t)bytes[cs + pb + k] : 0u;
+      pos[k] = (uint32_t)(pb + k);
     }
-    group_merge_loop<32, true>(tb, id, rk, pos, m);
-    if (i < nch) {
-      if (g < m) {
-        sm.tok[i][g] = id;
-        sm.pos[i][g] = (uint8_t)pos;
+    const uint32_t n0 = lane_up1(id[0]);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const uint32_t nx = k < 3 ? id[k + 1] : n0;
+      rk[k] = pb + k + 1 < len ? tb.byte_pair[(id[k] << 8) | (nx & 255u)] : RANK_NONE;
+    }
+    int m = len;
+    // a whole chunk of one byte value: its encoding from the run table (the
+    // group's least and greatest byte agree)
+    const uint32_t lo = group_min<8>(min(min(id[0], id[1]), min(id[2], id[3])));
+    const uint32_t hi = ~group_min<8>(~max(max(id[0], id[1]), max(id[2], id[3])));
+    if (len == SCH && lo == hi) {
+      const RunChunk& rc = tb.runs[lo];
+      m = (int)rc.cnt;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        id[k] = pb + k < m ? rc.id[pb + k] : 0u;
+        pos[k] = pb + k < m ? rc.pos[pb + k] : 0u;
+        rk[k] = RANK_NONE;
       }
+    }
+    group_merge4<8, true>(tb, id, rk, m, pos);
+    if (i < nch) {
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        if (pb + k < m) {
+          sm.tok[i][pb + k] = id[k];
+          sm.pos[i][pb + k] = (uint8_t)pos[k];
+        }
       if (g == 0) sm.cnt[i] = (uint8_t)m;
     }
   }
@@ -2400,23 +2430,38 @@ __device__ int stitch_region(const uint8_t* __restrict__ bytes, const Tables& tb
     }
     __syncthreads();
     if (uniform(sm.nfail) != 0u) break;
-    // the windows, one per wavefront and pass
+    // the windows, four per wavefront and pass: groups of 16 lanes, four
+    // byte positions per lane
     const int nl = (int)uniform(sm.nlist);
-    for (int q = wid; q < nl; q += 4) {
-      const int bb = (int)uniform(sm.list[q]);
-      const int32_t ws = (int32_t)uniform((uint32_t)sm.wstart[bb]);
-      const int wl = (int)uniform(sm.wlen[bb]);
-      uint32_t id = lane < wl ? (uint32_t)bytes[ws + lane] : 0u;
-      const uint32_t nx = lane_up1(id);
-      uint32_t rk = lane + 1 < wl ? tb.byte_pair[(id << 8) | (nx & 255u)] : RANK_NONE;
-      uint32_t pos = (uint32_t)lane;
-      int m = wl;
-      group_merge_loop<64, true>(tb, id, rk, pos, m);
-      if (lane < m && lane < SWIN_TOK) {
-        sm.win[bb][lane] = id;
-        sm.wpos[bb][lane] = (uint8_t)pos;
+    for (int q = 0; q < nl; q += 16) {
+      const int wi = q + 4 * wid + (lane >> 4), g = lane & 15, pb = 4 * g;
+      const bool valid = wi < nl;
+      const int bb = valid ? (int)sm.list[wi] : 0;
+      const int32_t ws = valid ? sm.wstart[bb] : 0;
+      const int wl = valid ? (int)sm.wlen[bb] : 0;
+      uint32_t id[4], rk[4], pos[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        id[k] = pb + k < wl ? (uint32_t)bytes[ws + pb + k] : 0u;
+        pos[k] = (uint32_t)(pb + k);
       }
-      if (lane == 0) sm.wcnt[bb] = (uint8_t)m;
+      const uint32_t n0 = lane_up1(id[0]);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const uint32_t nx = k < 3 ? id[k + 1] : n0;
+        rk[k] = pb + k + 1 < wl ? tb.byte_pair[(id[k] << 8) | (nx & 255u)] : RANK_NONE;
+      }
+      int m = wl;
+      group_merge4<16, true>(tb, id, rk, m, pos);
+      if (valid) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+          if (pb + k < m && pb + k < SWIN_TOK) {
+            sm.win[bb][pb + k] = id[k];
+            sm.wpos[bb][pb + k] = (uint8_t)pos[k];
+          }
+        if (g == 0) sm.wcnt[bb] = (uint8_t)m;
+      }
     }
     __syncthreads();
     // the window's edge tokens against the chunk tokens next to it
