@@ -2867,7 +2867,14 @@ __global__ __launch_bounds__(PT_THREADS) __attribute__((amdgpu_waves_per_eu(6)))
 // so the longest merge chains start first.  The item index is the same in
 // every lane, so the loop and the class branches are scalar.
 constexpr int MERGE_THREADS = 256;
-__global__ __launch_bounds__(MERGE_THREADS) __attribute__((amdgpu_waves_per_eu(8, 8))) void k_bpe_merge(const uint8_t* __restrict__ bytes, Work w, Tables tb) {
+constexpr int64_t MERGE_SMALL = (int64_t)1 << 21;  // inputs up to 2 MiB: the 4-wave merge pass
+// WAVES: wavefronts per SIMD the register budget is made for.  An input of
+// up to MERGE_SMALL bytes has fewer work items than a 4-wave grid has
+// wavefronts, and its time is its longest merge chains: 4 waves per SIMD
+// give those chains registers (no spills) and the SIMDs to themselves.
+// Larger inputs keep 8 waves per SIMD to hide the probes' latency.
+template <int WAVES>
+__global__ __launch_bounds__(MERGE_THREADS) __attribute__((amdgpu_waves_per_eu(WAVES, WAVES))) void k_bpe_merge(const uint8_t* __restrict__ bytes, Work w, Tables tb) {
   __shared__ uint32_t pre[6];
   __shared__ BigSmem big;  // LDS of the fallback rounds
   // pieces whose stitching failed: exact rounds, a whole workgroup each, first
@@ -3464,8 +3471,13 @@ hipError_t launch_pretokenize(const uint8_t* bytes, int64_t n, const int64_t* of
 hipError_t launch_bpe_emit(const uint8_t* bytes, int64_t n, const Tables& tb, const Work& w, int32_t* out_ids,
                            int64_t* out_n, int32_t* out_starts, hipStream_t st) {
   // enough wavefronts to fill the chip; each one loops over work items
-  const int g_merge = max(QGROUPS, capped_grid(n, 256, 2048));  // every queue group has workgroups
-  hipLaunchKernelGGL(k_bpe_merge, dim3(g_merge), dim3(MERGE_THREADS), 0, st, bytes, w, tb); prof_mark("k_bpe_merge", st);
+  if (n <= MERGE_SMALL)
+    hipLaunchKernelGGL(k_bpe_merge<4>, dim3(max(QGROUPS, capped_grid(n, 256, 1024))), dim3(MERGE_THREADS), 0, st,
+                       bytes, w, tb);
+  else  // every queue group has workgroups either way
+    hipLaunchKernelGGL(k_bpe_merge<8>, dim3(max(QGROUPS, capped_grid(n, 256, 2048))), dim3(MERGE_THREADS), 0, st,
+                       bytes, w, tb);
+  prof_mark("k_bpe_merge", st);
   const int ntiles = ceil_div(n, TILE);
   const bool sb = ntiles > SB_MIN_TILES;  // the two-level tile prefix, as in pre-tokenization
   if (sb) {
