@@ -2709,6 +2709,8 @@ __global__ __launch_bounds__(PT_THREADS) __attribute__((amdgpu_waves_per_eu(6)))
   if (stage_fast) sv = *reinterpret_cast<const uint4*>(bytes + sg);
   const uint32_t nc1 = (CLASSIFY && t + 1 + lane < ntiles) ? w.tile_cnt[t + 1 + lane] : 0u;
   const uint32_t fl1 = (CLASSIFY && t + 1 < ntiles) ? w.flags[(int64_t)(t + 1) * PT_THREADS + lane] : 0u;
+  // the previous tile's count, for the end of a long piece that began before this tile
+  const uint32_t prev_cnt = (CLASSIFY && t > 0) ? w.tile_cnt[t - 1] : 0u;
   uint32_t hi;
   // the last tile also folds its own count and error bits into the totals
   const uint32_t base = tile_prefix<SB>(w.tile_cnt, w.sb_cnt, w.sb_err, last ? t + 1 : t, cmask, red, &hi) -
@@ -2844,7 +2846,7 @@ __global__ __launch_bounds__(PT_THREADS) __attribute__((amdgpu_waves_per_eu(6)))
   const int32_t le = (int32_t)uniform((uint32_t)sst[tot]);
   __syncthreads();  // the classification's LDS is read; the stitching reuses it
   uint32_t hh = 0, ht = 0;
-  if (t > 0 && fs > t0 && (w.tile_cnt[t - 1] & cmask) == 0u) {
+  if (t > 0 && fs > t0 && (prev_cnt & cmask) == 0u) {
     const int32_t sp = last_start_before<SB>(w, t, cmask);
     if (fs - sp > BIG_BYTES) hh = stitch_piece(bytes, w, tb, base - 1, sp, fs, (int32_t)t0, fs, t0, st);
   }
@@ -2875,8 +2877,13 @@ constexpr int64_t MERGE_SMALL = (int64_t)1 << 21;  // inputs up to 2 MiB: the 4-
 // Larger inputs keep 8 waves per SIMD to hide the probes' latency.
 template <int WAVES>
 __global__ __launch_bounds__(MERGE_THREADS) __attribute__((amdgpu_waves_per_eu(WAVES, WAVES))) void k_bpe_merge(const uint8_t* __restrict__ bytes, Work w, Tables tb) {
-  __shared__ uint32_t pre[6];
+  __shared__ uint32_t pre[6], qlen[5];
   __shared__ BigSmem big;  // LDS of the fallback rounds
+  const uint32_t x = blockIdx.x % QGROUPS;
+  // this group's queue counts, loaded with the fallback count (their loads
+  // overlap); class c's count goes to qlen[c], so that an item's first
+  // load is its queue entries
+  const uint32_t qk = threadIdx.x < 5 ? w.qctr[x * QCTR_STRIDE + 4 - threadIdx.x] : 0u;
   // pieces whose stitching failed: exact rounds, a whole workgroup each, first
   const uint32_t nfall = w.ctr[CTR_NFALL];
   for (uint32_t f = blockIdx.x; f < nfall; f += gridDim.x)
@@ -2887,7 +2894,6 @@ __global__ __launch_bounds__(MERGE_THREADS) __attribute__((amdgpu_waves_per_eu(W
   // XCDs in turn, so these are the XCD that compacted those tiles and will
   // emit them: the pieces' starts, bytes and output ids stay in one L2.
   // (The grid has at least QGROUPS workgroups.)
-  const uint32_t x = blockIdx.x % QGROUPS;
   const uint32_t nwx = (gridDim.x - x + QGROUPS - 1) / QGROUPS * (MERGE_THREADS / 64);
   const uint32_t wx = uniform((blockIdx.x / QGROUPS) * (MERGE_THREADS / 64) + wid);
   // work items per class, longest first: a long piece (65 bytes .. BIG_BYTES,
@@ -2897,7 +2903,7 @@ __global__ __launch_bounds__(MERGE_THREADS) __attribute__((amdgpu_waves_per_eu(W
   // lane.  pre[i]: items before class 4 - i.
   if (threadIdx.x < 5) {
     const uint32_t c = 4u - threadIdx.x;
-    const uint32_t qk = w.qctr[x * QCTR_STRIDE + c];
+    qlen[c] = qk;
     pre[threadIdx.x + 1] = c >= 3u ? qk : (qk + (32u >> c) - 1) >> (5 - c);
   }
   __syncthreads();
@@ -2922,7 +2928,7 @@ __global__ __launch_bounds__(MERGE_THREADS) __attribute__((amdgpu_waves_per_eu(W
       long_bpe(bytes, w, tb, uniform((uint32_t)w.long_list[x * w.lcap + item]));
       continue;
     }
-    const uint32_t qn = w.qctr[x * QCTR_STRIDE + c];
+    const uint32_t qn = uniform(qlen[c]);
     const uint32_t* q = w.queue[c] + x * w.qcap[c];
     if (c == 3) {
       __builtin_amdgcn_s_setprio(3);
@@ -3034,6 +3040,7 @@ __global__ __launch_bounds__(EMIT_THREADS) void k_emit(Work w, int ntiles, int32
   const uint32_t pbase = w.tile_pbase[t];
   const uint32_t np = w.tile_cnt[t] & cmask;
   const uint32_t hh = uniform(w.huge_hc[2 * t]), ht = uniform(w.huge_hc[2 * t + 1]);
+  const uint32_t nhuge = uniform(w.ctr[CTR_NHUGE]);  // read now: the loads below overlap it
   uint32_t off0 = tile_prefix<SB>(w.tile_tok, w.sb_tok, nullptr, t, ~0u, red, &hi);
   const int32_t t0 = t * TILE;
   const int32_t tend = (int32_t)min(cap, (uint32_t)(t0 + TILE));
@@ -3100,7 +3107,6 @@ __global__ __launch_bounds__(EMIT_THREADS) void k_emit(Work w, int ntiles, int32
     }
   }
   // huge pieces: work item i = (piece, chunk) goes to workgroup i mod grid
-  const uint32_t nhuge = w.ctr[CTR_NHUGE];
   uint32_t item = 0;
   for (uint32_t h = 0; h < nhuge; ++h) {
     const uint32_t p = (uint32_t)w.huge_list[h];
