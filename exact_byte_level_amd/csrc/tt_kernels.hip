@@ -1629,6 +1629,41 @@ __device__ __forceinline__ uint32_t pair_rank_new(const Tables& tb, uint32_t x, 
   return e2.z == k ? e2.w : r;
 }
 
+// pair_rank_new for the lanes with on set, RANK_NONE elsewhere, without a
+// branch: the other lanes load the table's first bucket (one cache line for
+// all of them) and drop the result.  Inside a merge step some lane of the
+// wavefront always probes, so a branch around the probe would skip nothing;
+// without it the step's other work can be scheduled into the probe's wait.
+__device__ __forceinline__ uint32_t pair_rank_if(const Tables& tb, bool on, uint32_t x, uint32_t y) {
+  uint32_t h = __umul24(x, PAIR_MUL_X) ^ __umul24(y, PAIR_MUL_Y);
+  h ^= h >> 13;
+  h *= 0x85EBCA6Bu;
+  const uint32_t part = ((x ^ y) & ((1u << tb.pair_pbits) - 1u)) << 4;
+  const int rs = tb.pair_pbits + 4;
+  const uint32_t o1 = on ? ((h >> tb.pair_shift) << rs) | part : 0u;
+  const uint32_t o2 = on ? ((pair_alt(h) >> tb.pair_shift) << rs) | part : 0u;
+  const char* base = reinterpret_cast<const char*>(tb.pair_tab);
+  const uint4 e1 = *reinterpret_cast<const uint4*>(base + o1);
+  const uint4 e2 = *reinterpret_cast<const uint4*>(base + o2);
+  const uint32_t k = pair_slot_key(x, y, tb.pair_kshift, tb.pair_pbits);
+  uint32_t r = e1.x == k ? e1.y : RANK_NONE;
+  r = e1.z == k ? e1.w : r;
+  r = e2.x == k ? e2.y : r;
+  r = e2.z == k ? e2.w : r;
+  return on ? r : RANK_NONE;
+}
+
+// A merge step's probe: branch-free (LAT, for latency-bound passes: the
+// step's other work fills the probe's wait) or behind a branch (fewer
+// instructions, for passes bound by instruction issue).
+template <bool LAT>
+__device__ __forceinline__ uint32_t probe_step(const Tables& tb, bool on, uint32_t x, uint32_t y) {
+  if (LAT) return pair_rank_if(tb, on, x, y);
+  uint32_t r = RANK_NONE;
+  if (on) r = pair_rank_new(tb, x, y);
+  return r;
+}
+
 // Rank of merging the adjacent pair (x, y), or RANK_NONE: the byte-pair
 // table for two bytes, else the two-choice table (both loaded together).
 __device__ __forceinline__ uint32_t pair_rank(const Tables& tb, uint32_t x, uint32_t y) {
@@ -1748,7 +1783,7 @@ __device__ __forceinline__ uint32_t group_min(uint32_t x) {
 // token probe the pair-rank table (both probes in flight together).  The
 // loop runs while any group of the wavefront still has a merge (ballot: a
 // wave-uniform exit around the DPP moves).
-template <int G, bool TRACK>
+template <int G, bool TRACK, bool LAT = true>
 __device__ __forceinline__ void group_merge_loop(const Tables& tb, uint32_t& id, uint32_t& rk, uint32_t& pos, int& m) {
   const int g = (int)(threadIdx.x & 63u) & (G - 1);
   for (;;) {
@@ -1762,8 +1797,7 @@ __device__ __forceinline__ void group_merge_loop(const Tables& tb, uint32_t& id,
     const uint32_t rk1 = g == G - 1 ? RANK_NONE : rs;  // nothing enters from the next group
     const bool do_l = act && g == bk - 1;
     const bool do_r = act && g == bk && bk + 2 < m;
-    uint32_t r = RANK_NONE;
-    if (do_l || do_r) r = pair_rank_new(tb, do_l ? id : nid, do_l ? nid : id2);
+    const uint32_t r = probe_step<LAT>(tb, do_l || do_r, do_l ? id : nid, do_l ? nid : id2);
     if (act) {
       const uint32_t nid_here = (g < bk) ? id : ((g == bk) ? nid : id1);
       rk = (g < bk - 1) ? rk : ((g == bk - 1 || g == bk) ? r : rk1);
@@ -1777,7 +1811,7 @@ __device__ __forceinline__ void group_merge_loop(const Tables& tb, uint32_t& id,
 // Classic BPE of up to 64 / G queued pieces (queue entries chunk * (64 / G)
 // ...), one per aligned group of G lanes, one byte position per lane (piece
 // length <= G).  Tokens go to tmp_ids[s, s + cnt).
-template <int G>
+template <int G, bool LAT>
 __device__ void group_bpe(const uint8_t* __restrict__ bytes, const Work& w, const Tables& tb,
                           const uint32_t* queue, int qn, int chunk) {
   const int lane = (int)(threadIdx.x & 63u);
@@ -1798,7 +1832,7 @@ __device__ void group_bpe(const uint8_t* __restrict__ bytes, const Work& w, cons
   // a lane, (RANK_NONE << 6) | g, lies above every real key (< 2^26)
   uint32_t rk = (g + 1 < m) ? tb.byte_pair[(id << 8) | (nx & 255u)] : RANK_NONE;
   uint32_t pos = 0;
-  group_merge_loop<G, false>(tb, id, rk, pos, m);
+  group_merge_loop<G, false, LAT>(tb, id, rk, pos, m);
   if (valid) {
     if (g < m) w.tmp_ids[s + g] = (int32_t)id;
     if (g == 0) w.piece_cnt[p] = m;
@@ -1844,7 +1878,7 @@ __device__ __forceinline__ uint32_t group_rev(uint32_t x) {  // lane g reads lan
   return G == 2 ? dpp_all<0xB1>(x) : G == 4 ? dpp_all<0x1B>(x) : G == 8 ? dpp_all<0x141>(x) : dpp_all<0x140>(x);
 }
 
-template <int G, bool TRACK = false>
+template <int G, bool TRACK = false, bool LAT = true>
 __device__ __forceinline__ void group_merge4(const Tables& tb, uint32_t (&id)[4], uint32_t (&rk)[4], int& m,
                                              uint32_t (&pos)[4]) {
   static_assert(G == 2 || G == 4 || G == 8 || G == 16, "groups within one DPP row");
@@ -1880,8 +1914,7 @@ __device__ __forceinline__ void group_merge4(const Tables& tb, uint32_t (&id)[4]
     const uint32_t yl = (b & 1u) ? id[1] : id[0];
     const uint32_t y = b < 2u ? yl : (b == 2u ? id[2] : p3);
     const uint32_t px = do_l ? x : nid, py = do_l ? nid : y;
-    uint32_t res = RANK_NONE;
-    if (do_l || do_r) res = pair_rank_new(tb, px, py);
+    const uint32_t res = probe_step<LAT>(tb, do_l || do_r, px, py);
     // the right probe's result belongs to the lane holding the pair: the
     // prober itself (pair at slot 0) or the cyclically previous lane
     const uint32_t rvr = group_rev<G>(res), upr = lane_up1(res);
@@ -1916,7 +1949,7 @@ __device__ __forceinline__ void group_merge4(const Tables& tb, uint32_t (&id)[4]
 // positions per lane.  Tokens go to tmp_ids[s, s + cnt); the pieces' token
 // counts are added to the tiles they start in, one atomic per run of pieces
 // in one tile.
-template <int G>
+template <int G, bool LAT>
 __device__ void group_bpe4(const uint8_t* __restrict__ bytes, const Work& w, const Tables& tb,
                            const uint32_t* queue, int qn, int chunk) {
   const int lane = (int)(threadIdx.x & 63u);
@@ -1942,7 +1975,7 @@ __device__ void group_bpe4(const uint8_t* __restrict__ bytes, const Work& w, con
     rk[k] = pb + k + 1 < m ? tb.byte_pair[(id[k] << 8) | nx] : RANK_NONE;
   }
   uint32_t pos[4];
-  group_merge4<G>(tb, id, rk, m, pos);
+  group_merge4<G, false, LAT>(tb, id, rk, m, pos);
   if (valid) {
 #pragma unroll
     for (int k = 0; k < 4; ++k)
@@ -2932,16 +2965,16 @@ __global__ __launch_bounds__(MERGE_THREADS) __attribute__((amdgpu_waves_per_eu(W
     const uint32_t* q = w.queue[c] + x * w.qcap[c];
     if (c == 3) {
       __builtin_amdgcn_s_setprio(3);
-      group_bpe<64>(bytes, w, tb, q, (int)qn, (int)item);
+      group_bpe<64, WAVES == 4>(bytes, w, tb, q, (int)qn, (int)item);
     } else if (c == 2) {
       __builtin_amdgcn_s_setprio(2);
-      group_bpe4<8>(bytes, w, tb, q, (int)qn, (int)item);
+      group_bpe4<8, WAVES == 4>(bytes, w, tb, q, (int)qn, (int)item);
     } else if (c == 1) {
       __builtin_amdgcn_s_setprio(1);
-      group_bpe4<4>(bytes, w, tb, q, (int)qn, (int)item);
+      group_bpe4<4, WAVES == 4>(bytes, w, tb, q, (int)qn, (int)item);
     } else {
       __builtin_amdgcn_s_setprio(0);
-      group_bpe4<2>(bytes, w, tb, q, (int)qn, (int)item);
+      group_bpe4<2, WAVES == 4>(bytes, w, tb, q, (int)qn, (int)item);
     }
   }
 }
