@@ -1640,8 +1640,9 @@ __device__ __forceinline__ uint32_t pair_rank_if(const Tables& tb, bool on, uint
   h *= 0x85EBCA6Bu;
   const uint32_t part = ((x ^ y) & ((1u << tb.pair_pbits) - 1u)) << 4;
   const int rs = tb.pair_pbits + 4;
-  const uint32_t o1 = on ? ((h >> tb.pair_shift) << rs) | part : 0u;
-  const uint32_t o2 = on ? ((pair_alt(h) >> tb.pair_shift) << rs) | part : 0u;
+  const uint32_t keep = on ? ~0u : 0u;  // a mask, not a select of the offsets (that became a branch)
+  const uint32_t o1 = (((h >> tb.pair_shift) << rs) | part) & keep;
+  const uint32_t o2 = (((pair_alt(h) >> tb.pair_shift) << rs) | part) & keep;
   const char* base = reinterpret_cast<const char*>(tb.pair_tab);
   const uint4 e1 = *reinterpret_cast<const uint4*>(base + o1);
   const uint4 e2 = *reinterpret_cast<const uint4*>(base + o2);
@@ -1911,8 +1912,9 @@ __device__ __forceinline__ void group_merge4(const Tables& tb, uint32_t (&id)[4]
     const uint32_t a = (uint32_t)(lb - 1), b = (uint32_t)(lb + 2);
     const uint32_t xl = (a & 1u) ? id[1] : id[0], xh = (a & 1u) ? id[3] : id[2];
     const uint32_t x = (a & 2u) ? xh : xl;
-    const uint32_t yl = (b & 1u) ? id[1] : id[0];
-    const uint32_t y = b < 2u ? yl : (b == 2u ? id[2] : p3);
+    uint32_t y = b == 2u ? id[2] : p3;  // flat selects (nested ones compiled into a branch)
+    y = b == 1u ? id[1] : y;
+    y = b == 0u ? id[0] : y;
     const uint32_t px = do_l ? x : nid, py = do_l ? nid : y;
     const uint32_t res = probe_step<LAT>(tb, do_l || do_r, px, py);
     // the right probe's result belongs to the lane holding the pair: the
