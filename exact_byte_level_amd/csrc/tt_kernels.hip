@@ -1796,8 +1796,8 @@ __device__ __forceinline__ void group_merge_loop(const Tables& tb, uint32_t& id,
     const uint32_t id1 = lane_up1(id), id2 = lane_up1(id1), rs = lane_up1(rk);
     const uint32_t pos1 = TRACK ? lane_up1(pos) : 0u;
     const uint32_t rk1 = g == G - 1 ? RANK_NONE : rs;  // nothing enters from the next group
-    const bool do_l = act && g == bk - 1;
-    const bool do_r = act && g == bk && bk + 2 < m;
+    const bool do_l = LAT ? act & (g == bk - 1) : act && g == bk - 1;  // (bitwise: no branches)
+    const bool do_r = LAT ? act & (g == bk) & (bk + 2 < m) : act && g == bk && bk + 2 < m;
     const uint32_t r = probe_step<LAT>(tb, do_l || do_r, do_l ? id : nid, do_l ? nid : id2);
     if (act) {
       const uint32_t nid_here = (g < bk) ? id : ((g == bk) ? nid : id1);
@@ -1905,8 +1905,11 @@ __device__ __forceinline__ void group_merge4(const Tables& tb, uint32_t (&id)[4]
     // (that token, new); the lane holding the token three after the pair's
     // left one (lane 0 of the group if that is past the group) probes (new,
     // token after the pair).  No lane has both roles.
-    const bool do_l = lb >= 1 && lb <= 4;
-    const bool do_r = act && bk + 2 < m && ((lb >= -3 && lb <= 0) || (first && bk + 3 >= 4 * G));
+    // (LAT: bitwise on the bools, as the short-circuit form compiles into
+    // branches; it is the shorter code where instruction issue is the bound)
+    const bool do_l = (uint32_t)(lb - 1) < 4u;
+    const bool do_r = LAT ? act & (bk + 2 < m) & (((uint32_t)(lb + 3) < 4u) | (first & (bk + 3 >= 4 * G)))
+                          : act && bk + 2 < m && ((lb >= -3 && lb <= 0) || (first && bk + 3 >= 4 * G));
     // x = id[lb - 1] (lb in 1..4), y = id[lb + 2] (lb in -2..0) else p3: selects on
     // the bits of the slot number
     const uint32_t a = (uint32_t)(lb - 1), b = (uint32_t)(lb + 2);
