@@ -60,16 +60,14 @@ __host__ __device__ inline uint64_t pair_key(uint32_t x, uint32_t y) {
 __host__ __device__ inline uint32_t pair_slot_key(uint32_t x, uint32_t y, int kshift, int pbits) {
   return (x << kshift) | (y >> pbits);
 }
-// 32-bit hash of (x, y): 24-bit products (exact for ids < 2^20), an
-// xor-shift and one 32-bit product; bucket choice 1 = its top bits, choice 2
-// = the top bits of its 16-bit rotation xor a constant.
+// Bucket choices of (x, y): m = the xor of two 24-bit products (exact for
+// ids < 2^20); choice i = the top bits of m * PAIR_MUL_i, two independent
+// products of m, so that a probe computes both side by side.
 constexpr uint32_t PAIR_MUL_X = 0x9E3779u, PAIR_MUL_Y = 0x7FEB35u;
+constexpr uint32_t PAIR_MUL_1 = 0x85EBCA6Bu, PAIR_MUL_2 = 0xC2B2AE35u;
 __host__ __device__ inline uint32_t pair_mix(uint32_t x, uint32_t y) {
-  uint32_t h = (uint32_t)(x * PAIR_MUL_X) ^ (uint32_t)(y * PAIR_MUL_Y);
-  h ^= h >> 13;
-  return h * 0x85EBCA6Bu;
+  return (uint32_t)(x * PAIR_MUL_X) ^ (uint32_t)(y * PAIR_MUL_Y);
 }
-__host__ __device__ inline uint32_t pair_alt(uint32_t h) { return ((h >> 16) | (h << 16)) ^ 0x5BD1E995u; }
 
 // Whole-pre-token table: buckets of CACHE_SLOTS entries in one 128-byte line
 // (struct of arrays).  Entry k holds the piece bytes zero-padded into w0[k] /

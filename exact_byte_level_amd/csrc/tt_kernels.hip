@@ -1612,13 +1612,12 @@ __global__ __launch_bounds__(PT_THREADS) void k_pretok(const uint8_t* __restrict
 // keys compared; 24-bit products for the hash (exact: ids < 2^20), 32-bit
 // byte offsets from the table base.
 __device__ __forceinline__ uint32_t pair_rank_new(const Tables& tb, uint32_t x, uint32_t y) {
-  uint32_t h = __umul24(x, PAIR_MUL_X) ^ __umul24(y, PAIR_MUL_Y);
-  h ^= h >> 13;
-  h *= 0x85EBCA6Bu;
+  const uint32_t mx = __umul24(x, PAIR_MUL_X) ^ __umul24(y, PAIR_MUL_Y);
+  const uint32_t h1 = mx * PAIR_MUL_1, h2 = mx * PAIR_MUL_2;
   // byte offset of the partition in a row of 2^p buckets
   const uint32_t part = ((x ^ y) & ((1u << tb.pair_pbits) - 1u)) << 4;
   const int rs = tb.pair_pbits + 4;
-  const uint32_t o1 = ((h >> tb.pair_shift) << rs) | part, o2 = ((pair_alt(h) >> tb.pair_shift) << rs) | part;
+  const uint32_t o1 = ((h1 >> tb.pair_shift) << rs) | part, o2 = ((h2 >> tb.pair_shift) << rs) | part;
   const char* base = reinterpret_cast<const char*>(tb.pair_tab);
   const uint4 e1 = *reinterpret_cast<const uint4*>(base + o1);
   const uint4 e2 = *reinterpret_cast<const uint4*>(base + o2);
@@ -1635,14 +1634,13 @@ __device__ __forceinline__ uint32_t pair_rank_new(const Tables& tb, uint32_t x, 
 // wavefront always probes, so a branch around the probe would skip nothing;
 // without it the step's other work can be scheduled into the probe's wait.
 __device__ __forceinline__ uint32_t pair_rank_if(const Tables& tb, bool on, uint32_t x, uint32_t y) {
-  uint32_t h = __umul24(x, PAIR_MUL_X) ^ __umul24(y, PAIR_MUL_Y);
-  h ^= h >> 13;
-  h *= 0x85EBCA6Bu;
+  const uint32_t mx = __umul24(x, PAIR_MUL_X) ^ __umul24(y, PAIR_MUL_Y);
+  const uint32_t h1 = mx * PAIR_MUL_1, h2 = mx * PAIR_MUL_2;
   const uint32_t part = ((x ^ y) & ((1u << tb.pair_pbits) - 1u)) << 4;
   const int rs = tb.pair_pbits + 4;
   const uint32_t keep = on ? ~0u : 0u;  // a mask, not a select of the offsets (that became a branch)
-  const uint32_t o1 = (((h >> tb.pair_shift) << rs) | part) & keep;
-  const uint32_t o2 = (((pair_alt(h) >> tb.pair_shift) << rs) | part) & keep;
+  const uint32_t o1 = (((h1 >> tb.pair_shift) << rs) | part) & keep;
+  const uint32_t o2 = (((h2 >> tb.pair_shift) << rs) | part) & keep;
   const char* base = reinterpret_cast<const char*>(tb.pair_tab);
   const uint4 e1 = *reinterpret_cast<const uint4*>(base + o1);
   const uint4 e2 = *reinterpret_cast<const uint4*>(base + o2);
