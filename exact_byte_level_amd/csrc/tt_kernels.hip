@@ -1638,9 +1638,12 @@ __device__ __forceinline__ uint32_t pair_rank_if(const Tables& tb, bool on, uint
   const uint32_t h1 = mx * PAIR_MUL_1, h2 = mx * PAIR_MUL_2;
   const uint32_t part = ((x ^ y) & ((1u << tb.pair_pbits) - 1u)) << 4;
   const int rs = tb.pair_pbits + 4;
-  const uint32_t keep = on ? ~0u : 0u;  // a mask, not a select of the offsets (that became a branch)
-  const uint32_t o1 = (((h1 >> tb.pair_shift) << rs) | part) & keep;
-  const uint32_t o2 = (((h2 >> tb.pair_shift) << rs) | part) & keep;
+  // the offsets masked by an AND the compiler does not see through: as a
+  // select it became a branch, or a select of 64-bit addresses
+  const uint32_t keep = on ? ~0u : 0u;
+  uint32_t o1 = ((h1 >> tb.pair_shift) << rs) | part, o2 = ((h2 >> tb.pair_shift) << rs) | part;
+  asm("v_and_b32 %0, %1, %2" : "=v"(o1) : "v"(o1), "v"(keep));
+  asm("v_and_b32 %0, %1, %2" : "=v"(o2) : "v"(o2), "v"(keep));
   const char* base = reinterpret_cast<const char*>(tb.pair_tab);
   const uint4 e1 = *reinterpret_cast<const uint4*>(base + o1);
   const uint4 e2 = *reinterpret_cast<const uint4*>(base + o2);
