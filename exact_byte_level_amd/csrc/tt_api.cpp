@@ -348,8 +348,8 @@ int tt_load_bpe_ex(const int32_t* merges, const int32_t* ranks, int64_t n_merges
     // the two buckets of a pair
     auto buckets = [&](uint32_t x, uint32_t y, uint64_t* b1, uint64_t* b2) {
       const uint32_t m = pair_mix(x, y), part = (x ^ y) & pmask;
-      *b1 = ((uint64_t)((m * PAIR_MUL_1) >> pair_shift) << pbits) | part;
-      *b2 = ((uint64_t)((m * PAIR_MUL_2) >> pair_shift) << pbits) | part;
+      *b1 = ((uint64_t)(pair_choice(m, PAIR_MUL_1) >> pair_shift) << pbits) | part;
+      *b2 = ((uint64_t)(pair_choice(m, PAIR_MUL_2) >> pair_shift) << pbits) | part;
     };
     bool ok = true;
     uint64_t lcg = 0x9E3779B97F4A7C15ull;  // eviction choices (fixed seed: the table is reproducible)

@@ -61,13 +61,15 @@ __host__ __device__ inline uint32_t pair_slot_key(uint32_t x, uint32_t y, int ks
   return (x << kshift) | (y >> pbits);
 }
 // Bucket choices of (x, y): m = the xor of two 24-bit products (exact for
-// ids < 2^20); choice i = the top bits of m * PAIR_MUL_i, two independent
-// products of m, so that a probe computes both side by side.
+// ids < 2^20); choice i = the top bits of the 32-bit product of m's low 24
+// bits and PAIR_MUL_i: two independent full-rate 24-bit products of m, which
+// a probe computes side by side.
 constexpr uint32_t PAIR_MUL_X = 0x9E3779u, PAIR_MUL_Y = 0x7FEB35u;
-constexpr uint32_t PAIR_MUL_1 = 0x85EBCA6Bu, PAIR_MUL_2 = 0xC2B2AE35u;
+constexpr uint32_t PAIR_MUL_1 = 0xEBCA6Bu, PAIR_MUL_2 = 0xB2AE35u;
 __host__ __device__ inline uint32_t pair_mix(uint32_t x, uint32_t y) {
   return (uint32_t)(x * PAIR_MUL_X) ^ (uint32_t)(y * PAIR_MUL_Y);
 }
+__host__ __device__ inline uint32_t pair_choice(uint32_t m, uint32_t mul) { return (m & 0xFFFFFFu) * mul; }
 
 // Whole-pre-token table: buckets of CACHE_SLOTS entries in one 128-byte line
 // (struct of arrays).  Entry k holds the piece bytes zero-padded into w0[k] /

@@ -1607,13 +1607,22 @@ __global__ __launch_bounds__(PT_THREADS) void k_pretok(const uint8_t* __restrict
 
 // ----------------------------------------------------------------------- BPE
 
+// 24-bit product (x < 2^24) as one full-rate instruction: with __umul24 the
+// optimizer saw that only the low 24 bits of these products feed the bucket
+// choices and turned them into quarter-rate 32-bit products.
+__device__ __forceinline__ uint32_t mul_u24(uint32_t x, uint32_t c) {
+  uint32_t r;
+  asm("v_mul_u32_u24 %0, %1, %2" : "=v"(r) : "s"(c), "v"(x));
+  return r;
+}
+
 // Rank of a pair with an operand >= 256 (every pair next to a new token),
 // or RANK_NONE: its two buckets loaded together (16 bytes each), four slot
 // keys compared; 24-bit products for the hash (exact: ids < 2^20), 32-bit
 // byte offsets from the table base.
 __device__ __forceinline__ uint32_t pair_rank_new(const Tables& tb, uint32_t x, uint32_t y) {
-  const uint32_t mx = __umul24(x, PAIR_MUL_X) ^ __umul24(y, PAIR_MUL_Y);
-  const uint32_t h1 = mx * PAIR_MUL_1, h2 = mx * PAIR_MUL_2;
+  const uint32_t mx = mul_u24(x, PAIR_MUL_X) ^ mul_u24(y, PAIR_MUL_Y);
+  const uint32_t h1 = __umul24(mx, PAIR_MUL_1), h2 = __umul24(mx, PAIR_MUL_2);  // = pair_choice
   // byte offset of the partition in a row of 2^p buckets
   const uint32_t part = ((x ^ y) & ((1u << tb.pair_pbits) - 1u)) << 4;
   const int rs = tb.pair_pbits + 4;
@@ -1634,8 +1643,8 @@ __device__ __forceinline__ uint32_t pair_rank_new(const Tables& tb, uint32_t x, 
 // wavefront always probes, so a branch around the probe would skip nothing;
 // without it the step's other work can be scheduled into the probe's wait.
 __device__ __forceinline__ uint32_t pair_rank_if(const Tables& tb, bool on, uint32_t x, uint32_t y) {
-  const uint32_t mx = __umul24(x, PAIR_MUL_X) ^ __umul24(y, PAIR_MUL_Y);
-  const uint32_t h1 = mx * PAIR_MUL_1, h2 = mx * PAIR_MUL_2;
+  const uint32_t mx = mul_u24(x, PAIR_MUL_X) ^ mul_u24(y, PAIR_MUL_Y);
+  const uint32_t h1 = __umul24(mx, PAIR_MUL_1), h2 = __umul24(mx, PAIR_MUL_2);  // = pair_choice
   const uint32_t part = ((x ^ y) & ((1u << tb.pair_pbits) - 1u)) << 4;
   const int rs = tb.pair_pbits + 4;
   // the offsets masked by an AND the compiler does not see through: as a
