@@ -2847,15 +2847,19 @@ __global__ __launch_bounds__(PT_THREADS) __attribute__((amdgpu_waves_per_eu(6)))
       } else {
         uint32_t hit = RANK_NONE;
         if (len <= CACHE_MAXLEN) {
-          uint64_t w0 = 0, w1 = 0;
-#pragma unroll
-          for (int j = 0; j < CACHE_MAXLEN; ++j) {
-            if (j < len) {
-              const uint64_t by = sb[off + j];
-              if (j < 8) w0 |= by << (8 * j);
-              else w1 |= by << (8 * (j - 8));
-            }
-          }
+          // the key's bytes from three aligned 8-byte LDS reads, shifted and
+          // masked to the piece (a byte-by-byte loop under len compiled into
+          // sixteen branches, each waiting for its read): the staging ends
+          // at byte TILE + CACHE_MAXLEN, so the reads up to (off & ~7) + 24
+          // stay inside it for every off in the tile
+          static_assert(CACHE_MAXLEN == 16 && (TILE + CACHE_MAXLEN) % 8 == 0, "three 8-byte words cover a key");
+          const uint64_t* sq = reinterpret_cast<const uint64_t*>(stage);
+          const int q = off >> 3, sh = (off & 7) * 8;
+          const uint64_t q0 = sq[q], q1 = sq[q + 1], q2 = sq[q + 2];
+          uint64_t w0 = sh ? (q0 >> sh) | (q1 << (64 - sh)) : q0;
+          uint64_t w1 = sh ? (q1 >> sh) | (q2 << (64 - sh)) : q1;
+          w0 = len >= 8 ? w0 : w0 & ((1ull << (8 * len)) - 1ull);
+          w1 = len >= 16 ? w1 : len > 8 ? w1 & ((1ull << (8 * (len - 8))) - 1ull) : 0ull;
           hit = cache_lookup(tb, w0, w1, (uint32_t)len);
         }
         if (hit != RANK_NONE) {
