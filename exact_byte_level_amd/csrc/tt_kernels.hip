@@ -1566,6 +1566,7 @@ __global__ __launch_bounds__(PT_THREADS) void k_pretok(const uint8_t* __restrict
   uint32_t bits = 0;
   uint32_t cnt;
   bool counted = false, bad, unsup = false;
+  int ebits = -1;  // the tile's error flags (bit 0 UTF-8, bit 1 offsets) once gathered
   if (PAT != 0) {
     // cl100k- and o200k-style rules: classes from the code bytes of the
     // summary pass
@@ -1582,9 +1583,16 @@ __global__ __launch_bounds__(PT_THREADS) void k_pretok(const uint8_t* __restrict
       uint32_t wc;
       const bool plain = t0 - HALO >= 0 && t0 - HALO + 16 * RAW_WORDS <= n && (!offs || sm.seq_lo == sm.seq_hi);
       bits = plain ? gpt2_ascii_bits<true>(sm, n, t0, &wc) : gpt2_ascii_bits<false>(sm, n, t0, &wc);
-      if ((threadIdx.x & 63u) == 0) sm.red[threadIdx.x >> 6] = wc;
+      // the wavefronts' counts and offset-check flags (an ASCII tile has no
+      // UTF-8 error) through one barrier
+      const uint32_t woff = __ballot(bad_off) ? 2u : 0u;
+      if ((threadIdx.x & 63u) == 0) {
+        sm.red[threadIdx.x >> 6] = wc;
+        sm.red[4 + (threadIdx.x >> 6)] = woff;
+      }
       __syncthreads();
       cnt = sm.red[0] + sm.red[1] + sm.red[2] + sm.red[3];
+      ebits = (int)(sm.red[4] | sm.red[5] | sm.red[6] | sm.red[7]);
       counted = true;
     } else {
 #pragma unroll
@@ -1596,8 +1604,8 @@ __global__ __launch_bounds__(PT_THREADS) void k_pretok(const uint8_t* __restrict
   }
   w.flags[(int64_t)t * PT_THREADS + threadIdx.x] = (uint16_t)bits;
   if (!counted) cnt = block_sum(__popc(bits), sm.red);
-  const uint32_t err = (__syncthreads_or(bad) ? ERR_UTF8 : 0u) | (__syncthreads_or(bad_off) ? ERR_OFFSETS : 0u) |
-                       (unsup ? ERR_UNSUP : 0u);
+  if (ebits < 0) ebits = (__syncthreads_or(bad) ? 1 : 0) | (__syncthreads_or(bad_off) ? 2 : 0);
+  const uint32_t err = ((ebits & 1) ? ERR_UTF8 : 0u) | ((ebits & 2) ? ERR_OFFSETS : 0u) | (unsup ? ERR_UNSUP : 0u);
   if (threadIdx.x == 0) {
     w.tile_cnt[t] = cnt | (err << TILE_ERR_SHIFT);
     // reset for the long-piece stitching of the next pass
