@@ -2892,8 +2892,12 @@ __global__ __launch_bounds__(PT_THREADS) __attribute__((amdgpu_waves_per_eu(6)))
                             : reinterpret_cast<uint32_t*>(w.long_list) + (t % QGROUPS) * w.lcap;
       q[qbase[cls] + slot] = p;
     }
-    if (threadIdx.x < 5) qn[threadIdx.x] = 0;
-    __syncthreads();
+    // another round reuses the class counts and reads qbase again: a barrier
+    // between (after the last round the block sum below orders what follows)
+    if (k0 + PT_THREADS < tot) {
+      if (threadIdx.x < 5) qn[threadIdx.x] = 0;
+      __syncthreads();
+    }
   }
   // tokens of the tile's finished pieces; merged pieces add theirs later
   const uint32_t tok = block_sum(fin, red);
