@@ -1233,8 +1233,9 @@ __device__ bool stage_codes(int64_t n, int64_t t0, const Work& w, TileSmem& sm, 
 // the five class-index bits, sequence start, sequence last).  lf, rb: the
 // forward / backward run states (o200k-style classes) before c_lo and from
 // e on; tl: the tail state before c_lo.  *unsup (the same in every lane):
-// the word's outcome depends on a contraction chain or on a word restart
-// that lies before the span, which these carries do not hold.
+// the word's outcome depends on a contraction chain that began before the
+// window or on a word restart that lies before the span, which these
+// carries do not hold.
 __device__ uint32_t o2_word_bits(const uint32_t* pl, int lane, int c_lo, int e, uint32_t lf, uint32_t rb, uint32_t tl,
                                  bool* unsup) {
   const uint32_t b0 = pl[0], b1 = pl[1], b2 = pl[2], b3 = pl[3], b4 = pl[4], SS = pl[5], SL = pl[6];
@@ -1271,7 +1272,34 @@ __device__ uint32_t o2_word_bits(const uint32_t* pl, int lane, int c_lo, int e, 
   const uint32_t CS2 = AP & ~SSn & ~SSn2 & ((bs_dn<1>(RV) & bs_dn<2>(E)) | (bs_dn<1>(LL) & bs_dn<2>(LL)));
   const uint32_t CAND = (CS1 | CS2) & bs_up<1>(LI) & ~SS;
   const uint32_t LINK = bs_up<2>(CS1) | bs_up<3>(CS2);  // right after a contraction shape: a chain
-  const uint32_t ATT = CAND & ~LINK;
+  // a chain of shapes, each right after the letters of the one before: its
+  // first shape (HEAD) attaches when a letter comes before it, and every
+  // later one attaches exactly when the one before did not (a word that took
+  // a contraction is over; one that did not takes the next).  So a linked
+  // shape attaches when the count of shapes from its head, itself included,
+  // is odd and the head attached, or even and it did not: P (prefix parity
+  // of the shapes) xor the head's P ^ CAND, filled along the chain's chars.
+  const uint32_t CSX = CS1 | CS2;
+  const uint32_t LNK = CSX & LINK & ~SS;
+  const uint32_t HEAD = CSX & ~LNK;
+  const uint32_t RC = CSX | bs_up<1>(CSX) | bs_up<2>(CS2);
+  uint32_t P = CSX;
+  P ^= P << 1;
+  P ^= P << 2;
+  P ^= P << 4;
+  P ^= P << 8;
+  P ^= P << 16;
+  if (__popcll(__ballot(__popc(CSX) & 1) & ((1ull << lane) - 1ull)) & 1) P = ~P;
+  // a shape in the window's first three chars may link to one before the
+  // window, unless the window starts a sequence: chains from there are unknown
+  const bool seq0 = __ballot((SS & bs_range(x0, 0, 1)) != 0u) != 0ull;
+  const uint32_t EDGE = seq0 ? 0u : bs_range(x0, -(1 << 20), 3);
+  const uint32_t HC = HEAD & ~EDGE;
+  const uint32_t S1 = HC & (P ^ CAND);
+  const uint32_t F = bs_fill_up((RC & ~HEAD) | S1, S1, lane) | S1;
+  const uint32_t SU0 = RC & EDGE & ~bs_up<1>(RC);
+  const uint32_t UNK = bs_fill_up(RC & ~HC, SU0, lane) | SU0;
+  const uint32_t ATT = CAND & (~LINK | ((P ^ F) & ~UNK));
   const uint32_t IC = bs_up<1>(ATT) | bs_up<2>(ATT & CS2);  // letters of an attached contraction
   const uint32_t AFTER = LI & ~SS & (bs_up<2>(ATT & CS1) | bs_up<3>(ATT & CS2));
   // case rules inside a letter run: PREVW, the last cased char of the word
@@ -1309,10 +1337,11 @@ __device__ uint32_t o2_word_bits(const uint32_t* pl, int lane, int c_lo, int e, 
   const uint32_t BWN = WN & ~Wp & ~Op;
   const uint32_t BWS = WS & (~Wp | (bs_up<1>(WN) & (ENDS | bs_up<1>(ABSO))) | (bs_up<1>(WS) & ~SL & ~bs_dn<1>(W)));
   const uint32_t own = bs_range(x0, c_lo, e);
-  // undecided cases: a contraction chain near the own chars, or an upper-case
-  // own char whose word may restart before the span
+  // undecided cases: a contraction chain near the own chars whose head may
+  // lie before the window, or an upper-case own char whose word may restart
+  // before the span
   const uint32_t near = bs_range(x0, c_lo - 4, e + 4);
-  const bool chain = __ballot((CAND & LINK & near) != 0u) != 0ull;
+  const bool chain = __ballot((CAND & LNK & UNK & near) != 0u) != 0ull;
   bool restart = false;
   if (amb) {
     // the run from the span's first char reaches the first own upper-case

@@ -6,10 +6,11 @@ Brute force over every string of length <= 5 of a class-covering alphabet
 multibyte strings, runs that cross tiles for each fact carried between tiles
 (digit groups, whitespace before CR/LF, CR/LF after "other" chars, CR/LF/'/'
 tails, upper-case runs to the end of a word, Lm/Lo runs after a lower-case
-letter), and a 1M-char encode.  Inputs holding back-to-back contraction
-suffixes (whose attachment alternates along the chain) are the one case the
-GPU rules leave undecided: the call reports TT_EUNSUPPORTED, never a wrong
-split.
+letter), contraction chains (back-to-back suffixes, whose attachment
+alternates from the chain's first suffix) inside a tile and across tile
+starts, and a 1M-char encode.  A chain whose first suffix lies more than the
+halo before a tile start is the case the GPU rules leave undecided: the call
+reports TT_EUNSUPPORTED, never a wrong split.
 """
 import itertools
 import os
@@ -28,10 +29,12 @@ from oracle.pretok import O200K, piece_starts_batch, split_bytes  # noqa: E402
 from synth import mix_text  # noqa: E402
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-# an apostrophe after a letter or mark with a contraction shape after it,
-# right after another contraction shape
+# an apostrophe with a contraction shape after it, right after another one
 _SHAPE = "(?:[sStTmMdD]|[rRvV][eE]|[lL][lL])"
 CHAIN = re.compile("'" + _SHAPE + "'" + _SHAPE)
+# five or more shapes in a row can cross a tile start with the chain's first
+# shape more than the halo before it (four span at most 12 bytes)
+LONG_CHAIN = re.compile("(?:'" + _SHAPE + "){5,}")
 
 
 def say(*a):
@@ -92,7 +95,7 @@ ALPHA = ["a", "A", "s", "S", "r", "e", "ª", "́", "1", ".", "/", "'", " ", "\n"
 def test_every_short_string():
     load()
     strings = ["".join(t) for n in range(6) for t in itertools.product(ALPHA, repeat=n)]
-    strings = [s for s in strings if not CHAIN.search(s)]
+    assert sum(1 for s in strings if CHAIN.search(s)) == 120
     say("o200k brute force: %d strings" % len(strings))
     check_batch(strings)
 
@@ -107,7 +110,7 @@ def test_random_multibyte_strings():
     strings = []
     while len(strings) < 40_000:
         s = "".join(rng.choice(ALPHA2) for _ in range(rng.randint(0, 40)))
-        if not CHAIN.search(s):
+        if not LONG_CHAIN.search(s):
             strings.append(s)
     say("o200k random batch: %d strings" % len(strings))
     check_batch(strings)
@@ -176,18 +179,51 @@ def test_encode_mix_1m():
     assert np.array_equal(got, want)
 
 
-def test_contraction_chain_is_reported_unsupported():
+CHAIN_TEXTS = ["a's's", "it's'll go", "x" * 3000 + "'d've", "'s's's", " 's's", "a'S'Re'll'd", "A'LL'M'T'D'S'VE",
+               "Don't'cha", "rock'n'roll's'", "3's's", "x's'sa's", "'rE's'm", "y" * 100 + "'s" * 300 + " z"]
+
+
+def _chain_edge_text(seed, tile=1024, ntiles=40):
+    """At each tile start, a chain of one to four shapes whose first shape
+    lies 0-13 bytes before it, after a letter or after a space."""
+    rng = random.Random(seed)
+    shapes = ["'s", "'S", "'t", "'m", "'d", "'re", "'Re", "'rE", "'ve", "'ll", "'LL"]
+    out = bytearray()
+    for t in range(1, ntiles):
+        chain = "".join(rng.choice(shapes) for _ in range(rng.randint(1, 4))).encode()
+        head = t * tile - rng.randint(0, min(13, len(chain) - 1))
+        while len(out) < head - 1:
+            out += rng.choice([b"ab ", b"it ", b"x1 ", b"Q ", b". ", b"\n"])
+        del out[head - 1:]
+        out += rng.choice([b"a", b" ", b"Z", b"."])
+        out += chain + rng.choice([b" ", b"x", b"'", b"!", b"\n"])
+    return bytes(out)
+
+
+def test_contraction_chains():
+    v = load()
+    texts = CHAIN_TEXTS + [_chain_edge_text(s).decode() for s in (5, 6, 7)]
+    for text in texts:
+        data = text.encode()
+        say("o200k chain: %d bytes %r" % (len(data), text[-12:]))
+        _, want = split_bytes(data, O200K)
+        assert gpu_starts(data) == want
+        got = tt.encode(dev(data)).cpu().numpy()
+        assert np.array_equal(got, np.asarray(oracle_encode(data, v, O200K, {}), dtype=np.int32))
+    check_batch(texts)
+    # a lone contraction and a quote after one
+    for text in ["it's", "'it's'", "rock'n'roll"]:
+        got = tt.encode(dev(text.encode())).cpu().numpy()
+        assert np.array_equal(got, np.asarray(oracle_encode(text.encode(), v, O200K, {}), dtype=np.int32))
+
+
+def test_long_chain_across_a_tile_start_is_reported_unsupported():
     load()
-    for text in ["a's's", "it's'll go", "x" * 3000 + "'d've"]:
-        say("o200k chain: %r" % text[-12:])
+    for text in ["x" + "'s" * 2000, " " * 1000 + "'re" * 10 + " a"]:
+        say("o200k long chain: %d bytes" % len(text))
         with pytest.raises(tt.TTError) as ei:
             tt.encode(dev(text.encode()))
         assert ei.value.code == tt.TT_EUNSUPPORTED
-    # a lone contraction and a quote after one are decided
-    for text in ["it's", "'it's'", "rock'n'roll"]:
-        v = load()
-        got = tt.encode(dev(text.encode())).cpu().numpy()
-        assert np.array_equal(got, np.asarray(oracle_encode(text.encode(), v, O200K, {}), dtype=np.int32))
 
 
 def test_sessions_are_refused():
