@@ -146,6 +146,7 @@ size_t layout(int64_t n, char* base, Work* w) {
   t.tile_cnt = (uint32_t*)take(ntiles * 4);
   t.codes = (uint8_t*)take(ntiles * TILE + 64);
   t.tile_tail = (uint32_t*)take(ntiles * 4);
+  t.tile_chain = (uint32_t*)take(ntiles * 4);
   t.flags = (uint16_t*)take(ntiles * PT_THREADS * 2);
   t.piece_start = (int32_t*)take((nn + 1) * 4);
   t.piece_cnt = (int32_t*)take(nn * 4);

@@ -169,6 +169,7 @@ struct Work {
   uint32_t* tile_cnt;    // [ntiles] pre-token starts of each tile | error bits << TILE_ERR_SHIFT
   uint8_t* codes;        // [(ntiles + 1) * TILE] cl100k/o200k-style rules: one code byte per text byte
   uint32_t* tile_tail;   // [ntiles] o200k-style rules: CR/LF/'/' tail summary of each tile
+  uint32_t* tile_chain;  // [ntiles] o200k-style rules: contraction-chain map of each tile
   uint16_t* flags;       // [ntiles * PT_THREADS] start bits of each thread's PT_CHUNK bytes
   int32_t* piece_start;  // [n + 1]
   int32_t* piece_cnt;    // [n] tokens of each piece

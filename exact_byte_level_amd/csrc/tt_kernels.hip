@@ -107,7 +107,7 @@ struct TileSmem {
   uint64_t bsw[7][17];   // cl100k/o200k-style rules: bit planes of the span's chars (64 per entry)
   uint32_t cbits[34];    // their start bits by char (tiles with non-ASCII bytes)
   int64_t seq_lo, seq_hi;
-  uint32_t carry_fwd, carry_bwd, carry_tail;
+  uint32_t carry_fwd, carry_bwd, carry_tail, carry_chain;
   int flag;
   // cl100k-style rules: the span's code bytes (by position), its chars in
   // order (code bytes) and their positions, and the tile's start bits
@@ -345,6 +345,7 @@ struct FwdOp {
     }
     return b;
   }
+  __device__ static __forceinline__ bool closed(uint32_t a) { return (a & 1u) && !(a & 2u); }
 };
 
 // Forward state for the o200k-style CR/LF/'/' tails, of the trailing run of
@@ -379,6 +380,56 @@ struct TailOp {
     }
     return r;
   }
+  __device__ static __forceinline__ bool closed(uint32_t a) { return (a & 1u) && !(a & 2u); }
+};
+
+// Contraction-chain state (o200k-style rules) of a range of chars, as a map
+// from the state before the range to the state after it.  Phases: 0 no
+// chain and the last char is no letter, 1 no chain after a letter, 2 an
+// apostrophe that may start a contraction shape, 3 / 4 that apostrophe and
+// r or v / l, 5 a whole shape; phases 2-5 also hold whether that shape
+// attaches (a chain's first shape attaches after a letter; each later one
+// attaches exactly when the one before did not).  Entry p (5 bits at 5 p):
+// bits 0-2 the phase after, bit 4 the attachment after, taken as is or, with
+// bit 3, xor the attachment before.  Phases 0 and 1 keep bits 3-4 clear.
+// Bit 30: a constant map (every entry the same, bit 3 clear); bit 31: the
+// range has chars.
+struct ChainOp {
+  static constexpr uint32_t IDENT = 0, HAS = 1u << 31, CONST = 1u << 30, REP = 0x2108421u;
+  __device__ static __forceinline__ uint32_t entry(uint32_t f, uint32_t p) { return (f >> (5u * p)) & 31u; }
+  __device__ static __forceinline__ uint32_t pack(uint32_t f) {
+    return f | HAS | ((f == (f & 31u) * REP && !(f & 8u)) ? CONST : 0u);
+  }
+  // the map of one char: idx its o200k-style class index, ss it starts a sequence
+  __device__ static __forceinline__ uint32_t elem(uint32_t idx, bool ss) {
+    const uint32_t att = ss ? 0u : 16u, t = idx & 7u;
+    if (idx == 3u) {  // an apostrophe: after a whole shape it links, unless a sequence starts
+      const uint32_t e5 = ss ? 2u : (2u | 8u | 16u);
+      return pack(2u | ((2u | att) << 5) | (2u << 10) | ((2u | att) << 15) | ((2u | att) << 20) | (e5 << 25));
+    }
+    if (idx & 16u) {  // a letter: shape letters go on; any other resets to phase 1
+      const uint32_t ea = ss ? 1u : t == 1u ? 13u : t == 2u ? 11u : t == 3u ? 12u : 1u;
+      const uint32_t er = !ss && t == 4u ? 13u : 1u, el = !ss && t == 3u ? 13u : 1u;
+      return pack(1u | (1u << 5) | (ea << 10) | (er << 15) | (el << 20) | (1u << 25));
+    }
+    return HAS | CONST;  // any other char: phase 0 from every state
+  }
+  // entry ea followed by the map b
+  __device__ static __forceinline__ uint32_t then(uint32_t ea, uint32_t b) {
+    const uint32_t eb = entry(b, ea & 7u);
+    return (eb ^ ((eb << 1) & ea & 16u)) & (ea | 0x17u);
+  }
+  __device__ static __forceinline__ uint32_t combine(uint32_t a, uint32_t b) {
+    if (!(b & HAS)) return a;
+    if (!(a & HAS)) return b;
+    if (b & CONST) return b;
+    if (a & CONST) return then(a & 31u, b) * REP | HAS | CONST;
+    uint32_t r = 0u;
+#pragma unroll
+    for (uint32_t p = 0; p < 6u; ++p) r |= then(entry(a, p), b) << (5u * p);
+    return pack(r);
+  }
+  __device__ static __forceinline__ bool closed(uint32_t a) { return (a & HAS) && (a & CONST); }
 };
 
 // Backward state, for the leading run: bit 0 has chars, bit 1 open (the run
@@ -707,7 +758,7 @@ __global__ __launch_bounds__(PT_THREADS) void k_tile_summary(const uint8_t* __re
                                                              Work w) {
   __shared__ uint16_t ascii[128];
   __shared__ uint32_t sbm[TILE / 32 + 3];  // sequence starts in [t0 - 32, t0 + TILE + 64)
-  __shared__ uint32_t red[12];
+  __shared__ uint32_t red[18];
   __shared__ uint32_t cbl[(4 + TILE) / 4];  // DeepSeek-style: code bytes of [t0 - 4, t0 + TILE)
   const int tid = (int)threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int t = blockIdx.x;
@@ -810,12 +861,37 @@ __global__ __launch_bounds__(PT_THREADS) void k_tile_summary(const uint8_t* __re
   if (PAT == 2) {
     const uint32_t wt = wave_incl_fwd<TailOp>(tv, lane);
     if (lane == 63) red[8 + wid] = wt;
+    // a contraction chain can be open at the tile's end only with an
+    // apostrophe among its last 3 chars; else the tile's chain map is the
+    // constant "no chain" (phase 1 after a letter, else 0)
+    if (tid == PT_THREADS - 1) {
+      uint32_t last = 0u;
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        if (ch[k]) last = (out >> (8 * k)) & CB_IDX;
+      const uint32_t x = d0 ^ 0x27272727u;
+      red[12] = ((x - 0x01010101u) & ~x & 0x80808080u) != 0u;
+      red[13] = ((last & 16u) ? ChainOp::REP : 0u) | ChainOp::HAS | ChainOp::CONST;
+    }
   }
   __syncthreads();
   if (tid == 0) {
     w.tile_fwd[t] = FwdOp::combine(FwdOp::combine(red[0], red[1]), FwdOp::combine(red[2], red[3]));
     w.tile_bwd[t] = BwdOp::combine(BwdOp::combine(red[4], red[5]), BwdOp::combine(red[6], red[7]));
     if (PAT == 2) w.tile_tail[t] = TailOp::combine(TailOp::combine(red[8], red[9]), TailOp::combine(red[10], red[11]));
+    if (PAT == 2 && !red[12]) w.tile_chain[t] = red[13];
+  }
+  if (PAT == 2 && red[12]) {
+    // the whole tile's chain map (the same branch in every thread)
+    uint32_t cv = ChainOp::IDENT;
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      if (ch[k]) cv = ChainOp::combine(cv, ChainOp::elem((out >> (8 * k)) & CB_IDX, (out >> (8 * k)) & CB_SS));
+    const uint32_t wc = wave_incl_fwd<ChainOp>(cv, lane);
+    if (lane == 63) red[14 + wid] = wc;
+    __syncthreads();
+    if (tid == 0)
+      w.tile_chain[t] = ChainOp::combine(ChainOp::combine(red[14], red[15]), ChainOp::combine(red[16], red[17]));
   }
 }
 
@@ -841,7 +917,7 @@ __device__ __forceinline__ uint32_t look_back(const uint32_t* __restrict__ src, 
     for (int i = PER - 1; i >= 0; --i) v = Op::combine(v, x[i]);
     const uint32_t all = (uint32_t)__builtin_amdgcn_readlane((int)wave_incl_bwd<RevOp<Op>>(v, lane), 0);
     acc = uniform(Op::combine(all, acc));
-    if ((acc & 1u) && !(acc & 2u)) break;
+    if (Op::closed(acc)) break;
     b -= 64 * per;
     per = PER;
   }
@@ -878,6 +954,9 @@ __device__ void tile_carries(const Work& w, int t, int ntiles, TileSmem& sm) {
   } else if (wid == 2 && PAT == 2) {
     const uint32_t acc = look_back<TailOp>(w.tile_tail, t, lane);
     if (lane == 0) sm.carry_tail = acc;
+  } else if (wid == 3 && PAT == 2) {
+    const uint32_t acc = look_back<ChainOp>(w.tile_chain, t, lane);
+    if (lane == 0) sm.carry_chain = acc;
   }
   __syncthreads();
 }
@@ -1232,12 +1311,13 @@ __device__ bool stage_codes(int64_t n, int64_t t0, const Work& w, TileSmem& sm, 
 // o200k-style start bits of this lane's word (one wavefront; the planes are
 // the five class-index bits, sequence start, sequence last).  lf, rb: the
 // forward / backward run states (o200k-style classes) before c_lo and from
-// e on; tl: the tail state before c_lo.  *unsup (the same in every lane):
-// the word's outcome depends on a contraction chain that began before the
-// window or on a word restart that lies before the span, which these
-// carries do not hold.
+// e on; tl: the tail state before c_lo; ch: the contraction-chain map of
+// the text before the tile.  *unsup (the same in every lane): the word's
+// outcome depends on a contraction chain whose head lies before the window
+// and which ends before the tile, or on a word restart that lies before the
+// span, which these carries do not hold.
 __device__ uint32_t o2_word_bits(const uint32_t* pl, int lane, int c_lo, int e, uint32_t lf, uint32_t rb, uint32_t tl,
-                                 bool* unsup) {
+                                 uint32_t ch, bool* unsup) {
   const uint32_t b0 = pl[0], b1 = pl[1], b2 = pl[2], b3 = pl[3], b4 = pl[4], SS = pl[5], SL = pl[6];
   const int x0 = c_lo - 32 + 32 * lane;
   const uint32_t CH = b0 | b1 | b2 | b3 | b4;
@@ -1275,10 +1355,9 @@ __device__ uint32_t o2_word_bits(const uint32_t* pl, int lane, int c_lo, int e, 
   // a chain of shapes, each right after the letters of the one before: its
   // first shape (HEAD) attaches when a letter comes before it, and every
   // later one attaches exactly when the one before did not (a word that took
-  // a contraction is over; one that did not takes the next).  So a linked
-  // shape attaches when the count of shapes from its head, itself included,
-  // is odd and the head attached, or even and it did not: P (prefix parity
-  // of the shapes) xor the head's P ^ CAND, filled along the chain's chars.
+  // a contraction is over; one that did not takes the next).  So a shape's
+  // attachment is P (prefix parity of the shapes) xor a base that is the
+  // same along the chain: the head's P ^ CAND, filled along the chain's chars.
   const uint32_t CSX = CS1 | CS2;
   const uint32_t LNK = CSX & LINK & ~SS;
   const uint32_t HEAD = CSX & ~LNK;
@@ -1291,15 +1370,35 @@ __device__ uint32_t o2_word_bits(const uint32_t* pl, int lane, int c_lo, int e, 
   P ^= P << 16;
   if (__popcll(__ballot(__popc(CSX) & 1) & ((1ull << lane) - 1ull)) & 1) P = ~P;
   // a shape in the window's first three chars may link to one before the
-  // window, unless the window starts a sequence: chains from there are unknown
+  // window, unless the window starts a sequence: heads there are not known
   const bool seq0 = __ballot((SS & bs_range(x0, 0, 1)) != 0u) != 0ull;
   const uint32_t EDGE = seq0 ? 0u : bs_range(x0, -(1 << 20), 3);
-  const uint32_t HC = HEAD & ~EDGE;
-  const uint32_t S1 = HC & (P ^ CAND);
-  const uint32_t F = bs_fill_up((RC & ~HEAD) | S1, S1, lane) | S1;
-  const uint32_t SU0 = RC & EDGE & ~bs_up<1>(RC);
+  uint32_t HC = HEAD & ~EDGE;
+  uint32_t S1 = HC & (P ^ CAND);
+  // a chain that reaches the tile start with its head before the window:
+  // the carry (the chain state at the tile start) holds the attachment of
+  // its last shape before the tile, which fixes the base for the whole run
+  // of chain chars that ends at c_lo - 1 (lane 0, bit 31)
+  uint32_t SEED = 0u;
+  if ((ChainOp::entry(ch, 0u) & 7u) >= 2u) {
+    const uint32_t r0 = (uint32_t)__builtin_amdgcn_readlane((int)RC, 0);
+    const uint32_t h0 = (uint32_t)__builtin_amdgcn_readlane((int)HC, 0);
+    const uint32_t g0 = (uint32_t)__builtin_amdgcn_readlane((int)EDGE, 0);
+    if (r0 >> 31) {
+      const int z = 31 - __clz((int)~r0);  // the char before that run (chars before the text are 0)
+      if (!(h0 & (~0u << (z + 1))) && ((g0 >> (z + 1)) & 1u)) {
+        const uint32_t p0 = (uint32_t)__builtin_amdgcn_readlane((int)P, 0);
+        SEED = lane == 0 ? 1u << (z + 1) : 0u;
+        if (((p0 >> 31) ^ (ChainOp::entry(ch, 0u) >> 4)) & 1u) S1 |= SEED;
+      }
+    }
+  }
+  HC |= SEED;
+  const uint32_t F = bs_fill_up((RC & ~HC) | S1, S1, lane) | S1;
+  // chains whose head is not known: from a run start in the first three chars
+  const uint32_t SU0 = RC & EDGE & ~bs_up<1>(RC) & ~SEED;
   const uint32_t UNK = bs_fill_up(RC & ~HC, SU0, lane) | SU0;
-  const uint32_t ATT = CAND & (~LINK | ((P ^ F) & ~UNK));
+  const uint32_t ATT = (CAND | (CSX & EDGE & ~UNK)) & ((~UNK & (P ^ F)) | (UNK & ~LINK));
   const uint32_t IC = bs_up<1>(ATT) | bs_up<2>(ATT & CS2);  // letters of an attached contraction
   const uint32_t AFTER = LI & ~SS & (bs_up<2>(ATT & CS1) | bs_up<3>(ATT & CS2));
   // case rules inside a letter run: PREVW, the last cased char of the word
@@ -1337,11 +1436,16 @@ __device__ uint32_t o2_word_bits(const uint32_t* pl, int lane, int c_lo, int e, 
   const uint32_t BWN = WN & ~Wp & ~Op;
   const uint32_t BWS = WS & (~Wp | (bs_up<1>(WN) & (ENDS | bs_up<1>(ABSO))) | (bs_up<1>(WS) & ~SL & ~bs_dn<1>(W)));
   const uint32_t own = bs_range(x0, c_lo, e);
-  // undecided cases: a contraction chain near the own chars whose head may
-  // lie before the window, or an upper-case own char whose word may restart
-  // before the span
-  const uint32_t near = bs_range(x0, c_lo - 4, e + 4);
-  const bool chain = __ballot((CAND & LNK & UNK & near) != 0u) != 0ull;
+  // undecided cases: a shape of a chain whose head is not known, whose
+  // attachment reaches the own chars (its chars or the char after it from
+  // c_lo on, or a run of Lm/Lo/marks from the char after it to c_lo), or an
+  // upper-case own char whose word may restart before the span
+  const uint32_t ULU = CSX & UNK & (LNK | EDGE);
+  const uint32_t AQ = (bs_up<2>(ULU & CS1) | bs_up<3>(ULU & CS2)) & BT & ~SS;
+  const uint32_t BR = bs_fill_up(BT & ~SS, AQ, lane) | AQ;
+  const uint32_t reach = (ULU & ((CS1 & bs_range(x0, c_lo - 2, e)) | (CS2 & bs_range(x0, c_lo - 3, e)))) |
+                         (BR & bs_range(x0, c_lo - 1, e));
+  const bool chain = __ballot(reach != 0u) != 0ull;
   bool restart = false;
   if (amb) {
     // the run from the span's first char reaches the first own upper-case
@@ -1477,7 +1581,8 @@ __device__ uint32_t pat_bits(TileSmem& sm, uint32_t* cnt, bool* unsup) {
     const uint32_t B = PAT == 3 ? ds_word_bits(pl, lane, c_lo, c_lo + n_own, uniform(sm.carry_fwd),
                                                uniform(sm.carry_bwd))
                      : PAT == 2 ? o2_word_bits(pl, lane, c_lo, c_lo + n_own, uniform(sm.carry_fwd),
-                                               uniform(sm.carry_bwd), uniform(sm.carry_tail), &uns)
+                                               uniform(sm.carry_bwd), uniform(sm.carry_tail),
+                                               uniform(sm.carry_chain), &uns)
                                 : cl_word_bits(pl, lane, c_lo, c_lo + n_own, uniform(sm.carry_fwd),
                                                uniform(sm.carry_bwd));
     const uint32_t tot = wave_incl_fwd<SumOp>((uint32_t)__popc(B), lane);

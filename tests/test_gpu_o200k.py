@@ -7,10 +7,11 @@ multibyte strings, runs that cross tiles for each fact carried between tiles
 (digit groups, whitespace before CR/LF, CR/LF after "other" chars, CR/LF/'/'
 tails, upper-case runs to the end of a word, Lm/Lo runs after a lower-case
 letter), contraction chains (back-to-back suffixes, whose attachment
-alternates from the chain's first suffix) inside a tile and across tile
-starts, and a 1M-char encode.  A chain whose first suffix lies more than the
-halo before a tile start is the case the GPU rules leave undecided: the call
-reports TT_EUNSUPPORTED, never a wrong split.
+alternates from the chain's first suffix) inside a tile, across tile starts
+and over whole tiles, and a 1M-char encode.  A chain that ends before a tile
+start with its first suffix out of the tile's view, followed by an Lm/Lo/mark
+run into the tile, is a case the GPU rules leave undecided: the call reports
+TT_EUNSUPPORTED, never a wrong split.
 """
 import itertools
 import os
@@ -32,9 +33,6 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 # an apostrophe with a contraction shape after it, right after another one
 _SHAPE = "(?:[sStTmMdD]|[rRvV][eE]|[lL][lL])"
 CHAIN = re.compile("'" + _SHAPE + "'" + _SHAPE)
-# five or more shapes in a row can cross a tile start with the chain's first
-# shape more than the halo before it (four span at most 12 bytes)
-LONG_CHAIN = re.compile("(?:'" + _SHAPE + "){5,}")
 
 
 def say(*a):
@@ -110,8 +108,7 @@ def test_random_multibyte_strings():
     strings = []
     while len(strings) < 40_000:
         s = "".join(rng.choice(ALPHA2) for _ in range(rng.randint(0, 40)))
-        if not LONG_CHAIN.search(s):
-            strings.append(s)
+        strings.append(s)
     say("o200k random batch: %d strings" % len(strings))
     check_batch(strings)
 
@@ -183,15 +180,18 @@ CHAIN_TEXTS = ["a's's", "it's'll go", "x" * 3000 + "'d've", "'s's's", " 's's", "
                "Don't'cha", "rock'n'roll's'", "3's's", "x's'sa's", "'rE's'm", "y" * 100 + "'s" * 300 + " z"]
 
 
-def _chain_edge_text(seed, tile=1024, ntiles=40):
-    """At each tile start, a chain of one to four shapes whose first shape
-    lies 0-13 bytes before it, after a letter or after a space."""
+def _chain_edge_text(seed, units=(1, 4), tile=1024, ntiles=40):
+    """At each tile start, a chain of shapes (their count drawn from units)
+    whose first shape lies before it, after a letter or a space, so that the
+    tile start falls anywhere in the chain."""
     rng = random.Random(seed)
     shapes = ["'s", "'S", "'t", "'m", "'d", "'re", "'Re", "'rE", "'ve", "'ll", "'LL"]
     out = bytearray()
     for t in range(1, ntiles):
-        chain = "".join(rng.choice(shapes) for _ in range(rng.randint(1, 4))).encode()
-        head = t * tile - rng.randint(0, min(13, len(chain) - 1))
+        chain = "".join(rng.choice(shapes) for _ in range(rng.randint(*units))).encode()
+        head = t * tile - rng.randint(0, len(chain) - 1)
+        if head - 1 <= len(out):
+            continue
         while len(out) < head - 1:
             out += rng.choice([b"ab ", b"it ", b"x1 ", b"Q ", b". ", b"\n"])
         del out[head - 1:]
@@ -200,16 +200,20 @@ def _chain_edge_text(seed, tile=1024, ntiles=40):
     return bytes(out)
 
 
+def _check_text(text, v):
+    data = text.encode()
+    say("o200k chain: %d bytes %r" % (len(data), text[-12:]))
+    _, want = split_bytes(data, O200K)
+    assert gpu_starts(data) == want
+    got = tt.encode(dev(data)).cpu().numpy()
+    assert np.array_equal(got, np.asarray(oracle_encode(data, v, O200K, {}), dtype=np.int32))
+
+
 def test_contraction_chains():
     v = load()
     texts = CHAIN_TEXTS + [_chain_edge_text(s).decode() for s in (5, 6, 7)]
     for text in texts:
-        data = text.encode()
-        say("o200k chain: %d bytes %r" % (len(data), text[-12:]))
-        _, want = split_bytes(data, O200K)
-        assert gpu_starts(data) == want
-        got = tt.encode(dev(data)).cpu().numpy()
-        assert np.array_equal(got, np.asarray(oracle_encode(data, v, O200K, {}), dtype=np.int32))
+        _check_text(text, v)
     check_batch(texts)
     # a lone contraction and a quote after one
     for text in ["it's", "'it's'", "rock'n'roll"]:
@@ -217,13 +221,31 @@ def test_contraction_chains():
         assert np.array_equal(got, np.asarray(oracle_encode(text.encode(), v, O200K, {}), dtype=np.int32))
 
 
-def test_long_chain_across_a_tile_start_is_reported_unsupported():
+def test_long_chains_across_tiles():
+    """Chains whose first shape lies tiles before the tile start: the chain
+    state is carried between tiles."""
+    v = load()
+    texts = ["x" + "'s" * 2000, " " * 1000 + "'re" * 10 + " a", "Q" + "'d're'LL" * 700 + "x",
+             "'" + "s'" * 3000, " " * 1020 + "'s" * 20 + "A", "y" * 1015 + "'rE" * 5 + "'m" * 900 + "ª" * 9 + "Ab"]
+    texts += [_chain_edge_text(s, units=(5, 40)).decode() for s in (8, 9)]
+    texts += [_chain_edge_text(s, units=(200, 900), ntiles=24).decode() for s in (10,)]
+    for text in texts:
+        _check_text(text, v)
+    # the same texts as one batch: chains cut by sequence starts
+    check_batch(texts + ["'s's", "x's'" + "d's" * 700, "'ll" * 400])
+
+
+def test_chain_end_then_lm_lo_run_into_a_tile_is_reported_unsupported():
+    """A chain that ends just before a tile's halo with its first shape out of
+    view, then an Lo run up to the tile start and an upper-case letter: the
+    letter's split depends on whether the chain's last shape attached."""
     load()
-    for text in ["x" + "'s" * 2000, " " * 1000 + "'re" * 10 + " a"]:
-        say("o200k long chain: %d bytes" % len(text))
-        with pytest.raises(tt.TTError) as ei:
-            tt.encode(dev(text.encode()))
-        assert ei.value.code == tt.TT_EUNSUPPORTED
+    text = "y " * 484 + "yx" + "'s" * 20 + "ª" * 7 + "Ab"
+    data = text.encode()
+    assert data.index(b"\xc2\xaa") == 1010 and len(data) == 1026
+    with pytest.raises(tt.TTError) as ei:
+        tt.encode(dev(data))
+    assert ei.value.code == tt.TT_EUNSUPPORTED
 
 
 def test_sessions_are_refused():
