@@ -319,17 +319,12 @@ __device__ bool load_tile(const uint8_t* __restrict__ bytes, int64_t n, const in
 // Forward state of a range of chars, for the trailing run:
 //   bit 0 has chars, bit 1 open (the run reaches the range start and no
 //   sequence starts there), bits 2-4 class, bits 5-7 class of the char before
-//   the run (C_NONE at a sequence start), bits 8-9 run length mod 3, bit 10
-//   the char before the run is an ASCII letter that can end a contraction
-//   suffix (s t m d e l, either case), bit 11 the range's last char is one.
+//   the run (C_NONE at a sequence start), bits 8-9 run length mod 3.
 struct FwdOp {
   static constexpr uint32_t IDENT = 0;
-  static constexpr uint32_t CB_CL = 1u << 10, LAST_CL = 1u << 11;
   __device__ static __forceinline__ uint32_t elem(uint32_t code) {
     uint32_t open = (code & K_SEQ_START) ? 0u : 2u;
-    const uint32_t lt = (code >> K_LETTER_SHIFT) & 15u;  // 0 unless an ASCII letter
-    const bool cl = (0x1D6u >> lt) & 1u;                 // LT_S T E M L D
-    return 1u | open | (cls_of(code) << 2) | (1u << 8) | (cl ? LAST_CL : 0u);
+    return 1u | open | (cls_of(code) << 2) | (1u << 8);
   }
   __device__ static __forceinline__ uint32_t combine(uint32_t a, uint32_t b) {
     if (!(b & 1u)) return a;
@@ -339,9 +334,9 @@ struct FwdOp {
       if (ca == cb) {
         uint32_t len = ((a >> 8) & 3u) + ((b >> 8) & 3u);  // each < 3: the sum mod 3 by one subtraction
         len -= len >= 3u ? 3u : 0u;
-        return (a & (0xFFu | CB_CL)) | (len << 8) | (b & LAST_CL);
+        return (a & 0xFFu) | (len << 8);
       }
-      return 1u | (cb << 2) | (ca << 5) | (b & 0x300u) | ((a & LAST_CL) ? CB_CL : 0u) | (b & LAST_CL);
+      return 1u | (cb << 2) | (ca << 5) | (b & 0x300u);
     }
     return b;
   }
@@ -387,49 +382,54 @@ struct TailOp {
 // from the state before the range to the state after it.  Phases: 0 no
 // chain and the last char is no letter, 1 no chain after a letter, 2 an
 // apostrophe that may start a contraction shape, 3 / 4 that apostrophe and
-// r or v / l, 5 a whole shape; phases 2-5 also hold whether that shape
+// r or v / l, 5 a whole shape, 6 inside a run of Lm/Lo/marks that began
+// right after a whole shape; phases 2-6 also hold whether that shape
 // attaches (a chain's first shape attaches after a letter; each later one
-// attaches exactly when the one before did not).  Entry p (5 bits at 5 p):
-// bits 0-2 the phase after, bit 4 the attachment after, taken as is or, with
-// bit 3, xor the attachment before.  Phases 0 and 1 keep bits 3-4 clear.
-// Bit 30: a constant map (every entry the same, bit 3 clear); bit 31: the
-// range has chars.
+// attaches exactly when the one before did not).  Entry p (5 bits at 5 p,
+// phases 0-5): bits 0-2 the phase after, bit 4 the attachment after, taken
+// as is or, with bit 3, xor the attachment before; phases 0 and 1 keep bits
+// 3-4 clear.  Phase 6 needs no entry: it stays 6 over a range of such marks
+// and letters only (bit 30) and otherwise goes where phase 1 goes.  Bit 31:
+// the range has chars.
 struct ChainOp {
-  static constexpr uint32_t IDENT = 0, HAS = 1u << 31, CONST = 1u << 30, REP = 0x2108421u;
+  static constexpr uint32_t IDENT = 0, HAS = 1u << 31, ALLB = 1u << 30, REP = 0x2108421u;
   __device__ static __forceinline__ uint32_t entry(uint32_t f, uint32_t p) { return (f >> (5u * p)) & 31u; }
-  __device__ static __forceinline__ uint32_t pack(uint32_t f) {
-    return f | HAS | ((f == (f & 31u) * REP && !(f & 8u)) ? CONST : 0u);
+  __device__ static __forceinline__ bool constant(uint32_t f) {
+    return (f & 0x3FFFFFFFu) == (f & 31u) * REP && !(f & 8u);
   }
   // the map of one char: idx its o200k-style class index, ss it starts a sequence
   __device__ static __forceinline__ uint32_t elem(uint32_t idx, bool ss) {
     const uint32_t att = ss ? 0u : 16u, t = idx & 7u;
     if (idx == 3u) {  // an apostrophe: after a whole shape it links, unless a sequence starts
       const uint32_t e5 = ss ? 2u : (2u | 8u | 16u);
-      return pack(2u | ((2u | att) << 5) | (2u << 10) | ((2u | att) << 15) | ((2u | att) << 20) | (e5 << 25));
+      return HAS | 2u | ((2u | att) << 5) | (2u << 10) | ((2u | att) << 15) | ((2u | att) << 20) | (e5 << 25);
     }
+    if (idx == 23u && !ss)  // Lm/Lo/mark: after a whole shape, phase 6 keeps its attachment
+      return HAS | ALLB | (1u * (REP & 0x1FFFFFu)) | (14u << 25);
     if (idx & 16u) {  // a letter: shape letters go on; any other resets to phase 1
       const uint32_t ea = ss ? 1u : t == 1u ? 13u : t == 2u ? 11u : t == 3u ? 12u : 1u;
       const uint32_t er = !ss && t == 4u ? 13u : 1u, el = !ss && t == 3u ? 13u : 1u;
-      return pack(1u | (1u << 5) | (ea << 10) | (er << 15) | (el << 20) | (1u << 25));
+      return HAS | 1u | (1u << 5) | (ea << 10) | (er << 15) | (el << 20) | (1u << 25);
     }
-    return HAS | CONST;  // any other char: phase 0 from every state
+    return HAS;  // any other char: phase 0 from every state
   }
   // entry ea followed by the map b
   __device__ static __forceinline__ uint32_t then(uint32_t ea, uint32_t b) {
-    const uint32_t eb = entry(b, ea & 7u);
+    const uint32_t pa = ea & 7u;
+    const uint32_t eb = pa == 6u ? ((b & ALLB) ? 14u : entry(b, 1u)) : entry(b, pa);
     return (eb ^ ((eb << 1) & ea & 16u)) & (ea | 0x17u);
   }
   __device__ static __forceinline__ uint32_t combine(uint32_t a, uint32_t b) {
     if (!(b & HAS)) return a;
     if (!(a & HAS)) return b;
-    if (b & CONST) return b;
-    if (a & CONST) return then(a & 31u, b) * REP | HAS | CONST;
+    if (constant(b)) return b;
+    if (constant(a)) return then(a & 31u, b) * REP | HAS;
     uint32_t r = 0u;
 #pragma unroll
     for (uint32_t p = 0; p < 6u; ++p) r |= then(entry(a, p), b) << (5u * p);
-    return pack(r);
+    return r | HAS | (a & b & ALLB);
   }
-  __device__ static __forceinline__ bool closed(uint32_t a) { return (a & HAS) && (a & CONST); }
+  __device__ static __forceinline__ bool closed(uint32_t a) { return (a & HAS) && constant(a); }
 };
 
 // Backward state, for the leading run: bit 0 has chars, bit 1 open (the run
@@ -861,17 +861,18 @@ __global__ __launch_bounds__(PT_THREADS) void k_tile_summary(const uint8_t* __re
   if (PAT == 2) {
     const uint32_t wt = wave_incl_fwd<TailOp>(tv, lane);
     if (lane == 63) red[8 + wid] = wt;
-    // a contraction chain can be open at the tile's end only with an
-    // apostrophe among its last 3 chars; else the tile's chain map is the
-    // constant "no chain" (phase 1 after a letter, else 0)
+    // the chain state at the tile's end can be other than "no chain" only
+    // with an apostrophe among its last 3 chars or an Lm/Lo/mark as its last
+    // char; else the tile's chain map is that constant (phase 1 after a
+    // letter, else 0)
     if (tid == PT_THREADS - 1) {
       uint32_t last = 0u;
 #pragma unroll
       for (int k = 0; k < 4; ++k)
         if (ch[k]) last = (out >> (8 * k)) & CB_IDX;
       const uint32_t x = d0 ^ 0x27272727u;
-      red[12] = ((x - 0x01010101u) & ~x & 0x80808080u) != 0u;
-      red[13] = ((last & 16u) ? ChainOp::REP : 0u) | ChainOp::HAS | ChainOp::CONST;
+      red[12] = (((x - 0x01010101u) & ~x & 0x80808080u) != 0u) || last == 23u;
+      red[13] = ((last & 16u) ? ChainOp::REP : 0u) | ChainOp::HAS;
     }
   }
   __syncthreads();
@@ -1313,9 +1314,8 @@ __device__ bool stage_codes(int64_t n, int64_t t0, const Work& w, TileSmem& sm, 
 // forward / backward run states (o200k-style classes) before c_lo and from
 // e on; tl: the tail state before c_lo; ch: the contraction-chain map of
 // the text before the tile.  *unsup (the same in every lane): the word's
-// outcome depends on a contraction chain whose head lies before the window
-// and which ends before the tile, or on a word restart that lies before the
-// span, which these carries do not hold.
+// outcome depends on a contraction chain whose head these carries do not
+// fix (a check: the chain map covers every such chain).
 __device__ uint32_t o2_word_bits(const uint32_t* pl, int lane, int c_lo, int e, uint32_t lf, uint32_t rb, uint32_t tl,
                                  uint32_t ch, bool* unsup) {
   const uint32_t b0 = pl[0], b1 = pl[1], b2 = pl[2], b3 = pl[3], b4 = pl[4], SS = pl[5], SL = pl[6];
@@ -1379,8 +1379,9 @@ __device__ uint32_t o2_word_bits(const uint32_t* pl, int lane, int c_lo, int e, 
   // the carry (the chain state at the tile start) holds the attachment of
   // its last shape before the tile, which fixes the base for the whole run
   // of chain chars that ends at c_lo - 1 (lane 0, bit 31)
+  const uint32_t cst = ChainOp::entry(ch, 0u);  // (the text starts in phase 0)
   uint32_t SEED = 0u;
-  if ((ChainOp::entry(ch, 0u) & 7u) >= 2u) {
+  if ((cst & 7u) - 2u <= 3u) {
     const uint32_t r0 = (uint32_t)__builtin_amdgcn_readlane((int)RC, 0);
     const uint32_t h0 = (uint32_t)__builtin_amdgcn_readlane((int)HC, 0);
     const uint32_t g0 = (uint32_t)__builtin_amdgcn_readlane((int)EDGE, 0);
@@ -1389,7 +1390,7 @@ __device__ uint32_t o2_word_bits(const uint32_t* pl, int lane, int c_lo, int e, 
       if (!(h0 & (~0u << (z + 1))) && ((g0 >> (z + 1)) & 1u)) {
         const uint32_t p0 = (uint32_t)__builtin_amdgcn_readlane((int)P, 0);
         SEED = lane == 0 ? 1u << (z + 1) : 0u;
-        if (((p0 >> 31) ^ (ChainOp::entry(ch, 0u) >> 4)) & 1u) S1 |= SEED;
+        if (((p0 >> 31) ^ (cst >> 4)) & 1u) S1 |= SEED;
       }
     }
   }
@@ -1401,18 +1402,24 @@ __device__ uint32_t o2_word_bits(const uint32_t* pl, int lane, int c_lo, int e, 
   const uint32_t ATT = (CAND | (CSX & EDGE & ~UNK)) & ((~UNK & (P ^ F)) | (UNK & ~LINK));
   const uint32_t IC = bs_up<1>(ATT) | bs_up<2>(ATT & CS2);  // letters of an attached contraction
   const uint32_t AFTER = LI & ~SS & (bs_up<2>(ATT & CS1) | bs_up<3>(ATT & CS2));
+  // the run of Lm/Lo/marks (no sequence start in it) that ends at c_lo - 1,
+  // if any: the carried chain state says whether it began right after a
+  // whole shape that attached, so whether its first char restarts the word,
+  // also where that shape or the run's start lies before the window
+  uint32_t AFT = AFTER;
+  const uint32_t bn0 = (uint32_t)__builtin_amdgcn_readlane((int)(BT & ~SS), 0);
+  if (bn0 >> 31) {
+    const uint32_t qb = 1u << (32 - __clz((int)~bn0));  // the run's first char (chars before the text are 0)
+    if (lane == 0) AFT = (AFTER & ~qb) | (((cst & 7u) == 6u && (cst & 16u)) ? qb : 0u);
+  }
   // case rules inside a letter run: PREVW, the last cased char of the word
   // before this char is lower case (Lm/Lo/marks carry it; a restart after a
   // contraction cuts it)
-  const uint32_t RB = BT & ~AFTER & ~SS;
+  const uint32_t RB = BT & ~AFT & ~SS;
   uint32_t SB = RB & bs_up<1>(LW);
-  bool amb = false;
   if ((lf & 1u) && ((lf >> 2) & 7u) == C_L2B && ((lf >> 5) & 7u) == C_L) {
     // an Lm/Lo/mark run that began before the span, after a lower-case letter
     SB |= RB & X0;
-    // ... which might be a contraction's last letter (then the run restarts
-    // the word): undecided if the run covers the whole left context
-    amb = (lf & FwdOp::CB_CL) != 0u;
   }
   const uint32_t LWB = bs_fill_up(RB, SB, lane);
   const uint32_t PREVW = bs_up<1>(LW | LWB);
@@ -1436,29 +1443,12 @@ __device__ uint32_t o2_word_bits(const uint32_t* pl, int lane, int c_lo, int e, 
   const uint32_t BWN = WN & ~Wp & ~Op;
   const uint32_t BWS = WS & (~Wp | (bs_up<1>(WN) & (ENDS | bs_up<1>(ABSO))) | (bs_up<1>(WS) & ~SL & ~bs_dn<1>(W)));
   const uint32_t own = bs_range(x0, c_lo, e);
-  // undecided cases: a shape of a chain whose head is not known, whose
-  // attachment reaches the own chars (its chars or the char after it from
-  // c_lo on, or a run of Lm/Lo/marks from the char after it to c_lo), or an
-  // upper-case own char whose word may restart before the span
+  // undecided: a shape of a chain whose head is not known whose own chars
+  // or next char lie from c_lo on.  The carried chain state covers every
+  // chain that reaches c_lo - 1, so this does not arise; it stays a check.
   const uint32_t ULU = CSX & UNK & (LNK | EDGE);
-  const uint32_t AQ = (bs_up<2>(ULU & CS1) | bs_up<3>(ULU & CS2)) & BT & ~SS;
-  const uint32_t BR = bs_fill_up(BT & ~SS, AQ, lane) | AQ;
-  const uint32_t reach = (ULU & ((CS1 & bs_range(x0, c_lo - 2, e)) | (CS2 & bs_range(x0, c_lo - 3, e)))) |
-                         (BR & bs_range(x0, c_lo - 1, e));
-  const bool chain = __ballot(reach != 0u) != 0ull;
-  bool restart = false;
-  if (amb) {
-    // the run from the span's first char reaches the first own upper-case
-    // char that takes PREVW from it
-    const uint32_t notb = CH & ~BT;
-    const uint64_t m = __ballot(notb != 0u);
-    const int l1 = m ? __ffsll((unsigned long long)m) - 1 : 64;
-    const uint32_t w1 = (uint32_t)__builtin_amdgcn_readlane((int)notb, l1 < 64 ? l1 : 0);
-    const uint32_t u1 = (uint32_t)__builtin_amdgcn_readlane((int)UC, l1 < 64 ? l1 : 0);
-    const int first = l1 < 64 ? c_lo - 32 + 32 * l1 + (__ffs((int)w1) - 1) : (1 << 20);
-    restart = first >= c_lo && first < e && ((u1 >> (first - (c_lo - 32 + 32 * l1))) & 1u);
-  }
-  *unsup = chain || restart;
+  const uint32_t reach = ULU & ((CS1 & bs_range(x0, c_lo - 2, e)) | (CS2 & bs_range(x0, c_lo - 3, e)));
+  *unsup = __ballot(reach != 0u) != 0ull;
   return CH & (SS | BN | BL_IN | BL_ST | BO | BWN | BWS) & own;
 }
 

@@ -8,10 +8,8 @@ multibyte strings, runs that cross tiles for each fact carried between tiles
 tails, upper-case runs to the end of a word, Lm/Lo runs after a lower-case
 letter), contraction chains (back-to-back suffixes, whose attachment
 alternates from the chain's first suffix) inside a tile, across tile starts
-and over whole tiles, and a 1M-char encode.  A chain that ends before a tile
-start with its first suffix out of the tile's view, followed by an Lm/Lo/mark
-run into the tile, is a case the GPU rules leave undecided: the call reports
-TT_EUNSUPPORTED, never a wrong split.
+and over whole tiles, Lm/Lo/mark runs into a tile right after a contraction,
+and a 1M-char encode.
 """
 import itertools
 import os
@@ -235,17 +233,37 @@ def test_long_chains_across_tiles():
     check_batch(texts + ["'s's", "x's'" + "d's" * 700, "'ll" * 400])
 
 
-def test_chain_end_then_lm_lo_run_into_a_tile_is_reported_unsupported():
-    """A chain that ends just before a tile's halo with its first shape out of
-    view, then an Lo run up to the tile start and an upper-case letter: the
-    letter's split depends on whether the chain's last shape attached."""
-    load()
-    text = "y " * 484 + "yx" + "'s" * 20 + "ª" * 7 + "Ab"
-    data = text.encode()
-    assert data.index(b"\xc2\xaa") == 1010 and len(data) == 1026
-    with pytest.raises(tt.TTError) as ei:
-        tt.encode(dev(data))
-    assert ei.value.code == tt.TT_EUNSUPPORTED
+def test_mark_runs_after_contractions_across_tiles():
+    """An Lm/Lo/mark run that reaches a tile start right after a contraction:
+    whether the contraction attached (then the run restarts the word) decides
+    the split of an upper-case letter after the run.  The run's start, the
+    contraction or its chain's head may lie before the tile's view."""
+    v = load()
+    texts = []
+    for lead in ["it's", "a's's", "its", "x'S", "x're're", "It'd", "I'm'", "x'LL'd"]:
+        for run in ["中" * 600, "ª" * 700, "́" * 530, "ª" * 7, "ʰ" * 3]:
+            for pad in (0, 1, 5, 1000):
+                texts.append("y " * pad + lead + run + "Ab")
+    # a chain that ends just before a tile's halo, its head out of view, then
+    # an Lo run up to the tile start: both parities of the chain
+    for units in (19, 20):
+        t = "y " * 484 + "yx" + "'s" * 20 + "ª" * 7 + "Ab"
+        texts.append(t if units == 20 else t.replace("yx'", "yx''", 1))
+    for text in texts:
+        _check_text(text, v)
+    check_batch(texts)
+
+
+def test_random_chain_and_mark_text():
+    """A long random text of contraction shapes, apostrophes, Lm/Lo/marks,
+    case runs and separators: every tile start falls somewhere random in it."""
+    v = load()
+    toks = ["'s", "'re", "'ll", "'d", "'S", "'LL", "'Ve", "'", "a", "A", "s", "e", "l", "中", "ª", "́", "ʰ",
+            " ", "x", "\n", "1", "AB", "Ab", ".", "y's"]
+    for seed in (1, 2):
+        rng = random.Random(seed)
+        text = "".join(rng.choice(toks) for _ in range(90_000))
+        _check_text(text, v)
 
 
 def test_sessions_are_refused():
