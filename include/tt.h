@@ -40,12 +40,11 @@ extern "C" {
 #define TT_EOFFSETS   -7  /* batch offsets not monotone / not ending at n (device-side) */
 #define TT_ETOOBIG    -8  /* size beyond the library's limits or the tt_reserve size */
 #define TT_ESTALE     -9  /* tokenizer replaced since the session was reset (sessions below) */
-#define TT_EUNSUPPORTED -10 /* o200k-style rules: the input holds a case the GPU rules do not
-                              decide (device-side): a run of Lm/Lo/marks that reaches a 1 KiB
-                              tile start right after the end of a chain of back-to-back
-                              contraction suffixes begun more than ~16 bytes before the tile, or
-                              an upper-case letter after a run of Lm/Lo/marks that crosses a
-                              tile start right after a letter that can end a contraction */
+#define TT_EUNSUPPORTED -10 /* o200k-style rules: a device-side check that every contraction
+                              chain's attachment was fixed where it decides a split failed.  The
+                              carried chain state covers every chain, so no input is known to
+                              reach it; it stays so that such a case could never pass as a
+                              wrong split */
 
 #define TT_PATTERN_GPT2   0  /* GPT-2-style rules: lower-case contractions, ' ?letters', ' ?digits',
                                 ' ?other', whitespace with the not-followed-by-non-space rule */
