@@ -861,18 +861,36 @@ __global__ __launch_bounds__(PT_THREADS) void k_tile_summary(const uint8_t* __re
   if (PAT == 2) {
     const uint32_t wt = wave_incl_fwd<TailOp>(tv, lane);
     if (lane == 63) red[8 + wid] = wt;
-    // the chain state at the tile's end can be other than "no chain" only
-    // with an apostrophe among its last 3 chars or an Lm/Lo/mark as its last
-    // char; else the tile's chain map is that constant (phase 1 after a
-    // letter, else 0)
-    if (tid == PT_THREADS - 1) {
+    // the tile's contraction-chain map.  The state at the tile's end can be
+    // other than "no chain" only with an apostrophe among its last 3 chars
+    // or an Lm/Lo/mark as its last char; else the map is that constant
+    // (phase 1 after a letter, else 0).  Otherwise the last wavefront's map
+    // of its 256 bytes, when constant (any char that resets the state, as
+    // text between chains has), is the tile's; only a tile whose last 256
+    // bytes carry a chain state through takes the whole tile's scan below.
+    if (wid == PT_THREADS / 64 - 1) {
       uint32_t last = 0u;
 #pragma unroll
       for (int k = 0; k < 4; ++k)
         if (ch[k]) last = (out >> (8 * k)) & CB_IDX;
       const uint32_t x = d0 ^ 0x27272727u;
-      red[12] = (((x - 0x01010101u) & ~x & 0x80808080u) != 0u) || last == 23u;
-      red[13] = ((last & 16u) ? ChainOp::REP : 0u) | ChainOp::HAS;
+      const bool open = lane == 63 && ((((x - 0x01010101u) & ~x & 0x80808080u) != 0u) || last == 23u);
+      const uint32_t l63 = (uint32_t)__builtin_amdgcn_readlane((int)last, 63);
+      uint32_t m = ((l63 & 16u) ? ChainOp::REP : 0u) | ChainOp::HAS;
+      bool whole = false;
+      if (__ballot(open)) {
+        uint32_t cv = ChainOp::IDENT;
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+          if (ch[k]) cv = ChainOp::combine(cv, ChainOp::elem((out >> (8 * k)) & CB_IDX, (out >> (8 * k)) & CB_SS));
+        const uint32_t m3 = (uint32_t)__builtin_amdgcn_readlane((int)wave_incl_fwd<ChainOp>(cv, lane), 63);
+        if (ChainOp::closed(m3)) m = m3;
+        else whole = true;
+      }
+      if (lane == 0) {
+        red[12] = whole;
+        red[13] = m;
+      }
     }
   }
   __syncthreads();
