@@ -731,12 +731,13 @@ __device__ __forceinline__ uint32_t code_byte(uint32_t code) {
 
 // First index s in [0, cnt) with a[s] >= v (cnt if none), by one wavefront:
 // 64 probes per step, so a step narrows the range 64-fold.
-__device__ int64_t wave_lower_bound(const int64_t* __restrict__ a, int64_t cnt, int64_t v, int lane) {
+template <typename T>
+__device__ int64_t wave_lower_bound(const T* __restrict__ a, int64_t cnt, int64_t v, int lane) {
   int64_t lo = 0, hi = cnt;  // the answer lies in [lo, hi]
   while (hi > lo) {
     const int64_t step = (hi - lo + 63) / 64;
     const int64_t q = lo + step * lane;
-    const uint64_t m = __ballot(q < hi && a[q] < v);  // lanes 0 .. c - 1 (a is sorted)
+    const uint64_t m = __ballot(q < hi && (int64_t)a[q] < v);  // lanes 0 .. c - 1 (a is sorted)
     const int64_t c = __popcll(m);
     if (c == 0) return lo;
     const int64_t lo2 = lo + step * (c - 1) + 1;
@@ -3578,25 +3579,23 @@ __global__ void k_finish_count(const uint32_t* ctr, int which, int64_t* out) {
   *out = e ? err_code(e) : (int64_t)ctr[which];
 }
 
-__global__ void k_batch_offsets(const int64_t* __restrict__ offs, int nseq, int64_t n, Work w,
-                                int64_t* __restrict__ out_off) {
-  int s = blockIdx.x * blockDim.x + threadIdx.x;
+// One wavefront per sequence (and one for the total): the first piece that
+// starts at or after the sequence's first byte, by a 64-way search.
+constexpr int BATCH_OFF_WAVES = 4;
+__global__ __launch_bounds__(64 * BATCH_OFF_WAVES) void k_batch_offsets(const int64_t* __restrict__ offs, int nseq,
+                                                                      int64_t n, Work w,
+                                                                      int64_t* __restrict__ out_off) {
+  const int s = blockIdx.x * BATCH_OFF_WAVES + (int)(threadIdx.x >> 6), lane = (int)(threadIdx.x & 63u);
   if (s > nseq) return;
-  const uint32_t e = w.ctr[CTR_ERR];
-  const uint32_t P = w.ctr[CTR_P];
   if (s == nseq) {
-    out_off[s] = e ? err_code(e) : (int64_t)w.ctr[CTR_T];
+    const uint32_t e = w.ctr[CTR_ERR];
+    if (lane == 0) out_off[s] = e ? err_code(e) : (int64_t)w.ctr[CTR_T];
     return;
   }
   int64_t o = offs[s];
   o = o < 0 ? 0 : (o > n ? n : o);
-  // first piece starting at or after o
-  uint32_t lo = 0, hi = P;
-  while (lo < hi) {
-    uint32_t mid = (lo + hi) >> 1;
-    if ((int64_t)w.piece_start[mid] < o) lo = mid + 1; else hi = mid;
-  }
-  out_off[s] = (int64_t)w.tok_off[lo];
+  const int64_t lo = wave_lower_bound(w.piece_start, (int64_t)w.ctr[CTR_P], o, lane);
+  if (lane == 0) out_off[s] = (int64_t)w.tok_off[lo];
 }
 
 __global__ void k_write_zero_i64(int64_t* out, int cnt) {
@@ -3725,7 +3724,8 @@ hipError_t launch_finish_count(const Work& w, int which, int64_t* out, hipStream
 
 hipError_t launch_batch_offsets(const int64_t* offs, int nseq, int64_t n, const Work& w, int64_t* out_off,
                                 hipStream_t st) {
-  hipLaunchKernelGGL(k_batch_offsets, dim3(ceil_div((int64_t)nseq + 1, 256)), dim3(256), 0, st, offs, nseq, n, w,
+  hipLaunchKernelGGL(k_batch_offsets, dim3(ceil_div((int64_t)nseq + 1, BATCH_OFF_WAVES)), dim3(64 * BATCH_OFF_WAVES), 0, st,
+                     offs, nseq, n, w,
                      out_off); prof_mark("k_batch_offsets", st);
   return hipGetLastError();
 }
