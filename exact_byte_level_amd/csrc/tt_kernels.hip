@@ -1381,44 +1381,50 @@ __device__ uint32_t o2_word_bits(const uint32_t* pl, int lane, int c_lo, int e, 
   const uint32_t LNK = CSX & LINK & ~SS;
   const uint32_t HEAD = CSX & ~LNK;
   const uint32_t RC = CSX | bs_up<1>(CSX) | bs_up<2>(CS2);
-  uint32_t P = CSX;
-  P ^= P << 1;
-  P ^= P << 2;
-  P ^= P << 4;
-  P ^= P << 8;
-  P ^= P << 16;
-  if (__popcll(__ballot(__popc(CSX) & 1) & ((1ull << lane) - 1ull)) & 1) P = ~P;
-  // a shape in the window's first three chars may link to one before the
-  // window, unless the window starts a sequence: heads there are not known
-  const bool seq0 = __ballot((SS & bs_range(x0, 0, 1)) != 0u) != 0ull;
-  const uint32_t EDGE = seq0 ? 0u : bs_range(x0, -(1 << 20), 3);
-  uint32_t HC = HEAD & ~EDGE;
-  uint32_t S1 = HC & (P ^ CAND);
-  // a chain that reaches the tile start with its head before the window:
-  // the carry (the chain state at the tile start) holds the attachment of
-  // its last shape before the tile, which fixes the base for the whole run
-  // of chain chars that ends at c_lo - 1 (lane 0, bit 31)
   const uint32_t cst = ChainOp::entry(ch, 0u);  // (the text starts in phase 0)
-  uint32_t SEED = 0u;
-  if ((cst & 7u) - 2u <= 3u) {
-    const uint32_t r0 = (uint32_t)__builtin_amdgcn_readlane((int)RC, 0);
-    const uint32_t h0 = (uint32_t)__builtin_amdgcn_readlane((int)HC, 0);
-    const uint32_t g0 = (uint32_t)__builtin_amdgcn_readlane((int)EDGE, 0);
-    if (r0 >> 31) {
-      const int z = 31 - __clz((int)~r0);  // the char before that run (chars before the text are 0)
-      if (!(h0 & (~0u << (z + 1))) && ((g0 >> (z + 1)) & 1u)) {
-        const uint32_t p0 = (uint32_t)__builtin_amdgcn_readlane((int)P, 0);
-        SEED = lane == 0 ? 1u << (z + 1) : 0u;
-        if (((p0 >> 31) ^ (cst >> 4)) & 1u) S1 |= SEED;
+  uint32_t ATT = CAND, UNK = 0u;
+  // with no linked shape in the window and no chain carried in, every shape
+  // is its chain's head and the rule below gives ATT = CAND
+  if (__ballot(LNK != 0u) != 0ull || (cst & 7u) - 2u <= 3u) {
+    uint32_t P = CSX;
+    P ^= P << 1;
+    P ^= P << 2;
+    P ^= P << 4;
+    P ^= P << 8;
+    P ^= P << 16;
+    if (__popcll(__ballot(__popc(CSX) & 1) & ((1ull << lane) - 1ull)) & 1) P = ~P;
+    // a shape in the window's first three chars may link to one before the
+    // window, unless the window starts a sequence: heads there are not known
+    const bool seq0 = __ballot((SS & bs_range(x0, 0, 1)) != 0u) != 0ull;
+    const uint32_t EDGE = seq0 ? 0u : bs_range(x0, -(1 << 20), 3);
+    uint32_t HC = HEAD & ~EDGE;
+    uint32_t S1 = HC & (P ^ CAND);
+    // a chain that reaches the tile start with its head before the window:
+    // the carry (the chain state at the tile start) holds the attachment of
+    // its last shape before the tile, which fixes the base for the whole run
+    // of chain chars that ends at c_lo - 1 (lane 0, bit 31)
+    uint32_t SEED = 0u;
+    if ((cst & 7u) - 2u <= 3u) {
+      const uint32_t r0 = (uint32_t)__builtin_amdgcn_readlane((int)RC, 0);
+      const uint32_t h0 = (uint32_t)__builtin_amdgcn_readlane((int)HC, 0);
+      const uint32_t g0 = (uint32_t)__builtin_amdgcn_readlane((int)EDGE, 0);
+      if (r0 >> 31) {
+        const int z = 31 - __clz((int)~r0);  // the char before that run (chars before the text are 0)
+        if (!(h0 & (~0u << (z + 1))) && ((g0 >> (z + 1)) & 1u)) {
+          const uint32_t p0 = (uint32_t)__builtin_amdgcn_readlane((int)P, 0);
+          SEED = lane == 0 ? 1u << (z + 1) : 0u;
+          if (((p0 >> 31) ^ (cst >> 4)) & 1u) S1 |= SEED;
+        }
       }
     }
+    HC |= SEED;
+    const uint32_t F = bs_fill_up((RC & ~HC) | S1, S1, lane) | S1;
+    // chains whose head is not known: from a run start in the first three chars
+    const uint32_t SU0 = RC & EDGE & ~bs_up<1>(RC) & ~SEED;
+    UNK = bs_fill_up(RC & ~HC, SU0, lane) | SU0;
+    ATT = (CAND | (CSX & EDGE & ~UNK)) & ((~UNK & (P ^ F)) | (UNK & ~LINK));
+    UNK &= CSX & (LNK | EDGE);
   }
-  HC |= SEED;
-  const uint32_t F = bs_fill_up((RC & ~HC) | S1, S1, lane) | S1;
-  // chains whose head is not known: from a run start in the first three chars
-  const uint32_t SU0 = RC & EDGE & ~bs_up<1>(RC) & ~SEED;
-  const uint32_t UNK = bs_fill_up(RC & ~HC, SU0, lane) | SU0;
-  const uint32_t ATT = (CAND | (CSX & EDGE & ~UNK)) & ((~UNK & (P ^ F)) | (UNK & ~LINK));
   const uint32_t IC = bs_up<1>(ATT) | bs_up<2>(ATT & CS2);  // letters of an attached contraction
   const uint32_t AFTER = LI & ~SS & (bs_up<2>(ATT & CS1) | bs_up<3>(ATT & CS2));
   // the run of Lm/Lo/marks (no sequence start in it) that ends at c_lo - 1,
@@ -1465,8 +1471,7 @@ __device__ uint32_t o2_word_bits(const uint32_t* pl, int lane, int c_lo, int e, 
   // undecided: a shape of a chain whose head is not known whose own chars
   // or next char lie from c_lo on.  The carried chain state covers every
   // chain that reaches c_lo - 1, so this does not arise; it stays a check.
-  const uint32_t ULU = CSX & UNK & (LNK | EDGE);
-  const uint32_t reach = ULU & ((CS1 & bs_range(x0, c_lo - 2, e)) | (CS2 & bs_range(x0, c_lo - 3, e)));
+  const uint32_t reach = UNK & ((CS1 & bs_range(x0, c_lo - 2, e)) | (CS2 & bs_range(x0, c_lo - 3, e)));
   *unsup = __ballot(reach != 0u) != 0ull;
   return CH & (SS | BN | BL_IN | BL_ST | BO | BWN | BWS) & own;
 }
