@@ -711,9 +711,9 @@ __device__ __forceinline__ uint32_t ds_index(uint32_t code) {
 // ASCII letters C_L2U; ASCII punctuation/symbols that can start a D1 piece
 // (d1: no punctuation, symbol or space of its segment before it) C_L2B; other
 // punctuation/symbols C_O; other letters, marks, "other" chars and every
-// CJK char C_L.
-__device__ __forceinline__ uint32_t ds_sum_code(uint32_t code, bool d1) {
-  const uint32_t idx = ds_index(code), c4 = idx & 15u;
+// CJK char C_L.  idx: ds_index(code).
+__device__ __forceinline__ uint32_t ds_sum_code(uint32_t code, bool d1, uint32_t idx) {
+  const uint32_t c4 = idx & 15u;
   const bool keep = (idx == 0u) | (c4 == 1u) | (c4 - 3u <= 2u);  // no char, digits, whitespace
   uint32_t c = C_L;
   c = c4 == 7u ? C_O : c;
@@ -834,7 +834,7 @@ __global__ __launch_bounds__(PT_THREADS) void k_tile_summary(const uint8_t* __re
       const uint64_t m = starts & (0xFFFFFFull << (8 * (k + 1)));  // window bytes k + 1 .. k + 3
       const int pos = m ? (63 - __clzll((long long)m)) >> 3 : k;
       const uint32_t pidx = (uint32_t)(win >> (8 * pos)) & CB_IDX, pc4 = pidx & 15u;
-      cap[k] = (ds_index(code[k]) & 31u) == 6u &&
+      cap[k] = ((out >> (8 * k)) & CB_IDX) == 6u &&
                ((code[k] & K_SEQ_START) || pidx == 0u || (pidx & 16u) || !(pc4 == 4u || pc4 == 6u || pc4 == 7u));
     }
   }
@@ -845,7 +845,7 @@ __global__ __launch_bounds__(PT_THREADS) void k_tile_summary(const uint8_t* __re
     // o200k-style summaries see marks as letters and letters by case (class
     // values 6 and 7 included)
     if (PAT == 2) code[k] = o2_sum_code(code[k]);
-    if (PAT == 3) code[k] = ds_sum_code(code[k], cap[k]);
+    if (PAT == 3) code[k] = ds_sum_code(code[k], cap[k], (out >> (8 * k)) & CB_IDX);
     if (ch[k]) {
       fv = FwdOp::combine(fv, FwdOp::elem(code[k]));
       if (PAT == 2) tv = TailOp::combine(tv, TailOp::elem(code[k]));
