@@ -682,8 +682,7 @@ __device__ __forceinline__ uint32_t o2_index(uint32_t code) {
 // are letters, and letters split into three classes (upper case C_L2U, lower
 // case C_L, Lm/Lo/marks C_L2B) so that a run of one case is one run.
 constexpr uint32_t C_L2U = 6u, C_L2B = 7u;
-__device__ __forceinline__ uint32_t o2_sum_code(uint32_t code) {
-  const uint32_t idx = o2_index(code);
+__device__ __forceinline__ uint32_t o2_sum_code(uint32_t code, uint32_t idx) {  // idx: o2_index(code)
   if (!(idx & 16u)) return code;
   const uint32_t c = (idx & 8u) ? C_L : (idx & 7u) == 7u ? C_L2B : C_L2U;
   return (code & ~7u) | c;
@@ -844,7 +843,7 @@ __global__ __launch_bounds__(PT_THREADS) void k_tile_summary(const uint8_t* __re
     ch[k] = is_char(code[k]);
     // o200k-style summaries see marks as letters and letters by case (class
     // values 6 and 7 included)
-    if (PAT == 2) code[k] = o2_sum_code(code[k]);
+    if (PAT == 2) code[k] = o2_sum_code(code[k], (out >> (8 * k)) & CB_IDX);
     if (PAT == 3) code[k] = ds_sum_code(code[k], cap[k], (out >> (8 * k)) & CB_IDX);
     if (ch[k]) {
       fv = FwdOp::combine(fv, FwdOp::elem(code[k]));
