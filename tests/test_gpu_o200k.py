@@ -23,7 +23,7 @@ torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
 
 import exact_byte_level_amd as tt  # noqa: E402
-from oracle.bpe import Vocab, encode as oracle_encode  # noqa: E402
+from oracle.bpe import Vocab, encode as oracle_encode, encode_batch as oracle_encode_batch, token_starts  # noqa: E402
 from oracle.pretok import O200K, piece_starts_batch, split_bytes  # noqa: E402
 from synth import mix_text  # noqa: E402
 
@@ -264,6 +264,29 @@ def test_random_chain_and_mark_text():
         rng = random.Random(seed)
         text = "".join(rng.choice(toks) for _ in range(90_000))
         _check_text(text, v)
+
+
+def test_chain_batch_encode_and_offsets():
+    """tt_encode_batch and tt_encode_offsets on a batch of chain and mark-run
+    texts (sequence starts inside chains and runs): ids, per-sequence token
+    offsets and every token's byte start against the oracle."""
+    v = load()
+    texts = CHAIN_TEXTS + ["x" + "'s" * 700, "'ll" * 400, "it's" + "中" * 600 + "Ab", "a's's" + "ª" * 700 + "Ab",
+                           _chain_edge_text(11, units=(5, 40), ntiles=12).decode(), "", "'", "s", "ª" * 5 + "A"]
+    data, offs = batch(texts)
+    want_ids, want_off = oracle_encode_batch(data, offs, v, O200K, {})
+    off_t = torch.tensor(offs, dtype=torch.int64, device="cuda")
+    say("o200k chain batch: %d texts, %d bytes" % (len(texts), len(data)))
+    ids, out_off = tt.encode_batch(dev(data), off_t)
+    assert out_off.tolist() == want_off
+    assert np.array_equal(ids.cpu().numpy(), np.asarray(want_ids, dtype=np.int32))
+    ids2, starts, cnt = tt.encode_offsets(dev(data), off_t)
+    assert cnt.tolist() == want_off
+    assert np.array_equal(ids2.cpu().numpy(), np.asarray(want_ids, dtype=np.int32))
+    want_st = []
+    for q in range(len(texts)):
+        want_st += token_starts(want_ids[want_off[q]:want_off[q + 1]], v, offs[q])[:-1]
+    assert starts.cpu().numpy().tolist() == want_st + [len(data)]
 
 
 def test_sessions_are_refused():
