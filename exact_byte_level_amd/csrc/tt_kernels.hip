@@ -3436,16 +3436,6 @@ __device__ __forceinline__ int64_t prev_char_start(const uint8_t* __restrict__ t
   return s;
 }
 
-// first index i in [0, cnt] with a[i] >= v
-__device__ __forceinline__ int64_t lower_bound_i32(const int32_t* __restrict__ a, int64_t cnt, int64_t v) {
-  int64_t lo = 0, hi = cnt;
-  while (lo < hi) {
-    const int64_t mid = (lo + hi) >> 1;
-    if ((int64_t)a[mid] < v) lo = mid + 1; else hi = mid;
-  }
-  return lo;
-}
-
 // window starts of the next append for a text of n bytes: char starts at or
 // before n - (tail << k), or 0
 __device__ void session_next_windows(const uint8_t* __restrict__ text, int64_t n, int64_t tail, int64_t* info) {
@@ -3482,12 +3472,8 @@ __global__ __launch_bounds__(256) void k_splice_find(const uint8_t* __restrict__
     p = 0;  // the window is the whole text
   } else {
     const int64_t lo = 16, hi = n_old - 20 - w0;  // window-relative range of p
-    // first piece starting at or after lo
-    uint32_t a = 0, b = P;
-    while (a < b) {
-      const uint32_t mid = (a + b) >> 1;
-      if ((int64_t)w.piece_start[mid] < lo) a = mid + 1; else b = mid;
-    }
+    // first piece starting at or after lo (each wavefront searches 64-way)
+    const uint32_t a = (uint32_t)wave_lower_bound(w.piece_start, (int64_t)P, lo, (int)(threadIdx.x & 63u));
     for (uint32_t k0 = a; k0 < P; k0 += 256) {
       const uint32_t k = k0 + threadIdx.x;
       uint32_t best = 0xFFFFFFFFu;
@@ -3510,15 +3496,24 @@ __global__ __launch_bounds__(256) void k_splice_find(const uint8_t* __restrict__
       if (last > hi) break;
     }
   }
-  if (threadIdx.x != 0) return;
-  info[SI_ERROR] = 0;
-  info[SI_TWIN] = wc;
+  if (threadIdx.x >= 64) return;
+  const int lane = (int)threadIdx.x;
+  if (lane == 0) {
+    info[SI_ERROR] = 0;
+    info[SI_TWIN] = wc;
+  }
   if (p < 0) {
-    info[SI_STATUS] = SS_NONE;
+    if (lane == 0) info[SI_STATUS] = SS_NONE;
     return;
   }
-  const int64_t iw = lower_bound_i32(win_starts, wc, p - w0);
-  const int64_t io = lower_bound_i32(starts, t_old, p);
+  // token index of p on both sides, by 64-way searches of one wavefront.  In
+  // the old text every token index below t_old - (n_old - w0) - 1 starts
+  // before w0 < p (tokens are at least a byte long and end at n_old), so that
+  // search starts there
+  const int64_t iw = wave_lower_bound(win_starts, wc, p - w0, lane);
+  const int64_t ob = max<int64_t>(0, t_old - (n_old - w0) - 1);
+  const int64_t io = ob + wave_lower_bound(starts + ob, t_old - ob, p, lane);
+  if (lane != 0) return;
   // p must start a token on both sides (it does whenever the reach argument
   // holds; a mismatch falls back to a full encode)
   const bool odd = iw > wc || win_starts[iw] != (int32_t)(p - w0) || io > t_old || starts[io] != (int32_t)p;
@@ -3702,8 +3697,12 @@ hipError_t launch_bpe_emit(const uint8_t* bytes, int64_t n, const Tables& tb, co
   }
   const dim3 g(ntiles), b(EMIT_THREADS);
   if (out_starts) {
-    hipLaunchKernelGGL(k_chunk_sums, dim3(capped_grid(n, HUGE_CHUNK, 1024)), dim3(EMIT_THREADS), 0, st, w, tb.tok_len);
-    prof_mark("k_chunk_sums", st);
+    // a piece of more than HUGE_CHUNK tokens has more than HUGE_CHUNK bytes
+    if (n > (int64_t)HUGE_CHUNK) {
+      hipLaunchKernelGGL(k_chunk_sums, dim3(capped_grid(n, HUGE_CHUNK, 1024)), dim3(EMIT_THREADS), 0, st, w,
+                         tb.tok_len);
+      prof_mark("k_chunk_sums", st);
+    }
     if (sb)
       hipLaunchKernelGGL((k_emit<true, true>), g, b, 0, st, w, ntiles, out_ids, out_n, (uint32_t)n, out_starts,
                          tb.tok_len);
