@@ -3453,10 +3453,14 @@ __device__ void session_next_windows(const uint8_t* __restrict__ text, int64_t n
 // One workgroup: pick the splice byte (the first qualifying pre-token start
 // of the window) and the token indices on both sides.
 __global__ __launch_bounds__(256) void k_splice_find(const uint8_t* __restrict__ text, int64_t w0, int64_t n_old,
-                                                     int pattern, const int32_t* __restrict__ starts, int64_t t_old,
+                                                     int pattern, int32_t* __restrict__ starts, int64_t t_old,
                                                      const int32_t* __restrict__ win_starts, Work w,
-                                                     int64_t* __restrict__ info) {
+                                                     int64_t* __restrict__ info, int64_t n_new, int64_t tail,
+                                                     int32_t* __restrict__ ids, const int32_t* __restrict__ win_ids,
+                                                     bool do_copy) {
   __shared__ uint32_t red[8];
+  __shared__ int64_t sh_io, sh_iw;
+  __shared__ int sh_status;
   const int64_t wc = info[SI_WIN_CNT];
   const uint32_t err = w.ctr[CTR_ERR];
   if (wc < 0 || err) {
@@ -3496,32 +3500,55 @@ __global__ __launch_bounds__(256) void k_splice_find(const uint8_t* __restrict__
       if (last > hi) break;
     }
   }
-  if (threadIdx.x >= 64) return;
-  const int lane = (int)threadIdx.x;
-  if (lane == 0) {
-    info[SI_ERROR] = 0;
-    info[SI_TWIN] = wc;
+  if (threadIdx.x < 64) {
+    const int lane = (int)threadIdx.x;
+    if (lane == 0) {
+      info[SI_ERROR] = 0;
+      info[SI_TWIN] = wc;
+    }
+    int status = SS_NONE;
+    int64_t iw = 0, io = 0;
+    if (p >= 0) {
+      // token index of p on both sides, by 64-way searches of one wavefront.
+      // In the old text every token index below t_old - (n_old - w0) - 1
+      // starts before w0 < p (tokens are at least a byte long and end at
+      // n_old), so that search starts there
+      iw = wave_lower_bound(win_starts, wc, p - w0, lane);
+      const int64_t ob = max<int64_t>(0, t_old - (n_old - w0) - 1);
+      io = ob + wave_lower_bound(starts + ob, t_old - ob, p, lane);
+      // p must start a token on both sides (it does whenever the reach
+      // argument holds; a mismatch falls back to a full encode)
+      const bool odd = iw > wc || win_starts[iw] != (int32_t)(p - w0) || io > t_old || starts[io] != (int32_t)p;
+      status = odd ? SS_ODD : SS_SPLICED;
+      if (lane == 0) {
+        info[SI_P] = p;
+        info[SI_IOLD] = io;
+        info[SI_IWIN] = iw;
+        info[SI_T] = io + (wc - iw);
+      }
+    }
+    if (lane == 0) {
+      info[SI_STATUS] = status;
+      sh_status = status;
+      sh_io = io;
+      sh_iw = iw;
+    }
   }
-  if (p < 0) {
-    if (lane == 0) info[SI_STATUS] = SS_NONE;
-    return;
+  // the splice itself, for a window small enough for one workgroup (else
+  // k_splice_copy does it): W's tokens from p over the session's arrays
+  // from A's token index of p (the check above read starts[io] first)
+  if (!do_copy) return;
+  __syncthreads();
+  if (sh_status != SS_SPLICED) return;
+  const int64_t io = sh_io, iw = sh_iw;
+  for (int64_t i = iw + (int64_t)threadIdx.x; i < wc; i += 256) {
+    ids[io + (i - iw)] = win_ids[i];
+    starts[io + (i - iw)] = (int32_t)(win_starts[i] + w0);
   }
-  // token index of p on both sides, by 64-way searches of one wavefront.  In
-  // the old text every token index below t_old - (n_old - w0) - 1 starts
-  // before w0 < p (tokens are at least a byte long and end at n_old), so that
-  // search starts there
-  const int64_t iw = wave_lower_bound(win_starts, wc, p - w0, lane);
-  const int64_t ob = max<int64_t>(0, t_old - (n_old - w0) - 1);
-  const int64_t io = ob + wave_lower_bound(starts + ob, t_old - ob, p, lane);
-  if (lane != 0) return;
-  // p must start a token on both sides (it does whenever the reach argument
-  // holds; a mismatch falls back to a full encode)
-  const bool odd = iw > wc || win_starts[iw] != (int32_t)(p - w0) || io > t_old || starts[io] != (int32_t)p;
-  info[SI_STATUS] = odd ? SS_ODD : SS_SPLICED;
-  info[SI_P] = p;
-  info[SI_IOLD] = io;
-  info[SI_IWIN] = iw;
-  info[SI_T] = io + (wc - iw);
+  if (threadIdx.x == 0) {
+    starts[io + (wc - iw)] = (int32_t)n_new;
+    session_next_windows(text, n_new, tail, info);
+  }
 }
 
 // The splice itself: W's tokens from p (ids, and starts shifted by w0) over
@@ -3754,12 +3781,17 @@ hipError_t launch_zero_counters(const Work& w, hipStream_t st) {
 hipError_t launch_splice(const uint8_t* text, int64_t w0, int64_t n_old, int64_t n_new, int pattern, int64_t tail,
                          int32_t* ids, int32_t* starts, int64_t t_old, const int32_t* win_ids,
                          const int32_t* win_starts, const Work& w, int64_t* info, hipStream_t st) {
+  // a window of up to 64 KiB (at most that many tokens) is spliced by the
+  // search's own workgroup; a larger one by the grid-wide copy after it
+  const bool fused = n_new - w0 <= ((int64_t)1 << 16);
   hipLaunchKernelGGL(k_splice_find, dim3(1), dim3(256), 0, st, text, w0, n_old, pattern, starts, t_old, win_starts, w,
-                     info);
+                     info, n_new, tail, ids, win_ids, fused);
   prof_mark("k_splice_find", st);
-  hipLaunchKernelGGL(k_splice_copy, dim3(capped_grid(n_new - w0, 4096, 1024)), dim3(256), 0, st, text, w0, n_new, tail,
-                     ids, starts, win_ids, win_starts, info);
-  prof_mark("k_splice_copy", st);
+  if (!fused) {
+    hipLaunchKernelGGL(k_splice_copy, dim3(capped_grid(n_new - w0, 4096, 1024)), dim3(256), 0, st, text, w0, n_new,
+                       tail, ids, starts, win_ids, win_starts, info);
+    prof_mark("k_splice_copy", st);
+  }
   return hipGetLastError();
 }
 

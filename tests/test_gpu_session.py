@@ -155,6 +155,28 @@ def test_capacity_reset_and_reload():
     check(s, b"abc def ghi", v, GPT2, memo)
 
 
+@pytest.mark.parametrize("pattern,vocab_name", [(GPT2, "c1"), (CL100K, "c3")])
+def test_large_appends(pattern, vocab_name):
+    """Appends whose window is over 64 KiB (spliced by the grid-wide copy) and
+    small ones after them (spliced by the search's own workgroup)."""
+    v = load(vocab_name, pattern)
+    memo = {}
+    s = tt.Session(400_000, 256)
+    text = mix_text(6_000, 90 + pattern, multibyte=True)
+    s.reset(dev(text))
+    say("session large appends pattern", pattern)
+    src = mix_text(200_000, 91 + pattern, multibyte=True)
+    pos = 0
+    for k in (80_000, 300, 70_000, 1400):
+        d = _whole_chars(src, pos, k)
+        pos += len(d)
+        info = s.append(dev(d))
+        text += d
+        assert info["tokens"] == s.sizes()[1]
+        check(s, text, v, pattern, memo)
+    s.close()
+
+
 def test_million_char_context():
     v = load("c2", GPT2)
     from synth.text import workload
