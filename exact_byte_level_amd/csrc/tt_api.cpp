@@ -244,7 +244,8 @@ struct tt_session {
   int32_t* win_ids = nullptr;
   int32_t* win_starts = nullptr;
   int64_t* info_dev = nullptr;
-  int64_t* info_host = nullptr;
+  int64_t* info_host = nullptr;  // pinned, mapped: the kernels that finish a step write it
+  int64_t* info_map = nullptr;   // its device address
   int64_t next_w0[SESSION_LEVELS] = {};
 };
 
@@ -263,9 +264,8 @@ void session_release(tt_session* s) {
 
 // Read the info block of the last step (one stream synchronisation).
 int session_read_info(tt_session* s, hipStream_t st) {
-  if (hipMemcpyAsync(s->info_host, s->info_dev, SI_COUNT * sizeof(int64_t), hipMemcpyDeviceToHost, st) != hipSuccess ||
-      hipStreamSynchronize(st) != hipSuccess)
-    return TT_EHIP;
+  // the step's last kernel wrote info_host through its mapped address
+  if (hipStreamSynchronize(st) != hipSuccess) return TT_EHIP;
   return TT_OK;
 }
 
@@ -277,7 +277,7 @@ void session_take_windows(tt_session* s) {
 int session_full(tt_session* s, int64_t n, hipStream_t st) {
   if (launch_pretokenize(s->text, n, nullptr, 1, g.pattern, g.w, g.w.piece_start, nullptr, &g.tb, st) != hipSuccess ||
       launch_bpe_emit(s->text, n, g.tb, g.w, s->ids, s->info_dev + SI_WIN_CNT, s->starts, st) != hipSuccess ||
-      launch_session_full(s->text, n, s->tail, g.w, s->info_dev, st) != hipSuccess)
+      launch_session_full(s->text, n, s->tail, g.w, s->info_dev, s->info_map, st) != hipSuccess)
     return TT_EHIP;
   return session_read_info(s, st);
 }
@@ -715,7 +715,9 @@ int tt_session_create(int64_t capacity, int64_t tail_bytes, tt_session** out) {
             hipMalloc((void**)&s->starts, c1 * 4) == hipSuccess && hipMalloc((void**)&s->win_ids, c1 * 4) == hipSuccess &&
             hipMalloc((void**)&s->win_starts, c1 * 4) == hipSuccess &&
             hipMalloc((void**)&s->info_dev, SI_COUNT * sizeof(int64_t)) == hipSuccess &&
-            hipHostMalloc((void**)&s->info_host, SI_COUNT * sizeof(int64_t), hipHostMallocDefault) == hipSuccess;
+            hipHostMalloc((void**)&s->info_host, SI_COUNT * sizeof(int64_t),
+                          hipHostMallocMapped | hipHostMallocCoherent) == hipSuccess &&
+            hipHostGetDevicePointer((void**)&s->info_map, s->info_host, 0) == hipSuccess;
   if (!ok) {
     (void)hipGetLastError();
     session_release(s);
@@ -794,7 +796,7 @@ int tt_session_append(tt_session* s, const uint8_t* dev_delta, int64_t nd, int64
         launch_bpe_emit(s->text + w0, nw, g.tb, g.w, s->win_ids, s->info_dev + SI_WIN_CNT, s->win_starts, stream) !=
             hipSuccess ||
         launch_splice(s->text, w0, n_old, n_new, g.pattern, s->tail, s->ids, s->starts, s->T, s->win_ids,
-                      s->win_starts, g.w, s->info_dev, stream) != hipSuccess)
+                      s->win_starts, g.w, s->info_dev, s->info_map, stream) != hipSuccess)
       return TT_EHIP;
     if ((rc = session_read_info(s, stream)) != TT_OK) return rc;
     const int64_t* h = s->info_host;

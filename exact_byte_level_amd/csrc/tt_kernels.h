@@ -34,13 +34,14 @@ hipError_t launch_batch_offsets(const int64_t* offs, int nseq, int64_t n, const 
 // win_ids / win_starts (count in info[SI_WIN_CNT]): choose the splice byte
 // and, if one qualifies, copy the window's tokens from it over ids / starts
 // (t_old tokens of text[0, n_old)).  Results and the next append's window
-// starts go to info (device int64[SI_COUNT]).
+// starts go to info (device int64[SI_COUNT]), and a copy of info, once final,
+// to info_out (the device address of pinned, mapped host memory).
 hipError_t launch_splice(const uint8_t* text, int64_t w0, int64_t n_old, int64_t n_new, int pattern, int64_t tail,
                          int32_t* ids, int32_t* starts, int64_t t_old, const int32_t* win_ids,
-                         const int32_t* win_starts, const Work& w, int64_t* info, hipStream_t st);
+                         const int32_t* win_starts, const Work& w, int64_t* info, int64_t* info_out, hipStream_t st);
 // After a full encode of text[0, n) with its count in info[SI_WIN_CNT].
 hipError_t launch_session_full(const uint8_t* text, int64_t n, int64_t tail, const Work& w, int64_t* info,
-                               hipStream_t st);
+                               int64_t* info_out, hipStream_t st);
 
 // Device address of the fixed scratch array of the no-alloc encode on the
 // current device: looked up with hipGetSymbolAddress on the first call per

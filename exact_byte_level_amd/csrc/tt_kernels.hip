@@ -3438,6 +3438,13 @@ __device__ __forceinline__ int64_t prev_char_start(const uint8_t* __restrict__ t
 
 // window starts of the next append for a text of n bytes: char starts at or
 // before n - (tail << k), or 0
+// The session's info words to the host's copy (pinned, mapped host memory
+// that kernels only write): by the thread that wrote the last of them.
+__device__ __forceinline__ void publish_info(const int64_t* info, int64_t* __restrict__ out) {
+#pragma unroll
+  for (int i = 0; i < SI_COUNT; ++i) out[i] = info[i];
+}
+
 __device__ void session_next_windows(const uint8_t* __restrict__ text, int64_t n, int64_t tail, int64_t* info) {
   for (int k = 0; k < SESSION_LEVELS; ++k) {
     int64_t s = n - (tail << k);
@@ -3457,7 +3464,7 @@ __global__ __launch_bounds__(256) void k_splice_find(const uint8_t* __restrict__
                                                      const int32_t* __restrict__ win_starts, Work w,
                                                      int64_t* __restrict__ info, int64_t n_new, int64_t tail,
                                                      int32_t* __restrict__ ids, const int32_t* __restrict__ win_ids,
-                                                     bool do_copy) {
+                                                     bool do_copy, int64_t* __restrict__ info_out) {
   __shared__ uint32_t red[8];
   __shared__ int64_t sh_io, sh_iw;
   __shared__ int sh_status;
@@ -3467,6 +3474,7 @@ __global__ __launch_bounds__(256) void k_splice_find(const uint8_t* __restrict__
     if (threadIdx.x == 0) {
       info[SI_STATUS] = SS_NONE;
       info[SI_ERROR] = wc < 0 ? wc : err_code(err);
+      publish_info(info, info_out);
     }
     return;
   }
@@ -3529,6 +3537,7 @@ __global__ __launch_bounds__(256) void k_splice_find(const uint8_t* __restrict__
     }
     if (lane == 0) {
       info[SI_STATUS] = status;
+      publish_info(info, info_out);  // final unless the splice below adds the next windows
       sh_status = status;
       sh_io = io;
       sh_iw = iw;
@@ -3548,6 +3557,7 @@ __global__ __launch_bounds__(256) void k_splice_find(const uint8_t* __restrict__
   if (threadIdx.x == 0) {
     starts[io + (wc - iw)] = (int32_t)n_new;
     session_next_windows(text, n_new, tail, info);
+    publish_info(info, info_out);
   }
 }
 
@@ -3559,7 +3569,7 @@ __global__ __launch_bounds__(256) void k_splice_copy(const uint8_t* __restrict__
                                                      int32_t* __restrict__ starts,
                                                      const int32_t* __restrict__ win_ids,
                                                      const int32_t* __restrict__ win_starts,
-                                                     int64_t* __restrict__ info) {
+                                                     int64_t* __restrict__ info, int64_t* __restrict__ info_out) {
   if (info[SI_STATUS] != SS_SPLICED) return;
   const int64_t io = info[SI_IOLD], iw = info[SI_IWIN], wc = info[SI_TWIN];
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
@@ -3570,13 +3580,14 @@ __global__ __launch_bounds__(256) void k_splice_copy(const uint8_t* __restrict__
   if (blockIdx.x == 0 && threadIdx.x == 0) {
     starts[io + (wc - iw)] = (int32_t)n_new;
     session_next_windows(text, n_new, tail, info);
+    publish_info(info, info_out);
   }
 }
 
 // After a full encode of the session text into its own arrays (count in
 // info[SI_WIN_CNT]): status, T and the next append's window starts.
 __global__ void k_session_full(const uint8_t* __restrict__ text, int64_t n, int64_t tail, Work w,
-                               int64_t* __restrict__ info) {
+                               int64_t* __restrict__ info, int64_t* __restrict__ info_out) {
   const int64_t c = info[SI_WIN_CNT];
   const uint32_t err = w.ctr[CTR_ERR];
   info[SI_STATUS] = SS_FULL;
@@ -3584,6 +3595,7 @@ __global__ void k_session_full(const uint8_t* __restrict__ text, int64_t n, int6
   info[SI_T] = c < 0 ? 0 : c;
   info[SI_P] = 0;
   session_next_windows(text, n, tail, info);
+  publish_info(info, info_out);
 }
 
 // ------------------------------------------------------------- small kernels
@@ -3780,24 +3792,24 @@ hipError_t launch_zero_counters(const Work& w, hipStream_t st) {
 
 hipError_t launch_splice(const uint8_t* text, int64_t w0, int64_t n_old, int64_t n_new, int pattern, int64_t tail,
                          int32_t* ids, int32_t* starts, int64_t t_old, const int32_t* win_ids,
-                         const int32_t* win_starts, const Work& w, int64_t* info, hipStream_t st) {
+                         const int32_t* win_starts, const Work& w, int64_t* info, int64_t* info_out, hipStream_t st) {
   // a window of up to 64 KiB (at most that many tokens) is spliced by the
   // search's own workgroup; a larger one by the grid-wide copy after it
   const bool fused = n_new - w0 <= ((int64_t)1 << 16);
   hipLaunchKernelGGL(k_splice_find, dim3(1), dim3(256), 0, st, text, w0, n_old, pattern, starts, t_old, win_starts, w,
-                     info, n_new, tail, ids, win_ids, fused);
+                     info, n_new, tail, ids, win_ids, fused, info_out);
   prof_mark("k_splice_find", st);
   if (!fused) {
     hipLaunchKernelGGL(k_splice_copy, dim3(capped_grid(n_new - w0, 4096, 1024)), dim3(256), 0, st, text, w0, n_new,
-                       tail, ids, starts, win_ids, win_starts, info);
+                       tail, ids, starts, win_ids, win_starts, info, info_out);
     prof_mark("k_splice_copy", st);
   }
   return hipGetLastError();
 }
 
 hipError_t launch_session_full(const uint8_t* text, int64_t n, int64_t tail, const Work& w, int64_t* info,
-                               hipStream_t st) {
-  hipLaunchKernelGGL(k_session_full, dim3(1), dim3(1), 0, st, text, n, tail, w, info);
+                               int64_t* info_out, hipStream_t st) {
+  hipLaunchKernelGGL(k_session_full, dim3(1), dim3(1), 0, st, text, n, tail, w, info, info_out);
   prof_mark("k_session_full", st);
   return hipGetLastError();
 }
